@@ -1,0 +1,198 @@
+"""CPU fp64 oracle for single-token decode attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library (``kv_cache_gqa_amd``) and never imports it.
+
+The arithmetic lives in ``kvc_oracle.c`` (plain loops, double precision); this
+module only marshals arrays into it.  Pages followed:
+
+* "大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com), section 三 3.3:
+  query head i uses KV head floor(i*g/h); section 二: KV cache size formula.
+* "每生成一个词为何又重算全文？KV Cache 的增量解码" (zwjcode.cn), sections 02,
+  04, 08, 10: per-step shapes, worked example, append position, invisible
+  unwritten slots; section 02 also the element count 2*L*N*H*T*d.
+* "KV Cache 优化与注意力机制加速：FlashAttention / PagedAttention"
+  (plumephp.com), sections 2.2-2.5 (m, l, lse = m + log l, sequence split),
+  3.2 (size formula), 4.2-4.3 (block table lookup).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvc_oracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    vp, ip, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    lib.kvo_decode.argtypes = [vp, vp, vp, ip, vp, ip, ip, vp, ip, ip, ip, ip, ip, dp,
+                               vp, vp, ip]
+    lib.kvo_decode.restype = None
+    lib.kvo_decode_split.argtypes = [vp, vp, vp, ip, vp, ip, ip, vp, ip, ip, ip, ip, ip,
+                                     dp, ip, vp, vp, ip]
+    lib.kvo_decode_split.restype = None
+    lib.kvo_append.argtypes = [vp, vp, vp, vp, ip, vp, ip, ip, vp, ip, ip, ip, ip]
+    lib.kvo_append.restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _lib = configure(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _raw(x, dtype_code=None):
+    """Return (contiguous numpy view of the raw storage, dtype code).
+
+    Accepts numpy arrays or CPU torch tensors (float32, bfloat16, int32).
+    bfloat16 storage is passed as its uint16 bit pattern, unchanged."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        t = x.detach()
+        if t.device.type != "cpu":
+            raise ValueError("oracle inputs must be host (CPU) tensors")
+        t = t.contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16), BF16
+        if t.dtype == torch.float32:
+            return t.numpy(), F32
+        if t.dtype == torch.int32:
+            return t.numpy(), None
+        raise TypeError(f"unsupported oracle input dtype {t.dtype}")
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:  # raw bf16 bits
+        return a, BF16
+    if a.dtype == np.int32:
+        return a, None
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def _i32(x):
+    """Contiguous int32 numpy copy of a list, numpy array or CPU torch tensor."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _same_dtype(*codes):
+    codes = [c for c in codes if c is not None]
+    if len(set(codes)) != 1:
+        raise TypeError("q, K and V must share one dtype")
+    return codes[0]
+
+
+def decode(q, k, v, seq_lens, scale, block_table=None, block_size=16, nthreads=0):
+    """out [B,h,d] float64, lse [B,h] float64 of single-token decode attention.
+
+    q [B,h,d]; k, v contiguous [B,g,t_cap,d] or (with block_table [B,max_blocks])
+    paged pools [num_blocks,g,block_size,d]; seq_lens [B] attended lengths.
+    ``scale`` is used as the float32 value the GPU receives, widened exactly."""
+    qa, qd = _raw(q)
+    ka, kd = _raw(k)
+    va, vd = _raw(v)
+    dt = _same_dtype(qd, kd, vd)
+    sl = _i32(seq_lens)
+    B, h, d = qa.shape
+    if block_table is None:
+        _, g, t_cap, _ = ka.shape
+        bt, max_blocks, bsz = None, 0, 0
+    else:
+        bt = _i32(block_table)
+        _, g, bsz, _ = ka.shape
+        assert bsz == block_size
+        max_blocks = bt.shape[1]
+        t_cap = 0
+    out = np.zeros((B, h, d), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    sc = float(np.float32(scale))
+    _load().kvo_decode(_ptr(qa), _ptr(ka), _ptr(va), dt,
+                       _ptr(bt) if bt is not None else None, max_blocks, bsz,
+                       _ptr(sl), B, h, g, d, t_cap, sc, _ptr(out), _ptr(lse), int(nthreads))
+    return out, lse
+
+
+def decode_split(q, k, v, seq_lens, scale, chunk_len, block_table=None, block_size=16,
+                 nthreads=0):
+    """Split-and-merge reference: chunks of ``chunk_len`` positions, each turned
+    into (O_c, lse_c), then merged by log-sum-exp.  Same arguments as decode."""
+    qa, qd = _raw(q)
+    ka, kd = _raw(k)
+    va, vd = _raw(v)
+    dt = _same_dtype(qd, kd, vd)
+    sl = _i32(seq_lens)
+    B, h, d = qa.shape
+    if block_table is None:
+        _, g, t_cap, _ = ka.shape
+        bt, max_blocks, bsz = None, 0, 0
+    else:
+        bt = _i32(block_table)
+        _, g, bsz, _ = ka.shape
+        max_blocks = bt.shape[1]
+        t_cap = 0
+    out = np.zeros((B, h, d), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    sc = float(np.float32(scale))
+    _load().kvo_decode_split(_ptr(qa), _ptr(ka), _ptr(va), dt,
+                             _ptr(bt) if bt is not None else None, max_blocks, bsz,
+                             _ptr(sl), B, h, g, d, t_cap, sc, int(chunk_len),
+                             _ptr(out), _ptr(lse), int(nthreads))
+    return out, lse
+
+
+def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, block_size=16):
+    """Return new (k_cache, v_cache) numpy arrays (raw storage) with the new
+    token's K/V of every (b, j) written at position seq_lens_before[b]."""
+    kn, kd = _raw(k_new)
+    vn, vd = _raw(v_new)
+    kc, kcd = _raw(k_cache)
+    vc, vcd = _raw(v_cache)
+    dt = _same_dtype(kd, vd, kcd, vcd)
+    kc = kc.copy()
+    vc = vc.copy()
+    sl = _i32(seq_lens_before)
+    B, g, d = kn.shape
+    if block_table is None:
+        t_cap = kc.shape[2]
+        bt, max_blocks, bsz = None, 0, 0
+    else:
+        bt = _i32(block_table)
+        max_blocks = bt.shape[1]
+        bsz = kc.shape[2]
+        t_cap = 0
+    _load().kvo_append(_ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), dt,
+                       _ptr(bt) if bt is not None else None, max_blocks, bsz,
+                       _ptr(sl), B, g, d, t_cap)
+    return kc, vc
+
+
+def kv_cache_bytes(layers: int, batch: int, kv_heads: int, tokens: int, head_dim: int,
+                   elem_bytes: int) -> int:
+    """Closed-form KV cache size: 2 (K and V) x layers x batch x KV heads x
+    tokens x head_dim x element bytes.  The zwjcode.cn page (section 02) gives
+    the element count 2*L*N*H*T*d; the limoncc.com page (section 二) and the
+    plumephp.com page (section 3.2) give the byte form."""
+    return 2 * layers * batch * kv_heads * tokens * head_dim * elem_bytes

@@ -1,0 +1,368 @@
+"""Pins that tie the CPU fp64 oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees.  They
+are run by tests/test_oracle.py directly and again by the mutation test,
+which plants plausible mistakes in copies of the oracle source and checks that
+at least one pin fails for every mistake.
+
+Pages:
+  [P1] "大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com)
+  [P2] "从KV cache共享到批量调度：注意力机制下的隔离问题与口令实验" (0539edu.com)
+  [P3] "每生成一个词为何又重算全文？KV Cache 的增量解码" (zwjcode.cn)
+  [P4] "KV Cache 优化与注意力机制加速：FlashAttention / PagedAttention" (plumephp.com)
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import kvc_workloads as W
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f64(t):
+    return t.to(torch.float64)
+
+
+def sdpa_reference(q, k, v, lengths, scale):
+    """torch scaled_dot_product_attention in fp64 on the CPU, GQA through
+    ``enable_gqa`` ([P3] section 06 and 15), invalid positions masked out.
+    q [B,h,d], k/v [B,g,T,d]; returns out [B,h,d], and lse computed by
+    torch.logsumexp over the masked scores (library routines only)."""
+    B, h, d = q.shape
+    T = k.shape[2]
+    qq = _f64(q).unsqueeze(2)                  # [B,h,1,d]
+    kk, vv = _f64(k), _f64(v)
+    valid = torch.arange(T).view(1, T) < torch.as_tensor(lengths).view(-1, 1)  # [B,T]
+    mask = valid.view(B, 1, 1, T)
+    out = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=scale,
+                                         enable_gqa=True).squeeze(2)
+    g = k.shape[1]
+    kx = kk.repeat_interleave(h // g, dim=1)   # [B,h,T,d]
+    scores = torch.matmul(qq, kx.transpose(-1, -2).contiguous()).squeeze(2) * scale  # [B,h,T]
+    scores = scores.masked_fill(~valid.view(B, 1, T), float("-inf"))
+    lse = torch.logsumexp(scores, dim=-1)
+    return out.numpy(), lse.numpy()
+
+
+# ----------------------------------------------------------------------------
+# [P3] section 04: the d = 1 worked example.
+def pin_d1_worked_example():
+    g = _golden("d1_worked_example.json")
+    k = np.zeros((1, 1, 4, 1), np.float32)
+    v = np.zeros((1, 1, 4, 1), np.float32)
+    k[0, 0, :2, 0] = g["k_prefill"]
+    v[0, 0, :2, 0] = g["v_prefill"]
+    kc, vc = oracle.append(np.full((1, 1, 1), g["k_new"], np.float32),
+                           np.full((1, 1, 1), g["v_new"], np.float32), k, v, [2])
+    assert kc[0, 0, :3, 0].tolist() == g["k_after_append"]
+    assert vc[0, 0, :3, 0].tolist() == g["v_after_append"]
+    out, lse = oracle.decode(np.full((1, 1, 1), g["q"], np.float32), kc, vc, [3], g["scale"])
+    tol_o = 0.5 * 10 ** (-g["output_printed_decimals"])
+    assert abs(out[0, 0, 0] - g["output_printed"]) <= tol_o, out[0, 0, 0]
+    # The softmax weights themselves: with V = identity rows, out = weights.
+    kk = np.zeros((1, 1, 3, 3), np.float32)
+    kk[0, 0, :, 0] = g["k_after_append"]
+    eye = np.eye(3, dtype=np.float32).reshape(1, 1, 3, 3)
+    qq = np.array([[[g["q"], 0.0, 0.0]]], np.float32)
+    w, _ = oracle.decode(qq, kk, eye, [3], g["scale"])
+    tol_w = 0.5 * 10 ** (-g["softmax_printed_decimals"])
+    assert np.all(np.abs(w[0, 0] - np.array(g["softmax_printed"])) <= tol_w), w[0, 0]
+    # The page's own arithmetic: o = sum(printed weight * V) = printed output.
+    assert abs(float(np.dot(g["softmax_printed"], g["v_after_append"])) - g["output_printed"]) < 1e-9
+    # lse = ln(sum exp(scores)) for the printed scores.
+    assert abs(lse[0, 0] - math.log(sum(math.exp(s) for s in g["scores_printed"]))) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Library cross-check: fp64 SDPA with enable_gqa ([P3] sections 06, 15).
+def pin_sdpa_crosscheck():
+    cases = [
+        (W.WORKLOADS["tiny_gqa_f32"], None),
+        (W.Workload("t1", B=3, h=8, g=2, d=32, dtype="bf16", T_range=(1, 70), seed=11), None),
+        (W.Workload("t2", B=2, h=6, g=6, d=8, dtype="f32", T=17, seed=12), None),
+        (W.Workload("t3", B=2, h=5, g=1, d=64, dtype="bf16", T=40, seed=13), None),
+    ]
+    for w, _ in cases:
+        x = W.make_contiguous(w)
+        L = x["seq_lens_before"]
+        out, lse = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+        sc = float(np.float32(x["scale"]))
+        ro, rl = sdpa_reference(x["q"], x["k_cache"], x["v_cache"], L, sc)
+        assert np.max(np.abs(out - ro)) < 1e-12, (w.name, np.max(np.abs(out - ro)))
+        assert np.max(np.abs(lse - rl)) < 1e-12, (w.name, np.max(np.abs(lse - rl)))
+
+
+# ----------------------------------------------------------------------------
+# [P1] section 三 3.3 and the repeat_kv helper of section 四 4.1: GQA(h, g) on
+# the cache equals MHA(h, h) on the cache with every KV head repeated m times
+# (contiguous groups), bit for bit.
+def pin_gqa_equals_mha_on_expanded_cache():
+    w = W.Workload("e", B=2, h=12, g=3, d=16, dtype="bf16", T_range=(5, 50), seed=21)
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    o1, l1 = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    m = w.h // w.g
+    ke = x["k_cache"].repeat_interleave(m, dim=1).contiguous()
+    ve = x["v_cache"].repeat_interleave(m, dim=1).contiguous()
+    o2, l2 = oracle.decode(x["q"], ke, ve, L, x["scale"])
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# [P4] section 5.1: MQA has one KV head; every query head is then a plain
+# single-head attention over that head.
+def pin_mqa_is_per_head_single_attention():
+    w = W.Workload("mq", B=2, h=4, g=1, d=8, dtype="f32", T=9, seed=22)
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    o, l = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    for i in range(w.h):
+        oi, li = oracle.decode(x["q"][:, i:i + 1].contiguous(), x["k_cache"], x["v_cache"], L,
+                               x["scale"])
+        assert np.array_equal(o[:, i], oi[:, 0]) and np.array_equal(l[:, i], li[:, 0])
+
+
+# MHA (g = h): head i reads KV head i, i.e. a plain batched single-head attention.
+def pin_mha_head_i_reads_kv_head_i():
+    w = W.Workload("mh", B=1, h=3, g=3, d=4, dtype="f32", T=6, seed=23)
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    o, _ = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    for i in range(w.h):
+        oi, _ = oracle.decode(x["q"][:, i:i + 1].contiguous(),
+                              x["k_cache"][:, i:i + 1].contiguous(),
+                              x["v_cache"][:, i:i + 1].contiguous(), L, x["scale"])
+        assert np.array_equal(o[:, i], oi[:, 0])
+
+
+# ----------------------------------------------------------------------------
+# [P4] sections 4.2-4.3: the paged layout holds the same logical cache, so the
+# result equals the contiguous one exactly.
+def pin_paged_equals_contiguous():
+    bs = 16
+    w = W.Workload("pg", B=4, h=8, g=2, d=16, dtype="bf16", T_range=(1, 60), seed=31)
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    table, nb = W.make_block_table(L, bs, perm_seed=32, extra_blocks=3)
+    kp = W.scatter_to_pool(x["k_cache"], L, table, nb, bs)
+    vp = W.scatter_to_pool(x["v_cache"], L, table, nb, bs)
+    o1, l1 = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    o2, l2 = oracle.decode(x["q"], kp, vp, L, x["scale"], block_table=table, block_size=bs)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # block size other than 16 ([P2] section 5.3 names 8 and 32 too)
+    for bs2 in (8, 32):
+        t2, nb2 = W.make_block_table(L, bs2, perm_seed=33)
+        kp2 = W.scatter_to_pool(x["k_cache"], L, t2, nb2, bs2)
+        vp2 = W.scatter_to_pool(x["v_cache"], L, t2, nb2, bs2)
+        o3, l3 = oracle.decode(x["q"], kp2, vp2, L, x["scale"], block_table=t2, block_size=bs2)
+        assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+# ----------------------------------------------------------------------------
+# [P3] section 07: decoding token by token over the cache reproduces every
+# row of a full causal forward.  The full forward is torch SDPA in fp64 with
+# is_causal=True (square, so its alignment is unambiguous).
+def pin_incremental_equals_full_causal():
+    for (N, H, G, T, d, seed) in [(2, 4, 4, 6, 4, 0), (2, 8, 2, 9, 8, 1)]:
+        gen = torch.Generator().manual_seed(seed)
+        q = torch.randn(N, H, T, d, generator=gen)
+        k = torch.randn(N, G, T, d, generator=gen)
+        v = torch.randn(N, G, T, d, generator=gen)
+        sc = float(np.float32(1.0 / math.sqrt(d)))
+        full = F.scaled_dot_product_attention(_f64(q), _f64(k), _f64(v), is_causal=True,
+                                              scale=sc, enable_gqa=True).numpy()
+        kc = np.zeros((N, G, T, d), np.float32)
+        vc = np.zeros((N, G, T, d), np.float32)
+        for t in range(T):
+            before = [t] * N
+            kc, vc = oracle.append(k[:, :, t].contiguous(), v[:, :, t].contiguous(), kc, vc, before)
+            o, _ = oracle.decode(q[:, :, t].contiguous(), kc, vc, [t + 1] * N, sc)
+            assert np.max(np.abs(o - full[:, :, t])) < 1e-12, (t, np.max(np.abs(o - full[:, :, t])))
+        # after T steps the cache holds every position ([P3] section 07 checks
+        # the cache shape (2, 4, 6, 4) for its 2 x 6 x 16 input with 4 heads)
+        assert np.array_equal(kc, k.numpy()) and np.array_equal(vc, v.numpy())
+        if (N, H, T, d) == (2, 4, 6, 4):
+            assert kc.shape == (2, 4, 6, 4)
+
+
+# ----------------------------------------------------------------------------
+# [P4] sections 2.2, 2.3, 2.5: chunked partial results merged by log-sum-exp
+# equal the unsplit result.
+def pin_split_merge_equals_unsplit():
+    w = W.Workload("sp", B=3, h=4, g=2, d=16, dtype="bf16", T_range=(0, 130), seed=41)
+    lengths = torch.tensor([0, 1, 130], dtype=torch.int32)
+    x = W.make_contiguous(w, lengths=lengths)
+    L = x["seq_lens_before"]
+    o, l = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    for chunk in (1, 2, 7, 64, 130, 1000):
+        os_, ls = oracle.decode_split(x["q"], x["k_cache"], x["v_cache"], L, x["scale"], chunk)
+        assert np.max(np.abs(os_ - o)) < 1e-13, chunk
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(ls))
+        assert np.max(np.abs(ls[fin] - l[fin])) < 1e-13, chunk
+
+
+# ----------------------------------------------------------------------------
+# Closed forms of the softmax definition ([P4] section 2.2).
+def pin_closed_forms():
+    w = W.Workload("cf", B=2, h=4, g=2, d=8, dtype="f32", T_range=(3, 40), seed=51)
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    # scale = 0: uniform weights, out = mean of the valid V rows, lse = ln L.
+    o, l = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, 0.0)
+    for b in range(w.B):
+        Lb = int(L[b])
+        for i in range(w.h):
+            j = i * w.g // w.h
+            mean = x["v_cache"][b, j, :Lb].double().mean(0).numpy()
+            assert np.max(np.abs(o[b, i] - mean)) < 1e-12
+            assert abs(l[b, i] - math.log(Lb)) < 1e-12
+    # every V row equal to one vector v: out = v whatever the scores.
+    vc = x["v_cache"].clone()
+    vrow = torch.randn(w.B, w.g, 1, w.d, generator=torch.Generator().manual_seed(52))
+    vc[:] = vrow
+    o, _ = oracle.decode(x["q"], x["k_cache"], vc, L, x["scale"])
+    for b in range(w.B):
+        for i in range(w.h):
+            assert np.max(np.abs(o[b, i] - vrow[b, i * w.g // w.h, 0].double().numpy())) < 1e-12
+    # needle: one key aligned with q at a large multiple; its weight is
+    # 1/(1 + sum_{p != n} exp(s_p - s_n)), so out is V[n] up to that bound.
+    kc = x["k_cache"].clone()
+    for b in range(w.B):
+        Lb = int(L[b])
+        n = (7 * b + 3) % Lb
+        for j in range(w.g):
+            qs = x["q"][b, j * (w.h // w.g)]
+            kc[b, j, n] = 60.0 * qs / qs.norm()
+    o, _ = oracle.decode(x["q"], kc, x["v_cache"], L, x["scale"])
+    for b in range(w.B):
+        Lb = int(L[b])
+        n = (7 * b + 3) % Lb
+        for j in range(w.g):
+            i = j * (w.h // w.g)
+            assert np.max(np.abs(o[b, i] - x["v_cache"][b, j, n].double().numpy())) < 1e-6
+
+
+# A sequence of length 0 ([P2] section 3.3 warns that one empty request can
+# corrupt a whole batch): its rows are 0 with lse = -inf and the other
+# sequences are unaffected.
+def pin_zero_length_rows():
+    w = W.Workload("z", B=3, h=4, g=2, d=8, dtype="bf16", T=10, seed=61)
+    lengths = torch.tensor([10, 0, 7], dtype=torch.int32)
+    x = W.make_contiguous(w, lengths=lengths)
+    o, l = oracle.decode(x["q"], x["k_cache"], x["v_cache"], lengths, x["scale"])
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(l[1]))
+    for b in (0, 2):
+        ob, lb = oracle.decode(x["q"][b:b + 1].contiguous(), x["k_cache"][b:b + 1].contiguous(),
+                               x["v_cache"][b:b + 1].contiguous(), lengths[b:b + 1], x["scale"])
+        assert np.array_equal(o[b], ob[0]) and np.array_equal(l[b], lb[0])
+
+
+# Positions at or beyond a sequence's length are never read ([P3] section
+# 10): poisoning them with NaN changes nothing.
+def pin_unwritten_slots_invisible():
+    w = W.Workload("u", B=2, h=4, g=2, d=8, dtype="bf16", T_range=(1, 30), seed=71)
+    x0 = W.make_contiguous(w, fill=0.0)
+    xn = W.make_contiguous(w, fill=float("nan"))
+    L = x0["seq_lens_before"]
+    o0, l0 = oracle.decode(x0["q"], x0["k_cache"], x0["v_cache"], L, x0["scale"])
+    o1, l1 = oracle.decode(xn["q"], xn["k_cache"], xn["v_cache"], L, xn["scale"])
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+# ----------------------------------------------------------------------------
+# Append ([P1] section 四 4.1 concat along the sequence axis; [P3] section 08
+# position = current cache length): exactly the target slots change.
+def pin_append_writes_only_target_slots():
+    w = W.Workload("ap", B=3, h=4, g=2, d=8, dtype="bf16", T_range=(0, 40), seed=81)
+    lengths = torch.tensor([0, 15, 40], dtype=torch.int32)
+    x = W.make_contiguous(w, lengths=lengths, t_cap=48)
+    kc, vc = oracle.append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], lengths)
+    k0 = x["k_cache"].view(torch.int16).numpy().view(np.uint16)
+    v0 = x["v_cache"].view(torch.int16).numpy().view(np.uint16)
+    kn = x["k_new"].view(torch.int16).numpy().view(np.uint16)
+    vn = x["v_new"].view(torch.int16).numpy().view(np.uint16)
+    expect_k, expect_v = k0.copy(), v0.copy()
+    for b in range(w.B):
+        expect_k[b, :, int(lengths[b])] = kn[b]
+        expect_v[b, :, int(lengths[b])] = vn[b]
+    assert np.array_equal(kc, expect_k) and np.array_equal(vc, expect_v)
+    # paged: the slot is block_table[b, pos // bs], offset pos % bs
+    bs = 16
+    table, nb = W.make_block_table(lengths + 1, bs, perm_seed=82)
+    kp = W.scatter_to_pool(x["k_cache"], lengths, table, nb, bs)
+    vp = W.scatter_to_pool(x["v_cache"], lengths, table, nb, bs)
+    kp2, vp2 = oracle.append(x["k_new"], x["v_new"], kp, vp, lengths, block_table=table)
+    ek = kp.view(torch.int16).numpy().view(np.uint16).copy()
+    ev = vp.view(torch.int16).numpy().view(np.uint16).copy()
+    for b in range(w.B):
+        pos = int(lengths[b])
+        phys = int(table[b, pos // bs])
+        ek[phys, :, pos % bs] = kn[b]
+        ev[phys, :, pos % bs] = vn[b]
+    assert np.array_equal(kp2, ek) and np.array_equal(vp2, ev)
+
+
+# ----------------------------------------------------------------------------
+# Brute force on the tiny workload: plain Python floats, one position at a
+# time, straight from softmax(q K^T scale) V.
+def pin_tiny_brute_force():
+    w = W.WORKLOADS["tiny_gqa_f32"]
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    o, l = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    q = x["q"].double().tolist()
+    K = x["k_cache"].double().tolist()
+    V = x["v_cache"].double().tolist()
+    sc = float(np.float32(x["scale"]))
+    for b in range(w.B):
+        for i in range(w.h):
+            j = i // (w.h // w.g)
+            s = [sc * sum(a * c for a, c in zip(q[b][i], K[b][j][p])) for p in range(int(L[b]))]
+            e = [math.exp(z) for z in s]
+            tot = sum(e)
+            ref = [sum(e[p] * V[b][j][p][k] for p in range(len(e))) / tot for k in range(w.d)]
+            assert max(abs(a - c) for a, c in zip(o[b, i], ref)) < 1e-12
+            assert abs(l[b, i] - math.log(tot)) < 1e-12
+
+
+# The scale enters as the float32 value the GPU receives.
+def pin_scale_is_float32_value():
+    w = W.Workload("s32", B=1, h=2, g=1, d=4, dtype="f32", T=5, seed=91)
+    x = W.make_contiguous(w)
+    L = x["seq_lens_before"]
+    o1, l1 = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, 0.1)
+    o2, l2 = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, float(np.float32(0.1)))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, l3 = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, 0.2)
+    assert not np.array_equal(l1, l3)
+
+
+ALL_PINS = [
+    pin_d1_worked_example,
+    pin_sdpa_crosscheck,
+    pin_gqa_equals_mha_on_expanded_cache,
+    pin_mqa_is_per_head_single_attention,
+    pin_mha_head_i_reads_kv_head_i,
+    pin_paged_equals_contiguous,
+    pin_incremental_equals_full_causal,
+    pin_split_merge_equals_unsplit,
+    pin_closed_forms,
+    pin_zero_length_rows,
+    pin_unwritten_slots_invisible,
+    pin_append_writes_only_target_slots,
+    pin_tiny_brute_force,
+    pin_scale_is_float32_value,
+]

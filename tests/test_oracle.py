@@ -1,0 +1,119 @@
+"""CPU-only: the fp64 oracle against its pins, the closed-form KV sizes, and
+a mutation check that every planted mistake in the oracle fails a pin."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import kvc_workloads as W
+import oracle
+import oracle_pins as P
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=[p.__name__ for p in P.ALL_PINS])
+def test_pin(pin):
+    pin()
+
+
+# ----------------------------------------------------------------------------
+# Closed-form KV cache sizes the pages print (tests/golden/kv_cache_sizes.json).
+def test_kv_cache_bytes_printed_cases():
+    with open(os.path.join(HERE, "golden", "kv_cache_sizes.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        n = oracle.kv_cache_bytes(c["layers"], c["batch"], c["kv_heads"], c["tokens"],
+                                  c["head_dim"], c["elem_bytes"])
+        assert n == c["bytes_exact"], c["citation"]
+        unit = c["printed_unit"]
+        if unit.startswith("GB (read as GiB)"):
+            assert n / 2 ** 30 == c["printed"], c["citation"]
+        else:  # bytes / (1000 * 1024^2), printed to one decimal
+            assert round(n / (1000 * 2 ** 20), 1) == c["printed"], c["citation"]
+
+
+def test_kv_cache_bytes_exercise_and_ratios():
+    # zwjcode.cn section 17 exercise: 24 layers, N=4, H=16, T=2048, d=64, fp16.
+    elems = oracle.kv_cache_bytes(24, 4, 16, 2048, 64, 1)
+    assert elems == 402_653_184
+    assert oracle.kv_cache_bytes(24, 4, 16, 2048, 64, 2) == 3 * 2 ** 28  # 0.75 GiB
+    assert oracle.kv_cache_bytes(24, 4, 4, 2048, 64, 2) * 4 == oracle.kv_cache_bytes(
+        24, 4, 16, 2048, 64, 2)
+    # limoncc.com section 三 3.3: h=64, g=8 shrinks the cache to 1/8;
+    # plumephp.com section 5.1: MQA : GQA : MHA = 1 : 8 : 64.
+    sizes = [oracle.kv_cache_bytes(80, 1, kv, 4096, 128, 2) for kv in (1, 8, 64)]
+    assert sizes[1] == 8 * sizes[0] and sizes[2] == 64 * sizes[0]
+
+
+def test_workload_caches_match_closed_form():
+    """The allocated caches of the generated workloads hold exactly
+    2 x B x g x capacity x d x elem_bytes bytes (one layer)."""
+    w = W.WORKLOADS["tiny_gqa_f32"]
+    x = W.make_contiguous(w)
+    nbytes = x["k_cache"].numel() * 4 + x["v_cache"].numel() * 4
+    assert nbytes == oracle.kv_cache_bytes(1, w.B, w.g, x["t_cap"], w.d, 4)
+    w2 = W.Workload("p", B=3, h=4, g=2, d=8, dtype="bf16", T_range=(10, 40), paged=True, seed=5)
+    xp = W.make_paged(w2)
+    nb = xp["num_blocks"]
+    assert xp["k_pool"].numel() * 2 * 2 == oracle.kv_cache_bytes(1, 1, w2.g, nb * 16, w2.d, 2)
+
+
+# ----------------------------------------------------------------------------
+# Mutation check: plant a plausible mistake in a copy of the oracle source,
+# build it, and require that at least one pin fails.
+MUTATIONS = {
+    "head_map_mod_g": ("int j = (int)(((long)i * g) / h);", "int j = (int)(i % g);"),
+    "drop_scale": ("s[p - p0] = scale * dot;", "s[p - p0] = dot;"),
+    "exp_sign": ("double w = exp(s[p - p0] - m);", "double w = exp(m - s[p - p0]);"),
+    "lse_drops_max": ("lse[bi] = m + log(l);", "lse[bi] = log(l);"),
+    "len_off_by_one": ("0, seq_lens[b], h, g, d, t_cap, scale, s, acc, &m, &l);",
+                       "0, seq_lens[b] - (seq_lens[b] > 1), h, g, d, t_cap, scale, s, acc, &m, &l);"),
+    "pv_reads_k": ("acc[k] += w * load_elem(vc, row * d + k, dtype);",
+                   "acc[k] += w * load_elem(kc, row * d + k, dtype);"),
+    "paged_offset": ("int offset = p % block_size;", "int offset = (p + 1) % block_size;"),
+    # pool read as [num_blocks, block_size, g, d] instead of [num_blocks, g, block_size, d]
+    "paged_pool_layout": ("return ((size_t)physical * g + j) * (size_t)block_size + (size_t)offset;",
+                          "return ((size_t)physical * block_size + offset) * (size_t)g + (size_t)j;"),
+    "append_pos_minus_one": ("int pos = seq_lens_before[b];",
+                             "int pos = seq_lens_before[b] > 0 ? seq_lens_before[b] - 1 : 0;"),
+    # contiguous K read as [B, g, d, t_cap] (transposed) instead of [B, g, t_cap, d]
+    "k_transposed": ("dot += load_elem(q, qbase + k, dtype) * load_elem(kc, row * d + k, dtype);",
+                     "dot += load_elem(q, qbase + k, dtype) * load_elem(kc, block_table ? row * d + k"
+                     " : (((size_t)b * g + j) * d + k) * (size_t)t_cap + p, dtype);"),
+    # q of head i read from head i + 1 (mod h): an index slip in the query operand
+    "q_head_slip": ("size_t qbase = ((size_t)b * h + i) * (size_t)d;",
+                    "size_t qbase = ((size_t)b * h + (i + 1) % h) * (size_t)d;"),
+    "split_weight_no_exp": ("double w = exp(plse[c] - M);", "double w = plse[c] - M + 1.0;"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "kvc_oracle.c")).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutant = src.replace(old, new)
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(mutant)
+    lib_path = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(lib_path), str(csrc),
+                    "-lm"], check=True)
+    saved = oracle._lib
+    oracle._lib = oracle.configure(ctypes.CDLL(str(lib_path)))
+    failed = []
+    try:
+        for pin in P.ALL_PINS:
+            try:
+                pin()
+            except (AssertionError, Exception):  # noqa: BLE001 - any failure counts
+                failed.append(pin.__name__)
+    finally:
+        oracle._lib = saved
+    assert failed, f"no pin caught the planted mistake {name}"
