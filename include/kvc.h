@@ -1,0 +1,171 @@
+/*
+ * kvc.h -- C ABI of libkvc: single-token decode attention over a KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of causal self-attention for a batch of sequences:
+ *   1. kvc_append writes the new token's K and V of every (sequence, KV head)
+ *      into the cache at position seq_lens_before[b];
+ *   2. kvc_decode_attention / kvc_decode_attention_paged compute, for every
+ *      sequence b and query head i, with KV head j = floor(i * g / h),
+ *        out[b,i,:] = softmax(scale * q[b,i,:] . K[b,j,p,:]) V[b,j,p,:]
+ *      over positions p < seq_lens[b], and lse[b,i] = ln sum_p exp(score_p).
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [P1] "大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com): section 二
+ *        (cache K_t, V_t and append them each step), section 三 3.1-3.3 (MHA,
+ *        MQA, GQA; head map j = floor(i/m) = floor(i*g/h) with m = h/g
+ *        consecutive query heads per group), section 四 4.1 (concatenate the
+ *        new K/V after the past cache along the sequence axis, then scaled
+ *        dot-product attention; h must be divisible by g).
+ *   [P2] "从KV cache共享到批量调度：注意力机制下的隔离问题与口令实验"
+ *        (0539edu.com): section 2.1 (scale 1/sqrt(d_k)), section 3.1 (paged
+ *        blocks; the block table lives on the GPU and the kernel computes
+ *        addresses itself), section 3.3 (variable lengths; a length-0 entry
+ *        must not corrupt the batch).
+ *   [P3] "每生成一个词为何又重算全文？KV Cache 的增量解码" (zwjcode.cn):
+ *        section 02 (per-step shapes q [N,H,1,d], cache [N,H,t,d]), section
+ *        08 (the new token's position is the current cache length), section
+ *        10 (preallocated static cache; unwritten slots are invisible).
+ *   [P4] "KV Cache 优化与注意力机制加速：FlashAttention / PagedAttention"
+ *        (plumephp.com): section 2.2-2.3 (online softmax statistics m, l and
+ *        the log-sum-exp L = m + log l returned with O), section 2.5
+ *        (parallelism over the sequence dimension), section 4.2-4.3 (block
+ *        of 16 tokens, block table, logical block = pos / block_size,
+ *        offset = pos % block_size).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing and keeps no state besides a cached device
+ *     property query.  Outputs must not alias inputs.
+ *   - Every launch is asynchronous on the caller's `stream`; no entry point
+ *     synchronises the host.  Validation of the host-side arguments happens
+ *     before any HIP call and needs no GPU.
+ *   - dtype: KVC_F32 or KVC_BF16, shared by q, the caches and k/v_new.
+ *     out and lse are always float32.
+ *   - Device-side integers (seq_lens, block_table) are trusted.  They are
+ *     clamped inside the kernels so that a bad value cannot fault the GPU:
+ *     lengths to [0, capacity], physical block ids to [0, num_blocks).  A
+ *     clamped value gives unspecified (but in-bounds) results.
+ *   - Return value: a kvc_status.  No C++ exception crosses the ABI.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_INVALID = 1,      /* null pointer, non-positive size, h % g != 0, bad block size */
+    KVC_ERR_UNSUPPORTED = 2,  /* dtype or head_dim not built (head_dim must be 1..256) */
+    KVC_ERR_WORKSPACE = 3,    /* workspace missing or smaller than kvc_decode_workspace_bytes */
+    KVC_ERR_HIP = 4           /* a HIP launch reported an error */
+} kvc_status;
+
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int kvc_version(void);
+
+/* Human-readable text of a kvc_status value (static string). */
+const char* kvc_status_string(int status);
+
+/*
+ * kvc_append -- write the new token's K/V into the cache ([P1] 二 and 四 4.1
+ * concat; [P3] section 08 position = current length; [P4] 4.3 block lookup).
+ *
+ *   k_new, v_new      [B, g, d] of dtype
+ *   k_cache, v_cache  contiguous [B, g, capacity, d] when block_table == NULL;
+ *                     else pools [capacity, g, block_size, d] (capacity = number
+ *                     of physical blocks)
+ *   block_table       NULL, or device int32 [B, max_blocks]: physical block id
+ *                     of each logical block of each sequence
+ *   seq_lens_before   device int32 [B]: cache length before this step = the
+ *                     slot written.  Not modified.
+ *   For every b < B and j < g: with pos = seq_lens_before[b], the d elements
+ *   of k_new[b,j,:] are copied byte-exactly to K[b, j, pos, :] (contiguous), or
+ *   to pool[block_table[b, pos / block_size], j, pos % block_size, :] (paged),
+ *   and likewise for V.  Nothing else is written.  Positions outside the
+ *   capacity (pos < 0, pos >= capacity, logical block >= max_blocks, or a
+ *   negative / out-of-range physical id) are skipped.
+ *   The caller makes sure that the target block is allocated and private to
+ *   the sequence (copy-on-write is the caller's policy).
+ */
+int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+               const int32_t* block_table, int max_blocks, int block_size,
+               const int32_t* seq_lens_before, int B, int g, int d, int capacity,
+               int dtype, hipStream_t stream);
+
+/*
+ * Work split.  A sequence's positions are cut into chunks of chunk_len
+ * positions; each (sequence, KV head, chunk) is one work-group that serves
+ * all m = h/g query heads of the group, so every K/V byte is read once.
+ * When more than one chunk exists, partial (O, lse) results go to the
+ * workspace and a second kernel merges them by log-sum-exp ([P4] 2.2-2.5).
+ * num_splits = 0 lets the library choose; num_splits > 0 asks for that many
+ * chunks over max_seq_len (chunk_len is rounded up to a multiple of 32, so
+ * the count can come out slightly lower).
+ *
+ * kvc_decode_plan writes the chosen chunk_len and number of chunks.
+ * kvc_decode_workspace_bytes returns the workspace the decode call needs for
+ * the same arguments (0 when the plan has one chunk).  max_seq_len is t_cap
+ * for the contiguous entry point and max_blocks * block_size for the paged
+ * one.  Both are pure host arithmetic.
+ */
+int kvc_decode_plan(int B, int h, int g, int d, int max_seq_len, int num_splits,
+                    int* chunk_len, int* num_chunks);
+size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int max_seq_len, int num_splits);
+
+/*
+ * kvc_decode_attention -- decode attention over a contiguous cache.
+ *
+ *   q            [B, h, d] of dtype: one query per sequence and head
+ *   k_cache      [B, g, t_cap, d] of dtype
+ *   v_cache      [B, g, t_cap, d] of dtype
+ *   seq_lens     device int32 [B]: number of attended positions (after the
+ *                append), 0..t_cap.  Positions >= seq_lens[b] are never read.
+ *   B, h, g, d   batch, query heads, KV heads (h % g == 0), head dim
+ *   scale        multiplies every q.k (usually 1/sqrt(d))
+ *   num_splits   see "Work split"
+ *   workspace    device buffer of at least kvc_decode_workspace_bytes(B, h, g,
+ *                d, t_cap, num_splits) bytes (may be NULL when that is 0)
+ *   out          [B, h, d] float32; lse [B, h] float32 (natural log).
+ *   A sequence of length 0 gets out = 0 and lse = -inf.
+ */
+int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
+                         float scale, int dtype, int num_splits,
+                         void* workspace, size_t workspace_bytes,
+                         float* out, float* lse, hipStream_t stream);
+
+/*
+ * kvc_decode_attention_paged -- decode attention over a paged cache.
+ *
+ *   k_pool, v_pool  [num_blocks, g, block_size, d] of dtype: physical blocks
+ *   block_table     device int32 [B, max_blocks]; entry (b, n) is the
+ *                   physical block holding positions [n*block_size,
+ *                   (n+1)*block_size) of sequence b.  Entries past the last
+ *                   block a sequence uses are never read.
+ *   block_size      power of two, 8..256
+ *   seq_lens        device int32 [B], 0..max_blocks*block_size
+ *   other arguments as kvc_decode_attention; the workspace size uses
+ *   max_seq_len = max_blocks * block_size.
+ */
+int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, int max_blocks, int block_size,
+                               int num_blocks, const int32_t* seq_lens,
+                               int B, int h, int g, int d, float scale, int dtype,
+                               int num_splits, void* workspace, size_t workspace_bytes,
+                               float* out, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

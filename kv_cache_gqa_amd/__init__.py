@@ -1,0 +1,194 @@
+"""kv_cache_gqa_amd -- single-token decode attention over a KV cache on AMD
+MI355X (gfx950).
+
+A thin ctypes binding over ``libkvc.so`` (the C ABI in ``include/kvc.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor properties and passes device pointers, sizes and the
+current HIP stream.  PyTorch provides device memory and streams.
+
+    append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None)
+    out, lse = decode(q, k_cache, v_cache, seq_lens, scale=None, num_splits=0)
+    out, lse = decode_paged(q, k_pool, v_pool, block_table, seq_lens, ...)
+
+There is no CPU fallback: without the built library (``python -m
+kv_cache_gqa_amd.build``) or without a GPU every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["append", "decode", "decode_paged", "plan", "workspace_bytes", "KvcError",
+           "load_library", "LIB_PATH", "F32", "BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
+F32, BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype or shape",
+           3: "workspace missing or too small", 4: "HIP launch error"}
+
+_lib = None
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, 'unknown')} (status {status})")
+        self.status = status
+
+
+def load_library():
+    """Load libkvc.so and declare its C signatures.  Raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m kv_cache_gqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ip, fp, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kvc_version.argtypes = []
+    lib.kvc_version.restype = ip
+    lib.kvc_status_string.argtypes = [ip]
+    lib.kvc_status_string.restype = ctypes.c_char_p
+    lib.kvc_append.argtypes = [vp, vp, vp, vp, vp, ip, ip, vp, ip, ip, ip, ip, ip, vp]
+    lib.kvc_append.restype = ip
+    lib.kvc_decode_plan.argtypes = [ip, ip, ip, ip, ip, ip, ctypes.POINTER(ip), ctypes.POINTER(ip)]
+    lib.kvc_decode_plan.restype = ip
+    lib.kvc_decode_workspace_bytes.argtypes = [ip, ip, ip, ip, ip, ip]
+    lib.kvc_decode_workspace_bytes.restype = sz
+    lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
+                                         vp, vp, vp]
+    lib.kvc_decode_attention.restype = ip
+    lib.kvc_decode_attention_paged.argtypes = [vp, vp, vp, vp, ip, ip, ip, vp, ip, ip, ip, ip, fp,
+                                               ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_paged.restype = ip
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KvcError(fn, status)
+
+
+def plan(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0) -> Tuple[int, int]:
+    """(chunk_len, num_chunks) the library uses for these arguments."""
+    lib = load_library()
+    cl, nc = ctypes.c_int(0), ctypes.c_int(0)
+    _check("kvc_decode_plan", lib.kvc_decode_plan(B, h, g, d, max_seq_len, num_splits,
+                                                  ctypes.byref(cl), ctypes.byref(nc)))
+    return cl.value, nc.value
+
+
+def workspace_bytes(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0) -> int:
+    return int(load_library().kvc_decode_workspace_bytes(B, h, g, d, max_seq_len, num_splits))
+
+
+def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, stream=None):
+    """Write k_new/v_new [B,g,d] at position seq_lens_before[b] of each
+    sequence's cache: contiguous [B,g,T,d], or pools [NB,g,bs,d] through
+    block_table [B,max_blocks].  In place; seq_lens_before is not changed."""
+    lib = load_library()
+    dt = _dtype_code(k_cache)
+    B, g, d = k_new.shape
+    if block_table is None:
+        capacity, mb, bs, bt = k_cache.shape[2], 0, 0, None
+    else:
+        capacity, bs, mb = k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
+        bt = _dev(block_table, "block_table", torch.int32)
+    st = lib.kvc_append(_dev(k_new, "k_new", k_cache.dtype), _dev(v_new, "v_new", k_cache.dtype),
+                        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
+                        bt, mb, bs, _dev(seq_lens_before, "seq_lens_before", torch.int32),
+                        B, g, d, capacity, dt, _stream(stream))
+    _check("kvc_append", st)
+
+
+def _outputs(q, out, lse):
+    B, h, d = q.shape
+    if out is None:
+        out = torch.empty((B, h, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def _workspace(nbytes: int, q: torch.Tensor, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, num_splits: int = 0,
+           workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
+    """Decode attention over a contiguous cache.
+
+    q [B,h,d]; k_cache, v_cache [B,g,t_cap,d]; seq_lens int32 [B] (attended
+    lengths).  Returns (out [B,h,d] float32, lse [B,h] float32)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, d = q.shape
+    _, g, t_cap, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, t_cap, num_splits), q, workspace)
+    st = lib.kvc_decode_attention(
+        _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(seq_lens, "seq_lens", torch.int32), B, h, g, d, t_cap, float(scale), dt, num_splits,
+        ws.data_ptr() if ws is not None else None, wsb,
+        _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+    _check("kvc_decode_attention", st)
+    return out, lse
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float] = None,
+                 num_splits: int = 0, workspace: Optional[torch.Tensor] = None, out=None, lse=None,
+                 stream=None):
+    """Decode attention over a paged cache: pools [NB,g,bs,d], block_table
+    int32 [B,max_blocks], seq_lens int32 [B].  Returns (out, lse)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, d = q.shape
+    nb, g, bs, _ = k_pool.shape
+    mb = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, mb * bs, num_splits), q,
+                         workspace)
+    st = lib.kvc_decode_attention_paged(
+        _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype), _dev(v_pool, "v_pool", q.dtype),
+        _dev(block_table, "block_table", torch.int32), mb, bs, nb,
+        _dev(seq_lens, "seq_lens", torch.int32), B, h, g, d, float(scale), dt, num_splits,
+        ws.data_ptr() if ws is not None else None, wsb,
+        _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+    _check("kvc_decode_attention_paged", st)
+    return out, lse

@@ -1,0 +1,80 @@
+// append.hip -- write the new token's K/V into the cache.
+//
+// Follows "大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com) section
+// 四 4.1 (the new K/V go after the past cache along the sequence axis) and
+// "KV Cache 的增量解码" (zwjcode.cn) section 08 (the new position equals the
+// current cache length) and section 10 (preallocated cache written in place).
+// Paged placement follows "KV Cache 优化与注意力机制加速" (plumephp.com)
+// section 4.3: physical block = table[b, pos / block_size], offset
+// pos % block_size.
+//
+// One thread moves one vector of W bytes (16, 4 or 2 depending on the row
+// size) of one (tensor, sequence, KV head); the copy is bit-exact.
+#include "kvc_device.h"
+
+namespace kvc {
+
+template <typename V>
+__global__ void __launch_bounds__(256) append_kernel(
+    const V* __restrict__ k_new, const V* __restrict__ v_new, V* __restrict__ k_cache,
+    V* __restrict__ v_cache, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, const int32_t* __restrict__ seq_lens, int B, int g, int vec_per_row,
+    int capacity) {
+    const long total = (long)B * g * vec_per_row;
+    long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool is_v = t >= total;
+    if (is_v) t -= total;
+    if (t >= total) return;
+    const int vec = (int)(t % vec_per_row);
+    const long bj = t / vec_per_row;
+    const int b = (int)(bj / g);
+    const int j = (int)(bj % g);
+    const int pos = seq_lens[b];
+    long row;
+    if (block_table == nullptr) {
+        if (pos < 0 || pos >= capacity) return;
+        row = bj * (long)capacity + pos;
+    } else {
+        if (pos < 0) return;
+        const int logical = pos / block_size;
+        if (logical >= max_blocks) return;
+        const int phys = block_table[(long)b * max_blocks + logical];
+        if (phys < 0 || phys >= capacity) return;
+        row = ((long)phys * g + j) * block_size + (pos % block_size);
+    }
+    const V* src = is_v ? v_new : k_new;
+    V* dst = is_v ? v_cache : k_cache;
+    dst[row * vec_per_row + vec] = src[bj * vec_per_row + vec];
+}
+
+hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* block_table, int max_blocks, int block_size,
+                         const int32_t* seq_lens_before, int B, int g, int d, int capacity,
+                         int elem_bytes, hipStream_t s) {
+    const long row_bytes = (long)d * elem_bytes;
+    const int threads = 256;
+    if (row_bytes % 16 == 0) {
+        const int vpr = (int)(row_bytes / 16);
+        const long n = 2L * B * g * vpr;
+        append_kernel<uint4><<<dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s>>>(
+            (const uint4*)k_new, (const uint4*)v_new, (uint4*)k_cache, (uint4*)v_cache,
+            block_table, max_blocks, block_size, seq_lens_before, B, g, vpr, capacity);
+    } else if (row_bytes % 4 == 0) {
+        const int vpr = (int)(row_bytes / 4);
+        const long n = 2L * B * g * vpr;
+        append_kernel<uint32_t><<<dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s>>>(
+            (const uint32_t*)k_new, (const uint32_t*)v_new, (uint32_t*)k_cache,
+            (uint32_t*)v_cache, block_table, max_blocks, block_size, seq_lens_before, B, g, vpr,
+            capacity);
+    } else {
+        const int vpr = (int)(row_bytes / 2);
+        const long n = 2L * B * g * vpr;
+        append_kernel<uint16_t><<<dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s>>>(
+            (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
+            (uint16_t*)v_cache, block_table, max_blocks, block_size, seq_lens_before, B, g, vpr,
+            capacity);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvc

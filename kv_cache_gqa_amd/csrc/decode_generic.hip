@@ -1,0 +1,117 @@
+// decode_generic.hip -- decode attention for any head_dim <= 256, float32 or
+// bf16, any group size, contiguous or paged.  The path for shapes the
+// specialised bf16/d=128 kernels do not cover (the fp32 d=16 workload, the
+// d=1 worked example).
+//
+// One wavefront per (chunk, query head, sequence).  Lane k holds dims k,
+// k+64, k+128, k+192.  Positions are visited one at a time: the partial dot
+// products are summed across the wave, then the online-softmax update of
+// "KV Cache 优化与注意力机制加速" (plumephp.com) section 2.2 is applied:
+// m' = max(m, s), l' = l exp(m - m') + exp(s - m'), acc' = acc exp(m - m') +
+// exp(s - m') V_p, all in base 2.  Query head i reads KV head
+// floor(i*g/h) ("大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com),
+// section 三 3.3).
+#include "kvc_device.h"
+
+namespace kvc {
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p, long idx);
+template <>
+__device__ __forceinline__ float load_f<float>(const float* p, long idx) { return p[idx]; }
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, long idx) {
+    return __uint_as_float((uint32_t)p[idx] << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row16_sum(x);
+    x += shfl_xor_f(x, 16);
+    x += shfl_xor_f(x, 32);
+    return x;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
+    const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int d = a.d;
+    const int j = (int)(((long)i * a.g) / a.h);
+    const int L = clamp_len(a.seq_lens[b], a.cap_len);
+    const int p0 = c * a.chunk_len;
+    const int p1 = min(p0 + a.chunk_len, L);
+    const bool single = a.num_chunks == 1;
+    if (p0 >= L && !single) return;  // chunk past the end: the merge skips it
+
+    const T* q = (const T*)a.q;
+    const T* K = (const T*)a.k;
+    const T* V = (const T*)a.v;
+    float qv[4], acc[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int dim = lane + 64 * kk;
+        qv[kk] = dim < d ? load_f(q, ((long)b * a.h + i) * d + dim) * a.scale_log2e : 0.0f;
+        acc[kk] = 0.0f;
+    }
+    float m = kNegInf, l = 0.0f;
+    const long contig_base = ((long)b * a.g + j) * a.t_cap;
+    for (int p = p0; p < p1; ++p) {
+        long row;
+        if (a.block_table != nullptr) {
+            int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+            phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+            row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+        } else {
+            row = contig_base + p;
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int dim = lane + 64 * kk;
+            if (dim < d) part += qv[kk] * load_f(K, row * d + dim);
+        }
+        const float s = wave_sum(part);
+        const float mnew = fmaxf(m, s);
+        const float alpha = fast_exp2(m - mnew);  // m = -inf on the first position -> 0
+        const float pw = fast_exp2(s - mnew);
+        l = l * alpha + pw;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int dim = lane + 64 * kk;
+            if (dim < d) acc[kk] = acc[kk] * alpha + pw * load_f(V, row * d + dim);
+        }
+        m = mnew;
+    }
+
+    const long row_out = (long)b * a.h + i;
+    if (single) {
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int dim = lane + 64 * kk;
+            if (dim < d) a.out[row_out * d + dim] = acc[kk] * inv;
+        }
+        if (lane == 0) a.lse[row_out] = l > 0.0f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+    } else {
+        const long prow = row_out * a.num_chunks + c;
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int dim = lane + 64 * kk;
+            if (dim < d) a.part_o[prow * d + dim] = acc[kk] * inv;
+        }
+        if (lane == 0) a.part_lse[prow] = m + fast_log2(l);
+    }
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s) {
+    dim3 grid((unsigned)a.num_chunks, (unsigned)a.h, (unsigned)a.B);
+    if (dtype == 0) {
+        decode_generic_kernel<float><<<grid, dim3(64), 0, s>>>(a);
+    } else {
+        decode_generic_kernel<uint16_t><<<grid, dim3(64), 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvc

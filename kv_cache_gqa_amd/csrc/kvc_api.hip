@@ -1,0 +1,193 @@
+// kvc_api.hip -- the C ABI of libkvc (declared in include/kvc.h): argument
+// validation, work-split planning and kernel selection.  Validation runs
+// before any HIP call; every launch goes to the caller's stream.
+#include "kvc.h"
+
+#include <math.h>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+static long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
+    if (max_seq_len <= 0) return Plan{kTileTokens, 1};
+    long C;
+    if (num_splits > 0) {
+        C = num_splits;
+    } else {
+        const long units = (long)B * g;
+        C = ceil_div(kTargetWorkgroups, units > 0 ? units : 1);
+        const long by_len = ceil_div(max_seq_len, kMinAutoChunk);
+        if (C > by_len) C = by_len;
+        if (C < 1) C = 1;
+    }
+    long chunk = ceil_div(max_seq_len, C);
+    chunk = ceil_div(chunk, kTileTokens) * kTileTokens;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    if (chunk < kTileTokens) chunk = kTileTokens;
+    return Plan{(int)chunk, (int)ceil_div(max_seq_len, chunk)};
+}
+
+KernelKind choose_kernel(int dtype, int d, int m) {
+    if (dtype == KVC_BF16 && d == 128) {
+        if (m <= 3) return kValu;
+        if (m <= 32) return kMfma;
+    }
+    return kGeneric;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static size_t workspace_for(int B, int h, int d, const Plan& p) {
+    if (p.num_chunks <= 1) return 0;
+    const size_t rows = (size_t)B * h * p.num_chunks;
+    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+static int ilog2_exact(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return (1 << l) == x ? l : -1;
+}
+
+static int check_common(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                        int B, int h, int g, int d, float scale, int dtype, int num_splits,
+                        const float* out, const float* lse) {
+    if (B < 0 || h <= 0 || g <= 0 || d <= 0 || num_splits < 0) return KVC_ERR_INVALID;
+    if (h % g != 0) return KVC_ERR_INVALID;
+    if (!isfinite(scale)) return KVC_ERR_INVALID;
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+    if (d > 256) return KVC_ERR_UNSUPPORTED;
+    if (B > 0 && (!q || !k || !v || !seq_lens || !out || !lse)) return KVC_ERR_INVALID;
+    if (B > 65535 || g > 65535) return KVC_ERR_UNSUPPORTED;
+    return KVC_OK;
+}
+
+static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    const Plan plan = make_plan(a.B, a.g, max_len, num_splits);
+    a.chunk_len = plan.chunk_len;
+    a.num_chunks = plan.num_chunks;
+    const size_t need = workspace_for(a.B, a.h, a.d, plan);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
+        const size_t rows = (size_t)a.B * a.h * plan.num_chunks;
+        a.part_o = static_cast<float*>(workspace);
+        a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              align256(rows * a.d * sizeof(float)));
+    } else {
+        a.part_o = nullptr;
+        a.part_lse = nullptr;
+    }
+    if (a.B == 0) return KVC_OK;
+    hipError_t err;
+    switch (choose_kernel(dtype, a.d, a.m)) {
+        case kValu: err = launch_decode_valu_bf16_d128(a, stream); break;
+        case kMfma: err = launch_decode_mfma_bf16_d128(a, stream); break;
+        default: err = launch_decode_generic(a, dtype, stream); break;
+    }
+    if (err != hipSuccess) return KVC_ERR_HIP;
+    if (plan.num_chunks > 1) {
+        if (launch_merge(a, stream) != hipSuccess) return KVC_ERR_HIP;
+    }
+    return KVC_OK;
+}
+
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" {
+
+int kvc_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* kvc_status_string(int status) {
+    switch (status) {
+        case KVC_OK: return "ok";
+        case KVC_ERR_INVALID: return "invalid argument";
+        case KVC_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+        case KVC_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVC_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int kvc_decode_plan(int B, int h, int g, int d, int max_seq_len, int num_splits,
+                    int* chunk_len, int* num_chunks) {
+    if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < 0 || max_seq_len < 0)
+        return KVC_ERR_INVALID;
+    const Plan p = make_plan(B, g, max_seq_len, num_splits);
+    if (chunk_len) *chunk_len = p.chunk_len;
+    if (num_chunks) *num_chunks = p.num_chunks;
+    return KVC_OK;
+}
+
+size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int max_seq_len, int num_splits) {
+    if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < 0 || max_seq_len < 0)
+        return 0;
+    return workspace_for(B, h, d, make_plan(B, g, max_seq_len, num_splits));
+}
+
+int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+               const int32_t* block_table, int max_blocks, int block_size,
+               const int32_t* seq_lens_before, int B, int g, int d, int capacity, int dtype,
+               hipStream_t stream) {
+    if (B < 0 || g <= 0 || d <= 0 || capacity <= 0) return KVC_ERR_INVALID;
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+    if (B == 0) return KVC_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens_before) return KVC_ERR_INVALID;
+    if (block_table != nullptr && (max_blocks <= 0 || block_size <= 0)) return KVC_ERR_INVALID;
+    const int eb = dtype == KVC_F32 ? 4 : 2;
+    if (launch_append(k_new, v_new, k_cache, v_cache, block_table, max_blocks, block_size,
+                      seq_lens_before, B, g, d, capacity, eb, stream) != hipSuccess)
+        return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
+int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
+                         float scale, int dtype, int num_splits, void* workspace,
+                         size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+    int st = check_common(q, k_cache, v_cache, seq_lens, B, h, g, d, scale, dtype, num_splits,
+                          out, lse);
+    if (st != KVC_OK) return st;
+    if (t_cap <= 0) return KVC_ERR_INVALID;
+    DecodeArgs a{};
+    a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens;
+    a.block_table = nullptr; a.max_blocks = 0; a.block_size = 1; a.log2_bs = 0; a.num_blocks = 0;
+    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g;
+    a.t_cap = t_cap; a.cap_len = t_cap;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.out = out; a.lse = lse;
+    return run_decode(a, dtype, t_cap, num_splits, workspace, workspace_bytes, stream);
+}
+
+int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, int max_blocks, int block_size,
+                               int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                               int d, float scale, int dtype, int num_splits, void* workspace,
+                               size_t workspace_bytes, float* out, float* lse,
+                               hipStream_t stream) {
+    int st = check_common(q, k_pool, v_pool, seq_lens, B, h, g, d, scale, dtype, num_splits,
+                          out, lse);
+    if (st != KVC_OK) return st;
+    if (max_blocks <= 0 || num_blocks <= 0) return KVC_ERR_INVALID;
+    if (B > 0 && block_table == nullptr) return KVC_ERR_INVALID;
+    const int lg = ilog2_exact(block_size);
+    if (block_size < 8 || block_size > 256 || lg < 0) return KVC_ERR_INVALID;
+    const long cap = (long)max_blocks * block_size;
+    if (cap > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;
+    DecodeArgs a{};
+    a.q = q; a.k = k_pool; a.v = v_pool; a.seq_lens = seq_lens;
+    a.block_table = block_table; a.max_blocks = max_blocks; a.block_size = block_size;
+    a.log2_bs = lg; a.num_blocks = num_blocks;
+    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g;
+    a.t_cap = 0; a.cap_len = (int)cap;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.out = out; a.lse = lse;
+    return run_decode(a, dtype, (int)cap, num_splits, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// kvc_device.h -- device-side helpers shared by the libkvc kernels (gfx950,
+// wave64).  Scores are kept in base 2: s2 = (scale * log2 e) * q.k, so that
+// exp(s - m) = exp2(s2 - m2) maps onto v_exp_f32 directly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 pair (little-endian: element 2k in the low half) to two floats.  A
+// bf16 value is the high half of the float with the same value.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16 bits (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane moves inside a row of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    x += dpp_f<kDppMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+// 16-byte global load through the vector memory path.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// Merge two online-softmax states (m2, l, acc) in base 2.  -inf maxima
+// (no positions seen) are handled so that no (-inf) - (-inf) is formed.
+__device__ __forceinline__ void rescale_pair(float ma, float mb, float& fa, float& fb, float& mnew) {
+    mnew = fmaxf(ma, mb);
+    float ref = (mnew == kNegInf) ? 0.0f : mnew;
+    fa = fast_exp2(ma - ref);
+    fb = fast_exp2(mb - ref);
+}
+
+// Clamp a device-side length to [0, cap].
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+}  // namespace kvc

@@ -1,0 +1,69 @@
+// kvc_internal.h -- host-side declarations shared by the launch code of
+// libkvc.  Not part of the public ABI (that is include/kvc.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// Positions per sub-tile: the unit every decode kernel walks the cache in.
+constexpr int kTileTokens = 32;
+// Upper bound on one chunk: keeps a chunk's slice of the block table
+// (chunk_len / block_size + 2 entries for block_size >= 8) inside LDS.
+constexpr int kMaxChunk = 4096;
+constexpr int kMaxTableSlice = kMaxChunk / 8 + 2;
+// Auto split: aim for about this many work-groups per launch, but never
+// chunks shorter than kMinAutoChunk positions.
+constexpr int kTargetWorkgroups = 2048;
+constexpr int kMinAutoChunk = 256;
+
+struct Plan {
+    int chunk_len;   // positions per chunk (multiple of kTileTokens)
+    int num_chunks;  // chunks over max_seq_len (>= 1)
+};
+
+Plan make_plan(int B, int g, int max_seq_len, int num_splits);
+
+// Everything one decode launch needs.  Layout facts:
+//   q [B,h,d]; contiguous K/V [B,g,t_cap,d]; paged pools [nblk,g,bs,d];
+//   block_table [B,max_blocks]; out [B,h,d] f32; lse [B,h] f32;
+//   partial O [B,h,C,d] f32 and partial lse2 [B,h,C] f32 in the workspace.
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* seq_lens;
+    const int32_t* block_table;  // nullptr => contiguous
+    int max_blocks;
+    int block_size;
+    int log2_bs;
+    int num_blocks;
+    int B, h, g, d, m;
+    int t_cap;        // contiguous capacity in positions
+    int cap_len;      // clamp bound for seq_lens: t_cap or max_blocks*block_size
+    float scale_log2e;  // scale * log2(e): scores are kept in base 2
+    int chunk_len;
+    int num_chunks;
+    float* part_o;    // [B,h,C,d] (C > 1 only)
+    float* part_lse;  // [B,h,C]   base-2 log-sum-exp of each chunk
+    float* out;
+    float* lse;
+};
+
+// Kernel families.  Each returns hipGetLastError() after its launch.
+hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* block_table, int max_blocks, int block_size,
+                         const int32_t* seq_lens_before, int B, int g, int d, int capacity,
+                         int elem_bytes, hipStream_t s);
+
+// Which decode kernel a configuration uses (exposed for tests and tools).
+enum KernelKind { kGeneric = 0, kValu = 1, kMfma = 2 };
+KernelKind choose_kernel(int dtype, int d, int m);
+
+}  // namespace kvc

@@ -1,0 +1,134 @@
+"""Host-only checks of libkvc: the library loads, exports every function
+include/kvc.h declares, plans work splits as documented, and rejects bad
+arguments with the documented status before touching the GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_gqa_amd as kvc
+import kvc_workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvc.LIB_PATH),
+                                reason="libkvc.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kvc_append", "kvc_decode_attention", "kvc_decode_attention_paged",
+              "kvc_decode_workspace_bytes", "kvc_decode_plan", "kvc_status_string", "kvc_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvc.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = kvc.load_library()
+    assert lib.kvc_status_string(0) == b"ok"
+    assert lib.kvc_status_string(3).startswith(b"workspace")
+    assert lib.kvc_version() > 0
+
+
+def test_plan_auto_and_explicit():
+    # explicit 64 splits over 131073 positions: chunks of 2080 (a multiple of 32)
+    assert kvc.plan(4, 32, 1, 128, 131073 + 15, 64) == (2080, 64)
+    # one chunk when splitting is not asked for and the grid is already large
+    cl, nc = kvc.plan(1024, 8, 8, 128, 512, 0)
+    assert nc == 1 and cl == 512
+    # auto: every chunk is a multiple of 32, covers max_seq_len, and <= 4096
+    for (B, h, g, T) in [(8, 32, 32, 2064), (32, 64, 8, 4112), (64, 32, 8, 8208), (4, 32, 1, 131088),
+                         (1, 4, 2, 48)]:
+        cl, nc = kvc.plan(B, h, g, 128, T, 0)
+        assert cl % 32 == 0 and cl * nc >= T and cl * (nc - 1) < T and cl <= 4096
+
+
+def test_workspace_bytes():
+    assert kvc.workspace_bytes(1, 4, 2, 16, 48, 1) == 0
+    cl, nc = kvc.plan(4, 32, 1, 128, 131088, 64)
+    rows = 4 * 32 * nc
+    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert kvc.workspace_bytes(4, 32, 1, 128, 131088, 64) == expect
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, B=2, h=8, g=2, d=128, t_cap=64, scale=0.1, dtype=1,
+             splits=1, ws=None, wsb=0, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.kvc_decode_attention(a["q"], a["k"], a["v"], a["sl"], a["B"], a["h"], a["g"], a["d"],
+                                    a["t_cap"], a["scale"], a["dtype"], a["splits"], a["ws"],
+                                    a["wsb"], a["out"], a["lse"], None)
+
+
+def test_decode_validation_codes():
+    lib = kvc.load_library()
+    assert _decode(lib, h=8, g=3) == INVALID             # h % g != 0
+    assert _decode(lib, g=0) == INVALID
+    assert _decode(lib, d=0) == INVALID
+    assert _decode(lib, q=None) == INVALID                # null pointer
+    assert _decode(lib, out=None) == INVALID
+    assert _decode(lib, t_cap=0) == INVALID
+    assert _decode(lib, scale=float("inf")) == INVALID
+    assert _decode(lib, splits=-1) == INVALID
+    assert _decode(lib, d=300) == UNSUPPORTED
+    assert _decode(lib, dtype=7) == UNSUPPORTED
+    assert _decode(lib, splits=2, ws=None, wsb=0) == WORKSPACE   # plan needs a workspace
+    need = lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 64, 2)
+    assert need > 0
+    assert _decode(lib, splits=2, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert _decode(lib, B=0) == OK                        # nothing to do, nothing launched
+
+
+def test_paged_validation_codes():
+    lib = kvc.load_library()
+
+    def call(**kw):
+        a = dict(bt=FAKE, mb=8, bs=16, nb=10, B=2, h=8, g=2, d=128, splits=1)
+        a.update(kw)
+        return lib.kvc_decode_attention_paged(FAKE, FAKE, FAKE, a["bt"], a["mb"], a["bs"], a["nb"],
+                                              FAKE, a["B"], a["h"], a["g"], a["d"], 0.1, 1,
+                                              a["splits"], None, 0, FAKE, FAKE, None)
+    assert call(bt=None) == INVALID
+    assert call(bs=12) == INVALID      # not a power of two
+    assert call(bs=4) == INVALID       # below 8
+    assert call(bs=512) == INVALID     # above 256
+    assert call(mb=0) == INVALID
+    assert call(nb=0) == INVALID
+    assert call(h=6, g=4) == INVALID
+    assert call(splits=2) == WORKSPACE
+
+
+def test_append_validation_codes():
+    lib = kvc.load_library()
+    f = lib.kvc_append
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 2, 0, 128, 64, 1, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 2, 2, 128, 0, 1, None) == INVALID
+    assert f(None, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 2, 2, 128, 64, 1, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16, FAKE, 2, 2, 128, 64, 1, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 2, 2, 128, 64, 9, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 0, 2, 128, 64, 1, None) == OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    w = W.WORKLOADS["tiny_gqa_f32"]
+    x = W.make_contiguous(w)
+    with pytest.raises(ValueError):
+        kvc.decode(x["q"], x["k_cache"], x["v_cache"], x["seq_lens_after"])
