@@ -78,6 +78,8 @@ def main():
                     help="override the workload's split count (0 = library's choice)")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying HIP graphs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -123,48 +125,77 @@ def main():
         max_len = bt.shape[1] * x["block_size"]
     else:
         max_len = k0.shape[2]
-    ws_bytes = kvc.workspace_bytes(w.B, w.h, w.g, w.d, max_len, ns)
+    ws_bytes = kvc.workspace_bytes(w.B, w.h, w.g, w.d, max_len, ns, dtype=w.torch_dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    chunk_len, num_chunks = kvc.plan(w.B, w.h, w.g, w.d, max_len, ns)
+    split_mode, chunk_len, num_chunks = kvc.plan(w.B, w.h, w.g, w.d, max_len, ns,
+                                                 dtype=w.torch_dtype)
 
-    def step(i, ev=None):
+    def append_call(i):
+        kc, vc = ks[i % copies], vs[i % copies]
+        kvc.append(k_new, v_new, kc, vc, sl_before, block_table=bt)
+
+    def decode_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
         if w.paged:
-            kvc.append(k_new, v_new, kc, vc, sl_before, block_table=bt)
-            if ev is not None:
-                ev[0].record()
             kvc.decode_paged(q, kc, vc, bt, sl_after, scale=x["scale"], num_splits=ns,
                              workspace=ws, out=out, lse=lse)
         else:
-            kvc.append(k_new, v_new, kc, vc, sl_before)
-            if ev is not None:
-                ev[0].record()
             kvc.decode(q, kc, vc, sl_after, scale=x["scale"], num_splits=ns, workspace=ws,
                        out=out, lse=lse)
-        if ev is not None:
-            ev[1].record()
 
-    print(f"[bench] {copies} cache copies ({cache_bytes * copies / 2**30:.2f} GiB), plan "
-          f"chunk_len={chunk_len} num_chunks={num_chunks}; warmup {args.warmup}",
+    def step(i):
+        append_call(i)
+        decode_call(i)
+
+    print(f"[bench] {copies} cache copies ({cache_bytes * copies / 2**30:.2f} GiB), split "
+          f"{split_mode} chunk_len={chunk_len} num_chunks={num_chunks}; warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(args.warmup, copies)):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
-    # Timed region: K steps between two synchronisations; per-step events
-    # around the decode call (the dominant kernel(s)) on the launch stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # One HIP graph per cache copy, each holding one whole step (append,
+    # decode, merge), so that host launch latency does not sit between the
+    # kernels of a step.  --eager launches from Python instead.
+    graphs = []
+    if not args.eager:
+        for r in range(copies):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(r)
+            graphs.append(gr)
+        for r in range(copies):
+            graphs[r].replay()
+        torch.cuda.synchronize()
+
+    # Timed region: exactly K steps between two synchronisations.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            step(i)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+
+    # The dominant kernel(s): K decode calls back to back on the launch
+    # stream, HIP events around each call.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        decode_call(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
     dec_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_med_ms = dec_ms[len(dec_ms) // 2]
@@ -195,11 +226,13 @@ def main():
             "workload": w.name, "B": w.B, "h": w.h, "g": w.g, "d": w.d,
             "kv_len_before_step": w.T if w.T is not None else list(w.T_range),
             "paged": w.paged, "block_size": w.block_size if w.paged else None,
-            "num_splits": ns, "chunk_len": chunk_len, "num_chunks": num_chunks,
+            "num_splits": ns, "split": split_mode, "chunk_len": chunk_len,
+            "num_chunks": num_chunks,
             "cache_copies_rotated": copies, "parallelism": "single GPU",
         },
         "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
         "decode_ms_median": round(dec_med_ms, 5),
+        "timing": "eager" if args.eager else "HIP graph per step",
         "roofline": {
             "bound": "hbm", "kernel": "decode (partials + log-sum-exp merge)",
             "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

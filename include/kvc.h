@@ -35,8 +35,9 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing and keeps no state besides a cached device
- *     property query.  Outputs must not alias inputs.
+ *     library allocates nothing and keeps no state besides cached answers to
+ *     device queries (compute-unit count, resident work-groups per kernel).
+ *     Outputs must not alias inputs.
  *   - Every launch is asynchronous on the caller's `stream`; no entry point
  *     synchronises the host.  Validation of the host-side arguments happens
  *     before any HIP call and needs no GPU.
@@ -103,24 +104,34 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
                int dtype, hipStream_t stream);
 
 /*
- * Work split.  A sequence's positions are cut into chunks of chunk_len
- * positions; each (sequence, KV head, chunk) is one work-group that serves
- * all m = h/g query heads of the group, so every K/V byte is read once.
- * When more than one chunk exists, partial (O, lse) results go to the
- * workspace and a second kernel merges them by log-sum-exp ([P4] 2.2-2.5).
- * num_splits = 0 lets the library choose; num_splits > 0 asks for that many
- * chunks over max_seq_len (chunk_len is rounded up to a multiple of 32, so
- * the count can come out slightly lower).
+ * Work split.  The attention of one (sequence, KV head) over positions
+ * [0, L) may be cut into position ranges whose partial (O, lse) results
+ * combine exactly by log-sum-exp ([P4] 2.2-2.5).  Every work-group serves
+ * all m = h/g query heads of its KV head, so every K/V byte is read once.
  *
- * kvc_decode_plan writes the chosen chunk_len and number of chunks.
- * kvc_decode_workspace_bytes returns the workspace the decode call needs for
- * the same arguments (0 when the plan has one chunk).  max_seq_len is t_cap
- * for the contiguous entry point and max_blocks * block_size for the paged
- * one.  Both are pure host arithmetic.
+ *   num_splits = 0 (automatic): for the bf16 head_dim-128 kernels and
+ *     B <= 1024, a persistent grid of as many work-groups as the device
+ *     keeps resident (KVC_SPLIT_STREAM); all (sequence, KV head) ranges are
+ *     laid end to end and every work-group takes an equal share of the
+ *     positions, so ragged lengths stay balanced.  Otherwise chunks.
+ *   num_splits > 0: every sequence's positions are cut into chunks of
+ *     chunk_len (a multiple of 32) so that about num_splits chunks cover
+ *     max_seq_len (KVC_SPLIT_CHUNKS); each (chunk, sequence, KV head) is one
+ *     work-group.
+ * When results are split, partials go to the caller's workspace and a
+ * second kernel merges them.
+ *
+ * kvc_decode_plan reports the mode and, for chunks, chunk_len and the chunk
+ * count.  kvc_decode_workspace_bytes returns the workspace the decode call
+ * needs for the same arguments (0 if none).  max_seq_len is t_cap for the
+ * contiguous entry point and max_blocks * block_size for the paged one.
+ * Both are pure host arithmetic.
  */
-int kvc_decode_plan(int B, int h, int g, int d, int max_seq_len, int num_splits,
-                    int* chunk_len, int* num_chunks);
-size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int max_seq_len, int num_splits);
+enum { KVC_SPLIT_CHUNKS = 0, KVC_SPLIT_STREAM = 1 };
+int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
+                    int* mode, int* chunk_len, int* num_chunks);
+size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max_seq_len,
+                                  int num_splits);
 
 /*
  * kvc_decode_attention -- decode attention over a contiguous cache.
@@ -134,7 +145,8 @@ size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int max_seq_len, i
  *   scale        multiplies every q.k (usually 1/sqrt(d))
  *   num_splits   see "Work split"
  *   workspace    device buffer of at least kvc_decode_workspace_bytes(B, h, g,
- *                d, t_cap, num_splits) bytes (may be NULL when that is 0)
+ *                d, dtype, t_cap, num_splits) bytes (may be NULL when that is
+ *                0); its contents need no initialisation
  *   out          [B, h, d] float32; lse [B, h] float32 (natural log).
  *   A sequence of length 0 gets out = 0 and lse = -inf.
  */

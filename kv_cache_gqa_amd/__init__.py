@@ -54,9 +54,10 @@ def load_library():
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_append.argtypes = [vp, vp, vp, vp, vp, ip, ip, vp, ip, ip, ip, ip, ip, vp]
     lib.kvc_append.restype = ip
-    lib.kvc_decode_plan.argtypes = [ip, ip, ip, ip, ip, ip, ctypes.POINTER(ip), ctypes.POINTER(ip)]
+    lib.kvc_decode_plan.argtypes = [ip, ip, ip, ip, ip, ip, ip, ctypes.POINTER(ip),
+                                    ctypes.POINTER(ip), ctypes.POINTER(ip)]
     lib.kvc_decode_plan.restype = ip
-    lib.kvc_decode_workspace_bytes.argtypes = [ip, ip, ip, ip, ip, ip]
+    lib.kvc_decode_workspace_bytes.argtypes = [ip, ip, ip, ip, ip, ip, ip]
     lib.kvc_decode_workspace_bytes.restype = sz
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
@@ -97,17 +98,28 @@ def _check(fn: str, status: int):
         raise KvcError(fn, status)
 
 
-def plan(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0) -> Tuple[int, int]:
-    """(chunk_len, num_chunks) the library uses for these arguments."""
+def _code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    return BF16 if dtype in (torch.bfloat16, "bf16") else F32
+
+
+def plan(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0,
+         dtype=torch.bfloat16) -> Tuple[str, int, int]:
+    """(mode, chunk_len, num_chunks) the library uses: mode "stream" (persistent
+    position-balanced grid; chunk fields 0) or "chunks"."""
     lib = load_library()
-    cl, nc = ctypes.c_int(0), ctypes.c_int(0)
-    _check("kvc_decode_plan", lib.kvc_decode_plan(B, h, g, d, max_seq_len, num_splits,
-                                                  ctypes.byref(cl), ctypes.byref(nc)))
-    return cl.value, nc.value
+    mode, cl, nc = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check("kvc_decode_plan", lib.kvc_decode_plan(B, h, g, d, _code(dtype), max_seq_len, num_splits,
+                                                  ctypes.byref(mode), ctypes.byref(cl),
+                                                  ctypes.byref(nc)))
+    return ("stream" if mode.value == 1 else "chunks"), cl.value, nc.value
 
 
-def workspace_bytes(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0) -> int:
-    return int(load_library().kvc_decode_workspace_bytes(B, h, g, d, max_seq_len, num_splits))
+def workspace_bytes(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0,
+                    dtype=torch.bfloat16) -> int:
+    return int(load_library().kvc_decode_workspace_bytes(B, h, g, d, _code(dtype), max_seq_len,
+                                                         num_splits))
 
 
 def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, stream=None):
@@ -159,7 +171,8 @@ def decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, num_spl
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
-    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, t_cap, num_splits), q, workspace)
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, t_cap, num_splits), q,
+                         workspace)
     st = lib.kvc_decode_attention(
         _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
         _dev(seq_lens, "seq_lens", torch.int32), B, h, g, d, t_cap, float(scale), dt, num_splits,
@@ -182,7 +195,7 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
-    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, mb * bs, num_splits), q,
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, mb * bs, num_splits), q,
                          workspace)
     st = lib.kvc_decode_attention_paged(
         _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype), _dev(v_pool, "v_pool", q.dtype),

@@ -1,16 +1,17 @@
 // decode_mfma.hip -- bf16, head_dim 128, query groups of m = h/g in [4, 32].
 //
-// One work-group of four wavefronts per (chunk, KV head j, sequence b); it
-// serves the m query heads j*m..j*m+m-1 that share KV head j
-// ("大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com) section 三 3.3),
-// so every K/V byte is read once.  With m >= 4 the group's queries times a
-// tile of positions is a real dense product, so both products run on the
-// gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate):
+// A work-group of four wavefronts computes one segment at a time: the m
+// query heads j*m..j*m+m-1 that share KV head j of sequence b
+// ("大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com) section 三 3.3)
+// over a range of positions, so every K/V byte is read once.  With m >= 4 the
+// group's queries times a tile of positions is a real dense product, so both
+// products run on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32
+// accumulate):
 //
 //   S^T[16 pos x 16 q] = K_tile[16 pos x 128] . Q^T[128 x 16 q]
 //     A operand = K rows straight from HBM: lane l loads 16 bytes of row
 //     (l % 16) at dims 32*ks + 8*(l/16); B operand = the group's queries,
-//     loaded once; queries >= m are zero columns.
+//     loaded once per segment; queries >= m are zero columns.
 //   O^T[16 dims x 16 q] += V^T[16 dims x 32 pos] . P^T[32 pos x 16 q]
 //     the S^T result already sits in the B-operand layout this needs
 //     (lane l holds positions 4*(l/16)+v of both 16-position halves), so P
@@ -24,12 +25,19 @@
 // P is rounded to bf16 for the PV product.  Two sums are kept: lr (the
 // rounded P, from the ones product) normalises out = sum bf16(P) V / lr, so
 // the weights applied to V add up to one; l (the fp32 P, summed on the VALU)
-// gives lse = m + log2 l without the rounding bias of the bf16 weights.
+// gives lse = m + log2 l without the bias the matrix-core sum of the rounded
+// weights showed on MI355X (about 1e-3 in lse).
 //
 // V^T reads use ds_read_b64_tr_b16: within each 16-lane group, lanes 4r..4r+3
 // read 8 contiguous bytes each of one V row r, and lane i receives element i
 // of each of the four rows -- one dim of four positions, the MFMA A layout.
-#include "kvc_device.h"
+//
+// K and V are read with streaming (non-temporal) loads, double-buffered: the
+// next 32-position sub-tile is in flight while the current one is computed.
+//
+// Two entry points share the segment code: a chunked grid (chunk, KV head,
+// sequence) and the persistent stream grid of kvc_schedule.h.
+#include "kvc_schedule.h"
 
 namespace kvc {
 
@@ -65,16 +73,6 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
     return __builtin_bit_cast(uint2, r);
 }
 
-template <bool PAGED>
-__device__ __forceinline__ long kv_row(const DecodeArgs& a, const int* tbl, int blk0, long bj_base,
-                                       int j, int p) {
-    if (PAGED) {
-        const int phys = tbl[(p >> a.log2_bs) - blk0];
-        return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
-    }
-    return bj_base + p;
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -86,294 +84,339 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+#ifndef KVC_MFMA_PREFETCH
+#define KVC_MFMA_PREFETCH 1
+#endif
+
+template <int NQT, bool PAGED>
+struct MfmaEngine {
+    struct Shared {
+        int tbl[PAGED ? kMaxTableSlice : 1];
+        __attribute__((aligned(16))) unsigned char lds[Lds<NQT>::kBytes];
+    };
+
+    // The m query heads of KV head j of sequence b over positions [s, e)
+    // (possibly empty).  Called by all 256 threads.
+    __device__ static void segment(const DecodeArgs& a, Shared& sh, int b, int j, int s, int e,
+                                   const SegDst& dst) {
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int G = lane >> 4, col = lane & 15;
+        const int m = a.m;
+        __syncthreads();  // the previous segment is done with the shared memory
+
+        const uint16_t* K = (const uint16_t*)a.k;
+        const uint16_t* Vc = (const uint16_t*)a.v;
+        const uint16_t* Q = (const uint16_t*)a.q;
+
+        // B operand of Q K^T: query column 16*qt + col, dims 32*ks + 8*G .. +8.
+        uint4 qb[NQT][4];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            const int qi = 16 * qt + col;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                qb[qt][ks] = qi < m ? ld16(Q + (((long)b * a.h + (long)j * m + qi) * kD + 32 * ks + 8 * G))
+                                    : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+
+        f32x4_t acc[NQT][8];
+        f32x4_t lacc[NQT];  // sum of bf16-rounded P (normalises out)
+        float lex[NQT];     // sum of fp32 P over this lane's positions (gives lse)
+        float mrun[NQT];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            mrun[qt] = kNegInf;
+            lex[qt] = 0.0f;
+            lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+
+        unsigned char* vst = sh.lds + wave * kVStageBytes;
+        const long bj_base = ((long)b * a.g + j) * a.t_cap;
+        const float sl2 = a.scale_log2e;
+        const int* tbl = sh.tbl;
+        int blk0 = 0;
+        int w1 = e;  // end of the current window
+
+        auto kv_row = [&](int p) -> long {
+            if (PAGED) {
+                const int phys = tbl[(p >> a.log2_bs) - blk0];
+                return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+            }
+            return bj_base + p;
+        };
+
+        // Loads of the 32-position sub-tile at t0; positions are clamped to
+        // the window's last one, so a sub-tile past the end stays in bounds.
+        auto load_tile = [&](int t0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const long row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16_stream(K + row * kD + 32 * ks + 8 * G);
+            }
+            // V rows 4u + G, 16-byte chunk col: four whole rows per instruction.
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const long row = kv_row(min(t0 + 4 * u + G, w1 - 1));
+                vr[u] = ld16_stream(Vc + row * kD + 8 * col);
+            }
+        };
+
+        auto compute_tile = [&](int t0, const uint4 (&kr)[2][4], const uint4 (&vr)[8]) {
+            f32x4_t S[NQT][2];
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) s4 = mfma(kr[tt][ks], qb[qt][ks], s4);
+                    S[qt][tt] = s4;
+                }
+            }
+            // Stage V into this wavefront's LDS area.
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = 4 * u + G;
+                *reinterpret_cast<uint4*>(vst + r * kVRowBytes + ((col ^ vswz(r)) << 4)) = vr[u];
+            }
+            // Online softmax; P as the B operand of the PV product.
+            uint4 pb[NQT];
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                float sv[8];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int p = t0 + 16 * tt + 4 * G + v;
+                        const float x = S[qt][tt][v] * sl2;
+                        sv[4 * tt + v] = p < w1 ? x : kNegInf;
+                    }
+                }
+                float mt = sv[0];
+#pragma unroll
+                for (int k = 1; k < 8; ++k) mt = fmaxf(mt, sv[k]);
+                mt = fmaxf(mt, shfl_xor_f(mt, 16));
+                mt = fmaxf(mt, shfl_xor_f(mt, 32));
+                const float mnew = fmaxf(mrun[qt], mt);
+                const float ref = (mnew == kNegInf) ? 0.0f : mnew;
+                const float alpha = fast_exp2(mrun[qt] - ref);
+                mrun[qt] = mnew;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
+                lacc[qt] *= alpha;
+                float pv[8];
+                float psum = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    pv[k] = fast_exp2(sv[k] - ref);
+                    psum += pv[k];
+                }
+                lex[qt] = lex[qt] * alpha + psum;
+                pb[qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+            }
+
+            wave_lds_sync();
+
+            // PV: A operand = V^T rows (dims 16*nt + col) x positions
+            // {4G + r} U {16 + 4G + r}, r = 0..3.  Lane 16G + 4r + qd reads 8
+            // bytes of V row (16h + 4G + r) at dims 16*nt + 4*qd; the
+            // transposing read hands lane 16G + i dim 16*nt + i of those rows.
+            const int tr_r = (lane >> 2) & 3, tr_q = lane & 3;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const int ch = 2 * nt + (tr_q >> 1);
+                const int sub = (tr_q & 1) * 8;
+                const int r0 = 4 * G + tr_r, r1 = 16 + 4 * G + tr_r;
+                const uint2 lo = lds_read_tr16(vst + r0 * kVRowBytes + ((ch ^ vswz(r0)) << 4) + sub);
+                const uint2 hi = lds_read_tr16(vst + r1 * kVRowBytes + ((ch ^ vswz(r1)) << 4) + sub);
+                const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma(av, pb[qt], acc[qt][nt]);
+            }
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) lacc[qt] = mfma(ones, pb[qt], lacc[qt]);
+
+            wave_lds_sync();
+        };
+
+        // Windows of at most kMaxChunk positions, so that a window's slice of
+        // the block table fits in shared memory.
+        for (int w0 = s; w0 < e; w0 = w1) {
+            w1 = min(e, w0 + kMaxChunk);
+            if (PAGED) {
+                blk0 = w0 >> a.log2_bs;
+                const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
+                for (int t = tid; t < nblk; t += 256) {
+                    const int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
+                    sh.tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                }
+                __syncthreads();
+            }
+            const int stride = kWaves * kTileTokens;
+            int t0 = w0 + wave * kTileTokens;
+#if KVC_MFMA_PREFETCH
+            uint4 kA[2][4], vA[8], kB[2][4], vB[8];
+            load_tile(t0, kA, vA);
+            for (;;) {
+                if (t0 >= w1) break;
+                load_tile(t0 + stride, kB, vB);
+                compute_tile(t0, kA, vA);
+                t0 += stride;
+                if (t0 >= w1) break;
+                load_tile(t0 + stride, kA, vA);
+                compute_tile(t0, kB, vB);
+                t0 += stride;
+            }
+#else
+            for (; t0 < w1; t0 += stride) {
+                uint4 kr[2][4], vr[8];
+                load_tile(t0, kr, vr);
+                compute_tile(t0, kr, vr);
+            }
+#endif
+            if (PAGED) __syncthreads();  // the next window rewrites the table slice
+        }
+
+        // lex holds this lane's positions only: sum the four row groups.
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            lex[qt] += shfl_xor_f(lex[qt], 16);
+            lex[qt] += shfl_xor_f(lex[qt], 32);
+        }
+
+        // ---- merge the four wavefronts: (2,3) -> (0,1), then 1 -> 0 ----
+        float* slot0 = reinterpret_cast<float*>(sh.lds);
+        float* slot1 = slot0 + Lds<NQT>::kSlotFloats;
+        __syncthreads();  // every wavefront is done with its V staging area
+        auto store_state = [&](float* slot) {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int qi = 16 * qt + col;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    *reinterpret_cast<f32x4_t*>(slot + qi * kOStride + 16 * nt + 4 * G) = acc[qt][nt];
+                if (G == 0) {
+                    slot[16 * NQT * kOStride + qi] = mrun[qt];
+                    slot[16 * NQT * kOStride + 16 * NQT + qi] = lacc[qt][0];
+                    slot[16 * NQT * kOStride + 32 * NQT + qi] = lex[qt];
+                }
+            }
+        };
+        auto merge_state = [&](const float* slot) {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int qi = 16 * qt + col;
+                const float mo = slot[16 * NQT * kOStride + qi];
+                const float lo = slot[16 * NQT * kOStride + 16 * NQT + qi];
+                const float xo = slot[16 * NQT * kOStride + 32 * NQT + qi];
+                float fa, fb, mnew;
+                rescale_pair(mrun[qt], mo, fa, fb, mnew);
+                mrun[qt] = mnew;
+                lacc[qt] = lacc[qt] * fa + lo * fb;
+                lex[qt] = lex[qt] * fa + xo * fb;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const f32x4_t o =
+                        *reinterpret_cast<const f32x4_t*>(slot + qi * kOStride + 16 * nt + 4 * G);
+                    acc[qt][nt] = acc[qt][nt] * fa + o * fb;
+                }
+            }
+        };
+        if (wave >= 2) store_state(wave == 2 ? slot0 : slot1);
+        __syncthreads();
+        if (wave < 2) merge_state(wave == 0 ? slot0 : slot1);
+        __syncthreads();
+        if (wave == 1) store_state(slot0);
+        __syncthreads();
+        if (wave == 0) {
+            merge_state(slot0);
+            // ---- write: lane holds dims 16*nt + 4G + v of query 16*qt + col ----
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int qi = 16 * qt + col;
+                if (qi >= m) continue;
+                const float l = lex[qt];
+                const float lr = lacc[qt][0];
+                float* o = dst.o + (long)qi * dst.o_stride;
+                const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    *reinterpret_cast<f32x4_t*>(o + 16 * nt + 4 * G) = acc[qt][nt] * inv;
+                if (G == 0) {
+                    float v;
+                    if (dst.final_) v = l > 0.0f ? (mrun[qt] + fast_log2(l)) * kLn2 : kNegInf;
+                    else v = l > 0.0f ? mrun[qt] + fast_log2(l) : kNegInf;
+                    dst.lse[(long)qi * dst.lse_stride] = v;
+                }
+            }
+        }
+    }
+};
+
 }  // namespace
 
 template <int NQT, bool PAGED>
-__global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) decode_mfma_chunked(DecodeArgs a) {
+    using E = MfmaEngine<NQT, PAGED>;
+    __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int G = lane >> 4, col = lane & 15;
-    const int m = a.m;
     const int L = clamp_len(a.seq_lens[b], a.cap_len);
     const int p0 = c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;
-    if (p0 >= L && !single) return;
+    if (p0 >= L && !single) return;  // past the end: the merge skips this chunk
+    E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
+}
 
-    __shared__ int tbl[PAGED ? kMaxTableSlice : 1];
-    __shared__ __attribute__((aligned(16))) unsigned char lds[Lds<NQT>::kBytes];
-
-    int blk0 = 0;
-    if (PAGED) {
-        blk0 = p0 >> a.log2_bs;
-        const int nblk = p1 > p0 ? ((p1 - 1) >> a.log2_bs) - blk0 + 1 : 0;
-        for (int t = tid; t < nblk; t += 256) {
-            int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
-            tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
-        }
-        __syncthreads();
-    }
-
-    const uint16_t* K = (const uint16_t*)a.k;
-    const uint16_t* Vc = (const uint16_t*)a.v;
-    const uint16_t* Q = (const uint16_t*)a.q;
-
-    // B operand of Q K^T: query column 16*qt + col, dims 32*ks + 8*G .. +8.
-    uint4 qb[NQT][4];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        const int qi = 16 * qt + col;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (qi < m) {
-                qb[qt][ks] = ld16(Q + (((long)b * a.h + (long)j * m + qi) * kD + 32 * ks + 8 * G));
-            } else {
-                qb[qt][ks] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-    }
-
-    f32x4_t acc[NQT][8];
-    f32x4_t lacc[NQT];   // sum of bf16-rounded P (normalises out)
-    float lex[NQT];      // sum of fp32 P over this lane's positions (gives lse)
-    float mrun[NQT];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        mrun[qt] = kNegInf;
-        lex[qt] = 0.0f;
-        lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-
-    unsigned char* vst = lds + wave * kVStageBytes;
-    const long bj_base = ((long)b * a.g + j) * a.t_cap;
-    const float sl2 = a.scale_log2e;
-
-    // Loads of a 32-position sub-tile starting at t0.  Positions are clamped
-    // to p1 - 1, so a sub-tile past the end reloads the last row (in bounds).
-    auto load_tile = [&](int t0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
-        // K rows of the two 16-position halves, in A-operand layout.
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int p = min(t0 + 16 * tt + col, p1 - 1);
-            const long row = kv_row<PAGED>(a, tbl, blk0, bj_base, j, p);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16(K + row * kD + 32 * ks + 8 * G);
-        }
-        // V rows 4u + G, 16-byte chunk col: four whole rows per instruction.
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int p = min(t0 + 4 * u + G, p1 - 1);
-            const long row = kv_row<PAGED>(a, tbl, blk0, bj_base, j, p);
-            vr[u] = ld16(Vc + row * kD + 8 * col);
-        }
-    };
-    auto compute_tile = [&](int t0, const uint4 (&kr)[2][4], const uint4 (&vr)[8]) {
-        // Scores.
-        f32x4_t S[NQT][2];
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) s4 = mfma(kr[tt][ks], qb[qt][ks], s4);
-                S[qt][tt] = s4;
-            }
-        }
-
-        // Stage V into this wavefront's LDS area.
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int r = 4 * u + G;
-            *reinterpret_cast<uint4*>(vst + r * kVRowBytes + ((col ^ vswz(r)) << 4)) = vr[u];
-        }
-
-        // Online softmax; P as the B operand of the PV product.
-        uint4 pb[NQT];
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            float sv[8];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int p = t0 + 16 * tt + 4 * G + v;
-                    const float x = S[qt][tt][v] * sl2;
-                    sv[4 * tt + v] = p < p1 ? x : kNegInf;
-                }
-            }
-            float mt = sv[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-            mt = fmaxf(mt, shfl_xor_f(mt, 16));
-            mt = fmaxf(mt, shfl_xor_f(mt, 32));
-            const float mnew = fmaxf(mrun[qt], mt);
-            const float ref = (mnew == kNegInf) ? 0.0f : mnew;
-            const float alpha = fast_exp2(mrun[qt] - ref);
-            mrun[qt] = mnew;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
-            lacc[qt] *= alpha;
-            float pv[8];
-            float psum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pv[e] = fast_exp2(sv[e] - ref);
-                psum += pv[e];
-            }
-            lex[qt] = lex[qt] * alpha + psum;
-            pb[qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
-        }
-
-        wave_lds_sync();
-
-        // PV: A operand = V^T rows (dims 16*nt + col) x positions
-        // {4G + r} U {16 + 4G + r}, r = 0..3.  Lane 16G + 4r + qd reads 8
-        // bytes of V row (16h + 4G + r) at dims 16*nt + 4*qd; the transposing
-        // read hands lane 16G + i dim 16*nt + i of those four rows.
-        const int tr_r = (lane >> 2) & 3, tr_q = lane & 3;
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int ch = 2 * nt + (tr_q >> 1);
-            const int sub = (tr_q & 1) * 8;
-            const int r0 = 4 * G + tr_r, r1 = 16 + 4 * G + tr_r;
-            const uint2 lo = lds_read_tr16(vst + r0 * kVRowBytes + ((ch ^ vswz(r0)) << 4) + sub);
-            const uint2 hi = lds_read_tr16(vst + r1 * kVRowBytes + ((ch ^ vswz(r1)) << 4) + sub);
-            const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma(av, pb[qt], acc[qt][nt]);
-        }
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) lacc[qt] = mfma(ones, pb[qt], lacc[qt]);
-
-        wave_lds_sync();
-    };
-
-#ifndef KVC_MFMA_PREFETCH
-#define KVC_MFMA_PREFETCH 1
-#endif
-    if (p1 > p0) {
-        const int stride = kWaves * kTileTokens;
-        int t0 = p0 + wave * kTileTokens;
-#if KVC_MFMA_PREFETCH
-        // Double-buffered walk over this wavefront's sub-tiles: the loads of
-        // the next sub-tile are in flight while the current one is computed.
-        uint4 kA[2][4], vA[8], kB[2][4], vB[8];
-        load_tile(t0, kA, vA);
-        for (;;) {
-            if (t0 >= p1) break;
-            load_tile(t0 + stride, kB, vB);
-            compute_tile(t0, kA, vA);
-            t0 += stride;
-            if (t0 >= p1) break;
-            load_tile(t0 + stride, kA, vA);
-            compute_tile(t0, kB, vB);
-            t0 += stride;
-        }
-#else
-        for (; t0 < p1; t0 += stride) {
-            uint4 kr[2][4], vr[8];
-            load_tile(t0, kr, vr);
-            compute_tile(t0, kr, vr);
-        }
-#endif
-    }
-
-    // lex holds this lane's positions only: sum the four row groups.
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        lex[qt] += shfl_xor_f(lex[qt], 16);
-        lex[qt] += shfl_xor_f(lex[qt], 32);
-    }
-
-    // ---- merge the four wavefronts: (2,3) -> (0,1), then 1 -> 0 ----
-    float* slot0 = reinterpret_cast<float*>(lds);
-    float* slot1 = slot0 + Lds<NQT>::kSlotFloats;
-    __syncthreads();  // every wavefront is done with its V staging area
-    auto store_state = [&](float* slot) {
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            const int qi = 16 * qt + col;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                *reinterpret_cast<f32x4_t*>(slot + qi * kOStride + 16 * nt + 4 * G) = acc[qt][nt];
-            if (G == 0) {
-                slot[16 * NQT * kOStride + qi] = mrun[qt];
-                slot[16 * NQT * kOStride + 16 * NQT + qi] = lacc[qt][0];
-                slot[16 * NQT * kOStride + 32 * NQT + qi] = lex[qt];
-            }
-        }
-    };
-    auto merge_state = [&](const float* slot) {
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            const int qi = 16 * qt + col;
-            const float mo = slot[16 * NQT * kOStride + qi];
-            const float lo = slot[16 * NQT * kOStride + 16 * NQT + qi];
-            const float xo = slot[16 * NQT * kOStride + 32 * NQT + qi];
-            float fa, fb, mnew;
-            rescale_pair(mrun[qt], mo, fa, fb, mnew);
-            mrun[qt] = mnew;
-            lacc[qt] = lacc[qt] * fa + lo * fb;
-            lex[qt] = lex[qt] * fa + xo * fb;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const f32x4_t o = *reinterpret_cast<const f32x4_t*>(slot + qi * kOStride + 16 * nt + 4 * G);
-                acc[qt][nt] = acc[qt][nt] * fa + o * fb;
-            }
-        }
-    };
-    if (wave >= 2) store_state(wave == 2 ? slot0 : slot1);
-    __syncthreads();
-    if (wave < 2) merge_state(wave == 0 ? slot0 : slot1);
-    __syncthreads();
-    if (wave == 1) store_state(slot0);
-    __syncthreads();
-    if (wave != 0) return;
-    merge_state(slot0);
-
-    // ---- write: lane holds dims 16*nt + 4G + v of query 16*qt + col ----
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-        const int qi = 16 * qt + col;
-        if (qi >= m) continue;
-        const float l = lex[qt];
-        const float lr = lacc[qt][0];
-        const long row_out = (long)b * a.h + (long)j * m + qi;
-        if (single) {
-            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                *reinterpret_cast<f32x4_t*>(a.out + row_out * kD + 16 * nt + 4 * G) = acc[qt][nt] * inv;
-            if (G == 0) a.lse[row_out] = l > 0.0f ? (mrun[qt] + fast_log2(l)) * kLn2 : kNegInf;
-        } else {
-            const long prow = row_out * a.num_chunks + c;
-            const float inv = 1.0f / lr;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                *reinterpret_cast<f32x4_t*>(a.part_o + prow * kD + 16 * nt + 4 * G) = acc[qt][nt] * inv;
-            if (G == 0) a.part_lse[prow] = mrun[qt] + fast_log2(l);
-        }
-    }
+template <int NQT, bool PAGED>
+__global__ void __launch_bounds__(256) decode_mfma_stream(DecodeArgs a) {
+    using E = MfmaEngine<NQT, PAGED>;
+    __shared__ typename E::Shared sh;
+    __shared__ long long cum[kStreamMaxB + 1];
+    __shared__ long long part[256];
+    stream_prefix(a, cum, part);
+    stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
+        E::segment(a, sh, b, j, s, e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
+    });
 }
 
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
     const bool paged = a.block_table != nullptr;
-    if (a.m <= 16) {
-        if (paged) decode_mfma_kernel<1, true><<<grid, dim3(256), 0, s>>>(a);
-        else decode_mfma_kernel<1, false><<<grid, dim3(256), 0, s>>>(a);
-    } else if (a.m <= 32) {
-        if (paged) decode_mfma_kernel<2, true><<<grid, dim3(256), 0, s>>>(a);
-        else decode_mfma_kernel<2, false><<<grid, dim3(256), 0, s>>>(a);
+    if (a.m > 32) return hipErrorInvalidValue;
+    const bool two = a.m > 16;
+    if (a.stream) {
+        dim3 grid((unsigned)a.num_wgs);
+        if (two) {
+            if (paged) decode_mfma_stream<2, true><<<grid, dim3(256), 0, s>>>(a);
+            else decode_mfma_stream<2, false><<<grid, dim3(256), 0, s>>>(a);
+        } else {
+            if (paged) decode_mfma_stream<1, true><<<grid, dim3(256), 0, s>>>(a);
+            else decode_mfma_stream<1, false><<<grid, dim3(256), 0, s>>>(a);
+        }
     } else {
-        return hipErrorInvalidValue;
+        dim3 grid((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
+        if (two) {
+            if (paged) decode_mfma_chunked<2, true><<<grid, dim3(256), 0, s>>>(a);
+            else decode_mfma_chunked<2, false><<<grid, dim3(256), 0, s>>>(a);
+        } else {
+            if (paged) decode_mfma_chunked<1, true><<<grid, dim3(256), 0, s>>>(a);
+            else decode_mfma_chunked<1, false><<<grid, dim3(256), 0, s>>>(a);
+        }
     }
     return hipGetLastError();
+}
+
+const void* mfma_stream_kernel(int m, bool paged) {
+    if (m > 16)
+        return paged ? (const void*)decode_mfma_stream<2, true> : (const void*)decode_mfma_stream<2, false>;
+    return paged ? (const void*)decode_mfma_stream<1, true> : (const void*)decode_mfma_stream<1, false>;
 }
 
 }  // namespace kvc

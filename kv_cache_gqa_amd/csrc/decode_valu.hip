@@ -1,19 +1,25 @@
 // decode_valu.hip -- bf16, head_dim 128, small query groups (m = h/g <= 3).
 //
-// One work-group of four wavefronts per (chunk, KV head j, sequence b).  The
-// work-group serves all m query heads that share KV head j ("大语言模型研究15
-// ——注意力机制优化之KV缓存" (limoncc.com) section 三 3.3: heads j*m..j*m+m-1
-// use KV head j), so every K/V byte of the chunk is read from HBM once.
+// A work-group of four wavefronts computes one segment at a time: the m
+// query heads that share KV head j of sequence b ("大语言模型研究15——注意力
+// 机制优化之KV缓存" (limoncc.com) section 三 3.3: heads j*m..j*m+m-1 use KV
+// head j) over a range of positions, so every K/V byte is read from HBM once.
+// With m <= 3 the product is too thin for the matrix cores; it runs on the
+// vector ALUs.
 //
 // Lane layout: lane l covers dims [8*(l%16), 8*(l%16)+8) of position
 // (l/16) + 4u of the current 32-position sub-tile, u = 0..7.  One 16-byte
 // load per lane per u reads four whole 256-byte K (or V) rows per wavefront
-// instruction, fully coalesced.  q.k is v_dot2_f32_bf16 on the raw bf16
-// pairs, summed over the 16 lanes of a row with DPP.  Each row of 16 lanes
-// keeps its own online-softmax state (m, l, acc) ("KV Cache 优化与注意力机制
-// 加速" (plumephp.com) section 2.2); the four row states of a wavefront and
-// the four wavefronts are merged once at the end of the chunk.
-#include "kvc_device.h"
+// instruction, fully coalesced, as streaming (non-temporal) loads.  q.k is
+// v_dot2_f32_bf16 on the raw bf16 pairs, summed over the 16 lanes of a row
+// with DPP.  Each row of 16 lanes keeps its own online-softmax state (m, l,
+// acc) ("KV Cache 优化与注意力机制加速" (plumephp.com) section 2.2); the four
+// row states of a wavefront and the four wavefronts are merged once at the
+// end of the segment.
+//
+// Two entry points share the segment code: a chunked grid (chunk, KV head,
+// sequence) and the persistent stream grid of kvc_schedule.h.
+#include "kvc_schedule.h"
 
 namespace kvc {
 
@@ -22,198 +28,265 @@ namespace {
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 
-template <bool PAGED>
-__device__ __forceinline__ long kv_row(const DecodeArgs& a, const int* tbl, int blk0, long bj_base,
-                                       int j, int p) {
-    if (PAGED) {
-        const int phys = tbl[(p >> a.log2_bs) - blk0];
-        return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+#ifndef KVC_VALU_PREFETCH
+#define KVC_VALU_PREFETCH 0
+#endif
+
+template <int M, bool PAGED>
+struct ValuEngine {
+    struct Shared {
+        int tbl[PAGED ? kMaxTableSlice : 1];
+        float red_m[kWaves][M];
+        float red_l[kWaves][M];
+        float red_o[kWaves][M][kD];
+    };
+
+    // The M query heads of KV head j of sequence b over positions [s, e)
+    // (possibly empty).  Called by all 256 threads.
+    __device__ static void segment(const DecodeArgs& a, Shared& sh, int b, int j, int s, int e,
+                                   const SegDst& dst) {
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int tsub = lane >> 4, ds = lane & 15;
+        __syncthreads();  // the previous segment is done with the shared memory
+
+        const uint16_t* K = (const uint16_t*)a.k;
+        const uint16_t* Vc = (const uint16_t*)a.v;
+        const uint16_t* Q = (const uint16_t*)a.q;
+
+        uint32_t qp[M][4];
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            const uint4 v = ld16(Q + (((long)b * a.h + (long)j * M + r) * kD + 8 * ds));
+            qp[r][0] = v.x; qp[r][1] = v.y; qp[r][2] = v.z; qp[r][3] = v.w;
+        }
+        float mrun[M], lrun[M], acc[M][8];
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            mrun[r] = kNegInf;
+            lrun[r] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[r][k] = 0.0f;
+        }
+        const long bj_base = ((long)b * a.g + j) * a.t_cap;
+        const float sl2 = a.scale_log2e;
+        const int* tbl = sh.tbl;
+        int blk0 = 0;
+        int w1 = e;
+
+        auto kv_row = [&](int p) -> long {
+            if (PAGED) {
+                const int phys = tbl[(p >> a.log2_bs) - blk0];
+                return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+            }
+            return bj_base + p;
+        };
+        // Positions clamped to the window's last one (in bounds past the end).
+        auto load_tile = [&](int t0, uint4 (&kv)[8], uint4 (&vv)[8]) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const long row = kv_row(min(t0 + 4 * u + tsub, w1 - 1));
+                kv[u] = ld16_stream(K + row * kD + 8 * ds);
+                vv[u] = ld16_stream(Vc + row * kD + 8 * ds);
+            }
+        };
+        auto compute_tile = [&](int t0, const uint4 (&kv)[8], const uint4 (&vv)[8]) {
+            float sc[M][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool valid = (t0 + 4 * u + tsub) < w1;
+#pragma unroll
+                for (int r = 0; r < M; ++r) {
+                    float dot = dot2_bf16(qp[r][0], kv[u].x, 0.0f);
+                    dot = dot2_bf16(qp[r][1], kv[u].y, dot);
+                    dot = dot2_bf16(qp[r][2], kv[u].z, dot);
+                    dot = dot2_bf16(qp[r][3], kv[u].w, dot);
+                    dot = row16_sum(dot) * sl2;
+                    sc[r][u] = valid ? dot : kNegInf;
+                }
+            }
+            float pr[M][8];
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                float mt = sc[r][0];
+#pragma unroll
+                for (int u = 1; u < 8; ++u) mt = fmaxf(mt, sc[r][u]);
+                const float mnew = fmaxf(mrun[r], mt);
+                const float ref = (mnew == kNegInf) ? 0.0f : mnew;
+                const float alpha = fast_exp2(mrun[r] - ref);
+                mrun[r] = mnew;
+                float lsum = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    pr[r][u] = fast_exp2(sc[r][u] - ref);
+                    lsum += pr[r][u];
+                }
+                lrun[r] = lrun[r] * alpha + lsum;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[r][k] *= alpha;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float vf[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y),
+                                     bf16_hi(vv[u].y), bf16_lo(vv[u].z), bf16_hi(vv[u].z),
+                                     bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
+#pragma unroll
+                for (int r = 0; r < M; ++r) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) acc[r][k] += pr[r][u] * vf[k];
+                }
+            }
+        };
+
+        // Windows of at most kMaxChunk positions (block-table slice in LDS).
+        for (int w0 = s; w0 < e; w0 = w1) {
+            w1 = min(e, w0 + kMaxChunk);
+            if (PAGED) {
+                blk0 = w0 >> a.log2_bs;
+                const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
+                for (int t = tid; t < nblk; t += 256) {
+                    const int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
+                    sh.tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                }
+                __syncthreads();
+            }
+            const int stride = kWaves * kTileTokens;
+            int t0 = w0 + wave * kTileTokens;
+#if KVC_VALU_PREFETCH
+            uint4 kA[8], vA[8], kB[8], vB[8];
+            load_tile(t0, kA, vA);
+            for (;;) {
+                if (t0 >= w1) break;
+                load_tile(t0 + stride, kB, vB);
+                compute_tile(t0, kA, vA);
+                t0 += stride;
+                if (t0 >= w1) break;
+                load_tile(t0 + stride, kA, vA);
+                compute_tile(t0, kB, vB);
+                t0 += stride;
+            }
+#else
+            for (; t0 < w1; t0 += stride) {
+                uint4 kv[8], vv[8];
+                load_tile(t0, kv, vv);
+                compute_tile(t0, kv, vv);
+            }
+#endif
+            if (PAGED) __syncthreads();  // the next window rewrites the table slice
+        }
+
+        // Merge the four rows of 16 lanes (positions interleaved by lane/16).
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+#pragma unroll
+            for (int mask = 16; mask <= 32; mask <<= 1) {
+                const float mo = shfl_xor_f(mrun[r], mask);
+                const float lo = shfl_xor_f(lrun[r], mask);
+                float fa, fb, mnew;
+                rescale_pair(mrun[r], mo, fa, fb, mnew);
+                lrun[r] = lrun[r] * fa + lo * fb;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float ao = shfl_xor_f(acc[r][k], mask);
+                    acc[r][k] = acc[r][k] * fa + ao * fb;
+                }
+                mrun[r] = mnew;
+            }
+        }
+        if (tsub == 0) {
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) sh.red_o[wave][r][8 * ds + k] = acc[r][k];
+                if (ds == 0) {
+                    sh.red_m[wave][r] = mrun[r];
+                    sh.red_l[wave][r] = lrun[r];
+                }
+            }
+        }
+        __syncthreads();
+
+        // Merge the four wavefronts and write the rows.
+        for (int idx = tid; idx < M * kD; idx += 256) {
+            const int r = idx / kD, dim = idx % kD;
+            float mm = sh.red_m[0][r];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, sh.red_m[w][r]);
+            const float ref = (mm == kNegInf) ? 0.0f : mm;
+            float l = 0.0f, o = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = fast_exp2(sh.red_m[w][r] - ref);
+                l += sh.red_l[w][r] * f;
+                o += sh.red_o[w][r][dim] * f;
+            }
+            dst.o[(long)r * dst.o_stride + dim] = l > 0.0f ? o / l : 0.0f;
+            if (dim == 0) {
+                float v;
+                if (dst.final_) v = l > 0.0f ? (mm + fast_log2(l)) * kLn2 : kNegInf;
+                else v = l > 0.0f ? mm + fast_log2(l) : kNegInf;
+                dst.lse[(long)r * dst.lse_stride] = v;
+            }
+        }
     }
-    return bj_base + p;
-}
+};
 
 }  // namespace
 
 template <int M, bool PAGED>
-__global__ void __launch_bounds__(256) decode_valu_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) decode_valu_chunked(DecodeArgs a) {
+    using E = ValuEngine<M, PAGED>;
+    __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tsub = lane >> 4, ds = lane & 15;
     const int L = clamp_len(a.seq_lens[b], a.cap_len);
     const int p0 = c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;
-    if (p0 >= L && !single) return;
+    if (p0 >= L && !single) return;  // past the end: the merge skips this chunk
+    E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
+}
 
-    __shared__ int tbl[PAGED ? kMaxTableSlice : 1];
-    __shared__ float red_m[kWaves][M], red_l[kWaves][M];
-    __shared__ float red_o[kWaves][M][kD];
+template <int M, bool PAGED>
+__global__ void __launch_bounds__(256) decode_valu_stream(DecodeArgs a) {
+    using E = ValuEngine<M, PAGED>;
+    __shared__ typename E::Shared sh;
+    __shared__ long long cum[kStreamMaxB + 1];
+    __shared__ long long part[256];
+    stream_prefix(a, cum, part);
+    stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
+        E::segment(a, sh, b, j, s, e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
+    });
+}
 
-    int blk0 = 0;
-    if (PAGED) {
-        blk0 = p0 >> a.log2_bs;
-        const int nblk = p1 > p0 ? ((p1 - 1) >> a.log2_bs) - blk0 + 1 : 0;
-        for (int t = tid; t < nblk; t += 256) {
-            int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
-            tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
-        }
-        __syncthreads();
-    }
-
-    const uint16_t* K = (const uint16_t*)a.k;
-    const uint16_t* Vc = (const uint16_t*)a.v;
-    const uint16_t* Q = (const uint16_t*)a.q;
-
-    uint32_t qp[M][4];
-#pragma unroll
-    for (int r = 0; r < M; ++r) {
-        const uint4 v = ld16(Q + (((long)b * a.h + (long)j * M + r) * kD + 8 * ds));
-        qp[r][0] = v.x; qp[r][1] = v.y; qp[r][2] = v.z; qp[r][3] = v.w;
-    }
-    float mrun[M], lrun[M], acc[M][8];
-#pragma unroll
-    for (int r = 0; r < M; ++r) {
-        mrun[r] = kNegInf;
-        lrun[r] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
-    }
-    const long bj_base = ((long)b * a.g + j) * a.t_cap;
-    const float sl2 = a.scale_log2e;
-
-    for (int t0 = p0 + wave * kTileTokens; t0 < p1; t0 += kWaves * kTileTokens) {
-        uint4 kv[8], vv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int p = min(t0 + 4 * u + tsub, p1 - 1);
-            const long row = kv_row<PAGED>(a, tbl, blk0, bj_base, j, p);
-            kv[u] = ld16(K + row * kD + 8 * ds);
-            vv[u] = ld16(Vc + row * kD + 8 * ds);
-        }
-        float s[M][8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool valid = (t0 + 4 * u + tsub) < p1;
-#pragma unroll
-            for (int r = 0; r < M; ++r) {
-                float dot = dot2_bf16(qp[r][0], kv[u].x, 0.0f);
-                dot = dot2_bf16(qp[r][1], kv[u].y, dot);
-                dot = dot2_bf16(qp[r][2], kv[u].z, dot);
-                dot = dot2_bf16(qp[r][3], kv[u].w, dot);
-                dot = row16_sum(dot) * sl2;
-                s[r][u] = valid ? dot : kNegInf;
-            }
-        }
-        float pr[M][8];
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-            float mt = s[r][0];
-#pragma unroll
-            for (int u = 1; u < 8; ++u) mt = fmaxf(mt, s[r][u]);
-            const float mnew = fmaxf(mrun[r], mt);
-            const float ref = (mnew == kNegInf) ? 0.0f : mnew;
-            const float alpha = fast_exp2(mrun[r] - ref);
-            mrun[r] = mnew;
-            float lsum = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                pr[r][u] = fast_exp2(s[r][u] - ref);
-                lsum += pr[r][u];
-            }
-            lrun[r] = lrun[r] * alpha + lsum;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float vf[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y),
-                                 bf16_hi(vv[u].y), bf16_lo(vv[u].z), bf16_hi(vv[u].z),
-                                 bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
-#pragma unroll
-            for (int r = 0; r < M; ++r) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[r][e] += pr[r][u] * vf[e];
-            }
-        }
-    }
-
-    // Merge the four rows of 16 lanes (positions interleaved by lane/16).
-#pragma unroll
-    for (int r = 0; r < M; ++r) {
-#pragma unroll
-        for (int mask = 16; mask <= 32; mask <<= 1) {
-            const float mo = shfl_xor_f(mrun[r], mask);
-            const float lo = shfl_xor_f(lrun[r], mask);
-            float fa, fb, mnew;
-            rescale_pair(mrun[r], mo, fa, fb, mnew);
-            lrun[r] = lrun[r] * fa + lo * fb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ao = shfl_xor_f(acc[r][e], mask);
-                acc[r][e] = acc[r][e] * fa + ao * fb;
-            }
-            mrun[r] = mnew;
-        }
-    }
-    if (tsub == 0) {
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red_o[wave][r][8 * ds + e] = acc[r][e];
-            if (ds == 0) {
-                red_m[wave][r] = mrun[r];
-                red_l[wave][r] = lrun[r];
-            }
-        }
-    }
-    __syncthreads();
-
-    // Merge the four wavefronts and write the result (final or partial).
-    for (int idx = tid; idx < M * kD; idx += 256) {
-        const int r = idx / kD, dim = idx % kD;
-        float mm = red_m[0][r];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, red_m[w][r]);
-        const float ref = (mm == kNegInf) ? 0.0f : mm;
-        float l = 0.0f, o = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = fast_exp2(red_m[w][r] - ref);
-            l += red_l[w][r] * f;
-            o += red_o[w][r][dim] * f;
-        }
-        const long row_out = (long)b * a.h + (long)j * M + r;
-        if (single) {
-            a.out[row_out * kD + dim] = l > 0.0f ? o / l : 0.0f;
-            if (dim == 0) a.lse[row_out] = l > 0.0f ? (mm + fast_log2(l)) * kLn2 : kNegInf;
-        } else {
-            const long prow = row_out * a.num_chunks + c;
-            a.part_o[prow * kD + dim] = o / l;
-            if (dim == 0) a.part_lse[prow] = mm + fast_log2(l);
-        }
+template <int M>
+static void launch_valu_m(const DecodeArgs& a, hipStream_t s) {
+    const bool paged = a.block_table != nullptr;
+    if (a.stream) {
+        dim3 grid((unsigned)a.num_wgs);
+        if (paged) decode_valu_stream<M, true><<<grid, dim3(256), 0, s>>>(a);
+        else decode_valu_stream<M, false><<<grid, dim3(256), 0, s>>>(a);
+    } else {
+        dim3 grid((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
+        if (paged) decode_valu_chunked<M, true><<<grid, dim3(256), 0, s>>>(a);
+        else decode_valu_chunked<M, false><<<grid, dim3(256), 0, s>>>(a);
     }
 }
 
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
-    const bool paged = a.block_table != nullptr;
-#define KVC_VALU_CASE(MM)                                                      \
-    case MM:                                                                   \
-        if (paged)                                                             \
-            decode_valu_kernel<MM, true><<<grid, dim3(256), 0, s>>>(a);        \
-        else                                                                   \
-            decode_valu_kernel<MM, false><<<grid, dim3(256), 0, s>>>(a);       \
-        break;
     switch (a.m) {
-        KVC_VALU_CASE(1)
-        KVC_VALU_CASE(2)
-        KVC_VALU_CASE(3)
-        KVC_VALU_CASE(4)
-        default:
-            return hipErrorInvalidValue;
+        case 1: launch_valu_m<1>(a, s); break;
+        case 2: launch_valu_m<2>(a, s); break;
+        case 3: launch_valu_m<3>(a, s); break;
+        default: return hipErrorInvalidValue;
     }
-#undef KVC_VALU_CASE
     return hipGetLastError();
+}
+
+const void* valu_stream_kernel(int m, bool paged) {
+    switch (m) {
+        case 1: return paged ? (const void*)decode_valu_stream<1, true> : (const void*)decode_valu_stream<1, false>;
+        case 2: return paged ? (const void*)decode_valu_stream<2, true> : (const void*)decode_valu_stream<2, false>;
+        default: return paged ? (const void*)decode_valu_stream<3, true> : (const void*)decode_valu_stream<3, false>;
+    }
 }
 
 }  // namespace kvc

@@ -40,10 +40,64 @@ KernelKind choose_kernel(int dtype, int d, int m) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static size_t workspace_for(int B, int h, int d, const Plan& p) {
-    if (p.num_chunks <= 1) return 0;
-    const size_t rows = (size_t)B * h * p.num_chunks;
+// A decode launch: the kernel family and how positions are split.
+struct Schedule {
+    KernelKind kind;
+    bool stream;  // persistent, position-balanced grid (automatic split)
+    Plan plan;    // chunked mode
+};
+
+static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq_len,
+                              int num_splits) {
+    Schedule sc;
+    sc.kind = choose_kernel(dtype, d, h / g);
+    // Stream mode keeps global positions in 64-bit products p * total with
+    // p <= 1024: it is used only while B * g * max_seq_len < 2^40.
+    const bool small_enough = (long double)B * g * max_seq_len < (long double)(1LL << 40);
+    sc.stream = num_splits == 0 && sc.kind != kGeneric && B <= kStreamMaxB && small_enough;
+    sc.plan = make_plan(B, g, max_seq_len, num_splits);
+    return sc;
+}
+
+static size_t workspace_for(int B, int h, int g, int d, const Schedule& sc) {
+    size_t rows;
+    if (sc.stream) {
+        rows = (size_t)kStreamMaxCUs * kStreamMaxWgPerCu * 2 * (size_t)(h / g);
+    } else {
+        if (sc.plan.num_chunks <= 1) return 0;
+        rows = (size_t)B * h * sc.plan.num_chunks;
+    }
     return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kStreamMaxCUs;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = kStreamMaxCUs;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
+// Resident work-groups of 256 threads per compute unit for a kernel (cached).
+static int resident_wgs(const void* fn) {
+    struct Entry { const void* fn; int n; };
+    static Entry cache[16] = {};
+    for (auto& e : cache)
+        if (e.fn == fn) return e.n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess || n <= 0) n = 1;
+    for (auto& e : cache)
+        if (e.fn == nullptr) {
+            e.fn = fn;
+            e.n = n;
+            break;
+        }
+    return n;
 }
 
 static int ilog2_exact(int x) {
@@ -67,13 +121,16 @@ static int check_common(const void* q, const void* k, const void* v, const int32
 
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-    const Plan plan = make_plan(a.B, a.g, max_len, num_splits);
-    a.chunk_len = plan.chunk_len;
-    a.num_chunks = plan.num_chunks;
-    const size_t need = workspace_for(a.B, a.h, a.d, plan);
+    const Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits);
+    a.chunk_len = sc.plan.chunk_len;
+    a.num_chunks = sc.plan.num_chunks;
+    a.stream = sc.stream ? 1 : 0;
+    a.num_wgs = 0;
+    const size_t need = workspace_for(a.B, a.h, a.g, a.d, sc);
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
-        const size_t rows = (size_t)a.B * a.h * plan.num_chunks;
+        const size_t rows = sc.stream ? (size_t)kStreamMaxCUs * kStreamMaxWgPerCu * 2 * a.m
+                                      : (size_t)a.B * a.h * sc.plan.num_chunks;
         a.part_o = static_cast<float*>(workspace);
         a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                               align256(rows * a.d * sizeof(float)));
@@ -82,14 +139,29 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
         a.part_lse = nullptr;
     }
     if (a.B == 0) return KVC_OK;
+    if (sc.stream) {
+        const bool paged = a.block_table != nullptr;
+        const void* fn = sc.kind == kMfma ? mfma_stream_kernel(a.m, paged) : valu_stream_kernel(a.m, paged);
+        int per_cu = resident_wgs(fn);
+        if (per_cu > kStreamMaxWgPerCu) per_cu = kStreamMaxWgPerCu;
+        int cus = device_cus();
+        if (cus > kStreamMaxCUs) cus = kStreamMaxCUs;
+        long P = (long)cus * per_cu;
+        // No more work-groups than 256-position pieces of the largest possible batch.
+        const long pieces = ((long)a.B * a.g * a.cap_len + 255) / 256;
+        if (P > pieces) P = pieces;
+        a.num_wgs = (int)(P < 1 ? 1 : P);
+    }
     hipError_t err;
-    switch (choose_kernel(dtype, a.d, a.m)) {
+    switch (sc.kind) {
         case kValu: err = launch_decode_valu_bf16_d128(a, stream); break;
         case kMfma: err = launch_decode_mfma_bf16_d128(a, stream); break;
         default: err = launch_decode_generic(a, dtype, stream); break;
     }
     if (err != hipSuccess) return KVC_ERR_HIP;
-    if (plan.num_chunks > 1) {
+    if (sc.stream) {
+        if (launch_merge_stream(a, stream) != hipSuccess) return KVC_ERR_HIP;
+    } else if (sc.plan.num_chunks > 1) {
         if (launch_merge(a, stream) != hipSuccess) return KVC_ERR_HIP;
     }
     return KVC_OK;
@@ -114,20 +186,24 @@ const char* kvc_status_string(int status) {
     }
 }
 
-int kvc_decode_plan(int B, int h, int g, int d, int max_seq_len, int num_splits,
-                    int* chunk_len, int* num_chunks) {
+int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
+                    int* mode, int* chunk_len, int* num_chunks) {
     if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < 0 || max_seq_len < 0)
         return KVC_ERR_INVALID;
-    const Plan p = make_plan(B, g, max_seq_len, num_splits);
-    if (chunk_len) *chunk_len = p.chunk_len;
-    if (num_chunks) *num_chunks = p.num_chunks;
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits);
+    if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : KVC_SPLIT_CHUNKS;
+    if (chunk_len) *chunk_len = sc.stream ? 0 : sc.plan.chunk_len;
+    if (num_chunks) *num_chunks = sc.stream ? 0 : sc.plan.num_chunks;
     return KVC_OK;
 }
 
-size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int max_seq_len, int num_splits) {
+size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max_seq_len,
+                                  int num_splits) {
     if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < 0 || max_seq_len < 0)
         return 0;
-    return workspace_for(B, h, d, make_plan(B, g, max_seq_len, num_splits));
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
+    return workspace_for(B, h, g, d, make_schedule(B, h, g, d, dtype, max_seq_len, num_splits));
 }
 
 int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

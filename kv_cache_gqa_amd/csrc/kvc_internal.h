@@ -18,6 +18,13 @@ constexpr int kMaxTableSlice = kMaxChunk / 8 + 2;
 // chunks shorter than kMinAutoChunk positions.
 constexpr int kTargetWorkgroups = 2048;
 constexpr int kMinAutoChunk = 256;
+// Stream mode (persistent, position-balanced) needs the prefix sums of all
+// sequence lengths in shared memory: batches up to kStreamMaxB sequences.
+constexpr int kStreamMaxB = 1024;
+// Stream-mode partial records are sized for at most this many resident
+// work-groups per compute unit on a 256-CU device.
+constexpr int kStreamMaxWgPerCu = 4;
+constexpr int kStreamMaxCUs = 256;
 
 struct Plan {
     int chunk_len;   // positions per chunk (multiple of kTileTokens)
@@ -44,10 +51,14 @@ struct DecodeArgs {
     int t_cap;        // contiguous capacity in positions
     int cap_len;      // clamp bound for seq_lens: t_cap or max_blocks*block_size
     float scale_log2e;  // scale * log2(e): scores are kept in base 2
-    int chunk_len;
+    int chunk_len;    // chunked mode
     int num_chunks;
-    float* part_o;    // [B,h,C,d] (C > 1 only)
-    float* part_lse;  // [B,h,C]   base-2 log-sum-exp of each chunk
+    int stream;       // 1: persistent position-balanced grid of num_wgs work-groups
+    int num_wgs;
+    // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
+    // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
+    float* part_o;
+    float* part_lse;
     float* out;
     float* lse;
 };
@@ -57,6 +68,10 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
+// Stream-mode kernel functions (for occupancy queries).
+const void* mfma_stream_kernel(int m, bool paged);
+const void* valu_stream_kernel(int m, bool paged);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int d, int capacity,

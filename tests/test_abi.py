@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import kv_cache_gqa_amd as kvc
 import kvc_workloads as W
@@ -50,23 +51,31 @@ def test_status_strings_and_version():
 
 def test_plan_auto_and_explicit():
     # explicit 64 splits over 131073 positions: chunks of 2080 (a multiple of 32)
-    assert kvc.plan(4, 32, 1, 128, 131073 + 15, 64) == (2080, 64)
-    # one chunk when splitting is not asked for and the grid is already large
-    cl, nc = kvc.plan(1024, 8, 8, 128, 512, 0)
-    assert nc == 1 and cl == 512
-    # auto: every chunk is a multiple of 32, covers max_seq_len, and <= 4096
+    assert kvc.plan(4, 32, 1, 128, 131073 + 15, 64) == ("chunks", 2080, 64)
+    # automatic split for the bf16 head_dim-128 kernels: persistent stream grid
+    for (B, h, g, T) in [(8, 32, 32, 2064), (32, 64, 8, 4112), (64, 32, 8, 8208), (4, 32, 1, 131088)]:
+        assert kvc.plan(B, h, g, 128, T, 0) == ("stream", 0, 0)
+    # ... but chunks for the generic kernel (fp32, other head dims, m > 32) and large batches
+    assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
+    assert kvc.plan(2, 64, 1, 128, 4096, 0)[0] == "chunks"
+    assert kvc.plan(2048, 8, 8, 128, 512, 0)[0] == "chunks"
+    # chunks: a multiple of 32, covering max_seq_len, at most 4096
     for (B, h, g, T) in [(8, 32, 32, 2064), (32, 64, 8, 4112), (64, 32, 8, 8208), (4, 32, 1, 131088),
                          (1, 4, 2, 48)]:
-        cl, nc = kvc.plan(B, h, g, 128, T, 0)
-        assert cl % 32 == 0 and cl * nc >= T and cl * (nc - 1) < T and cl <= 4096
+        for ns in (1, 3, 8, 64):
+            _, cl, nc = kvc.plan(B, h, g, 128, T, ns)
+            assert cl % 32 == 0 and cl * nc >= T and cl * (nc - 1) < T and cl <= 4096
 
 
 def test_workspace_bytes():
-    assert kvc.workspace_bytes(1, 4, 2, 16, 48, 1) == 0
-    cl, nc = kvc.plan(4, 32, 1, 128, 131088, 64)
+    assert kvc.workspace_bytes(1, 4, 2, 16, 48, 1, dtype=torch.float32) == 0
+    _, cl, nc = kvc.plan(4, 32, 1, 128, 131088, 64)
     rows = 4 * 32 * nc
     expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert kvc.workspace_bytes(4, 32, 1, 128, 131088, 64) == expect
+    # stream mode: two records of m rows for each of at most 1024 work-groups
+    rows = 1024 * 2 * 8
+    assert kvc.workspace_bytes(32, 64, 8, 128, 4112, 0) == rows * 128 * 4 + rows * 4
 
 
 def _decode(lib, **kw):
@@ -91,7 +100,7 @@ def test_decode_validation_codes():
     assert _decode(lib, d=300) == UNSUPPORTED
     assert _decode(lib, dtype=7) == UNSUPPORTED
     assert _decode(lib, splits=2, ws=None, wsb=0) == WORKSPACE   # plan needs a workspace
-    need = lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 64, 2)
+    need = lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2)
     assert need > 0
     assert _decode(lib, splits=2, ws=FAKE, wsb=need - 1) == WORKSPACE
     assert _decode(lib, B=0) == OK                        # nothing to do, nothing launched

@@ -123,7 +123,8 @@ def test_workload_needles(name):
     x = W.make_contiguous(w, lengths=lengths)
     Lafter = x["seq_lens_after"]
     max_len = int(x["t_cap"]) if not w.paged else int(W.block_counts(Lafter, 16).max()) * 16
-    cl, _ = kvc.plan(w.B, w.h, w.g, w.d, max_len, w.num_splits)
+    _, cl, _ = kvc.plan(w.B, w.h, w.g, w.d, max_len, w.num_splits)
+    cl = cl or 2049  # stream mode cuts anywhere: probe odd offsets too
     special = [0, -1, -2, 15, 16, 31, 32, 33, 127, 128, cl - 1, cl, 2 * cl - 1, 2 * cl, 3 * cl + 16]
     pos = needle_positions(lengths, w.g, special, seed=w.seed)
     plant_needles_contig(x, pos)
