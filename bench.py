@@ -125,10 +125,11 @@ def main():
         max_len = bt.shape[1] * x["block_size"]
     else:
         max_len = k0.shape[2]
-    ws_bytes = kvc.workspace_bytes(w.B, w.h, w.g, w.d, max_len, ns, dtype=w.torch_dtype)
+    ws_bytes = kvc.workspace_bytes(w.B, w.h, w.g, w.d, max_len, ns, dtype=w.torch_dtype,
+                                   paged=w.paged)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     split_mode, chunk_len, num_chunks = kvc.plan(w.B, w.h, w.g, w.d, max_len, ns,
-                                                 dtype=w.torch_dtype)
+                                                 dtype=w.torch_dtype, paged=w.paged)
 
     def append_call(i):
         kc, vc = ks[i % copies], vs[i % copies]

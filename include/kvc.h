@@ -63,7 +63,8 @@ extern "C" {
 
 typedef enum kvc_status {
     KVC_OK = 0,
-    KVC_ERR_INVALID = 1,      /* null pointer, non-positive size, h % g != 0, bad block size */
+    KVC_ERR_INVALID = 1,      /* null pointer, non-positive size, h % g != 0, bad block size,
+                                 num_splits < -1 */
     KVC_ERR_UNSUPPORTED = 2,  /* dtype or head_dim not built (head_dim must be 1..256) */
     KVC_ERR_WORKSPACE = 3,    /* workspace missing or smaller than kvc_decode_workspace_bytes */
     KVC_ERR_HIP = 4           /* a HIP launch reported an error */
@@ -108,30 +109,41 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
  * [0, L) may be cut into position ranges whose partial (O, lse) results
  * combine exactly by log-sum-exp ([P4] 2.2-2.5).  Every work-group serves
  * all m = h/g query heads of its KV head, so every K/V byte is read once.
+ * num_splits selects the split:
  *
- *   num_splits = 0 (automatic): for the bf16 head_dim-128 kernels and
- *     B <= 1024, a persistent grid of as many work-groups as the device
- *     keeps resident (KVC_SPLIT_STREAM); all (sequence, KV head) ranges are
- *     laid end to end and every work-group takes an equal share of the
- *     positions, so ragged lengths stay balanced.  Otherwise chunks.
- *   num_splits > 0: every sequence's positions are cut into chunks of
- *     chunk_len (a multiple of 32) so that about num_splits chunks cover
- *     max_seq_len (KVC_SPLIT_CHUNKS); each (chunk, sequence, KV head) is one
- *     work-group.
- * When results are split, partials go to the caller's workspace and a
- * second kernel merges them.
+ *   0 (automatic)
+ *     contiguous cache: chunks (KVC_SPLIT_AUTO_CHUNKS); the number of chunks
+ *       per (sequence, KV head) is chosen at launch so that the work-groups
+ *       fill the device's resident work-group slots once (compute units x
+ *       work-groups per CU that the kernel's registers and LDS allow).
+ *     paged cache: stream mode (KVC_SPLIT_STREAM, below), which stays
+ *       balanced whatever the mix of sequence lengths.
+ *   KVC_SPLITS_STREAM (-1): stream mode for any layout.  A persistent grid of
+ *     as many work-groups as the device keeps resident; all (sequence, KV
+ *     head) ranges are laid end to end and every work-group takes an equal
+ *     share of the positions.
+ *   n > 0: chunks of chunk_len positions (a multiple of 32) so that about n
+ *     chunks cover max_seq_len (KVC_SPLIT_CHUNKS); each (chunk, sequence, KV
+ *     head) is one work-group.
+ * Stream mode needs the bf16 head_dim-128 kernels, B <= 1024 and
+ * B * g * max_seq_len < 2^40; otherwise the automatic choice is chunks.
+ * When results are split, partials go to the workspace and a second kernel
+ * merges them.
  *
- * kvc_decode_plan reports the mode and, for chunks, chunk_len and the chunk
- * count.  kvc_decode_workspace_bytes returns the workspace the decode call
- * needs for the same arguments (0 if none).  max_seq_len is t_cap for the
- * contiguous entry point and max_blocks * block_size for the paged one.
- * Both are pure host arithmetic.
+ * kvc_decode_plan reports the mode and, for KVC_SPLIT_CHUNKS, chunk_len and
+ * the chunk count (0 for the other modes).  kvc_decode_workspace_bytes
+ * returns the workspace the decode call needs for the same arguments (0 if
+ * none); for the automatic chunk count it covers the largest count any
+ * device can select.  max_seq_len is t_cap for the contiguous entry point
+ * and max_blocks * block_size for the paged one; paged is 0 or 1.  Both are
+ * pure host arithmetic.
  */
-enum { KVC_SPLIT_CHUNKS = 0, KVC_SPLIT_STREAM = 1 };
+enum { KVC_SPLITS_STREAM = -1 };
+enum { KVC_SPLIT_CHUNKS = 0, KVC_SPLIT_STREAM = 1, KVC_SPLIT_AUTO_CHUNKS = 2 };
 int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
-                    int* mode, int* chunk_len, int* num_chunks);
+                    int paged, int* mode, int* chunk_len, int* num_chunks);
 size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max_seq_len,
-                                  int num_splits);
+                                  int num_splits, int paged);
 
 /*
  * kvc_decode_attention -- decode attention over a contiguous cache.
@@ -145,8 +157,10 @@ size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max
  *   scale        multiplies every q.k (usually 1/sqrt(d))
  *   num_splits   see "Work split"
  *   workspace    device buffer of at least kvc_decode_workspace_bytes(B, h, g,
- *                d, dtype, t_cap, num_splits) bytes (may be NULL when that is
- *                0); its contents need no initialisation
+ *                d, dtype, t_cap, num_splits, 0) bytes (may be NULL when that
+ *                is 0); no initialisation needed.  Calls that share a
+ *                workspace must not overlap in time (same stream, or
+ *                synchronised).
  *   out          [B, h, d] float32; lse [B, h] float32 (natural log).
  *   A sequence of length 0 gets out = 0 and lse = -inf.
  */
@@ -167,7 +181,7 @@ int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache
  *   block_size      power of two, 8..256
  *   seq_lens        device int32 [B], 0..max_blocks*block_size
  *   other arguments as kvc_decode_attention; the workspace size uses
- *   max_seq_len = max_blocks * block_size.
+ *   max_seq_len = max_blocks * block_size and paged = 1.
  */
 int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, int max_blocks, int block_size,

@@ -23,10 +23,12 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["append", "decode", "decode_paged", "plan", "workspace_bytes", "KvcError",
-           "load_library", "LIB_PATH", "F32", "BF16"]
+           "load_library", "LIB_PATH", "F32", "BF16", "SPLITS_STREAM"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
 F32, BF16 = 0, 1
+SPLITS_STREAM = -1  # num_splits value that asks for the stream split
+_MODES = {0: "chunks", 1: "stream", 2: "auto_chunks"}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype or shape",
            3: "workspace missing or too small", 4: "HIP launch error"}
 
@@ -54,10 +56,10 @@ def load_library():
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_append.argtypes = [vp, vp, vp, vp, vp, ip, ip, vp, ip, ip, ip, ip, ip, vp]
     lib.kvc_append.restype = ip
-    lib.kvc_decode_plan.argtypes = [ip, ip, ip, ip, ip, ip, ip, ctypes.POINTER(ip),
+    lib.kvc_decode_plan.argtypes = [ip, ip, ip, ip, ip, ip, ip, ip, ctypes.POINTER(ip),
                                     ctypes.POINTER(ip), ctypes.POINTER(ip)]
     lib.kvc_decode_plan.restype = ip
-    lib.kvc_decode_workspace_bytes.argtypes = [ip, ip, ip, ip, ip, ip, ip]
+    lib.kvc_decode_workspace_bytes.argtypes = [ip, ip, ip, ip, ip, ip, ip, ip]
     lib.kvc_decode_workspace_bytes.restype = sz
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
@@ -105,21 +107,21 @@ def _code(dtype) -> int:
 
 
 def plan(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0,
-         dtype=torch.bfloat16) -> Tuple[str, int, int]:
-    """(mode, chunk_len, num_chunks) the library uses: mode "stream" (persistent
-    position-balanced grid; chunk fields 0) or "chunks"."""
+         dtype=torch.bfloat16, paged: bool = False) -> Tuple[str, int, int]:
+    """(mode, chunk_len, num_chunks) of the split: mode "chunks" (chunk fields
+    set), "auto_chunks" (count chosen at launch) or "stream"."""
     lib = load_library()
     mode, cl, nc = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     _check("kvc_decode_plan", lib.kvc_decode_plan(B, h, g, d, _code(dtype), max_seq_len, num_splits,
-                                                  ctypes.byref(mode), ctypes.byref(cl),
+                                                  int(paged), ctypes.byref(mode), ctypes.byref(cl),
                                                   ctypes.byref(nc)))
-    return ("stream" if mode.value == 1 else "chunks"), cl.value, nc.value
+    return _MODES[mode.value], cl.value, nc.value
 
 
 def workspace_bytes(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0,
-                    dtype=torch.bfloat16) -> int:
+                    dtype=torch.bfloat16, paged: bool = False) -> int:
     return int(load_library().kvc_decode_workspace_bytes(B, h, g, d, _code(dtype), max_seq_len,
-                                                         num_splits))
+                                                         num_splits, int(paged)))
 
 
 def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, stream=None):
@@ -171,7 +173,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, num_spl
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
-    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, t_cap, num_splits), q,
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, t_cap, num_splits, 0), q,
                          workspace)
     st = lib.kvc_decode_attention(
         _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
@@ -195,7 +197,7 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
-    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, mb * bs, num_splits), q,
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, mb * bs, num_splits, 1), q,
                          workspace)
     st = lib.kvc_decode_attention_paged(
         _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype), _dev(v_pool, "v_pool", q.dtype),

@@ -362,8 +362,17 @@ struct MfmaEngine {
 
 }  // namespace
 
+// Two resident wavefronts per SIMD for the 16-query variant: the register
+// allocator is asked to fit 256 registers (it does, without spills, with the
+// accumulators in arch VGPRs).  The 32-query variant would spill and keeps
+// one wavefront per SIMD.
+template <int NQT>
+struct MfmaOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 2 : 1; };
+
 template <int NQT, bool PAGED>
-__global__ void __launch_bounds__(256) decode_mfma_chunked(DecodeArgs a) {
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
+decode_mfma_chunked(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -376,12 +385,13 @@ __global__ void __launch_bounds__(256) decode_mfma_chunked(DecodeArgs a) {
 }
 
 template <int NQT, bool PAGED>
-__global__ void __launch_bounds__(256) decode_mfma_stream(DecodeArgs a) {
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
+decode_mfma_stream(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
-    __shared__ long long part[256];
-    stream_prefix(a, cum, part);
+    stream_prefix(a, cum);
     stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
         E::segment(a, sh, b, j, s, e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
     });
@@ -417,6 +427,12 @@ const void* mfma_stream_kernel(int m, bool paged) {
     if (m > 16)
         return paged ? (const void*)decode_mfma_stream<2, true> : (const void*)decode_mfma_stream<2, false>;
     return paged ? (const void*)decode_mfma_stream<1, true> : (const void*)decode_mfma_stream<1, false>;
+}
+
+const void* mfma_chunked_kernel(int m, bool paged) {
+    if (m > 16)
+        return paged ? (const void*)decode_mfma_chunked<2, true> : (const void*)decode_mfma_chunked<2, false>;
+    return paged ? (const void*)decode_mfma_chunked<1, true> : (const void*)decode_mfma_chunked<1, false>;
 }
 
 }  // namespace kvc

@@ -29,7 +29,7 @@ constexpr int kD = 128;
 constexpr int kWaves = 4;
 
 #ifndef KVC_VALU_PREFETCH
-#define KVC_VALU_PREFETCH 0
+#define KVC_VALU_PREFETCH 1
 #endif
 
 template <int M, bool PAGED>
@@ -250,8 +250,7 @@ __global__ void __launch_bounds__(256) decode_valu_stream(DecodeArgs a) {
     using E = ValuEngine<M, PAGED>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
-    __shared__ long long part[256];
-    stream_prefix(a, cum, part);
+    stream_prefix(a, cum);
     stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
         E::segment(a, sh, b, j, s, e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
     });
@@ -286,6 +285,14 @@ const void* valu_stream_kernel(int m, bool paged) {
         case 1: return paged ? (const void*)decode_valu_stream<1, true> : (const void*)decode_valu_stream<1, false>;
         case 2: return paged ? (const void*)decode_valu_stream<2, true> : (const void*)decode_valu_stream<2, false>;
         default: return paged ? (const void*)decode_valu_stream<3, true> : (const void*)decode_valu_stream<3, false>;
+    }
+}
+
+const void* valu_chunked_kernel(int m, bool paged) {
+    switch (m) {
+        case 1: return paged ? (const void*)decode_valu_chunked<1, true> : (const void*)decode_valu_chunked<1, false>;
+        case 2: return paged ? (const void*)decode_valu_chunked<2, true> : (const void*)decode_valu_chunked<2, false>;
+        default: return paged ? (const void*)decode_valu_chunked<3, true> : (const void*)decode_valu_chunked<3, false>;
     }
 }
 

@@ -7,6 +7,10 @@
 
 #include "kvc_internal.h"
 
+#ifndef KVC_STREAM_WG_CAP
+#define KVC_STREAM_WG_CAP kStreamMaxWgPerCu
+#endif
+
 namespace kvc {
 
 static long ceil_div(long a, long b) { return (a + b - 1) / b; }
@@ -41,32 +45,69 @@ KernelKind choose_kernel(int dtype, int d, int m) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // A decode launch: the kernel family and how positions are split.
+//   stream       persistent position-balanced grid (paged caches, or asked for)
+//   auto_chunks  contiguous cache, automatic: as many chunks per (sequence, KV
+//                head) as fill the resident work-group slots once; the count
+//                is fixed at launch from the device (workspace sized for the
+//                largest possible count)
+//   otherwise    chunks from num_splits (or the generic kernel's heuristic)
 struct Schedule {
     KernelKind kind;
-    bool stream;  // persistent, position-balanced grid (automatic split)
-    Plan plan;    // chunked mode
+    bool stream;
+    bool auto_chunks;
+    Plan plan;
 };
 
+static long clamp_chunks(long C, int max_seq_len) {
+    const long lo = ceil_div(max_seq_len, kMaxChunk);
+    const long hi = ceil_div(max_seq_len, kTileTokens);
+    if (C < lo) C = lo;
+    if (C > hi) C = hi;
+    return C < 1 ? 1 : C;
+}
+
+static Plan plan_for_chunks(int max_seq_len, long C) {
+    if (max_seq_len <= 0) return Plan{kTileTokens, 1};
+    long chunk = ceil_div(ceil_div(max_seq_len, C), kTileTokens) * kTileTokens;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    return Plan{(int)chunk, (int)ceil_div(max_seq_len, chunk)};
+}
+
+// Chunks per (sequence, KV head) that fill `slots` work-group slots once.
+static long chunks_for_slots(long slots, int B, int g, int max_seq_len) {
+    const long units = (long)B * g;
+    return clamp_chunks(ceil_div(slots, units > 0 ? units : 1), max_seq_len);
+}
+
 static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq_len,
-                              int num_splits) {
+                              int num_splits, bool paged) {
     Schedule sc;
     sc.kind = choose_kernel(dtype, d, h / g);
     // Stream mode keeps global positions in 64-bit products p * total with
     // p <= 1024: it is used only while B * g * max_seq_len < 2^40.
     const bool small_enough = (long double)B * g * max_seq_len < (long double)(1LL << 40);
-    sc.stream = num_splits == 0 && sc.kind != kGeneric && B <= kStreamMaxB && small_enough;
-    sc.plan = make_plan(B, g, max_seq_len, num_splits);
+    const bool can_stream = sc.kind != kGeneric && B <= kStreamMaxB && small_enough;
+    sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM || (num_splits == 0 && paged));
+    sc.auto_chunks = !sc.stream && num_splits <= 0 && sc.kind != kGeneric;
+    if (sc.auto_chunks) {
+        // workspace bound: every slot of a 256-CU device, 4 work-groups each
+        sc.plan = plan_for_chunks(max_seq_len, chunks_for_slots((long)kStreamMaxCUs * kStreamMaxWgPerCu,
+                                                                 B, g, max_seq_len));
+    } else {
+        sc.plan = make_plan(B, g, max_seq_len, num_splits > 0 ? num_splits : 0);
+    }
     return sc;
 }
 
+// Workspace layout: partial O rows | partial lse rows.
+static size_t workspace_rows(int B, int h, int g, const Schedule& sc) {
+    if (sc.stream) return (size_t)kStreamMaxCUs * kStreamMaxWgPerCu * 2 * (size_t)(h / g);
+    return sc.plan.num_chunks <= 1 ? 0 : (size_t)B * h * sc.plan.num_chunks;
+}
+
 static size_t workspace_for(int B, int h, int g, int d, const Schedule& sc) {
-    size_t rows;
-    if (sc.stream) {
-        rows = (size_t)kStreamMaxCUs * kStreamMaxWgPerCu * 2 * (size_t)(h / g);
-    } else {
-        if (sc.plan.num_chunks <= 1) return 0;
-        rows = (size_t)B * h * sc.plan.num_chunks;
-    }
+    const size_t rows = workspace_rows(B, h, g, sc);
+    if (rows == 0) return 0;
     return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
 }
 
@@ -86,7 +127,7 @@ static int device_cus() {
 // Resident work-groups of 256 threads per compute unit for a kernel (cached).
 static int resident_wgs(const void* fn) {
     struct Entry { const void* fn; int n; };
-    static Entry cache[16] = {};
+    static Entry cache[32] = {};
     for (auto& e : cache)
         if (e.fn == fn) return e.n;
     int n = 0;
@@ -100,6 +141,16 @@ static int resident_wgs(const void* fn) {
     return n;
 }
 
+// Work-group slots of the current device for a kernel: CUs x resident
+// work-groups, capped at 256 CUs x 4 (the workspace bound).
+static long device_slots(const void* fn) {
+    int per_cu = resident_wgs(fn);
+    if (per_cu > KVC_STREAM_WG_CAP) per_cu = KVC_STREAM_WG_CAP;
+    int cus = device_cus();
+    if (cus > kStreamMaxCUs) cus = kStreamMaxCUs;
+    return (long)cus * per_cu;
+}
+
 static int ilog2_exact(int x) {
     int l = 0;
     while ((1 << l) < x) ++l;
@@ -109,7 +160,7 @@ static int ilog2_exact(int x) {
 static int check_common(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                         int B, int h, int g, int d, float scale, int dtype, int num_splits,
                         const float* out, const float* lse) {
-    if (B < 0 || h <= 0 || g <= 0 || d <= 0 || num_splits < 0) return KVC_ERR_INVALID;
+    if (B < 0 || h <= 0 || g <= 0 || d <= 0 || num_splits < KVC_SPLITS_STREAM) return KVC_ERR_INVALID;
     if (h % g != 0) return KVC_ERR_INVALID;
     if (!isfinite(scale)) return KVC_ERR_INVALID;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
@@ -121,36 +172,34 @@ static int check_common(const void* q, const void* k, const void* v, const int32
 
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-    const Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits);
-    a.chunk_len = sc.plan.chunk_len;
-    a.num_chunks = sc.plan.num_chunks;
+    const bool paged = a.block_table != nullptr;
+    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
+    const size_t need = workspace_for(a.B, a.h, a.g, a.d, sc);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+    if (a.B == 0) return KVC_OK;
     a.stream = sc.stream ? 1 : 0;
     a.num_wgs = 0;
-    const size_t need = workspace_for(a.B, a.h, a.g, a.d, sc);
-    if (need > 0) {
-        if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
-        const size_t rows = sc.stream ? (size_t)kStreamMaxCUs * kStreamMaxWgPerCu * 2 * a.m
-                                      : (size_t)a.B * a.h * sc.plan.num_chunks;
-        a.part_o = static_cast<float*>(workspace);
-        a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                              align256(rows * a.d * sizeof(float)));
-    } else {
-        a.part_o = nullptr;
-        a.part_lse = nullptr;
-    }
-    if (a.B == 0) return KVC_OK;
     if (sc.stream) {
-        const bool paged = a.block_table != nullptr;
         const void* fn = sc.kind == kMfma ? mfma_stream_kernel(a.m, paged) : valu_stream_kernel(a.m, paged);
-        int per_cu = resident_wgs(fn);
-        if (per_cu > kStreamMaxWgPerCu) per_cu = kStreamMaxWgPerCu;
-        int cus = device_cus();
-        if (cus > kStreamMaxCUs) cus = kStreamMaxCUs;
-        long P = (long)cus * per_cu;
+        long P = device_slots(fn);
         // No more work-groups than 256-position pieces of the largest possible batch.
         const long pieces = ((long)a.B * a.g * a.cap_len + 255) / 256;
         if (P > pieces) P = pieces;
         a.num_wgs = (int)(P < 1 ? 1 : P);
+    } else if (sc.auto_chunks) {
+        const void* fn = sc.kind == kMfma ? mfma_chunked_kernel(a.m, paged) : valu_chunked_kernel(a.m, paged);
+        sc.plan = plan_for_chunks(max_len, chunks_for_slots(device_slots(fn), a.B, a.g, max_len));
+    }
+    a.chunk_len = sc.plan.chunk_len;
+    a.num_chunks = sc.plan.num_chunks;
+    const size_t rows = workspace_rows(a.B, a.h, a.g, sc);
+    if (rows > 0) {
+        char* w = static_cast<char*>(workspace);
+        a.part_o = reinterpret_cast<float*>(w);
+        a.part_lse = reinterpret_cast<float*>(w + align256(rows * a.d * sizeof(float)));
+    } else {
+        a.part_o = nullptr;
+        a.part_lse = nullptr;
     }
     hipError_t err;
     switch (sc.kind) {
@@ -161,7 +210,7 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
     if (err != hipSuccess) return KVC_ERR_HIP;
     if (sc.stream) {
         if (launch_merge_stream(a, stream) != hipSuccess) return KVC_ERR_HIP;
-    } else if (sc.plan.num_chunks > 1) {
+    } else if (a.num_chunks > 1) {
         if (launch_merge(a, stream) != hipSuccess) return KVC_ERR_HIP;
     }
     return KVC_OK;
@@ -187,23 +236,26 @@ const char* kvc_status_string(int status) {
 }
 
 int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
-                    int* mode, int* chunk_len, int* num_chunks) {
-    if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < 0 || max_seq_len < 0)
+                    int paged, int* mode, int* chunk_len, int* num_chunks) {
+    if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
+        max_seq_len < 0)
         return KVC_ERR_INVALID;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
-    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits);
-    if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : KVC_SPLIT_CHUNKS;
-    if (chunk_len) *chunk_len = sc.stream ? 0 : sc.plan.chunk_len;
-    if (num_chunks) *num_chunks = sc.stream ? 0 : sc.plan.num_chunks;
+    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
+    if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : (sc.auto_chunks ? KVC_SPLIT_AUTO_CHUNKS : KVC_SPLIT_CHUNKS);
+    const bool fixed = !sc.stream && !sc.auto_chunks;
+    if (chunk_len) *chunk_len = fixed ? sc.plan.chunk_len : 0;
+    if (num_chunks) *num_chunks = fixed ? sc.plan.num_chunks : 0;
     return KVC_OK;
 }
 
 size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max_seq_len,
-                                  int num_splits) {
-    if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < 0 || max_seq_len < 0)
+                                  int num_splits, int paged) {
+    if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
+        max_seq_len < 0)
         return 0;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
-    return workspace_for(B, h, g, d, make_schedule(B, h, g, d, dtype, max_seq_len, num_splits));
+    return workspace_for(B, h, g, d, make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0));
 }
 
 int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

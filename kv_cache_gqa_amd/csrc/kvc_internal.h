@@ -72,6 +72,8 @@ hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
 // Stream-mode kernel functions (for occupancy queries).
 const void* mfma_stream_kernel(int m, bool paged);
 const void* valu_stream_kernel(int m, bool paged);
+const void* mfma_chunked_kernel(int m, bool paged);
+const void* valu_chunked_kernel(int m, bool paged);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int d, int capacity,

@@ -34,41 +34,43 @@ __device__ __forceinline__ long long stream_owner(long long x, long long total, 
     return p < P - 1 ? p : P - 1;
 }
 
-// Inclusive prefix sums of the clamped lengths into cum[0..B] (cum[0] = 0),
-// computed by the whole work-group (blockDim.x = 256 threads).  B <=
-// kStreamMaxB.  Ends with a barrier.
-__device__ inline void stream_prefix(const DecodeArgs& a, long long* cum, long long* part) {
+// Prefix sums of the clamped lengths into cum[0..B] (cum[0] = 0), B <=
+// kStreamMaxB.  Wavefront 0 does it: lane l owns sequences [16 l, 16 l + 16),
+// issues all its loads at once, and a shuffle scan across the 64 lanes gives
+// each lane its starting offset.  Called by the whole work-group; ends with
+// a barrier.
+constexpr int kScanPerLane = kStreamMaxB / 64;
+
+__device__ inline void stream_prefix(const DecodeArgs& a, long long* cum) {
     const int tid = threadIdx.x;
-    const int B = a.B;
-    const int per = (B + 255) / 256;
-    const int b0 = tid * per;
-    long long sum = 0;
-    for (int k = 0; k < per; ++k) {
-        const int b = b0 + k;
-        if (b < B) {
-            const long long L = clamp_len(a.seq_lens[b], a.cap_len);
-            sum += L;
-            cum[b + 1] = L;  // lengths for now
+    if (tid < 64) {
+        const int b0 = tid * kScanPerLane;
+        int len[kScanPerLane];
+        // Unconditional loads (index clamped to B - 1, B >= 1) so that all of
+        // them are in flight together; entries past B are zeroed afterwards.
+#pragma unroll
+        for (int k = 0; k < kScanPerLane; ++k) len[k] = a.seq_lens[min(b0 + k, a.B - 1)];
+#pragma unroll
+        for (int k = 0; k < kScanPerLane; ++k)
+            len[k] = b0 + k < a.B ? clamp_len(len[k], a.cap_len) : 0;
+        long long sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanPerLane; ++k) sum += len[k];
+        long long incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += y;
         }
-    }
-    part[tid] = sum;
-    __syncthreads();
-    // Hillis-Steele scan of the 256 per-thread sums.
-    for (int off = 1; off < 256; off <<= 1) {
-        const long long v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    long long run = part[tid] - sum;  // exclusive prefix of this thread's block
-    for (int k = 0; k < per; ++k) {
-        const int b = b0 + k;
-        if (b < B) {
-            run += cum[b + 1];
-            cum[b + 1] = run;
+        long long run = incl - sum;
+#pragma unroll
+        for (int k = 0; k < kScanPerLane; ++k) {
+            const int b = b0 + k;
+            run += len[k];
+            if (b < a.B) cum[b + 1] = run;
         }
+        if (tid == 0) cum[0] = 0;
     }
-    if (tid == 0) cum[0] = 0;
     __syncthreads();
 }
 
@@ -82,6 +84,32 @@ __device__ __forceinline__ int stream_find_seq(const long long* cum, int B, int 
         else hi = mid - 1;
     }
     return lo;
+}
+
+// The work-groups holding partial records of unit (b, j): pa..pb, record slot
+// 1 of pa when pa's range starts before the unit (the unit is then pa's last
+// segment), slot 0 otherwise; work-groups with an empty range hold none.
+struct UnitSpan {
+    long long pa, pb, total, P;
+    bool pa_last;
+    __device__ bool empty(long long q) const {
+        return stream_start(q, total, P) >= stream_start(q + 1, total, P);
+    }
+    __device__ long long record(long long q, int m, int r) const {
+        return (q * 2 + ((q == pa && pa_last) ? 1 : 0)) * m + r;
+    }
+};
+
+__device__ inline UnitSpan unit_span(const DecodeArgs& a, const long long* cum, int b, int j) {
+    UnitSpan sp;
+    const long long L = cum[b + 1] - cum[b];
+    const long long U = (long long)a.g * cum[b] + (long long)j * L;
+    sp.total = (long long)a.g * cum[a.B];
+    sp.P = a.num_wgs;
+    sp.pa = stream_owner(U, sp.total, sp.P);
+    sp.pb = stream_owner(U + L - 1, sp.total, sp.P);
+    sp.pa_last = stream_start(sp.pa, sp.total, sp.P) < U;
+    return sp;
 }
 
 // Walk the segments of work-group p.  `seg(b, j, s, e, complete, slot)` is

@@ -15,9 +15,70 @@
 
 namespace kvc {
 
-// Chunks are consumed eight at a time with all their loads issued together,
-// so the latency of reading a row's partials is paid once per eight chunks.
+// Chunks/records are consumed eight at a time: the lse and O loads of a
+// batch are all issued together and folded in with online rescaling, so a
+// row costs one round trip to memory per eight partial results.
 constexpr int kMergeBatch = 8;
+
+// Lane k holds dims 2k, 2k+1 (d <= 128 and even) or k, k+64, k+128, k+192.
+struct MergeAcc {
+    float M = kNegInf;
+    float wsum = 0.0f;
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Fold in a batch of partial results: lse (base 2) and lane values v.
+    __device__ void add(const float (&lse)[kMergeBatch], const float (&v)[kMergeBatch][4]) {
+        float bm = M;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, lse[k]);
+        const float ref = (bm == kNegInf) ? 0.0f : bm;
+        const float f = fast_exp2(M - ref);  // 0 while nothing was added
+        wsum *= f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) o[kk] *= f;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const float w = fast_exp2(lse[k] - ref);  // -inf -> 0 for absent entries
+            wsum += w;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) o[kk] += w * v[k][kk];
+        }
+        M = bm;
+    }
+};
+
+__device__ __forceinline__ void load_lane(const float* src, bool ok, int lane, int d, bool pairs,
+                                          float (&v)[4]) {
+    if (pairs) {
+        float2 t = make_float2(0.0f, 0.0f);
+        if (ok && 2 * lane < d) t = *reinterpret_cast<const float2*>(src + 2 * lane);
+        v[0] = t.x; v[1] = t.y; v[2] = 0.0f; v[3] = 0.0f;
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int dim = lane + 64 * kk;
+            v[kk] = (ok && dim < d) ? src[dim] : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void write_row(const DecodeArgs& a, long row, int lane, bool pairs,
+                                          const MergeAcc& acc) {
+    const int d = a.d;
+    const float inv = acc.wsum > 0.0f ? 1.0f / acc.wsum : 0.0f;
+    if (pairs) {
+        if (2 * lane < d)
+            *reinterpret_cast<float2*>(a.out + row * d + 2 * lane) =
+                make_float2(acc.o[0] * inv, acc.o[1] * inv);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int dim = lane + 64 * kk;
+            if (dim < d) a.out[row * d + dim] = acc.o[kk] * inv;
+        }
+    }
+    if (lane == 0) a.lse[row] = acc.wsum > 0.0f ? (acc.M + fast_log2(acc.wsum)) * kLn2 : kNegInf;
+}
 
 __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
     const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -28,59 +89,21 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
     const int b = (int)(row / a.h);
     const int L = clamp_len(a.seq_lens[b], a.cap_len);
     const int nc = (L + a.chunk_len - 1) / a.chunk_len;
-    const float* pl = a.part_lse + row * C;
-
-    float M = kNegInf;
-    for (int c = lane; c < nc; c += 64) M = fmaxf(M, pl[c]);
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) M = fmaxf(M, shfl_xor_f(M, mask));
-    const float ref = (M == kNegInf) ? 0.0f : M;
-
-    // Lane k holds dims 2k, 2k+1 (d <= 128, even) or k, k+64, k+128, k+192.
     const bool pairs = (d % 2 == 0) && d <= 128;
-    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float wsum = 0.0f;
-    const float* po = a.part_o + row * C * d;
+    MergeAcc acc;
     for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
-        float w[kMergeBatch], v[kMergeBatch][4];
+        float lse[kMergeBatch], v[kMergeBatch][4];
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
             const int c = c0 + k;
             const bool ok = c < nc;
-            w[k] = ok ? pl[c] : kNegInf;
-            const float* src = po + (long)(ok ? c : 0) * d;
-            if (pairs) {
-                float2 t = make_float2(0.0f, 0.0f);
-                if (ok && 2 * lane < d) t = *reinterpret_cast<const float2*>(src + 2 * lane);
-                v[k][0] = t.x; v[k][1] = t.y; v[k][2] = 0.0f; v[k][3] = 0.0f;
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int dim = lane + 64 * kk;
-                    v[k][kk] = (ok && dim < d) ? src[dim] : 0.0f;
-                }
-            }
+            const long rec = row * C + (ok ? c : 0);
+            lse[k] = ok ? a.part_lse[rec] : kNegInf;
+            load_lane(a.part_o + rec * d, ok, lane, d, pairs, v[k]);
         }
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-            const float wk = fast_exp2(w[k] - ref);  // -inf -> 0 for absent chunks
-            wsum += wk;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) o[kk] += wk * v[k][kk];
-        }
+        acc.add(lse, v);
     }
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    if (pairs) {
-        if (2 * lane < d)
-            *reinterpret_cast<float2*>(a.out + row * d + 2 * lane) = make_float2(o[0] * inv, o[1] * inv);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int dim = lane + 64 * kk;
-            if (dim < d) a.out[row * d + dim] = o[kk] * inv;
-        }
-    }
-    if (lane == 0) a.lse[row] = wsum > 0.0f ? (M + fast_log2(wsum)) * kLn2 : kNegInf;
+    write_row(a, row, lane, pairs, acc);
 }
 
 // Stream mode: unit u = (b, j) occupies global positions [U, U + L).  If its
@@ -136,56 +159,20 @@ __global__ void __launch_bounds__(256) merge_stream_kernel(DecodeArgs a) {
         return stream_start(q, total, P) >= stream_start(q + 1, total, P);
     };
 
-    float M = kNegInf;
-    for (long long q = pa + lane; q <= pb; q += 64)
-        if (!empty(q)) M = fmaxf(M, a.part_lse[rec(q)]);
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) M = fmaxf(M, shfl_xor_f(M, mask));
-    const float ref = (M == kNegInf) ? 0.0f : M;
-
-    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float wsum = 0.0f;
+    MergeAcc acc;
     for (long long q0 = pa; q0 <= pb; q0 += kMergeBatch) {
-        float w[kMergeBatch], v[kMergeBatch][4];
+        float lse[kMergeBatch], v[kMergeBatch][4];
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
             const long long q = q0 + k;
             const bool ok = q <= pb && !empty(q);
             const long long rr = ok ? rec(q) : 0;
-            w[k] = ok ? a.part_lse[rr] : kNegInf;
-            const float* src = a.part_o + rr * d;
-            if (pairs) {
-                float2 t = make_float2(0.0f, 0.0f);
-                if (ok && 2 * lane < d) t = *reinterpret_cast<const float2*>(src + 2 * lane);
-                v[k][0] = t.x; v[k][1] = t.y; v[k][2] = 0.0f; v[k][3] = 0.0f;
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int dim = lane + 64 * kk;
-                    v[k][kk] = (ok && dim < d) ? src[dim] : 0.0f;
-                }
-            }
+            lse[k] = ok ? a.part_lse[rr] : kNegInf;
+            load_lane(a.part_o + rr * d, ok, lane, d, pairs, v[k]);
         }
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-            const float wk = fast_exp2(w[k] - ref);
-            wsum += wk;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) o[kk] += wk * v[k][kk];
-        }
+        acc.add(lse, v);
     }
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    if (pairs) {
-        if (2 * lane < d)
-            *reinterpret_cast<float2*>(a.out + row * d + 2 * lane) = make_float2(o[0] * inv, o[1] * inv);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int dim = lane + 64 * kk;
-            if (dim < d) a.out[row * d + dim] = o[kk] * inv;
-        }
-    }
-    if (lane == 0) a.lse[row] = wsum > 0.0f ? (M + fast_log2(wsum)) * kLn2 : kNegInf;
+    write_row(a, row, lane, pairs, acc);
 }
 
 hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s) {

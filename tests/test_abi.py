@@ -49,16 +49,20 @@ def test_status_strings_and_version():
     assert lib.kvc_version() > 0
 
 
-def test_plan_auto_and_explicit():
+def test_plan_modes():
     # explicit 64 splits over 131073 positions: chunks of 2080 (a multiple of 32)
     assert kvc.plan(4, 32, 1, 128, 131073 + 15, 64) == ("chunks", 2080, 64)
-    # automatic split for the bf16 head_dim-128 kernels: persistent stream grid
+    # automatic: contiguous -> chunk count fixed at launch; paged -> stream
     for (B, h, g, T) in [(8, 32, 32, 2064), (32, 64, 8, 4112), (64, 32, 8, 8208), (4, 32, 1, 131088)]:
-        assert kvc.plan(B, h, g, 128, T, 0) == ("stream", 0, 0)
-    # ... but chunks for the generic kernel (fp32, other head dims, m > 32) and large batches
+        assert kvc.plan(B, h, g, 128, T, 0) == ("auto_chunks", 0, 0)
+        assert kvc.plan(B, h, g, 128, T, 0, paged=True) == ("stream", 0, 0)
+        assert kvc.plan(B, h, g, 128, T, kvc.SPLITS_STREAM) == ("stream", 0, 0)
+    # the generic kernel (fp32, other head dims, m > 32) always chunks
     assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
-    assert kvc.plan(2, 64, 1, 128, 4096, 0)[0] == "chunks"
-    assert kvc.plan(2048, 8, 8, 128, 512, 0)[0] == "chunks"
+    assert kvc.plan(2, 64, 1, 128, 4096, 0, paged=True)[0] == "chunks"
+    assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM)[0] == "chunks"
+    # stream mode needs B <= 1024
+    assert kvc.plan(2048, 8, 8, 128, 512, 0, paged=True)[0] == "auto_chunks"
     # chunks: a multiple of 32, covering max_seq_len, at most 4096
     for (B, h, g, T) in [(8, 32, 32, 2064), (32, 64, 8, 4112), (64, 32, 8, 8208), (4, 32, 1, 131088),
                          (1, 4, 2, 48)]:
@@ -67,15 +71,22 @@ def test_plan_auto_and_explicit():
             assert cl % 32 == 0 and cl * nc >= T and cl * (nc - 1) < T and cl <= 4096
 
 
+def _ws(rows, d=128):
+    return -(-rows * d * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+
+
 def test_workspace_bytes():
     assert kvc.workspace_bytes(1, 4, 2, 16, 48, 1, dtype=torch.float32) == 0
     _, cl, nc = kvc.plan(4, 32, 1, 128, 131088, 64)
-    rows = 4 * 32 * nc
-    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
-    assert kvc.workspace_bytes(4, 32, 1, 128, 131088, 64) == expect
+    assert kvc.workspace_bytes(4, 32, 1, 128, 131088, 64) == _ws(4 * 32 * nc)
     # stream mode: two records of m rows for each of at most 1024 work-groups
-    rows = 1024 * 2 * 8
-    assert kvc.workspace_bytes(32, 64, 8, 128, 4112, 0) == rows * 128 * 4 + rows * 4
+    assert kvc.workspace_bytes(32, 64, 8, 128, 4112, 0, paged=True) == _ws(1024 * 2 * 8)
+    # automatic chunks: sized for 1024 work-groups -> 4 chunks per (b, j) at B*g = 256
+    assert kvc.workspace_bytes(32, 64, 8, 128, 4112, 0) == _ws(32 * 64 * 4)
+    # B*g = 4: 256 chunks asked, rounded to 544-position chunks -> 241 chunks
+    chunk = -(-(-(-131088 // 256)) // 32) * 32
+    assert chunk == 544
+    assert kvc.workspace_bytes(4, 32, 1, 128, 131088, 0) == _ws(4 * 32 * -(-131088 // chunk))
 
 
 def _decode(lib, **kw):
@@ -96,11 +107,11 @@ def test_decode_validation_codes():
     assert _decode(lib, out=None) == INVALID
     assert _decode(lib, t_cap=0) == INVALID
     assert _decode(lib, scale=float("inf")) == INVALID
-    assert _decode(lib, splits=-1) == INVALID
+    assert _decode(lib, splits=-2) == INVALID
     assert _decode(lib, d=300) == UNSUPPORTED
     assert _decode(lib, dtype=7) == UNSUPPORTED
     assert _decode(lib, splits=2, ws=None, wsb=0) == WORKSPACE   # plan needs a workspace
-    need = lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2)
+    need = lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2, 0)
     assert need > 0
     assert _decode(lib, splits=2, ws=FAKE, wsb=need - 1) == WORKSPACE
     assert _decode(lib, B=0) == OK                        # nothing to do, nothing launched

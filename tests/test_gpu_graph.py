@@ -31,7 +31,7 @@ def test_graph_replay_matches_eager(h, g, paged, splits):
     q, kn, vn = x["q"].to(dev), x["k_new"].to(dev), x["v_new"].to(dev)
     before, after = x["seq_lens_before"].to(dev), x["seq_lens_after"].to(dev)
     max_len = bt.shape[1] * 16 if paged else kc.shape[2]
-    ws = torch.empty(max(1, kvc.workspace_bytes(w.B, h, g, 128, max_len, splits)),
+    ws = torch.empty(max(1, kvc.workspace_bytes(w.B, h, g, 128, max_len, splits, paged=paged)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty(w.B, h, 128, device=dev)
     lse = torch.empty(w.B, h, device=dev)

@@ -38,8 +38,9 @@ def test_stream_contiguous(shape, case):
     L = _lengths(case)
     w = W.Workload(name, B=len(L), h=h, g=g, d=128, dtype="bf16", T=0, seed=500)
     x = W.make_contiguous(w, lengths=L, fill=float("nan"))
-    assert kvc.plan(w.B, h, g, 128, x["t_cap"], 0)[0] == "stream"
-    out, lse = kvc.decode(dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]), dev(L))
+    assert kvc.plan(w.B, h, g, 128, x["t_cap"], kvc.SPLITS_STREAM)[0] == "stream"
+    out, lse = kvc.decode(dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]), dev(L),
+                          num_splits=kvc.SPLITS_STREAM)
     ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
     check_parity(out, lse, ro, rl, attended_vmax_contig(x["v_cache"], L), f"{name}/{case}")
 
@@ -69,7 +70,55 @@ def test_stream_large_batch(shape):
     L = torch.randint(0, 41, (1024,), generator=gen, dtype=torch.int32)
     w = W.Workload(name, B=1024, h=h, g=g, d=128, dtype="bf16", T=0, seed=503)
     x = W.make_contiguous(w, lengths=L, t_cap=48)
-    assert kvc.plan(1024, h, g, 128, 48, 0)[0] == "stream"
-    out, lse = kvc.decode(dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]), dev(L))
+    assert kvc.plan(1024, h, g, 128, 48, kvc.SPLITS_STREAM)[0] == "stream"
+    out, lse = kvc.decode(dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]), dev(L),
+                          num_splits=kvc.SPLITS_STREAM)
     ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
     check_parity(out, lse, ro, rl, attended_vmax_contig(x["v_cache"], L), f"{name}/large_batch")
+
+
+
+LARGE_SHAPES = [("valu_m1_wide", 8, 8, 64), ("mfma_m8_wide", 16, 2, 64), ("mfma_m4_wide", 32, 8, 48)]
+
+
+@pytest.mark.parametrize("shape", LARGE_SHAPES, ids=[s[0] for s in LARGE_SHAPES])
+@pytest.mark.parametrize("paged", [False, True])
+def test_stream_repeated_calls_one_workspace(shape, paged):
+    """Batches where each (sequence, KV head) spans few work-groups; ragged
+    lengths with zeros; five stream-mode calls on one workspace give the
+    oracle's result and identical bits every time."""
+    name, h, g, B = shape
+    print(f"case stream_repeat {name} paged={paged}", file=sys.stderr, flush=True)
+    gen = torch.Generator().manual_seed(504)
+    L = torch.randint(1, 3000, (B,), generator=gen, dtype=torch.int32)
+    L[::7] = 0
+    w = W.Workload(name, B=B, h=h, g=g, d=128, dtype="bf16", T=0, paged=paged, seed=505)
+    if paged:
+        x = W.make_paged(w, lengths=L, fill=float("nan"))
+        kc, vc, bt = dev(x["k_pool"]), dev(x["v_pool"]), dev(x["block_table"])
+        max_len = x["block_table"].shape[1] * 16
+        ro, rl = oracle.decode(x["q"], x["k_pool"], x["v_pool"], L, x["scale"],
+                               block_table=x["block_table"], block_size=16)
+        vmax = attended_vmax_paged(x["v_pool"], x["block_table"], L, 16)
+    else:
+        x = W.make_contiguous(w, lengths=L, fill=float("nan"))
+        kc, vc, bt = dev(x["k_cache"]), dev(x["v_cache"]), None
+        max_len = x["t_cap"]
+        ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+        vmax = attended_vmax_contig(x["v_cache"], L)
+    ns = kvc.SPLITS_STREAM
+    assert kvc.plan(B, h, g, 128, max_len, ns, paged=paged)[0] == "stream"
+    ws = torch.empty(kvc.workspace_bytes(B, h, g, 128, max_len, ns, paged=paged), dtype=torch.uint8,
+                     device="cuda")
+    q, sl = dev(x["q"]), dev(L)
+    first = None
+    for call in range(5):
+        if paged:
+            out, lse = kvc.decode_paged(q, kc, vc, bt, sl, num_splits=ns, workspace=ws)
+        else:
+            out, lse = kvc.decode(q, kc, vc, sl, num_splits=ns, workspace=ws)
+        check_parity(out, lse, ro, rl, vmax, f"{name}/call{call}")
+        if first is None:
+            first = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out, first[0]) and torch.equal(lse, first[1]), f"call {call}"
