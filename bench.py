@@ -17,6 +17,8 @@ Prints one JSON line.  The KV caches rotate over enough copies (>= 3 and
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +29,101 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's kernel and ABI sources: a stored traffic
+    figure is valid only for the sources it was measured on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_gqa_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    files.append(os.path.join(ROOT, "include", "kvc.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_{workload}_hbm_traffic.txt")
+
+
+def _is_decode_call_kernel(name: str) -> bool:
+    return name.startswith("void kvc::decode_") or name.startswith("kvc::merge")
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, calib_mib: int, commands):
+    """Turn two rocprofv3 --pmc runs of `bench.py --eager --calibration-copy-mib N`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into the stored HBM
+    traffic of one decode call.  The counters are scaled by what they read
+    for the calibration copy (a plain device-to-device copy of N MiB: N MiB
+    read and N MiB written)."""
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        return {int(r["Dispatch_Id"]): (r["Kernel_Name"], float(r["Counter_Value"])) for r in rows}
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    calib = calib_mib * 2**20
+    copies = [d for d, (n, v) in write.items()
+              if "copyBuffer" in n and abs(v * 1024 - calib) <= 0.02 * calib]
+    if len(copies) != 1 or copies[0] not in fetch or "copyBuffer" not in fetch[copies[0]][0]:
+        raise SystemExit(f"calibration copy of {calib} bytes not found exactly once in both runs")
+    c = copies[0]
+    fetch_factor = calib / (fetch[c][1] * 1024)
+    write_factor = calib / (write[c][1] * 1024)
+    per = {}
+    for tab, key in ((fetch, "fetch"), (write, "write")):
+        for d, (n, v) in tab.items():
+            if _is_decode_call_kernel(n):
+                e = per.setdefault(n, {"fetch": [], "write": []})
+                e[key].append(v)
+    decode_names = [n for n in per if n.startswith("void kvc::decode_")]
+    if len(decode_names) != 1:
+        raise SystemExit(f"expected one decode kernel, found {decode_names}")
+    calls = len(per[decode_names[0]]["fetch"])
+    fetch_b = sum(sum(e["fetch"]) for e in per.values()) * 1024 * fetch_factor / calls
+    write_b = sum(sum(e["write"]) for e in per.values()) * 1024 * write_factor / calls
+    lines = [f"# HBM traffic of one decode call, workload {workload}",
+             "# rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by the same",
+             "# counters over a plain device-to-device copy of known size.",
+             "# commands (from the repository root):"]
+    lines += [f"#   {cmd}" for cmd in commands]
+    for n, e in sorted(per.items()):
+        lines.append(f"# kernel {n}: {len(e['fetch'])} dispatches, FETCH_SIZE avg "
+                     f"{sum(e['fetch']) / max(len(e['fetch']), 1):.1f} KiB, WRITE_SIZE avg "
+                     f"{sum(e['write']) / max(len(e['write']), 1):.1f} KiB")
+    lines += [f"calibration_copy_bytes: {calib}",
+              f"calibration_fetch_kib: {fetch[c][1]:.1f}",
+              f"calibration_write_kib: {write[c][1]:.1f}",
+              f"fetch_factor: {fetch_factor:.4f}",
+              f"write_factor: {write_factor:.4f}",
+              f"decode_call_kernels: {'; '.join(sorted(per))}",
+              f"fetch_bytes_per_call: {fetch_b:.0f}",
+              f"write_bytes_per_call: {write_b:.0f}",
+              f"traffic_bytes_per_call: {fetch_b + write_b:.0f}",
+              f"source_sha256: {kernel_source_hash()}"]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per decode call from the stored counter runs, or None when
+    there are none or the kernel sources changed since they were taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_call"])
 
 
 def algorithmic_bytes(w, lengths_after, nblocks=None):
@@ -80,7 +177,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before warm-up, copy this many MiB device-to-device once (a plain copy "
+                         "of known size for scaling hardware byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
+                         "an --eager --calibration-copy-mib run into the stored traffic figure")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize-pmc: a command line to record in the summary")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.calibration_copy_mib or 1024, args.command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -130,6 +240,19 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     split_mode, chunk_len, num_chunks = kvc.plan(w.B, w.h, w.g, w.d, max_len, ns,
                                                  dtype=w.torch_dtype, paged=w.paged)
+    waves, n_wgs, launch_chunk, launch_chunks = kvc.launch_shape(
+        w.B, w.h, w.g, w.d, max_len, ns, dtype=w.torch_dtype, paged=w.paged)
+    merged = split_mode == "stream" or launch_chunks > 1
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
 
     def append_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
@@ -188,20 +311,32 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # The dominant kernel(s): K decode calls back to back on the launch
-    # stream, HIP events around each call.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        evs[i][0].record()
-        decode_call(i)
-        evs[i][1].record()
+    # The dominant kernel: decode calls alone, back to back on the launch
+    # stream (a HIP graph holding one call per cache copy, replayed until at
+    # least K calls ran), between two HIP events on that stream.
+    reps = -(-args.steps // copies)
+    if graphs:
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            for r in range(copies):
+                decode_call(r)
+        dgraph.replay()
+        torch.cuda.synchronize()
+    d_start = torch.cuda.Event(enable_timing=True)
+    d_end = torch.cuda.Event(enable_timing=True)
+    d_start.record()
+    for i in range(reps):
+        if graphs:
+            dgraph.replay()
+        else:
+            for r in range(copies):
+                decode_call(r)
+    d_end.record()
     torch.cuda.synchronize()
-    dec_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
-    dec_med_ms = dec_ms[len(dec_ms) // 2]
+    dec_avg_ms = d_start.elapsed_time(d_end) / (reps * copies)
 
     nbytes = algorithmic_bytes(w, x["seq_lens_after"], nblocks)
+    traffic = stored_traffic(w.name)
     achieved_gbs = nbytes["decode"] / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.B / (ms_per_step * 1e-3)
 
@@ -229,16 +364,21 @@ def main():
             "paged": w.paged, "block_size": w.block_size if w.paged else None,
             "num_splits": ns, "split": split_mode, "chunk_len": chunk_len,
             "num_chunks": num_chunks,
+            "launch": {"waves_per_workgroup": waves, "workgroups": n_wgs,
+                       "chunk_len": launch_chunk, "chunks": launch_chunks},
             "cache_copies_rotated": copies, "parallelism": "single GPU",
         },
         "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
-        "decode_ms_median": round(dec_med_ms, 5),
         "timing": "eager" if args.eager else "HIP graph per step",
         "roofline": {
-            "bound": "hbm", "kernel": "decode (partials + log-sum-exp merge)",
+            "bound": "hbm",
+            "kernel": "decode call: " + ("partials + log-sum-exp merge" if merged
+                                         else "one kernel, no merge"),
             "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_launch": nbytes["decode"], "traffic": None,
+            "algorithmic_bytes_per_launch": nbytes["decode"],
+            "decode_call_ms_avg": round(dec_avg_ms, 5),
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
     }

@@ -112,10 +112,15 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
  * num_splits selects the split:
  *
  *   0 (automatic)
- *     contiguous cache: chunks (KVC_SPLIT_AUTO_CHUNKS); the number of chunks
- *       per (sequence, KV head) is chosen at launch so that the work-groups
- *       fill the device's resident work-group slots once (compute units x
- *       work-groups per CU that the kernel's registers and LDS allow).
+ *     contiguous cache: chunks (KVC_SPLIT_AUTO_CHUNKS) chosen at launch from
+ *       the device's resident work-group slots (compute units x work-groups
+ *       per CU that the kernel's registers and LDS allow).  For the MFMA
+ *       kernel with 4 <= h/g <= 16, when there are at least as many
+ *       (sequence, KV head) units as slots of an 8-wavefront work-group
+ *       (and they fill at least 7/8 of the slot rounds), each unit is one
+ *       8-wavefront work-group: one chunk, no merge.  Otherwise
+ *       4-wavefront work-groups take ceil(slots / units) chunks per unit,
+ *       so that they fill the slots once.
  *     paged cache: stream mode (KVC_SPLIT_STREAM, below), which stays
  *       balanced whatever the mix of sequence lengths.
  *   KVC_SPLITS_STREAM (-1): stream mode for any layout.  A persistent grid of
@@ -144,6 +149,19 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
                     int paged, int* mode, int* chunk_len, int* num_chunks);
 size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max_seq_len,
                                   int num_splits, int paged);
+/*
+ * The launch kvc_decode_attention (paged = 0, max_seq_len = t_cap) or
+ * kvc_decode_attention_paged (paged = 1, max_seq_len = max_blocks *
+ * block_size) makes on the current device for these arguments: wavefronts
+ * per work-group, work-groups of the decode kernel, and for the chunked
+ * modes the chunk length and chunk count per (sequence, KV head) (0 in stream
+ * mode).  Resolves the automatic choices, which query the device's
+ * occupancy, so it needs a current HIP device.  Returns KVC_OK, or the
+ * validation status the decode call would return.
+ */
+int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_len,
+                            int num_splits, int paged, int* waves, int* num_wgs,
+                            int* chunk_len, int* num_chunks);
 
 /*
  * kvc_decode_attention -- decode attention over a contiguous cache.

@@ -61,6 +61,8 @@ def load_library():
     lib.kvc_decode_plan.restype = ip
     lib.kvc_decode_workspace_bytes.argtypes = [ip, ip, ip, ip, ip, ip, ip, ip]
     lib.kvc_decode_workspace_bytes.restype = sz
+    lib.kvc_decode_launch_shape.argtypes = [ip] * 8 + [ctypes.POINTER(ip)] * 4
+    lib.kvc_decode_launch_shape.restype = ip
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
     lib.kvc_decode_attention.restype = ip
@@ -122,6 +124,18 @@ def workspace_bytes(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits
                     dtype=torch.bfloat16, paged: bool = False) -> int:
     return int(load_library().kvc_decode_workspace_bytes(B, h, g, d, _code(dtype), max_seq_len,
                                                          num_splits, int(paged)))
+
+
+def launch_shape(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: int = 0,
+                 dtype=torch.bfloat16, paged: bool = False) -> Tuple[int, int, int, int]:
+    """(waves per work-group, work-groups, chunk_len, num_chunks) of the decode
+    launch on the current device (chunk fields 0 in stream mode)."""
+    lib = load_library()
+    out = [ctypes.c_int(0) for _ in range(4)]
+    _check("kvc_decode_launch_shape",
+           lib.kvc_decode_launch_shape(B, h, g, d, _code(dtype), max_seq_len, num_splits, int(paged),
+                                       *(ctypes.byref(x) for x in out)))
+    return tuple(x.value for x in out)
 
 
 def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, stream=None):

@@ -44,16 +44,18 @@ namespace kvc {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
 constexpr int kVRowBytes = kD * 2;                      // 256
 constexpr int kVStageBytes = kTileTokens * kVRowBytes;  // 8 KB per wavefront
 constexpr int kOStride = kD + 4;                        // padded LDS row (floats)
 
-template <int NQT>
+// Shared memory of a W-wavefront work-group: one V stage per wavefront,
+// reused after the walk for the pairwise merge of the wavefront states
+// (W/2 slots at the first level).
+template <int NQT, int W>
 struct Lds {
     static constexpr int kSlotFloats = 16 * NQT * kOStride + 3 * 16 * NQT;
-    static constexpr int kStageBytes = kWaves * kVStageBytes;
-    static constexpr int kMergeBytes = 2 * kSlotFloats * 4;
+    static constexpr int kStageBytes = W * kVStageBytes;
+    static constexpr int kMergeBytes = (W / 2) * kSlotFloats * 4;
     static constexpr int kBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
 };
 
@@ -88,15 +90,16 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 #define KVC_MFMA_PREFETCH 1
 #endif
 
-template <int NQT, bool PAGED>
+template <int NQT, bool PAGED, int W>
 struct MfmaEngine {
+    using L = Lds<NQT, W>;
     struct Shared {
         int tbl[PAGED ? kMaxTableSlice : 1];
-        __attribute__((aligned(16))) unsigned char lds[Lds<NQT>::kBytes];
+        __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     };
 
     // The m query heads of KV head j of sequence b over positions [s, e)
-    // (possibly empty).  Called by all 256 threads.
+    // (possibly empty).  Called by all 64*W threads.
     __device__ static void segment(const DecodeArgs& a, Shared& sh, int b, int j, int s, int e,
                                    const SegDst& dst) {
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -253,13 +256,13 @@ struct MfmaEngine {
             if (PAGED) {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
-                for (int t = tid; t < nblk; t += 256) {
+                for (int t = tid; t < nblk; t += 64 * W) {
                     const int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
                     sh.tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
                 }
                 __syncthreads();
             }
-            const int stride = kWaves * kTileTokens;
+            const int stride = W * kTileTokens;
             int t0 = w0 + wave * kTileTokens;
 #if KVC_MFMA_PREFETCH
             uint4 kA[2][4], vA[8], kB[2][4], vB[8];
@@ -291,9 +294,9 @@ struct MfmaEngine {
             lex[qt] += shfl_xor_f(lex[qt], 32);
         }
 
-        // ---- merge the four wavefronts: (2,3) -> (0,1), then 1 -> 0 ----
-        float* slot0 = reinterpret_cast<float*>(sh.lds);
-        float* slot1 = slot0 + Lds<NQT>::kSlotFloats;
+        // ---- merge the wavefront states pairwise: waves [h, 2h) into
+        // waves [0, h) for h = W/2, ..., 1 ----
+        float* slots = reinterpret_cast<float*>(sh.lds);
         __syncthreads();  // every wavefront is done with its V staging area
         auto store_state = [&](float* slot) {
 #pragma unroll
@@ -329,14 +332,14 @@ struct MfmaEngine {
                 }
             }
         };
-        if (wave >= 2) store_state(wave == 2 ? slot0 : slot1);
-        __syncthreads();
-        if (wave < 2) merge_state(wave == 0 ? slot0 : slot1);
-        __syncthreads();
-        if (wave == 1) store_state(slot0);
-        __syncthreads();
+#pragma unroll
+        for (int half = W / 2; half >= 1; half >>= 1) {
+            if (wave >= half && wave < 2 * half) store_state(slots + (wave - half) * L::kSlotFloats);
+            __syncthreads();
+            if (wave < half) merge_state(slots + wave * L::kSlotFloats);
+            __syncthreads();
+        }
         if (wave == 0) {
-            merge_state(slot0);
             // ---- write: lane holds dims 16*nt + 4G + v of query 16*qt + col ----
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -369,11 +372,11 @@ struct MfmaEngine {
 template <int NQT>
 struct MfmaOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 2 : 1; };
 
-template <int NQT, bool PAGED>
-__global__ void __launch_bounds__(256)
+template <int NQT, bool PAGED, int W>
+__global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
-    using E = MfmaEngine<NQT, PAGED>;
+    using E = MfmaEngine<NQT, PAGED, W>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int L = clamp_len(a.seq_lens[b], a.cap_len);
@@ -384,11 +387,11 @@ decode_mfma_chunked(DecodeArgs a) {
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
 }
 
-template <int NQT, bool PAGED>
-__global__ void __launch_bounds__(256)
+template <int NQT, bool PAGED, int W>
+__global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_stream(DecodeArgs a) {
-    using E = MfmaEngine<NQT, PAGED>;
+    using E = MfmaEngine<NQT, PAGED, W>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
     stream_prefix(a, cum);
@@ -397,42 +400,33 @@ decode_mfma_stream(DecodeArgs a) {
     });
 }
 
-hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
-    const bool paged = a.block_table != nullptr;
-    if (a.m > 32) return hipErrorInvalidValue;
-    const bool two = a.m > 16;
-    if (a.stream) {
-        dim3 grid((unsigned)a.num_wgs);
-        if (two) {
-            if (paged) decode_mfma_stream<2, true><<<grid, dim3(256), 0, s>>>(a);
-            else decode_mfma_stream<2, false><<<grid, dim3(256), 0, s>>>(a);
-        } else {
-            if (paged) decode_mfma_stream<1, true><<<grid, dim3(256), 0, s>>>(a);
-            else decode_mfma_stream<1, false><<<grid, dim3(256), 0, s>>>(a);
+// Kernel function for (m, layout, split mode, wavefronts per work-group);
+// nullptr when that combination is not built.  Every (m, layout, mode) has a
+// 4-wavefront kernel; one tile of query heads (m <= 16) on a contiguous cache
+// also has an 8-wavefront chunked kernel, for whole-unit work-groups.  (Two
+// tiles need more registers than 8 wavefronts per work-group leave.)
+const void* mfma_kernel(int m, bool paged, bool stream, int waves) {
+    const bool two = m > 16;
+    if (waves == 4) {
+        if (stream) {
+            if (two) return paged ? (const void*)decode_mfma_stream<2, true, 4> : (const void*)decode_mfma_stream<2, false, 4>;
+            return paged ? (const void*)decode_mfma_stream<1, true, 4> : (const void*)decode_mfma_stream<1, false, 4>;
         }
-    } else {
-        dim3 grid((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
-        if (two) {
-            if (paged) decode_mfma_chunked<2, true><<<grid, dim3(256), 0, s>>>(a);
-            else decode_mfma_chunked<2, false><<<grid, dim3(256), 0, s>>>(a);
-        } else {
-            if (paged) decode_mfma_chunked<1, true><<<grid, dim3(256), 0, s>>>(a);
-            else decode_mfma_chunked<1, false><<<grid, dim3(256), 0, s>>>(a);
-        }
+        if (two) return paged ? (const void*)decode_mfma_chunked<2, true, 4> : (const void*)decode_mfma_chunked<2, false, 4>;
+        return paged ? (const void*)decode_mfma_chunked<1, true, 4> : (const void*)decode_mfma_chunked<1, false, 4>;
     }
-    return hipGetLastError();
+    if (waves == 8 && !two && !paged && !stream) return (const void*)decode_mfma_chunked<1, false, 8>;
+    return nullptr;
 }
 
-const void* mfma_stream_kernel(int m, bool paged) {
-    if (m > 16)
-        return paged ? (const void*)decode_mfma_stream<2, true> : (const void*)decode_mfma_stream<2, false>;
-    return paged ? (const void*)decode_mfma_stream<1, true> : (const void*)decode_mfma_stream<1, false>;
-}
-
-const void* mfma_chunked_kernel(int m, bool paged) {
-    if (m > 16)
-        return paged ? (const void*)decode_mfma_chunked<2, true> : (const void*)decode_mfma_chunked<2, false>;
-    return paged ? (const void*)decode_mfma_chunked<1, true> : (const void*)decode_mfma_chunked<1, false>;
+hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
+    if (a.m > 32) return hipErrorInvalidValue;
+    const void* fn = mfma_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves);
+    if (fn == nullptr) return hipErrorInvalidValue;
+    const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
+                               : dim3((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
+    void* args[] = {const_cast<DecodeArgs*>(&a)};
+    return hipLaunchKernel(fn, grid, dim3(64 * a.waves), args, 0, s);
 }
 
 }  // namespace kvc

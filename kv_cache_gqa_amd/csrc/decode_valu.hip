@@ -26,23 +26,22 @@ namespace kvc {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
 
 #ifndef KVC_VALU_PREFETCH
 #define KVC_VALU_PREFETCH 1
 #endif
 
-template <int M, bool PAGED>
+template <int M, bool PAGED, int W>
 struct ValuEngine {
     struct Shared {
         int tbl[PAGED ? kMaxTableSlice : 1];
-        float red_m[kWaves][M];
-        float red_l[kWaves][M];
-        float red_o[kWaves][M][kD];
+        float red_m[W][M];
+        float red_l[W][M];
+        float red_o[W][M][kD];
     };
 
     // The M query heads of KV head j of sequence b over positions [s, e)
-    // (possibly empty).  Called by all 256 threads.
+    // (possibly empty).  Called by all 64*W threads.
     __device__ static void segment(const DecodeArgs& a, Shared& sh, int b, int j, int s, int e,
                                    const SegDst& dst) {
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -143,13 +142,13 @@ struct ValuEngine {
             if (PAGED) {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
-                for (int t = tid; t < nblk; t += 256) {
+                for (int t = tid; t < nblk; t += 64 * W) {
                     const int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
                     sh.tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
                 }
                 __syncthreads();
             }
-            const int stride = kWaves * kTileTokens;
+            const int stride = W * kTileTokens;
             int t0 = w0 + wave * kTileTokens;
 #if KVC_VALU_PREFETCH
             uint4 kA[8], vA[8], kB[8], vB[8];
@@ -205,16 +204,16 @@ struct ValuEngine {
         }
         __syncthreads();
 
-        // Merge the four wavefronts and write the rows.
-        for (int idx = tid; idx < M * kD; idx += 256) {
+        // Merge the W wavefronts and write the rows.
+        for (int idx = tid; idx < M * kD; idx += 64 * W) {
             const int r = idx / kD, dim = idx % kD;
             float mm = sh.red_m[0][r];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, sh.red_m[w][r]);
+            for (int w = 1; w < W; ++w) mm = fmaxf(mm, sh.red_m[w][r]);
             const float ref = (mm == kNegInf) ? 0.0f : mm;
             float l = 0.0f, o = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = 0; w < W; ++w) {
                 const float f = fast_exp2(sh.red_m[w][r] - ref);
                 l += sh.red_l[w][r] * f;
                 o += sh.red_o[w][r][dim] * f;
@@ -232,9 +231,9 @@ struct ValuEngine {
 
 }  // namespace
 
-template <int M, bool PAGED>
-__global__ void __launch_bounds__(256) decode_valu_chunked(DecodeArgs a) {
-    using E = ValuEngine<M, PAGED>;
+template <int M, bool PAGED, int W>
+__global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
+    using E = ValuEngine<M, PAGED, W>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int L = clamp_len(a.seq_lens[b], a.cap_len);
@@ -245,9 +244,9 @@ __global__ void __launch_bounds__(256) decode_valu_chunked(DecodeArgs a) {
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
 }
 
-template <int M, bool PAGED>
-__global__ void __launch_bounds__(256) decode_valu_stream(DecodeArgs a) {
-    using E = ValuEngine<M, PAGED>;
+template <int M, bool PAGED, int W>
+__global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
+    using E = ValuEngine<M, PAGED, W>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
     stream_prefix(a, cum);
@@ -257,43 +256,32 @@ __global__ void __launch_bounds__(256) decode_valu_stream(DecodeArgs a) {
 }
 
 template <int M>
-static void launch_valu_m(const DecodeArgs& a, hipStream_t s) {
-    const bool paged = a.block_table != nullptr;
-    if (a.stream) {
-        dim3 grid((unsigned)a.num_wgs);
-        if (paged) decode_valu_stream<M, true><<<grid, dim3(256), 0, s>>>(a);
-        else decode_valu_stream<M, false><<<grid, dim3(256), 0, s>>>(a);
-    } else {
-        dim3 grid((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
-        if (paged) decode_valu_chunked<M, true><<<grid, dim3(256), 0, s>>>(a);
-        else decode_valu_chunked<M, false><<<grid, dim3(256), 0, s>>>(a);
+static const void* valu_pick_m(bool paged, bool stream, int waves) {
+    if (waves != 4) return nullptr;
+    if (stream) return paged ? (const void*)decode_valu_stream<M, true, 4> : (const void*)decode_valu_stream<M, false, 4>;
+    return paged ? (const void*)decode_valu_chunked<M, true, 4> : (const void*)decode_valu_chunked<M, false, 4>;
+}
+
+// Kernel function for (m, layout, split mode, wavefronts per work-group);
+// nullptr when that combination is not built.  Only 4-wavefront kernels: one
+// wide work-group per (sequence, KV head) measured slower than split chunks
+// plus a merge for these kernels (8 and 16 wavefronts, m = 1).
+const void* valu_kernel(int m, bool paged, bool stream, int waves) {
+    switch (m) {
+        case 1: return valu_pick_m<1>(paged, stream, waves);
+        case 2: return valu_pick_m<2>(paged, stream, waves);
+        case 3: return valu_pick_m<3>(paged, stream, waves);
+        default: return nullptr;
     }
 }
 
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s) {
-    switch (a.m) {
-        case 1: launch_valu_m<1>(a, s); break;
-        case 2: launch_valu_m<2>(a, s); break;
-        case 3: launch_valu_m<3>(a, s); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-const void* valu_stream_kernel(int m, bool paged) {
-    switch (m) {
-        case 1: return paged ? (const void*)decode_valu_stream<1, true> : (const void*)decode_valu_stream<1, false>;
-        case 2: return paged ? (const void*)decode_valu_stream<2, true> : (const void*)decode_valu_stream<2, false>;
-        default: return paged ? (const void*)decode_valu_stream<3, true> : (const void*)decode_valu_stream<3, false>;
-    }
-}
-
-const void* valu_chunked_kernel(int m, bool paged) {
-    switch (m) {
-        case 1: return paged ? (const void*)decode_valu_chunked<1, true> : (const void*)decode_valu_chunked<1, false>;
-        case 2: return paged ? (const void*)decode_valu_chunked<2, true> : (const void*)decode_valu_chunked<2, false>;
-        default: return paged ? (const void*)decode_valu_chunked<3, true> : (const void*)decode_valu_chunked<3, false>;
-    }
+    const void* fn = valu_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves);
+    if (fn == nullptr) return hipErrorInvalidValue;
+    const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
+                               : dim3((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
+    void* args[] = {const_cast<DecodeArgs*>(&a)};
+    return hipLaunchKernel(fn, grid, dim3(64 * a.waves), args, 0, s);
 }
 
 }  // namespace kvc

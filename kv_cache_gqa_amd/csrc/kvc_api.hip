@@ -10,6 +10,11 @@
 #ifndef KVC_STREAM_WG_CAP
 #define KVC_STREAM_WG_CAP kStreamMaxWgPerCu
 #endif
+// 1: automatic chunking of contiguous caches may use one wide work-group per
+// (sequence, KV head) instead of split chunks plus a merge pass.
+#ifndef KVC_AUTO_WIDE
+#define KVC_AUTO_WIDE 1
+#endif
 
 namespace kvc {
 
@@ -124,14 +129,15 @@ static int device_cus() {
     return n;
 }
 
-// Resident work-groups of 256 threads per compute unit for a kernel (cached).
-static int resident_wgs(const void* fn) {
+// Resident work-groups per compute unit for a kernel launched with `threads`
+// threads per work-group (cached).
+static int resident_wgs(const void* fn, int threads) {
     struct Entry { const void* fn; int n; };
-    static Entry cache[32] = {};
+    static Entry cache[64] = {};
     for (auto& e : cache)
         if (e.fn == fn) return e.n;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess || n <= 0) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 0) n = 0;
     for (auto& e : cache)
         if (e.fn == nullptr) {
             e.fn = fn;
@@ -141,14 +147,52 @@ static int resident_wgs(const void* fn) {
     return n;
 }
 
-// Work-group slots of the current device for a kernel: CUs x resident
-// work-groups, capped at 256 CUs x 4 (the workspace bound).
-static long device_slots(const void* fn) {
-    int per_cu = resident_wgs(fn);
+// Work-group slots of the current device for a kernel of `waves` wavefronts
+// per work-group: CUs x resident work-groups, capped at 256 CUs x 4 (the
+// workspace bound).  0 when the kernel cannot be resident at all.
+static long device_slots(const void* fn, int waves) {
+    int per_cu = resident_wgs(fn, 64 * waves);
     if (per_cu > KVC_STREAM_WG_CAP) per_cu = KVC_STREAM_WG_CAP;
     int cus = device_cus();
     if (cus > kStreamMaxCUs) cus = kStreamMaxCUs;
     return (long)cus * per_cu;
+}
+
+static const void* kernel_for(KernelKind kind, int m, bool paged, bool stream, int waves) {
+    return kind == kMfma ? mfma_kernel(m, paged, stream, waves) : valu_kernel(m, paged, stream, waves);
+}
+
+// Fraction of the slot-rounds a grid of `wgs` equal work-groups keeps busy.
+static double fill(long wgs, long slots) {
+    const long rounds = ceil_div(wgs, slots);
+    return (double)wgs / (double)(rounds * slots);
+}
+
+// Automatic chunking of a contiguous cache.  Two shapes compete:
+//   whole units  one 8-wavefront work-group per (sequence, KV head), no
+//                partial results and no merge pass;
+//   chunks       4-wavefront work-groups, ceil(slots / units) chunks per
+//                unit, merged afterwards.
+// Whole units win when they keep at least as many wavefronts per CU resident
+// and the grid fills the slots nearly as well (>= 7/8 of slot-rounds busy).
+struct AutoShape {
+    int waves;
+    long chunks;
+};
+
+static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len) {
+    const long units = (long)B * g;
+    const void* f4 = kernel_for(kind, m, false, false, 4);
+    const long slots4 = device_slots(f4, 4);
+    AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};
+#if KVC_AUTO_WIDE
+    const int wv = 8;
+    const void* fn = kernel_for(kind, m, false, false, wv);
+    const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
+    if (slots > 0 && units >= slots && slots * wv >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
+        return AutoShape{wv, 1};
+#endif
+    return split;
 }
 
 static int ilog2_exact(int x) {
@@ -170,6 +214,30 @@ static int check_common(const void* q, const void* k, const void* v, const int32
     return KVC_OK;
 }
 
+// Fix the launch on the current device: stream grid size, automatic chunk
+// count and work-group width.  Needs a.B, a.g, a.m, a.cap_len.
+static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len) {
+    a.stream = sc.stream ? 1 : 0;
+    a.num_wgs = 0;
+    a.waves = sc.kind == kGeneric ? 1 : 4;
+    if (sc.stream) {
+        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4), 4);
+        // No more work-groups than 256-position pieces of the largest possible batch.
+        const long pieces = ((long)a.B * a.g * a.cap_len + 255) / 256;
+        if (P > pieces) P = pieces;
+        a.num_wgs = (int)(P < 1 ? 1 : P);
+    } else if (sc.auto_chunks) {
+        const AutoShape sh = auto_shape(sc.kind, a.m, a.B, a.g, max_len);
+        a.waves = sh.waves;
+        // One chunk per unit may exceed kMaxChunk: the engines walk a chunk in
+        // windows of at most kMaxChunk positions.
+        sc.plan = sh.chunks == 1 ? Plan{(int)(ceil_div(max_len, kTileTokens) * kTileTokens), 1}
+                                 : plan_for_chunks(max_len, sh.chunks);
+    }
+    a.chunk_len = sc.plan.chunk_len;
+    a.num_chunks = sc.plan.num_chunks;
+}
+
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
     const bool paged = a.block_table != nullptr;
@@ -177,21 +245,7 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
     const size_t need = workspace_for(a.B, a.h, a.g, a.d, sc);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
     if (a.B == 0) return KVC_OK;
-    a.stream = sc.stream ? 1 : 0;
-    a.num_wgs = 0;
-    if (sc.stream) {
-        const void* fn = sc.kind == kMfma ? mfma_stream_kernel(a.m, paged) : valu_stream_kernel(a.m, paged);
-        long P = device_slots(fn);
-        // No more work-groups than 256-position pieces of the largest possible batch.
-        const long pieces = ((long)a.B * a.g * a.cap_len + 255) / 256;
-        if (P > pieces) P = pieces;
-        a.num_wgs = (int)(P < 1 ? 1 : P);
-    } else if (sc.auto_chunks) {
-        const void* fn = sc.kind == kMfma ? mfma_chunked_kernel(a.m, paged) : valu_chunked_kernel(a.m, paged);
-        sc.plan = plan_for_chunks(max_len, chunks_for_slots(device_slots(fn), a.B, a.g, max_len));
-    }
-    a.chunk_len = sc.plan.chunk_len;
-    a.num_chunks = sc.plan.num_chunks;
+    resolve_launch(a, sc, paged, max_len);
     const size_t rows = workspace_rows(a.B, a.h, a.g, sc);
     if (rows > 0) {
         char* w = static_cast<char*>(workspace);
@@ -246,6 +300,25 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
     const bool fixed = !sc.stream && !sc.auto_chunks;
     if (chunk_len) *chunk_len = fixed ? sc.plan.chunk_len : 0;
     if (num_chunks) *num_chunks = fixed ? sc.plan.num_chunks : 0;
+    return KVC_OK;
+}
+
+int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
+                            int paged, int* waves, int* num_wgs, int* chunk_len, int* num_chunks) {
+    if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
+        max_seq_len <= 0)
+        return KVC_ERR_INVALID;
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+    if (d > 256) return KVC_ERR_UNSUPPORTED;
+    Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
+    DecodeArgs a{};
+    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.cap_len = max_seq_len;
+    resolve_launch(a, sc, paged != 0, max_seq_len);
+    if (waves) *waves = a.waves;
+    const int per_chunk = sc.kind == kGeneric ? h : g;   // the generic kernel: one wavefront per query head
+    if (num_wgs) *num_wgs = a.stream ? a.num_wgs : a.num_chunks * per_chunk * B;
+    if (chunk_len) *chunk_len = a.stream ? 0 : a.chunk_len;
+    if (num_chunks) *num_chunks = a.stream ? 0 : a.num_chunks;
     return KVC_OK;
 }
 

@@ -55,6 +55,7 @@ struct DecodeArgs {
     int num_chunks;
     int stream;       // 1: persistent position-balanced grid of num_wgs work-groups
     int num_wgs;
+    int waves;        // wavefronts per work-group (4, 8 or 16)
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
     // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
     float* part_o;
@@ -69,11 +70,11 @@ hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
-// Stream-mode kernel functions (for occupancy queries).
-const void* mfma_stream_kernel(int m, bool paged);
-const void* valu_stream_kernel(int m, bool paged);
-const void* mfma_chunked_kernel(int m, bool paged);
-const void* valu_chunked_kernel(int m, bool paged);
+// Kernel function for (m, layout, split mode, wavefronts per work-group), for
+// launches and occupancy queries; nullptr when that combination is not
+// built.  MFMA: waves in {4, 8}; VALU: 4.
+const void* mfma_kernel(int m, bool paged, bool stream, int waves);
+const void* valu_kernel(int m, bool paged, bool stream, int waves);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int d, int capacity,
