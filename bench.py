@@ -2,9 +2,11 @@
 """Benchmark of one decode step on one MI355X.
 
 A step is the whole hot path over one batch of synthetic, seeded input that
-is already resident in HBM: kvc_append (new token's K/V into the cache), then
-kvc_decode_attention[_paged] (GQA head map, scores, online softmax, PV,
-split-K partials and their log-sum-exp merge when the plan splits).
+is already resident in HBM: one kvc_append_decode_attention[_paged] call
+(the new token's K/V into the cache, GQA head map, scores, online softmax,
+PV, and the log-sum-exp merge of split partials when the plan splits).
+--separate times kvc_append followed by kvc_decode_attention[_paged]
+instead.
 
 Metric: decode tokens/s = B / step time (one new token per sequence), with
 the achieved HBM bandwidth of the decode kernel against the 8 TB/s peak.
@@ -137,7 +139,10 @@ def algorithmic_bytes(w, lengths_after, nblocks=None):
     append_read = 2 * B * g * d * eb
     table = 0 if nblocks is None else int(nblocks.sum()) * 4
     decode = kv_read + q_read + out_write + table + B * 4
-    return dict(decode=decode, step=decode + append_write + append_read + B * 4, kv_read=kv_read)
+    # One-call step: the new token's K/V are read once (from k_new / v_new,
+    # counted in kv_read) and written once into the cache.
+    return dict(decode=decode, step=decode + append_write + append_read + B * 4,
+                fused=decode + append_write, kv_read=kv_read)
 
 
 def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0):
@@ -175,6 +180,9 @@ def main():
                     help="override the workload's split count (0 = library's choice)")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="a step is kvc_append then the decode call (two calls) instead of one "
+                         "kvc_append_decode_attention call")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -267,9 +275,20 @@ def main():
             kvc.decode(q, kc, vc, sl_after, scale=x["scale"], num_splits=ns, workspace=ws,
                        out=out, lse=lse)
 
+    def fused_call(i):
+        kc, vc = ks[i % copies], vs[i % copies]
+        kvc.append_decode(q, k_new, v_new, kc, vc, sl_before, block_table=bt, scale=x["scale"],
+                          num_splits=ns, workspace=ws, out=out, lse=lse)
+
     def step(i):
-        append_call(i)
-        decode_call(i)
+        if args.separate:
+            append_call(i)
+            decode_call(i)
+        else:
+            fused_call(i)
+
+    # The call whose bandwidth the roofline reports.
+    timed_call = decode_call if args.separate else fused_call
 
     print(f"[bench] {copies} cache copies ({cache_bytes * copies / 2**30:.2f} GiB), split "
           f"{split_mode} chunk_len={chunk_len} num_chunks={num_chunks}; warmup {args.warmup}",
@@ -282,29 +301,42 @@ def main():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
-    # One HIP graph per cache copy, each holding one whole step (append,
-    # decode, merge), so that host launch latency does not sit between the
-    # kernels of a step.  --eager launches from Python instead.
+    # HIP graphs hold whole steps (every kernel of a step), so that host
+    # launch latency does not sit between the kernels.  --eager launches from
+    # Python instead.
     graphs = []
+    cycle = None
     if not args.eager:
         for r in range(copies):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 step(r)
             graphs.append(gr)
+        # one graph holding a step on every cache copy, back to back, as a
+        # model's decode graph holds one attention step per layer
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle):
+            for r in range(copies):
+                step(r)
         for r in range(copies):
             graphs[r].replay()
+        cycle.replay()
         torch.cuda.synchronize()
 
-    # Timed region: exactly K steps between two synchronisations.
+    # Timed region: exactly K steps between two synchronisations (whole
+    # cycles of `copies` steps, then single steps for the remainder).
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % copies].replay()
-        else:
+    if graphs:
+        full, rest = divmod(args.steps, copies)
+        for _ in range(full):
+            cycle.replay()
+        for r in range(rest):
+            graphs[r].replay()
+    else:
+        for i in range(args.steps):
             step(i)
     t_end.record()
     torch.cuda.synchronize()
@@ -319,7 +351,7 @@ def main():
         dgraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(dgraph):
             for r in range(copies):
-                decode_call(r)
+                timed_call(r)
         dgraph.replay()
         torch.cuda.synchronize()
     d_start = torch.cuda.Event(enable_timing=True)
@@ -330,14 +362,16 @@ def main():
             dgraph.replay()
         else:
             for r in range(copies):
-                decode_call(r)
+                timed_call(r)
     d_end.record()
     torch.cuda.synchronize()
     dec_avg_ms = d_start.elapsed_time(d_end) / (reps * copies)
 
     nbytes = algorithmic_bytes(w, x["seq_lens_after"], nblocks)
-    traffic = stored_traffic(w.name)
-    achieved_gbs = nbytes["decode"] / (dec_avg_ms * 1e-3) / 1e9
+    # stored counter runs are of the default (one-call) step
+    traffic = None if args.separate else stored_traffic(w.name)
+    call_bytes = nbytes["decode"] if args.separate else nbytes["fused"]
+    achieved_gbs = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.B / (ms_per_step * 1e-3)
 
     cpu = None
@@ -368,15 +402,17 @@ def main():
                        "chunk_len": launch_chunk, "chunks": launch_chunks},
             "cache_copies_rotated": copies, "parallelism": "single GPU",
         },
-        "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
-        "timing": "eager" if args.eager else "HIP graph per step",
+        "step": "kvc_append + decode call" if args.separate else "one kvc_append_decode_attention call",
+        "step_hbm_gbs": round((nbytes["step"] if args.separate else nbytes["fused"])
+                              / (ms_per_step * 1e-3) / 1e9, 1),
+        "timing": "eager" if args.eager else "HIP graphs of whole steps (one step per cache copy)",
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode call: " + ("partials + log-sum-exp merge" if merged
-                                         else "one kernel, no merge"),
+            "kernel": ("decode call" if args.separate else "append+decode call") + ": "
+                      + ("partials + log-sum-exp merge" if merged else "one kernel, no merge"),
             "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_launch": nbytes["decode"],
+            "algorithmic_bytes_per_launch": call_bytes,
             "decode_call_ms_avg": round(dec_avg_ms, 5),
             "traffic": traffic,
         },

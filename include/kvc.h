@@ -208,6 +208,44 @@ int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_
                                int num_splits, void* workspace, size_t workspace_bytes,
                                float* out, float* lse, hipStream_t stream);
 
+/*
+ * kvc_append_decode_attention / kvc_append_decode_attention_paged -- the
+ * whole decode step in one call: the same result as kvc_append(k_new, v_new,
+ * ..., seq_lens_before, ...) followed by kvc_decode_attention[_paged] with
+ * seq_lens = seq_lens_before + 1 (each sequence attends to the positions it
+ * had and to the new token, which it sees last: [P1] 4.1, [P3] 04 and 08).
+ *
+ *   q, caches, block table, B, h, g, d, t_cap, scale, dtype, num_splits,
+ *   workspace, out, lse, stream: as for the decode entry points; the
+ *     workspace size is kvc_decode_workspace_bytes of the same shapes.
+ *   k_new, v_new      [B, g, d] of dtype: the new token's K and V.
+ *   seq_lens_before   device int32 [B]: cache length before the step; not
+ *                     modified.  The new token goes to that position.
+ *
+ * The decode kernels read the new token from k_new / v_new and write it into
+ * its cache slot themselves (one launch, plus the merge when results are
+ * split).  Out-of-range positions are skipped as kvc_append skips them (a
+ * length at or past the capacity attends to the capacity and appends
+ * nothing).  One difference from the two-call sequence: when the paged
+ * table entry of the new position is not a valid block, kvc_append writes
+ * nothing and a following decode reads whatever block the clamped entry
+ * names; the fused call also writes nothing but attends to the new token's
+ * true K/V.  k_new, v_new must not alias the caches.  Same status codes as
+ * the decode entry points.
+ */
+int kvc_append_decode_attention(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* seq_lens_before,
+                                int B, int h, int g, int d, int t_cap, float scale, int dtype,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream);
+int kvc_append_decode_attention_paged(const void* q, const void* k_new, const void* v_new,
+                                      void* k_pool, void* v_pool, const int32_t* block_table,
+                                      int max_blocks, int block_size, int num_blocks,
+                                      const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                      float scale, int dtype, int num_splits, void* workspace,
+                                      size_t workspace_bytes, float* out, float* lse,
+                                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

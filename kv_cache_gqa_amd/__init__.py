@@ -63,6 +63,12 @@ def load_library():
     lib.kvc_decode_workspace_bytes.restype = sz
     lib.kvc_decode_launch_shape.argtypes = [ip] * 8 + [ctypes.POINTER(ip)] * 4
     lib.kvc_decode_launch_shape.restype = ip
+    lib.kvc_append_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip,
+                                                ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention.restype = ip
+    lib.kvc_append_decode_attention_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, vp, ip,
+                                                      ip, ip, ip, fp, ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_paged.restype = ip
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
     lib.kvc_decode_attention.restype = ip
@@ -220,4 +226,44 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float
         ws.data_ptr() if ws is not None else None, wsb,
         _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
     _check("kvc_decode_attention_paged", st)
+    return out, lse
+
+
+def append_decode(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None,
+                  scale: Optional[float] = None, num_splits: int = 0,
+                  workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
+    """One decode step in one call: append k_new/v_new [B,g,d] at position
+    seq_lens_before[b] of each sequence's cache (contiguous [B,g,t_cap,d], or
+    pools [NB,g,bs,d] through block_table [B,max_blocks]) and attend over the
+    seq_lens_before[b] + 1 positions.  seq_lens_before is not modified.
+    Returns (out [B,h,d] float32, lse [B,h] float32)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    kn, vn = _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype)
+    sl = _dev(seq_lens_before, "seq_lens_before", torch.int32)
+    if block_table is None:
+        _, g, t_cap, _ = k_cache.shape
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, t_cap, num_splits, 0),
+                             q, workspace)
+        st = lib.kvc_append_decode_attention(
+            _dev(q, "q"), kn, vn, _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+            sl, B, h, g, d, t_cap, float(scale), dt, num_splits,
+            ws.data_ptr() if ws is not None else None, wsb,
+            _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_append_decode_attention", st)
+    else:
+        nb, g, bs, _ = k_cache.shape
+        mb = block_table.shape[1]
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, mb * bs, num_splits, 1),
+                             q, workspace)
+        st = lib.kvc_append_decode_attention_paged(
+            _dev(q, "q"), kn, vn, _dev(k_cache, "k_pool", q.dtype), _dev(v_cache, "v_pool", q.dtype),
+            _dev(block_table, "block_table", torch.int32), mb, bs, nb, sl, B, h, g, d,
+            float(scale), dt, num_splits, ws.data_ptr() if ws is not None else None, wsb,
+            _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_append_decode_attention_paged", st)
     return out, lse

@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int d = a.d;
     const int j = (int)(((long)i * a.g) / a.h);
-    const int L = clamp_len(a.seq_lens[b], a.cap_len);
+    const int L = attended_len(a, a.seq_lens[b]);
     const int p0 = c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;

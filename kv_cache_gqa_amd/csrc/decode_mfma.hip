@@ -37,6 +37,7 @@
 //
 // Two entry points share the segment code: a chunked grid (chunk, KV head,
 // sequence) and the persistent stream grid of kvc_schedule.h.
+
 #include "kvc_schedule.h"
 
 namespace kvc {
@@ -152,6 +153,16 @@ struct MfmaEngine {
             return bj_base + p;
         };
 
+        // A call that appends reads the new token from k_new / v_new (and
+        // writes it into its cache slot here, once per unit).
+        const int newp = new_pos(a, b);
+        const bool has_new = newp >= s && newp < e;  // then newp == e - 1
+        const int e_cache = has_new ? newp : e;
+        if (has_new && wave == 0) store_new_row_bf16_d128(a, b, j, newp, lane);
+        const long bj = (long)b * a.g + j;
+        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * kD : K;
+        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * kD : Vc;
+
         // Loads of the 32-position sub-tile at t0; positions are clamped to
         // the window's last one, so a sub-tile past the end stays in bounds.
         auto load_tile = [&](int t0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
@@ -167,6 +178,16 @@ struct MfmaEngine {
                 const long row = kv_row(min(t0 + 4 * u + G, w1 - 1));
                 vr[u] = ld16_stream(Vc + row * kD + 8 * col);
             }
+        };
+        // Every row of the tile is the appended token's (only its first
+        // position is unmasked).
+        auto load_new_tile = [&](uint4 (&kr)[2][4], uint4 (&vr)[8]) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16(KN + 32 * ks + 8 * G);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) vr[u] = ld16(VN + 8 * col);
         };
 
         auto compute_tile = [&](int t0, const uint4 (&kr)[2][4], const uint4 (&vr)[8]) {
@@ -251,8 +272,8 @@ struct MfmaEngine {
 
         // Windows of at most kMaxChunk positions, so that a window's slice of
         // the block table fits in shared memory.
-        for (int w0 = s; w0 < e; w0 = w1) {
-            w1 = min(e, w0 + kMaxChunk);
+        for (int w0 = s; w0 < e_cache; w0 = w1) {
+            w1 = min(e_cache, w0 + kMaxChunk);
             if (PAGED) {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
@@ -285,6 +306,15 @@ struct MfmaEngine {
             }
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
+        }
+        // An appended token (the last attended position) is taken last, as a
+        // one-position tile read from k_new / v_new by the wavefront next in
+        // turn.
+        if (e_cache < e && wave == ((newp - s) / kTileTokens) % W) {
+            w1 = newp + 1;
+            uint4 kr[2][4], vr[8];
+            load_new_tile(kr, vr);
+            compute_tile(newp, kr, vr);
         }
 
         // lex holds this lane's positions only: sum the four row groups.
@@ -379,7 +409,7 @@ decode_mfma_chunked(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED, W>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int L = clamp_len(a.seq_lens[b], a.cap_len);
+    const int L = attended_len(a, a.seq_lens[b]);
     const int p0 = c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;

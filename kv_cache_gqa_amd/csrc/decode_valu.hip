@@ -19,6 +19,7 @@
 //
 // Two entry points share the segment code: a chunked grid (chunk, KV head,
 // sequence) and the persistent stream grid of kvc_schedule.h.
+
 #include "kvc_schedule.h"
 
 namespace kvc {
@@ -79,6 +80,16 @@ struct ValuEngine {
             }
             return bj_base + p;
         };
+        // A call that appends reads the new token from k_new / v_new (and
+        // writes it into its cache slot here, once per unit).
+        const int newp = new_pos(a, b);
+        const bool has_new = newp >= s && newp < e;  // then newp == e - 1
+        const int e_cache = has_new ? newp : e;
+        if (has_new && wave == 0) store_new_row_bf16_d128(a, b, j, newp, lane);
+        const long bj = (long)b * a.g + j;
+        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * kD : K;
+        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * kD : Vc;
+
         // Positions clamped to the window's last one (in bounds past the end).
         auto load_tile = [&](int t0, uint4 (&kv)[8], uint4 (&vv)[8]) {
 #pragma unroll
@@ -86,6 +97,15 @@ struct ValuEngine {
                 const long row = kv_row(min(t0 + 4 * u + tsub, w1 - 1));
                 kv[u] = ld16_stream(K + row * kD + 8 * ds);
                 vv[u] = ld16_stream(Vc + row * kD + 8 * ds);
+            }
+        };
+        // Every row of the tile is the appended token's (only its first
+        // position is unmasked).
+        auto load_new_tile = [&](uint4 (&kv)[8], uint4 (&vv)[8]) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                kv[u] = ld16(KN + 8 * ds);
+                vv[u] = ld16(VN + 8 * ds);
             }
         };
         auto compute_tile = [&](int t0, const uint4 (&kv)[8], const uint4 (&vv)[8]) {
@@ -137,8 +157,8 @@ struct ValuEngine {
         };
 
         // Windows of at most kMaxChunk positions (block-table slice in LDS).
-        for (int w0 = s; w0 < e; w0 = w1) {
-            w1 = min(e, w0 + kMaxChunk);
+        for (int w0 = s; w0 < e_cache; w0 = w1) {
+            w1 = min(e_cache, w0 + kMaxChunk);
             if (PAGED) {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
@@ -171,6 +191,15 @@ struct ValuEngine {
             }
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
+        }
+        // An appended token (the last attended position) is taken last, as a
+        // one-position tile read from k_new / v_new by the wavefront next in
+        // turn.
+        if (e_cache < e && wave == ((newp - s) / kTileTokens) % W) {
+            w1 = newp + 1;
+            uint4 kv[8], vv[8];
+            load_new_tile(kv, vv);
+            compute_tile(newp, kv, vv);
         }
 
         // Merge the four rows of 16 lanes (positions interleaved by lane/16).
@@ -236,7 +265,7 @@ __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
     using E = ValuEngine<M, PAGED, W>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int L = clamp_len(a.seq_lens[b], a.cap_len);
+    const int L = attended_len(a, a.seq_lens[b]);
     const int p0 = c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;

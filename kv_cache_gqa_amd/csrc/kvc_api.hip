@@ -246,6 +246,17 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
     if (a.B == 0) return KVC_OK;
     resolve_launch(a, sc, paged, max_len);
+    if (a.len_add != 0 && sc.kind == kGeneric) {
+        // The generic kernel does not take the new token itself: append it
+        // first, then attend over the cache.
+        const int eb = dtype == KVC_F32 ? 4 : 2;
+        if (launch_append(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
+                          a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g, a.d,
+                          paged ? a.num_blocks : a.t_cap, eb, stream) != hipSuccess)
+            return KVC_ERR_HIP;
+        a.k_new = nullptr;
+        a.v_new = nullptr;
+    }
     const size_t rows = workspace_rows(a.B, a.h, a.g, sc);
     if (rows > 0) {
         char* w = static_cast<char*>(workspace);
@@ -347,10 +358,11 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
     return KVC_OK;
 }
 
-int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
-                         float scale, int dtype, int num_splits, void* workspace,
-                         size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+static int decode_contiguous(const void* q, const void* k_new, const void* v_new,
+                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                             int B, int h, int g, int d, int t_cap, float scale, int dtype,
+                             int num_splits, void* workspace, size_t workspace_bytes, float* out,
+                             float* lse, hipStream_t stream) {
     int st = check_common(q, k_cache, v_cache, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
@@ -362,15 +374,16 @@ int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache
     a.t_cap = t_cap; a.cap_len = t_cap;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
+    a.len_add = k_new != nullptr ? 1 : 0;
+    a.k_new = k_new; a.v_new = v_new;
     return run_decode(a, dtype, t_cap, num_splits, workspace, workspace_bytes, stream);
 }
 
-int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
-                               const int32_t* block_table, int max_blocks, int block_size,
-                               int num_blocks, const int32_t* seq_lens, int B, int h, int g,
-                               int d, float scale, int dtype, int num_splits, void* workspace,
-                               size_t workspace_bytes, float* out, float* lse,
-                               hipStream_t stream) {
+static int decode_paged(const void* q, const void* k_new, const void* v_new, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, int max_blocks,
+                        int block_size, int num_blocks, const int32_t* seq_lens, int B, int h,
+                        int g, int d, float scale, int dtype, int num_splits, void* workspace,
+                        size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
     int st = check_common(q, k_pool, v_pool, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
@@ -388,7 +401,52 @@ int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_
     a.t_cap = 0; a.cap_len = (int)cap;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
+    a.len_add = k_new != nullptr ? 1 : 0;
+    a.k_new = k_new; a.v_new = v_new;
     return run_decode(a, dtype, (int)cap, num_splits, workspace, workspace_bytes, stream);
+}
+
+int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
+                         float scale, int dtype, int num_splits, void* workspace,
+                         size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, t_cap,
+                             scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, int max_blocks, int block_size,
+                               int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                               int d, float scale, int dtype, int num_splits, void* workspace,
+                               size_t workspace_bytes, float* out, float* lse,
+                               hipStream_t stream) {
+    return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
+                        num_blocks, seq_lens, B, h, g, d, scale, dtype, num_splits, workspace,
+                        workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* seq_lens_before,
+                                int B, int h, int g, int d, int t_cap, float scale, int dtype,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
+                             seq_lens_before, B, h, g, d, t_cap, scale, dtype, num_splits,
+                             workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_paged(const void* q, const void* k_new, const void* v_new,
+                                      void* k_pool, void* v_pool, const int32_t* block_table,
+                                      int max_blocks, int block_size, int num_blocks,
+                                      const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                      float scale, int dtype, int num_splits, void* workspace,
+                                      size_t workspace_bytes, float* out, float* lse,
+                                      hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, scale,
+                        dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

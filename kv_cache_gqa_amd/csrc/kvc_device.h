@@ -116,4 +116,40 @@ __device__ __forceinline__ SegDst stream_dst(const DecodeArgs& a, int slot) {
 // Clamp a device-side length to [0, cap].
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// Attended length from a raw seq_lens entry: the entry, plus the new token
+// when the call also appends it, clamped to [0, cap_len].
+__device__ __forceinline__ int attended_len(const DecodeArgs& a, int raw) {
+    const long L = (long)raw + a.len_add;
+    return L < 0 ? 0 : (L > a.cap_len ? a.cap_len : (int)L);
+}
+
+// Position of sequence b's new token when the kernel itself appends it (it
+// is then read from k_new / v_new), else -1.  When attended it is the last
+// attended position.
+__device__ __forceinline__ int new_pos(const DecodeArgs& a, int b) {
+    return a.k_new != nullptr ? a.seq_lens[b] : -1;
+}
+
+// bf16, d = 128: write the new token's K and V rows of unit (b, j) into the
+// cache slot of position p (16 bytes per lane; lanes 0-15 K, 16-31 V; other
+// lanes do nothing).  Paged: skipped when the block-table entry is not a
+// valid block, as the append entry point does.
+__device__ __forceinline__ void store_new_row_bf16_d128(const DecodeArgs& a, int b, int j, int p,
+                                                        int lane) {
+    if (lane >= 32) return;
+    long row;
+    if (a.block_table != nullptr) {
+        const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+        if (phys < 0 || phys >= a.num_blocks) return;
+        row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+    } else {
+        row = ((long)b * a.g + j) * a.t_cap + p;
+    }
+    const bool is_v = lane >= 16;
+    const int c = lane & 15;
+    const uint4* src = reinterpret_cast<const uint4*>(is_v ? a.v_new : a.k_new) + ((long)b * a.g + j) * 16 + c;
+    uint4* dst = reinterpret_cast<uint4*>(const_cast<void*>(is_v ? a.v : a.k)) + row * 16 + c;
+    *dst = *src;
+}
+
 }  // namespace kvc

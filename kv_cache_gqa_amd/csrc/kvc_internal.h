@@ -55,7 +55,14 @@ struct DecodeArgs {
     int num_chunks;
     int stream;       // 1: persistent position-balanced grid of num_wgs work-groups
     int num_wgs;
-    int waves;        // wavefronts per work-group (4, 8 or 16)
+    int waves;        // wavefronts per work-group (4 or 8)
+    // Fused append: seq_lens holds the lengths before the step, the attended
+    // length is seq_lens[b] + len_add, and when k_new is set the kernel reads
+    // the new token (position seq_lens[b]) from k_new / v_new and writes it
+    // into its cache slot.
+    int len_add;
+    const void* k_new;
+    const void* v_new;
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
     // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
     float* part_o;

@@ -52,7 +52,7 @@ __device__ inline void stream_prefix(const DecodeArgs& a, long long* cum) {
         for (int k = 0; k < kScanPerLane; ++k) len[k] = a.seq_lens[min(b0 + k, a.B - 1)];
 #pragma unroll
         for (int k = 0; k < kScanPerLane; ++k)
-            len[k] = b0 + k < a.B ? clamp_len(len[k], a.cap_len) : 0;
+            len[k] = b0 + k < a.B ? attended_len(a, len[k]) : 0;
         long long sum = 0;
 #pragma unroll
         for (int k = 0; k < kScanPerLane; ++k) sum += len[k];

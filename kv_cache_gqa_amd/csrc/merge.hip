@@ -9,8 +9,6 @@
 //   out = sum_c w_c O_c / sum_c w_c,  lse = (M + log2 sum_c w_c) ln 2.
 // Only chunks that hold positions of the sequence are read; a sequence of
 // length 0 gets out = 0 and lse = -inf.
-//
-// One wavefront per (sequence, query head) row.
 #include "kvc_schedule.h"
 
 namespace kvc {
@@ -80,30 +78,92 @@ __device__ __forceinline__ void write_row(const DecodeArgs& a, long row, int lan
     if (lane == 0) a.lse[row] = acc.wsum > 0.0f ? (acc.M + fast_log2(acc.wsum)) * kLn2 : kNegInf;
 }
 
-__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (long)a.B * a.h) return;
-    const int lane = threadIdx.x & 63;
-    const int d = a.d;
-    const int C = a.num_chunks;
+// Chunked plans: one work-group per (sequence, query head) row.  Thread t
+// owns V dims (e = t % nE, nE = d / V) of the chunks c = cg, cg + G, ...
+// (cg = t / nE, G = 256 / nE chunk groups), folds them in eight per round
+// trip with online rescaling, and the G partial states are combined through
+// LDS.  All loads of a row are independent of each other, so a row costs
+// about one memory round trip after its length is known.
+template <int V>
+__device__ __forceinline__ void merge_row_chunked(const DecodeArgs& a, long row) {
+    __shared__ float sm_m[256];
+    __shared__ float sm_w[256];
+    __shared__ float sm_o[256 * 4];
+    const int d = a.d, C = a.num_chunks;
+    const int nE = d / V;
+    const int G = 256 / nE;
+    const int t = threadIdx.x;
+    const int cg = t / nE, e = t - (t / nE) * nE;
     const int b = (int)(row / a.h);
-    const int L = clamp_len(a.seq_lens[b], a.cap_len);
-    const int nc = (L + a.chunk_len - 1) / a.chunk_len;
-    const bool pairs = (d % 2 == 0) && d <= 128;
-    MergeAcc acc;
-    for (int c0 = 0; c0 < nc; c0 += kMergeBatch) {
-        float lse[kMergeBatch], v[kMergeBatch][4];
+    const int L = attended_len(a, a.seq_lens[b]);
+    const int nc = (L + a.chunk_len - 1) / a.chunk_len;  // chunks that hold positions
+    if (cg < G) {
+        float M = kNegInf, W = 0.0f, o[V];
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-            const int c = c0 + k;
-            const bool ok = c < nc;
-            const long rec = row * C + (ok ? c : 0);
-            lse[k] = ok ? a.part_lse[rec] : kNegInf;
-            load_lane(a.part_o + rec * d, ok, lane, d, pairs, v[k]);
+        for (int v = 0; v < V; ++v) o[v] = 0.0f;
+        for (int c0 = cg; c0 < nc; c0 += G * kMergeBatch) {
+            float lse[kMergeBatch], x[kMergeBatch][V];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const int c = c0 + k * G;
+                const bool ok = c < nc;
+                const long rec = row * C + (ok ? c : 0);
+                lse[k] = ok ? a.part_lse[rec] : kNegInf;
+                const float* src = a.part_o + rec * d + e * V;
+                if constexpr (V == 4) {
+                    const float4 q4 = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    x[k][0] = q4.x;
+                    x[k][1] = q4.y;
+                    x[k][2] = q4.z;
+                    x[k][3] = q4.w;
+                } else {
+                    x[k][0] = ok ? src[0] : 0.0f;
+                }
+            }
+            float bm = M;
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, lse[k]);
+            const float ref = (bm == kNegInf) ? 0.0f : bm;
+            const float f = fast_exp2(M - ref);
+            W *= f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) o[v] *= f;
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const float w = fast_exp2(lse[k] - ref);  // 0 for absent chunks
+                W += w;
+#pragma unroll
+                for (int v = 0; v < V; ++v) o[v] += w * x[k][v];
+            }
+            M = bm;
         }
-        acc.add(lse, v);
+        if (e == 0) {
+            sm_m[cg] = M;
+            sm_w[cg] = W;
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) sm_o[cg * d + e * V + v] = o[v];
     }
-    write_row(a, row, lane, pairs, acc);
+    __syncthreads();
+    for (int dim = t; dim < d; dim += 256) {
+        float Mx = kNegInf;
+        for (int q = 0; q < G; ++q) Mx = fmaxf(Mx, sm_m[q]);
+        const float ref = (Mx == kNegInf) ? 0.0f : Mx;
+        float Wt = 0.0f, ot = 0.0f;
+        for (int q = 0; q < G; ++q) {
+            const float f = fast_exp2(sm_m[q] - ref);
+            Wt += sm_w[q] * f;
+            ot += sm_o[q * d + dim] * f;
+        }
+        a.out[row * d + dim] = Wt > 0.0f ? ot / Wt : 0.0f;
+        if (dim == 0) a.lse[row] = Wt > 0.0f ? (Mx + fast_log2(Wt)) * kLn2 : kNegInf;
+    }
+}
+
+__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
+    const long row = blockIdx.x;
+    if (a.d % 4 == 0) merge_row_chunked<4>(a, row);
+    else merge_row_chunked<1>(a, row);
 }
 
 // Stream mode: unit u = (b, j) occupies global positions [U, U + L).  If its
@@ -126,7 +186,7 @@ __global__ void __launch_bounds__(256) merge_stream_kernel(DecodeArgs a) {
     const int b = (int)(row / a.h);
     const int i = (int)(row % a.h);
     const int j = i / m, r = i % m;
-    const long long L = clamp_len(a.seq_lens[b], a.cap_len);
+    const long long L = attended_len(a, a.seq_lens[b]);
     const bool pairs = (d % 2 == 0) && d <= 128;
     if (L == 0) {
         if (pairs) {
@@ -139,7 +199,7 @@ __global__ void __launch_bounds__(256) merge_stream_kernel(DecodeArgs a) {
     }
     long long before = 0, all = 0;
     for (int bb = lane; bb < a.B; bb += 64) {
-        const long long Lb = clamp_len(a.seq_lens[bb], a.cap_len);
+        const long long Lb = attended_len(a, a.seq_lens[bb]);
         all += Lb;
         if (bb < b) before += Lb;
     }
@@ -183,7 +243,7 @@ hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
     const long rows = (long)a.B * a.h;
-    merge_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(a);
+    merge_kernel<<<dim3((unsigned)rows), dim3(256), 0, s>>>(a);
     return hipGetLastError();
 }
 

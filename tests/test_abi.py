@@ -32,7 +32,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kvc_append", "kvc_decode_attention", "kvc_decode_attention_paged",
-              "kvc_decode_workspace_bytes", "kvc_decode_plan", "kvc_status_string", "kvc_version"):
+              "kvc_append_decode_attention", "kvc_append_decode_attention_paged",
+              "kvc_decode_workspace_bytes", "kvc_decode_plan", "kvc_decode_launch_shape",
+              "kvc_status_string", "kvc_version"):
         assert n in names
 
 
@@ -152,3 +154,27 @@ def test_python_binding_refuses_cpu_tensors():
     x = W.make_contiguous(w)
     with pytest.raises(ValueError):
         kvc.decode(x["q"], x["k_cache"], x["v_cache"], x["seq_lens_after"])
+
+
+def test_fused_validation_codes():
+    lib = kvc.load_library()
+    f = lib.kvc_append_decode_attention
+    # every call below fails validation (or has B = 0) before any HIP call
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, 1, None, 0, FAKE, FAKE, None]
+    bad = list(args); bad[1] = None                  # k_new missing
+    assert f(*bad) == INVALID
+    bad = list(args); bad[2] = None                  # v_new missing
+    assert f(*bad) == INVALID
+    bad = list(args); bad[8] = 3                     # h % g != 0
+    assert f(*bad) == INVALID
+    bad = list(args); bad[13] = 2                    # a split plan needs a workspace
+    assert f(*bad) == WORKSPACE
+    bad = list(args); bad[6] = 0                     # nothing to do
+    assert f(*bad) == OK
+    fp = lib.kvc_append_decode_attention_paged
+    pargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 0.1, 1, 1, None, 0,
+             FAKE, FAKE, None]
+    bad = list(pargs); bad[1] = None
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[7] = 12                   # block size not a power of two
+    assert fp(*bad) == INVALID

@@ -13,10 +13,13 @@ import kvc_workloads as W
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("h,g,paged,splits", [(16, 2, False, 5), (4, 4, False, 3), (32, 8, True, 4),
-                                              (32, 1, False, 64)])
-def test_graph_replay_matches_eager(h, g, paged, splits):
-    print(f"case graph h={h} g={g} paged={paged} splits={splits}", file=sys.stderr, flush=True)
+                                              (32, 1, False, 64), (64, 8, False, 0),
+                                              (32, 8, True, 0)])
+def test_graph_replay_matches_eager(h, g, paged, splits, fused):
+    print(f"case graph h={h} g={g} paged={paged} splits={splits} fused={fused}", file=sys.stderr,
+          flush=True)
     w = W.Workload("gr", B=3, h=h, g=g, d=128, dtype="bf16", T_range=(100, 900), paged=paged,
                    seed=400)
     dev = torch.device("cuda:0")
@@ -37,6 +40,10 @@ def test_graph_replay_matches_eager(h, g, paged, splits):
     lse = torch.empty(w.B, h, device=dev)
 
     def step():
+        if fused:
+            kvc.append_decode(q, kn, vn, kc, vc, before, block_table=bt, num_splits=splits,
+                              workspace=ws, out=out, lse=lse)
+            return
         kvc.append(kn, vn, kc, vc, before, block_table=bt)
         if paged:
             kvc.decode_paged(q, kc, vc, bt, after, num_splits=splits, workspace=ws, out=out, lse=lse)
