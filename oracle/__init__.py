@@ -14,7 +14,13 @@ module only marshals arrays into it.  Pages followed:
   unwritten slots; section 02 also the element count 2*L*N*H*T*d.
 * "KV Cache 优化与注意力机制加速：FlashAttention / PagedAttention"
   (plumephp.com), sections 2.2-2.5 (m, l, lse = m + log l, sequence split),
-  3.2 (size formula), 4.2-4.3 (block table lookup).
+  3.2 (size formula), 4.2-4.3 (block table lookup), 5.3 (speculative
+  decoding: several draft tokens checked in one pass).
+* Several new tokens at once (a prefill after a cached prefix, limoncc.com
+  section 5.2; draft tokens, plumephp.com section 5.3): token t of a sequence
+  with P cached positions sits at position P + t and sees positions 0..P + t
+  (the causal mask of the full sequence, aligned to its bottom-right corner,
+  which zwjcode.cn section 13 warns a non-square is_causal mask gets wrong).
 """
 from __future__ import annotations
 
@@ -196,3 +202,45 @@ def kv_cache_bytes(layers: int, batch: int, kv_heads: int, tokens: int, head_dim
     the element count 2*L*N*H*T*d; the limoncc.com page (section 二) and the
     plumephp.com page (section 3.2) give the byte form."""
     return 2 * layers * batch * kv_heads * tokens * head_dim * elem_bytes
+
+
+def _multi_position(before, t):
+    """Position of new token t of a sequence that had ``before`` cached ones."""
+    return before + t
+
+
+def _multi_visible(before, t):
+    """Positions new token t sees: the cached ones and new tokens 0..t."""
+    return before + t + 1
+
+
+def append_multi(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None):
+    """k_new, v_new [B,g,n,d]: token t of sequence b is written at position
+    seq_lens_before[b] + t.  Returns new (k_cache, v_cache) raw numpy arrays."""
+    kn, _ = _raw(k_new)
+    vn, _ = _raw(v_new)
+    before = _i32(seq_lens_before)
+    kc, vc = k_cache, v_cache
+    for t in range(kn.shape[2]):
+        kc, vc = append(np.ascontiguousarray(kn[:, :, t]), np.ascontiguousarray(vn[:, :, t]), kc, vc,
+                        _multi_position(before, t).astype(np.int32), block_table)
+    return kc, vc
+
+
+def decode_multi(q, k, v, seq_lens_before, scale, block_table=None, block_size=16, nthreads=0):
+    """q [B,h,n,d]: query token t of sequence b attends, through the single
+    token definition above, to the positions it sees (``_multi_visible``) of a
+    cache that already holds every new token.  Returns out [B,h,n,d] and lse
+    [B,h,n], float64."""
+    qa, _ = _raw(q)
+    before = _i32(seq_lens_before)
+    B, h, n, d = qa.shape
+    out = np.zeros((B, h, n, d), dtype=np.float64)
+    lse = np.zeros((B, h, n), dtype=np.float64)
+    for t in range(n):
+        o, l = decode(np.ascontiguousarray(qa[:, :, t]), k, v,
+                      _multi_visible(before, t).astype(np.int32), scale, block_table=block_table,
+                      block_size=block_size, nthreads=nthreads)
+        out[:, :, t] = o
+        lse[:, :, t] = l
+    return out, lse

@@ -350,6 +350,51 @@ def pin_scale_is_float32_value():
     assert not np.array_equal(l1, l3)
 
 
+# ----------------------------------------------------------------------------
+# Several new tokens at once ([P1] 5.2: prefill of new tokens after a cached
+# prefix; [P4] 5.3: draft tokens verified in one pass).  Appending them after
+# the prefix and attending with each token's own visible length reproduces
+# the last rows of a full causal forward over prefix + new tokens (torch SDPA
+# in fp64, is_causal on the square problem, so its alignment is unambiguous);
+# lse matches torch.logsumexp over the same causal scores.  Paged = contiguous.
+def pin_multi_query_equals_causal_prefill():
+    for (N, H, G, P, n, d, seed) in [(2, 8, 2, 7, 5, 8, 10), (1, 4, 4, 0, 6, 4, 11),
+                                     (3, 6, 1, 20, 1, 16, 12), (2, 4, 2, 33, 3, 8, 13)]:
+        gen = torch.Generator().manual_seed(seed)
+        S = P + n
+        q = torch.randn(N, H, S, d, generator=gen)
+        k = torch.randn(N, G, S, d, generator=gen)
+        v = torch.randn(N, G, S, d, generator=gen)
+        sc = float(np.float32(1.0 / math.sqrt(d)))
+        full = F.scaled_dot_product_attention(_f64(q), _f64(k), _f64(v), is_causal=True,
+                                              scale=sc, enable_gqa=True).numpy()
+        kx = _f64(k).repeat_interleave(H // G, dim=1)
+        scores = torch.matmul(_f64(q), kx.transpose(-1, -2).contiguous()) * sc      # [N,H,S,S]
+        causal = torch.ones(S, S, dtype=torch.bool).tril()
+        full_lse = torch.logsumexp(scores.masked_fill(~causal, float("-inf")), dim=-1).numpy()
+        t_cap = S + 3
+        kc = np.zeros((N, G, t_cap, d), np.float32)
+        vc = np.zeros((N, G, t_cap, d), np.float32)
+        kc[:, :, :P] = k[:, :, :P].numpy()
+        vc[:, :, :P] = v[:, :, :P].numpy()
+        before = [P] * N
+        kc, vc = oracle.append_multi(k[:, :, P:].contiguous(), v[:, :, P:].contiguous(), kc, vc,
+                                     before)
+        assert np.array_equal(kc[:, :, :S], k.numpy()) and np.array_equal(vc[:, :, :S], v.numpy())
+        assert not kc[:, :, S:].any() and not vc[:, :, S:].any()
+        o, l = oracle.decode_multi(q[:, :, P:].contiguous(), kc, vc, before, sc)
+        assert np.max(np.abs(o - full[:, :, P:])) < 1e-12, np.max(np.abs(o - full[:, :, P:]))
+        assert np.max(np.abs(l - full_lse[:, :, P:])) < 1e-12
+        # paged: the same logical cache through a shuffled block table
+        lens = torch.full((N,), S, dtype=torch.int32)
+        table, nb = W.make_block_table(lens, 4, perm_seed=seed, extra_blocks=2)
+        kp = W.scatter_to_pool(torch.from_numpy(kc), lens, table, nb, 4)
+        vp = W.scatter_to_pool(torch.from_numpy(vc), lens, table, nb, 4)
+        op, lp = oracle.decode_multi(q[:, :, P:].contiguous(), kp, vp, before, sc,
+                                     block_table=table, block_size=4)
+        assert np.array_equal(op, o) and np.array_equal(lp, l)
+
+
 ALL_PINS = [
     pin_d1_worked_example,
     pin_sdpa_crosscheck,
@@ -365,4 +410,5 @@ ALL_PINS = [
     pin_append_writes_only_target_slots,
     pin_tiny_brute_force,
     pin_scale_is_float32_value,
+    pin_multi_query_equals_causal_prefill,
 ]

@@ -117,3 +117,24 @@ def test_planted_mistake_is_caught(name, tmp_path):
     finally:
         oracle._lib = saved
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+# Plausible mistakes in the several-new-tokens composition (positions and
+# visibility), each of which the multi-query pin must catch.  Every variant
+# stays inside the pin's cache capacity (t_cap = prefix + n + 3).
+MULTI_MUTATIONS = {
+    "top_left_alignment": ("_multi_visible", lambda before, t: t + 1),
+    "excludes_itself": ("_multi_visible", lambda before, t: before + t),
+    "ignores_token_index": ("_multi_visible", lambda before, t: before + 1),
+    "sees_next_token": ("_multi_visible", lambda before, t: before + t + 2),
+    "append_shifted": ("_multi_position", lambda before, t: before + t + 1),
+    "append_all_at_prefix_end": ("_multi_position", lambda before, t: before),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_MUTATIONS))
+def test_planted_multi_query_mistake_is_caught(name, monkeypatch):
+    attr, fn = MULTI_MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    with pytest.raises(Exception):
+        P.pin_multi_query_equals_causal_prefill()
