@@ -246,6 +246,58 @@ int kvc_append_decode_attention_paged(const void* q, const void* k_new, const vo
                                       size_t workspace_bytes, float* out, float* lse,
                                       hipStream_t stream);
 
+/*
+ * Several new tokens per sequence at once: kvc_decode_attention_multi[_paged]
+ * and kvc_append_decode_attention_multi[_paged] (a prefill of new tokens
+ * after a cached prefix, [P1] 5.2; draft tokens checked in one pass, [P4]
+ * 5.3).  Query token t of sequence b sits at position P_b + t, where P_b is
+ * the number of positions cached before the n new tokens, and attends to
+ * positions 0 .. P_b + t: the causal mask of the whole sequence aligned to
+ * its bottom-right corner ([P3] 13 warns that a non-square is_causal mask is
+ * aligned otherwise).
+ *
+ *   q      [B, h, n, d] of dtype: token t of head i at q[b, i, t, :]
+ *   out    [B, h, n, d] fp32;  lse [B, h, n] fp32
+ *   n      new tokens per sequence, >= 1; h * n <= 65535
+ *   kvc_decode_attention_multi[_paged]: the n tokens are already in the
+ *     cache and seq_lens[b] = P_b + n (the length after them).
+ *   kvc_append_decode_attention_multi[_paged]: k_new, v_new [B, g, n, d];
+ *     seq_lens_before[b] = P_b (not modified).  Token t is written at
+ *     position P_b + t (skipped outside the capacity, as kvc_append skips),
+ *     and the tokens attend as above, in one launch plus the merge when the
+ *     results are split.
+ *   Token t sees min(P_b + t + 1, capacity) positions (0 if negative).
+ * Everything else is as for the single-token calls, which are the case
+ * n = 1.  The workspace is kvc_decode_workspace_bytes(B, h * n, g, d, ...);
+ * kvc_decode_plan and kvc_decode_launch_shape likewise take h * n as h.  The
+ * bf16 d = 128 kernels serve (h / g) * n <= 32 query rows per KV head; more
+ * rows go to the generic kernel.
+ */
+int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                               int t_cap, float scale, int dtype, int num_splits, void* workspace,
+                               size_t workspace_bytes, float* out, float* lse, hipStream_t stream);
+int kvc_decode_attention_multi_paged(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int max_blocks, int block_size,
+                                     int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                                     int d, int n, float scale, int dtype, int num_splits,
+                                     void* workspace, size_t workspace_bytes, float* out,
+                                     float* lse, hipStream_t stream);
+int kvc_append_decode_attention_multi(const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache,
+                                      const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                      int n, int t_cap, float scale, int dtype, int num_splits,
+                                      void* workspace, size_t workspace_bytes, float* out,
+                                      float* lse, hipStream_t stream);
+int kvc_append_decode_attention_multi_paged(const void* q, const void* k_new, const void* v_new,
+                                            void* k_pool, void* v_pool,
+                                            const int32_t* block_table, int max_blocks,
+                                            int block_size, int num_blocks,
+                                            const int32_t* seq_lens_before, int B, int h, int g,
+                                            int d, int n, float scale, int dtype, int num_splits,
+                                            void* workspace, size_t workspace_bytes, float* out,
+                                            float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,19 @@ def load_library():
     lib.kvc_append_decode_attention_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, vp, ip,
                                                       ip, ip, ip, fp, ip, ip, vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention_paged.restype = ip
+    lib.kvc_decode_attention_multi.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, fp, ip, ip,
+                                               vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_multi.restype = ip
+    lib.kvc_decode_attention_multi_paged.argtypes = [vp, vp, vp, vp, ip, ip, ip, vp, ip, ip, ip,
+                                                     ip, ip, fp, ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_multi_paged.restype = ip
+    lib.kvc_append_decode_attention_multi.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip,
+                                                      ip, fp, ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_multi.restype = ip
+    lib.kvc_append_decode_attention_multi_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip,
+                                                            vp, ip, ip, ip, ip, ip, fp, ip, ip,
+                                                            vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_multi_paged.restype = ip
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
     lib.kvc_decode_attention.restype = ip
@@ -266,4 +279,92 @@ def append_decode(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_tabl
             float(scale), dt, num_splits, ws.data_ptr() if ws is not None else None, wsb,
             _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_append_decode_attention_paged", st)
+    return out, lse
+
+
+def _outputs_multi(q, out, lse):
+    B, h, n, d = q.shape
+    if out is None:
+        out = torch.empty((B, h, n, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def decode_multi(q, k_cache, v_cache, seq_lens, block_table=None, scale: Optional[float] = None,
+                 num_splits: int = 0, workspace: Optional[torch.Tensor] = None, out=None, lse=None,
+                 stream=None):
+    """n query tokens per sequence over a cache that already holds them.
+
+    q [B,h,n,d]; seq_lens int32 [B] = cached length including the n tokens;
+    token t sees positions 0 .. seq_lens[b] - n + t.  Contiguous caches
+    [B,g,t_cap,d], or pools [NB,g,bs,d] with block_table.  Returns (out
+    [B,h,n,d] float32, lse [B,h,n] float32)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs_multi(q, out, lse)
+    sl = _dev(seq_lens, "seq_lens", torch.int32)
+    if block_table is None:
+        _, g, t_cap, _ = k_cache.shape
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, t_cap, num_splits, 0),
+                             q, workspace)
+        st = lib.kvc_decode_attention_multi(
+            _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype), sl,
+            B, h, g, d, n, t_cap, float(scale), dt, num_splits,
+            ws.data_ptr() if ws is not None else None, wsb,
+            _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_decode_attention_multi", st)
+    else:
+        nb, g, bs, _ = k_cache.shape
+        mb = block_table.shape[1]
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, mb * bs, num_splits,
+                                                            1), q, workspace)
+        st = lib.kvc_decode_attention_multi_paged(
+            _dev(q, "q"), _dev(k_cache, "k_pool", q.dtype), _dev(v_cache, "v_pool", q.dtype),
+            _dev(block_table, "block_table", torch.int32), mb, bs, nb, sl, B, h, g, d, n,
+            float(scale), dt, num_splits, ws.data_ptr() if ws is not None else None, wsb,
+            _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_decode_attention_multi_paged", st)
+    return out, lse
+
+
+def append_decode_multi(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None,
+                        scale: Optional[float] = None, num_splits: int = 0,
+                        workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
+    """Append n new tokens per sequence (k_new, v_new [B,g,n,d]; token t at
+    position seq_lens_before[b] + t) and attend with q [B,h,n,d], token t
+    seeing positions 0 .. seq_lens_before[b] + t, in one call.  Returns
+    (out [B,h,n,d] float32, lse [B,h,n] float32)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs_multi(q, out, lse)
+    kn, vn = _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype)
+    sl = _dev(seq_lens_before, "seq_lens_before", torch.int32)
+    if block_table is None:
+        _, g, t_cap, _ = k_cache.shape
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, t_cap, num_splits, 0),
+                             q, workspace)
+        st = lib.kvc_append_decode_attention_multi(
+            _dev(q, "q"), kn, vn, _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+            sl, B, h, g, d, n, t_cap, float(scale), dt, num_splits,
+            ws.data_ptr() if ws is not None else None, wsb,
+            _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_append_decode_attention_multi", st)
+    else:
+        nb, g, bs, _ = k_cache.shape
+        mb = block_table.shape[1]
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, mb * bs, num_splits,
+                                                            1), q, workspace)
+        st = lib.kvc_append_decode_attention_multi_paged(
+            _dev(q, "q"), kn, vn, _dev(k_cache, "k_pool", q.dtype), _dev(v_cache, "v_pool", q.dtype),
+            _dev(block_table, "block_table", torch.int32), mb, bs, nb, sl, B, h, g, d, n,
+            float(scale), dt, num_splits, ws.data_ptr() if ws is not None else None, wsb,
+            _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_append_decode_attention_multi_paged", st)
     return out, lse

@@ -9,7 +9,8 @@
 // pos % block_size.
 //
 // One thread moves one vector of W bytes (16, 4 or 2 depending on the row
-// size) of one (tensor, sequence, KV head); the copy is bit-exact.
+// size) of one (tensor, sequence, KV head, new token); the copy is
+// bit-exact.  New token k of sequence b goes to position seq_lens[b] + k.
 #include "kvc_device.h"
 
 namespace kvc {
@@ -18,24 +19,27 @@ template <typename V>
 __global__ void __launch_bounds__(256) append_kernel(
     const V* __restrict__ k_new, const V* __restrict__ v_new, V* __restrict__ k_cache,
     V* __restrict__ v_cache, const int32_t* __restrict__ block_table, int max_blocks,
-    int block_size, const int32_t* __restrict__ seq_lens, int B, int g, int vec_per_row,
+    int block_size, const int32_t* __restrict__ seq_lens, int B, int g, int n, int vec_per_row,
     int capacity) {
-    const long total = (long)B * g * vec_per_row;
+    const long total = (long)B * g * n * vec_per_row;
     long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const bool is_v = t >= total;
     if (is_v) t -= total;
     if (t >= total) return;
     const int vec = (int)(t % vec_per_row);
-    const long bj = t / vec_per_row;
+    const long tok = t / vec_per_row;       // (b * g + j) * n + token
+    const int k = (int)(tok % n);
+    const long bj = tok / n;
     const int b = (int)(bj / g);
     const int j = (int)(bj % g);
-    const int pos = seq_lens[b];
+    const long pos_l = (long)seq_lens[b] + k;
+    if (pos_l < 0 || pos_l > 0x7fffffffL) return;
+    const int pos = (int)pos_l;
     long row;
     if (block_table == nullptr) {
-        if (pos < 0 || pos >= capacity) return;
+        if (pos >= capacity) return;
         row = bj * (long)capacity + pos;
     } else {
-        if (pos < 0) return;
         const int logical = pos / block_size;
         if (logical >= max_blocks) return;
         const int phys = block_table[(long)b * max_blocks + logical];
@@ -44,36 +48,37 @@ __global__ void __launch_bounds__(256) append_kernel(
     }
     const V* src = is_v ? v_new : k_new;
     V* dst = is_v ? v_cache : k_cache;
-    dst[row * vec_per_row + vec] = src[bj * vec_per_row + vec];
+    dst[row * vec_per_row + vec] = src[tok * vec_per_row + vec];
+}
+
+template <typename V>
+static void launch_append_t(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* block_table, int max_blocks, int block_size,
+                            const int32_t* seq_lens_before, int B, int g, int n, int vpr,
+                            int capacity, hipStream_t s) {
+    const int threads = 256;
+    const long total = 2L * B * g * n * vpr;
+    append_kernel<V><<<dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, s>>>(
+        (const V*)k_new, (const V*)v_new, (V*)k_cache, (V*)v_cache, block_table, max_blocks,
+        block_size, seq_lens_before, B, g, n, vpr, capacity);
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
-                         const int32_t* seq_lens_before, int B, int g, int d, int capacity,
+                         const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,
                          int elem_bytes, hipStream_t s) {
     const long row_bytes = (long)d * elem_bytes;
-    const int threads = 256;
-    if (row_bytes % 16 == 0) {
-        const int vpr = (int)(row_bytes / 16);
-        const long n = 2L * B * g * vpr;
-        append_kernel<uint4><<<dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s>>>(
-            (const uint4*)k_new, (const uint4*)v_new, (uint4*)k_cache, (uint4*)v_cache,
-            block_table, max_blocks, block_size, seq_lens_before, B, g, vpr, capacity);
-    } else if (row_bytes % 4 == 0) {
-        const int vpr = (int)(row_bytes / 4);
-        const long n = 2L * B * g * vpr;
-        append_kernel<uint32_t><<<dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s>>>(
-            (const uint32_t*)k_new, (const uint32_t*)v_new, (uint32_t*)k_cache,
-            (uint32_t*)v_cache, block_table, max_blocks, block_size, seq_lens_before, B, g, vpr,
-            capacity);
-    } else {
-        const int vpr = (int)(row_bytes / 2);
-        const long n = 2L * B * g * vpr;
-        append_kernel<uint16_t><<<dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s>>>(
-            (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-            (uint16_t*)v_cache, block_table, max_blocks, block_size, seq_lens_before, B, g, vpr,
-            capacity);
-    }
+    if (row_bytes % 16 == 0)
+        launch_append_t<uint4>(k_new, v_new, k_cache, v_cache, block_table, max_blocks, block_size,
+                               seq_lens_before, B, g, n, (int)(row_bytes / 16), capacity, s);
+    else if (row_bytes % 4 == 0)
+        launch_append_t<uint32_t>(k_new, v_new, k_cache, v_cache, block_table, max_blocks,
+                                  block_size, seq_lens_before, B, g, n, (int)(row_bytes / 4),
+                                  capacity, s);
+    else
+        launch_append_t<uint16_t>(k_new, v_new, k_cache, v_cache, block_table, max_blocks,
+                                  block_size, seq_lens_before, B, g, n, (int)(row_bytes / 2),
+                                  capacity, s);
     return hipGetLastError();
 }
 

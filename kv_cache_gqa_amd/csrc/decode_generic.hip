@@ -37,11 +37,13 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int d = a.d;
     const int j = (int)(((long)i * a.g) / a.h);
-    const int L = attended_len(a, a.seq_lens[b]);
+    const int raw = a.seq_lens[b];
+    const int L = attended_len(a, raw);
     const int p0 = c * a.chunk_len;
-    const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;
     if (p0 >= L && !single) return;  // chunk past the end: the merge skips it
+    // row i is token i % n, which sees visible_len positions
+    const int p1 = min(min(p0 + a.chunk_len, L), visible_len(a, raw, i % a.n));
 
     const T* q = (const T*)a.q;
     const T* K = (const T*)a.k;
@@ -94,13 +96,13 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         if (lane == 0) a.lse[row_out] = l > 0.0f ? (m + fast_log2(l)) * kLn2 : kNegInf;
     } else {
         const long prow = row_out * a.num_chunks + c;
-        const float inv = 1.0f / l;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // l = 0: nothing visible in this chunk
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int dim = lane + 64 * kk;
             if (dim < d) a.part_o[prow * d + dim] = acc[kk] * inv;
         }
-        if (lane == 0) a.part_lse[prow] = m + fast_log2(l);
+        if (lane == 0) a.part_lse[prow] = l > 0.0f ? m + fast_log2(l) : kNegInf;
     }
 }
 

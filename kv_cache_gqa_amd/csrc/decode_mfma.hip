@@ -153,15 +153,23 @@ struct MfmaEngine {
             return bj_base + p;
         };
 
-        // A call that appends reads the new token from k_new / v_new (and
-        // writes it into its cache slot here, once per unit).
-        const int newp = new_pos(a, b);
-        const bool has_new = newp >= s && newp < e;  // then newp == e - 1
-        const int e_cache = has_new ? newp : e;
-        if (has_new && wave == 0) store_new_row_bf16_d128(a, b, j, newp, lane);
+        // Query column 16*qt + col is token (16*qt + col) % n, which sees
+        // positions below lim[qt].
+        const int raw = a.seq_lens[b];
+        int lim[NQT];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) lim[qt] = visible_len(a, raw, (16 * qt + col) % a.n);
+
+        // A call that appends reads its new tokens (positions raw .. raw+n-1,
+        // the last ones of the unit) from k_new / v_new and writes them into
+        // their cache slots here, once per unit.
+        const int fresh_lo = max(s, raw);
+        const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 32 positions
+        const int e_cache = has_new ? fresh_lo : e;
+        if (has_new) store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         const long bj = (long)b * a.g + j;
-        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * kD : K;
-        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * kD : Vc;
+        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
+        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
 
         // Loads of the 32-position sub-tile at t0; positions are clamped to
         // the window's last one, so a sub-tile past the end stays in bounds.
@@ -179,15 +187,20 @@ struct MfmaEngine {
                 vr[u] = ld16_stream(Vc + row * kD + 8 * col);
             }
         };
-        // Every row of the tile is the appended token's (only its first
-        // position is unmasked).
-        auto load_new_tile = [&](uint4 (&kr)[2][4], uint4 (&vr)[8]) {
+        // The appended tokens' tile at t0 (>= raw): position p is row p - raw
+        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.
+        auto load_new_tile = [&](int t0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt) {
+                const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16(KN + 32 * ks + 8 * G);
+                for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16(KN + r * kD + 32 * ks + 8 * G);
+            }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) vr[u] = ld16(VN + 8 * col);
+            for (int u = 0; u < 8; ++u) {
+                const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
+                vr[u] = ld16(VN + r * kD + 8 * col);
+            }
         };
 
         auto compute_tile = [&](int t0, const uint4 (&kr)[2][4], const uint4 (&vr)[8]) {
@@ -219,7 +232,7 @@ struct MfmaEngine {
                     for (int v = 0; v < 4; ++v) {
                         const int p = t0 + 16 * tt + 4 * G + v;
                         const float x = S[qt][tt][v] * sl2;
-                        sv[4 * tt + v] = p < w1 ? x : kNegInf;
+                        sv[4 * tt + v] = (p < w1 && p < lim[qt]) ? x : kNegInf;
                     }
                 }
                 float mt = sv[0];
@@ -307,14 +320,14 @@ struct MfmaEngine {
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
-        // An appended token (the last attended position) is taken last, as a
-        // one-position tile read from k_new / v_new by the wavefront next in
+        // The appended tokens (the last positions of the unit) are taken
+        // last, as one tile read from k_new / v_new by the wavefront next in
         // turn.
-        if (e_cache < e && wave == ((newp - s) / kTileTokens) % W) {
-            w1 = newp + 1;
+        if (has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
+            w1 = e;
             uint4 kr[2][4], vr[8];
-            load_new_tile(kr, vr);
-            compute_tile(newp, kr, vr);
+            load_new_tile(fresh_lo, kr, vr);
+            compute_tile(fresh_lo, kr, vr);
         }
 
         // lex holds this lane's positions only: sum the four row groups.

@@ -80,15 +80,22 @@ struct ValuEngine {
             }
             return bj_base + p;
         };
-        // A call that appends reads the new token from k_new / v_new (and
-        // writes it into its cache slot here, once per unit).
-        const int newp = new_pos(a, b);
-        const bool has_new = newp >= s && newp < e;  // then newp == e - 1
-        const int e_cache = has_new ? newp : e;
-        if (has_new && wave == 0) store_new_row_bf16_d128(a, b, j, newp, lane);
+        // Row r is token r % n, which sees positions below lim[r].
+        const int raw = a.seq_lens[b];
+        int lim[M];
+#pragma unroll
+        for (int r = 0; r < M; ++r) lim[r] = visible_len(a, raw, r % a.n);
+
+        // A call that appends reads its new tokens (positions raw .. raw+n-1,
+        // the last ones of the unit) from k_new / v_new and writes them into
+        // their cache slots here, once per unit.
+        const int fresh_lo = max(s, raw);
+        const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 3 positions
+        const int e_cache = has_new ? fresh_lo : e;
+        if (has_new) store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         const long bj = (long)b * a.g + j;
-        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * kD : K;
-        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * kD : Vc;
+        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
+        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
 
         // Positions clamped to the window's last one (in bounds past the end).
         auto load_tile = [&](int t0, uint4 (&kv)[8], uint4 (&vv)[8]) {
@@ -99,20 +106,21 @@ struct ValuEngine {
                 vv[u] = ld16_stream(Vc + row * kD + 8 * ds);
             }
         };
-        // Every row of the tile is the appended token's (only its first
-        // position is unmasked).
-        auto load_new_tile = [&](uint4 (&kv)[8], uint4 (&vv)[8]) {
+        // The appended tokens' tile at t0 (>= raw): position p is row p - raw
+        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.
+        auto load_new_tile = [&](int t0, uint4 (&kv)[8], uint4 (&vv)[8]) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                kv[u] = ld16(KN + 8 * ds);
-                vv[u] = ld16(VN + 8 * ds);
+                const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
+                kv[u] = ld16(KN + r * kD + 8 * ds);
+                vv[u] = ld16(VN + r * kD + 8 * ds);
             }
         };
         auto compute_tile = [&](int t0, const uint4 (&kv)[8], const uint4 (&vv)[8]) {
             float sc[M][8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const bool valid = (t0 + 4 * u + tsub) < w1;
+                const int p = t0 + 4 * u + tsub;
 #pragma unroll
                 for (int r = 0; r < M; ++r) {
                     float dot = dot2_bf16(qp[r][0], kv[u].x, 0.0f);
@@ -120,7 +128,7 @@ struct ValuEngine {
                     dot = dot2_bf16(qp[r][2], kv[u].z, dot);
                     dot = dot2_bf16(qp[r][3], kv[u].w, dot);
                     dot = row16_sum(dot) * sl2;
-                    sc[r][u] = valid ? dot : kNegInf;
+                    sc[r][u] = (p < w1 && p < lim[r]) ? dot : kNegInf;
                 }
             }
             float pr[M][8];
@@ -192,14 +200,14 @@ struct ValuEngine {
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
-        // An appended token (the last attended position) is taken last, as a
-        // one-position tile read from k_new / v_new by the wavefront next in
+        // The appended tokens (the last positions of the unit) are taken
+        // last, as one tile read from k_new / v_new by the wavefront next in
         // turn.
-        if (e_cache < e && wave == ((newp - s) / kTileTokens) % W) {
-            w1 = newp + 1;
+        if (has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
+            w1 = e;
             uint4 kv[8], vv[8];
-            load_new_tile(kv, vv);
-            compute_tile(newp, kv, vv);
+            load_new_tile(fresh_lo, kv, vv);
+            compute_tile(fresh_lo, kv, vv);
         }
 
         // Merge the four rows of 16 lanes (positions interleaved by lane/16).

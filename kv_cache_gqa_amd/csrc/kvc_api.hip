@@ -251,8 +251,8 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
         // first, then attend over the cache.
         const int eb = dtype == KVC_F32 ? 4 : 2;
         if (launch_append(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
-                          a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g, a.d,
-                          paged ? a.num_blocks : a.t_cap, eb, stream) != hipSuccess)
+                          a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g, a.n,
+                          a.d, paged ? a.num_blocks : a.t_cap, eb, stream) != hipSuccess)
             return KVC_ERR_HIP;
         a.k_new = nullptr;
         a.v_new = nullptr;
@@ -353,28 +353,32 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
     if (block_table != nullptr && (max_blocks <= 0 || block_size <= 0)) return KVC_ERR_INVALID;
     const int eb = dtype == KVC_F32 ? 4 : 2;
     if (launch_append(k_new, v_new, k_cache, v_cache, block_table, max_blocks, block_size,
-                      seq_lens_before, B, g, d, capacity, eb, stream) != hipSuccess)
+                      seq_lens_before, B, g, 1, d, capacity, eb, stream) != hipSuccess)
         return KVC_ERR_HIP;
     return KVC_OK;
 }
 
+// Shared body of the contiguous entry points.  n queries per sequence
+// (q [B, h, n, d]); k_new != nullptr: the call also appends the n new tokens
+// (k_new [B, g, n, d]) and seq_lens holds the lengths before the step.
 static int decode_contiguous(const void* q, const void* k_new, const void* v_new,
                              const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                             int B, int h, int g, int d, int t_cap, float scale, int dtype,
+                             int B, int h, int g, int d, int n, int t_cap, float scale, int dtype,
                              int num_splits, void* workspace, size_t workspace_bytes, float* out,
                              float* lse, hipStream_t stream) {
     int st = check_common(q, k_cache, v_cache, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
-    if (t_cap <= 0) return KVC_ERR_INVALID;
+    if (t_cap <= 0 || n <= 0) return KVC_ERR_INVALID;
+    if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
     DecodeArgs a{};
     a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens;
     a.block_table = nullptr; a.max_blocks = 0; a.block_size = 1; a.log2_bs = 0; a.num_blocks = 0;
-    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g;
+    a.B = B; a.h = h * n; a.g = g; a.d = d; a.m = (h / g) * n; a.n = n;
     a.t_cap = t_cap; a.cap_len = t_cap;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
-    a.len_add = k_new != nullptr ? 1 : 0;
+    a.len_add = k_new != nullptr ? n : 0;
     a.k_new = k_new; a.v_new = v_new;
     return run_decode(a, dtype, t_cap, num_splits, workspace, workspace_bytes, stream);
 }
@@ -382,26 +386,28 @@ static int decode_contiguous(const void* q, const void* k_new, const void* v_new
 static int decode_paged(const void* q, const void* k_new, const void* v_new, const void* k_pool,
                         const void* v_pool, const int32_t* block_table, int max_blocks,
                         int block_size, int num_blocks, const int32_t* seq_lens, int B, int h,
-                        int g, int d, float scale, int dtype, int num_splits, void* workspace,
-                        size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+                        int g, int d, int n, float scale, int dtype, int num_splits,
+                        void* workspace, size_t workspace_bytes, float* out, float* lse,
+                        hipStream_t stream) {
     int st = check_common(q, k_pool, v_pool, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
-    if (max_blocks <= 0 || num_blocks <= 0) return KVC_ERR_INVALID;
+    if (max_blocks <= 0 || num_blocks <= 0 || n <= 0) return KVC_ERR_INVALID;
     if (B > 0 && block_table == nullptr) return KVC_ERR_INVALID;
     const int lg = ilog2_exact(block_size);
     if (block_size < 8 || block_size > 256 || lg < 0) return KVC_ERR_INVALID;
     const long cap = (long)max_blocks * block_size;
     if (cap > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;
+    if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
     DecodeArgs a{};
     a.q = q; a.k = k_pool; a.v = v_pool; a.seq_lens = seq_lens;
     a.block_table = block_table; a.max_blocks = max_blocks; a.block_size = block_size;
     a.log2_bs = lg; a.num_blocks = num_blocks;
-    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g;
+    a.B = B; a.h = h * n; a.g = g; a.d = d; a.m = (h / g) * n; a.n = n;
     a.t_cap = 0; a.cap_len = (int)cap;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
-    a.len_add = k_new != nullptr ? 1 : 0;
+    a.len_add = k_new != nullptr ? n : 0;
     a.k_new = k_new; a.v_new = v_new;
     return run_decode(a, dtype, (int)cap, num_splits, workspace, workspace_bytes, stream);
 }
@@ -410,7 +416,7 @@ int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
                          float scale, int dtype, int num_splits, void* workspace,
                          size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
-    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, t_cap,
+    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, 1, t_cap,
                              scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
@@ -421,7 +427,7 @@ int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_
                                size_t workspace_bytes, float* out, float* lse,
                                hipStream_t stream) {
     return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
-                        num_blocks, seq_lens, B, h, g, d, scale, dtype, num_splits, workspace,
+                        num_blocks, seq_lens, B, h, g, d, 1, scale, dtype, num_splits, workspace,
                         workspace_bytes, out, lse, stream);
 }
 
@@ -432,7 +438,7 @@ int kvc_append_decode_attention(const void* q, const void* k_new, const void* v_
                                 float* out, float* lse, hipStream_t stream) {
     if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
     return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
-                             seq_lens_before, B, h, g, d, t_cap, scale, dtype, num_splits,
+                             seq_lens_before, B, h, g, d, 1, t_cap, scale, dtype, num_splits,
                              workspace, workspace_bytes, out, lse, stream);
 }
 
@@ -445,7 +451,52 @@ int kvc_append_decode_attention_paged(const void* q, const void* k_new, const vo
                                       hipStream_t stream) {
     if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
     return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
-                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, scale,
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, 1, scale,
+                        dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                               int t_cap, float scale, int dtype, int num_splits, void* workspace,
+                               size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, n, t_cap,
+                             scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_decode_attention_multi_paged(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int max_blocks, int block_size,
+                                     int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                                     int d, int n, float scale, int dtype, int num_splits,
+                                     void* workspace, size_t workspace_bytes, float* out,
+                                     float* lse, hipStream_t stream) {
+    return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
+                        num_blocks, seq_lens, B, h, g, d, n, scale, dtype, num_splits, workspace,
+                        workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_multi(const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache,
+                                      const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                      int n, int t_cap, float scale, int dtype, int num_splits,
+                                      void* workspace, size_t workspace_bytes, float* out,
+                                      float* lse, hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
+                             seq_lens_before, B, h, g, d, n, t_cap, scale, dtype, num_splits,
+                             workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_multi_paged(const void* q, const void* k_new, const void* v_new,
+                                            void* k_pool, void* v_pool,
+                                            const int32_t* block_table, int max_blocks,
+                                            int block_size, int num_blocks,
+                                            const int32_t* seq_lens_before, int B, int h, int g,
+                                            int d, int n, float scale, int dtype, int num_splits,
+                                            void* workspace, size_t workspace_bytes, float* out,
+                                            float* lse, hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, n, scale,
                         dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 

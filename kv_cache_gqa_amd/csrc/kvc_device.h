@@ -123,33 +123,41 @@ __device__ __forceinline__ int attended_len(const DecodeArgs& a, int raw) {
     return L < 0 ? 0 : (L > a.cap_len ? a.cap_len : (int)L);
 }
 
-// Position of sequence b's new token when the kernel itself appends it (it
-// is then read from k_new / v_new), else -1.  When attended it is the last
-// attended position.
-__device__ __forceinline__ int new_pos(const DecodeArgs& a, int b) {
-    return a.k_new != nullptr ? a.seq_lens[b] : -1;
+// Positions query token t (of the n per sequence) sees, from the raw
+// seq_lens entry: raw + len_add - (n - 1 - t), clamped to [0, cap_len].  The
+// last token sees the whole attended length.
+__device__ __forceinline__ int visible_len(const DecodeArgs& a, int raw, int t) {
+    const long L = (long)raw + a.len_add - (a.n - 1 - t);
+    return L < 0 ? 0 : (L > a.cap_len ? a.cap_len : (int)L);
 }
 
-// bf16, d = 128: write the new token's K and V rows of unit (b, j) into the
-// cache slot of position p (16 bytes per lane; lanes 0-15 K, 16-31 V; other
-// lanes do nothing).  Paged: skipped when the block-table entry is not a
-// valid block, as the append entry point does.
-__device__ __forceinline__ void store_new_row_bf16_d128(const DecodeArgs& a, int b, int j, int p,
-                                                        int lane) {
-    if (lane >= 32) return;
-    long row;
-    if (a.block_table != nullptr) {
-        const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
-        if (phys < 0 || phys >= a.num_blocks) return;
-        row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
-    } else {
-        row = ((long)b * a.g + j) * a.t_cap + p;
+// bf16, d = 128: write the appended tokens at positions [lo, hi) of unit
+// (b, j) into their cache slots.  Position p holds new token p - raw of
+// k_new / v_new [B, g, n, d].  Each of the `nthreads` threads moves 16-byte
+// pieces (32 per position: 16 of K, 16 of V).  Paged: a position whose
+// block-table entry is not a valid block is skipped, as the append entry
+// point skips it.
+__device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, int b, int j, int raw,
+                                                         int lo, int hi, int tid, int nthreads) {
+    const long unit = (long)b * a.g + j;
+    for (int idx = tid; idx < (hi - lo) * 32; idx += nthreads) {
+        const int p = lo + (idx >> 5);
+        const int part = idx & 31;
+        long row;
+        if (a.block_table != nullptr) {
+            const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+            if (phys < 0 || phys >= a.num_blocks) continue;
+            row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+        } else {
+            row = unit * a.t_cap + p;
+        }
+        const bool is_v = part >= 16;
+        const int c = part & 15;
+        const uint4* src = reinterpret_cast<const uint4*>(is_v ? a.v_new : a.k_new) +
+                           (unit * a.n + (p - raw)) * 16 + c;
+        uint4* dst = reinterpret_cast<uint4*>(const_cast<void*>(is_v ? a.v : a.k)) + row * 16 + c;
+        *dst = *src;
     }
-    const bool is_v = lane >= 16;
-    const int c = lane & 15;
-    const uint4* src = reinterpret_cast<const uint4*>(is_v ? a.v_new : a.k_new) + ((long)b * a.g + j) * 16 + c;
-    uint4* dst = reinterpret_cast<uint4*>(const_cast<void*>(is_v ? a.v : a.k)) + row * 16 + c;
-    *dst = *src;
 }
 
 }  // namespace kvc

@@ -63,6 +63,11 @@ struct DecodeArgs {
     int len_add;
     const void* k_new;
     const void* v_new;
+    // Queries per sequence (new tokens attending at once).  The kernels see
+    // h = heads * n query rows per sequence and m = (heads / g) * n rows per
+    // unit; row i is head i / n, token i % n, and token t sees
+    // raw + len_add - (n - 1 - t) positions (clamped).
+    int n;
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
     // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
     float* part_o;
@@ -84,7 +89,7 @@ const void* mfma_kernel(int m, bool paged, bool stream, int waves);
 const void* valu_kernel(int m, bool paged, bool stream, int waves);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
-                         const int32_t* seq_lens_before, int B, int g, int d, int capacity,
+                         const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,
                          int elem_bytes, hipStream_t s);
 
 // Which decode kernel a configuration uses (exposed for tests and tools).

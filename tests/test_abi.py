@@ -178,3 +178,26 @@ def test_fused_validation_codes():
     assert fp(*bad) == INVALID
     bad = list(pargs); bad[7] = 12                   # block size not a power of two
     assert fp(*bad) == INVALID
+
+
+def test_multi_validation_codes():
+    lib = kvc.load_library()
+    f = lib.kvc_decode_attention_multi
+    # every call below fails validation before any HIP call
+    args = [FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 4, 64, 0.1, 1, 1, None, 0, FAKE, FAKE, None]
+    bad = list(args); bad[8] = 0                     # n = 0
+    assert f(*bad) == INVALID
+    bad = list(args); bad[8] = 10000                 # h * n > 65535
+    assert f(*bad) == UNSUPPORTED
+    bad = list(args); bad[12] = 2                    # split plan needs a workspace
+    assert f(*bad) == WORKSPACE
+    fa = lib.kvc_append_decode_attention_multi
+    aargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 4, 64, 0.1, 1, 1, None, 0, FAKE,
+             FAKE, None]
+    bad = list(aargs); bad[1] = None                 # k_new missing
+    assert fa(*bad) == INVALID
+    bad = list(aargs); bad[10] = -1                  # n < 1
+    assert fa(*bad) == INVALID
+    # the workspace of a multi call is that of h * n query rows
+    need = lib.kvc_decode_workspace_bytes(2, 8 * 4, 2, 128, 1, 64, 2, 0)
+    assert need > lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2, 0) > 0
