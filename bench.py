@@ -128,15 +128,16 @@ def stored_traffic(workload: str):
     return int(kv["traffic_bytes_per_call"])
 
 
-def algorithmic_bytes(w, lengths_after, nblocks=None):
+def algorithmic_bytes(w, lengths_after, nblocks=None, n=1):
     """Bytes one step must move: KV read, q read, out and lse written
-    (float32), the appended K/V written, and the block table read (paged)."""
+    (float32), the appended K/V written, and the block table read (paged).
+    n new tokens (queries) per sequence."""
     B, h, g, d, eb = w.B, w.h, w.g, w.d, w.elem_bytes
     kv_read = 2 * int(lengths_after.sum()) * g * d * eb
-    q_read = B * h * d * eb
-    out_write = B * h * d * 4 + B * h * 4
-    append_write = 2 * B * g * d * eb
-    append_read = 2 * B * g * d * eb
+    q_read = B * h * n * d * eb
+    out_write = B * h * n * d * 4 + B * h * n * 4
+    append_write = 2 * B * g * n * d * eb
+    append_read = 2 * B * g * n * d * eb
     table = 0 if nblocks is None else int(nblocks.sum()) * 4
     decode = kv_read + q_read + out_write + table + B * 4
     # One-call step: the new token's K/V are read once (from k_new / v_new,
@@ -183,6 +184,9 @@ def main():
     ap.add_argument("--separate", action="store_true",
                     help="a step is kvc_append then the decode call (two calls) instead of one "
                          "kvc_append_decode_attention call")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="new tokens per sequence in one step (draft tokens checked at once, or a "
+                         "prefill chunk after the cached prefix): kvc_append_decode_attention_multi")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -233,23 +237,39 @@ def main():
     k0, v0 = k_src.to(dev), v_src.to(dev)
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
-    q = x["q"].to(dev)
-    k_new, v_new = x["k_new"].to(dev), x["v_new"].to(dev)
+    nq = args.queries
+    if nq < 1 or (nq > 1 and (args.separate or w.paged or nq > w.cap_pad)):
+        print(f"--queries takes n >= 1; n > 1 only with the one-call step on a contiguous "
+              f"workload, n <= {w.cap_pad} (the spare capacity)", file=sys.stderr)
+        sys.exit(2)
+    if nq > 1:
+        gen = torch.Generator().manual_seed(w.seed + 77)
+        q = W.randn((w.B, w.h, nq, w.d), w.torch_dtype, gen).to(dev)
+        k_new = W.randn((w.B, w.g, nq, w.d), w.torch_dtype, gen).to(dev)
+        v_new = W.randn((w.B, w.g, nq, w.d), w.torch_dtype, gen).to(dev)
+    else:
+        q = x["q"].to(dev)
+        k_new, v_new = x["k_new"].to(dev), x["v_new"].to(dev)
     sl_before, sl_after = x["seq_lens_before"].to(dev), x["seq_lens_after"].to(dev)
     bt = x["block_table"].to(dev) if w.paged else None
-    out = torch.empty((w.B, w.h, w.d), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.B, w.h), dtype=torch.float32, device=dev)
+    if nq > 1:
+        out = torch.empty((w.B, w.h, nq, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.B, w.h, nq), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((w.B, w.h, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.B, w.h), dtype=torch.float32, device=dev)
+    hq = w.h * nq  # query rows per sequence (the planning calls take h * n)
     if w.paged:
         max_len = bt.shape[1] * x["block_size"]
     else:
         max_len = k0.shape[2]
-    ws_bytes = kvc.workspace_bytes(w.B, w.h, w.g, w.d, max_len, ns, dtype=w.torch_dtype,
+    ws_bytes = kvc.workspace_bytes(w.B, hq, w.g, w.d, max_len, ns, dtype=w.torch_dtype,
                                    paged=w.paged)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    split_mode, chunk_len, num_chunks = kvc.plan(w.B, w.h, w.g, w.d, max_len, ns,
+    split_mode, chunk_len, num_chunks = kvc.plan(w.B, hq, w.g, w.d, max_len, ns,
                                                  dtype=w.torch_dtype, paged=w.paged)
     waves, n_wgs, launch_chunk, launch_chunks = kvc.launch_shape(
-        w.B, w.h, w.g, w.d, max_len, ns, dtype=w.torch_dtype, paged=w.paged)
+        w.B, hq, w.g, w.d, max_len, ns, dtype=w.torch_dtype, paged=w.paged)
     merged = split_mode == "stream" or launch_chunks > 1
 
     if args.calibration_copy_mib > 0:
@@ -277,8 +297,13 @@ def main():
 
     def fused_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        kvc.append_decode(q, k_new, v_new, kc, vc, sl_before, block_table=bt, scale=x["scale"],
-                          num_splits=ns, workspace=ws, out=out, lse=lse)
+        if nq > 1:
+            kvc.append_decode_multi(q, k_new, v_new, kc, vc, sl_before, block_table=bt,
+                                    scale=x["scale"], num_splits=ns, workspace=ws, out=out,
+                                    lse=lse)
+        else:
+            kvc.append_decode(q, k_new, v_new, kc, vc, sl_before, block_table=bt, scale=x["scale"],
+                              num_splits=ns, workspace=ws, out=out, lse=lse)
 
     def step(i):
         if args.separate:
@@ -367,15 +392,15 @@ def main():
     torch.cuda.synchronize()
     dec_avg_ms = d_start.elapsed_time(d_end) / (reps * copies)
 
-    nbytes = algorithmic_bytes(w, x["seq_lens_after"], nblocks)
+    nbytes = algorithmic_bytes(w, x["seq_lens_before"] + nq, nblocks, n=nq)
     # stored counter runs are of the default (one-call) step
-    traffic = None if args.separate else stored_traffic(w.name)
+    traffic = None if (args.separate or nq > 1) else stored_traffic(w.name)
     call_bytes = nbytes["decode"] if args.separate else nbytes["fused"]
     achieved_gbs = call_bytes / (dec_avg_ms * 1e-3) / 1e9
-    tokens_per_s = w.B / (ms_per_step * 1e-3)
+    tokens_per_s = w.B * nq / (ms_per_step * 1e-3)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and nq == 1:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, x, w.paged)
 
@@ -397,12 +422,14 @@ def main():
             "kv_len_before_step": w.T if w.T is not None else list(w.T_range),
             "paged": w.paged, "block_size": w.block_size if w.paged else None,
             "num_splits": ns, "split": split_mode, "chunk_len": chunk_len,
-            "num_chunks": num_chunks,
+            "num_chunks": num_chunks, "queries_per_sequence": nq,
             "launch": {"waves_per_workgroup": waves, "workgroups": n_wgs,
                        "chunk_len": launch_chunk, "chunks": launch_chunks},
             "cache_copies_rotated": copies, "parallelism": "single GPU",
         },
-        "step": "kvc_append + decode call" if args.separate else "one kvc_append_decode_attention call",
+        "step": ("kvc_append + decode call" if args.separate
+                 else f"one kvc_append_decode_attention_multi call ({nq} tokens per sequence)"
+                 if nq > 1 else "one kvc_append_decode_attention call"),
         "step_hbm_gbs": round((nbytes["step"] if args.separate else nbytes["fused"])
                               / (ms_per_step * 1e-3) / 1e9, 1),
         "timing": "eager" if args.eager else "HIP graphs of whole steps (one step per cache copy)",

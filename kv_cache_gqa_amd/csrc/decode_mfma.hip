@@ -99,13 +99,14 @@ struct MfmaEngine {
         __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     };
 
-    // The m query heads of KV head j of sequence b over positions [s, e)
-    // (possibly empty).  Called by all 64*W threads.
+    // Query rows row0 .. row0 + 16*NQT - 1 (those below a.m) of KV head j
+    // of sequence b over positions [s, e) (possibly empty).  Called by all
+    // 64*W threads.
     __device__ static void segment(const DecodeArgs& a, Shared& sh, int b, int j, int s, int e,
-                                   const SegDst& dst) {
+                                   const SegDst& dst, int row0 = 0) {
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int G = lane >> 4, col = lane & 15;
-        const int m = a.m;
+        const int m = min(a.m - row0, 16 * NQT);  // rows of this slice
         __syncthreads();  // the previous segment is done with the shared memory
 
         const uint16_t* K = (const uint16_t*)a.k;
@@ -119,7 +120,7 @@ struct MfmaEngine {
             const int qi = 16 * qt + col;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                qb[qt][ks] = qi < m ? ld16(Q + (((long)b * a.h + (long)j * m + qi) * kD + 32 * ks + 8 * G))
+                qb[qt][ks] = qi < m ? ld16(Q + (((long)b * a.h + (long)j * a.m + row0 + qi) * kD + 32 * ks + 8 * G))
                                     : make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -158,7 +159,7 @@ struct MfmaEngine {
         const int raw = a.seq_lens[b];
         int lim[NQT];
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) lim[qt] = visible_len(a, raw, (16 * qt + col) % a.n);
+        for (int qt = 0; qt < NQT; ++qt) lim[qt] = visible_len(a, raw, (row0 + 16 * qt + col) % a.n);
 
         // A call that appends reads its new tokens (positions raw .. raw+n-1,
         // the last ones of the unit) from k_new / v_new and writes them into
@@ -421,13 +422,14 @@ __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED, W>;
     __shared__ typename E::Shared sh;
-    const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int j = blockIdx.y / a.slices, row0 = (blockIdx.y - j * a.slices) * 16 * NQT;
     const int L = attended_len(a, a.seq_lens[b]);
     const int p0 = c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, L);
     const bool single = a.num_chunks == 1;
     if (p0 >= L && !single) return;  // past the end: the merge skips this chunk
-    E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
+    E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c, row0), row0);
 }
 
 template <int NQT, bool PAGED, int W>
@@ -463,11 +465,14 @@ const void* mfma_kernel(int m, bool paged, bool stream, int waves) {
 }
 
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
-    if (a.m > 32) return hipErrorInvalidValue;
-    const void* fn = mfma_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves);
+    // more than 32 rows: slices of 32 (chunked mode only)
+    if (a.slices < 1 || (a.m > 32 * a.slices) || (a.slices > 1 && (a.stream || a.m <= 32)))
+        return hipErrorInvalidValue;
+    const void* fn = mfma_kernel(min(a.m, 32), a.block_table != nullptr, a.stream != 0, a.waves);
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
-                               : dim3((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);
+                               : dim3((unsigned)a.num_chunks, (unsigned)(a.g * a.slices),
+                                      (unsigned)a.B);
     void* args[] = {const_cast<DecodeArgs*>(&a)};
     return hipLaunchKernel(fn, grid, dim3(64 * a.waves), args, 0, s);
 }

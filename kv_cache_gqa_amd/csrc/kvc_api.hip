@@ -40,12 +40,14 @@ Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
 }
 
 KernelKind choose_kernel(int dtype, int d, int m) {
-    if (dtype == KVC_BF16 && d == 128) {
-        if (m <= 3) return kValu;
-        if (m <= 32) return kMfma;
-    }
+    if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : kMfma;
     return kGeneric;
 }
+
+// Work-groups per unit that split its query rows: the MFMA kernels hold at
+// most 32 rows, so more rows (several new tokens per sequence) take slices
+// of 32, each reading the unit's K/V.
+static int row_slices(KernelKind kind, int m) { return (kind == kMfma && m > 32) ? (m + 31) / 32 : 1; }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -91,13 +93,14 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     // Stream mode keeps global positions in 64-bit products p * total with
     // p <= 1024: it is used only while B * g * max_seq_len < 2^40.
     const bool small_enough = (long double)B * g * max_seq_len < (long double)(1LL << 40);
-    const bool can_stream = sc.kind != kGeneric && B <= kStreamMaxB && small_enough;
+    const int slices = row_slices(sc.kind, h / g);
+    const bool can_stream = sc.kind != kGeneric && slices == 1 && B <= kStreamMaxB && small_enough;
     sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM || (num_splits == 0 && paged));
     sc.auto_chunks = !sc.stream && num_splits <= 0 && sc.kind != kGeneric;
     if (sc.auto_chunks) {
         // workspace bound: every slot of a 256-CU device, 4 work-groups each
         sc.plan = plan_for_chunks(max_seq_len, chunks_for_slots((long)kStreamMaxCUs * kStreamMaxWgPerCu,
-                                                                 B, g, max_seq_len));
+                                                                 B * slices, g, max_seq_len));
     } else {
         sc.plan = make_plan(B, g, max_seq_len, num_splits > 0 ? num_splits : 0);
     }
@@ -220,6 +223,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     a.stream = sc.stream ? 1 : 0;
     a.num_wgs = 0;
     a.waves = sc.kind == kGeneric ? 1 : 4;
+    a.slices = row_slices(sc.kind, a.m);
     if (sc.stream) {
         long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4), 4);
         // No more work-groups than 256-position pieces of the largest possible batch.
@@ -227,7 +231,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
         if (P > pieces) P = pieces;
         a.num_wgs = (int)(P < 1 ? 1 : P);
     } else if (sc.auto_chunks) {
-        const AutoShape sh = auto_shape(sc.kind, a.m, a.B, a.g, max_len);
+        const AutoShape sh = auto_shape(sc.kind, a.m < 32 ? a.m : 32, a.B * a.slices, a.g, max_len);
         a.waves = sh.waves;
         // One chunk per unit may exceed kMaxChunk: the engines walk a chunk in
         // windows of at most kMaxChunk positions.
@@ -326,7 +330,9 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.cap_len = max_seq_len;
     resolve_launch(a, sc, paged != 0, max_seq_len);
     if (waves) *waves = a.waves;
-    const int per_chunk = sc.kind == kGeneric ? h : g;   // the generic kernel: one wavefront per query head
+    // the generic kernel: one wavefront per query row; the others: per unit
+    // and row slice
+    const int per_chunk = sc.kind == kGeneric ? h : g * a.slices;
     if (num_wgs) *num_wgs = a.stream ? a.num_wgs : a.num_chunks * per_chunk * B;
     if (chunk_len) *chunk_len = a.stream ? 0 : a.chunk_len;
     if (num_chunks) *num_chunks = a.stream ? 0 : a.num_chunks;

@@ -94,15 +94,16 @@ struct SegDst {
     bool final_;
 };
 
-__device__ __forceinline__ SegDst final_dst(const DecodeArgs& a, int b, int j) {
-    const long row = (long)b * a.h + (long)j * a.m;
+__device__ __forceinline__ SegDst final_dst(const DecodeArgs& a, int b, int j, int row0 = 0) {
+    const long row = (long)b * a.h + (long)j * a.m + row0;
     return SegDst{a.out + row * a.d, a.lse + row, (long)a.d, 1, true};
 }
 
-// Chunked mode: chunk c of the rows of (b, j); a single chunk writes final rows.
-__device__ __forceinline__ SegDst chunk_dst(const DecodeArgs& a, int b, int j, int c) {
-    if (a.num_chunks == 1) return final_dst(a, b, j);
-    const long row = (long)b * a.h + (long)j * a.m;
+// Chunked mode: chunk c of the rows of (b, j) from row0 on; a single chunk
+// writes final rows.
+__device__ __forceinline__ SegDst chunk_dst(const DecodeArgs& a, int b, int j, int c, int row0 = 0) {
+    if (a.num_chunks == 1) return final_dst(a, b, j, row0);
+    const long row = (long)b * a.h + (long)j * a.m + row0;
     return SegDst{a.part_o + (row * a.num_chunks + c) * a.d, a.part_lse + row * a.num_chunks + c,
                   (long)a.num_chunks * a.d, (long)a.num_chunks, false};
 }

@@ -68,6 +68,10 @@ struct DecodeArgs {
     // unit; row i is head i / n, token i % n, and token t sees
     // raw + len_add - (n - 1 - t) positions (clamped).
     int n;
+    // Query-row slices per unit (chunked mode): more than 32 rows per KV head
+    // are served by ceil(m / 32) work-groups of 32 rows each, blockIdx.y =
+    // j * slices + slice.
+    int slices;
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
     // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
     float* part_o;

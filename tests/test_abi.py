@@ -59,10 +59,13 @@ def test_plan_modes():
         assert kvc.plan(B, h, g, 128, T, 0) == ("auto_chunks", 0, 0)
         assert kvc.plan(B, h, g, 128, T, 0, paged=True) == ("stream", 0, 0)
         assert kvc.plan(B, h, g, 128, T, kvc.SPLITS_STREAM) == ("stream", 0, 0)
-    # the generic kernel (fp32, other head dims, m > 32) always chunks
+    # the generic kernel (fp32, other head dims) always chunks
     assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
-    assert kvc.plan(2, 64, 1, 128, 4096, 0, paged=True)[0] == "chunks"
-    assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM)[0] == "chunks"
+    assert kvc.plan(2, 8, 2, 64, 4096, 0, paged=True)[0] == "chunks"
+    assert kvc.plan(2, 8, 2, 128, 4096, kvc.SPLITS_STREAM, dtype=torch.float32)[0] == "chunks"
+    # more than 32 query rows per KV head: MFMA row slices, never stream mode
+    assert kvc.plan(2, 64, 1, 128, 4096, 0, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"
     # stream mode needs B <= 1024
     assert kvc.plan(2048, 8, 8, 128, 512, 0, paged=True)[0] == "auto_chunks"
     # chunks: a multiple of 32, covering max_seq_len, at most 4096

@@ -27,8 +27,10 @@ CASES = [
     ("mfma_rows16", dict(h=8, g=2, d=128, dtype="bf16"), 4),
     ("mfma_rows32", dict(h=16, g=2, d=128, dtype="bf16"), 4),
     ("mfma_rows30", dict(h=6, g=1, d=128, dtype="bf16"), 5),
-    ("generic_rows64", dict(h=16, g=2, d=128, dtype="bf16"), 8),
+    ("mfma_slices_64", dict(h=16, g=2, d=128, dtype="bf16"), 8),
+    ("mfma_slices_33", dict(h=11, g=1, d=128, dtype="bf16"), 3),
     ("generic_f32_d16", dict(h=4, g=2, d=16, dtype="f32"), 3),
+    ("generic_f32_rows40", dict(h=8, g=1, d=16, dtype="f32"), 5),
 ]
 BEFORE = [0, 1, 14, 15, 16, 29, 30, 31, 32, 127, 1000, 4093, 4096, 4200]
 T_CAP = 4210
@@ -150,7 +152,7 @@ def test_multi_capacity_clamp():
                      f"clamp t={t}")
 
 
-@pytest.mark.parametrize("n", [2, 4])
+@pytest.mark.parametrize("n", [2, 4, 8])
 def test_multi_full_size_70b(n):
     """The 70B GQA shape (B=32, h=64, g=8, d=128, 4096 cached positions) with
     n draft tokens per sequence, in the launch the benchmark times."""
