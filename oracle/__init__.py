@@ -16,6 +16,11 @@ module only marshals arrays into it.  Pages followed:
   (plumephp.com), sections 2.2-2.5 (m, l, lse = m + log l, sequence split),
   3.2 (size formula), 4.2-4.3 (block table lookup), 5.3 (speculative
   decoding: several draft tokens checked in one pass).
+* Sliding window (plumephp.com section 5.2: a token attends within a local
+  window to its left; zwjcode.cn section 10: a window cache keeps only the
+  last W positions, so its memory is bounded): the token at position x sees
+  positions max(0, x + 1 - W) .. x, the last W including itself.  A ring
+  cache of t_cap slots keeps position p in slot p mod t_cap.
 * Several new tokens at once (a prefill after a cached prefix, limoncc.com
   section 5.2; draft tokens, plumephp.com section 5.3): token t of a sequence
   with P cached positions sits at position P + t and sees positions 0..P + t
@@ -49,6 +54,9 @@ def configure(lib):
     lib.kvo_decode_split.restype = None
     lib.kvo_append.argtypes = [vp, vp, vp, vp, ip, vp, ip, ip, vp, ip, ip, ip, ip]
     lib.kvo_append.restype = None
+    lib.kvo_decode_range.argtypes = [vp, vp, vp, ip, vp, ip, ip, vp, vp, ip, ip, ip, ip, ip, dp,
+                                     vp, vp, ip]
+    lib.kvo_decode_range.restype = None
     return lib
 
 
@@ -241,6 +249,102 @@ def decode_multi(q, k, v, seq_lens_before, scale, block_table=None, block_size=1
         o, l = decode(np.ascontiguousarray(qa[:, :, t]), k, v,
                       _multi_visible(before, t).astype(np.int32), scale, block_table=block_table,
                       block_size=block_size, nthreads=nthreads)
+        out[:, :, t] = o
+        lse[:, :, t] = l
+    return out, lse
+
+
+def decode_range(q, k, v, starts, seq_lens, scale, block_table=None, block_size=16, nthreads=0):
+    """Like ``decode`` over positions [starts[b], seq_lens[b]) only."""
+    qa, qd = _raw(q)
+    ka, kd = _raw(k)
+    va, vd = _raw(v)
+    dt = _same_dtype(qd, kd, vd)
+    st = _i32(starts)
+    sl = _i32(seq_lens)
+    B, h, d = qa.shape
+    if block_table is None:
+        _, g, t_cap, _ = ka.shape
+        bt, max_blocks, bsz = None, 0, 0
+    else:
+        bt = _i32(block_table)
+        _, g, bsz, _ = ka.shape
+        assert bsz == block_size
+        max_blocks = bt.shape[1]
+        t_cap = 0
+    out = np.zeros((B, h, d), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    sc = float(np.float32(scale))
+    _load().kvo_decode_range(_ptr(qa), _ptr(ka), _ptr(va), dt,
+                             _ptr(bt) if bt is not None else None, max_blocks, bsz,
+                             _ptr(st), _ptr(sl), B, h, g, d, t_cap, sc, _ptr(out), _ptr(lse),
+                             int(nthreads))
+    return out, lse
+
+
+def _window_start(visible, window):
+    """First position a token sees when it sees ``visible`` positions under a
+    sliding window of ``window`` (0: no window)."""
+    if window <= 0:
+        return np.zeros_like(visible)
+    return np.maximum(visible - window, 0)
+
+
+def _ring_slot(p, t_cap):
+    return p % t_cap
+
+
+def append_window(k_new, v_new, k_cache, v_cache, seq_lens_before, ring=False, block_table=None):
+    """Write n new tokens per sequence (k_new, v_new [B,g,n,d]) at positions
+    seq_lens_before[b] + t; a ring cache (contiguous [B,g,t_cap,d]) keeps
+    position p in slot p mod t_cap.  Returns raw numpy caches."""
+    if not ring:
+        return append_multi(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table)
+    kn, _ = _raw(k_new)
+    vn, _ = _raw(v_new)
+    t_cap = _raw(k_cache)[0].shape[2]
+    before = _i32(seq_lens_before)
+    kc, vc = k_cache, v_cache
+    for t in range(kn.shape[2]):
+        slot = _ring_slot(_multi_position(before, t), t_cap).astype(np.int32)
+        kc, vc = append(np.ascontiguousarray(kn[:, :, t]), np.ascontiguousarray(vn[:, :, t]), kc, vc,
+                        slot)
+    return kc, vc
+
+
+def _linearize_ring(cache_raw, lo, hi):
+    """[B,g,max(hi),d] raw array holding position p of sequence b (lo[b] <= p
+    < hi[b]) taken from ring slot p mod t_cap; other positions are zero."""
+    B, g, t_cap, d = cache_raw.shape
+    L = int(max(int(np.max(hi)) if len(hi) else 0, 1))
+    lin = np.zeros((B, g, L, d), dtype=cache_raw.dtype)
+    for b in range(B):
+        p = np.arange(int(lo[b]), int(hi[b]))
+        lin[b, :, p] = np.moveaxis(cache_raw[b][:, _ring_slot(p, t_cap)], 1, 0)
+    return lin
+
+
+def decode_window(q, k, v, seq_lens_before, scale, window, ring=False, block_table=None,
+                  block_size=16, nthreads=0):
+    """q [B,h,n,d]: token t of sequence b sits at position seq_lens_before[b]
+    + t and attends to positions max(0, x + 1 - window) .. x (window 0: all
+    of 0 .. x) of a cache that already holds every new token (a ring cache
+    when ``ring``).  Returns out [B,h,n,d], lse [B,h,n] (float64)."""
+    qa, _ = _raw(q)
+    before = _i32(seq_lens_before)
+    B, h, n, d = qa.shape
+    out = np.zeros((B, h, n, d), dtype=np.float64)
+    lse = np.zeros((B, h, n), dtype=np.float64)
+    for t in range(n):
+        hi = _multi_visible(before, t).astype(np.int32)
+        lo = _window_start(hi, window).astype(np.int32)
+        kk, vv = k, v
+        if ring:
+            kk = _linearize_ring(_raw(k)[0], lo, hi)
+            vv = _linearize_ring(_raw(v)[0], lo, hi)
+        o, l = decode_range(np.ascontiguousarray(qa[:, :, t]), kk, vv, lo, hi, scale,
+                            block_table=None if ring else block_table, block_size=block_size,
+                            nthreads=nthreads)
         out[:, :, t] = o
         lse[:, :, t] = l
     return out, lse

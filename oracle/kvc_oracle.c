@@ -126,10 +126,10 @@ static void attend_range(const void* q, const void* kc, const void* vc, int dtyp
  * Query head i reads KV head j = (i*g)/h ([P1] 三 3.3).  Positions
  * >= seq_lens[b] are never read ([P3] section 10).  A sequence of length 0
  * gets out = 0 and lse = -inf.  out = acc / l, lse = m + ln l ([P4] 2.3). */
-void kvo_decode(const void* q, const void* k, const void* v, int dtype,
-                const int32_t* block_table, int max_blocks, int block_size,
-                const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
-                double scale, double* out, double* lse, int nthreads) {
+static void decode_rows(const void* q, const void* k, const void* v, int dtype,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        const int32_t* starts, const int32_t* seq_lens, int B, int h, int g,
+                        int d, int t_cap, double scale, double* out, double* lse, int nthreads) {
     int max_len = 0;
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] > max_len) max_len = seq_lens[b];
@@ -148,7 +148,7 @@ void kvo_decode(const void* q, const void* k, const void* v, int dtype,
             int j = (int)(((long)i * g) / h);
             double m, l;
             attend_range(q, k, v, dtype, block_table, max_blocks, block_size, b, i, j,
-                         0, seq_lens[b], h, g, d, t_cap, scale, s, acc, &m, &l);
+                         starts ? starts[b] : 0, seq_lens[b], h, g, d, t_cap, scale, s, acc, &m, &l);
             double* o = out + (size_t)bi * d;
             if (l > 0.0) {
                 for (int kk = 0; kk < d; ++kk) o[kk] = acc[kk] / l;
@@ -161,6 +161,26 @@ void kvo_decode(const void* q, const void* k, const void* v, int dtype,
         free(s);
         free(acc);
     }
+}
+
+void kvo_decode(const void* q, const void* k, const void* v, int dtype,
+                const int32_t* block_table, int max_blocks, int block_size,
+                const int32_t* seq_lens, int B, int h, int g, int d, int t_cap,
+                double scale, double* out, double* lse, int nthreads) {
+    decode_rows(q, k, v, dtype, block_table, max_blocks, block_size, NULL, seq_lens, B, h, g, d,
+                t_cap, scale, out, lse, nthreads);
+}
+
+/* Decode attention over positions [starts[b], seq_lens[b]) only: the last
+ * positions a sliding window keeps ([P4] 5.2: each token attends within a
+ * local window to its left; [P3] section 10: a window cache keeps only the
+ * most recent W positions).  Otherwise as kvo_decode. */
+void kvo_decode_range(const void* q, const void* k, const void* v, int dtype,
+                      const int32_t* block_table, int max_blocks, int block_size,
+                      const int32_t* starts, const int32_t* seq_lens, int B, int h, int g, int d,
+                      int t_cap, double scale, double* out, double* lse, int nthreads) {
+    decode_rows(q, k, v, dtype, block_table, max_blocks, block_size, starts, seq_lens, B, h, g, d,
+                t_cap, scale, out, lse, nthreads);
 }
 
 /* Split reference: the context of every sequence is cut into chunks of

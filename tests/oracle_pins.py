@@ -395,6 +395,82 @@ def pin_multi_query_equals_causal_prefill():
         assert np.array_equal(op, o) and np.array_equal(lp, l)
 
 
+# ----------------------------------------------------------------------------
+# Sliding window ([P4] 5.2; [P3] section 10): the token at position x sees the
+# last `window` positions up to x.  Pinned by (1) the plain definition on a
+# cache cut down to those positions, (2) a window at least as long as the
+# context equal to full attention, (3) a window of 1: out is the token's own
+# V and lse its own score, (4) a ring cache of t_cap slots (position p in
+# slot p mod t_cap) filled step by step gives the linear cache's results.
+def _truncated_decode(q_t, k, v, lo, hi, scale):
+    """Single-token attention over positions [lo[b], hi[b]) by copying them
+    to the front of a fresh cache and attending to all of it."""
+    B, g, _, d = k.shape
+    L = max(int(max(hi - lo)), 1)
+    kt = torch.zeros(B, g, L, d, dtype=k.dtype)
+    vt = torch.zeros(B, g, L, d, dtype=v.dtype)
+    for b in range(B):
+        kt[b, :, : hi[b] - lo[b]] = k[b, :, lo[b]:hi[b]]
+        vt[b, :, : hi[b] - lo[b]] = v[b, :, lo[b]:hi[b]]
+    return oracle.decode(q_t, kt, vt, torch.as_tensor(hi - lo, dtype=torch.int32), scale)
+
+
+def pin_sliding_window():
+    gen = torch.Generator().manual_seed(21)
+    B, h, g, d, n, t_cap = 4, 6, 2, 8, 3, 64
+    before = np.array([0, 5, 17, 50], dtype=np.int32)
+    q = torch.randn(B, h, n, d, generator=gen)
+    k = torch.randn(B, g, t_cap, d, generator=gen)
+    v = torch.randn(B, g, t_cap, d, generator=gen)
+    sc = float(np.float32(0.3))
+    for window in (1, 2, 7, 16, 53):
+        o, l = oracle.decode_window(q, k, v, before, sc, window)
+        for t in range(n):
+            hi = before + t + 1
+            lo = np.maximum(hi - window, 0)
+            ot, lt = _truncated_decode(q[:, :, t].contiguous(), k, v, lo, hi, sc)
+            assert np.array_equal(o[:, :, t], ot) and np.array_equal(l[:, :, t], lt), (window, t)
+            if window == 1:
+                for b in range(B):
+                    x = hi[b] - 1
+                    for i in range(h):
+                        j = i * g // h
+                        assert np.array_equal(o[b, i, t], v[b, j, x].double().numpy())
+                        s = sc * float(torch.dot(q[b, i, t].double(), k[b, j, x].double()))
+                        assert abs(l[b, i, t] - s) < 1e-12
+    o_full, l_full = oracle.decode_multi(q, k, v, before, sc)
+    o_w, l_w = oracle.decode_window(q, k, v, before, sc, 10 ** 6)
+    assert np.array_equal(o_full, o_w) and np.array_equal(l_full, l_w)
+    o_0, l_0 = oracle.decode_window(q, k, v, before, sc, 0)
+    assert np.array_equal(o_full, o_0) and np.array_equal(l_full, l_0)
+
+
+def pin_ring_cache_equals_linear():
+    gen = torch.Generator().manual_seed(22)
+    B, h, g, d, window, steps, n = 2, 4, 2, 8, 5, 12, 2
+    for t_cap in (window + n - 1, window + n + 2):
+        lin_k = np.zeros((B, g, steps * n + 4, d), np.float32)
+        lin_v = np.zeros_like(lin_k)
+        ring_k = np.zeros((B, g, t_cap, d), np.float32)
+        ring_v = np.zeros_like(ring_k)
+        before = np.array([0, 3], dtype=np.int32)
+        for step in range(steps):
+            kn = torch.randn(B, g, n, d, generator=gen)
+            vn = torch.randn(B, g, n, d, generator=gen)
+            q = torch.randn(B, h, n, d, generator=gen)
+            lin_k, lin_v = oracle.append_window(kn, vn, lin_k, lin_v, before)
+            ring_k, ring_v = oracle.append_window(kn, vn, ring_k, ring_v, before, ring=True)
+            o1, l1 = oracle.decode_window(q, lin_k, lin_v, before, 0.5, window)
+            o2, l2 = oracle.decode_window(q, ring_k, ring_v, before, 0.5, window, ring=True)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2), (t_cap, step)
+            # the ring holds exactly the last t_cap positions of each sequence
+            for b in range(B):
+                end = before[b] + n
+                for p in range(max(0, end - t_cap), end):
+                    assert np.array_equal(ring_k[b, :, p % t_cap], lin_k[b, :, p])
+            before = before + n
+
+
 ALL_PINS = [
     pin_d1_worked_example,
     pin_sdpa_crosscheck,
@@ -411,4 +487,6 @@ ALL_PINS = [
     pin_tiny_brute_force,
     pin_scale_is_float32_value,
     pin_multi_query_equals_causal_prefill,
+    pin_sliding_window,
+    pin_ring_cache_equals_linear,
 ]

@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 import kvc_workloads as W
@@ -72,8 +73,11 @@ MUTATIONS = {
     "drop_scale": ("s[p - p0] = scale * dot;", "s[p - p0] = dot;"),
     "exp_sign": ("double w = exp(s[p - p0] - m);", "double w = exp(m - s[p - p0]);"),
     "lse_drops_max": ("lse[bi] = m + log(l);", "lse[bi] = log(l);"),
-    "len_off_by_one": ("0, seq_lens[b], h, g, d, t_cap, scale, s, acc, &m, &l);",
-                       "0, seq_lens[b] - (seq_lens[b] > 1), h, g, d, t_cap, scale, s, acc, &m, &l);"),
+    "len_off_by_one": ("starts ? starts[b] : 0, seq_lens[b], h, g, d, t_cap, scale, s, acc, &m, &l);",
+                       "starts ? starts[b] : 0, seq_lens[b] - (seq_lens[b] > 1), h, g, d, t_cap, "
+                       "scale, s, acc, &m, &l);"),
+    "window_start_off_by_one": ("starts ? starts[b] : 0, seq_lens[b]",
+                                "starts ? starts[b] + 1 : 0, seq_lens[b]"),
     "pv_reads_k": ("acc[k] += w * load_elem(vc, row * d + k, dtype);",
                    "acc[k] += w * load_elem(kc, row * d + k, dtype);"),
     "paged_offset": ("int offset = p % block_size;", "int offset = (p + 1) % block_size;"),
@@ -138,3 +142,27 @@ def test_planted_multi_query_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(oracle, attr, fn)
     with pytest.raises(Exception):
         P.pin_multi_query_equals_causal_prefill()
+
+
+# Plausible mistakes in the window and ring compositions.
+WINDOW_MUTATIONS = {
+    "window_one_short": ("_window_start", lambda vis, w: np.maximum(vis - w + 1, 0) if w > 0
+                         else np.zeros_like(vis)),
+    "window_one_long": ("_window_start", lambda vis, w: np.maximum(vis - w - 1, 0) if w > 0
+                        else np.zeros_like(vis)),
+    "window_ignored": ("_window_start", lambda vis, w: np.zeros_like(vis)),
+    "ring_slot_shifted": ("_ring_slot", lambda p, t_cap: (p + 1) % t_cap),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WINDOW_MUTATIONS))
+def test_planted_window_mistake_is_caught(name, monkeypatch):
+    attr, fn = WINDOW_MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    failed = 0
+    for pin in (P.pin_sliding_window, P.pin_ring_cache_equals_linear):
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure counts
+            failed += 1
+    assert failed, f"no window pin caught {name}"
