@@ -298,6 +298,56 @@ int kvc_append_decode_attention_multi_paged(const void* q, const void* k_new, co
                                             void* workspace, size_t workspace_bytes, float* out,
                                             float* lse, hipStream_t stream);
 
+/*
+ * Sliding window: kvc_decode_attention_window[_paged] and
+ * kvc_append_decode_attention_window[_paged].  As the _multi calls (n new
+ * tokens per sequence; n = 1 is single-token decode), with a window W >= 1:
+ * the token at position x attends only to positions max(0, x + 1 - W) .. x,
+ * the last W including itself ([P4] 5.2: attention within a local window to
+ * the left; [P3] 10: a window cache keeps only the most recent W positions,
+ * so its memory is bounded).  W = 0 means no window (the _multi calls).
+ * Only the positions some token sees are read: a paged table may hold -1 for
+ * blocks wholly before every window.
+ *
+ *   ring (contiguous calls only): 1 = the cache is a ring of t_cap slots,
+ *     position p in slot p mod t_cap, positions not limited by t_cap.
+ *     Requires W >= 1 and W + n - 1 <= t_cap (so that writing the n new
+ *     tokens never overwrites a position some token sees); KVC_ERR_INVALID
+ *     otherwise.  0 = positions are slots, limited by t_cap as in the other
+ *     calls.
+ *   window  0 or W >= 1; negative is KVC_ERR_INVALID.
+ * Workspace: kvc_decode_workspace_bytes(B, h * n, g, d, dtype, L, ...) with
+ * L = min(W + n - 1, capacity) for W > 0, else the capacity; any larger L
+ * gives a workspace that is also large enough.
+ */
+int kvc_decode_attention_window(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                                int t_cap, int window, int ring, float scale, int dtype,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream);
+int kvc_decode_attention_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, int max_blocks, int block_size,
+                                      int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                                      int d, int n, int window, float scale, int dtype,
+                                      int num_splits, void* workspace, size_t workspace_bytes,
+                                      float* out, float* lse, hipStream_t stream);
+int kvc_append_decode_attention_window(const void* q, const void* k_new, const void* v_new,
+                                       void* k_cache, void* v_cache,
+                                       const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                       int n, int t_cap, int window, int ring, float scale,
+                                       int dtype, int num_splits, void* workspace,
+                                       size_t workspace_bytes, float* out, float* lse,
+                                       hipStream_t stream);
+int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, const void* v_new,
+                                             void* k_pool, void* v_pool,
+                                             const int32_t* block_table, int max_blocks,
+                                             int block_size, int num_blocks,
+                                             const int32_t* seq_lens_before, int B, int h, int g,
+                                             int d, int n, int window, float scale, int dtype,
+                                             int num_splits, void* workspace,
+                                             size_t workspace_bytes, float* out, float* lse,
+                                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -82,6 +82,19 @@ def load_library():
                                                             vp, ip, ip, ip, ip, ip, fp, ip, ip,
                                                             vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention_multi_paged.restype = ip
+    lib.kvc_decode_attention_window.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, ip, ip, ip, fp,
+                                                ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_window.restype = ip
+    lib.kvc_decode_attention_window_paged.argtypes = [vp, vp, vp, vp, ip, ip, ip, vp, ip, ip, ip,
+                                                      ip, ip, ip, fp, ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_window_paged.restype = ip
+    lib.kvc_append_decode_attention_window.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip,
+                                                       ip, ip, ip, fp, ip, ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_window.restype = ip
+    lib.kvc_append_decode_attention_window_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip,
+                                                             vp, ip, ip, ip, ip, ip, ip, fp, ip,
+                                                             ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_window_paged.restype = ip
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
     lib.kvc_decode_attention.restype = ip
@@ -367,4 +380,72 @@ def append_decode_multi(q, k_new, v_new, k_cache, v_cache, seq_lens_before, bloc
             float(scale), dt, num_splits, ws.data_ptr() if ws is not None else None, wsb,
             _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_append_decode_attention_multi_paged", st)
+    return out, lse
+
+
+def _plan_len(capacity: int, window: int, n: int) -> int:
+    return min(window + n - 1, capacity) if window > 0 else capacity
+
+
+def decode_window(q, k_cache, v_cache, seq_lens, window: int, ring: bool = False,
+                  block_table=None, scale: Optional[float] = None, num_splits: int = 0,
+                  workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None,
+                  k_new=None, v_new=None):
+    """Sliding-window attention for q [B,h,n,d] (n tokens per sequence): the
+    token at position x sees positions max(0, x + 1 - window) .. x.
+
+    Without k_new: the tokens are in the cache and seq_lens counts them.  With
+    k_new, v_new [B,g,n,d]: seq_lens holds the lengths before the step and
+    the call appends them (one launch).  ring: the contiguous cache is a ring
+    of t_cap slots (position p in slot p mod t_cap).  Returns (out
+    [B,h,n,d] float32, lse [B,h,n] float32)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs_multi(q, out, lse)
+    sl = _dev(seq_lens, "seq_lens", torch.int32)
+    fused = k_new is not None
+    kn = _dev(k_new, "k_new", q.dtype) if fused else None
+    vn = _dev(v_new, "v_new", q.dtype) if fused else None
+    wsp = lambda nbytes: _workspace(nbytes, q, workspace)  # noqa: E731
+    if block_table is None:
+        _, g, t_cap, _ = k_cache.shape
+        ws, wsb = wsp(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, _plan_len(t_cap, window, n),
+                                                     num_splits, 0))
+        wsptr = ws.data_ptr() if ws is not None else None
+        kc, vc = _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype)
+        if fused:
+            st = lib.kvc_append_decode_attention_window(
+                _dev(q, "q"), kn, vn, kc, vc, sl, B, h, g, d, n, t_cap, window, int(ring),
+                float(scale), dt, num_splits, wsptr, wsb, _dev(out, "out", torch.float32),
+                _dev(lse, "lse", torch.float32), _stream(stream))
+        else:
+            st = lib.kvc_decode_attention_window(
+                _dev(q, "q"), kc, vc, sl, B, h, g, d, n, t_cap, window, int(ring), float(scale), dt,
+                num_splits, wsptr, wsb, _dev(out, "out", torch.float32),
+                _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_*decode_attention_window", st)
+    else:
+        if ring:
+            raise ValueError("a ring cache is contiguous")
+        nb, g, bs, _ = k_cache.shape
+        mb = block_table.shape[1]
+        ws, wsb = wsp(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt,
+                                                     _plan_len(mb * bs, window, n), num_splits, 1))
+        wsptr = ws.data_ptr() if ws is not None else None
+        kp, vp = _dev(k_cache, "k_pool", q.dtype), _dev(v_cache, "v_pool", q.dtype)
+        bt = _dev(block_table, "block_table", torch.int32)
+        if fused:
+            st = lib.kvc_append_decode_attention_window_paged(
+                _dev(q, "q"), kn, vn, kp, vp, bt, mb, bs, nb, sl, B, h, g, d, n, window,
+                float(scale), dt, num_splits, wsptr, wsb, _dev(out, "out", torch.float32),
+                _dev(lse, "lse", torch.float32), _stream(stream))
+        else:
+            st = lib.kvc_decode_attention_window_paged(
+                _dev(q, "q"), kp, vp, bt, mb, bs, nb, sl, B, h, g, d, n, window, float(scale), dt,
+                num_splits, wsptr, wsb, _dev(out, "out", torch.float32),
+                _dev(lse, "lse", torch.float32), _stream(stream))
+        _check("kvc_*decode_attention_window_paged", st)
     return out, lse

@@ -20,7 +20,7 @@ __global__ void __launch_bounds__(256) append_kernel(
     const V* __restrict__ k_new, const V* __restrict__ v_new, V* __restrict__ k_cache,
     V* __restrict__ v_cache, const int32_t* __restrict__ block_table, int max_blocks,
     int block_size, const int32_t* __restrict__ seq_lens, int B, int g, int n, int vec_per_row,
-    int capacity) {
+    int capacity, int ring) {
     const long total = (long)B * g * n * vec_per_row;
     long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const bool is_v = t >= total;
@@ -37,8 +37,12 @@ __global__ void __launch_bounds__(256) append_kernel(
     const int pos = (int)pos_l;
     long row;
     if (block_table == nullptr) {
-        if (pos >= capacity) return;
-        row = bj * (long)capacity + pos;
+        if (ring) {
+            row = bj * (long)capacity + pos % capacity;  // ring cache: slot pos mod capacity
+        } else {
+            if (pos >= capacity) return;
+            row = bj * (long)capacity + pos;
+        }
     } else {
         const int logical = pos / block_size;
         if (logical >= max_blocks) return;
@@ -55,30 +59,30 @@ template <typename V>
 static void launch_append_t(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* block_table, int max_blocks, int block_size,
                             const int32_t* seq_lens_before, int B, int g, int n, int vpr,
-                            int capacity, hipStream_t s) {
+                            int capacity, int ring, hipStream_t s) {
     const int threads = 256;
     const long total = 2L * B * g * n * vpr;
     append_kernel<V><<<dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, s>>>(
         (const V*)k_new, (const V*)v_new, (V*)k_cache, (V*)v_cache, block_table, max_blocks,
-        block_size, seq_lens_before, B, g, n, vpr, capacity);
+        block_size, seq_lens_before, B, g, n, vpr, capacity, ring);
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,
-                         int elem_bytes, hipStream_t s) {
+                         int ring, int elem_bytes, hipStream_t s) {
     const long row_bytes = (long)d * elem_bytes;
     if (row_bytes % 16 == 0)
         launch_append_t<uint4>(k_new, v_new, k_cache, v_cache, block_table, max_blocks, block_size,
-                               seq_lens_before, B, g, n, (int)(row_bytes / 16), capacity, s);
+                               seq_lens_before, B, g, n, (int)(row_bytes / 16), capacity, ring, s);
     else if (row_bytes % 4 == 0)
         launch_append_t<uint32_t>(k_new, v_new, k_cache, v_cache, block_table, max_blocks,
                                   block_size, seq_lens_before, B, g, n, (int)(row_bytes / 4),
-                                  capacity, s);
+                                  capacity, ring, s);
     else
         launch_append_t<uint16_t>(k_new, v_new, k_cache, v_cache, block_table, max_blocks,
                                   block_size, seq_lens_before, B, g, n, (int)(row_bytes / 2),
-                                  capacity, s);
+                                  capacity, ring, s);
     return hipGetLastError();
 }
 

@@ -38,12 +38,14 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const int d = a.d;
     const int j = (int)(((long)i * a.g) / a.h);
     const int raw = a.seq_lens[b];
-    const int L = attended_len(a, raw);
-    const int p0 = c * a.chunk_len;
+    const PosRange ur = unit_range(a, raw);  // chunks cover [lo, hi)
+    const int c0 = ur.lo + c * a.chunk_len;
     const bool single = a.num_chunks == 1;
-    if (p0 >= L && !single) return;  // chunk past the end: the merge skips it
-    // row i is token i % n, which sees visible_len positions
-    const int p1 = min(min(p0 + a.chunk_len, L), visible_len(a, raw, i % a.n));
+    if (c0 >= ur.hi && !single) return;  // chunk past the end: the merge skips it
+    // row i is token i % n, which sees [window_lo(vis), vis)
+    const int vis = visible_len(a, raw, i % a.n);
+    const int p0 = max(c0, window_lo(a, vis));
+    const int p1 = min(min(c0 + a.chunk_len, ur.hi), vis);
 
     const T* q = (const T*)a.q;
     const T* K = (const T*)a.k;
@@ -64,7 +66,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
             phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
             row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
         } else {
-            row = contig_base + p;
+            row = contig_base + cache_slot(a, p);
         }
         float part = 0.0f;
 #pragma unroll

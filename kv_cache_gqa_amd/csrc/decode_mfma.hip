@@ -91,7 +91,10 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 #define KVC_MFMA_PREFETCH 1
 #endif
 
-template <int NQT, bool PAGED, int W>
+// GEN: several query tokens per sequence, sliding windows or ring caches
+// (per-row visibility masks, ring-aware windows).  Without it a row sees
+// every position of its segment, which keeps the common path's registers.
+template <int NQT, bool PAGED, int W, bool GEN>
 struct MfmaEngine {
     using L = Lds<NQT, W>;
     struct Shared {
@@ -141,6 +144,7 @@ struct MfmaEngine {
 
         unsigned char* vst = sh.lds + wave * kVStageBytes;
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
+        long cbase = bj_base;  // row of position 0 in the current window (ring: shifted)
         const float sl2 = a.scale_log2e;
         const int* tbl = sh.tbl;
         int blk0 = 0;
@@ -151,15 +155,18 @@ struct MfmaEngine {
                 const int phys = tbl[(p >> a.log2_bs) - blk0];
                 return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
             }
-            return bj_base + p;
+            return cbase + p;
         };
 
-        // Query column 16*qt + col is token (16*qt + col) % n, which sees
-        // positions below lim[qt].
+        // Query column 16*qt + col is token (row0 + 16*qt + col) % n, which
+        // sees positions [lim[qt] - wlen, lim[qt]): p is visible when
+        // lim - 1 - p, as unsigned, is below wlen (the window, or 2^31).
         const int raw = a.seq_lens[b];
+        const unsigned wlen = GEN && a.window > 0 ? (unsigned)a.window : 0x80000000u;
         int lim[NQT];
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) lim[qt] = visible_len(a, raw, (row0 + 16 * qt + col) % a.n);
+        for (int qt = 0; qt < NQT; ++qt)
+            lim[qt] = GEN ? visible_len(a, raw, (row0 + 16 * qt + col) % a.n) : 0;
 
         // A call that appends reads its new tokens (positions raw .. raw+n-1,
         // the last ones of the unit) from k_new / v_new and writes them into
@@ -233,7 +240,8 @@ struct MfmaEngine {
                     for (int v = 0; v < 4; ++v) {
                         const int p = t0 + 16 * tt + 4 * G + v;
                         const float x = S[qt][tt][v] * sl2;
-                        sv[4 * tt + v] = (p < w1 && p < lim[qt]) ? x : kNegInf;
+                        const bool vis = GEN ? (p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen) : p < w1;
+                        sv[4 * tt + v] = vis ? x : kNegInf;
                     }
                 }
                 float mt = sv[0];
@@ -288,6 +296,12 @@ struct MfmaEngine {
         // the block table fits in shared memory.
         for (int w0 = s; w0 < e_cache; w0 = w1) {
             w1 = min(e_cache, w0 + kMaxChunk);
+            if (GEN && !PAGED && a.ring) {
+                // a window never wraps around the ring: slot = p - wbase in it
+                const int wbase = w0 - w0 % a.t_cap;
+                w1 = min(w1, wbase + a.t_cap);
+                cbase = bj_base - wbase;
+            }
             if (PAGED) {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
@@ -416,51 +430,62 @@ struct MfmaEngine {
 template <int NQT>
 struct MfmaOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 2 : 1; };
 
-template <int NQT, bool PAGED, int W>
+template <int NQT, bool PAGED, int W, bool GEN>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
-    using E = MfmaEngine<NQT, PAGED, W>;
+    using E = MfmaEngine<NQT, PAGED, W, GEN>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, b = blockIdx.z;
     const int j = blockIdx.y / a.slices, row0 = (blockIdx.y - j * a.slices) * 16 * NQT;
-    const int L = attended_len(a, a.seq_lens[b]);
-    const int p0 = c * a.chunk_len;
-    const int p1 = min(p0 + a.chunk_len, L);
+    // chunks cover [lo, hi); without the general features lo = 0
+    const PosRange ur = GEN ? unit_range(a, a.seq_lens[b])
+                            : PosRange{0, attended_len(a, a.seq_lens[b])};
+    const int p0 = ur.lo + c * a.chunk_len;
+    const int p1 = min(p0 + a.chunk_len, ur.hi);
     const bool single = a.num_chunks == 1;
-    if (p0 >= L && !single) return;  // past the end: the merge skips this chunk
+    if (p0 >= ur.hi && !single) return;  // past the end: the merge skips this chunk
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c, row0), row0);
 }
 
-template <int NQT, bool PAGED, int W>
+template <int NQT, bool PAGED, int W, bool GEN>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_stream(DecodeArgs a) {
-    using E = MfmaEngine<NQT, PAGED, W>;
+    using E = MfmaEngine<NQT, PAGED, W, GEN>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
     stream_prefix(a, cum);
     stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
-        E::segment(a, sh, b, j, s, e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
+        const int lo = GEN ? unit_range(a, a.seq_lens[b]).lo : 0;  // walk offsets are relative to it
+        E::segment(a, sh, b, j, lo + s, lo + e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
     });
 }
 
-// Kernel function for (m, layout, split mode, wavefronts per work-group);
-// nullptr when that combination is not built.  Every (m, layout, mode) has a
-// 4-wavefront kernel; one tile of query heads (m <= 16) on a contiguous cache
-// also has an 8-wavefront chunked kernel, for whole-unit work-groups.  (Two
-// tiles need more registers than 8 wavefronts per work-group leave.)
-const void* mfma_kernel(int m, bool paged, bool stream, int waves) {
+template <int NQT, bool PG, int WV>
+static const void* mfma_pick(bool stream, bool gen) {
+    if (stream)
+        return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true>
+                   : (const void*)decode_mfma_stream<NQT, PG, WV, false>;
+    return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true>
+               : (const void*)decode_mfma_chunked<NQT, PG, WV, false>;
+}
+
+// Kernel function for (m, layout, split mode, wavefronts per work-group,
+// general features); nullptr when that combination is not built.  Every
+// (m, layout, mode) has a 4-wavefront kernel; one tile of query rows
+// (m <= 16) on a contiguous cache also has an 8-wavefront chunked kernel,
+// for whole-unit work-groups.  (Two tiles need more registers than 8
+// wavefronts per work-group leave.)
+const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen) {
     const bool two = m > 16;
     if (waves == 4) {
-        if (stream) {
-            if (two) return paged ? (const void*)decode_mfma_stream<2, true, 4> : (const void*)decode_mfma_stream<2, false, 4>;
-            return paged ? (const void*)decode_mfma_stream<1, true, 4> : (const void*)decode_mfma_stream<1, false, 4>;
-        }
-        if (two) return paged ? (const void*)decode_mfma_chunked<2, true, 4> : (const void*)decode_mfma_chunked<2, false, 4>;
-        return paged ? (const void*)decode_mfma_chunked<1, true, 4> : (const void*)decode_mfma_chunked<1, false, 4>;
+        if (two) return paged ? mfma_pick<2, true, 4>(stream, gen) : mfma_pick<2, false, 4>(stream, gen);
+        return paged ? mfma_pick<1, true, 4>(stream, gen) : mfma_pick<1, false, 4>(stream, gen);
     }
-    if (waves == 8 && !two && !paged && !stream) return (const void*)decode_mfma_chunked<1, false, 8>;
+    if (waves == 8 && !two && !paged && !stream)
+        return gen ? (const void*)decode_mfma_chunked<1, false, 8, true>
+                   : (const void*)decode_mfma_chunked<1, false, 8, false>;
     return nullptr;
 }
 
@@ -468,7 +493,8 @@ hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
     // more than 32 rows: slices of 32 (chunked mode only)
     if (a.slices < 1 || (a.m > 32 * a.slices) || (a.slices > 1 && (a.stream || a.m <= 32)))
         return hipErrorInvalidValue;
-    const void* fn = mfma_kernel(min(a.m, 32), a.block_table != nullptr, a.stream != 0, a.waves);
+    const void* fn = mfma_kernel(min(a.m, 32), a.block_table != nullptr, a.stream != 0, a.waves,
+                                 general_features(a));
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
                                : dim3((unsigned)a.num_chunks, (unsigned)(a.g * a.slices),

@@ -32,7 +32,9 @@ constexpr int kD = 128;
 #define KVC_VALU_PREFETCH 1
 #endif
 
-template <int M, bool PAGED, int W>
+// GEN: several query tokens per sequence, sliding windows or ring caches
+// (per-row visibility masks, ring-aware windows).
+template <int M, bool PAGED, int W, bool GEN>
 struct ValuEngine {
     struct Shared {
         int tbl[PAGED ? kMaxTableSlice : 1];
@@ -68,6 +70,7 @@ struct ValuEngine {
             for (int k = 0; k < 8; ++k) acc[r][k] = 0.0f;
         }
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
+        long cbase = bj_base;  // row of position 0 in the current window (ring: shifted)
         const float sl2 = a.scale_log2e;
         const int* tbl = sh.tbl;
         int blk0 = 0;
@@ -78,13 +81,16 @@ struct ValuEngine {
                 const int phys = tbl[(p >> a.log2_bs) - blk0];
                 return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
             }
-            return bj_base + p;
+            return cbase + p;
         };
-        // Row r is token r % n, which sees positions below lim[r].
+        // Row r is token r % n, which sees positions [lim[r] - wlen, lim[r]):
+        // p is visible when lim - 1 - p, as unsigned, is below wlen (the
+        // window, or 2^31).
         const int raw = a.seq_lens[b];
+        const unsigned wlen = GEN && a.window > 0 ? (unsigned)a.window : 0x80000000u;
         int lim[M];
 #pragma unroll
-        for (int r = 0; r < M; ++r) lim[r] = visible_len(a, raw, r % a.n);
+        for (int r = 0; r < M; ++r) lim[r] = GEN ? visible_len(a, raw, r % a.n) : 0;
 
         // A call that appends reads its new tokens (positions raw .. raw+n-1,
         // the last ones of the unit) from k_new / v_new and writes them into
@@ -128,7 +134,8 @@ struct ValuEngine {
                     dot = dot2_bf16(qp[r][2], kv[u].z, dot);
                     dot = dot2_bf16(qp[r][3], kv[u].w, dot);
                     dot = row16_sum(dot) * sl2;
-                    sc[r][u] = (p < w1 && p < lim[r]) ? dot : kNegInf;
+                    const bool vis = GEN ? (p < w1 && (unsigned)(lim[r] - 1 - p) < wlen) : p < w1;
+                    sc[r][u] = vis ? dot : kNegInf;
                 }
             }
             float pr[M][8];
@@ -167,6 +174,12 @@ struct ValuEngine {
         // Windows of at most kMaxChunk positions (block-table slice in LDS).
         for (int w0 = s; w0 < e_cache; w0 = w1) {
             w1 = min(e_cache, w0 + kMaxChunk);
+            if (GEN && !PAGED && a.ring) {
+                // a window never wraps around the ring: slot = p - wbase in it
+                const int wbase = w0 - w0 % a.t_cap;
+                w1 = min(w1, wbase + a.t_cap);
+                cbase = bj_base - wbase;
+            }
             if (PAGED) {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
@@ -268,52 +281,60 @@ struct ValuEngine {
 
 }  // namespace
 
-template <int M, bool PAGED, int W>
+template <int M, bool PAGED, int W, bool GEN>
 __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
-    using E = ValuEngine<M, PAGED, W>;
+    using E = ValuEngine<M, PAGED, W, GEN>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int L = attended_len(a, a.seq_lens[b]);
-    const int p0 = c * a.chunk_len;
-    const int p1 = min(p0 + a.chunk_len, L);
+    // chunks cover [lo, hi); without the general features lo = 0
+    const PosRange ur = GEN ? unit_range(a, a.seq_lens[b])
+                            : PosRange{0, attended_len(a, a.seq_lens[b])};
+    const int p0 = ur.lo + c * a.chunk_len;
+    const int p1 = min(p0 + a.chunk_len, ur.hi);
     const bool single = a.num_chunks == 1;
-    if (p0 >= L && !single) return;  // past the end: the merge skips this chunk
+    if (p0 >= ur.hi && !single) return;  // past the end: the merge skips this chunk
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
 }
 
-template <int M, bool PAGED, int W>
+template <int M, bool PAGED, int W, bool GEN>
 __global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
-    using E = ValuEngine<M, PAGED, W>;
+    using E = ValuEngine<M, PAGED, W, GEN>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
     stream_prefix(a, cum);
     stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
-        E::segment(a, sh, b, j, s, e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
+        const int lo = GEN ? unit_range(a, a.seq_lens[b]).lo : 0;  // walk offsets are relative to it
+        E::segment(a, sh, b, j, lo + s, lo + e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
     });
 }
 
-template <int M>
-static const void* valu_pick_m(bool paged, bool stream, int waves) {
-    if (waves != 4) return nullptr;
-    if (stream) return paged ? (const void*)decode_valu_stream<M, true, 4> : (const void*)decode_valu_stream<M, false, 4>;
-    return paged ? (const void*)decode_valu_chunked<M, true, 4> : (const void*)decode_valu_chunked<M, false, 4>;
+template <int M, bool PG>
+static const void* valu_pick(bool stream, bool gen) {
+    if (stream)
+        return gen ? (const void*)decode_valu_stream<M, PG, 4, true>
+                   : (const void*)decode_valu_stream<M, PG, 4, false>;
+    return gen ? (const void*)decode_valu_chunked<M, PG, 4, true>
+               : (const void*)decode_valu_chunked<M, PG, 4, false>;
 }
 
-// Kernel function for (m, layout, split mode, wavefronts per work-group);
-// nullptr when that combination is not built.  Only 4-wavefront kernels: one
-// wide work-group per (sequence, KV head) measured slower than split chunks
-// plus a merge for these kernels (8 and 16 wavefronts, m = 1).
-const void* valu_kernel(int m, bool paged, bool stream, int waves) {
+// Kernel function for (m, layout, split mode, wavefronts per work-group,
+// general features); nullptr when that combination is not built.  Only
+// 4-wavefront kernels: one wide work-group per (sequence, KV head) measured
+// slower than split chunks plus a merge for these kernels (8 and 16
+// wavefronts, m = 1).
+const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen) {
+    if (waves != 4) return nullptr;
     switch (m) {
-        case 1: return valu_pick_m<1>(paged, stream, waves);
-        case 2: return valu_pick_m<2>(paged, stream, waves);
-        case 3: return valu_pick_m<3>(paged, stream, waves);
+        case 1: return paged ? valu_pick<1, true>(stream, gen) : valu_pick<1, false>(stream, gen);
+        case 2: return paged ? valu_pick<2, true>(stream, gen) : valu_pick<2, false>(stream, gen);
+        case 3: return paged ? valu_pick<3, true>(stream, gen) : valu_pick<3, false>(stream, gen);
         default: return nullptr;
     }
 }
 
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s) {
-    const void* fn = valu_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves);
+    const void* fn = valu_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves,
+                                 general_features(a));
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
                                : dim3((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);

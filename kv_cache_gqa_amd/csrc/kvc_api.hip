@@ -161,8 +161,9 @@ static long device_slots(const void* fn, int waves) {
     return (long)cus * per_cu;
 }
 
-static const void* kernel_for(KernelKind kind, int m, bool paged, bool stream, int waves) {
-    return kind == kMfma ? mfma_kernel(m, paged, stream, waves) : valu_kernel(m, paged, stream, waves);
+static const void* kernel_for(KernelKind kind, int m, bool paged, bool stream, int waves, bool gen) {
+    return kind == kMfma ? mfma_kernel(m, paged, stream, waves, gen)
+                         : valu_kernel(m, paged, stream, waves, gen);
 }
 
 // Fraction of the slot-rounds a grid of `wgs` equal work-groups keeps busy.
@@ -183,14 +184,14 @@ struct AutoShape {
     long chunks;
 };
 
-static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len) {
+static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, bool gen) {
     const long units = (long)B * g;
-    const void* f4 = kernel_for(kind, m, false, false, 4);
+    const void* f4 = kernel_for(kind, m, false, false, 4, gen);
     const long slots4 = device_slots(f4, 4);
     AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};
 #if KVC_AUTO_WIDE
     const int wv = 8;
-    const void* fn = kernel_for(kind, m, false, false, wv);
+    const void* fn = kernel_for(kind, m, false, false, wv, gen);
     const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
     if (slots > 0 && units >= slots && slots * wv >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
         return AutoShape{wv, 1};
@@ -225,13 +226,14 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     a.waves = sc.kind == kGeneric ? 1 : 4;
     a.slices = row_slices(sc.kind, a.m);
     if (sc.stream) {
-        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4), 4);
+        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4, general_features(a)), 4);
         // No more work-groups than 256-position pieces of the largest possible batch.
-        const long pieces = ((long)a.B * a.g * a.cap_len + 255) / 256;
+        const long pieces = ((long)a.B * a.g * max_len + 255) / 256;
         if (P > pieces) P = pieces;
         a.num_wgs = (int)(P < 1 ? 1 : P);
     } else if (sc.auto_chunks) {
-        const AutoShape sh = auto_shape(sc.kind, a.m < 32 ? a.m : 32, a.B * a.slices, a.g, max_len);
+        const AutoShape sh = auto_shape(sc.kind, a.m < 32 ? a.m : 32, a.B * a.slices, a.g, max_len,
+                                        general_features(a));
         a.waves = sh.waves;
         // One chunk per unit may exceed kMaxChunk: the engines walk a chunk in
         // windows of at most kMaxChunk positions.
@@ -256,7 +258,7 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
         const int eb = dtype == KVC_F32 ? 4 : 2;
         if (launch_append(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
                           a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g, a.n,
-                          a.d, paged ? a.num_blocks : a.t_cap, eb, stream) != hipSuccess)
+                          a.d, paged ? a.num_blocks : a.t_cap, a.ring, eb, stream) != hipSuccess)
             return KVC_ERR_HIP;
         a.k_new = nullptr;
         a.v_new = nullptr;
@@ -327,7 +329,7 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     if (d > 256) return KVC_ERR_UNSUPPORTED;
     Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
     DecodeArgs a{};
-    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.cap_len = max_seq_len;
+    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.n = 1; a.cap_len = max_seq_len;
     resolve_launch(a, sc, paged != 0, max_seq_len);
     if (waves) *waves = a.waves;
     // the generic kernel: one wavefront per query row; the others: per unit
@@ -359,9 +361,18 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
     if (block_table != nullptr && (max_blocks <= 0 || block_size <= 0)) return KVC_ERR_INVALID;
     const int eb = dtype == KVC_F32 ? 4 : 2;
     if (launch_append(k_new, v_new, k_cache, v_cache, block_table, max_blocks, block_size,
-                      seq_lens_before, B, g, 1, d, capacity, eb, stream) != hipSuccess)
+                      seq_lens_before, B, g, 1, d, capacity, 0, eb, stream) != hipSuccess)
         return KVC_ERR_HIP;
     return KVC_OK;
+}
+
+// Longest position range a unit can read: the capacity, or with a sliding
+// window the window plus the other new tokens.  Chunk plans and workspaces
+// are sized for it.
+static int plan_len(int capacity, int window, int n) {
+    if (window <= 0) return capacity;
+    const long w = (long)window + n - 1;
+    return w < capacity ? (int)w : capacity;
 }
 
 // Shared body of the contiguous entry points.  n queries per sequence
@@ -369,36 +380,40 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
 // (k_new [B, g, n, d]) and seq_lens holds the lengths before the step.
 static int decode_contiguous(const void* q, const void* k_new, const void* v_new,
                              const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                             int B, int h, int g, int d, int n, int t_cap, float scale, int dtype,
-                             int num_splits, void* workspace, size_t workspace_bytes, float* out,
-                             float* lse, hipStream_t stream) {
+                             int B, int h, int g, int d, int n, int t_cap, int window, int ring,
+                             float scale, int dtype, int num_splits, void* workspace,
+                             size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
     int st = check_common(q, k_cache, v_cache, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
-    if (t_cap <= 0 || n <= 0) return KVC_ERR_INVALID;
+    if (t_cap <= 0 || n <= 0 || window < 0) return KVC_ERR_INVALID;
+    // a ring keeps every position a token can see: window + n - 1 <= t_cap
+    if (ring && (window <= 0 || (long)window + n - 1 > t_cap)) return KVC_ERR_INVALID;
     if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
     DecodeArgs a{};
     a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens;
     a.block_table = nullptr; a.max_blocks = 0; a.block_size = 1; a.log2_bs = 0; a.num_blocks = 0;
     a.B = B; a.h = h * n; a.g = g; a.d = d; a.m = (h / g) * n; a.n = n;
-    a.t_cap = t_cap; a.cap_len = t_cap;
+    a.t_cap = t_cap; a.cap_len = ring ? 0x7fffffff : t_cap;
+    a.window = window; a.ring = ring ? 1 : 0;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
     a.len_add = k_new != nullptr ? n : 0;
     a.k_new = k_new; a.v_new = v_new;
-    return run_decode(a, dtype, t_cap, num_splits, workspace, workspace_bytes, stream);
+    return run_decode(a, dtype, plan_len(t_cap, window, n), num_splits, workspace, workspace_bytes,
+                      stream);
 }
 
 static int decode_paged(const void* q, const void* k_new, const void* v_new, const void* k_pool,
                         const void* v_pool, const int32_t* block_table, int max_blocks,
                         int block_size, int num_blocks, const int32_t* seq_lens, int B, int h,
-                        int g, int d, int n, float scale, int dtype, int num_splits,
+                        int g, int d, int n, int window, float scale, int dtype, int num_splits,
                         void* workspace, size_t workspace_bytes, float* out, float* lse,
                         hipStream_t stream) {
     int st = check_common(q, k_pool, v_pool, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
-    if (max_blocks <= 0 || num_blocks <= 0 || n <= 0) return KVC_ERR_INVALID;
+    if (max_blocks <= 0 || num_blocks <= 0 || n <= 0 || window < 0) return KVC_ERR_INVALID;
     if (B > 0 && block_table == nullptr) return KVC_ERR_INVALID;
     const int lg = ilog2_exact(block_size);
     if (block_size < 8 || block_size > 256 || lg < 0) return KVC_ERR_INVALID;
@@ -411,11 +426,13 @@ static int decode_paged(const void* q, const void* k_new, const void* v_new, con
     a.log2_bs = lg; a.num_blocks = num_blocks;
     a.B = B; a.h = h * n; a.g = g; a.d = d; a.m = (h / g) * n; a.n = n;
     a.t_cap = 0; a.cap_len = (int)cap;
+    a.window = window; a.ring = 0;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
     a.len_add = k_new != nullptr ? n : 0;
     a.k_new = k_new; a.v_new = v_new;
-    return run_decode(a, dtype, (int)cap, num_splits, workspace, workspace_bytes, stream);
+    return run_decode(a, dtype, plan_len((int)cap, window, n), num_splits, workspace,
+                      workspace_bytes, stream);
 }
 
 int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -423,7 +440,8 @@ int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          float scale, int dtype, int num_splits, void* workspace,
                          size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
     return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, 1, t_cap,
-                             scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+                             0, 0, scale, dtype, num_splits, workspace, workspace_bytes, out, lse,
+                             stream);
 }
 
 int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
@@ -433,7 +451,7 @@ int kvc_decode_attention_paged(const void* q, const void* k_pool, const void* v_
                                size_t workspace_bytes, float* out, float* lse,
                                hipStream_t stream) {
     return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
-                        num_blocks, seq_lens, B, h, g, d, 1, scale, dtype, num_splits, workspace,
+                        num_blocks, seq_lens, B, h, g, d, 1, 0, scale, dtype, num_splits, workspace,
                         workspace_bytes, out, lse, stream);
 }
 
@@ -444,7 +462,7 @@ int kvc_append_decode_attention(const void* q, const void* k_new, const void* v_
                                 float* out, float* lse, hipStream_t stream) {
     if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
     return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
-                             seq_lens_before, B, h, g, d, 1, t_cap, scale, dtype, num_splits,
+                             seq_lens_before, B, h, g, d, 1, t_cap, 0, 0, scale, dtype, num_splits,
                              workspace, workspace_bytes, out, lse, stream);
 }
 
@@ -457,8 +475,8 @@ int kvc_append_decode_attention_paged(const void* q, const void* k_new, const vo
                                       hipStream_t stream) {
     if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
     return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
-                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, 1, scale,
-                        dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, 1, 0,
+                        scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
@@ -466,7 +484,8 @@ int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v
                                int t_cap, float scale, int dtype, int num_splits, void* workspace,
                                size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
     return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, n, t_cap,
-                             scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+                             0, 0, scale, dtype, num_splits, workspace, workspace_bytes, out, lse,
+                             stream);
 }
 
 int kvc_decode_attention_multi_paged(const void* q, const void* k_pool, const void* v_pool,
@@ -476,7 +495,7 @@ int kvc_decode_attention_multi_paged(const void* q, const void* k_pool, const vo
                                      void* workspace, size_t workspace_bytes, float* out,
                                      float* lse, hipStream_t stream) {
     return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
-                        num_blocks, seq_lens, B, h, g, d, n, scale, dtype, num_splits, workspace,
+                        num_blocks, seq_lens, B, h, g, d, n, 0, scale, dtype, num_splits, workspace,
                         workspace_bytes, out, lse, stream);
 }
 
@@ -488,7 +507,7 @@ int kvc_append_decode_attention_multi(const void* q, const void* k_new, const vo
                                       float* lse, hipStream_t stream) {
     if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
     return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
-                             seq_lens_before, B, h, g, d, n, t_cap, scale, dtype, num_splits,
+                             seq_lens_before, B, h, g, d, n, t_cap, 0, 0, scale, dtype, num_splits,
                              workspace, workspace_bytes, out, lse, stream);
 }
 
@@ -502,8 +521,57 @@ int kvc_append_decode_attention_multi_paged(const void* q, const void* k_new, co
                                             float* lse, hipStream_t stream) {
     if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
     return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
-                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, n, scale,
-                        dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, n, 0,
+                        scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_decode_attention_window(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                                int t_cap, int window, int ring, float scale, int dtype,
+                                int num_splits, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream) {
+    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, n, t_cap,
+                             window, ring, scale, dtype, num_splits, workspace, workspace_bytes, out,
+                             lse, stream);
+}
+
+int kvc_decode_attention_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, int max_blocks, int block_size,
+                                      int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                                      int d, int n, int window, float scale, int dtype,
+                                      int num_splits, void* workspace, size_t workspace_bytes,
+                                      float* out, float* lse, hipStream_t stream) {
+    return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
+                        num_blocks, seq_lens, B, h, g, d, n, window, scale, dtype, num_splits,
+                        workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_window(const void* q, const void* k_new, const void* v_new,
+                                       void* k_cache, void* v_cache,
+                                       const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                       int n, int t_cap, int window, int ring, float scale,
+                                       int dtype, int num_splits, void* workspace,
+                                       size_t workspace_bytes, float* out, float* lse,
+                                       hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
+                             seq_lens_before, B, h, g, d, n, t_cap, window, ring, scale, dtype,
+                             num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, const void* v_new,
+                                             void* k_pool, void* v_pool,
+                                             const int32_t* block_table, int max_blocks,
+                                             int block_size, int num_blocks,
+                                             const int32_t* seq_lens_before, int B, int h, int g,
+                                             int d, int n, int window, float scale, int dtype,
+                                             int num_splits, void* workspace,
+                                             size_t workspace_bytes, float* out, float* lse,
+                                             hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, n, window,
+                        scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

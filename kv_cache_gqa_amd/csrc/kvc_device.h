@@ -132,6 +132,27 @@ __device__ __forceinline__ int visible_len(const DecodeArgs& a, int raw, int t) 
     return L < 0 ? 0 : (L > a.cap_len ? a.cap_len : (int)L);
 }
 
+// First position a token sees when it sees `visible` positions.
+__device__ __forceinline__ int window_lo(const DecodeArgs& a, int visible) {
+    return a.window > 0 ? max(visible - a.window, 0) : 0;
+}
+
+// Positions [lo, hi) that some query row of a sequence reads: hi is the
+// attended length (what the last token sees), lo what the first token's
+// window starts at.
+struct PosRange {
+    int lo, hi;
+};
+__device__ __forceinline__ PosRange unit_range(const DecodeArgs& a, int raw) {
+    return PosRange{window_lo(a, visible_len(a, raw, 0)), attended_len(a, raw)};
+}
+
+// Cache slot of position p in a contiguous cache: p, or p mod t_cap for a
+// ring cache.
+__device__ __forceinline__ int cache_slot(const DecodeArgs& a, int p) {
+    return a.ring ? p % a.t_cap : p;
+}
+
 // bf16, d = 128: write the appended tokens at positions [lo, hi) of unit
 // (b, j) into their cache slots.  Position p holds new token p - raw of
 // k_new / v_new [B, g, n, d].  Each of the `nthreads` threads moves 16-byte
@@ -150,7 +171,7 @@ __device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, in
             if (phys < 0 || phys >= a.num_blocks) continue;
             row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
         } else {
-            row = unit * a.t_cap + p;
+            row = unit * a.t_cap + cache_slot(a, p);
         }
         const bool is_v = part >= 16;
         const int c = part & 15;

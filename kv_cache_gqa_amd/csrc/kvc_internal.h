@@ -72,6 +72,11 @@ struct DecodeArgs {
     // are served by ceil(m / 32) work-groups of 32 rows each, blockIdx.y =
     // j * slices + slice.
     int slices;
+    // Sliding window: 0 = none; W > 0: a token at position x sees positions
+    // max(0, x + 1 - W) .. x.  ring (contiguous only): position p lives in
+    // slot p mod t_cap (positions are not clamped to the capacity).
+    int window;
+    int ring;
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
     // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
     float* part_o;
@@ -86,15 +91,18 @@ hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
-// Kernel function for (m, layout, split mode, wavefronts per work-group), for
-// launches and occupancy queries; nullptr when that combination is not
-// built.  MFMA: waves in {4, 8}; VALU: 4.
-const void* mfma_kernel(int m, bool paged, bool stream, int waves);
-const void* valu_kernel(int m, bool paged, bool stream, int waves);
+// Kernel function for (m, layout, split mode, wavefronts per work-group,
+// general features), for launches and occupancy queries; nullptr when that
+// combination is not built.  MFMA: waves in {4, 8}; VALU: 4.
+const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen);
+const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen);
+// Whether a call needs the kernels' general features: several query tokens
+// per sequence, a sliding window or a ring cache.
+inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,
-                         int elem_bytes, hipStream_t s);
+                         int ring, int elem_bytes, hipStream_t s);
 
 // Which decode kernel a configuration uses (exposed for tests and tools).
 enum KernelKind { kGeneric = 0, kValu = 1, kMfma = 2 };

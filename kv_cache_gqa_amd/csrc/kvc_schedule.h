@@ -34,7 +34,9 @@ __device__ __forceinline__ long long stream_owner(long long x, long long total, 
     return p < P - 1 ? p : P - 1;
 }
 
-// Prefix sums of the clamped lengths into cum[0..B] (cum[0] = 0), B <=
+// Prefix sums of the position-range lengths (hi - lo of unit_range: the
+// attended length, less what a sliding window skips) into cum[0..B]
+// (cum[0] = 0), B <=
 // kStreamMaxB.  Wavefront 0 does it: lane l owns sequences [16 l, 16 l + 16),
 // issues all its loads at once, and a shuffle scan across the 64 lanes gives
 // each lane its starting offset.  Called by the whole work-group; ends with
@@ -52,7 +54,12 @@ __device__ inline void stream_prefix(const DecodeArgs& a, long long* cum) {
         for (int k = 0; k < kScanPerLane; ++k) len[k] = a.seq_lens[min(b0 + k, a.B - 1)];
 #pragma unroll
         for (int k = 0; k < kScanPerLane; ++k)
-            len[k] = b0 + k < a.B ? attended_len(a, len[k]) : 0;
+            if (b0 + k < a.B) {
+                const PosRange r = unit_range(a, len[k]);
+                len[k] = r.hi - r.lo;
+            } else {
+                len[k] = 0;
+            }
         long long sum = 0;
 #pragma unroll
         for (int k = 0; k < kScanPerLane; ++k) sum += len[k];

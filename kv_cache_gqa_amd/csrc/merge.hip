@@ -95,8 +95,8 @@ __device__ __forceinline__ void merge_row_chunked(const DecodeArgs& a, long row)
     const int t = threadIdx.x;
     const int cg = t / nE, e = t - (t / nE) * nE;
     const int b = (int)(row / a.h);
-    const int L = attended_len(a, a.seq_lens[b]);
-    const int nc = (L + a.chunk_len - 1) / a.chunk_len;  // chunks that hold positions
+    const PosRange ur = unit_range(a, a.seq_lens[b]);
+    const int nc = (ur.hi - ur.lo + a.chunk_len - 1) / a.chunk_len;  // chunks that hold positions
     if (cg < G) {
         float M = kNegInf, W = 0.0f, o[V];
 #pragma unroll
@@ -186,7 +186,8 @@ __global__ void __launch_bounds__(256) merge_stream_kernel(DecodeArgs a) {
     const int b = (int)(row / a.h);
     const int i = (int)(row % a.h);
     const int j = i / m, r = i % m;
-    const long long L = attended_len(a, a.seq_lens[b]);
+    const PosRange ur = unit_range(a, a.seq_lens[b]);
+    const long long L = ur.hi - ur.lo;
     const bool pairs = (d % 2 == 0) && d <= 128;
     if (L == 0) {
         if (pairs) {
@@ -199,7 +200,8 @@ __global__ void __launch_bounds__(256) merge_stream_kernel(DecodeArgs a) {
     }
     long long before = 0, all = 0;
     for (int bb = lane; bb < a.B; bb += 64) {
-        const long long Lb = attended_len(a, a.seq_lens[bb]);
+        const PosRange rb = unit_range(a, a.seq_lens[bb]);
+        const long long Lb = rb.hi - rb.lo;
         all += Lb;
         if (bb < b) before += Lb;
     }

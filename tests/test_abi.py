@@ -204,3 +204,28 @@ def test_multi_validation_codes():
     # the workspace of a multi call is that of h * n query rows
     need = lib.kvc_decode_workspace_bytes(2, 8 * 4, 2, 128, 1, 64, 2, 0)
     assert need > lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2, 0) > 0
+
+
+def test_window_validation_codes():
+    lib = kvc.load_library()
+    f = lib.kvc_decode_attention_window
+    # every call below fails validation before any HIP call
+    args = [FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 2, 64, 10, 1, 0.1, 1, 1, None, 0, FAKE, FAKE,
+            None]
+    bad = list(args); bad[10] = 0                    # ring without a window
+    assert f(*bad) == INVALID
+    bad = list(args); bad[10] = 64                   # window + n - 1 > t_cap
+    assert f(*bad) == INVALID
+    bad = list(args); bad[10] = -3                   # negative window
+    assert f(*bad) == INVALID
+    # split plan without a workspace (window 60 + n - 1 = 61 positions: two chunks)
+    assert lib.kvc_decode_workspace_bytes(2, 16, 2, 128, 1, 61, 2, 0) > 0
+    bad = list(args); bad[10] = 60; bad[11] = 0; bad[14] = 2
+    assert f(*bad) == WORKSPACE
+    fp = lib.kvc_append_decode_attention_window_paged
+    pargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 2, 5, 0.1, 1, 1,
+             None, 0, FAKE, FAKE, None]
+    bad = list(pargs); bad[15] = -1                  # negative window
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[1] = None                 # k_new missing
+    assert fp(*bad) == INVALID
