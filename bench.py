@@ -128,12 +128,13 @@ def stored_traffic(workload: str):
     return int(kv["traffic_bytes_per_call"])
 
 
-def algorithmic_bytes(w, lengths_after, nblocks=None, n=1):
-    """Bytes one step must move: KV read, q read, out and lse written
-    (float32), the appended K/V written, and the block table read (paged).
-    n new tokens (queries) per sequence."""
+def algorithmic_bytes(w, attended, nblocks=None, n=1):
+    """Bytes one step must move: KV read (``attended`` positions per
+    sequence: all of them, or those a sliding window keeps), q read, out and
+    lse written (float32), the appended K/V written, and the block table read
+    (paged).  n new tokens (queries) per sequence."""
     B, h, g, d, eb = w.B, w.h, w.g, w.d, w.elem_bytes
-    kv_read = 2 * int(lengths_after.sum()) * g * d * eb
+    kv_read = 2 * int(attended.sum()) * g * d * eb
     q_read = B * h * n * d * eb
     out_write = B * h * n * d * 4 + B * h * n * 4
     append_write = 2 * B * g * n * d * eb
@@ -187,6 +188,11 @@ def main():
     ap.add_argument("--queries", type=int, default=1,
                     help="new tokens per sequence in one step (draft tokens checked at once, or a "
                          "prefill chunk after the cached prefix): kvc_append_decode_attention_multi")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window W: each token sees the last W positions up to itself "
+                         "(kvc_append_decode_attention_window)")
+    ap.add_argument("--ring", action="store_true",
+                    help="with --window: the contiguous cache is a ring of W + n + 14 slots")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -229,7 +235,8 @@ def main():
         k_src, v_src = x["k_pool"], x["v_pool"]
         nblocks = W.block_counts(x["seq_lens_after"], x["block_size"])
     else:
-        x = W.make_contiguous(w)
+        # a ring cache holds W + n - 1 positions plus spare slots, every slot written
+        x = W.make_contiguous(w, t_cap=args.window + args.queries + 14 if args.ring else None)
         k_src, v_src = x["k_cache"], x["v_cache"]
         nblocks = None
     cache_bytes = 2 * k_src.numel() * k_src.element_size()
@@ -238,10 +245,16 @@ def main():
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     nq = args.queries
-    if nq < 1 or (nq > 1 and (args.separate or w.paged or nq > w.cap_pad)):
+    win, ring = args.window, args.ring
+    if nq < 1 or (nq > 1 and (args.separate or w.paged or (nq > w.cap_pad and not ring))):
         print(f"--queries takes n >= 1; n > 1 only with the one-call step on a contiguous "
               f"workload, n <= {w.cap_pad} (the spare capacity)", file=sys.stderr)
         sys.exit(2)
+    if win < 0 or (win > 0 and args.separate) or (ring and (win <= 0 or w.paged)):
+        print("--window takes W >= 0 with the one-call step; --ring needs --window and a "
+              "contiguous workload", file=sys.stderr)
+        sys.exit(2)
+    windowed = win > 0
     if nq > 1:
         gen = torch.Generator().manual_seed(w.seed + 77)
         q = W.randn((w.B, w.h, nq, w.d), w.torch_dtype, gen).to(dev)
@@ -252,7 +265,10 @@ def main():
         k_new, v_new = x["k_new"].to(dev), x["v_new"].to(dev)
     sl_before, sl_after = x["seq_lens_before"].to(dev), x["seq_lens_after"].to(dev)
     bt = x["block_table"].to(dev) if w.paged else None
-    if nq > 1:
+    if windowed:  # the window calls take [B, h, n, d] queries for every n
+        q = q.view(w.B, w.h, nq, w.d)
+        k_new, v_new = k_new.view(w.B, w.g, nq, w.d), v_new.view(w.B, w.g, nq, w.d)
+    if nq > 1 or windowed:
         out = torch.empty((w.B, w.h, nq, w.d), dtype=torch.float32, device=dev)
         lse = torch.empty((w.B, w.h, nq), dtype=torch.float32, device=dev)
     else:
@@ -263,6 +279,8 @@ def main():
         max_len = bt.shape[1] * x["block_size"]
     else:
         max_len = k0.shape[2]
+    if windowed:  # plans and workspaces cover the positions a window reads
+        max_len = min(win + nq - 1, max_len)
     ws_bytes = kvc.workspace_bytes(w.B, hq, w.g, w.d, max_len, ns, dtype=w.torch_dtype,
                                    paged=w.paged)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -297,7 +315,11 @@ def main():
 
     def fused_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        if nq > 1:
+        if windowed:
+            kvc.decode_window(q, kc, vc, sl_before, win, ring=ring, block_table=bt,
+                              scale=x["scale"], num_splits=ns, workspace=ws, out=out, lse=lse,
+                              k_new=k_new, v_new=v_new)
+        elif nq > 1:
             kvc.append_decode_multi(q, k_new, v_new, kc, vc, sl_before, block_table=bt,
                                     scale=x["scale"], num_splits=ns, workspace=ws, out=out,
                                     lse=lse)
@@ -392,15 +414,18 @@ def main():
     torch.cuda.synchronize()
     dec_avg_ms = d_start.elapsed_time(d_end) / (reps * copies)
 
-    nbytes = algorithmic_bytes(w, x["seq_lens_before"] + nq, nblocks, n=nq)
+    hi = x["seq_lens_before"].to(torch.int64) + nq
+    lo = torch.clamp(x["seq_lens_before"].to(torch.int64) + 1 - win, min=0) if windowed \
+        else torch.zeros_like(hi)
+    nbytes = algorithmic_bytes(w, hi - lo, nblocks, n=nq)
     # stored counter runs are of the default (one-call) step
-    traffic = None if (args.separate or nq > 1) else stored_traffic(w.name)
+    traffic = None if (args.separate or nq > 1 or windowed) else stored_traffic(w.name)
     call_bytes = nbytes["decode"] if args.separate else nbytes["fused"]
     achieved_gbs = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.B * nq / (ms_per_step * 1e-3)
 
     cpu = None
-    if not args.no_cpu_baseline and nq == 1:
+    if not args.no_cpu_baseline and nq == 1 and not windowed:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, x, w.paged)
 
@@ -422,12 +447,16 @@ def main():
             "kv_len_before_step": w.T if w.T is not None else list(w.T_range),
             "paged": w.paged, "block_size": w.block_size if w.paged else None,
             "num_splits": ns, "split": split_mode, "chunk_len": chunk_len,
-            "num_chunks": num_chunks, "queries_per_sequence": nq,
-            "launch": {"waves_per_workgroup": waves, "workgroups": n_wgs,
-                       "chunk_len": launch_chunk, "chunks": launch_chunks},
+            "num_chunks": num_chunks, "queries_per_sequence": nq, "window": win,
+            "ring_cache": ring,
+            # the launch-shape query describes calls without a sliding window
+            "launch": None if windowed else {"waves_per_workgroup": waves, "workgroups": n_wgs,
+                                             "chunk_len": launch_chunk, "chunks": launch_chunks},
             "cache_copies_rotated": copies, "parallelism": "single GPU",
         },
         "step": ("kvc_append + decode call" if args.separate
+                 else f"one kvc_append_decode_attention_window call (W={win}, ring={ring}, "
+                      f"{nq} tokens per sequence)" if windowed
                  else f"one kvc_append_decode_attention_multi call ({nq} tokens per sequence)"
                  if nq > 1 else "one kvc_append_decode_attention call"),
         "step_hbm_gbs": round((nbytes["step"] if args.separate else nbytes["fused"])

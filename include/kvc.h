@@ -139,7 +139,8 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
  * the chunk count (0 for the other modes).  kvc_decode_workspace_bytes
  * returns the workspace the decode call needs for the same arguments (0 if
  * none); for the automatic chunk count it covers the largest count any
- * device can select.  max_seq_len is t_cap for the contiguous entry point
+ * device can select, and for automatic splits of a paged cache both the
+ * stream schedule and the chunks a sliding window uses.  max_seq_len is t_cap for the contiguous entry point
  * and max_blocks * block_size for the paged one; paged is 0 or 1.  Both are
  * pure host arithmetic.
  */
@@ -307,7 +308,8 @@ int kvc_append_decode_attention_multi_paged(const void* q, const void* k_new, co
  * the left; [P3] 10: a window cache keeps only the most recent W positions,
  * so its memory is bounded).  W = 0 means no window (the _multi calls).
  * Only the positions some token sees are read: a paged table may hold -1 for
- * blocks wholly before every window.
+ * blocks wholly before every window.  With num_splits = 0 a windowed paged
+ * call splits into chunks (its ranges are nearly equal), not stream mode.
  *
  *   ring (contiguous calls only): 1 = the cache is a ring of t_cap slots,
  *     position p in slot p mod t_cap, positions not limited by t_cap.

@@ -87,7 +87,7 @@ static long chunks_for_slots(long slots, int B, int g, int max_seq_len) {
 }
 
 static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq_len,
-                              int num_splits, bool paged) {
+                              int num_splits, bool paged, bool windowed = false) {
     Schedule sc;
     sc.kind = choose_kernel(dtype, d, h / g);
     // Stream mode keeps global positions in 64-bit products p * total with
@@ -95,7 +95,10 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     const bool small_enough = (long double)B * g * max_seq_len < (long double)(1LL << 40);
     const int slices = row_slices(sc.kind, h / g);
     const bool can_stream = sc.kind != kGeneric && slices == 1 && B <= kStreamMaxB && small_enough;
-    sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM || (num_splits == 0 && paged));
+    // automatic: paged caches stream (lengths vary); with a sliding window the
+    // ranges are at most W + n - 1 long and nearly equal, so they chunk
+    sc.stream = can_stream &&
+                (num_splits == KVC_SPLITS_STREAM || (num_splits == 0 && paged && !windowed));
     sc.auto_chunks = !sc.stream && num_splits <= 0 && sc.kind != kGeneric;
     if (sc.auto_chunks) {
         // workspace bound: every slot of a 256-CU device, 4 work-groups each
@@ -117,6 +120,20 @@ static size_t workspace_for(int B, int h, int g, int d, const Schedule& sc) {
     const size_t rows = workspace_rows(B, h, g, sc);
     if (rows == 0) return 0;
     return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// Workspace a call needs: for automatic splits of a paged cache, enough for
+// both schedules it may take (stream, or chunks under a sliding window), so
+// that one size query serves windowed and plain calls.
+static size_t required_workspace(int B, int h, int g, int d, int dtype, int max_len,
+                                 int num_splits, bool paged) {
+    size_t need = workspace_for(B, h, g, d, make_schedule(B, h, g, d, dtype, max_len, num_splits, paged));
+    if (paged && num_splits == 0) {
+        const size_t w = workspace_for(B, h, g, d,
+                                       make_schedule(B, h, g, d, dtype, max_len, num_splits, paged, true));
+        if (w > need) need = w;
+    }
+    return need;
 }
 
 // Compute units of the current device (cached per device).
@@ -184,14 +201,15 @@ struct AutoShape {
     long chunks;
 };
 
-static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, bool gen) {
+static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, bool paged,
+                            bool gen) {
     const long units = (long)B * g;
-    const void* f4 = kernel_for(kind, m, false, false, 4, gen);
+    const void* f4 = kernel_for(kind, m, paged, false, 4, gen);
     const long slots4 = device_slots(f4, 4);
     AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};
 #if KVC_AUTO_WIDE
     const int wv = 8;
-    const void* fn = kernel_for(kind, m, false, false, wv, gen);
+    const void* fn = kernel_for(kind, m, paged, false, wv, gen);
     const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
     if (slots > 0 && units >= slots && slots * wv >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
         return AutoShape{wv, 1};
@@ -233,7 +251,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
         a.num_wgs = (int)(P < 1 ? 1 : P);
     } else if (sc.auto_chunks) {
         const AutoShape sh = auto_shape(sc.kind, a.m < 32 ? a.m : 32, a.B * a.slices, a.g, max_len,
-                                        general_features(a));
+                                        paged, general_features(a));
         a.waves = sh.waves;
         // One chunk per unit may exceed kMaxChunk: the engines walk a chunk in
         // windows of at most kMaxChunk positions.
@@ -247,8 +265,8 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
     const bool paged = a.block_table != nullptr;
-    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
-    const size_t need = workspace_for(a.B, a.h, a.g, a.d, sc);
+    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0);
+    const size_t need = required_workspace(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
     if (a.B == 0) return KVC_OK;
     resolve_launch(a, sc, paged, max_len);
@@ -347,7 +365,7 @@ size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max
         max_seq_len < 0)
         return 0;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
-    return workspace_for(B, h, g, d, make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0));
+    return required_workspace(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
 }
 
 int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
