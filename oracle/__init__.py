@@ -21,6 +21,12 @@ module only marshals arrays into it.  Pages followed:
   last W positions, so its memory is bounded): the token at position x sees
   positions max(0, x + 1 - W) .. x, the last W including itself.  A ring
   cache of t_cap slots keeps position p in slot p mod t_cap.
+* Block operations on a paged pool (plumephp.com section 4.3: requests fork
+  a block table and share physical blocks; a block is copied before a
+  sharing request writes into it; zwjcode.cn section 11: after beams are
+  re-ranked, each beam's cache must follow its chosen parent): copy whole
+  blocks, gather block-table rows by parent, gather contiguous caches by
+  parent.  Plain index copies.
 * Several new tokens at once (a prefill after a cached prefix, limoncc.com
   section 5.2; draft tokens, plumephp.com section 5.3): token t of a sequence
   with P cached positions sits at position P + t and sees positions 0..P + t
@@ -348,3 +354,44 @@ def decode_window(q, k, v, seq_lens_before, scale, window, ring=False, block_tab
         out[:, :, t] = o
         lse[:, :, t] = l
     return out, lse
+
+
+def copy_blocks(k_pool, v_pool, pairs):
+    """Copy physical block src to dst (all KV heads, K and V) for every
+    (src, dst) in ``pairs``; pairs naming a block outside the pool are
+    skipped.  Returns new raw numpy pools."""
+    kp, _ = _raw(k_pool)
+    vp, _ = _raw(v_pool)
+    kp, vp = kp.copy(), vp.copy()
+    nb = kp.shape[0]
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= src < nb and 0 <= dst < nb:
+            kp[dst] = kp[src]
+            vp[dst] = vp[src]
+    return kp, vp
+
+
+def fork_tables(tables, seq_lens, parent):
+    """Row b of the result is row parent[b] of ``tables`` (and its length):
+    the forked requests share their parent's physical blocks."""
+    t = _i32(tables)
+    sl = _i32(seq_lens)
+    par = _i32(parent).astype(np.int64)
+    return t[par].copy(), sl[par].copy()
+
+
+def gather_cache(k_cache, v_cache, parent, seq_lens):
+    """Contiguous caches re-ranked by parent: position p < seq_lens[parent[b]]
+    of sequence b is position p of sequence parent[b].  Positions past that
+    length are zero.  Returns raw numpy caches [len(parent), g, t_cap, d]."""
+    kc, _ = _raw(k_cache)
+    vc, _ = _raw(v_cache)
+    sl = _i32(seq_lens)
+    par = _i32(parent).astype(np.int64)
+    ko = np.zeros((len(par),) + kc.shape[1:], dtype=kc.dtype)
+    vo = np.zeros_like(ko)
+    for b, pb in enumerate(par):
+        L = int(sl[pb])
+        ko[b, :, :L] = kc[pb, :, :L]
+        vo[b, :, :L] = vc[pb, :, :L]
+    return ko, vo

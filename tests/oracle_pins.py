@@ -471,6 +471,82 @@ def pin_ring_cache_equals_linear():
             before = before + n
 
 
+# ----------------------------------------------------------------------------
+# Shared prefixes with copy-on-write ([P4] 4.3; [P2] 3.2: a shared block is
+# copied before a request writes into it, so requests never see each other's
+# tokens) and beam re-ranking ([P3] 11).  Three requests fork one prompt's
+# block table; each appends its own tokens, copying the last shared block
+# first; every request's attention equals attention over its own private
+# contiguous cache, and the prompt blocks stay shared and unchanged.
+def pin_fork_copy_on_write_isolation():
+    gen = torch.Generator().manual_seed(31)
+    g, d, h, bs, P = 2, 8, 4, 4, 10          # 10-token prompt: blocks 0, 1 full, 2 partial
+    prompt_k = torch.randn(g, P, d, generator=gen)
+    prompt_v = torch.randn(g, P, d, generator=gen)
+    nb = 12
+    kp = np.zeros((nb, g, bs, d), np.float32)
+    vp = np.zeros_like(kp)
+    for lb in range(3):
+        n = min(bs, P - lb * bs)
+        kp[lb, :, :n] = prompt_k[:, lb * bs: lb * bs + n].numpy()
+        vp[lb, :, :n] = prompt_v[:, lb * bs: lb * bs + n].numpy()
+    table0 = np.array([[0, 1, 2, -1]], np.int32)
+    tables, lens = oracle.fork_tables(table0, [P], [0, 0, 0])
+    assert np.array_equal(tables, np.repeat(table0, 3, 0)) and list(lens) == [P] * 3
+    # requests 1 and 2 write into the shared block 2: copy it first (COW)
+    kp, vp = oracle.copy_blocks(kp, vp, [(2, 3), (2, 4)])
+    tables[1, 2], tables[2, 2] = 3, 4
+    new_k = torch.randn(3, g, 1, d, generator=gen)
+    new_v = torch.randn(3, g, 1, d, generator=gen)
+    kp, vp = oracle.append_multi(new_k, new_v, kp, vp, lens, block_table=tables)
+    # blocks 0 and 1 are still shared and hold the prompt; block 2 holds
+    # request 0's token, blocks 3 and 4 the others'
+    for lb in range(2):
+        assert np.array_equal(kp[lb], prompt_k[:, lb * bs:(lb + 1) * bs].numpy())
+    q = torch.randn(3, h, 1, d, generator=gen)
+    o, l = oracle.decode_multi(q, kp, vp, lens, 0.5, block_table=tables, block_size=bs)
+    for r in range(3):
+        kc = torch.cat([prompt_k, new_k[r, :, :, :]], 1).unsqueeze(0).contiguous()
+        vc = torch.cat([prompt_v, new_v[r, :, :, :]], 1).unsqueeze(0).contiguous()
+        orr, lr = oracle.decode(q[r:r + 1, :, 0].contiguous(), kc, vc, [P + 1], 0.5)
+        assert np.array_equal(o[r:r + 1, :, 0], orr) and np.array_equal(l[r:r + 1, :, 0], lr)
+    # out-of-pool pairs are skipped; copying a block onto itself changes nothing
+    kq, vq = oracle.copy_blocks(kp, vp, [(0, nb), (-1, 5), (1, 1)])
+    assert np.array_equal(kq, kp) and np.array_equal(vq, vp)
+
+
+def pin_beam_gather():
+    gen = torch.Generator().manual_seed(32)
+    B, g, T, d = 4, 2, 9, 4
+    kc = torch.randn(B, g, T, d, generator=gen)
+    vc = torch.randn(B, g, T, d, generator=gen)
+    lens = torch.tensor([9, 3, 0, 6], dtype=torch.int32)
+    parent = [3, 3, 0, 1, 2]
+    ko, vo = oracle.gather_cache(kc, vc, parent, lens)
+    assert ko.shape == (5, g, T, d)
+    for b, pb in enumerate(parent):
+        L = int(lens[pb])
+        assert np.array_equal(ko[b, :, :L], kc[pb, :, :L].numpy())
+        assert not ko[b, :, L:].any() and not vo[b, :, L:].any()
+        assert np.array_equal(vo[b, :, :L], vc[pb, :, :L].numpy())
+    # re-ranked beams attend to their parents' histories
+    q = torch.randn(5, 4, d, generator=gen)
+    o, l = oracle.decode(q, ko, vo, lens[parent], 0.7)
+    for b, pb in enumerate(parent):
+        o1, l1 = oracle.decode(q[b:b + 1], kc[pb:pb + 1].contiguous(), vc[pb:pb + 1].contiguous(),
+                               lens[pb:pb + 1], 0.7)
+        assert np.array_equal(o[b:b + 1], o1) and np.array_equal(l[b:b + 1], l1)
+    # the paged form: forking the block tables by parent (no data moves)
+    # gives the same attention as gathering the contiguous caches
+    table, nb = W.make_block_table(lens, 4, perm_seed=33, extra_blocks=1)
+    kp = W.scatter_to_pool(kc, lens, table, nb, 4)
+    vp = W.scatter_to_pool(vc, lens, table, nb, 4)
+    ft, fl = oracle.fork_tables(table, lens, parent)
+    assert list(fl) == [int(lens[pb]) for pb in parent]
+    op, lp = oracle.decode(q, kp, vp, fl, 0.7, block_table=ft, block_size=4)
+    assert np.array_equal(op, o) and np.array_equal(lp, l)
+
+
 ALL_PINS = [
     pin_d1_worked_example,
     pin_sdpa_crosscheck,
@@ -489,4 +565,6 @@ ALL_PINS = [
     pin_multi_query_equals_causal_prefill,
     pin_sliding_window,
     pin_ring_cache_equals_linear,
+    pin_fork_copy_on_write_isolation,
+    pin_beam_gather,
 ]

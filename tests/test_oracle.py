@@ -166,3 +166,47 @@ def test_planted_window_mistake_is_caught(name, monkeypatch):
         except Exception:  # noqa: BLE001 - any failure counts
             failed += 1
     assert failed, f"no window pin caught {name}"
+
+
+def _copy_blocks_k_only(k_pool, v_pool, pairs):
+    kp, _ = oracle._raw(k_pool)
+    vp, _ = oracle._raw(v_pool)
+    kp, vp = kp.copy(), vp.copy()
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= src < kp.shape[0] and 0 <= dst < kp.shape[0]:
+            kp[dst] = kp[src]
+    return kp, vp
+
+
+def _gather_whole_rows(k_cache, v_cache, parent, seq_lens):
+    kc, _ = oracle._raw(k_cache)
+    vc, _ = oracle._raw(v_cache)
+    par = np.asarray(parent, dtype=np.int64)
+    return kc[par].copy(), vc[par].copy()
+
+
+def _fork_by_index(tables, seq_lens, parent):
+    t = oracle._i32(tables)
+    sl = oracle._i32(seq_lens)
+    idx = np.arange(len(parent)) % t.shape[0]
+    return t[idx].copy(), sl[idx].copy()
+
+
+BLOCK_MUTATIONS = {
+    "copy_blocks_k_only": ("copy_blocks", _copy_blocks_k_only),
+    "gather_whole_rows": ("gather_cache", _gather_whole_rows),
+    "fork_by_index": ("fork_tables", _fork_by_index),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_MUTATIONS))
+def test_planted_block_op_mistake_is_caught(name, monkeypatch):
+    attr, fn = BLOCK_MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    failed = 0
+    for pin in (P.pin_fork_copy_on_write_isolation, P.pin_beam_gather):
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure counts
+            failed += 1
+    assert failed, f"no block-op pin caught {name}"
