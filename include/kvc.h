@@ -350,6 +350,43 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
                                              size_t workspace_bytes, float* out, float* lse,
                                              hipStream_t stream);
 
+/*
+ * Block operations for shared and re-ranked caches ([P4] 4.3: requests that
+ * share a prompt fork its block table and point at the same physical
+ * blocks; before one of them writes into a shared block, the block is copied
+ * and that request's table is pointed at the copy; [P2] 3.2: shared blocks
+ * are read-only, copied on write; [P3] 11: after beams are re-ranked, each
+ * beam's cache must follow its chosen parent).  The host keeps reference
+ * counts and allocates blocks; these calls move bytes and table rows,
+ * bit-exactly, asynchronously on `stream`.
+ *
+ * kvc_copy_blocks: for each of the num_pairs pairs (src, dst) of device
+ *   int32 pairs[num_pairs][2], copy physical block src of both pools
+ *   [num_blocks, g, block_size, d] (all KV heads) to block dst.  Pairs that
+ *   name a block outside [0, num_blocks), and src == dst, are skipped.  No
+ *   dst may appear twice or also be a src (the copies run concurrently).
+ * kvc_fork_block_tables: block_table_out[b, :] = block_table[parent[b], :]
+ *   and seq_lens_out[b] = seq_lens[parent[b]] for b < B (tables
+ *   [B_src, max_blocks] -> [B, max_blocks]); a parent outside [0, B_src)
+ *   gives a row of -1 and length 0.  Outputs must not alias the inputs.
+ * kvc_gather_cache: contiguous caches [B_src, g, t_cap, d] -> [B, g, t_cap,
+ *   d]: positions p < seq_lens[parent[b]] (clamped to [0, t_cap]) of
+ *   sequence b are copied from sequence parent[b]; other positions of the
+ *   destination are not written; nothing is written for a parent outside
+ *   [0, B_src).  The two destinations must be distinct buffers, distinct
+ *   from both sources.
+ * Status: KVC_ERR_INVALID for bad sizes, null pointers or aliasing,
+ *   KVC_ERR_UNSUPPORTED for other dtypes or t_cap > 4194240 (gather).
+ */
+int kvc_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
+                    int num_blocks, int g, int block_size, int d, int dtype, hipStream_t stream);
+int kvc_fork_block_tables(const int32_t* block_table, const int32_t* seq_lens, int B_src,
+                          int max_blocks, const int32_t* parent, int B, int32_t* block_table_out,
+                          int32_t* seq_lens_out, hipStream_t stream);
+int kvc_gather_cache(const void* k_src, const void* v_src, const int32_t* seq_lens, int B_src,
+                     const int32_t* parent, int B, void* k_dst, void* v_dst, int g, int t_cap,
+                     int d, int dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,12 @@ def load_library():
                                                              vp, ip, ip, ip, ip, ip, ip, fp, ip,
                                                              ip, vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention_window_paged.restype = ip
+    lib.kvc_copy_blocks.argtypes = [vp, vp, vp, ip, ip, ip, ip, ip, ip, vp]
+    lib.kvc_copy_blocks.restype = ip
+    lib.kvc_fork_block_tables.argtypes = [vp, vp, ip, ip, vp, ip, vp, vp, vp]
+    lib.kvc_fork_block_tables.restype = ip
+    lib.kvc_gather_cache.argtypes = [vp, vp, vp, ip, vp, ip, vp, vp, ip, ip, ip, ip, vp]
+    lib.kvc_gather_cache.restype = ip
     lib.kvc_decode_attention.argtypes = [vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, ip, vp, sz,
                                          vp, vp, vp]
     lib.kvc_decode_attention.restype = ip
@@ -449,3 +455,43 @@ def decode_window(q, k_cache, v_cache, seq_lens, window: int, ring: bool = False
                 _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_*decode_attention_window_paged", st)
     return out, lse
+
+
+def copy_blocks(k_pool, v_pool, pairs, stream=None):
+    """Copy physical block src -> dst of both pools [NB,g,bs,d] for every row
+    (src, dst) of the device int32 tensor ``pairs`` [n, 2] (copy-on-write)."""
+    lib = load_library()
+    nb, g, bs, d = k_pool.shape
+    n = pairs.shape[0] if pairs.numel() else 0
+    _check("kvc_copy_blocks", lib.kvc_copy_blocks(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+        _dev(pairs, "pairs", torch.int32) if n else None, n, nb, g, bs, d,
+        _dtype_code(k_pool), _stream(stream)))
+
+
+def fork_block_tables(block_table, seq_lens, parent, stream=None):
+    """Forked tables: row b is row parent[b] (and its length).  Returns
+    (tables [B,max_blocks], seq_lens [B]) on the device."""
+    lib = load_library()
+    B_src, mb = block_table.shape
+    B = parent.shape[0]
+    out_t = torch.empty((B, mb), dtype=torch.int32, device=block_table.device)
+    out_l = torch.empty((B,), dtype=torch.int32, device=block_table.device)
+    _check("kvc_fork_block_tables", lib.kvc_fork_block_tables(
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        B_src, mb, _dev(parent, "parent", torch.int32), B, _dev(out_t, "out"), _dev(out_l, "out"),
+        _stream(stream)))
+    return out_t, out_l
+
+
+def gather_cache(k_src, v_src, seq_lens, parent, k_dst, v_dst, stream=None):
+    """Contiguous caches re-ranked by parent into k_dst, v_dst [B,g,t_cap,d]:
+    positions below seq_lens[parent[b]] of sequence b come from parent[b]."""
+    lib = load_library()
+    B_src, g, t_cap, d = k_src.shape
+    B = parent.shape[0]
+    _check("kvc_gather_cache", lib.kvc_gather_cache(
+        _dev(k_src, "k_src"), _dev(v_src, "v_src", k_src.dtype),
+        _dev(seq_lens, "seq_lens", torch.int32), B_src, _dev(parent, "parent", torch.int32), B,
+        _dev(k_dst, "k_dst", k_src.dtype), _dev(v_dst, "v_dst", k_src.dtype), g, t_cap, d,
+        _dtype_code(k_src), _stream(stream)))

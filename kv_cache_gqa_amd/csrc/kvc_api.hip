@@ -592,4 +592,49 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
                         scale, dtype, num_splits, workspace, workspace_bytes, out, lse, stream);
 }
 
+int kvc_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
+                    int num_blocks, int g, int block_size, int d, int dtype, hipStream_t stream) {
+    if (num_pairs < 0 || num_blocks <= 0 || g <= 0 || block_size <= 0 || d <= 0)
+        return KVC_ERR_INVALID;
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return KVC_OK;
+    if (!k_pool || !v_pool || !pairs) return KVC_ERR_INVALID;
+    const long block_bytes = (long)g * block_size * d * (dtype == KVC_F32 ? 4 : 2);
+    if (launch_copy_blocks(k_pool, v_pool, pairs, num_pairs, num_blocks, block_bytes, stream) !=
+        hipSuccess)
+        return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
+int kvc_fork_block_tables(const int32_t* block_table, const int32_t* seq_lens, int B_src,
+                          int max_blocks, const int32_t* parent, int B, int32_t* block_table_out,
+                          int32_t* seq_lens_out, hipStream_t stream) {
+    if (B < 0 || B_src <= 0 || max_blocks <= 0) return KVC_ERR_INVALID;
+    if (B == 0) return KVC_OK;
+    if (!block_table || !seq_lens || !parent || !block_table_out || !seq_lens_out)
+        return KVC_ERR_INVALID;
+    if (block_table_out == block_table || seq_lens_out == seq_lens) return KVC_ERR_INVALID;
+    if (launch_fork_tables(block_table, seq_lens, B_src, max_blocks, parent, B, block_table_out,
+                           seq_lens_out, stream) != hipSuccess)
+        return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
+int kvc_gather_cache(const void* k_src, const void* v_src, const int32_t* seq_lens, int B_src,
+                     const int32_t* parent, int B, void* k_dst, void* v_dst, int g, int t_cap,
+                     int d, int dtype, hipStream_t stream) {
+    if (B < 0 || B_src <= 0 || g <= 0 || t_cap <= 0 || d <= 0) return KVC_ERR_INVALID;
+    if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+    if (B == 0) return KVC_OK;
+    if (!k_src || !v_src || !seq_lens || !parent || !k_dst || !v_dst) return KVC_ERR_INVALID;
+    if (k_dst == k_src || v_dst == v_src || k_dst == v_src || v_dst == k_src || k_dst == v_dst)
+        return KVC_ERR_INVALID;
+    if ((long)B * g > 0x7fffffffL || ceil_div(t_cap, 64) > 65535) return KVC_ERR_UNSUPPORTED;
+    const long row_bytes = (long)d * (dtype == KVC_F32 ? 4 : 2);
+    if (launch_gather_cache(k_src, v_src, k_dst, v_dst, seq_lens, B_src, parent, B, g, t_cap,
+                            row_bytes, stream) != hipSuccess)
+        return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
 }  // extern "C"

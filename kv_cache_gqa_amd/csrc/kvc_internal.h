@@ -99,6 +99,14 @@ const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs,
+                              int num_blocks, long block_bytes, hipStream_t s);
+hipError_t launch_fork_tables(const int32_t* tables, const int32_t* lens, int B_src, int max_blocks,
+                              const int32_t* parent, int B, int32_t* tables_out, int32_t* lens_out,
+                              hipStream_t s);
+hipError_t launch_gather_cache(const void* k_src, const void* v_src, void* k_dst, void* v_dst,
+                               const int32_t* lens, int B_src, const int32_t* parent, int B, int g,
+                               int t_cap, long row_bytes, hipStream_t s);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,

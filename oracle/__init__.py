@@ -380,16 +380,20 @@ def fork_tables(tables, seq_lens, parent):
     return t[par].copy(), sl[par].copy()
 
 
-def gather_cache(k_cache, v_cache, parent, seq_lens):
+def gather_cache(k_cache, v_cache, parent, seq_lens, k_dst=None, v_dst=None):
     """Contiguous caches re-ranked by parent: position p < seq_lens[parent[b]]
     of sequence b is position p of sequence parent[b].  Positions past that
-    length are zero.  Returns raw numpy caches [len(parent), g, t_cap, d]."""
+    length keep what k_dst / v_dst held (zero when not given).  Returns raw
+    numpy caches [len(parent), g, t_cap, d]."""
     kc, _ = _raw(k_cache)
     vc, _ = _raw(v_cache)
     sl = _i32(seq_lens)
     par = _i32(parent).astype(np.int64)
-    ko = np.zeros((len(par),) + kc.shape[1:], dtype=kc.dtype)
-    vo = np.zeros_like(ko)
+    if k_dst is None:
+        ko = np.zeros((len(par),) + kc.shape[1:], dtype=kc.dtype)
+        vo = np.zeros_like(ko)
+    else:
+        ko, vo = _raw(k_dst)[0].copy(), _raw(v_dst)[0].copy()
     for b, pb in enumerate(par):
         L = int(sl[pb])
         ko[b, :, :L] = kc[pb, :, :L]

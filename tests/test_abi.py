@@ -229,3 +229,22 @@ def test_window_validation_codes():
     assert fp(*bad) == INVALID
     bad = list(pargs); bad[1] = None                 # k_new missing
     assert fp(*bad) == INVALID
+
+
+def test_block_op_validation_codes():
+    lib = kvc.load_library()
+    # every call below fails validation (or has nothing to do) before any HIP call
+    assert lib.kvc_copy_blocks(FAKE, FAKE, FAKE, 2, 0, 2, 16, 128, 1, None) == INVALID   # no blocks
+    assert lib.kvc_copy_blocks(FAKE, FAKE, FAKE, -1, 8, 2, 16, 128, 1, None) == INVALID
+    assert lib.kvc_copy_blocks(FAKE, FAKE, FAKE, 2, 8, 2, 16, 128, 5, None) == UNSUPPORTED
+    assert lib.kvc_copy_blocks(None, FAKE, FAKE, 2, 8, 2, 16, 128, 1, None) == INVALID
+    assert lib.kvc_copy_blocks(FAKE, FAKE, None, 0, 8, 2, 16, 128, 1, None) == OK     # no pairs
+    f = lib.kvc_fork_block_tables
+    assert f(FAKE, FAKE, 0, 4, FAKE, 2, FAKE, FAKE, None) == INVALID                  # B_src = 0
+    assert f(FAKE, FAKE, 2, 4, FAKE, 2, FAKE, FAKE, None) == INVALID                  # aliasing
+    assert f(FAKE, FAKE, 2, 4, FAKE, 0, None, None, None) == OK
+    gc = lib.kvc_gather_cache
+    other = ctypes.c_void_p(0x2000)
+    assert gc(FAKE, FAKE, FAKE, 2, FAKE, 2, other, other, 2, 64, 128, 1, None) == INVALID  # aliasing
+    assert gc(FAKE, other, FAKE, 2, FAKE, 2, FAKE, other, 2, 64, 128, 1, None) == INVALID
+    assert gc(FAKE, FAKE, FAKE, 2, FAKE, 2, other, other, 2, 0, 128, 1, None) == INVALID   # t_cap = 0
