@@ -172,6 +172,66 @@ def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0):
                       f"{per_step:.3f} s per run"}
 
 
+def bench_block_op(args, torch, kvc, W):
+    """Bandwidth of the block operations: bytes read + written per call over
+    the average call time (K calls captured in one HIP graph)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(77)
+    if args.op == "copy_blocks":
+        w = W.WORKLOADS["paged_gqa_bf16"] if args.workload == "gqa_70b_bf16" else W.WORKLOADS[args.workload]
+        nb, n_pairs = 16384, 4096
+        kp = torch.empty((nb, w.g, w.block_size, w.d), dtype=w.torch_dtype, device=dev).normal_()
+        vp = torch.empty_like(kp).normal_()
+        perm = torch.randperm(nb, generator=gen)
+        pairs = torch.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], 1).to(torch.int32).to(dev)
+        moved = 2 * 2 * n_pairs * w.g * w.block_size * w.d * w.elem_bytes
+        call = lambda: kvc.copy_blocks(kp, vp, pairs)  # noqa: E731
+        cfg = {"workload": f"copy_blocks {n_pairs} of {nb} blocks [g={w.g}, bs={w.block_size}, "
+                           f"d={w.d}] bf16", "pairs": n_pairs}
+    else:
+        w = W.WORKLOADS[args.workload]
+        x = W.make_contiguous(w)
+        ks, vs = x["k_cache"].to(dev), x["v_cache"].to(dev)
+        kd, vd = torch.empty_like(ks), torch.empty_like(vs)
+        lens = x["seq_lens_after"].to(dev)
+        parent = torch.randint(0, w.B, (w.B,), generator=gen, dtype=torch.int32)
+        moved = 2 * 2 * int(x["seq_lens_after"][parent.long()].sum()) * w.g * w.d * w.elem_bytes
+        parent = parent.to(dev)
+        call = lambda: kvc.gather_cache(ks, vs, lens, parent, kd, vd)  # noqa: E731
+        cfg = {"workload": f"gather_cache {w.name} (B={w.B}, g={w.g}, T={w.T}, d={w.d})"}
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"{args.op} bandwidth (bytes read + written per call / call time)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (bit-exact copies)",
+        "data": "synthetic, seeded", "config": cfg,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": moved, "traffic": None},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +253,10 @@ def main():
                          "(kvc_append_decode_attention_window)")
     ap.add_argument("--ring", action="store_true",
                     help="with --window: the contiguous cache is a ring of W + n + 14 slots")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "gather_cache"],
+                    help="decode: the decode step (default); copy_blocks: copy-on-write copies of "
+                         "4096 pool blocks of the paged workload; gather_cache: beam re-ranking of "
+                         "the contiguous workload's caches")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -225,6 +289,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     kvc.load_library()
+    if args.op != "decode":
+        bench_block_op(args, torch, kvc, W)
+        return
     w = W.WORKLOADS[args.workload]
     ns = w.num_splits if args.num_splits is None else args.num_splits
     dev = torch.device("cuda:0")
