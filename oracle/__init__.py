@@ -27,6 +27,14 @@ module only marshals arrays into it.  Pages followed:
   re-ranked, each beam's cache must follow its chosen parent): copy whole
   blocks, gather block-table rows by parent, gather contiguous caches by
   parent.  Plain index copies.
+* Low-precision cache (plumephp.com section 2.5: FP8 attention;
+  zwjcode.cn section 14: low-bit K/V cut memory and bandwidth at a cost in
+  error): K and V stored as OCP FP8 E4M3 codes (1 sign, 4 exponent bits with
+  bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN; largest finite
+  value 448) with one float32 scale per KV head.  Stored code of x:
+  nearest E4M3 value to the float32 quotient x / scale, ties to the even
+  code, values beyond 448 saturating to 448.  Attention runs over the
+  dequantised values code * scale, exactly as over any other cache.
 * Several new tokens at once (a prefill after a cached prefix, limoncc.com
   section 5.2; draft tokens, plumephp.com section 5.3): token t of a sequence
   with P cached positions sits at position P + t and sees positions 0..P + t
@@ -399,3 +407,136 @@ def gather_cache(k_cache, v_cache, parent, seq_lens, k_dst=None, v_dst=None):
         ko[b, :, :L] = kc[pb, :, :L]
         vo[b, :, :L] = vc[pb, :, :L]
     return ko, vo
+
+
+def e4m3_values():
+    """float64 value of each of the 256 E4M3 codes (NaN for the two NaN codes)."""
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def e4m3_encode(y):
+    """Codes (uint8) of float32 values y: nearest E4M3 value, ties to the even
+    code, |y| > 448 saturating to 448, NaN to 0x7F with y's sign, and the sign
+    kept for values that round to zero."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)
+    pos = e4m3_values()[:127]                 # codes 0..126: 0 .. 448, increasing
+    a_sat = np.minimum(a, 448.0)
+    hi = np.searchsorted(pos, a_sat, side="left")   # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a_sat - pos[lo]
+    d_hi = pos[hi] - a_sat
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pos[hi] == a_sat, hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    code = np.where(np.isnan(a), np.uint8(0x7F), code).astype(np.uint8)
+    return (code | (np.signbit(y).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def quantize_fp8(x, scale, head_axis):
+    """E4M3 codes of bf16/float32 values x with one float32 scale per KV head
+    (``scale`` [g], indexed along ``head_axis`` of x): code of x / scale,
+    the quotient taken in float32."""
+    xa, xd = _raw(x)
+    xf = xa.astype(np.uint32) << 16 if xd == BF16 else xa
+    xf = xf.view(np.float32) if xd == BF16 else xf
+    sc = np.asarray(scale, dtype=np.float32)
+    shape = [1] * xf.ndim
+    shape[head_axis] = -1
+    return e4m3_encode((xf / sc.reshape(shape)).astype(np.float32))
+
+
+def append_fp8(k_new, v_new, k_codes, v_codes, k_scale, v_scale, seq_lens_before,
+               block_table=None):
+    """Quantise n new tokens per sequence (k_new, v_new [B,g,n,d] bf16) and
+    write their codes at positions seq_lens_before[b] + t of uint8 caches
+    (contiguous [B,g,t_cap,d] or pools [NB,g,bs,d] through block_table).
+    Returns new uint8 caches."""
+    kq = quantize_fp8(k_new, k_scale, 1)
+    vq = quantize_fp8(v_new, v_scale, 1)
+    kc = np.array(k_codes, dtype=np.uint8, copy=True)
+    vc = np.array(v_codes, dtype=np.uint8, copy=True)
+    before = _i32(seq_lens_before)
+    bt = None if block_table is None else _i32(block_table)
+    B, g, n, _ = kq.shape
+    for b in range(B):
+        for t in range(n):
+            p = int(before[b]) + t
+            if bt is None:
+                kc[b, :, p] = kq[b, :, t]
+                vc[b, :, p] = vq[b, :, t]
+            else:
+                bs = kc.shape[2]
+                blk = int(bt[b, p // bs])
+                kc[blk, :, p % bs] = kq[b, :, t]
+                vc[blk, :, p % bs] = vq[b, :, t]
+    return kc, vc
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale, block_table=None,
+               block_size=16, nthreads=0):
+    """Single-token attention over dequantised FP8 caches: K = code * k_scale[j],
+    V = code * v_scale[j].  The code values are exact in float32, so each KV
+    head j is attended with the plain definition over the code values with
+    score scale scale * k_scale[j] (the float32 scale times the float32 head
+    scale, exact in float64) and its output multiplied by v_scale[j]."""
+    vals = e4m3_values().astype(np.float32)
+    kf = vals[np.asarray(k_codes, dtype=np.uint8)]
+    vf = vals[np.asarray(v_codes, dtype=np.uint8)]
+    qa, _ = _raw(q)
+    B, h, d = qa.shape
+    g = kf.shape[1]
+    m = h // g
+    ks = np.asarray(k_scale, dtype=np.float32)
+    vs = np.asarray(v_scale, dtype=np.float32)
+    out = np.zeros((B, h, d), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    s32 = float(np.float32(scale))
+    for j in range(g):
+        qj = np.ascontiguousarray(qa[:, j * m:(j + 1) * m])
+        kj = np.ascontiguousarray(kf[:, j:j + 1])
+        vj = np.ascontiguousarray(vf[:, j:j + 1])
+        o, l = _decode_exact_scale(qj, kj, vj, seq_lens, s32 * float(ks[j]), block_table,
+                                   block_size, nthreads)
+        out[:, j * m:(j + 1) * m] = o * float(vs[j])
+        lse[:, j * m:(j + 1) * m] = l
+    return out, lse
+
+
+def _decode_exact_scale(q, k, v, seq_lens, scale_f64, block_table, block_size, nthreads):
+    """``decode`` with the score scale used as the given float64 value."""
+    qa, qd = _raw(q)
+    ka, kd = _raw(k)
+    va, vd = _raw(v)
+    if qd != kd:  # bf16 queries over float32 code values: widen q exactly
+        qa = (qa.astype(np.uint32) << 16).view(np.float32) if qd == BF16 else qa
+        qd = F32
+    dt = _same_dtype(qd, kd, vd)
+    sl = _i32(seq_lens)
+    B, h, d = qa.shape
+    if block_table is None:
+        _, g, t_cap, _ = ka.shape
+        bt, max_blocks, bsz = None, 0, 0
+    else:
+        bt = _i32(block_table)
+        _, g, bsz, _ = ka.shape
+        assert bsz == block_size
+        max_blocks = bt.shape[1]
+        t_cap = 0
+    out = np.zeros((B, h, d), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    _load().kvo_decode(_ptr(np.ascontiguousarray(qa)), _ptr(ka), _ptr(va), dt,
+                       _ptr(bt) if bt is not None else None, max_blocks, bsz,
+                       _ptr(sl), B, h, g, d, t_cap, float(scale_f64), _ptr(out), _ptr(lse),
+                       int(nthreads))
+    return out, lse

@@ -547,6 +547,71 @@ def pin_beam_gather():
     assert np.array_equal(op, o) and np.array_equal(lp, l)
 
 
+# ----------------------------------------------------------------------------
+# FP8 E4M3 cache ([P4] 2.5: FP8 attention; [P3] 14: low-bit K/V).  The
+# format's closed-form points, round trips, ties to even, saturation and the
+# sign of zero; torch's own float8_e4m3fn conversion agrees wherever it is
+# finite (below 464); attention over the dequantised caches equals torch SDPA
+# in float64 over torch's dequantisation of the same codes.
+def pin_fp8_format():
+    v = oracle.e4m3_values()
+    assert v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
+    assert v[0x38] == 1.0 and v[0x39] == 1.125 and v[0xB8] == -1.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and v[0x80] == 0 and np.signbit(v[0x80])
+    assert np.all(np.diff(v[:127]) > 0)
+    finite = [c for c in range(256) if not np.isnan(v[c])]
+    assert np.array_equal(oracle.e4m3_encode(v[finite].astype(np.float32)), np.array(finite, np.uint8))
+    enc = oracle.e4m3_encode
+    assert list(enc([1.0625, 1.1875, 500.0, 1e30, 448.0, 460.0, -1e-9, 2.0 ** -10, 1.5 * 2.0 ** -10])) \
+        == [0x38, 0x3A, 0x7E, 0x7E, 0x7E, 0x7E, 0x80, 0x00, 0x01]
+    # every midpoint between neighbours, random values, against torch
+    mids = ((v[:126] + v[1:127]) / 2).astype(np.float32)
+    gen = torch.Generator().manual_seed(41)
+    rnd = (torch.randn(20000, generator=gen) * torch.exp(torch.randn(20000, generator=gen) * 3))
+    ys = np.concatenate([mids, -mids, rnd.numpy().astype(np.float32)])
+    ys = ys[np.abs(ys) < 464]
+    ref = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc(ys), ref)
+
+
+def pin_fp8_dequantised_attention():
+    gen = torch.Generator().manual_seed(42)
+    B, h, g, T, d = 3, 8, 2, 50, 16
+    q = torch.randn(B, h, d, generator=gen)
+    k = torch.randn(B, g, T, d, generator=gen) * 3
+    v = torch.randn(B, g, T, d, generator=gen) * 2
+    ks = np.array([0.05, 0.2], np.float32)
+    vs = np.array([0.01, 0.5], np.float32)
+    kc = oracle.quantize_fp8(k, ks, 1)
+    vc = oracle.quantize_fp8(v, vs, 1)
+    # the codes are torch's conversion of the float32 quotient (all in range)
+    kq = (k / torch.from_numpy(ks).view(1, g, 1, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(kc, kq.numpy())
+    lens = [50, 7, 1]
+    sc = 0.25
+    o, l = oracle.decode_fp8(q, kc, vc, ks, vs, lens, sc)
+    kd = torch.from_numpy(kc).view(torch.float8_e4m3fn).to(torch.float64) * \
+        torch.from_numpy(ks).double().view(1, g, 1, 1)
+    vd = torch.from_numpy(vc).view(torch.float8_e4m3fn).to(torch.float64) * \
+        torch.from_numpy(vs).double().view(1, g, 1, 1)
+    ro, rl = sdpa_reference(q, kd, vd, lens, sc)
+    assert np.max(np.abs(o - ro)) < 1e-12 and np.max(np.abs(l - rl)) < 1e-12
+    # paged = contiguous; and the append writes the codes of the new token
+    lt = torch.tensor(lens, dtype=torch.int32)
+    table, nb = W.make_block_table(lt, 4, perm_seed=43, extra_blocks=1)
+    kp = W.scatter_to_pool(torch.from_numpy(kc), lt, table, nb, 4).numpy()
+    vp = W.scatter_to_pool(torch.from_numpy(vc), lt, table, nb, 4).numpy()
+    op, lp = oracle.decode_fp8(q, kp, vp, ks, vs, lens, sc, block_table=table, block_size=4)
+    assert np.array_equal(op, o) and np.array_equal(lp, l)
+    kn = torch.randn(B, g, 1, d, generator=gen)
+    k2, v2 = oracle.append_fp8(kn, kn, kc, vc, ks, vs, [6, 0, 1])
+    for b, p in enumerate([6, 0, 1]):
+        assert np.array_equal(k2[b, :, p], oracle.quantize_fp8(kn, ks, 1)[b, :, 0])
+        assert np.array_equal(v2[b, :, p], oracle.quantize_fp8(kn, vs, 1)[b, :, 0])
+    changed = (k2 != kc).any(axis=(1, 3))
+    assert changed.sum() <= B * 1 and not changed[0, 7:].any()
+
+
 ALL_PINS = [
     pin_d1_worked_example,
     pin_sdpa_crosscheck,
@@ -567,4 +632,6 @@ ALL_PINS = [
     pin_ring_cache_equals_linear,
     pin_fork_copy_on_write_isolation,
     pin_beam_gather,
+    pin_fp8_format,
+    pin_fp8_dequantised_attention,
 ]

@@ -210,3 +210,52 @@ def test_planted_block_op_mistake_is_caught(name, monkeypatch):
         except Exception:  # noqa: BLE001 - any failure counts
             failed += 1
     assert failed, f"no block-op pin caught {name}"
+
+
+def _encode_ties_odd(y):
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y).astype(np.float64), 448.0)
+    pos = oracle.e4m3_values()[:127]
+    hi = np.minimum(np.searchsorted(pos, a, side="left"), 126)
+    lo = np.maximum(hi - 1, 0)
+    pick_hi = (pos[hi] - a < a - pos[lo]) | ((pos[hi] - a == a - pos[lo]) & (hi % 2 == 1))
+    code = np.where(pos[hi] == a, hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return (code | (np.signbit(y).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def _encode_no_saturation(y):
+    y = np.asarray(y, dtype=np.float32)
+    code = _ORIG_ENCODE(y)
+    return np.where(np.abs(y) > 448, np.uint8(0x7F) | (code & 0x80), code).astype(np.uint8)
+
+
+_ORIG_ENCODE = oracle.e4m3_encode
+
+
+def _quantize_by_multiply(x, scale, head_axis):
+    xa, xd = oracle._raw(x)
+    xf = (xa.astype(np.uint32) << 16).view(np.float32) if xd == oracle.BF16 else xa
+    sc = np.asarray(scale, dtype=np.float32)
+    shape = [1] * xf.ndim
+    shape[head_axis] = -1
+    return oracle.e4m3_encode((xf * sc.reshape(shape)).astype(np.float32))
+
+
+FP8_MUTATIONS = {
+    "ties_to_odd": ("e4m3_encode", _encode_ties_odd),
+    "no_saturation": ("e4m3_encode", _encode_no_saturation),
+    "scale_multiplies": ("quantize_fp8", _quantize_by_multiply),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
+def test_planted_fp8_mistake_is_caught(name, monkeypatch):
+    attr, fn = FP8_MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    failed = 0
+    for pin in (P.pin_fp8_format, P.pin_fp8_dequantised_attention):
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure counts
+            failed += 1
+    assert failed, f"no fp8 pin caught {name}"
