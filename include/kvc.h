@@ -351,6 +351,57 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
                                              hipStream_t stream);
 
 /*
+ * FP8 caches ([P4] 2.5: FP8 attention; [P3] 14: low-bit K/V halve the
+ * bytes a bandwidth-bound step reads, at a cost in error): kvc_append_fp8,
+ * kvc_decode_attention_fp8[_paged] and kvc_append_decode_attention_fp8[_paged].
+ *
+ *   Caches hold OCP FP8 E4M3 codes, one byte per element, in the layouts of
+ *   the bf16 calls ([B, g, t_cap, d] or pools [NB, g, bs, d]).
+ *   k_scale, v_scale  device float32 [g]: one scale per KV head.
+ *   q, k_new, v_new   bf16, as in the bf16 calls; out, lse float32.
+ *   A new element x (bf16) is stored as the code of the float32 quotient
+ *   x / scale: the nearest E4M3 value, ties to the even code, magnitudes
+ *   above 448 saturating to 448, NaN to S.1111.111, the sign kept.
+ *   Attention is computed over the dequantised values code * scale (codes
+ *   are widened to bf16 exactly; the K scale is folded into the score scale
+ *   and the V scale into the output).
+ * Everything else (validation, splits, workspace from
+ * kvc_decode_workspace_bytes with dtype KVC_BF16, positions, status codes)
+ * is as in the bf16 single-token calls.  The fast kernels cover d = 128;
+ * other head dims take the generic kernel.
+ */
+int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                   int max_blocks, int block_size, const int32_t* seq_lens_before, int B, int g,
+                   int d, int capacity, hipStream_t stream);
+int kvc_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             int B, int h, int g, int d, int t_cap, float scale, int num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             hipStream_t stream);
+int kvc_decode_attention_fp8_paged(const void* q, const void* k_pool, const void* v_pool,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, int max_blocks, int block_size,
+                                   int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                                   int d, float scale, int num_splits, void* workspace,
+                                   size_t workspace_bytes, float* out, float* lse,
+                                   hipStream_t stream);
+int kvc_append_decode_attention_fp8(const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* seq_lens_before, int B,
+                                    int h, int g, int d, int t_cap, float scale, int num_splits,
+                                    void* workspace, size_t workspace_bytes, float* out,
+                                    float* lse, hipStream_t stream);
+int kvc_append_decode_attention_fp8_paged(const void* q, const void* k_new, const void* v_new,
+                                          void* k_pool, void* v_pool, const float* k_scale,
+                                          const float* v_scale, const int32_t* block_table,
+                                          int max_blocks, int block_size, int num_blocks,
+                                          const int32_t* seq_lens_before, int B, int h, int g,
+                                          int d, float scale, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* out, float* lse,
+                                          hipStream_t stream);
+
+/*
  * Block operations for shared and re-ranked caches ([P4] 4.3: requests that
  * share a prompt fork its block table and point at the same physical
  * blocks; before one of them writes into a shared block, the block is copied

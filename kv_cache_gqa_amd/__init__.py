@@ -95,6 +95,21 @@ def load_library():
                                                              vp, ip, ip, ip, ip, ip, ip, fp, ip,
                                                              ip, vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention_window_paged.restype = ip
+    lib.kvc_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ip, ip, vp, ip, ip, ip, ip, vp]
+    lib.kvc_append_fp8.restype = ip
+    lib.kvc_decode_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip, vp,
+                                             sz, vp, vp, vp]
+    lib.kvc_decode_attention_fp8.restype = ip
+    lib.kvc_decode_attention_fp8_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, vp, ip, ip,
+                                                   ip, ip, fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_fp8_paged.restype = ip
+    lib.kvc_append_decode_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, ip,
+                                                    ip, fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_fp8.restype = ip
+    lib.kvc_append_decode_attention_fp8_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, ip,
+                                                          ip, vp, ip, ip, ip, ip, fp, ip, vp, sz,
+                                                          vp, vp, vp]
+    lib.kvc_append_decode_attention_fp8_paged.restype = ip
     lib.kvc_copy_blocks.argtypes = [vp, vp, vp, ip, ip, ip, ip, ip, ip, vp]
     lib.kvc_copy_blocks.restype = ip
     lib.kvc_fork_block_tables.argtypes = [vp, vp, ip, ip, vp, ip, vp, vp, vp]
@@ -495,3 +510,80 @@ def gather_cache(k_src, v_src, seq_lens, parent, k_dst, v_dst, stream=None):
         _dev(seq_lens, "seq_lens", torch.int32), B_src, _dev(parent, "parent", torch.int32), B,
         _dev(k_dst, "k_dst", k_src.dtype), _dev(v_dst, "v_dst", k_src.dtype), g, t_cap, d,
         _dtype_code(k_src), _stream(stream)))
+
+
+def append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, seq_lens_before, block_table=None,
+               stream=None):
+    """Quantise the new token's K/V (bf16 [B,g,d]) into uint8 FP8 E4M3 caches
+    (contiguous [B,g,t_cap,d] or pools [NB,g,bs,d]) with per-KV-head float32
+    scales k_scale, v_scale [g]."""
+    lib = load_library()
+    B, g, d = k_new.shape
+    if block_table is None:
+        capacity, mb, bs, bt = k_cache.shape[2], 0, 0, None
+    else:
+        capacity, bs, mb = k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
+        bt = _dev(block_table, "block_table", torch.int32)
+    _check("kvc_append_fp8", lib.kvc_append_fp8(
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16),
+        _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32), bt, mb,
+        bs, _dev(seq_lens_before, "seq_lens_before", torch.int32), B, g, d, capacity,
+        _stream(stream)))
+
+
+def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table=None,
+               scale: Optional[float] = None, num_splits: int = 0,
+               workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None,
+               k_new=None, v_new=None):
+    """Decode attention (q bf16 [B,h,d]) over uint8 FP8 E4M3 caches with
+    per-KV-head scales.  Without k_new: seq_lens are attended lengths.  With
+    k_new, v_new (bf16 [B,g,d]): seq_lens holds the lengths before the step;
+    the call quantises and appends the new token and attends (one launch).
+    Returns (out [B,h,d] float32, lse [B,h] float32)."""
+    lib = load_library()
+    B, h, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    qp = _dev(q, "q", torch.bfloat16)
+    ks, vs = _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32)
+    sl = _dev(seq_lens, "seq_lens", torch.int32)
+    fused = k_new is not None
+    kn = _dev(k_new, "k_new", torch.bfloat16) if fused else None
+    vn = _dev(v_new, "v_new", torch.bfloat16) if fused else None
+    if block_table is None:
+        _, g, t_cap, _ = k_cache.shape
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, BF16, t_cap, num_splits, 0),
+                             q, workspace)
+        wsp = ws.data_ptr() if ws is not None else None
+        kc, vc = _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8)
+        if fused:
+            st = lib.kvc_append_decode_attention_fp8(qp, kn, vn, kc, vc, ks, vs, sl, B, h, g, d,
+                                                     t_cap, float(scale), num_splits, wsp, wsb,
+                                                     _dev(out, "out"), _dev(lse, "lse"),
+                                                     _stream(stream))
+        else:
+            st = lib.kvc_decode_attention_fp8(qp, kc, vc, ks, vs, sl, B, h, g, d, t_cap,
+                                              float(scale), num_splits, wsp, wsb,
+                                              _dev(out, "out"), _dev(lse, "lse"), _stream(stream))
+    else:
+        nb, g, bs, _ = k_cache.shape
+        mb = block_table.shape[1]
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, BF16, mb * bs, num_splits, 1),
+                             q, workspace)
+        wsp = ws.data_ptr() if ws is not None else None
+        kp, vp = _dev(k_cache, "k_pool", torch.uint8), _dev(v_cache, "v_pool", torch.uint8)
+        bt = _dev(block_table, "block_table", torch.int32)
+        if fused:
+            st = lib.kvc_append_decode_attention_fp8_paged(qp, kn, vn, kp, vp, ks, vs, bt, mb, bs,
+                                                           nb, sl, B, h, g, d, float(scale),
+                                                           num_splits, wsp, wsb, _dev(out, "out"),
+                                                           _dev(lse, "lse"), _stream(stream))
+        else:
+            st = lib.kvc_decode_attention_fp8_paged(qp, kp, vp, ks, vs, bt, mb, bs, nb, sl, B, h, g,
+                                                    d, float(scale), num_splits, wsp, wsb,
+                                                    _dev(out, "out"), _dev(lse, "lse"),
+                                                    _stream(stream))
+    _check("kvc_*decode_attention_fp8", st)
+    return out, lse

@@ -23,6 +23,10 @@ template <>
 __device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, long idx) {
     return __uint_as_float((uint32_t)p[idx] << 16);
 }
+template <>
+__device__ __forceinline__ float load_f<uint8_t>(const uint8_t* p, long idx) {
+    return e4m3_to_f32(p[idx]);  // FP8 E4M3 code
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
     x = row16_sum(x);
@@ -31,7 +35,9 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-template <typename T>
+// TQ: query element type; T: cache element type (uint8_t: FP8 E4M3 codes
+// with a float32 scale per KV head, folded into the query and the output).
+template <typename TQ, typename T>
 __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
@@ -47,14 +53,16 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const int p0 = max(c0, window_lo(a, vis));
     const int p1 = min(min(c0 + a.chunk_len, ur.hi), vis);
 
-    const T* q = (const T*)a.q;
+    const TQ* q = (const TQ*)a.q;
     const T* K = (const T*)a.k;
     const T* V = (const T*)a.v;
+    const float k_sc = a.kv8 ? a.k_scale[j] : 1.0f;
+    const float v_sc = a.kv8 ? a.v_scale[j] : 1.0f;
     float qv[4], acc[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int dim = lane + 64 * kk;
-        qv[kk] = dim < d ? load_f(q, ((long)b * a.h + i) * d + dim) * a.scale_log2e : 0.0f;
+        qv[kk] = dim < d ? load_f(q, ((long)b * a.h + i) * d + dim) * (a.scale_log2e * k_sc) : 0.0f;
         acc[kk] = 0.0f;
     }
     float m = kNegInf, l = 0.0f;
@@ -89,7 +97,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
 
     const long row_out = (long)b * a.h + i;
     if (single) {
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float inv = l > 0.0f ? v_sc / l : 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int dim = lane + 64 * kk;
@@ -98,7 +106,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         if (lane == 0) a.lse[row_out] = l > 0.0f ? (m + fast_log2(l)) * kLn2 : kNegInf;
     } else {
         const long prow = row_out * a.num_chunks + c;
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // l = 0: nothing visible in this chunk
+        const float inv = l > 0.0f ? v_sc / l : 0.0f;  // l = 0: nothing visible in this chunk
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int dim = lane + 64 * kk;
@@ -110,10 +118,12 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s) {
     dim3 grid((unsigned)a.num_chunks, (unsigned)a.h, (unsigned)a.B);
-    if (dtype == 0) {
-        decode_generic_kernel<float><<<grid, dim3(64), 0, s>>>(a);
+    if (a.kv8) {
+        decode_generic_kernel<uint16_t, uint8_t><<<grid, dim3(64), 0, s>>>(a);
+    } else if (dtype == 0) {
+        decode_generic_kernel<float, float><<<grid, dim3(64), 0, s>>>(a);
     } else {
-        decode_generic_kernel<uint16_t><<<grid, dim3(64), 0, s>>>(a);
+        decode_generic_kernel<uint16_t, uint16_t><<<grid, dim3(64), 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -91,10 +91,29 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 #define KVC_MFMA_PREFETCH 1
 #endif
 
+// Registers of one wavefront's 32-position tile.  bf16: K rows as MFMA A
+// operands (chunk ks: dims 32*ks + 8*G .. +8) and V rows 4u + G, dims
+// 8*col .. +8.  FP8: the raw codes, converted to bf16 when the tile is used:
+// K dims 64*hh + 16*G .. +16 per half hh (chunk ks = 2*hh + r takes bytes
+// 8r .. 8r+7), V as for bf16.
+template <bool KV8>
+struct TileRegs {
+    uint4 k[2][4];
+    uint4 v[8];
+};
+template <>
+struct TileRegs<true> {
+    uint4 k[2][2];
+    uint2 v[8];
+};
+
 // GEN: several query tokens per sequence, sliding windows or ring caches
 // (per-row visibility masks, ring-aware windows).  Without it a row sees
 // every position of its segment, which keeps the common path's registers.
-template <int NQT, bool PAGED, int W, bool GEN>
+// KV8: the cache holds FP8 E4M3 codes with a float32 scale per KV head;
+// the codes are converted to bf16 exactly and the head's scales are folded
+// into the score scale (K) and the output (V).
+template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
 struct MfmaEngine {
     using L = Lds<NQT, W>;
     struct Shared {
@@ -114,16 +133,21 @@ struct MfmaEngine {
 
         const uint16_t* K = (const uint16_t*)a.k;
         const uint16_t* Vc = (const uint16_t*)a.v;
+        const unsigned char* K8 = (const unsigned char*)a.k;
+        const unsigned char* V8 = (const unsigned char*)a.v;
         const uint16_t* Q = (const uint16_t*)a.q;
 
-        // B operand of Q K^T: query column 16*qt + col, dims 32*ks + 8*G .. +8.
+        // B operand of Q K^T: query column 16*qt + col; chunk ks holds dims
+        // 32*ks + 8*G .. +8 (bf16) or 64*(ks/2) + 16*G + 8*(ks%2) .. +8 (FP8:
+        // the dims of the lane's K bytes).
         uint4 qb[NQT][4];
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
             const int qi = 16 * qt + col;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                qb[qt][ks] = qi < m ? ld16(Q + (((long)b * a.h + (long)j * a.m + row0 + qi) * kD + 32 * ks + 8 * G))
+                const int dim0 = KV8 ? 64 * (ks >> 1) + 16 * G + 8 * (ks & 1) : 32 * ks + 8 * G;
+                qb[qt][ks] = qi < m ? ld16(Q + (((long)b * a.h + (long)j * a.m + row0 + qi) * kD + dim0))
                                     : make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -145,7 +169,9 @@ struct MfmaEngine {
         unsigned char* vst = sh.lds + wave * kVStageBytes;
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
         long cbase = bj_base;  // row of position 0 in the current window (ring: shifted)
-        const float sl2 = a.scale_log2e;
+        const float k_sc = KV8 ? a.k_scale[j] : 1.0f;  // FP8 head scales
+        const float v_sc = KV8 ? a.v_scale[j] : 1.0f;
+        const float sl2 = a.scale_log2e * k_sc;
         const int* tbl = sh.tbl;
         int blk0 = 0;
         int w1 = e;  // end of the current window
@@ -174,44 +200,78 @@ struct MfmaEngine {
         const int fresh_lo = max(s, raw);
         const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 32 positions
         const int e_cache = has_new ? fresh_lo : e;
-        if (has_new) store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+        if (has_new) {
+            if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+        }
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
 
         // Loads of the 32-position sub-tile at t0; positions are clamped to
         // the window's last one, so a sub-tile past the end stays in bounds.
-        auto load_tile = [&](int t0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
+        auto load_tile = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const long row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
+                if constexpr (KV8) {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16_stream(K + row * kD + 32 * ks + 8 * G);
+                    for (int hh = 0; hh < 2; ++hh) tr.k[tt][hh] = ld16_stream(K8 + row * kD + 64 * hh + 16 * G);
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16_stream(K + row * kD + 32 * ks + 8 * G);
+                }
             }
-            // V rows 4u + G, 16-byte chunk col: four whole rows per instruction.
+            // V rows 4u + G, chunk col: four whole rows per instruction.
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long row = kv_row(min(t0 + 4 * u + G, w1 - 1));
-                vr[u] = ld16_stream(Vc + row * kD + 8 * col);
+                if constexpr (KV8) tr.v[u] = ld8_stream(V8 + row * kD + 8 * col);
+                else tr.v[u] = ld16_stream(Vc + row * kD + 8 * col);
             }
         };
         // The appended tokens' tile at t0 (>= raw): position p is row p - raw
-        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.
-        auto load_new_tile = [&](int t0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
+        // of the unit's k_new / v_new rows (bf16; quantised to codes for an
+        // FP8 cache, so that the tile holds what the cache now holds);
+        // positions clamp to w1 - 1.
+        auto load_new_tile = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
+                if constexpr (KV8) {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16(KN + r * kD + 32 * ks + 8 * G);
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const uint2 c0 = bf16x8_to_e4m3(ld16(KN + r * kD + 64 * hh + 16 * G), k_sc);
+                        const uint2 c1 = bf16x8_to_e4m3(ld16(KN + r * kD + 64 * hh + 16 * G + 8), k_sc);
+                        tr.k[tt][hh] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16(KN + r * kD + 32 * ks + 8 * G);
+                }
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
-                vr[u] = ld16(VN + r * kD + 8 * col);
+                if constexpr (KV8) tr.v[u] = bf16x8_to_e4m3(ld16(VN + r * kD + 8 * col), v_sc);
+                else tr.v[u] = ld16(VN + r * kD + 8 * col);
             }
         };
+        // MFMA A operand of K chunk ks of sub-tile tt.
+        auto k_operand = [&](const TileRegs<KV8>& tr, int tt, int ks) -> uint4 {
+            if constexpr (KV8) {
+                const uint4 c = tr.k[tt][ks >> 1];
+                return e4m3x8_to_bf16((ks & 1) ? make_uint2(c.z, c.w) : make_uint2(c.x, c.y));
+            } else {
+                return tr.k[tt][ks];
+            }
+        };
+        auto v_row = [&](const TileRegs<KV8>& tr, int u) -> uint4 {
+            if constexpr (KV8) return e4m3x8_to_bf16(tr.v[u]);
+            else return tr.v[u];
+        };
 
-        auto compute_tile = [&](int t0, const uint4 (&kr)[2][4], const uint4 (&vr)[8]) {
+        auto compute_tile = [&](int t0, const TileRegs<KV8>& tr) {
             f32x4_t S[NQT][2];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -219,7 +279,7 @@ struct MfmaEngine {
                 for (int tt = 0; tt < 2; ++tt) {
                     f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) s4 = mfma(kr[tt][ks], qb[qt][ks], s4);
+                    for (int ks = 0; ks < 4; ++ks) s4 = mfma(k_operand(tr, tt, ks), qb[qt][ks], s4);
                     S[qt][tt] = s4;
                 }
             }
@@ -227,7 +287,7 @@ struct MfmaEngine {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int r = 4 * u + G;
-                *reinterpret_cast<uint4*>(vst + r * kVRowBytes + ((col ^ vswz(r)) << 4)) = vr[u];
+                *reinterpret_cast<uint4*>(vst + r * kVRowBytes + ((col ^ vswz(r)) << 4)) = v_row(tr, u);
             }
             // Online softmax; P as the B operand of the PV product.
             uint4 pb[NQT];
@@ -314,23 +374,23 @@ struct MfmaEngine {
             const int stride = W * kTileTokens;
             int t0 = w0 + wave * kTileTokens;
 #if KVC_MFMA_PREFETCH
-            uint4 kA[2][4], vA[8], kB[2][4], vB[8];
-            load_tile(t0, kA, vA);
+            TileRegs<KV8> tA, tB;
+            load_tile(t0, tA);
             for (;;) {
                 if (t0 >= w1) break;
-                load_tile(t0 + stride, kB, vB);
-                compute_tile(t0, kA, vA);
+                load_tile(t0 + stride, tB);
+                compute_tile(t0, tA);
                 t0 += stride;
                 if (t0 >= w1) break;
-                load_tile(t0 + stride, kA, vA);
-                compute_tile(t0, kB, vB);
+                load_tile(t0 + stride, tA);
+                compute_tile(t0, tB);
                 t0 += stride;
             }
 #else
             for (; t0 < w1; t0 += stride) {
-                uint4 kr[2][4], vr[8];
-                load_tile(t0, kr, vr);
-                compute_tile(t0, kr, vr);
+                TileRegs<KV8> tr;
+                load_tile(t0, tr);
+                compute_tile(t0, tr);
             }
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
@@ -340,9 +400,9 @@ struct MfmaEngine {
         // turn.
         if (has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
             w1 = e;
-            uint4 kr[2][4], vr[8];
-            load_new_tile(fresh_lo, kr, vr);
-            compute_tile(fresh_lo, kr, vr);
+            TileRegs<KV8> tr;
+            load_new_tile(fresh_lo, tr);
+            compute_tile(fresh_lo, tr);
         }
 
         // lex holds this lane's positions only: sum the four row groups.
@@ -406,7 +466,7 @@ struct MfmaEngine {
                 const float l = lex[qt];
                 const float lr = lacc[qt][0];
                 float* o = dst.o + (long)qi * dst.o_stride;
-                const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+                const float inv = lr > 0.0f ? v_sc / lr : 0.0f;  // FP8: the V head scale
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt)
                     *reinterpret_cast<f32x4_t*>(o + 16 * nt + 4 * G) = acc[qt][nt] * inv;
@@ -430,11 +490,11 @@ struct MfmaEngine {
 template <int NQT>
 struct MfmaOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 2 : 1; };
 
-template <int NQT, bool PAGED, int W, bool GEN>
+template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
-    using E = MfmaEngine<NQT, PAGED, W, GEN>;
+    using E = MfmaEngine<NQT, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, b = blockIdx.z;
     const int j = blockIdx.y / a.slices, row0 = (blockIdx.y - j * a.slices) * 16 * NQT;
@@ -448,11 +508,11 @@ decode_mfma_chunked(DecodeArgs a) {
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c, row0), row0);
 }
 
-template <int NQT, bool PAGED, int W, bool GEN>
+template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT>::kWavesPerEu)))
 decode_mfma_stream(DecodeArgs a) {
-    using E = MfmaEngine<NQT, PAGED, W, GEN>;
+    using E = MfmaEngine<NQT, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
     stream_prefix(a, cum);
@@ -463,29 +523,36 @@ decode_mfma_stream(DecodeArgs a) {
 }
 
 template <int NQT, bool PG, int WV>
-static const void* mfma_pick(bool stream, bool gen) {
+static const void* mfma_pick(bool stream, bool gen, bool kv8) {
+    if (kv8)  // FP8 caches: single-token calls only
+        return gen ? nullptr
+                   : stream ? (const void*)decode_mfma_stream<NQT, PG, WV, false, true>
+                            : (const void*)decode_mfma_chunked<NQT, PG, WV, false, true>;
     if (stream)
-        return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true>
-                   : (const void*)decode_mfma_stream<NQT, PG, WV, false>;
-    return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true>
-               : (const void*)decode_mfma_chunked<NQT, PG, WV, false>;
+        return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true, false>
+                   : (const void*)decode_mfma_stream<NQT, PG, WV, false, false>;
+    return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true, false>
+               : (const void*)decode_mfma_chunked<NQT, PG, WV, false, false>;
 }
 
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
-// general features); nullptr when that combination is not built.  Every
-// (m, layout, mode) has a 4-wavefront kernel; one tile of query rows
+// general features, FP8 cache); nullptr when that combination is not built.
+// Every (m, layout, mode) has a 4-wavefront kernel; one tile of query rows
 // (m <= 16) on a contiguous cache also has an 8-wavefront chunked kernel,
 // for whole-unit work-groups.  (Two tiles need more registers than 8
-// wavefronts per work-group leave.)
-const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen) {
+// wavefronts per work-group leave.)  FP8 caches have the kernels without the
+// general features.
+const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
     const bool two = m > 16;
     if (waves == 4) {
-        if (two) return paged ? mfma_pick<2, true, 4>(stream, gen) : mfma_pick<2, false, 4>(stream, gen);
-        return paged ? mfma_pick<1, true, 4>(stream, gen) : mfma_pick<1, false, 4>(stream, gen);
+        if (two) return paged ? mfma_pick<2, true, 4>(stream, gen, kv8) : mfma_pick<2, false, 4>(stream, gen, kv8);
+        return paged ? mfma_pick<1, true, 4>(stream, gen, kv8) : mfma_pick<1, false, 4>(stream, gen, kv8);
     }
-    if (waves == 8 && !two && !paged && !stream)
-        return gen ? (const void*)decode_mfma_chunked<1, false, 8, true>
-                   : (const void*)decode_mfma_chunked<1, false, 8, false>;
+    if (waves == 8 && !two && !paged && !stream) {
+        if (kv8) return gen ? nullptr : (const void*)decode_mfma_chunked<1, false, 8, false, true>;
+        return gen ? (const void*)decode_mfma_chunked<1, false, 8, true, false>
+                   : (const void*)decode_mfma_chunked<1, false, 8, false, false>;
+    }
     return nullptr;
 }
 
@@ -494,7 +561,7 @@ hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
     if (a.slices < 1 || (a.m > 32 * a.slices) || (a.slices > 1 && (a.stream || a.m <= 32)))
         return hipErrorInvalidValue;
     const void* fn = mfma_kernel(min(a.m, 32), a.block_table != nullptr, a.stream != 0, a.waves,
-                                 general_features(a));
+                                 general_features(a), a.kv8 != 0);
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
                                : dim3((unsigned)a.num_chunks, (unsigned)(a.g * a.slices),

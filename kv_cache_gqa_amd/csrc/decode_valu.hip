@@ -34,7 +34,22 @@ constexpr int kD = 128;
 
 // GEN: several query tokens per sequence, sliding windows or ring caches
 // (per-row visibility masks, ring-aware windows).
-template <int M, bool PAGED, int W, bool GEN>
+// Registers of one wavefront's tile: rows 4u + lane/16, dims 8*(lane%16)
+// .. +8, as bf16 or (FP8 cache) as raw codes converted when used.
+template <bool KV8>
+struct ValuTile {
+    uint4 k[8];
+    uint4 v[8];
+};
+template <>
+struct ValuTile<true> {
+    uint2 k[8];
+    uint2 v[8];
+};
+
+// KV8: the cache holds FP8 E4M3 codes with a float32 scale per KV head,
+// folded into the score scale (K) and the output (V).
+template <int M, bool PAGED, int W, bool GEN, bool KV8>
 struct ValuEngine {
     struct Shared {
         int tbl[PAGED ? kMaxTableSlice : 1];
@@ -71,7 +86,9 @@ struct ValuEngine {
         }
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
         long cbase = bj_base;  // row of position 0 in the current window (ring: shifted)
-        const float sl2 = a.scale_log2e;
+        const float k_sc = KV8 ? a.k_scale[j] : 1.0f;  // FP8 head scales
+        const float v_sc = KV8 ? a.v_scale[j] : 1.0f;
+        const float sl2 = a.scale_log2e * k_sc;
         const int* tbl = sh.tbl;
         int blk0 = 0;
         int w1 = e;
@@ -98,41 +115,60 @@ struct ValuEngine {
         const int fresh_lo = max(s, raw);
         const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 3 positions
         const int e_cache = has_new ? fresh_lo : e;
-        if (has_new) store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+        if (has_new) {
+            if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+        }
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
 
         // Positions clamped to the window's last one (in bounds past the end).
-        auto load_tile = [&](int t0, uint4 (&kv)[8], uint4 (&vv)[8]) {
+        auto load_tile = [&](int t0, ValuTile<KV8>& tr) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long row = kv_row(min(t0 + 4 * u + tsub, w1 - 1));
-                kv[u] = ld16_stream(K + row * kD + 8 * ds);
-                vv[u] = ld16_stream(Vc + row * kD + 8 * ds);
+                if constexpr (KV8) {
+                    tr.k[u] = ld8_stream((const unsigned char*)a.k + row * kD + 8 * ds);
+                    tr.v[u] = ld8_stream((const unsigned char*)a.v + row * kD + 8 * ds);
+                } else {
+                    tr.k[u] = ld16_stream(K + row * kD + 8 * ds);
+                    tr.v[u] = ld16_stream(Vc + row * kD + 8 * ds);
+                }
             }
         };
         // The appended tokens' tile at t0 (>= raw): position p is row p - raw
-        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.
-        auto load_new_tile = [&](int t0, uint4 (&kv)[8], uint4 (&vv)[8]) {
+        // of the unit's k_new / v_new rows (bf16; quantised to codes for an
+        // FP8 cache); positions clamp to w1 - 1.
+        auto load_new_tile = [&](int t0, ValuTile<KV8>& tr) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
-                kv[u] = ld16(KN + r * kD + 8 * ds);
-                vv[u] = ld16(VN + r * kD + 8 * ds);
+                if constexpr (KV8) {
+                    tr.k[u] = bf16x8_to_e4m3(ld16(KN + r * kD + 8 * ds), k_sc);
+                    tr.v[u] = bf16x8_to_e4m3(ld16(VN + r * kD + 8 * ds), v_sc);
+                } else {
+                    tr.k[u] = ld16(KN + r * kD + 8 * ds);
+                    tr.v[u] = ld16(VN + r * kD + 8 * ds);
+                }
             }
         };
-        auto compute_tile = [&](int t0, const uint4 (&kv)[8], const uint4 (&vv)[8]) {
+        auto as_bf16 = [&](const auto& x) -> uint4 {
+            if constexpr (KV8) return e4m3x8_to_bf16(x);
+            else return x;
+        };
+        auto compute_tile = [&](int t0, const ValuTile<KV8>& tr) {
             float sc[M][8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int p = t0 + 4 * u + tsub;
+                const uint4 kb = as_bf16(tr.k[u]);
 #pragma unroll
                 for (int r = 0; r < M; ++r) {
-                    float dot = dot2_bf16(qp[r][0], kv[u].x, 0.0f);
-                    dot = dot2_bf16(qp[r][1], kv[u].y, dot);
-                    dot = dot2_bf16(qp[r][2], kv[u].z, dot);
-                    dot = dot2_bf16(qp[r][3], kv[u].w, dot);
+                    float dot = dot2_bf16(qp[r][0], kb.x, 0.0f);
+                    dot = dot2_bf16(qp[r][1], kb.y, dot);
+                    dot = dot2_bf16(qp[r][2], kb.z, dot);
+                    dot = dot2_bf16(qp[r][3], kb.w, dot);
                     dot = row16_sum(dot) * sl2;
                     const bool vis = GEN ? (p < w1 && (unsigned)(lim[r] - 1 - p) < wlen) : p < w1;
                     sc[r][u] = vis ? dot : kNegInf;
@@ -160,9 +196,9 @@ struct ValuEngine {
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float vf[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y),
-                                     bf16_hi(vv[u].y), bf16_lo(vv[u].z), bf16_hi(vv[u].z),
-                                     bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
+                const uint4 vb = as_bf16(tr.v[u]);
+                const float vf[8] = {bf16_lo(vb.x), bf16_hi(vb.x), bf16_lo(vb.y), bf16_hi(vb.y),
+                                     bf16_lo(vb.z), bf16_hi(vb.z), bf16_lo(vb.w), bf16_hi(vb.w)};
 #pragma unroll
                 for (int r = 0; r < M; ++r) {
 #pragma unroll
@@ -192,23 +228,23 @@ struct ValuEngine {
             const int stride = W * kTileTokens;
             int t0 = w0 + wave * kTileTokens;
 #if KVC_VALU_PREFETCH
-            uint4 kA[8], vA[8], kB[8], vB[8];
-            load_tile(t0, kA, vA);
+            ValuTile<KV8> tA, tB;
+            load_tile(t0, tA);
             for (;;) {
                 if (t0 >= w1) break;
-                load_tile(t0 + stride, kB, vB);
-                compute_tile(t0, kA, vA);
+                load_tile(t0 + stride, tB);
+                compute_tile(t0, tA);
                 t0 += stride;
                 if (t0 >= w1) break;
-                load_tile(t0 + stride, kA, vA);
-                compute_tile(t0, kB, vB);
+                load_tile(t0 + stride, tA);
+                compute_tile(t0, tB);
                 t0 += stride;
             }
 #else
             for (; t0 < w1; t0 += stride) {
-                uint4 kv[8], vv[8];
-                load_tile(t0, kv, vv);
-                compute_tile(t0, kv, vv);
+                ValuTile<KV8> tr;
+                load_tile(t0, tr);
+                compute_tile(t0, tr);
             }
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
@@ -218,9 +254,9 @@ struct ValuEngine {
         // turn.
         if (has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
             w1 = e;
-            uint4 kv[8], vv[8];
-            load_new_tile(fresh_lo, kv, vv);
-            compute_tile(fresh_lo, kv, vv);
+            ValuTile<KV8> tr;
+            load_new_tile(fresh_lo, tr);
+            compute_tile(fresh_lo, tr);
         }
 
         // Merge the four rows of 16 lanes (positions interleaved by lane/16).
@@ -268,7 +304,7 @@ struct ValuEngine {
                 l += sh.red_l[w][r] * f;
                 o += sh.red_o[w][r][dim] * f;
             }
-            dst.o[(long)r * dst.o_stride + dim] = l > 0.0f ? o / l : 0.0f;
+            dst.o[(long)r * dst.o_stride + dim] = l > 0.0f ? o * v_sc / l : 0.0f;  // FP8: V head scale
             if (dim == 0) {
                 float v;
                 if (dst.final_) v = l > 0.0f ? (mm + fast_log2(l)) * kLn2 : kNegInf;
@@ -281,9 +317,9 @@ struct ValuEngine {
 
 }  // namespace
 
-template <int M, bool PAGED, int W, bool GEN>
+template <int M, bool PAGED, int W, bool GEN, bool KV8>
 __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
-    using E = ValuEngine<M, PAGED, W, GEN>;
+    using E = ValuEngine<M, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     // chunks cover [lo, hi); without the general features lo = 0
@@ -296,9 +332,9 @@ __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
 }
 
-template <int M, bool PAGED, int W, bool GEN>
+template <int M, bool PAGED, int W, bool GEN, bool KV8>
 __global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
-    using E = ValuEngine<M, PAGED, W, GEN>;
+    using E = ValuEngine<M, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
     __shared__ long long cum[kStreamMaxB + 1];
     stream_prefix(a, cum);
@@ -309,32 +345,36 @@ __global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
 }
 
 template <int M, bool PG>
-static const void* valu_pick(bool stream, bool gen) {
+static const void* valu_pick(bool stream, bool gen, bool kv8) {
+    if (kv8)  // FP8 caches: single-token calls only
+        return gen ? nullptr
+                   : stream ? (const void*)decode_valu_stream<M, PG, 4, false, true>
+                            : (const void*)decode_valu_chunked<M, PG, 4, false, true>;
     if (stream)
-        return gen ? (const void*)decode_valu_stream<M, PG, 4, true>
-                   : (const void*)decode_valu_stream<M, PG, 4, false>;
-    return gen ? (const void*)decode_valu_chunked<M, PG, 4, true>
-               : (const void*)decode_valu_chunked<M, PG, 4, false>;
+        return gen ? (const void*)decode_valu_stream<M, PG, 4, true, false>
+                   : (const void*)decode_valu_stream<M, PG, 4, false, false>;
+    return gen ? (const void*)decode_valu_chunked<M, PG, 4, true, false>
+               : (const void*)decode_valu_chunked<M, PG, 4, false, false>;
 }
 
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
-// general features); nullptr when that combination is not built.  Only
-// 4-wavefront kernels: one wide work-group per (sequence, KV head) measured
-// slower than split chunks plus a merge for these kernels (8 and 16
+// general features, FP8 cache); nullptr when that combination is not built.
+// Only 4-wavefront kernels: one wide work-group per (sequence, KV head)
+// measured slower than split chunks plus a merge for these kernels (8 and 16
 // wavefronts, m = 1).
-const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen) {
+const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
     if (waves != 4) return nullptr;
     switch (m) {
-        case 1: return paged ? valu_pick<1, true>(stream, gen) : valu_pick<1, false>(stream, gen);
-        case 2: return paged ? valu_pick<2, true>(stream, gen) : valu_pick<2, false>(stream, gen);
-        case 3: return paged ? valu_pick<3, true>(stream, gen) : valu_pick<3, false>(stream, gen);
+        case 1: return paged ? valu_pick<1, true>(stream, gen, kv8) : valu_pick<1, false>(stream, gen, kv8);
+        case 2: return paged ? valu_pick<2, true>(stream, gen, kv8) : valu_pick<2, false>(stream, gen, kv8);
+        case 3: return paged ? valu_pick<3, true>(stream, gen, kv8) : valu_pick<3, false>(stream, gen, kv8);
         default: return nullptr;
     }
 }
 
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s) {
     const void* fn = valu_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves,
-                                 general_features(a));
+                                 general_features(a), a.kv8 != 0);
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
                                : dim3((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);

@@ -178,9 +178,10 @@ static long device_slots(const void* fn, int waves) {
     return (long)cus * per_cu;
 }
 
-static const void* kernel_for(KernelKind kind, int m, bool paged, bool stream, int waves, bool gen) {
-    return kind == kMfma ? mfma_kernel(m, paged, stream, waves, gen)
-                         : valu_kernel(m, paged, stream, waves, gen);
+static const void* kernel_for(KernelKind kind, int m, bool paged, bool stream, int waves, bool gen,
+                              bool kv8) {
+    return kind == kMfma ? mfma_kernel(m, paged, stream, waves, gen, kv8)
+                         : valu_kernel(m, paged, stream, waves, gen, kv8);
 }
 
 // Fraction of the slot-rounds a grid of `wgs` equal work-groups keeps busy.
@@ -202,14 +203,14 @@ struct AutoShape {
 };
 
 static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, bool paged,
-                            bool gen) {
+                            bool gen, bool kv8) {
     const long units = (long)B * g;
-    const void* f4 = kernel_for(kind, m, paged, false, 4, gen);
+    const void* f4 = kernel_for(kind, m, paged, false, 4, gen, kv8);
     const long slots4 = device_slots(f4, 4);
     AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};
 #if KVC_AUTO_WIDE
     const int wv = 8;
-    const void* fn = kernel_for(kind, m, paged, false, wv, gen);
+    const void* fn = kernel_for(kind, m, paged, false, wv, gen, kv8);
     const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
     if (slots > 0 && units >= slots && slots * wv >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
         return AutoShape{wv, 1};
@@ -244,14 +245,14 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     a.waves = sc.kind == kGeneric ? 1 : 4;
     a.slices = row_slices(sc.kind, a.m);
     if (sc.stream) {
-        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4, general_features(a)), 4);
+        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4, general_features(a), a.kv8 != 0), 4);
         // No more work-groups than 256-position pieces of the largest possible batch.
         const long pieces = ((long)a.B * a.g * max_len + 255) / 256;
         if (P > pieces) P = pieces;
         a.num_wgs = (int)(P < 1 ? 1 : P);
     } else if (sc.auto_chunks) {
         const AutoShape sh = auto_shape(sc.kind, a.m < 32 ? a.m : 32, a.B * a.slices, a.g, max_len,
-                                        paged, general_features(a));
+                                        paged, general_features(a), a.kv8 != 0);
         a.waves = sh.waves;
         // One chunk per unit may exceed kMaxChunk: the engines walk a chunk in
         // windows of at most kMaxChunk positions.
@@ -274,10 +275,16 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
         // The generic kernel does not take the new token itself: append it
         // first, then attend over the cache.
         const int eb = dtype == KVC_F32 ? 4 : 2;
-        if (launch_append(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
-                          a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g, a.n,
-                          a.d, paged ? a.num_blocks : a.t_cap, a.ring, eb, stream) != hipSuccess)
-            return KVC_ERR_HIP;
+        const int capacity = paged ? a.num_blocks : a.t_cap;
+        const hipError_t e =
+            a.kv8 ? launch_append_fp8(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
+                                      a.k_scale, a.v_scale, a.block_table, a.max_blocks,
+                                      a.block_size, a.seq_lens, a.B, a.g, a.n, a.d, capacity,
+                                      a.ring, stream)
+                  : launch_append(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
+                                  a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g,
+                                  a.n, a.d, capacity, a.ring, eb, stream);
+        if (e != hipSuccess) return KVC_ERR_HIP;
         a.k_new = nullptr;
         a.v_new = nullptr;
     }
@@ -400,7 +407,8 @@ static int decode_contiguous(const void* q, const void* k_new, const void* v_new
                              const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                              int B, int h, int g, int d, int n, int t_cap, int window, int ring,
                              float scale, int dtype, int num_splits, void* workspace,
-                             size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+                             size_t workspace_bytes, float* out, float* lse, hipStream_t stream,
+                             const float* k_scale = nullptr, const float* v_scale = nullptr) {
     int st = check_common(q, k_cache, v_cache, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
@@ -414,6 +422,7 @@ static int decode_contiguous(const void* q, const void* k_new, const void* v_new
     a.B = B; a.h = h * n; a.g = g; a.d = d; a.m = (h / g) * n; a.n = n;
     a.t_cap = t_cap; a.cap_len = ring ? 0x7fffffff : t_cap;
     a.window = window; a.ring = ring ? 1 : 0;
+    a.kv8 = k_scale != nullptr ? 1 : 0; a.k_scale = k_scale; a.v_scale = v_scale;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
     a.len_add = k_new != nullptr ? n : 0;
@@ -427,7 +436,8 @@ static int decode_paged(const void* q, const void* k_new, const void* v_new, con
                         int block_size, int num_blocks, const int32_t* seq_lens, int B, int h,
                         int g, int d, int n, int window, float scale, int dtype, int num_splits,
                         void* workspace, size_t workspace_bytes, float* out, float* lse,
-                        hipStream_t stream) {
+                        hipStream_t stream, const float* k_scale = nullptr,
+                        const float* v_scale = nullptr) {
     int st = check_common(q, k_pool, v_pool, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
@@ -445,6 +455,7 @@ static int decode_paged(const void* q, const void* k_new, const void* v_new, con
     a.B = B; a.h = h * n; a.g = g; a.d = d; a.m = (h / g) * n; a.n = n;
     a.t_cap = 0; a.cap_len = (int)cap;
     a.window = window; a.ring = 0;
+    a.kv8 = k_scale != nullptr ? 1 : 0; a.k_scale = k_scale; a.v_scale = v_scale;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
     a.len_add = k_new != nullptr ? n : 0;
@@ -635,6 +646,74 @@ int kvc_gather_cache(const void* k_src, const void* v_src, const int32_t* seq_le
                             row_bytes, stream) != hipSuccess)
         return KVC_ERR_HIP;
     return KVC_OK;
+}
+
+int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                   int max_blocks, int block_size, const int32_t* seq_lens_before, int B, int g,
+                   int d, int capacity, hipStream_t stream) {
+    if (B < 0 || g <= 0 || d <= 0 || capacity <= 0) return KVC_ERR_INVALID;
+    if (B == 0) return KVC_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !seq_lens_before)
+        return KVC_ERR_INVALID;
+    if (block_table != nullptr && (max_blocks <= 0 || block_size <= 0)) return KVC_ERR_INVALID;
+    if (launch_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                          max_blocks, block_size, seq_lens_before, B, g, 1, d, capacity, 0,
+                          stream) != hipSuccess)
+        return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
+int kvc_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             int B, int h, int g, int d, int t_cap, float scale, int num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             hipStream_t stream) {
+    if (B > 0 && (!k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, 1, t_cap,
+                             0, 0, scale, KVC_BF16, num_splits, workspace, workspace_bytes, out,
+                             lse, stream, k_scale, v_scale);
+}
+
+int kvc_decode_attention_fp8_paged(const void* q, const void* k_pool, const void* v_pool,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, int max_blocks, int block_size,
+                                   int num_blocks, const int32_t* seq_lens, int B, int h, int g,
+                                   int d, float scale, int num_splits, void* workspace,
+                                   size_t workspace_bytes, float* out, float* lse,
+                                   hipStream_t stream) {
+    if (B > 0 && (!k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
+                        num_blocks, seq_lens, B, h, g, d, 1, 0, scale, KVC_BF16, num_splits,
+                        workspace, workspace_bytes, out, lse, stream, k_scale, v_scale);
+}
+
+int kvc_append_decode_attention_fp8(const void* q, const void* k_new, const void* v_new,
+                                    void* k_cache, void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* seq_lens_before, int B,
+                                    int h, int g, int d, int t_cap, float scale, int num_splits,
+                                    void* workspace, size_t workspace_bytes, float* out,
+                                    float* lse, hipStream_t stream) {
+    if (B > 0 && (!k_new || !v_new || !k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
+                             seq_lens_before, B, h, g, d, 1, t_cap, 0, 0, scale, KVC_BF16,
+                             num_splits, workspace, workspace_bytes, out, lse, stream, k_scale,
+                             v_scale);
+}
+
+int kvc_append_decode_attention_fp8_paged(const void* q, const void* k_new, const void* v_new,
+                                          void* k_pool, void* v_pool, const float* k_scale,
+                                          const float* v_scale, const int32_t* block_table,
+                                          int max_blocks, int block_size, int num_blocks,
+                                          const int32_t* seq_lens_before, int B, int h, int g,
+                                          int d, float scale, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* out, float* lse,
+                                          hipStream_t stream) {
+    if (B > 0 && (!k_new || !v_new || !k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, 1, 0,
+                        scale, KVC_BF16, num_splits, workspace, workspace_bytes, out, lse, stream,
+                        k_scale, v_scale);
 }
 
 }  // extern "C"

@@ -75,6 +75,73 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// 8-byte streaming load (global_load_dwordx2 ... nt).
+__device__ __forceinline__ uint2 ld8_stream(const void* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint2 ld8(const void* p) {
+    return *reinterpret_cast<const uint2*>(p);
+}
+
+// ---- OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// no infinities, S.1111.111 = NaN, largest finite 448) ----
+
+// Two codes (bytes 0-1 of w, or 2-3 when hi) as two bf16 in one 32-bit
+// word, low half first.  Exact: every E4M3 value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    const auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight codes (bytes of c, in order) as eight bf16.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
+    return make_uint4(e4m3x2_to_bf16x2<false>(c.x), e4m3x2_to_bf16x2<true>(c.x),
+                      e4m3x2_to_bf16x2<false>(c.y), e4m3x2_to_bf16x2<true>(c.y));
+}
+
+// One code as float.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false)[0];
+}
+
+// Code of a float: the nearest E4M3 value with ties to the even code,
+// magnitudes above 448 saturating to 448, NaN to S.1111.111, the sign kept
+// (also for values that round to zero).  Below 2^-6 the values are the
+// multiples of 2^-9, so the code is rint(|y| * 512) (exact scaling, ties to
+// even); above, the float's mantissa is rounded to 3 bits at bit 20 (ties
+// to even) and its exponent rebased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a != a) return sign | 0x7Fu;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+    uint32_t ua = __float_as_uint(a);
+    ua += 0x7FFFFu + ((ua >> 20) & 1u);
+    const uint32_t code = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Codes of 8 bf16 (uint4) divided by `scale` (the quotient in float32).
+__device__ __forceinline__ uint2 bf16x8_to_e4m3(uint4 x, float scale) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(w[i] << 16) / scale;
+        const float hi = __uint_as_float(w[i] & 0xFFFF0000u) / scale;
+        const uint32_t pair = e4m3_encode(lo) | (e4m3_encode(hi) << 8);
+        out[i >> 1] |= pair << (16 * (i & 1));
+    }
+    return make_uint2(out[0], out[1]);
+}
+
 // Merge two online-softmax states (m2, l, acc) in base 2.  -inf maxima
 // (no positions seen) are handled so that no (-inf) - (-inf) is formed.
 __device__ __forceinline__ void rescale_pair(float ma, float mb, float& fa, float& fb, float& mnew) {
@@ -179,6 +246,38 @@ __device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, in
                            (unit * a.n + (p - raw)) * 16 + c;
         uint4* dst = reinterpret_cast<uint4*>(const_cast<void*>(is_v ? a.v : a.k)) + row * 16 + c;
         *dst = *src;
+    }
+}
+
+// FP8 cache, d = 128: quantise the appended tokens at positions [lo, hi) of
+// unit (b, j) (bf16 rows of k_new / v_new, position p = row p - raw) and
+// write their codes into their cache slots.  Each of the `nthreads` threads
+// writes 16 codes at a time (16 pieces per position: 8 of K, 8 of V).
+// Paged: positions whose block-table entry is not a valid block are skipped.
+__device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int b, int j, int raw,
+                                                        int lo, int hi, int tid, int nthreads) {
+    const long unit = (long)b * a.g + j;
+    for (int idx = tid; idx < (hi - lo) * 16; idx += nthreads) {
+        const int p = lo + (idx >> 4);
+        const int part = idx & 15;
+        long row;
+        if (a.block_table != nullptr) {
+            const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+            if (phys < 0 || phys >= a.num_blocks) continue;
+            row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+        } else {
+            row = unit * a.t_cap + cache_slot(a, p);
+        }
+        const bool is_v = part >= 8;
+        const int c = part & 7;
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(is_v ? a.v_new : a.k_new) +
+                              (unit * a.n + (p - raw)) * 128 + 16 * c;
+        const float sc = is_v ? a.v_scale[j] : a.k_scale[j];
+        const uint2 c0 = bf16x8_to_e4m3(ld16(src), sc);
+        const uint2 c1 = bf16x8_to_e4m3(ld16(src + 8), sc);
+        unsigned char* dst = reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? a.v : a.k)) +
+                             row * 128 + 16 * c;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(c0.x, c0.y, c1.x, c1.y);
     }
 }
 

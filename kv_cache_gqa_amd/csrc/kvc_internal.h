@@ -77,6 +77,10 @@ struct DecodeArgs {
     // slot p mod t_cap (positions are not clamped to the capacity).
     int window;
     int ring;
+    // FP8 E4M3 cache (q, k_new, v_new stay bf16): per-KV-head float32 scales.
+    int kv8;
+    const float* k_scale;
+    const float* v_scale;
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
     // Stream mode: records [num_wgs][2][m][d] and [num_wgs][2][m].
     float* part_o;
@@ -92,10 +96,10 @@ hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
-// general features), for launches and occupancy queries; nullptr when that
-// combination is not built.  MFMA: waves in {4, 8}; VALU: 4.
-const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen);
-const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen);
+// general features, FP8 cache), for launches and occupancy queries; nullptr
+// when that combination is not built.  MFMA: waves in {4, 8}; VALU: 4.
+const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8);
+const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }
@@ -107,6 +111,11 @@ hipError_t launch_fork_tables(const int32_t* tables, const int32_t* lens, int B_
 hipError_t launch_gather_cache(const void* k_src, const void* v_src, void* k_dst, void* v_dst,
                                const int32_t* lens, int B_src, const int32_t* parent, int B, int g,
                                int t_cap, long row_bytes, hipStream_t s);
+hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int max_blocks, int block_size,
+                             const int32_t* seq_lens_before, int B, int g, int n, int d,
+                             int capacity, int ring, hipStream_t s);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,

@@ -248,3 +248,49 @@ def test_block_op_validation_codes():
     assert gc(FAKE, FAKE, FAKE, 2, FAKE, 2, other, other, 2, 64, 128, 1, None) == INVALID  # aliasing
     assert gc(FAKE, other, FAKE, 2, FAKE, 2, FAKE, other, 2, 64, 128, 1, None) == INVALID
     assert gc(FAKE, FAKE, FAKE, 2, FAKE, 2, other, other, 2, 0, 128, 1, None) == INVALID   # t_cap = 0
+
+
+def test_fp8_validation_codes():
+    lib = kvc.load_library()
+    # every call below fails validation (or has nothing to do) before any HIP call
+    ap = lib.kvc_append_fp8
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 2, 2, 128, 64, None]
+    bad = list(args); bad[4] = None                  # k_scale missing
+    assert ap(*bad) == INVALID
+    bad = list(args); bad[5] = None                  # v_scale missing
+    assert ap(*bad) == INVALID
+    bad = list(args); bad[13] = 0                    # no capacity
+    assert ap(*bad) == INVALID
+    bad = list(args); bad[6] = FAKE                  # table without max_blocks / block_size
+    assert ap(*bad) == INVALID
+    ok = list(args); ok[10] = 0                      # B = 0: nothing to do
+    assert ap(*ok) == OK
+    dc = lib.kvc_decode_attention_fp8
+    dargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, None, 0, FAKE, FAKE,
+             None]
+    bad = list(dargs); bad[3] = None
+    assert dc(*bad) == INVALID
+    bad = list(dargs); bad[7] = 7                    # h not a multiple of g
+    assert dc(*bad) == INVALID
+    bad = list(dargs); bad[12] = 2                   # a split plan needs a workspace
+    bad[10] = 4096
+    assert dc(*bad) == WORKSPACE
+    dp = lib.kvc_decode_attention_fp8_paged
+    pargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 0.1, 1, None, 0,
+             FAKE, FAKE, None]
+    bad = list(pargs); bad[4] = None
+    assert dp(*bad) == INVALID
+    bad = list(pargs); bad[7] = 0                    # block size 0
+    assert dp(*bad) == INVALID
+    fc = lib.kvc_append_decode_attention_fp8
+    fargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, None, 0,
+             FAKE, FAKE, None]
+    for i in (1, 2, 5, 6):                           # k_new, v_new, k_scale, v_scale
+        bad = list(fargs); bad[i] = None
+        assert fc(*bad) == INVALID
+    fpp = lib.kvc_append_decode_attention_fp8_paged
+    fpargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 0.1,
+              1, None, 0, FAKE, FAKE, None]
+    for i in (1, 2, 5, 6):
+        bad = list(fpargs); bad[i] = None
+        assert fpp(*bad) == INVALID
