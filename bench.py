@@ -6,7 +6,8 @@ is already resident in HBM: one kvc_append_decode_attention[_paged] call
 (the new token's K/V into the cache, GQA head map, scores, online softmax,
 PV, and the log-sum-exp merge of split partials when the plan splits).
 --separate times kvc_append followed by kvc_decode_attention[_paged]
-instead.
+instead.  --kv-fp8 keeps the cache as FP8 E4M3 codes with per-KV-head
+scales (kvc_append_decode_attention_fp8[_paged]).
 
 Metric: decode tokens/s = B / step time (one new token per sequence), with
 the achieved HBM bandwidth of the decode kernel against the 8 TB/s peak.
@@ -49,6 +50,8 @@ def kernel_source_hash() -> str:
 
 
 def traffic_file(workload: str) -> str:
+    """Stored counter figure of a workload; an FP8-cache run of workload X is
+    stored under the key X + "_kvfp8"."""
     return os.path.join(PROFILES, f"decode_{workload}_hbm_traffic.txt")
 
 
@@ -128,35 +131,46 @@ def stored_traffic(workload: str):
     return int(kv["traffic_bytes_per_call"])
 
 
-def algorithmic_bytes(w, attended, nblocks=None, n=1):
+def algorithmic_bytes(w, attended, nblocks=None, n=1, kv_bytes=None):
     """Bytes one step must move: KV read (``attended`` positions per
     sequence: all of them, or those a sliding window keeps), q read, out and
     lse written (float32), the appended K/V written, and the block table read
-    (paged).  n new tokens (queries) per sequence."""
+    (paged).  n new tokens (queries) per sequence.  kv_bytes: bytes per
+    cached element when the cache is stored narrower than the inputs (1 for
+    FP8 codes, whose per-KV-head scales are read too)."""
     B, h, g, d, eb = w.B, w.h, w.g, w.d, w.elem_bytes
-    kv_read = 2 * int(attended.sum()) * g * d * eb
+    cb = eb if kv_bytes is None else kv_bytes
+    kv_read = 2 * int(attended.sum()) * g * d * cb
     q_read = B * h * n * d * eb
     out_write = B * h * n * d * 4 + B * h * n * 4
-    append_write = 2 * B * g * n * d * eb
+    append_write = 2 * B * g * n * d * cb
     append_read = 2 * B * g * n * d * eb
     table = 0 if nblocks is None else int(nblocks.sum()) * 4
-    decode = kv_read + q_read + out_write + table + B * 4
-    # One-call step: the new token's K/V are read once (from k_new / v_new,
-    # counted in kv_read) and written once into the cache.
-    return dict(decode=decode, step=decode + append_write + append_read + B * 4,
-                fused=decode + append_write, kv_read=kv_read)
+    scales = 0 if kv_bytes is None else 2 * g * 4
+    decode = kv_read + q_read + out_write + table + B * 4 + scales
+    # One-call step: the new token's K/V are read once, from k_new / v_new
+    # (counted in kv_read at the cache's width, so the difference to the
+    # inputs' width is added), and written once into the cache.
+    new_read = 2 * B * g * n * d * (eb - cb)
+    return dict(decode=decode, step=decode + append_write + append_read + B * 4 + scales,
+                fused=decode + new_read + append_write, kv_read=kv_read)
 
 
-def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0):
+def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0, fp8=None):
     """The oracle (plain C, fp64, OpenMP over (sequence, head) rows) timed on
     this host on the same inputs.  Runs whole batches until about budget_s
-    seconds have passed (at least one), reports decode tokens/s."""
+    seconds have passed (at least one), reports decode tokens/s.  fp8:
+    (k codes, v codes, k scales, v scales) of an FP8 cache on the host."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     runs, t_total = 0, 0.0
     while True:
         t0 = time.perf_counter()
-        if paged:
+        if fp8 is not None:
+            oracle.decode_fp8(x["q"], *fp8, x["seq_lens_after"], x["scale"],
+                              block_table=x["block_table"] if paged else None,
+                              block_size=x.get("block_size", 16), nthreads=threads)
+        elif paged:
             oracle.decode(x["q"], x["k_pool"], x["v_pool"], x["seq_lens_after"], x["scale"],
                           block_table=x["block_table"], block_size=x["block_size"], nthreads=threads)
         else:
@@ -257,6 +271,9 @@ def main():
                     help="decode: the decode step (default); copy_blocks: copy-on-write copies of "
                          "4096 pool blocks of the paged workload; gather_cache: beam re-ranking of "
                          "the contiguous workload's caches")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="the cache holds FP8 E4M3 codes with per-KV-head scales "
+                         "(kvc_append_decode_attention_fp8); one token per sequence, no window")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -270,12 +287,13 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                      args.workload + ("_kvfp8" if args.kv_fp8 else ""),
                       args.calibration_copy_mib or 1024, args.command)
         return
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
@@ -306,6 +324,23 @@ def main():
         x = W.make_contiguous(w, t_cap=args.window + args.queries + 14 if args.ring else None)
         k_src, v_src = x["k_cache"], x["v_cache"]
         nblocks = None
+    fp8 = args.kv_fp8
+    if fp8 and (w.dtype != "bf16" or args.queries != 1 or args.window or args.ring):
+        print("--kv-fp8 takes a bf16 workload, one token per sequence and no window",
+              file=sys.stderr)
+        sys.exit(2)
+    if fp8:
+        # per-KV-head scales amax / 448 over the cache; codes by torch's
+        # float8_e4m3fn conversion (round to nearest even), from the same
+        # seeded N(0, 1) cache as the bf16 run
+        def quantise(t):
+            amax = t.float().abs().amax(dim=(0, 2, 3))
+            sc = (amax / 448.0).clamp(min=1e-12)
+            codes = (t.float() / sc.view(1, -1, 1, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
+            return codes, sc
+        k_src, k_sc = quantise(k_src)
+        v_src, v_sc = quantise(v_src)
+        k_sc_d, v_sc_d = k_sc.to(dev), v_sc.to(dev)
     cache_bytes = 2 * k_src.numel() * k_src.element_size()
     copies = args.copies or max(3, -(-800 * 2**20 // cache_bytes))
     k0, v0 = k_src.to(dev), v_src.to(dev)
@@ -369,11 +404,17 @@ def main():
 
     def append_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        kvc.append(k_new, v_new, kc, vc, sl_before, block_table=bt)
+        if fp8:
+            kvc.append_fp8(k_new, v_new, kc, vc, k_sc_d, v_sc_d, sl_before, block_table=bt)
+        else:
+            kvc.append(k_new, v_new, kc, vc, sl_before, block_table=bt)
 
     def decode_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        if w.paged:
+        if fp8:
+            kvc.decode_fp8(q, kc, vc, k_sc_d, v_sc_d, sl_after, block_table=bt, scale=x["scale"],
+                           num_splits=ns, workspace=ws, out=out, lse=lse)
+        elif w.paged:
             kvc.decode_paged(q, kc, vc, bt, sl_after, scale=x["scale"], num_splits=ns,
                              workspace=ws, out=out, lse=lse)
         else:
@@ -382,7 +423,11 @@ def main():
 
     def fused_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        if windowed:
+        if fp8:
+            kvc.decode_fp8(q, kc, vc, k_sc_d, v_sc_d, sl_before, block_table=bt, scale=x["scale"],
+                           num_splits=ns, workspace=ws, out=out, lse=lse, k_new=k_new,
+                           v_new=v_new)
+        elif windowed:
             kvc.decode_window(q, kc, vc, sl_before, win, ring=ring, block_table=bt,
                               scale=x["scale"], num_splits=ns, workspace=ws, out=out, lse=lse,
                               k_new=k_new, v_new=v_new)
@@ -484,9 +529,10 @@ def main():
     hi = x["seq_lens_before"].to(torch.int64) + nq
     lo = torch.clamp(x["seq_lens_before"].to(torch.int64) + 1 - win, min=0) if windowed \
         else torch.zeros_like(hi)
-    nbytes = algorithmic_bytes(w, hi - lo, nblocks, n=nq)
+    nbytes = algorithmic_bytes(w, hi - lo, nblocks, n=nq, kv_bytes=1 if fp8 else None)
     # stored counter runs are of the default (one-call) step
-    traffic = None if (args.separate or nq > 1 or windowed) else stored_traffic(w.name)
+    traffic = None if (args.separate or nq > 1 or windowed) else \
+        stored_traffic(w.name + ("_kvfp8" if fp8 else ""))
     call_bytes = nbytes["decode"] if args.separate else nbytes["fused"]
     achieved_gbs = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.B * nq / (ms_per_step * 1e-3)
@@ -494,7 +540,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and nq == 1 and not windowed:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x, w.paged)
+        cpu = cpu_baseline(w, x, w.paged,
+                           fp8=(k_src.numpy(), v_src.numpy(), k_sc.numpy(), v_sc.numpy())
+                           if fp8 else None)
 
     res = {
         "metric": "decode tokens/s (GQA KV-cache attention, one layer)",
@@ -507,7 +555,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 accumulate" if w.dtype == "bf16" else "f32",
+        "dtype": ("fp8 e4m3 KV cache (per-KV-head scales), bf16 q, fp32 accumulate" if fp8
+                  else "bf16 in, fp32 accumulate" if w.dtype == "bf16" else "f32"),
         "data": "synthetic, seeded N(0,1)",
         "config": {
             "workload": w.name, "B": w.B, "h": w.h, "g": w.g, "d": w.d,
@@ -515,13 +564,15 @@ def main():
             "paged": w.paged, "block_size": w.block_size if w.paged else None,
             "num_splits": ns, "split": split_mode, "chunk_len": chunk_len,
             "num_chunks": num_chunks, "queries_per_sequence": nq, "window": win,
-            "ring_cache": ring,
+            "ring_cache": ring, "kv_cache": "fp8_e4m3" if fp8 else w.dtype,
             # the launch-shape query describes calls without a sliding window
             "launch": None if windowed else {"waves_per_workgroup": waves, "workgroups": n_wgs,
                                              "chunk_len": launch_chunk, "chunks": launch_chunks},
             "cache_copies_rotated": copies, "parallelism": "single GPU",
         },
-        "step": ("kvc_append + decode call" if args.separate
+        "step": (("kvc_append_fp8 + decode call" if args.separate
+                  else "one kvc_append_decode_attention_fp8 call") if fp8
+                 else "kvc_append + decode call" if args.separate
                  else f"one kvc_append_decode_attention_window call (W={win}, ring={ring}, "
                       f"{nq} tokens per sequence)" if windowed
                  else f"one kvc_append_decode_attention_multi call ({nq} tokens per sequence)"

@@ -194,15 +194,21 @@ struct MfmaEngine {
         for (int qt = 0; qt < NQT; ++qt)
             lim[qt] = GEN ? visible_len(a, raw, (row0 + 16 * qt + col) % a.n) : 0;
 
-        // A call that appends reads its new tokens (positions raw .. raw+n-1,
-        // the last ones of the unit) from k_new / v_new and writes them into
-        // their cache slots here, once per unit.
+        // A call that appends writes its new tokens (positions raw ..
+        // raw+n-1, the last ones of the unit) into their cache slots here,
+        // once per unit.  bf16: the tokens are then read from k_new / v_new
+        // as a last tile.  FP8: they are quantised into the cache and, after
+        // a barrier, read back from it like every other position.
         const int fresh_lo = max(s, raw);
         const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 32 positions
-        const int e_cache = has_new ? fresh_lo : e;
+        const int e_cache = has_new && !KV8 ? fresh_lo : e;
         if (has_new) {
-            if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
-            else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            if constexpr (KV8) {
+                store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+                __syncthreads();  // has_new is uniform over the work-group
+            } else {
+                store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            }
         }
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
@@ -230,31 +236,22 @@ struct MfmaEngine {
                 else tr.v[u] = ld16_stream(Vc + row * kD + 8 * col);
             }
         };
-        // The appended tokens' tile at t0 (>= raw): position p is row p - raw
-        // of the unit's k_new / v_new rows (bf16; quantised to codes for an
-        // FP8 cache, so that the tile holds what the cache now holds);
-        // positions clamp to w1 - 1.
+        // The appended tokens' tile at t0 (>= raw, bf16 caches): position p
+        // is row p - raw of the unit's k_new / v_new rows; positions clamp to
+        // w1 - 1.
         auto load_new_tile = [&](int t0, TileRegs<KV8>& tr) {
+            if constexpr (!KV8) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
-                if constexpr (KV8) {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const uint2 c0 = bf16x8_to_e4m3(ld16(KN + r * kD + 64 * hh + 16 * G), k_sc);
-                        const uint2 c1 = bf16x8_to_e4m3(ld16(KN + r * kD + 64 * hh + 16 * G + 8), k_sc);
-                        tr.k[tt][hh] = make_uint4(c0.x, c0.y, c1.x, c1.y);
-                    }
-                } else {
+                for (int tt = 0; tt < 2; ++tt) {
+                    const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16(KN + r * kD + 32 * ks + 8 * G);
                 }
-            }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
-                if constexpr (KV8) tr.v[u] = bf16x8_to_e4m3(ld16(VN + r * kD + 8 * col), v_sc);
-                else tr.v[u] = ld16(VN + r * kD + 8 * col);
+                for (int u = 0; u < 8; ++u) {
+                    const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
+                    tr.v[u] = ld16(VN + r * kD + 8 * col);
+                }
             }
         };
         // MFMA A operand of K chunk ks of sub-tile tt.
@@ -395,10 +392,10 @@ struct MfmaEngine {
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
-        // The appended tokens (the last positions of the unit) are taken
-        // last, as one tile read from k_new / v_new by the wavefront next in
-        // turn.
-        if (has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
+        // bf16: the appended tokens (the last positions of the unit) are
+        // taken last, as one tile read from k_new / v_new by the wavefront
+        // next in turn.  (FP8 caches read them back in the loop above.)
+        if (!KV8 && has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
             w1 = e;
             TileRegs<KV8> tr;
             load_new_tile(fresh_lo, tr);

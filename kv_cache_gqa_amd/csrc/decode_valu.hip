@@ -109,15 +109,21 @@ struct ValuEngine {
 #pragma unroll
         for (int r = 0; r < M; ++r) lim[r] = GEN ? visible_len(a, raw, r % a.n) : 0;
 
-        // A call that appends reads its new tokens (positions raw .. raw+n-1,
-        // the last ones of the unit) from k_new / v_new and writes them into
-        // their cache slots here, once per unit.
+        // A call that appends writes its new tokens (positions raw ..
+        // raw+n-1, the last ones of the unit) into their cache slots here,
+        // once per unit.  bf16: the tokens are then read from k_new / v_new
+        // as a last tile.  FP8: they are quantised into the cache and, after
+        // a barrier, read back from it like every other position.
         const int fresh_lo = max(s, raw);
         const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 3 positions
-        const int e_cache = has_new ? fresh_lo : e;
+        const int e_cache = has_new && !KV8 ? fresh_lo : e;
         if (has_new) {
-            if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
-            else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            if constexpr (KV8) {
+                store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+                __syncthreads();  // has_new is uniform over the work-group
+            } else {
+                store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            }
         }
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
@@ -137,17 +143,14 @@ struct ValuEngine {
                 }
             }
         };
-        // The appended tokens' tile at t0 (>= raw): position p is row p - raw
-        // of the unit's k_new / v_new rows (bf16; quantised to codes for an
-        // FP8 cache); positions clamp to w1 - 1.
+        // The appended tokens' tile at t0 (>= raw, bf16 caches): position p
+        // is row p - raw of the unit's k_new / v_new rows; positions clamp to
+        // w1 - 1.
         auto load_new_tile = [&](int t0, ValuTile<KV8>& tr) {
+            if constexpr (!KV8) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
-                if constexpr (KV8) {
-                    tr.k[u] = bf16x8_to_e4m3(ld16(KN + r * kD + 8 * ds), k_sc);
-                    tr.v[u] = bf16x8_to_e4m3(ld16(VN + r * kD + 8 * ds), v_sc);
-                } else {
+                for (int u = 0; u < 8; ++u) {
+                    const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
                     tr.k[u] = ld16(KN + r * kD + 8 * ds);
                     tr.v[u] = ld16(VN + r * kD + 8 * ds);
                 }
@@ -249,10 +252,10 @@ struct ValuEngine {
 #endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
-        // The appended tokens (the last positions of the unit) are taken
-        // last, as one tile read from k_new / v_new by the wavefront next in
-        // turn.
-        if (has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
+        // bf16: the appended tokens (the last positions of the unit) are
+        // taken last, as one tile read from k_new / v_new by the wavefront
+        // next in turn.  (FP8 caches read them back in the loop above.)
+        if (!KV8 && has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
             w1 = e;
             ValuTile<KV8> tr;
             load_new_tile(fresh_lo, tr);

@@ -118,28 +118,18 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     const uint32_t u = __float_as_uint(y);
     const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fabsf(y);
-    if (a != a) return sign | 0x7Fu;
-    if (a >= 448.0f) return sign | 0x7Eu;
-    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
-    uint32_t ua = __float_as_uint(a);
-    ua += 0x7FFFFu + ((ua >> 20) & 1u);
-    const uint32_t code = (((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u);
-    return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
-// Codes of 8 bf16 (uint4) divided by `scale` (the quotient in float32).
-__device__ __forceinline__ uint2 bf16x8_to_e4m3(uint4 x, float scale) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(w[i] << 16) / scale;
-        const float hi = __uint_as_float(w[i] & 0xFFFF0000u) / scale;
-        const uint32_t pair = e4m3_encode(lo) | (e4m3_encode(hi) << 8);
-        out[i >> 1] |= pair << (16 * (i & 1));
-    }
-    return make_uint2(out[0], out[1]);
+    const uint32_t ua = u & 0x7FFFFFFFu;
+    const float a = __uint_as_float(ua);
+    // |y| >= 2^-6: keep 3 mantissa bits, rounding the 20 dropped bits to
+    // nearest even (a carry moves into the exponent); rebias 127 -> 7.
+    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+    const uint32_t normal = min((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u), 0x7Eu);
+    // |y| < 2^-6: subnormal codes are multiples of 2^-9, rounded to even.
+    const uint32_t sub = (uint32_t)rintf(fminf(a, 0.015625f) * 512.0f);
+    uint32_t code = a < 0.015625f ? sub : normal;
+    code = a >= 448.0f ? 0x7Eu : code;
+    code = a != a ? 0x7Fu : code;
+    return sign | code;
 }
 
 // Merge two online-softmax states (m2, l, acc) in base 2.  -inf maxima
@@ -251,15 +241,16 @@ __device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, in
 
 // FP8 cache, d = 128: quantise the appended tokens at positions [lo, hi) of
 // unit (b, j) (bf16 rows of k_new / v_new, position p = row p - raw) and
-// write their codes into their cache slots.  Each of the `nthreads` threads
-// writes 16 codes at a time (16 pieces per position: 8 of K, 8 of V).
-// Paged: positions whose block-table entry is not a valid block are skipped.
+// write their codes into their cache slots.  One code per thread and step
+// (256 per position: 128 of K, then 128 of V).  Paged: positions whose
+// block-table entry is not a valid block are skipped.
 __device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int b, int j, int raw,
                                                         int lo, int hi, int tid, int nthreads) {
     const long unit = (long)b * a.g + j;
-    for (int idx = tid; idx < (hi - lo) * 16; idx += nthreads) {
-        const int p = lo + (idx >> 4);
-        const int part = idx & 15;
+    for (int idx = tid; idx < (hi - lo) * 256; idx += nthreads) {
+        const int p = lo + (idx >> 8);
+        const bool is_v = (idx & 128) != 0;
+        const int e = idx & 127;
         long row;
         if (a.block_table != nullptr) {
             const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
@@ -268,16 +259,11 @@ __device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int
         } else {
             row = unit * a.t_cap + cache_slot(a, p);
         }
-        const bool is_v = part >= 8;
-        const int c = part & 7;
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(is_v ? a.v_new : a.k_new) +
-                              (unit * a.n + (p - raw)) * 128 + 16 * c;
+        const uint16_t x = reinterpret_cast<const uint16_t*>(is_v ? a.v_new : a.k_new)
+                               [(unit * a.n + (p - raw)) * 128 + e];
         const float sc = is_v ? a.v_scale[j] : a.k_scale[j];
-        const uint2 c0 = bf16x8_to_e4m3(ld16(src), sc);
-        const uint2 c1 = bf16x8_to_e4m3(ld16(src + 8), sc);
-        unsigned char* dst = reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? a.v : a.k)) +
-                             row * 128 + 16 * c;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(c0.x, c0.y, c1.x, c1.y);
+        unsigned char* dst = reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? a.v : a.k));
+        dst[row * 128 + e] = (unsigned char)e4m3_encode(__uint_as_float((uint32_t)x << 16) / sc);
     }
 }
 
