@@ -365,11 +365,11 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
  *   Attention is computed over the dequantised values code * scale (codes
  *   are widened to bf16 exactly; the K scale is folded into the score scale
  *   and the V scale into the output).
- *   The one-call step writes the new token's codes into its slot and then
- *   attends to the stored codes, so it gives exactly what kvc_append_fp8
- *   followed by kvc_decode_attention_fp8[_paged] gives, also when the
- *   new position's paged table entry is not a valid block (nothing is
- *   written and the clamped entry's block is read).
+ *   The one-call step attends to the new token's codes (what
+ *   kvc_append_fp8 stores), so it gives what kvc_append_fp8 followed by
+ *   kvc_decode_attention_fp8[_paged] gives; as with bf16, when the new
+ *   position's paged table entry is not a valid block nothing is written
+ *   but the token is still attended to.
  * Everything else (validation, splits, workspace from
  * kvc_decode_workspace_bytes with dtype KVC_BF16, positions, status codes)
  * is as in the bf16 single-token calls.  The fast kernels cover d = 128;

@@ -76,20 +76,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
     return __builtin_bit_cast(uint2, r);
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
-
-#ifndef KVC_MFMA_PREFETCH
-#define KVC_MFMA_PREFETCH 1
-#endif
 
 // Registers of one wavefront's 32-position tile.  bf16: K rows as MFMA A
 // operands (chunk ks: dims 32*ks + 8*G .. +8) and V rows 4u + G, dims
@@ -196,20 +186,19 @@ struct MfmaEngine {
 
         // A call that appends writes its new tokens (positions raw ..
         // raw+n-1, the last ones of the unit) into their cache slots here,
-        // once per unit.  bf16: the tokens are then read from k_new / v_new
-        // as a last tile.  FP8: they are quantised into the cache and, after
-        // a barrier, read back from it like every other position.
+        // once per unit, and attends to them as a last tile built from
+        // k_new / v_new (FP8: from their codes, n = 1).
         const int fresh_lo = max(s, raw);
         const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 32 positions
-        const int e_cache = has_new && !KV8 ? fresh_lo : e;
+        const int e_cache = has_new ? fresh_lo : e;
         if (has_new) {
-            if constexpr (KV8) {
-                store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
-                __syncthreads();  // has_new is uniform over the work-group
-            } else {
-                store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
-            }
+            if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         }
+        // The wavefront that takes the new tile; FP8: it loads the new row's
+        // bf16 values now so that the last tile does not wait for them.
+        const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
+        const uint2 new_pair = KV8 && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
@@ -236,11 +225,22 @@ struct MfmaEngine {
                 else tr.v[u] = ld16_stream(Vc + row * kD + 8 * col);
             }
         };
-        // The appended tokens' tile at t0 (>= raw, bf16 caches): position p
-        // is row p - raw of the unit's k_new / v_new rows; positions clamp to
-        // w1 - 1.
+        // The appended tokens' tile at t0 (>= raw): position p is row p - raw
+        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  FP8
+        // (one new token, so every position of the tile is that token): its
+        // codes, computed once into this wavefront's V staging area.
         auto load_new_tile = [&](int t0, TileRegs<KV8>& tr) {
-            if constexpr (!KV8) {
+            if constexpr (KV8) {
+                new_row_codes_fp8_d128(a, j, lane, new_pair, vst);
+                wave_lds_sync();
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        tr.k[tt][hh] = *reinterpret_cast<const uint4*>(vst + 64 * hh + 16 * G);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) tr.v[u] = *reinterpret_cast<const uint2*>(vst + 128 + 8 * col);
+            } else {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
@@ -368,34 +368,53 @@ struct MfmaEngine {
                 }
                 __syncthreads();
             }
-            const int stride = W * kTileTokens;
-            int t0 = w0 + wave * kTileTokens;
-#if KVC_MFMA_PREFETCH
-            TileRegs<KV8> tA, tB;
-            load_tile(t0, tA);
-            for (;;) {
-                if (t0 >= w1) break;
-                load_tile(t0 + stride, tB);
-                compute_tile(t0, tA);
-                t0 += stride;
-                if (t0 >= w1) break;
-                load_tile(t0 + stride, tA);
-                compute_tile(t0, tB);
-                t0 += stride;
+            // A wavefront takes kStep positions per step while the next
+            // step's loads are in flight.  FP8 tiles hold half the bytes: in
+            // the 8-wavefront kernels (one work-group per unit) a wavefront
+            // loads two 32-position tiles per step, which keeps as many bytes
+            // in flight as with bf16 (measured faster there; slower with 4
+            // wavefronts).
+            constexpr bool kPair = KV8 && W >= 8;
+            constexpr int kStep = kPair ? 2 * kTileTokens : kTileTokens;
+            const int stride = W * kStep;
+            int t0 = w0 + wave * kStep;
+            if constexpr (kPair) {
+                TileRegs<KV8> a0, a1, b0, b1;
+                load_tile(t0, a0);
+                load_tile(t0 + kTileTokens, a1);
+                for (;;) {
+                    if (t0 >= w1) break;
+                    load_tile(t0 + stride, b0);
+                    load_tile(t0 + stride + kTileTokens, b1);
+                    compute_tile(t0, a0);
+                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, a1);
+                    t0 += stride;
+                    if (t0 >= w1) break;
+                    load_tile(t0 + stride, a0);
+                    load_tile(t0 + stride + kTileTokens, a1);
+                    compute_tile(t0, b0);
+                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, b1);
+                    t0 += stride;
+                }
+            } else {
+                TileRegs<KV8> tA, tB;
+                load_tile(t0, tA);
+                for (;;) {
+                    if (t0 >= w1) break;
+                    load_tile(t0 + stride, tB);
+                    compute_tile(t0, tA);
+                    t0 += stride;
+                    if (t0 >= w1) break;
+                    load_tile(t0 + stride, tA);
+                    compute_tile(t0, tB);
+                    t0 += stride;
+                }
             }
-#else
-            for (; t0 < w1; t0 += stride) {
-                TileRegs<KV8> tr;
-                load_tile(t0, tr);
-                compute_tile(t0, tr);
-            }
-#endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
-        // bf16: the appended tokens (the last positions of the unit) are
-        // taken last, as one tile read from k_new / v_new by the wavefront
-        // next in turn.  (FP8 caches read them back in the loop above.)
-        if (!KV8 && has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
+        // The appended tokens (the last positions of the unit) are taken
+        // last, as one tile by the wavefront next in turn.
+        if (new_wave) {
             w1 = e;
             TileRegs<KV8> tr;
             load_new_tile(fresh_lo, tr);

@@ -28,10 +28,6 @@ namespace {
 
 constexpr int kD = 128;
 
-#ifndef KVC_VALU_PREFETCH
-#define KVC_VALU_PREFETCH 1
-#endif
-
 // GEN: several query tokens per sequence, sliding windows or ring caches
 // (per-row visibility masks, ring-aware windows).
 // Registers of one wavefront's tile: rows 4u + lane/16, dims 8*(lane%16)
@@ -56,6 +52,7 @@ struct ValuEngine {
         float red_m[W][M];
         float red_l[W][M];
         float red_o[W][M][kD];
+        __attribute__((aligned(16))) unsigned char nrow[KV8 ? W : 1][256];  // FP8 new-token codes
     };
 
     // The M query heads of KV head j of sequence b over positions [s, e)
@@ -111,20 +108,19 @@ struct ValuEngine {
 
         // A call that appends writes its new tokens (positions raw ..
         // raw+n-1, the last ones of the unit) into their cache slots here,
-        // once per unit.  bf16: the tokens are then read from k_new / v_new
-        // as a last tile.  FP8: they are quantised into the cache and, after
-        // a barrier, read back from it like every other position.
+        // once per unit, and attends to them as a last tile built from
+        // k_new / v_new (FP8: from their codes, n = 1).
         const int fresh_lo = max(s, raw);
         const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 3 positions
-        const int e_cache = has_new && !KV8 ? fresh_lo : e;
+        const int e_cache = has_new ? fresh_lo : e;
         if (has_new) {
-            if constexpr (KV8) {
-                store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
-                __syncthreads();  // has_new is uniform over the work-group
-            } else {
-                store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
-            }
+            if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
+            else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         }
+        // The wavefront that takes the new tile; FP8: it loads the new row's
+        // bf16 values now so that the last tile does not wait for them.
+        const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
+        const uint2 new_pair = KV8 && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
@@ -143,11 +139,21 @@ struct ValuEngine {
                 }
             }
         };
-        // The appended tokens' tile at t0 (>= raw, bf16 caches): position p
-        // is row p - raw of the unit's k_new / v_new rows; positions clamp to
-        // w1 - 1.
+        // The appended tokens' tile at t0 (>= raw): position p is row p - raw
+        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  FP8
+        // (one new token, so every position of the tile is that token): its
+        // codes, computed once into this wavefront's LDS area.
         auto load_new_tile = [&](int t0, ValuTile<KV8>& tr) {
-            if constexpr (!KV8) {
+            if constexpr (KV8) {
+                unsigned char* codes = sh.nrow[wave];
+                new_row_codes_fp8_d128(a, j, lane, new_pair, codes);
+                wave_lds_sync();
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    tr.k[u] = *reinterpret_cast<const uint2*>(codes + 8 * ds);
+                    tr.v[u] = *reinterpret_cast<const uint2*>(codes + 128 + 8 * ds);
+                }
+            } else {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
@@ -230,7 +236,6 @@ struct ValuEngine {
             }
             const int stride = W * kTileTokens;
             int t0 = w0 + wave * kTileTokens;
-#if KVC_VALU_PREFETCH
             ValuTile<KV8> tA, tB;
             load_tile(t0, tA);
             for (;;) {
@@ -243,19 +248,11 @@ struct ValuEngine {
                 compute_tile(t0, tB);
                 t0 += stride;
             }
-#else
-            for (; t0 < w1; t0 += stride) {
-                ValuTile<KV8> tr;
-                load_tile(t0, tr);
-                compute_tile(t0, tr);
-            }
-#endif
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
-        // bf16: the appended tokens (the last positions of the unit) are
-        // taken last, as one tile read from k_new / v_new by the wavefront
-        // next in turn.  (FP8 caches read them back in the loop above.)
-        if (!KV8 && has_new && wave == ((fresh_lo - s) / kTileTokens) % W) {
+        // The appended tokens (the last positions of the unit) are taken
+        // last, as one tile by the wavefront next in turn.
+        if (new_wave) {
             w1 = e;
             ValuTile<KV8> tr;
             load_new_tile(fresh_lo, tr);

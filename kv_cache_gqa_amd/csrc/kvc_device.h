@@ -239,6 +239,13 @@ __device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, in
     }
 }
 
+// LDS writes of a wavefront visible to all its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // FP8 cache, d = 128: quantise the appended tokens at positions [lo, hi) of
 // unit (b, j) (bf16 rows of k_new / v_new, position p = row p - raw) and
 // write their codes into their cache slots.  One code per thread and step
@@ -265,6 +272,32 @@ __device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int
         unsigned char* dst = reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? a.v : a.k));
         dst[row * 128 + e] = (unsigned char)e4m3_encode(__uint_as_float((uint32_t)x << 16) / sc);
     }
+}
+
+// d = 128: the bf16 pairs at dims 2*lane, 2*lane + 1 of unit (b, j)'s
+// first new K row (.x) and V row (.y).
+__device__ __forceinline__ uint2 new_row_pair_d128(const DecodeArgs& a, int b, int j, int lane) {
+    const long row = ((long)b * a.g + j) * a.n;
+    return make_uint2(reinterpret_cast<const uint32_t*>(a.k_new)[row * 64 + lane],
+                      reinterpret_cast<const uint32_t*>(a.v_new)[row * 64 + lane]);
+}
+
+// FP8 cache, d = 128, one new token per sequence: the codes of the new K
+// row (bytes 0..127 of `codes`) and V row (128..255) of KV head j, written
+// to the calling wavefront's LDS area `codes` by its 64 lanes from their
+// pairs (new_row_pair_d128), with the same quotient and encoder as
+// store_new_rows_fp8_d128, so they equal what that call stores.  The caller
+// syncs the wavefront (wave_lds_sync) before reading them.
+__device__ __forceinline__ void new_row_codes_fp8_d128(const DecodeArgs& a, int j, int lane, uint2 pair,
+                                                       unsigned char* codes) {
+    const uint32_t kx = pair.x, vx = pair.y;
+    const float ks = a.k_scale[j], vs = a.v_scale[j];
+    const uint32_t kc = e4m3_encode(__uint_as_float(kx << 16) / ks) |
+                        (e4m3_encode(__uint_as_float(kx & 0xFFFF0000u) / ks) << 8);
+    const uint32_t vc = e4m3_encode(__uint_as_float(vx << 16) / vs) |
+                        (e4m3_encode(__uint_as_float(vx & 0xFFFF0000u) / vs) << 8);
+    reinterpret_cast<uint16_t*>(codes)[lane] = (uint16_t)kc;
+    reinterpret_cast<uint16_t*>(codes + 128)[lane] = (uint16_t)vc;
 }
 
 }  // namespace kvc
