@@ -195,10 +195,13 @@ struct MfmaEngine {
             if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
             else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         }
-        // The wavefront that takes the new tile; FP8: it loads the new row's
-        // bf16 values now so that the last tile does not wait for them.
+        // The wavefront that takes the new tile.  With one new token (always
+        // so without GEN) it loads the token's K and V rows now, one bf16
+        // pair of each per lane, so that the last tile does not wait for
+        // them; the tile is then built from those pairs through LDS.
+        constexpr bool kNewPair = KV8 || !GEN;
         const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
-        const uint2 new_pair = KV8 && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
+        const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
@@ -226,9 +229,9 @@ struct MfmaEngine {
             }
         };
         // The appended tokens' tile at t0 (>= raw): position p is row p - raw
-        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  FP8
-        // (one new token, so every position of the tile is that token): its
-        // codes, computed once into this wavefront's V staging area.
+        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  With
+        // one new token every position of the tile is that token: its rows
+        // (FP8: their codes) go to this wavefront's V staging area first.
         auto load_new_tile = [&](int t0, TileRegs<KV8>& tr) {
             if constexpr (KV8) {
                 new_row_codes_fp8_d128(a, j, lane, new_pair, vst);
@@ -240,6 +243,17 @@ struct MfmaEngine {
                         tr.k[tt][hh] = *reinterpret_cast<const uint4*>(vst + 64 * hh + 16 * G);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) tr.v[u] = *reinterpret_cast<const uint2*>(vst + 128 + 8 * col);
+            } else if constexpr (kNewPair) {
+                reinterpret_cast<uint32_t*>(vst)[lane] = new_pair.x;        // K row, 256 bytes
+                reinterpret_cast<uint32_t*>(vst + 256)[lane] = new_pair.y;  // V row
+                wave_lds_sync();
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        tr.k[tt][ks] = *reinterpret_cast<const uint4*>(vst + 64 * ks + 16 * G);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) tr.v[u] = *reinterpret_cast<const uint4*>(vst + 256 + 16 * col);
             } else {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {

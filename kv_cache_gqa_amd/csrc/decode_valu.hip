@@ -52,7 +52,7 @@ struct ValuEngine {
         float red_m[W][M];
         float red_l[W][M];
         float red_o[W][M][kD];
-        __attribute__((aligned(16))) unsigned char nrow[KV8 ? W : 1][256];  // FP8 new-token codes
+        __attribute__((aligned(16))) unsigned char nrow[GEN && !KV8 ? 1 : W][512];  // one new token's rows
     };
 
     // The M query heads of KV head j of sequence b over positions [s, e)
@@ -117,10 +117,13 @@ struct ValuEngine {
             if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
             else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         }
-        // The wavefront that takes the new tile; FP8: it loads the new row's
-        // bf16 values now so that the last tile does not wait for them.
+        // The wavefront that takes the new tile.  With one new token (always
+        // so without GEN) it loads the token's K and V rows now, one bf16
+        // pair of each per lane, so that the last tile does not wait for
+        // them; the tile is then built from those pairs through LDS.
+        constexpr bool kNewPair = KV8 || !GEN;
         const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
-        const uint2 new_pair = KV8 && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
+        const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
@@ -140,9 +143,9 @@ struct ValuEngine {
             }
         };
         // The appended tokens' tile at t0 (>= raw): position p is row p - raw
-        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  FP8
-        // (one new token, so every position of the tile is that token): its
-        // codes, computed once into this wavefront's LDS area.
+        // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  With
+        // one new token every position of the tile is that token: its rows
+        // (FP8: their codes) go to this wavefront's LDS area first.
         auto load_new_tile = [&](int t0, ValuTile<KV8>& tr) {
             if constexpr (KV8) {
                 unsigned char* codes = sh.nrow[wave];
@@ -152,6 +155,16 @@ struct ValuEngine {
                 for (int u = 0; u < 8; ++u) {
                     tr.k[u] = *reinterpret_cast<const uint2*>(codes + 8 * ds);
                     tr.v[u] = *reinterpret_cast<const uint2*>(codes + 128 + 8 * ds);
+                }
+            } else if constexpr (kNewPair) {
+                unsigned char* rows = sh.nrow[wave];
+                reinterpret_cast<uint32_t*>(rows)[lane] = new_pair.x;        // K row, 256 bytes
+                reinterpret_cast<uint32_t*>(rows + 256)[lane] = new_pair.y;  // V row
+                wave_lds_sync();
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    tr.k[u] = *reinterpret_cast<const uint4*>(rows + 16 * ds);
+                    tr.v[u] = *reinterpret_cast<const uint4*>(rows + 256 + 16 * ds);
                 }
             } else {
 #pragma unroll
