@@ -106,6 +106,9 @@ struct TileRegs<true> {
 template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
 struct MfmaEngine {
     using L = Lds<NQT, W>;
+    // Two query tiles keep 64 accumulator and 32 query registers per lane;
+    // a single set of tile registers lets two wavefronts share a SIMD.
+    static constexpr bool kSingleBuffer = NQT >= 2;
     struct Shared {
         int tbl[PAGED ? kMaxTableSlice : 1];
         __attribute__((aligned(16))) unsigned char lds[L::kBytes];
@@ -208,7 +211,7 @@ struct MfmaEngine {
 
         // Loads of the 32-position sub-tile at t0; positions are clamped to
         // the window's last one, so a sub-tile past the end stays in bounds.
-        auto load_tile = [&](int t0, TileRegs<KV8>& tr) {
+        auto load_k = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const long row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
@@ -220,13 +223,19 @@ struct MfmaEngine {
                     for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16_stream(K + row * kD + 32 * ks + 8 * G);
                 }
             }
-            // V rows 4u + G, chunk col: four whole rows per instruction.
+        };
+        // V rows 4u + G, chunk col: four whole rows per instruction.
+        auto load_v = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long row = kv_row(min(t0 + 4 * u + G, w1 - 1));
                 if constexpr (KV8) tr.v[u] = ld8_stream(V8 + row * kD + 8 * col);
                 else tr.v[u] = ld16_stream(Vc + row * kD + 8 * col);
             }
+        };
+        auto load_tile = [&](int t0, TileRegs<KV8>& tr) {
+            load_k(t0, tr);
+            load_v(t0, tr);
         };
         // The appended tokens' tile at t0 (>= raw): position p is row p - raw
         // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  With
@@ -282,7 +291,10 @@ struct MfmaEngine {
             else return tr.v[u];
         };
 
-        auto compute_tile = [&](int t0, const TileRegs<KV8>& tr) {
+        // after_qk runs once the K registers are consumed, after_stage once
+        // the V registers are (a single-buffered walk reloads them there).
+        auto no_hook = [] {};
+        auto compute_tile = [&](int t0, const TileRegs<KV8>& tr, auto after_qk, auto after_stage) {
             f32x4_t S[NQT][2];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -294,12 +306,14 @@ struct MfmaEngine {
                     S[qt][tt] = s4;
                 }
             }
+            after_qk();
             // Stage V into this wavefront's LDS area.
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int r = 4 * u + G;
                 *reinterpret_cast<uint4*>(vst + r * kVRowBytes + ((col ^ vswz(r)) << 4)) = v_row(tr, u);
             }
+            after_stage();
             // Online softmax; P as the B operand of the PV product.
             uint4 pb[NQT];
 #pragma unroll
@@ -388,11 +402,25 @@ struct MfmaEngine {
             // loads two 32-position tiles per step, which keeps as many bytes
             // in flight as with bf16 (measured faster there; slower with 4
             // wavefronts).
-            constexpr bool kPair = KV8 && W >= 8;
+            constexpr bool kPair = KV8 && W >= 8 && !kSingleBuffer;
             constexpr int kStep = kPair ? 2 * kTileTokens : kTileTokens;
             const int stride = W * kStep;
             int t0 = w0 + wave * kStep;
-            if constexpr (kPair) {
+            if constexpr (kSingleBuffer) {
+                // One set of tile registers: the next tile's K is loaded as
+                // soon as the product has consumed this tile's K, its V once
+                // this tile's V is staged; the schedule barriers keep the
+                // compiler from hoisting the loads (which would need a
+                // second set of registers).
+                TileRegs<KV8> tr;
+                load_tile(t0, tr);
+                for (; t0 < w1; t0 += stride) {
+                    const int tn = t0 + stride;
+                    compute_tile(t0, tr,
+                                 [&] { __builtin_amdgcn_sched_barrier(0); load_k(tn, tr); __builtin_amdgcn_sched_barrier(0); },
+                                 [&] { __builtin_amdgcn_sched_barrier(0); load_v(tn, tr); __builtin_amdgcn_sched_barrier(0); });
+                }
+            } else if constexpr (kPair) {
                 TileRegs<KV8> a0, a1, b0, b1;
                 load_tile(t0, a0);
                 load_tile(t0 + kTileTokens, a1);
@@ -400,14 +428,14 @@ struct MfmaEngine {
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, b0);
                     load_tile(t0 + stride + kTileTokens, b1);
-                    compute_tile(t0, a0);
-                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, a1);
+                    compute_tile(t0, a0, no_hook, no_hook);
+                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, a1, no_hook, no_hook);
                     t0 += stride;
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, a0);
                     load_tile(t0 + stride + kTileTokens, a1);
-                    compute_tile(t0, b0);
-                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, b1);
+                    compute_tile(t0, b0, no_hook, no_hook);
+                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, b1, no_hook, no_hook);
                     t0 += stride;
                 }
             } else {
@@ -416,11 +444,11 @@ struct MfmaEngine {
                 for (;;) {
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, tB);
-                    compute_tile(t0, tA);
+                    compute_tile(t0, tA, no_hook, no_hook);
                     t0 += stride;
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, tA);
-                    compute_tile(t0, tB);
+                    compute_tile(t0, tB, no_hook, no_hook);
                     t0 += stride;
                 }
             }
@@ -432,7 +460,7 @@ struct MfmaEngine {
             w1 = e;
             TileRegs<KV8> tr;
             load_new_tile(fresh_lo, tr);
-            compute_tile(fresh_lo, tr);
+            compute_tile(fresh_lo, tr, no_hook, no_hook);
         }
 
         // lex holds this lane's positions only: sum the four row groups.
@@ -513,12 +541,11 @@ struct MfmaEngine {
 
 }  // namespace
 
-// Two resident wavefronts per SIMD for the 16-query variant: the register
-// allocator is asked to fit 256 registers (it does, without spills, with the
-// accumulators in arch VGPRs).  The 32-query variant would spill and keeps
-// one wavefront per SIMD.
+// Two resident wavefronts per SIMD: the register allocator is asked to fit
+// 256 registers (it does without spills: the 16-query variant with two sets
+// of tile registers, the 32-query variant with one).
 template <int NQT>
-struct MfmaOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 2 : 1; };
+struct MfmaOccupancy { static constexpr int kWavesPerEu = 2; };
 
 template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
 __global__ void __launch_bounds__(64 * W)
@@ -567,18 +594,22 @@ static const void* mfma_pick(bool stream, bool gen, bool kv8) {
 
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
 // general features, FP8 cache); nullptr when that combination is not built.
-// Every (m, layout, mode) has a 4-wavefront kernel; one tile of query rows
-// (m <= 16) on a contiguous cache also has an 8-wavefront chunked kernel,
-// for whole-unit work-groups.  (Two tiles need more registers than 8
-// wavefronts per work-group leave.)  FP8 caches have the kernels without the
-// general features.
+// Every (m, layout, mode) has a 4-wavefront kernel; a contiguous cache also
+// has 8-wavefront chunked kernels, for whole-unit work-groups and for chunk
+// grids smaller than the device's slots.  FP8 caches have the kernels
+// without the general features.
 const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
     const bool two = m > 16;
     if (waves == 4) {
         if (two) return paged ? mfma_pick<2, true, 4>(stream, gen, kv8) : mfma_pick<2, false, 4>(stream, gen, kv8);
         return paged ? mfma_pick<1, true, 4>(stream, gen, kv8) : mfma_pick<1, false, 4>(stream, gen, kv8);
     }
-    if (waves == 8 && !two && !paged && !stream) {
+    if (waves == 8 && !paged && !stream) {
+        if (two) {
+            if (kv8) return gen ? nullptr : (const void*)decode_mfma_chunked<2, false, 8, false, true>;
+            return gen ? (const void*)decode_mfma_chunked<2, false, 8, true, false>
+                       : (const void*)decode_mfma_chunked<2, false, 8, false, false>;
+        }
         if (kv8) return gen ? nullptr : (const void*)decode_mfma_chunked<1, false, 8, false, true>;
         return gen ? (const void*)decode_mfma_chunked<1, false, 8, true, false>
                    : (const void*)decode_mfma_chunked<1, false, 8, false, false>;

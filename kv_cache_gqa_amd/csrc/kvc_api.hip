@@ -261,6 +261,16 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     }
     a.chunk_len = sc.plan.chunk_len;
     a.num_chunks = sc.plan.num_chunks;
+    if (!sc.stream && !sc.auto_chunks && sc.kind == kMfma && a.m > 16) {
+        // Two query tiles per work-group: a fixed chunk grid that the device
+        // holds at once with 8-wavefront work-groups runs twice the
+        // wavefronts that way (with one tile, 4-wavefront work-groups keep
+        // the tiling of the paged kernels).
+        const void* f8 = kernel_for(sc.kind, a.m < 32 ? a.m : 32, paged, false, 8,
+                                    general_features(a), a.kv8 != 0);
+        const long wgs = (long)a.num_chunks * a.g * a.slices * a.B;
+        if (f8 != nullptr && wgs <= device_slots(f8, 8)) a.waves = 8;
+    }
 }
 
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
