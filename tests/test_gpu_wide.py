@@ -18,14 +18,14 @@ from gpu_util import attended_vmax_contig, check_parity, dev, plant_needles_cont
 pytestmark = pytest.mark.gpu
 
 # (id, shape, batch): units = B * g fill a 256-CU device's wide slots once
-# (256 units each).  The VALU kernels (m <= 3) and mfma_m32 have no wide kernel
-# with equal residency and stay on 4-wavefront chunks: parity must hold either way.
+# (256 units each).  The VALU kernels (m <= 3) have no wide kernel with equal
+# residency and stay on 4-wavefront chunks: parity must hold either way.
 CASES = [
     ("valu_m1", dict(h=32, g=32, d=128, dtype="bf16"), 8),
     ("valu_m2", dict(h=8, g=4, d=128, dtype="bf16"), 64),
     ("mfma_m8_w8", dict(h=64, g=8, d=128, dtype="bf16"), 32),
     ("mfma_m4_w8", dict(h=16, g=4, d=128, dtype="bf16"), 64),
-    ("mfma_m32", dict(h=64, g=2, d=128, dtype="bf16"), 128),
+    ("mfma_m32_w8", dict(h=64, g=2, d=128, dtype="bf16"), 128),
 ]
 EDGES = [0, 1, 31, 32, 33, 4095, 4096, 4097, 8193, 9000, 2, 257]
 
@@ -70,7 +70,48 @@ def test_wide_auto_chunks(case):
     ro, rl = oracle.decode(xs["q"], xs["k_cache"], xs["v_cache"], lengths, xs["scale"])
     e = check_parity(out, lse, ro, rl, attended_vmax_contig(xs["v_cache"], lengths), name)
     print(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}", file=sys.stderr, flush=True)
-    # the same inputs through explicit 4-wavefront chunks agree to the same bar
+    # the same inputs through explicit chunks agree to the same bar
     out2, lse2 = kvc.decode(dev(xs["q"]), dev(xs["k_cache"]), dev(xs["v_cache"]), dev(lengths),
                             scale=xs["scale"], num_splits=3)
     check_parity(out2, lse2, ro, rl, attended_vmax_contig(xs["v_cache"], lengths), name + "/3")
+
+
+@pytest.mark.parametrize("kv8", [False, True], ids=["bf16", "fp8"])
+def test_fixed_chunks_two_tiles_wide(kv8):
+    """32 query rows per KV head (long-context MQA shape) with a fixed grid of
+    64 chunks per sequence that the device holds at once: 8-wavefront
+    work-groups (on 256 CUs), each chunk split over eight wavefronts; needles
+    at chunk edges; parity with the oracle for bf16 and FP8 caches."""
+    print(f"case fixed_chunks_wide kv8={kv8}", file=sys.stderr, flush=True)
+    B, h, g, d, ns = 4, 32, 1, 128, 64
+    w = W.Workload("mqa_wide", B=B, h=h, g=g, d=d, dtype="bf16", seed=710)
+    lengths = torch.tensor([20000, 1, 12345, 19968], dtype=torch.int32)
+    x = W.make_contiguous(w, lengths=lengths, t_cap=20016, fill=float("nan"))
+    waves, wgs, cl, nc = kvc.launch_shape(B, h, g, d, 20016, ns)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"  waves={waves} wgs={wgs} chunk_len={cl} chunks={nc}", file=sys.stderr, flush=True)
+    if cus == 256:  # about 64 chunks of a multiple of 32 positions, all resident at once
+        assert waves == 8 and abs(nc - ns) <= 1
+    pos = [[min(p, int(lengths[b]) - 1)] for b, p in enumerate([cl - 1, 0, 5 * cl, 63 * cl])]
+    xs = dict(x)
+    plant_needles_contig(xs, pos)
+    if not kv8:
+        out, lse = kvc.decode(dev(xs["q"]), dev(xs["k_cache"]), dev(xs["v_cache"]), dev(lengths),
+                              scale=xs["scale"], num_splits=ns)
+        ro, rl = oracle.decode(xs["q"], xs["k_cache"], xs["v_cache"], lengths, xs["scale"])
+        vmax = attended_vmax_contig(xs["v_cache"], lengths)
+    else:
+        gen = torch.Generator().manual_seed(711)
+        ks = (torch.rand(g, generator=gen) * 0.05 + 0.01).to(torch.float32)
+        vs = (torch.rand(g, generator=gen) * 0.05 + 0.01).to(torch.float32)
+        kc = torch.from_numpy(oracle.quantize_fp8(xs["k_cache"], ks.numpy(), 1))
+        vc = torch.from_numpy(oracle.quantize_fp8(xs["v_cache"], vs.numpy(), 1))
+        out, lse = kvc.decode_fp8(dev(xs["q"]), dev(kc), dev(vc), dev(ks), dev(vs), dev(lengths),
+                                  scale=xs["scale"], num_splits=ns)
+        ro, rl = oracle.decode_fp8(xs["q"], kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(),
+                                   lengths, xs["scale"])
+        vals = torch.from_numpy(oracle.e4m3_values())
+        vmax = max(float((vals[vc[b, :, :int(lengths[b])].long()] * float(vs[0])).abs().max())
+                   for b in range(B))
+    e = check_parity(out, lse, ro, rl, vmax, f"fixed chunks kv8={kv8}")
+    print(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}", file=sys.stderr, flush=True)
