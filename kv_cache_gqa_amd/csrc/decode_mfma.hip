@@ -212,16 +212,23 @@ struct MfmaEngine {
 
         // Loads of the 32-position sub-tile at t0; positions are clamped to
         // the window's last one, so a sub-tile past the end stays in bounds.
+        // K/V read once are streamed (non-temporal loads); when the rows are
+        // cut into slices that each read the unit's K/V, ordinary loads keep
+        // the lines in the caches for the other slices (measured 20 % faster
+        // there, 10 % slower for single reads).
+        const bool reread = NQT >= 2 && a.slices > 1;
+        auto ld16_kv = [&](const void* p) { return reread ? ld16(p) : ld16_stream(p); };
+        auto ld8_kv = [&](const void* p) { return reread ? ld8(p) : ld8_stream(p); };
         auto load_k = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const long row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
                 if constexpr (KV8) {
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) tr.k[tt][hh] = ld16_stream(K8 + row * kD + 64 * hh + 16 * G);
+                    for (int hh = 0; hh < 2; ++hh) tr.k[tt][hh] = ld16_kv(K8 + row * kD + 64 * hh + 16 * G);
                 } else {
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16_stream(K + row * kD + 32 * ks + 8 * G);
+                    for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16_kv(K + row * kD + 32 * ks + 8 * G);
                 }
             }
         };
@@ -230,8 +237,8 @@ struct MfmaEngine {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long row = kv_row(min(t0 + 4 * u + G, w1 - 1));
-                if constexpr (KV8) tr.v[u] = ld8_stream(V8 + row * kD + 8 * col);
-                else tr.v[u] = ld16_stream(Vc + row * kD + 8 * col);
+                if constexpr (KV8) tr.v[u] = ld8_kv(V8 + row * kD + 8 * col);
+                else tr.v[u] = ld16_kv(Vc + row * kD + 8 * col);
             }
         };
         auto load_tile = [&](int t0, TileRegs<KV8>& tr) {
@@ -556,8 +563,25 @@ __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, KV8>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
-    const int c = blockIdx.x, b = blockIdx.z;
-    const int j = blockIdx.y / a.slices, row0 = (blockIdx.y - j * a.slices) * 16 * NQT;
+    int c = blockIdx.x, b = blockIdx.z;
+    int j = blockIdx.y / a.slices, row0 = (blockIdx.y - j * a.slices) * 16 * NQT;
+    if (a.slices > 1) {
+        // The slices of one (chunk, KV head, sequence) read the same K/V.
+        // Work-group ids go to the eight XCDs in turn, so the slices get ids
+        // eight apart: they run on one XCD at about the same time and the
+        // later reads find the lines in that XCD's L2.  Units go in groups
+        // of eight (the last group may be narrower); within a group, slice
+        // s of unit k has id s * width + k.
+        const long L = blockIdx.x + (long)gridDim.x * (blockIdx.y + (long)gridDim.y * blockIdx.z);
+        const long units = (long)a.num_chunks * a.g * a.B;
+        const long grp = L / (8L * a.slices), rem = L - grp * 8L * a.slices;
+        const long width = min(8L, units - grp * 8);
+        const long u = grp * 8 + rem % width;
+        row0 = (int)(rem / width) * 16 * NQT;
+        c = (int)(u % a.num_chunks);
+        j = (int)((u / a.num_chunks) % a.g);
+        b = (int)(u / ((long)a.num_chunks * a.g));
+    }
     // chunks cover [lo, hi); without the general features lo = 0
     const PosRange ur = GEN ? unit_range(a, a.seq_lens[b])
                             : PosRange{0, attended_len(a, a.seq_lens[b])};
