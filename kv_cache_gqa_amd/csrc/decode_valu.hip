@@ -373,8 +373,9 @@ static const void* valu_pick(bool stream, bool gen, bool kv8) {
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
 // general features, FP8 cache); nullptr when that combination is not built.
 // Only 4-wavefront kernels: one wide work-group per (sequence, KV head)
-// measured slower than split chunks plus a merge for these kernels (8 and 16
-// wavefronts, m = 1).
+// measured slower than split chunks plus a merge for these kernels (8, 12
+// and 16 wavefronts, m = 1; 12 keeps the occupancy of three chunks but not
+// their balance).
 const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
     if (waves != 4) return nullptr;
     switch (m) {
