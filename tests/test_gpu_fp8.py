@@ -190,3 +190,40 @@ def test_fp8_full_size_70b():
     ro, rl = oracle.decode_fp8(q, ek, ev, ks.numpy(), vs.numpy(), before + 1, w.scale)
     e = check_parity(out, lse, ro, rl, _vmax(torch.from_numpy(ev), vs, before + 1), "fp8 70b")
     _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
+
+
+def test_fp8_full_size_paged():
+    """The paged GQA workload (64 sequences of 128..8192 positions, blocks
+    of 16 in a seeded permutation) with an FP8 cache, one-call step, in the
+    launch the benchmark times; the pools hold seeded random codes."""
+    _log("case fp8_full_paged")
+    w = W.WORKLOADS["paged_gqa_bf16"]
+    x = W.make_paged(w)
+    gen = torch.Generator().manual_seed(1206)
+    shape = x["k_pool"].shape
+    kc = torch.randint(0, 256, shape, generator=gen, dtype=torch.int32).to(torch.uint8)
+    vc = torch.randint(0, 256, shape, generator=gen, dtype=torch.int32).to(torch.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x3C
+    vc[(vc & 0x7F) == 0x7F] = 0x3C
+    ks, vs = _scales(w.g, gen)
+    before, after, table = x["seq_lens_before"], x["seq_lens_after"], x["block_table"]
+    kd, vd = dev(kc), dev(vc)
+    out, lse = kvc.decode_fp8(dev(x["q"]), kd, vd, dev(ks), dev(vs), dev(before),
+                              block_table=dev(table), scale=x["scale"], num_splits=w.num_splits,
+                              k_new=dev(x["k_new"]), v_new=dev(x["v_new"]))
+    torch.cuda.synchronize()
+    ek, ev = oracle.append_fp8(x["k_new"].unsqueeze(2), x["v_new"].unsqueeze(2), kc.numpy(),
+                               vc.numpy(), ks.numpy(), vs.numpy(), before, block_table=table)
+    assert np.array_equal(kd.cpu().numpy(), ek) and np.array_equal(vd.cpu().numpy(), ev)
+    ro, rl = oracle.decode_fp8(x["q"], ek, ev, ks.numpy(), vs.numpy(), after, x["scale"],
+                               block_table=table)
+    vals = torch.from_numpy(oracle.e4m3_values())
+    evt = torch.from_numpy(ev)
+    vmax = 0.0
+    for b in range(w.B):
+        L = int(after[b])
+        nb = (L + 15) // 16
+        rows = evt[table[b, :nb].long()].permute(1, 0, 2, 3).reshape(w.g, nb * 16, w.d)[:, :L]
+        vmax = max(vmax, float((vals[rows.long()] * vs.double().view(-1, 1, 1)).abs().max()))
+    e = check_parity(out, lse, ro, rl, vmax, "fp8 paged")
+    _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")

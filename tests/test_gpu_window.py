@@ -179,3 +179,46 @@ def test_ring_incremental_many_wraps():
         vmax = _vmax(v_host, lengths, n, window, True)
         check_parity(out, lse, ro, rl, vmax, f"ring step {step}")
         lengths = lengths + n
+
+
+@pytest.mark.parametrize("layout", ["linear", "ring", "paged"])
+def test_window_full_size(layout):
+    """A window of 1024 at the 70B GQA shape (linear cache, or a ring of
+    1039 slots) and on the paged GQA workload, one token per sequence, in
+    the launch configuration the benchmark times."""
+    window = 1024
+    ring, paged = layout == "ring", layout == "paged"
+    _log(f"case window_full {layout}")
+    if paged:
+        w = W.WORKLOADS["paged_gqa_bf16"]
+        x = W.make_paged(w)
+        k, v, table = x["k_pool"], x["v_pool"], x["block_table"]
+    else:
+        w = W.WORKLOADS["gqa_70b_bf16"]
+        x = W.make_contiguous(w, t_cap=window + 15 if ring else None)
+        k, v, table = x["k_cache"], x["v_cache"], None
+    before = x["seq_lens_before"]
+    q = x["q"].view(w.B, w.h, 1, w.d)
+    kn, vn = x["k_new"].view(w.B, w.g, 1, w.d), x["v_new"].view(w.B, w.g, 1, w.d)
+    kd, vd = dev(k), dev(v)
+    out, lse = kvc.decode_window(dev(q), kd, vd, dev(before), window, ring=ring,
+                                 block_table=dev(table) if paged else None, scale=x["scale"],
+                                 num_splits=w.num_splits, k_new=dev(kn), v_new=dev(vn))
+    torch.cuda.synchronize()
+    ek, ev = oracle.append_window(kn, vn, k, v, before, ring=ring, block_table=table)
+    assert np.array_equal(_raw(kd), ek.view(_raw(kd).dtype)), f"{layout}: cache after the step"
+    assert np.array_equal(_raw(vd), ev.view(_raw(vd).dtype)), f"{layout}: cache after the step"
+    k_host, v_host = _to_torch(ek, k), _to_torch(ev, v)
+    ro, rl = oracle.decode_window(q, k_host, v_host, before, x["scale"], window, ring=ring,
+                                  block_table=table)
+    vmax = 0.0
+    for b in range(w.B):  # max |V| over the window of the new token
+        hi = int(before[b]) + 1
+        pos = torch.arange(max(0, hi - window), hi)
+        if paged:
+            rows = v_host[table[b, pos // 16].long(), :, pos % 16]
+        else:
+            rows = v_host[b][:, pos % v_host.shape[2] if ring else pos]
+        vmax = max(vmax, float(rows.float().abs().max()))
+    e = check_parity(out, lse, ro, rl, vmax, f"window full {layout}")
+    _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
