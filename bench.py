@@ -182,9 +182,31 @@ def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0, fp8=None):
         if t_total >= budget_s or t_total / runs > budget_s / 2:
             break
     per_step = t_total / runs
+    # one single-threaded run of the same batch
+    t0 = time.perf_counter()
+    if fp8 is not None:
+        oracle.decode_fp8(x["q"], *fp8, x["seq_lens_after"], x["scale"],
+                          block_table=x["block_table"] if paged else None,
+                          block_size=x.get("block_size", 16), nthreads=1)
+    elif paged:
+        oracle.decode(x["q"], x["k_pool"], x["v_pool"], x["seq_lens_after"], x["scale"],
+                      block_table=x["block_table"], block_size=x["block_size"], nthreads=1)
+    else:
+        oracle.decode(x["q"], x["k_cache"], x["v_cache"], x["seq_lens_after"], x["scale"],
+                      nthreads=1)
+    single = time.perf_counter() - t0
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": w.B / per_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"full batch of the workload (B={w.B}), decode only, {runs} run(s), "
-                      f"{per_step:.3f} s per run"}
+                      f"{per_step:.3f} s per run",
+            "single_thread_value": w.B / single, "host_cpu": model}
 
 
 def bench_block_op(args, torch, kvc, W):
@@ -506,6 +528,32 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    # Secondary figures, outside the timed region: each of K steps timed on
+    # its own (median and spread), and the hot repeat (one cache copy over
+    # and over, so that caches may serve part of it).
+    def replay_one(i):
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            step(i)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(marks):
+        e0.record()
+        replay_one(i)
+        e1.record()
+    torch.cuda.synchronize()
+    each = sorted(e0.elapsed_time(e1) for e0, e1 in marks)
+    pct = lambda q: each[min(len(each) - 1, int(q * (len(each) - 1) + 0.5))]  # noqa: E731
+    h_start = torch.cuda.Event(enable_timing=True)
+    h_end = torch.cuda.Event(enable_timing=True)
+    h_start.record()
+    for _ in range(args.steps):
+        replay_one(0)
+    h_end.record()
+    torch.cuda.synchronize()
+    hot_ms = h_start.elapsed_time(h_end) / args.steps
+
     # The dominant kernel: decode calls alone, back to back on the launch
     # stream (a HIP graph holding one call per cache copy, replayed until at
     # least K calls ran), between two HIP events on that stream.
@@ -585,6 +633,10 @@ def main():
                  if nq > 1 else "one kvc_append_decode_attention call"),
         "step_hbm_gbs": round((nbytes["step"] if args.separate else nbytes["fused"])
                               / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_ms_each": {"p10": round(pct(0.1), 5), "p50": round(pct(0.5), 5),
+                         "p90": round(pct(0.9), 5), "samples": len(each),
+                         "note": "each step timed alone (includes its launch)"},
+        "hot_ms_per_step": round(hot_ms, 5),
         "timing": "eager" if args.eager else "HIP graphs of whole steps (one step per cache copy)",
         "roofline": {
             "bound": "hbm",
