@@ -50,13 +50,12 @@ constexpr int kVStageBytes = kTileTokens * kVRowBytes;  // 8 KB per wavefront
 constexpr int kOStride = kD + 4;                        // padded LDS row (floats)
 
 // Shared memory of a W-wavefront work-group: one V stage per wavefront,
-// reused after the walk for the pairwise merge of the wavefront states
-// (W/2 slots at the first level).
+// reused after the walk for the wavefront states (one slot each).
 template <int NQT, int W>
 struct Lds {
     static constexpr int kSlotFloats = 16 * NQT * kOStride + 3 * 16 * NQT;
     static constexpr int kStageBytes = W * kVStageBytes;
-    static constexpr int kMergeBytes = (W / 2) * kSlotFloats * 4;
+    static constexpr int kMergeBytes = W * kSlotFloats * 4;
     static constexpr int kBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
 };
 
@@ -478,11 +477,12 @@ struct MfmaEngine {
             lex[qt] += shfl_xor_f(lex[qt], 32);
         }
 
-        // ---- merge the wavefront states pairwise: waves [h, 2h) into
-        // waves [0, h) for h = W/2, ..., 1 ----
+        // ---- every wavefront stores its state; then all threads combine
+        // the W states of (query row, 4 dims) items and write them ----
         float* slots = reinterpret_cast<float*>(sh.lds);
         __syncthreads();  // every wavefront is done with its V staging area
-        auto store_state = [&](float* slot) {
+        {
+            float* slot = slots + wave * L::kSlotFloats;
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
                 const int qi = 16 * qt + col;
@@ -495,53 +495,34 @@ struct MfmaEngine {
                     slot[16 * NQT * kOStride + 32 * NQT + qi] = lex[qt];
                 }
             }
-        };
-        auto merge_state = [&](const float* slot) {
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) {
-                const int qi = 16 * qt + col;
-                const float mo = slot[16 * NQT * kOStride + qi];
-                const float lo = slot[16 * NQT * kOStride + 16 * NQT + qi];
-                const float xo = slot[16 * NQT * kOStride + 32 * NQT + qi];
-                float fa, fb, mnew;
-                rescale_pair(mrun[qt], mo, fa, fb, mnew);
-                mrun[qt] = mnew;
-                lacc[qt] = lacc[qt] * fa + lo * fb;
-                lex[qt] = lex[qt] * fa + xo * fb;
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt) {
-                    const f32x4_t o =
-                        *reinterpret_cast<const f32x4_t*>(slot + qi * kOStride + 16 * nt + 4 * G);
-                    acc[qt][nt] = acc[qt][nt] * fa + o * fb;
-                }
-            }
-        };
-#pragma unroll
-        for (int half = W / 2; half >= 1; half >>= 1) {
-            if (wave >= half && wave < 2 * half) store_state(slots + (wave - half) * L::kSlotFloats);
-            __syncthreads();
-            if (wave < half) merge_state(slots + wave * L::kSlotFloats);
-            __syncthreads();
         }
-        if (wave == 0) {
-            // ---- write: lane holds dims 16*nt + 4G + v of query 16*qt + col ----
+        __syncthreads();
+        constexpr int kQuads = kD / 4;
+        for (int it = tid; it < m * kQuads; it += 64 * W) {
+            const int qi = it / kQuads, d4 = it - qi * kQuads;
+            float mx = kNegInf;
 #pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) {
-                const int qi = 16 * qt + col;
-                if (qi >= m) continue;
-                const float l = lex[qt];
-                const float lr = lacc[qt][0];
-                float* o = dst.o + (long)qi * dst.o_stride;
-                const float inv = lr > 0.0f ? v_sc / lr : 0.0f;  // FP8: the V head scale
+            for (int w = 0; w < W; ++w) mx = fmaxf(mx, slots[w * L::kSlotFloats + 16 * NQT * kOStride + qi]);
+            const float ref = (mx == kNegInf) ? 0.0f : mx;
+            float lr = 0.0f, l = 0.0f;
+            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt)
-                    *reinterpret_cast<f32x4_t*>(o + 16 * nt + 4 * G) = acc[qt][nt] * inv;
-                if (G == 0) {
-                    float v;
-                    if (dst.final_) v = l > 0.0f ? (mrun[qt] + fast_log2(l)) * kLn2 : kNegInf;
-                    else v = l > 0.0f ? mrun[qt] + fast_log2(l) : kNegInf;
-                    dst.lse[(long)qi * dst.lse_stride] = v;
-                }
+            for (int w = 0; w < W; ++w) {
+                const float* slot = slots + w * L::kSlotFloats;
+                const float f = fast_exp2(slot[16 * NQT * kOStride + qi] - ref);  // 0 for empty states
+                lr += slot[16 * NQT * kOStride + 16 * NQT + qi] * f;
+                l += slot[16 * NQT * kOStride + 32 * NQT + qi] * f;
+                o += *reinterpret_cast<const f32x4_t*>(slot + qi * kOStride + 4 * d4) * f;
+            }
+            // out = sum of bf16(P) V / the sum of the same bf16(P); lse from
+            // the fp32 sum; FP8: times the V head scale
+            const float inv = lr > 0.0f ? v_sc / lr : 0.0f;
+            *reinterpret_cast<f32x4_t*>(dst.o + (long)qi * dst.o_stride + 4 * d4) = o * inv;
+            if (d4 == 0) {
+                float v;
+                if (dst.final_) v = l > 0.0f ? (mx + fast_log2(l)) * kLn2 : kNegInf;
+                else v = l > 0.0f ? mx + fast_log2(l) : kNegInf;
+                dst.lse[(long)qi * dst.lse_stride] = v;
             }
         }
     }
