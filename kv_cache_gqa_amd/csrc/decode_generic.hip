@@ -47,7 +47,10 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const PosRange ur = unit_range(a, raw);  // chunks cover [lo, hi)
     const int c0 = ur.lo + c * a.chunk_len;
     const bool single = a.num_chunks == 1;
-    if (c0 >= ur.hi && !single) return;  // chunk past the end: the merge skips it
+    if (c0 >= ur.hi && !single) {  // past the end: a record of weight 0 for the merge
+        if (lane == 0) a.part_lse[((long)b * a.h + i) * a.num_chunks + c] = kNegInf;
+        return;
+    }
     // row i is token i % n, which sees [window_lo(vis), vis)
     const int vis = visible_len(a, raw, i % a.n);
     const int p0 = max(c0, window_lo(a, vis));

@@ -341,7 +341,10 @@ __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
     const int p0 = ur.lo + c * a.chunk_len;
     const int p1 = min(p0 + a.chunk_len, ur.hi);
     const bool single = a.num_chunks == 1;
-    if (p0 >= ur.hi && !single) return;  // past the end: the merge skips this chunk
+    if (p0 >= ur.hi && !single) {  // past the end: a record of weight 0 for the merge
+        mark_empty_rows(chunk_dst(a, b, j, c), M, threadIdx.x);
+        return;
+    }
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
 }
 

@@ -165,6 +165,13 @@ __device__ __forceinline__ SegDst chunk_dst(const DecodeArgs& a, int b, int j, i
                   (long)a.num_chunks * a.d, (long)a.num_chunks, false};
 }
 
+// A chunk that starts past the end of its unit: its `rows` partial rows get
+// lse = -inf (weight 0), so that the merge reads every chunk's record at
+// once without first reading the sequence length.
+__device__ __forceinline__ void mark_empty_rows(const SegDst& dst, int rows, int tid) {
+    if (tid < rows) dst.lse[(long)tid * dst.lse_stride] = kNegInf;
+}
+
 // Stream mode: record `slot` (0 = first segment, 1 = last) of this work-group.
 __device__ __forceinline__ SegDst stream_dst(const DecodeArgs& a, int slot) {
     const long rec = ((long)blockIdx.x * 2 + slot) * a.m;

@@ -7,7 +7,8 @@
 // sequence-dimension parallelism creates:
 //   M = max_c lse2_c,  w_c = 2^(lse2_c - M),
 //   out = sum_c w_c O_c / sum_c w_c,  lse = (M + log2 sum_c w_c) ln 2.
-// Only chunks that hold positions of the sequence are read; a sequence of
+// Chunked plans: every chunk has a record (chunks past the end of a unit
+// hold lse = -inf), so a row's records are all loaded at once; a sequence of
 // length 0 gets out = 0 and lse = -inf.
 #include "kvc_schedule.h"
 
@@ -83,7 +84,8 @@ __device__ __forceinline__ void write_row(const DecodeArgs& a, long row, int lan
 // (cg = t / nE, G = 256 / nE chunk groups), folds them in eight per round
 // trip with online rescaling, and the G partial states are combined through
 // LDS.  All loads of a row are independent of each other, so a row costs
-// about one memory round trip after its length is known.
+// about one memory round trip.  The O of a record of weight 0 is not used
+// (chunks past the end leave it unwritten).
 template <int V>
 __device__ __forceinline__ void merge_row_chunked(const DecodeArgs& a, long row) {
     __shared__ float sm_m[256];
@@ -94,9 +96,7 @@ __device__ __forceinline__ void merge_row_chunked(const DecodeArgs& a, long row)
     const int G = 256 / nE;
     const int t = threadIdx.x;
     const int cg = t / nE, e = t - (t / nE) * nE;
-    const int b = (int)(row / a.h);
-    const PosRange ur = unit_range(a, a.seq_lens[b]);
-    const int nc = (ur.hi - ur.lo + a.chunk_len - 1) / a.chunk_len;  // chunks that hold positions
+    const int nc = C;
     if (cg < G) {
         float M = kNegInf, W = 0.0f, o[V];
 #pragma unroll
@@ -130,10 +130,10 @@ __device__ __forceinline__ void merge_row_chunked(const DecodeArgs& a, long row)
             for (int v = 0; v < V; ++v) o[v] *= f;
 #pragma unroll
             for (int k = 0; k < kMergeBatch; ++k) {
-                const float w = fast_exp2(lse[k] - ref);  // 0 for absent chunks
+                const float w = fast_exp2(lse[k] - ref);  // 0 for absent and empty chunks
                 W += w;
 #pragma unroll
-                for (int v = 0; v < V; ++v) o[v] += w * x[k][v];
+                for (int v = 0; v < V; ++v) o[v] += w > 0.0f ? w * x[k][v] : 0.0f;
             }
             M = bm;
         }
