@@ -1,7 +1,9 @@
-// decode_mfma.hip -- bf16, head_dim 128, query groups of m = h/g in [4, 32].
+// decode_mfma.hip -- bf16 or FP8 caches, head_dim 128, 4 to 32 query rows
+// per KV head (more rows run as 32-row slices).
 //
-// A work-group of four wavefronts computes one segment at a time: the m
-// query heads j*m..j*m+m-1 that share KV head j of sequence b
+// A work-group of W = 4 or 8 wavefronts computes one segment at a time: the
+// m query heads j*m..j*m+m-1 (times n new tokens) that share KV head j of
+// sequence b
 // ("大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com) section 三 3.3)
 // over a range of positions, so every K/V byte is read once.  With m >= 4 the
 // group's queries times a tile of positions is a real dense product, so both
@@ -32,8 +34,12 @@
 // read 8 contiguous bytes each of one V row r, and lane i receives element i
 // of each of the four rows -- one dim of four positions, the MFMA A layout.
 //
-// K and V are read with streaming (non-temporal) loads, double-buffered: the
-// next 32-position sub-tile is in flight while the current one is computed.
+// K and V are read with streaming (non-temporal) loads while the next
+// 32-position sub-tile is in flight: double-buffered registers for 16 bf16
+// query rows, one set reloaded in place for 32 rows and for the 4-wavefront
+// FP8 kernels (register budget and residency at MfmaEngine and
+// MfmaOccupancy below).  At the end of a segment the W wavefront states go to
+// LDS and all threads combine them.
 //
 // Two entry points share the segment code: a chunked grid (chunk, KV head,
 // sequence) and the persistent stream grid of kvc_schedule.h.

@@ -1,4 +1,5 @@
-// decode_valu.hip -- bf16, head_dim 128, small query groups (m = h/g <= 3).
+// decode_valu.hip -- bf16 or FP8 caches, head_dim 128, small query groups
+// (at most 3 query rows per KV head).
 //
 // A work-group of four wavefronts computes one segment at a time: the m
 // query heads that share KV head j of sequence b ("大语言模型研究15——注意力
@@ -10,7 +11,8 @@
 // Lane layout: lane l covers dims [8*(l%16), 8*(l%16)+8) of position
 // (l/16) + 4u of the current 32-position sub-tile, u = 0..7.  One 16-byte
 // load per lane per u reads four whole 256-byte K (or V) rows per wavefront
-// instruction, fully coalesced, as streaming (non-temporal) loads.  q.k is
+// instruction (FP8: 8 bytes, four 128-byte rows), fully coalesced, as
+// streaming (non-temporal) loads.  q.k is
 // v_dot2_f32_bf16 on the raw bf16 pairs, summed over the 16 lanes of a row
 // with DPP.  Each row of 16 lanes keeps its own online-softmax state (m, l,
 // acc) ("KV Cache 优化与注意力机制加速" (plumephp.com) section 2.2); the four

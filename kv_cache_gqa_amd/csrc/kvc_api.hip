@@ -7,15 +7,6 @@
 
 #include "kvc_internal.h"
 
-#ifndef KVC_STREAM_WG_CAP
-#define KVC_STREAM_WG_CAP kStreamMaxWgPerCu
-#endif
-// 1: automatic chunking of contiguous caches may use one wide work-group per
-// (sequence, KV head) instead of split chunks plus a merge pass.
-#ifndef KVC_AUTO_WIDE
-#define KVC_AUTO_WIDE 1
-#endif
-
 namespace kvc {
 
 static long ceil_div(long a, long b) { return (a + b - 1) / b; }
@@ -172,7 +163,7 @@ static int resident_wgs(const void* fn, int threads) {
 // workspace bound).  0 when the kernel cannot be resident at all.
 static long device_slots(const void* fn, int waves) {
     int per_cu = resident_wgs(fn, 64 * waves);
-    if (per_cu > KVC_STREAM_WG_CAP) per_cu = KVC_STREAM_WG_CAP;
+    if (per_cu > kStreamMaxWgPerCu) per_cu = kStreamMaxWgPerCu;
     int cus = device_cus();
     if (cus > kStreamMaxCUs) cus = kStreamMaxCUs;
     return (long)cus * per_cu;
@@ -208,13 +199,11 @@ static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, b
     const void* f4 = kernel_for(kind, m, paged, false, 4, gen, kv8);
     const long slots4 = device_slots(f4, 4);
     AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};
-#if KVC_AUTO_WIDE
     const int wv = 8;
     const void* fn = kernel_for(kind, m, paged, false, wv, gen, kv8);
     const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
     if (slots > 0 && units >= slots && slots * wv >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
         return AutoShape{wv, 1};
-#endif
     return split;
 }
 
