@@ -307,3 +307,53 @@ def test_device_values_are_clamped_not_faulting():
     kvc.append(dev(x["k_new"]), dev(x["v_new"]), kc, vc,
                dev(torch.tensor([48, -1], dtype=torch.int32)))
     assert torch.equal(kc.cpu(), before)
+
+
+@pytest.mark.parametrize("shape", [KERNEL_SHAPES[0], KERNEL_SHAPES[4], KERNEL_SHAPES[7],
+                                   KERNEL_SHAPES[8]],
+                         ids=["valu_m1", "mfma_m8", "mfma_m32", "generic_m64"])
+@pytest.mark.parametrize("num_splits", [0, 3, -1])
+@pytest.mark.parametrize("paged", [False, True])
+def test_position_ramp(shape, num_splits, paged):
+    """V[p] = p mod 64 in every dim (exact in bf16).  With scale 0 every
+    attended position has the same weight, so out equals the mean of
+    (p mod 64) over exactly the attended positions (a dropped, repeated or
+    shifted position moves it) and lse = ln L; with the usual scale the
+    result matches the oracle."""
+    name, s = shape
+    _log(f"case ramp {name} splits={num_splits} paged={paged}")
+    lengths = torch.tensor([1, 17, 33, 64, 255, 1000, 4097, 0], dtype=torch.int32)
+    B = len(lengths)
+    w = W.Workload(name, B=B, seed=330, **s)
+    x = W.make_contiguous(w, lengths=lengths, fill=float("nan"))
+    T = x["v_cache"].shape[2]
+    ramp = (torch.arange(T) % 64).to(torch.float32)
+    vr = ramp.view(1, 1, T, 1).expand(B, w.g, T, w.d).to(x["v_cache"].dtype).clone()
+    vr[torch.arange(T).view(1, 1, T, 1).expand(B, w.g, T, w.d) >= lengths.view(-1, 1, 1, 1)] = \
+        float("nan")
+    x["v_cache"] = vr
+    if paged:
+        table, nb = W.make_block_table(lengths, 16, perm_seed=331, extra_blocks=3)
+        kp = W.scatter_to_pool(x["k_cache"], lengths, table, nb, 16, fill=float("nan"))
+        vp = W.scatter_to_pool(x["v_cache"], lengths, table, nb, 16, fill=float("nan"))
+        call = lambda sc: kvc.decode_paged(dev(x["q"]), dev(kp), dev(vp), dev(table),  # noqa: E731
+                                           dev(lengths), scale=sc, num_splits=num_splits)
+    else:
+        call = lambda sc: kvc.decode(dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]),  # noqa: E731
+                                     dev(lengths), scale=sc, num_splits=num_splits)
+    out, lse = call(0.0)
+    for b in range(B):
+        L = int(lengths[b])
+        o, l = out[b].cpu().double(), lse[b].cpu().double()
+        if L == 0:
+            assert torch.all(o == 0) and torch.all(torch.isinf(l) & (l < 0)), name
+            continue
+        # every weight is exactly 1 and the sums are integers below 2^24: the
+        # mean is exact up to float32 rounding, so one dropped position (which
+        # moves it by |ramp[p] - mean| / L) shows
+        mean = float(ramp[:L].double().mean())
+        assert float((o - mean).abs().max()) <= 1e-4, (name, b, L, float((o - mean).abs().max()))
+        assert float((l - np.log(L)).abs().max()) <= 1e-4, (name, b, L)
+    out, lse = call(x["scale"])
+    ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], lengths, x["scale"])
+    check_parity(out, lse, ro, rl, 63.0, name + "/ramp")
