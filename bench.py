@@ -415,7 +415,7 @@ def main():
     split_mode, chunk_len, num_chunks = kvc.plan(w.B, hq, w.g, w.d, max_len, ns,
                                                  dtype=w.torch_dtype, paged=w.paged)
     waves, n_wgs, launch_chunk, launch_chunks = kvc.launch_shape(
-        w.B, hq, w.g, w.d, max_len, ns, dtype=w.torch_dtype, paged=w.paged)
+        w.B, hq, w.g, w.d, max_len, ns, dtype="fp8" if fp8 else w.torch_dtype, paged=w.paged)
     merged = split_mode == "stream" or launch_chunks > 1
 
     if args.calibration_copy_mib > 0:

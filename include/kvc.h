@@ -70,7 +70,11 @@ typedef enum kvc_status {
     KVC_ERR_HIP = 4           /* a HIP launch reported an error */
 } kvc_status;
 
-typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+/* KVC_FP8_E4M3 is for the planning queries only (kvc_decode_plan,
+ * kvc_decode_workspace_bytes, kvc_decode_launch_shape): bf16 queries over an
+ * FP8 E4M3 cache, the *_fp8 entry points.  Plans and workspaces are those of
+ * KVC_BF16; the launch shape is the FP8 kernels' own. */
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1, KVC_FP8_E4M3 = 2 } kvc_dtype;
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
 int kvc_version(void);

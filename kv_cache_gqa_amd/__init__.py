@@ -155,9 +155,14 @@ def _check(fn: str, status: int):
         raise KvcError(fn, status)
 
 
+FP8_E4M3 = 2  # planning queries only: bf16 queries over an FP8 E4M3 cache
+
+
 def _code(dtype) -> int:
     if isinstance(dtype, int):
         return dtype
+    if dtype in ("fp8", "fp8_e4m3", torch.float8_e4m3fn):
+        return FP8_E4M3
     return BF16 if dtype in (torch.bfloat16, "bf16") else F32
 
 

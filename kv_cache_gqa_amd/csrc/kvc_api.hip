@@ -186,8 +186,10 @@ static double fill(long wgs, long slots) {
 //                partial results and no merge pass;
 //   chunks       4-wavefront work-groups, ceil(slots / units) chunks per
 //                unit, merged afterwards.
-// Whole units win when they keep at least as many wavefronts per CU resident
-// and the grid fills the slots nearly as well (>= 7/8 of slot-rounds busy).
+// Whole units win when they keep at least as many tiles in flight per CU
+// (resident wavefronts, counted twice for the 8-wavefront FP8 kernel, which
+// loads two tiles per step) and the grid fills the slots nearly as well
+// (>= 7/8 of slot-rounds busy).
 struct AutoShape {
     int waves;
     long chunks;
@@ -202,7 +204,9 @@ static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, b
     const int wv = 8;
     const void* fn = kernel_for(kind, m, paged, false, wv, gen, kv8);
     const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
-    if (slots > 0 && units >= slots && slots * wv >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
+    // resident tiles in flight: the 8-wavefront FP8 kernel loads two per step
+    const long inflight = slots * wv * (kind == kMfma && kv8 ? 2 : 1);
+    if (slots > 0 && units >= slots && inflight >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
         return AutoShape{wv, 1};
     return split;
 }
@@ -335,6 +339,7 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
     if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
         max_seq_len < 0)
         return KVC_ERR_INVALID;
+    if (dtype == KVC_FP8_E4M3) dtype = KVC_BF16;  // the same plans
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
     if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : (sc.auto_chunks ? KVC_SPLIT_AUTO_CHUNKS : KVC_SPLIT_CHUNKS);
@@ -349,11 +354,14 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
         max_seq_len <= 0)
         return KVC_ERR_INVALID;
+    const bool kv8 = dtype == KVC_FP8_E4M3;
+    if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     if (d > 256) return KVC_ERR_UNSUPPORTED;
     Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
     DecodeArgs a{};
     a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.n = 1; a.cap_len = max_seq_len;
+    a.kv8 = kv8 ? 1 : 0;
     resolve_launch(a, sc, paged != 0, max_seq_len);
     if (waves) *waves = a.waves;
     // the generic kernel: one wavefront per query row; the others: per unit
@@ -370,6 +378,7 @@ size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max
     if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
         max_seq_len < 0)
         return 0;
+    if (dtype == KVC_FP8_E4M3) dtype = KVC_BF16;  // the same workspaces
     if (dtype != KVC_F32 && dtype != KVC_BF16) return 0;
     return required_workspace(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
 }

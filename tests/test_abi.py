@@ -294,3 +294,16 @@ def test_fp8_validation_codes():
     for i in (1, 2, 5, 6):
         bad = list(fpargs); bad[i] = None
         assert fpp(*bad) == INVALID
+
+
+def test_fp8_planning_dtype_plans_like_bf16():
+    """KVC_FP8_E4M3 in the planning queries: the plans and workspaces of bf16."""
+    lib = kvc.load_library()
+    for shape in [(32, 64, 8, 128, 4112, 0, 0), (64, 32, 8, 128, 8208, 0, 1), (4, 32, 1, 128, 131088, 64, 0),
+                  (3, 8, 2, 128, 5000, 3, 1), (2, 8, 2, 64, 100, -1, 0)]:
+        B, h, g, d, L, ns, paged = shape
+        assert kvc.plan(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
+            kvc.plan(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
+        assert kvc.workspace_bytes(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
+            kvc.workspace_bytes(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
+    assert lib.kvc_decode_plan(2, 8, 2, 128, 3, 64, 0, 0, None, None, None) == UNSUPPORTED

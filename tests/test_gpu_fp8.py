@@ -227,3 +227,14 @@ def test_fp8_full_size_paged():
         vmax = max(vmax, float((vals[rows.long()] * vs.double().view(-1, 1, 1)).abs().max()))
     e = check_parity(out, lse, ro, rl, vmax, "fp8 paged")
     _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
+
+
+def test_fp8_launch_shape_70b():
+    """The 70B GQA shape with an FP8 cache runs one 8-wavefront work-group
+    per (sequence, KV head) on a 256-CU device (the FP8 8-wavefront kernel
+    keeps two tiles in flight per wavefront), with no merge pass."""
+    w = W.WORKLOADS["gqa_70b_bf16"]
+    waves, wgs, cl, nc = kvc.launch_shape(w.B, w.h, w.g, w.d, w.T + 16, 0, dtype="fp8")
+    _log(f"case fp8_launch_shape waves={waves} wgs={wgs} chunks={nc}")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (waves, wgs, nc) == (8, w.B * w.g, 1)
