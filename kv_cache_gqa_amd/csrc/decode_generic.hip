@@ -4,11 +4,15 @@
 // d=1 worked example).
 //
 // One wavefront per (chunk, query head, sequence).  Lane k holds dims k,
-// k+64, k+128, k+192.  Positions are visited one at a time: the partial dot
-// products are summed across the wave, then the online-softmax update of
-// "KV Cache 优化与注意力机制加速" (plumephp.com) section 2.2 is applied:
-// m' = max(m, s), l' = l exp(m - m') + exp(s - m'), acc' = acc exp(m - m') +
-// exp(s - m') V_p, all in base 2.  Query head i reads KV head
+// k+64, k+128, k+192; positions go in batches of eight (one round trip to
+// memory per batch).  A call that appends reads its new tokens (positions
+// seq_lens[b] ..) from k_new / v_new (FP8: as their codes), and the first
+// query row of each KV head's group writes its chunk's new positions into
+// their cache slots.  For each batch the partial dot products are summed
+// across the wave, then the online-softmax update of "KV Cache 优化与注意力
+// 机制加速" (plumephp.com) section 2.2 is applied once for the batch:
+// m' = max(m, max_p s_p), l' = l exp(m - m') + sum_p exp(s_p - m'),
+// acc' = acc exp(m - m') + sum_p exp(s_p - m') V_p, all in base 2.  Query head i reads KV head
 // floor(i*g/h) ("大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com),
 // section 三 3.3).
 #include "kvc_device.h"
@@ -35,8 +39,17 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// The value a new element x takes in the cache: itself, or (FP8) the value
+// of its code for the head's scale, as the FP8 append kernel stores it.
+template <typename T>
+__device__ __forceinline__ float new_value(float x, float scale) {
+    if constexpr (sizeof(T) == 1) return e4m3_to_f32((uint8_t)e4m3_encode(x / scale));
+    else return x;
+}
+
 // TQ: query element type; T: cache element type (uint8_t: FP8 E4M3 codes
-// with a float32 scale per KV head, folded into the query and the output).
+// with a float32 scale per KV head, folded into the query and the output;
+// k_new / v_new are then bf16, TQ).
 template <typename TQ, typename T>
 __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
@@ -61,6 +74,38 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const T* V = (const T*)a.v;
     const float k_sc = a.kv8 ? a.k_scale[j] : 1.0f;
     const float v_sc = a.kv8 ? a.v_scale[j] : 1.0f;
+    // new tokens: element type of k_new / v_new, their rows, cache rows
+    using TN = typename std::conditional<sizeof(T) == 1, TQ, T>::type;
+    const bool appends = a.k_new != nullptr;
+    const long new_base = ((long)b * a.g + j) * a.n - raw;  // k_new row of position p: new_base + p
+    const long contig_base = ((long)b * a.g + j) * a.t_cap;
+    if (appends && i == j * a.m) {
+        // this chunk's new positions go to their cache slots (skipped, as the
+        // append kernels skip them, when a paged table entry is not a block)
+        const int s0 = max(c0, raw), s1 = min(c0 + a.chunk_len, ur.hi);
+        for (int p = s0; p < s1; ++p) {
+            long row;
+            if (a.block_table != nullptr) {
+                const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+                if (phys < 0 || phys >= a.num_blocks) continue;
+                row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+            } else {
+                row = contig_base + cache_slot(a, p);
+            }
+            for (int dim = lane; dim < d; dim += 64) {
+                const long src = (new_base + p) * d + dim;
+                if constexpr (sizeof(T) == 1) {
+                    const float x = load_f((const TN*)a.k_new, src);
+                    const float y = load_f((const TN*)a.v_new, src);
+                    const_cast<T*>(K)[row * d + dim] = (T)e4m3_encode(x / k_sc);
+                    const_cast<T*>(V)[row * d + dim] = (T)e4m3_encode(y / v_sc);
+                } else {
+                    const_cast<T*>(K)[row * d + dim] = ((const T*)a.k_new)[src];
+                    const_cast<T*>(V)[row * d + dim] = ((const T*)a.v_new)[src];
+                }
+            }
+        }
+    }
     float qv[4], acc[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -69,31 +114,61 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         acc[kk] = 0.0f;
     }
     float m = kNegInf, l = 0.0f;
-    const long contig_base = ((long)b * a.g + j) * a.t_cap;
-    for (int p = p0; p < p1; ++p) {
-        long row;
+    // Positions go in batches of kBatch: the K and V loads of a batch are
+    // issued together, so a batch costs one memory round trip.
+    constexpr int kBatch = 8;
+    auto row_of = [&](int p, bool fresh) -> long {
+        if (fresh) return new_base + p;  // a row of k_new / v_new
         if (a.block_table != nullptr) {
             int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
             phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
-            row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
-        } else {
-            row = contig_base + cache_slot(a, p);
+            return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
         }
-        float part = 0.0f;
+        return contig_base + cache_slot(a, p);
+    };
+    for (int pb = p0; pb < p1; pb += kBatch) {
+        float kx[kBatch][4], vx[kBatch][4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int dim = lane + 64 * kk;
-            if (dim < d) part += qv[kk] * load_f(K, row * d + dim);
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = min(pb + u, p1 - 1);  // past the end: repeat the last position (masked)
+            const bool fresh = appends && p >= raw;  // uniform over the wavefront
+            const long row = row_of(p, fresh);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int dim = lane + 64 * kk;
+                kx[u][kk] = vx[u][kk] = 0.0f;
+                if (dim < d) {
+                    if (fresh) {
+                        kx[u][kk] = new_value<T>(load_f((const TN*)a.k_new, row * d + dim), k_sc);
+                        vx[u][kk] = new_value<T>(load_f((const TN*)a.v_new, row * d + dim), v_sc);
+                    } else {
+                        kx[u][kk] = load_f(K, row * d + dim);
+                        vx[u][kk] = load_f(V, row * d + dim);
+                    }
+                }
+            }
         }
-        const float s = wave_sum(part);
-        const float mnew = fmaxf(m, s);
-        const float alpha = fast_exp2(m - mnew);  // m = -inf on the first position -> 0
-        const float pw = fast_exp2(s - mnew);
-        l = l * alpha + pw;
+        float sc[kBatch];
+        float bmax = kNegInf;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int dim = lane + 64 * kk;
-            if (dim < d) acc[kk] = acc[kk] * alpha + pw * load_f(V, row * d + dim);
+        for (int u = 0; u < kBatch; ++u) {
+            float part = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) part += qv[kk] * kx[u][kk];
+            sc[u] = pb + u < p1 ? wave_sum(part) : kNegInf;
+            bmax = fmaxf(bmax, sc[u]);
+        }
+        const float mnew = fmaxf(m, bmax);
+        const float alpha = fast_exp2(m - mnew);  // m = -inf on the first batch -> 0
+        l *= alpha;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc[kk] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const float pw = fast_exp2(sc[u] - mnew);  // 0 for masked positions
+            l += pw;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc[kk] += pw * vx[u][kk];
         }
         m = mnew;
     }

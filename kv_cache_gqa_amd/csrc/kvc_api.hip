@@ -274,23 +274,6 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
     if (a.B == 0) return KVC_OK;
     resolve_launch(a, sc, paged, max_len);
-    if (a.len_add != 0 && sc.kind == kGeneric) {
-        // The generic kernel does not take the new token itself: append it
-        // first, then attend over the cache.
-        const int eb = dtype == KVC_F32 ? 4 : 2;
-        const int capacity = paged ? a.num_blocks : a.t_cap;
-        const hipError_t e =
-            a.kv8 ? launch_append_fp8(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
-                                      a.k_scale, a.v_scale, a.block_table, a.max_blocks,
-                                      a.block_size, a.seq_lens, a.B, a.g, a.n, a.d, capacity,
-                                      a.ring, stream)
-                  : launch_append(a.k_new, a.v_new, const_cast<void*>(a.k), const_cast<void*>(a.v),
-                                  a.block_table, a.max_blocks, a.block_size, a.seq_lens, a.B, a.g,
-                                  a.n, a.d, capacity, a.ring, eb, stream);
-        if (e != hipSuccess) return KVC_ERR_HIP;
-        a.k_new = nullptr;
-        a.v_new = nullptr;
-    }
     const size_t rows = workspace_rows(a.B, a.h, a.g, sc);
     if (rows > 0) {
         char* w = static_cast<char*>(workspace);
