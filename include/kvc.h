@@ -202,6 +202,8 @@ int kvc_decode_attention(const void* q, const void* k_cache, const void* v_cache
  *                   (n+1)*block_size) of sequence b.  Entries past the last
  *                   block a sequence uses are never read.
  *   block_size      power of two, 8..256
+ *   num_blocks      blocks in each pool; num_blocks * g * block_size must
+ *                   not exceed 2^32 - 1 (KVC_ERR_UNSUPPORTED otherwise)
  *   seq_lens        device int32 [B], 0..max_blocks*block_size
  *   other arguments as kvc_decode_attention; the workspace size uses
  *   max_seq_len = max_blocks * block_size and paged = 1.

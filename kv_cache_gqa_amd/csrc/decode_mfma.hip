@@ -116,7 +116,7 @@ struct MfmaEngine {
     // 4-wavefront FP8 kernels, three.
     static constexpr bool kSingleBuffer = NQT >= 2 || (KV8 && W == 4);
     struct Shared {
-        int tbl[PAGED ? kMaxTableSlice : 1];
+        uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
         __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     };
 
@@ -130,10 +130,6 @@ struct MfmaEngine {
         const int m = min(a.m - row0, 16 * NQT);  // rows of this slice
         __syncthreads();  // the previous segment is done with the shared memory
 
-        const uint16_t* K = (const uint16_t*)a.k;
-        const uint16_t* Vc = (const uint16_t*)a.v;
-        const unsigned char* K8 = (const unsigned char*)a.k;
-        const unsigned char* V8 = (const unsigned char*)a.v;
         const uint16_t* Q = (const uint16_t*)a.q;
 
         // B operand of Q K^T: query column 16*qt + col; chunk ks holds dims
@@ -167,20 +163,37 @@ struct MfmaEngine {
 
         unsigned char* vst = sh.lds + wave * kVStageBytes;
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
-        long cbase = bj_base;  // row of position 0 in the current window (ring: shifted)
         const float k_sc = KV8 ? a.k_scale[j] : 1.0f;  // FP8 head scales
         const float v_sc = KV8 ? a.v_scale[j] : 1.0f;
         const float sl2 = a.scale_log2e * k_sc;
-        const int* tbl = sh.tbl;
-        int blk0 = 0;
+        int blk0 = 0;  // first block of the current window (paged)
+        int w0 = s;  // start of the current window
         int w1 = e;  // end of the current window
 
-        auto kv_row = [&](int p) -> long {
+        // Rows of K/V: paged, the row of position p in the pool (the table
+        // slice holds each block's first row for head j; a pool of 2^32 rows
+        // exceeds any device); contiguous, p - w0 from the window's first row
+        // (kwin / vwin), so that a load is a uniform base plus a 32-bit
+        // offset.  A lane reads bytes klane.. of K rows and vlane.. of V rows
+        // (plus constant offsets): row_ptr(lane offset, r, constant).
+        constexpr int kRowBytes = KV8 ? kD : 2 * kD;
+        const char* kwin = (const char*)a.k;
+        const char* vwin = (const char*)a.v;
+        const uint32_t klane = 16 * G;                 // K chunk of the lane
+        const uint32_t vlane = (KV8 ? 8 : 16) * col;  // V chunk of the lane
+        auto kv_row = [&](int p) -> uint32_t {
+            if (PAGED) return sh.tbl[(p >> a.log2_bs) - blk0] + (uint32_t)(p & (a.block_size - 1));
+            return (uint32_t)(p - w0);
+        };
+        auto row_ptr = [&](const char* base, uint32_t lane_off, uint32_t r, int off) -> const void* {
             if (PAGED) {
-                const int phys = tbl[(p >> a.log2_bs) - blk0];
-                return ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+                // one shift-and-add for the 64-bit address, kept in the
+                // global address space
+                using gchar = const __attribute__((address_space(1))) char;
+                gchar* g = (gchar*)(((uint64_t)r << (KV8 ? 7 : 8)) + (uint64_t)base);
+                return (const char*)(g + (lane_off + off));
             }
-            return cbase + p;
+            return base + (r * (uint32_t)kRowBytes + lane_off) + off;
         };
 
         // Query column 16*qt + col is token (row0 + 16*qt + col) % n, which
@@ -212,8 +225,8 @@ struct MfmaEngine {
         const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
         const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
-        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
-        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
+        const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : Q;
+        const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Q;
 
         // Loads of the 32-position sub-tile at t0; positions are clamped to
         // the window's last one, so a sub-tile past the end stays in bounds.
@@ -227,13 +240,13 @@ struct MfmaEngine {
         auto load_k = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const long row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
+                const uint32_t row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
                 if constexpr (KV8) {
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) tr.k[tt][hh] = ld16_kv(K8 + row * kD + 64 * hh + 16 * G);
+                    for (int hh = 0; hh < 2; ++hh) tr.k[tt][hh] = ld16_kv(row_ptr(kwin, klane, row, 64 * hh));
                 } else {
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16_kv(K + row * kD + 32 * ks + 8 * G);
+                    for (int ks = 0; ks < 4; ++ks) tr.k[tt][ks] = ld16_kv(row_ptr(kwin, klane, row, 64 * ks));
                 }
             }
         };
@@ -241,9 +254,9 @@ struct MfmaEngine {
         auto load_v = [&](int t0, TileRegs<KV8>& tr) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const long row = kv_row(min(t0 + 4 * u + G, w1 - 1));
-                if constexpr (KV8) tr.v[u] = ld8_kv(V8 + row * kD + 8 * col);
-                else tr.v[u] = ld16_kv(Vc + row * kD + 8 * col);
+                const uint32_t row = kv_row(min(t0 + 4 * u + G, w1 - 1));
+                if constexpr (KV8) tr.v[u] = ld8_kv(row_ptr(vwin, vlane, row, 0));
+                else tr.v[u] = ld16_kv(row_ptr(vwin, vlane, row, 0));
             }
         };
         auto load_tile = [&](int t0, TileRegs<KV8>& tr) {
@@ -392,20 +405,25 @@ struct MfmaEngine {
 
         // Windows of at most kMaxChunk positions, so that a window's slice of
         // the block table fits in shared memory.
-        for (int w0 = s; w0 < e_cache; w0 = w1) {
+        for (w0 = s; w0 < e_cache; w0 = w1) {
             w1 = min(e_cache, w0 + kMaxChunk);
-            if (GEN && !PAGED && a.ring) {
-                // a window never wraps around the ring: slot = p - wbase in it
-                const int wbase = w0 - w0 % a.t_cap;
-                w1 = min(w1, wbase + a.t_cap);
-                cbase = bj_base - wbase;
-            }
-            if (PAGED) {
+            if (!PAGED) {
+                long first = bj_base + w0;  // row of position w0
+                if (GEN && a.ring) {
+                    // a window never wraps around the ring: slot = p - wbase in it
+                    const int wbase = w0 - w0 % a.t_cap;
+                    w1 = min(w1, wbase + a.t_cap);
+                    first -= wbase;
+                }
+                kwin = (const char*)a.k + first * kRowBytes;
+                vwin = (const char*)a.v + first * kRowBytes;
+            } else {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
                 for (int t = tid; t < nblk; t += 64 * W) {
-                    const int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
-                    sh.tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                    int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
+                    ph = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                    sh.tbl[t] = ((uint32_t)ph * (uint32_t)a.g + (uint32_t)j) * (uint32_t)a.block_size;
                 }
                 __syncthreads();
             }

@@ -439,6 +439,8 @@ static int decode_paged(const void* q, const void* k_new, const void* v_new, con
     const long cap = (long)max_blocks * block_size;
     if (cap > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;
     if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
+    // the kernels index pool rows (block, KV head, position) in 32 bits
+    if ((long)num_blocks * g * block_size > 0xffffffffL) return KVC_ERR_UNSUPPORTED;
     DecodeArgs a{};
     a.q = q; a.k = k_pool; a.v = v_pool; a.seq_lens = seq_lens;
     a.block_table = block_table; a.max_blocks = max_blocks; a.block_size = block_size;

@@ -139,6 +139,9 @@ def test_paged_validation_codes():
     assert call(nb=0) == INVALID
     assert call(h=6, g=4) == INVALID
     assert call(splits=2) == WORKSPACE
+    # pool rows (num_blocks * g * block_size) are indexed in 32 bits
+    assert call(nb=(1 << 31) - 1, g=2, h=8, bs=16) == UNSUPPORTED
+    assert call(nb=(1 << 27) - 1, g=2, h=8, bs=16, splits=2) == WORKSPACE  # 2^32 - 32 rows: accepted
 
 
 def test_append_validation_codes():
