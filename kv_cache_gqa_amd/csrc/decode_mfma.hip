@@ -51,6 +51,8 @@ namespace kvc {
 namespace {
 
 constexpr int kD = 128;
+// log2 of the largest softmax weight P before the reference maximum moves
+constexpr float kLazyRescale = 8.0f;
 constexpr int kVRowBytes = kD * 2;                      // 256
 constexpr int kVStageBytes = kTileTokens * kVRowBytes;  // 8 KB per wavefront
 constexpr int kOStride = kD + 4;                        // padded LDS row (floats)
@@ -360,13 +362,22 @@ struct MfmaEngine {
                 for (int k = 1; k < 8; ++k) mt = fmaxf(mt, sv[k]);
                 mt = fmaxf(mt, shfl_xor_f(mt, 16));
                 mt = fmaxf(mt, shfl_xor_f(mt, 32));
-                const float mnew = fmaxf(mrun[qt], mt);
-                const float ref = (mnew == kNegInf) ? 0.0f : mnew;
-                const float alpha = fast_exp2(mrun[qt] - ref);
-                mrun[qt] = mnew;
+                // The reference mrun moves (and the running sums are
+                // rescaled) only when some lane's tile maximum passes it by
+                // more than kLazyRescale; otherwise P = 2^(s - mrun) stays
+                // below 2^kLazyRescale.  out = acc / l and lse = mrun +
+                // log2 l do not depend on which reference the sums use.
+                if (__any(mt > mrun[qt] + kLazyRescale)) {  // uniform branch
+                    const float mnew = fmaxf(mrun[qt], mt);
+                    const float r = (mnew == kNegInf) ? 0.0f : mnew;
+                    const float alpha = fast_exp2(mrun[qt] - r);  // 0 while nothing was seen
+                    mrun[qt] = mnew;
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
-                lacc[qt] *= alpha;
+                    for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
+                    lacc[qt] *= alpha;
+                    lex[qt] *= alpha;
+                }
+                const float ref = (mrun[qt] == kNegInf) ? 0.0f : mrun[qt];
                 float pv[8];
                 float psum = 0.0f;
 #pragma unroll
@@ -374,7 +385,7 @@ struct MfmaEngine {
                     pv[k] = fast_exp2(sv[k] - ref);
                     psum += pv[k];
                 }
-                lex[qt] = lex[qt] * alpha + psum;
+                lex[qt] += psum;
                 pb[qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
             }
