@@ -238,3 +238,43 @@ def test_fp8_launch_shape_70b():
     _log(f"case fp8_launch_shape waves={waves} wgs={wgs} chunks={nc}")
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert (waves, wgs, nc) == (8, w.B * w.g, 1)
+
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[4], SHAPES[6]],
+                         ids=["valu_m1", "mfma_m8", "mfma_m32"])
+@pytest.mark.parametrize("num_splits", [0, -1])
+@pytest.mark.parametrize("paged", [False, True])
+def test_score_staircase_fp8(shape, num_splits, paged):
+    """K codes of 0.5 * min(floor(p / 37), 16) (exact in E4M3) with K scale 1
+    and q row i = 1 + (i mod 8)/8: the scores climb by 8.2 (1 + (i mod 8)/8)
+    log2 units at each of 16 steps that do not line up with the tiles, so
+    the running maximum moves again and again mid-sequence."""
+    name, s = shape
+    _log(f"case fp8_staircase {name} splits={num_splits} paged={paged}")
+    gen = torch.Generator().manual_seed(1210)
+    lengths = torch.tensor([1, 37, 38, 100, 1000, 4097], dtype=torch.int32)
+    B, g, h, d = len(lengths), s["g"], s["h"], s["d"]
+    T = int(lengths.max()) + 15
+    vals = oracle.e4m3_values()
+    level = 0.5 * np.minimum(np.arange(T) // 37, 16)
+    code_of = {float(vals[c]): c for c in range(0x7F)}  # non-negative codes
+    kcode = torch.tensor([code_of[float(x)] for x in level], dtype=torch.uint8)
+    kc = kcode.view(1, 1, T, 1).expand(B, g, T, d).clone()
+    kc[torch.arange(T).view(1, 1, T, 1).expand(B, g, T, d) >= lengths.view(-1, 1, 1, 1)] = NAN_CODE
+    vc = _codes(B, g, T, d, lengths, gen)
+    ks = torch.ones(g, dtype=torch.float32)
+    _, vs = _scales(g, gen)
+    q = (1.0 + (torch.arange(h) % 8).to(torch.float32) / 8.0).view(1, h, 1).expand(B, h, d)
+    q = q.to(torch.bfloat16).contiguous()
+    sc = float(d) ** -0.5
+    table = None
+    if paged:
+        table, nb = W.make_block_table(lengths, 16, perm_seed=1211, extra_blocks=2)
+        kc = W.scatter_to_pool(kc, lengths, table, nb, 16, fill=NAN_CODE)
+        vc = W.scatter_to_pool(vc, lengths, table, nb, 16, fill=NAN_CODE)
+    out, lse = kvc.decode_fp8(dev(q), dev(kc), dev(vc), dev(ks), dev(vs), dev(lengths),
+                              block_table=dev(table) if paged else None, scale=sc,
+                              num_splits=num_splits)
+    ro, rl = oracle.decode_fp8(q, kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(), lengths, sc,
+                               block_table=table)
+    check_parity(out, lse, ro, rl, _vmax(vc, vs, lengths, table), name + "/staircase")

@@ -357,3 +357,46 @@ def test_position_ramp(shape, num_splits, paged):
     out, lse = call(x["scale"])
     ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], lengths, x["scale"])
     check_parity(out, lse, ro, rl, 63.0, name + "/ramp")
+
+
+@pytest.mark.parametrize("shape", [KERNEL_SHAPES[0], KERNEL_SHAPES[4], KERNEL_SHAPES[7],
+                                   KERNEL_SHAPES[8]],
+                         ids=["valu_m1", "mfma_m8", "mfma_m32", "mfma_m64"])
+@pytest.mark.parametrize("num_splits", [0, -1])
+@pytest.mark.parametrize("paged", [False, True])
+def test_score_staircase(shape, num_splits, paged):
+    """Scores that climb in steps along the sequence: K[p] = 0.5 *
+    min(floor(p / 37), 16) in every dim and q row i = 1 + (i mod 8)/8, so
+    each of the 16 steps raises row i's score by 8.2 (1 + (i mod 8)/8) in
+    log2 units, at positions that do not line up with the tiles, by a
+    different amount per query row.  The running maximum of every row moves
+    again and again mid-sequence; the softmax weight of the positions before
+    a step drops by 2^-8 or more.  (The cap keeps lse below about 170, where
+    float32 still resolves the 1e-4 bar.)  Checked against the oracle."""
+    name, s = shape
+    _log(f"case staircase {name} splits={num_splits} paged={paged}")
+    lengths = torch.tensor([1, 37, 38, 100, 1000, 4097], dtype=torch.int32)
+    B = len(lengths)
+    w = W.Workload(name, B=B, seed=340, **s)
+    x = W.make_contiguous(w, lengths=lengths, fill=float("nan"))
+    T = x["k_cache"].shape[2]
+    level = 0.5 * torch.clamp(torch.div(torch.arange(T), 37, rounding_mode="floor"), max=16).to(torch.float32)
+    kr = level.view(1, 1, T, 1).expand(B, w.g, T, w.d).to(x["k_cache"].dtype).clone()
+    kr[torch.arange(T).view(1, 1, T, 1).expand(B, w.g, T, w.d) >= lengths.view(-1, 1, 1, 1)] = \
+        float("nan")
+    x["k_cache"] = kr
+    qrow = 1.0 + (torch.arange(w.h) % 8).to(torch.float32) / 8.0  # exact in bf16
+    x["q"] = qrow.view(1, w.h, 1).expand(B, w.h, w.d).to(x["q"].dtype).clone()
+    if paged:
+        table, nb = W.make_block_table(lengths, 16, perm_seed=341, extra_blocks=3)
+        kp = W.scatter_to_pool(x["k_cache"], lengths, table, nb, 16, fill=float("nan"))
+        vp = W.scatter_to_pool(x["v_cache"], lengths, table, nb, 16, fill=float("nan"))
+        out, lse = kvc.decode_paged(dev(x["q"]), dev(kp), dev(vp), dev(table), dev(lengths),
+                                    scale=x["scale"], num_splits=num_splits)
+        vmax = attended_vmax_paged(vp, table, lengths, 16)
+    else:
+        out, lse = kvc.decode(dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]), dev(lengths),
+                              scale=x["scale"], num_splits=num_splits)
+        vmax = attended_vmax_contig(x["v_cache"], lengths)
+    ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], lengths, x["scale"])
+    check_parity(out, lse, ro, rl, vmax, name + "/staircase")
