@@ -23,7 +23,10 @@
 //
 // Online softmax per query column in base 2 ("KV Cache 优化与注意力机制加速"
 // (plumephp.com) section 2.2): the sub-tile maximum is reduced over the four
-// row groups of the wavefront, O and the sums are rescaled by 2^(m - m'), and
+// row groups of the wavefront; when it passes the running reference m by
+// more than 8 (base-2 units) for some column, O and the sums are rescaled by
+// 2^(m - m') (otherwise the weights 2^(s - m) stay below 256 and nothing is
+// rescaled);
 // P is rounded to bf16 for the PV product.  Two sums are kept: lr (the
 // rounded P, from the ones product) normalises out = sum bf16(P) V / lr, so
 // the weights applied to V add up to one; l (the fp32 P, summed on the VALU)
