@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -128,10 +130,15 @@ static size_t required_workspace(int B, int h, int g, int d, int dtype, int max_
 }
 
 // Compute units of the current device (cached per device).
+// The per-process caches below may be filled from several host threads at
+// once; one lock guards them (held only for a lookup or one HIP query).
+static std::mutex g_cache_lock;
+
 static int device_cus() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kStreamMaxCUs;
+    std::lock_guard<std::mutex> lock(g_cache_lock);
     if (dev < 64 && cached[dev] > 0) return cached[dev];
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -145,6 +152,7 @@ static int device_cus() {
 static int resident_wgs(const void* fn, int threads) {
     struct Entry { const void* fn; int n; };
     static Entry cache[64] = {};
+    std::lock_guard<std::mutex> lock(g_cache_lock);
     for (auto& e : cache)
         if (e.fn == fn) return e.n;
     int n = 0;

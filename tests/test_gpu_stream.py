@@ -122,3 +122,37 @@ def test_stream_repeated_calls_one_workspace(shape, paged):
             first = (out.clone(), lse.clone())
         else:
             assert torch.equal(out, first[0]) and torch.equal(lse, first[1]), f"call {call}"
+
+
+def test_launch_planning_from_many_threads():
+    """The library caches occupancy queries per process; planning the same
+    launches from eight host threads at once gives every thread the shapes a
+    single thread gets (ctypes releases the GIL during the calls)."""
+    import threading
+    cases = [(32, 64, 8, 128, 4096, 0, "bf16", False), (64, 32, 8, 128, 8192, 0, "bf16", True),
+             (4, 32, 1, 128, 131072, 64, "bf16", False), (8, 32, 32, 128, 2048, 0, "bf16", False),
+             (32, 64, 8, 128, 4096, 0, "fp8", False), (64, 32, 8, 128, 8192, 0, "fp8", True),
+             (32, 512, 8, 128, 4096, 0, "bf16", False), (8, 8, 2, 64, 1000, 0, "f32", False)]
+    results, errors = {}, []
+
+    def work(tid):
+        try:
+            for r in range(20):
+                for k, c in enumerate(cases):
+                    B, h, g, d, L, ns, dt, paged = c
+                    results[(tid, r, k)] = kvc.launch_shape(B, h, g, d, L, ns, dtype=dt, paged=paged)
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for k, c in enumerate(cases):
+        B, h, g, d, L, ns, dt, paged = c
+        want = kvc.launch_shape(B, h, g, d, L, ns, dtype=dt, paged=paged)
+        assert want[1] > 1 or B * g == 1, (c, want)
+        got = {results[(t, r, k)] for t in range(8) for r in range(20)}
+        assert got == {want}, (c, got, want)
