@@ -16,14 +16,17 @@ kv_cache_gqa_amd.build``) or without a GPU every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["append", "decode", "decode_paged", "plan", "workspace_bytes", "KvcError",
-           "load_library", "LIB_PATH", "F32", "BF16", "SPLITS_STREAM"]
+__all__ = ["append", "decode", "decode_paged", "append_decode", "decode_multi",
+           "append_decode_multi", "decode_window", "append_fp8", "decode_fp8", "copy_blocks",
+           "fork_block_tables", "gather_cache", "plan", "workspace_bytes", "launch_shape",
+           "KvcError", "load_library", "LIB_PATH", "F32", "BF16", "FP8_E4M3", "SPLITS_STREAM"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
 F32, BF16 = 0, 1
@@ -134,9 +137,25 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
+def _on_device(fn):
+    """Run fn with the device of its first GPU tensor argument current, so
+    that the library's launches and device queries and the default stream
+    (torch's current stream) belong to the device that holds the data."""
+    @functools.wraps(fn)
+    def run(*args, **kw):
+        for a in list(args) + list(kw.values()):
+            if isinstance(a, torch.Tensor) and a.is_cuda:
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kw)
+        return fn(*args, **kw)
+    return run
+
+
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the call runs on cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -196,6 +215,7 @@ def launch_shape(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: i
     return tuple(x.value for x in out)
 
 
+@_on_device
 def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, stream=None):
     """Write k_new/v_new [B,g,d] at position seq_lens_before[b] of each
     sequence's cache: contiguous [B,g,T,d], or pools [NB,g,bs,d] through
@@ -232,6 +252,7 @@ def _workspace(nbytes: int, q: torch.Tensor, workspace: Optional[torch.Tensor]):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_on_device
 def decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, num_splits: int = 0,
            workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
     """Decode attention over a contiguous cache.
@@ -256,6 +277,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, num_spl
     return out, lse
 
 
+@_on_device
 def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float] = None,
                  num_splits: int = 0, workspace: Optional[torch.Tensor] = None, out=None, lse=None,
                  stream=None):
@@ -281,6 +303,7 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float
     return out, lse
 
 
+@_on_device
 def append_decode(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None,
                   scale: Optional[float] = None, num_splits: int = 0,
                   workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
@@ -330,6 +353,7 @@ def _outputs_multi(q, out, lse):
     return out, lse
 
 
+@_on_device
 def decode_multi(q, k_cache, v_cache, seq_lens, block_table=None, scale: Optional[float] = None,
                  num_splits: int = 0, workspace: Optional[torch.Tensor] = None, out=None, lse=None,
                  stream=None):
@@ -370,6 +394,7 @@ def decode_multi(q, k_cache, v_cache, seq_lens, block_table=None, scale: Optiona
     return out, lse
 
 
+@_on_device
 def append_decode_multi(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None,
                         scale: Optional[float] = None, num_splits: int = 0,
                         workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None):
@@ -413,6 +438,7 @@ def _plan_len(capacity: int, window: int, n: int) -> int:
     return min(window + n - 1, capacity) if window > 0 else capacity
 
 
+@_on_device
 def decode_window(q, k_cache, v_cache, seq_lens, window: int, ring: bool = False,
                   block_table=None, scale: Optional[float] = None, num_splits: int = 0,
                   workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None,
@@ -477,6 +503,7 @@ def decode_window(q, k_cache, v_cache, seq_lens, window: int, ring: bool = False
     return out, lse
 
 
+@_on_device
 def copy_blocks(k_pool, v_pool, pairs, stream=None):
     """Copy physical block src -> dst of both pools [NB,g,bs,d] for every row
     (src, dst) of the device int32 tensor ``pairs`` [n, 2] (copy-on-write)."""
@@ -489,6 +516,7 @@ def copy_blocks(k_pool, v_pool, pairs, stream=None):
         _dtype_code(k_pool), _stream(stream)))
 
 
+@_on_device
 def fork_block_tables(block_table, seq_lens, parent, stream=None):
     """Forked tables: row b is row parent[b] (and its length).  Returns
     (tables [B,max_blocks], seq_lens [B]) on the device."""
@@ -504,6 +532,7 @@ def fork_block_tables(block_table, seq_lens, parent, stream=None):
     return out_t, out_l
 
 
+@_on_device
 def gather_cache(k_src, v_src, seq_lens, parent, k_dst, v_dst, stream=None):
     """Contiguous caches re-ranked by parent into k_dst, v_dst [B,g,t_cap,d]:
     positions below seq_lens[parent[b]] of sequence b come from parent[b]."""
@@ -517,6 +546,7 @@ def gather_cache(k_src, v_src, seq_lens, parent, k_dst, v_dst, stream=None):
         _dtype_code(k_src), _stream(stream)))
 
 
+@_on_device
 def append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, seq_lens_before, block_table=None,
                stream=None):
     """Quantise the new token's K/V (bf16 [B,g,d]) into uint8 FP8 E4M3 caches
@@ -537,6 +567,7 @@ def append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, seq_lens_before
         _stream(stream)))
 
 
+@_on_device
 def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table=None,
                scale: Optional[float] = None, num_splits: int = 0,
                workspace: Optional[torch.Tensor] = None, out=None, lse=None, stream=None,

@@ -310,3 +310,14 @@ def test_fp8_planning_dtype_plans_like_bf16():
         assert kvc.workspace_bytes(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
             kvc.workspace_bytes(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
     assert lib.kvc_decode_plan(2, 8, 2, 128, 3, 64, 0, 0, None, None, None) == UNSUPPORTED
+
+
+def test_public_calls_carry_the_device_guard():
+    """Every binding call that takes tensors runs with the device of its
+    first GPU tensor made current (and rejects tensors of another device)."""
+    for name in ["append", "decode", "decode_paged", "append_decode", "decode_multi",
+                 "append_decode_multi", "decode_window", "copy_blocks", "fork_block_tables",
+                 "gather_cache", "append_fp8", "decode_fp8"]:
+        fn = getattr(kvc, name)
+        assert hasattr(fn, "__wrapped__"), name
+        assert name in kvc.__all__, name
