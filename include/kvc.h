@@ -36,7 +36,9 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library allocates nothing and keeps no state besides cached answers to
- *     device queries (compute-unit count, resident work-groups per kernel).
+ *     device queries (compute-unit count, resident work-groups per kernel),
+ *     guarded by a lock: entry points may be called from several host
+ *     threads.  The current HIP device must be the one holding the data.
  *     Outputs must not alias inputs.
  *   - Every launch is asynchronous on the caller's `stream`; no entry point
  *     synchronises the host.  Validation of the host-side arguments happens
