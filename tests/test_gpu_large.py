@@ -94,3 +94,43 @@ def test_paged_pools_past_4gb(h, num_splits):
         check_parity(out[b:b + 1], lse[b:b + 1], ro, rl, _vmax(vr), f"large paged b={b}")
     del kp, vp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("h", [32, 8], ids=["mfma_m4", "valu_m1"])
+def test_paged_fp8_pools_past_4gb(h):
+    _log(f"case large paged fp8 h={h}")
+    B, g, d, bs = 32, 8, 128, 16
+    gen = torch.Generator().manual_seed(1520)
+    lengths = torch.randint(1, 8193, (B,), generator=gen, dtype=torch.int32)
+    used = int(((lengths.to(torch.int64) + bs - 1) // bs).sum())
+    nb = 280000  # 280000 * 8 * 16 * 128 B = 4.6 GB per pool of one-byte codes
+    table, _ = W.make_block_table(lengths, bs, perm_seed=1521, extra_blocks=nb - used)
+    assert int(table.max()) * g * bs * d > 4 * GiB
+    gg = torch.Generator(device="cuda").manual_seed(1522)
+    pools = []
+    for _ in range(2):
+        c = torch.randint(0, 256, (nb, g, bs, d), device="cuda", dtype=torch.uint8, generator=gg)
+        c[(c & 0x7F) == 0x7F] = 0x3C  # finite codes only
+        pools.append(c)
+    kp, vp = pools
+    ks = (torch.rand(g, generator=gen) * 0.5 + 0.01).to(torch.float32)
+    vs = (torch.rand(g, generator=gen) * 0.5 + 0.01).to(torch.float32)
+    q = W.randn((B, h, d), torch.bfloat16, gen)
+    scale = d ** -0.5
+    bt = dev(table)
+    out, lse = kvc.decode_fp8(dev(q), kp, vp, dev(ks), dev(vs), dev(lengths), block_table=bt,
+                              scale=scale)
+    torch.cuda.synchronize()
+    vals = torch.from_numpy(oracle.e4m3_values())
+    for b in [int(torch.argmax(table.max(dim=1).values)), B - 1]:
+        Lb = int(lengths[b])
+        pos = torch.arange(Lb, device="cuda")
+        blk = bt[b, pos // bs].long()
+        kr = kp[blk, :, pos % bs].permute(1, 0, 2).unsqueeze(0).contiguous().cpu()
+        vr = vp[blk, :, pos % bs].permute(1, 0, 2).unsqueeze(0).contiguous().cpu()
+        ro, rl = oracle.decode_fp8(q[b:b + 1], kr.numpy(), vr.numpy(), ks.numpy(), vs.numpy(),
+                                   lengths[b:b + 1], scale)
+        vmax = float((vals[vr.long()] * vs.double().view(1, -1, 1, 1)).abs().max())
+        check_parity(out[b:b + 1], lse[b:b + 1], ro, rl, vmax, f"large paged fp8 b={b}")
+    del kp, vp, pools
+    torch.cuda.empty_cache()
