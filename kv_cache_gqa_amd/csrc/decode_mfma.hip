@@ -18,7 +18,7 @@
 //     the S^T result already sits in the B-operand layout this needs
 //     (lane l holds positions 4*(l/16)+v of both 16-position halves), so P
 //     never moves between lanes; V^T comes from a per-wavefront LDS copy of
-//     the 32 V rows (XOR-swizzled 16-byte chunks, conflict-free reads).
+//     the 32 V rows (XOR-swizzled 16-byte chunks).
 //   A ninth product with an all-ones A operand gives lr = sum_p bf16(P[p, q]).
 //
 // Online softmax per query column in base 2 ("KV Cache 优化与注意力机制加速"
@@ -72,8 +72,13 @@ struct Lds {
 
 // XOR swizzle of the 16-byte chunk index of V row r.  One transposing read
 // of a 16-lane group touches rows R..R+3 (R a multiple of 4) at the same
-// 32-byte column slice; the swizzle puts those four slices on disjoint LDS
-// bank groups.  It keeps chunk pairs (2k, 2k+1) adjacent.
+// 32-byte column slice; the swizzle puts those four slices on disjoint
+// groups of eight banks.  It keeps chunk pairs (2k, 2k+1) adjacent.  The
+// LDS serves two 16-lane groups together, and rows R..R+3 and R+4..R+7 land
+// on the same banks: a two-way conflict, 32 stall cycles per tile (22 % of
+// the LDS cycles, about 2 % of the kernel's time).  Layouts without it (the
+// group parity in the swizzle, or a padded 4-row pitch) measured no faster
+// in the whole-unit kernel and make the 4-wavefront stream kernels spill.
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
