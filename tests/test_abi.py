@@ -204,6 +204,24 @@ def test_multi_validation_codes():
     assert fa(*bad) == INVALID
     bad = list(aargs); bad[10] = -1                  # n < 1
     assert fa(*bad) == INVALID
+    fp = lib.kvc_decode_attention_multi_paged
+    pargs = [FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 4, 0.1, 1, 1, None, 0, FAKE,
+             FAKE, None]
+    bad = list(pargs); bad[12] = 0                   # n = 0
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[3] = None                 # no block table
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[5] = 12                   # block size not a power of two
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[15] = 2                   # split plan needs a workspace
+    assert fp(*bad) == WORKSPACE
+    fap = lib.kvc_append_decode_attention_multi_paged
+    apargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 4, 0.1, 1, 1,
+              None, 0, FAKE, FAKE, None]
+    bad = list(apargs); bad[2] = None                # v_new missing
+    assert fap(*bad) == INVALID
+    bad = list(apargs); bad[14] = 0                  # n = 0
+    assert fap(*bad) == INVALID
     # the workspace of a multi call is that of h * n query rows
     need = lib.kvc_decode_workspace_bytes(2, 8 * 4, 2, 128, 1, 64, 2, 0)
     assert need > lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2, 0) > 0
@@ -232,6 +250,22 @@ def test_window_validation_codes():
     assert fp(*bad) == INVALID
     bad = list(pargs); bad[1] = None                 # k_new missing
     assert fp(*bad) == INVALID
+    fwp = lib.kvc_decode_attention_window_paged
+    wargs = [FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 2, 5, 0.1, 1, 1, None, 0,
+             FAKE, FAKE, None]
+    bad = list(wargs); bad[13] = -1                  # negative window
+    assert fwp(*bad) == INVALID
+    bad = list(wargs); bad[6] = 0                    # empty pool
+    assert fwp(*bad) == INVALID
+    fwa = lib.kvc_append_decode_attention_window
+    waargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 2, 64, 10, 1, 0.1, 1, 1, None, 0,
+              FAKE, FAKE, None]
+    bad = list(waargs); bad[12] = 0                  # ring without a window
+    assert fwa(*bad) == INVALID
+    bad = list(waargs); bad[12] = 64                 # window + n - 1 > t_cap
+    assert fwa(*bad) == INVALID
+    bad = list(waargs); bad[1] = None                # k_new missing
+    assert fwa(*bad) == INVALID
 
 
 def test_block_op_validation_codes():
