@@ -45,6 +45,13 @@
  *     before any HIP call and needs no GPU.
  *   - dtype: KVC_F32 or KVC_BF16, shared by q, the caches and k/v_new.
  *     out and lse are always float32.
+ *   - Alignment: tensors of elements (q, caches and pools, k_new / v_new,
+ *     out, the workspace) must start on a 16-byte boundary, because the
+ *     kernels move them in 16-byte vectors; arrays of int32 or float32
+ *     values (seq_lens, block tables, lse, scales, pairs, parents) on a
+ *     4-byte boundary.  Any other pointer gives KVC_ERR_INVALID before any
+ *     HIP call.  Allocations from hipMalloc or PyTorch's allocator satisfy
+ *     both; a view at an element offset may not.
  *   - Device-side integers (seq_lens, block_table) are trusted.  They are
  *     clamped inside the kernels so that a bad value cannot fault the GPU:
  *     lengths to [0, capacity], physical block ids to [0, num_blocks).  A
@@ -278,9 +285,12 @@ int kvc_append_decode_attention_paged(const void* q, const void* k_new, const vo
  *   Token t sees min(P_b + t + 1, capacity) positions (0 if negative).
  * Everything else is as for the single-token calls, which are the case
  * n = 1.  The workspace is kvc_decode_workspace_bytes(B, h * n, g, d, ...);
- * kvc_decode_plan and kvc_decode_launch_shape likewise take h * n as h.  The
- * bf16 d = 128 kernels serve (h / g) * n <= 32 query rows per KV head; more
- * rows go to the generic kernel.
+ * kvc_decode_plan and kvc_decode_launch_shape likewise take h * n as h.
+ * Kernels by rows per KV head, r = (h / g) * n, for bf16 with d = 128: r <= 3
+ * the VALU kernel; 4 <= r <= 32 the matrix-core decode kernel; r > 32 the
+ * same kernel in ceil(r / 32) row slices of 32, each reading the unit's K/V
+ * (any n: the appended tokens' positions are taken 32 at a time).  fp32 or
+ * other head dims take the generic kernel for any r.
  */
 int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* seq_lens, int B, int h, int g, int d, int n,

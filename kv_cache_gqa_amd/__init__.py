@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import ctypes
 import functools
+import inspect
 import math
 import os
 from typing import Optional, Tuple
@@ -28,7 +29,10 @@ __all__ = ["append", "decode", "decode_paged", "append_decode", "decode_multi",
            "fork_block_tables", "gather_cache", "plan", "workspace_bytes", "launch_shape",
            "KvcError", "load_library", "LIB_PATH", "F32", "BF16", "FP8_E4M3", "SPLITS_STREAM"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
+# KVC_LIB names another build of the library (the sanitizer test loads one
+# whose host code is built with AddressSanitizer and UBSan).
+LIB_PATH = os.environ.get("KVC_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libkvc.so")
 F32, BF16 = 0, 1
 SPLITS_STREAM = -1  # num_splits value that asks for the stream split
 _MODES = {0: "chunks", 1: "stream", 2: "auto_chunks"}
@@ -140,15 +144,38 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _on_device(fn):
     """Run fn with the device of its first GPU tensor argument current, so
     that the library's launches and device queries and the default stream
-    (torch's current stream) belong to the device that holds the data."""
+    (torch's current stream) belong to the device that holds the data.  When
+    the caller names a stream, fn also runs with that stream current, so
+    that the tensors it allocates (out, lse, the workspace) belong to the
+    stream the kernels use: the caching allocator then reuses them only
+    after that stream's work."""
+    sig = inspect.signature(fn)
+
     @functools.wraps(fn)
     def run(*args, **kw):
         for a in list(args) + list(kw.values()):
             if isinstance(a, torch.Tensor) and a.is_cuda:
                 with torch.cuda.device(a.device):
-                    return fn(*args, **kw)
+                    stream = sig.bind_partial(*args, **kw).arguments.get("stream")
+                    if stream is None:
+                        return fn(*args, **kw)
+                    if not isinstance(stream, torch.cuda.Stream):
+                        stream = torch.cuda.ExternalStream(int(stream), device=a.device)
+                    with torch.cuda.stream(stream):
+                        return fn(*args, **kw)
         return fn(*args, **kw)
     return run
+
+
+def _shape(t, shape, name: str):
+    """Raise ValueError unless tensor t has the given shape (None: any size)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.dim() != len(shape) or any(e is not None and int(x) != int(e)
+                                    for x, e in zip(t.shape, shape)):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    return tuple(int(x) for x in t.shape)
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -215,6 +242,21 @@ def launch_shape(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: i
     return tuple(x.value for x in out)
 
 
+def _cache_shapes(k_cache, v_cache, B: int, d: int, block_table, names=("k_cache", "v_cache")):
+    """Check the cache tensors against the batch and head dim.  Contiguous:
+    [B, g, t_cap, d]; paged: pools [NB, g, bs, d] and block_table [B,
+    max_blocks].  Returns (g, capacity, block_size, max_blocks, num_blocks);
+    capacity is t_cap, or NB for pools."""
+    if block_table is None:
+        _, g, t_cap, _ = _shape(k_cache, (B, None, None, d), names[0])
+        _shape(v_cache, tuple(k_cache.shape), names[1])
+        return g, t_cap, 0, 0, 0
+    nb, g, bs, _ = _shape(k_cache, (None, None, None, d), names[0].replace("cache", "pool"))
+    _shape(v_cache, tuple(k_cache.shape), names[1].replace("cache", "pool"))
+    _, mb = _shape(block_table, (B, None), "block_table")
+    return g, nb, bs, mb, nb
+
+
 @_on_device
 def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, stream=None):
     """Write k_new/v_new [B,g,d] at position seq_lens_before[b] of each
@@ -222,12 +264,13 @@ def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, st
     block_table [B,max_blocks].  In place; seq_lens_before is not changed."""
     lib = load_library()
     dt = _dtype_code(k_cache)
-    B, g, d = k_new.shape
-    if block_table is None:
-        capacity, mb, bs, bt = k_cache.shape[2], 0, 0, None
-    else:
-        capacity, bs, mb = k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
-        bt = _dev(block_table, "block_table", torch.int32)
+    B, g, d = _shape(k_new, (None, None, None), "k_new")
+    _shape(v_new, (B, g, d), "v_new")
+    _shape(seq_lens_before, (B,), "seq_lens_before")
+    gc, capacity, bs, mb, _ = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    if gc != g:
+        raise ValueError(f"k_new has {g} KV heads, the cache {gc}")
+    bt = _dev(block_table, "block_table", torch.int32) if block_table is not None else None
     st = lib.kvc_append(_dev(k_new, "k_new", k_cache.dtype), _dev(v_new, "v_new", k_cache.dtype),
                         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
                         bt, mb, bs, _dev(seq_lens_before, "seq_lens_before", torch.int32),
@@ -236,12 +279,21 @@ def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, st
 
 
 def _outputs(q, out, lse):
-    B, h, d = q.shape
+    """out and lse for q [B, h, (n,) d]: out like q in float32, lse without
+    the last dim.  Caller-supplied tensors are checked against that."""
+    oshape, lshape = tuple(q.shape), tuple(q.shape[:-1])
     if out is None:
-        out = torch.empty((B, h, d), dtype=torch.float32, device=q.device)
+        out = torch.empty(oshape, dtype=torch.float32, device=q.device)
+    else:
+        _shape(out, oshape, "out")
     if lse is None:
-        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+        lse = torch.empty(lshape, dtype=torch.float32, device=q.device)
+    else:
+        _shape(lse, lshape, "lse")
     return out, lse
+
+
+_outputs_multi = _outputs
 
 
 def _workspace(nbytes: int, q: torch.Tensor, workspace: Optional[torch.Tensor]):
@@ -250,6 +302,13 @@ def _workspace(nbytes: int, q: torch.Tensor, workspace: Optional[torch.Tensor]):
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def _new_tokens(k_new, v_new, B: int, g: int, n, d: int):
+    """k_new, v_new [B, g, d] (n is None) or [B, g, n, d]."""
+    shape = (B, g, d) if n is None else (B, g, n, d)
+    _shape(k_new, shape, "k_new")
+    _shape(v_new, shape, "v_new")
 
 
 @_on_device
@@ -261,8 +320,9 @@ def decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, num_spl
     lengths).  Returns (out [B,h,d] float32, lse [B,h] float32)."""
     lib = load_library()
     dt = _dtype_code(q)
-    B, h, d = q.shape
-    _, g, t_cap, _ = k_cache.shape
+    B, h, d = _shape(q, (None, None, None), "q")
+    g, t_cap, _, _, _ = _cache_shapes(k_cache, v_cache, B, d, None)
+    _shape(seq_lens, (B,), "seq_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
@@ -285,9 +345,9 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float
     int32 [B,max_blocks], seq_lens int32 [B].  Returns (out, lse)."""
     lib = load_library()
     dt = _dtype_code(q)
-    B, h, d = q.shape
-    nb, g, bs, _ = k_pool.shape
-    mb = block_table.shape[1]
+    B, h, d = _shape(q, (None, None, None), "q")
+    g, _, bs, mb, nb = _cache_shapes(k_pool, v_pool, B, d, block_table)
+    _shape(seq_lens, (B,), "seq_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
@@ -314,25 +374,25 @@ def append_decode(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_tabl
     Returns (out [B,h,d] float32, lse [B,h] float32)."""
     lib = load_library()
     dt = _dtype_code(q)
-    B, h, d = q.shape
+    B, h, d = _shape(q, (None, None, None), "q")
+    g, cap, bs, mb, nb = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    _new_tokens(k_new, v_new, B, g, None, d)
+    _shape(seq_lens_before, (B,), "seq_lens_before")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
     kn, vn = _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype)
     sl = _dev(seq_lens_before, "seq_lens_before", torch.int32)
     if block_table is None:
-        _, g, t_cap, _ = k_cache.shape
-        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, t_cap, num_splits, 0),
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, cap, num_splits, 0),
                              q, workspace)
         st = lib.kvc_append_decode_attention(
             _dev(q, "q"), kn, vn, _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
-            sl, B, h, g, d, t_cap, float(scale), dt, num_splits,
+            sl, B, h, g, d, cap, float(scale), dt, num_splits,
             ws.data_ptr() if ws is not None else None, wsb,
             _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_append_decode_attention", st)
     else:
-        nb, g, bs, _ = k_cache.shape
-        mb = block_table.shape[1]
         ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, dt, mb * bs, num_splits, 1),
                              q, workspace)
         st = lib.kvc_append_decode_attention_paged(
@@ -341,15 +401,6 @@ def append_decode(q, k_new, v_new, k_cache, v_cache, seq_lens_before, block_tabl
             float(scale), dt, num_splits, ws.data_ptr() if ws is not None else None, wsb,
             _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_append_decode_attention_paged", st)
-    return out, lse
-
-
-def _outputs_multi(q, out, lse):
-    B, h, n, d = q.shape
-    if out is None:
-        out = torch.empty((B, h, n, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, h, n), dtype=torch.float32, device=q.device)
     return out, lse
 
 
@@ -365,24 +416,23 @@ def decode_multi(q, k_cache, v_cache, seq_lens, block_table=None, scale: Optiona
     [B,h,n,d] float32, lse [B,h,n] float32)."""
     lib = load_library()
     dt = _dtype_code(q)
-    B, h, n, d = q.shape
+    B, h, n, d = _shape(q, (None, None, None, None), "q")
+    g, cap, bs, mb, nb = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    _shape(seq_lens, (B,), "seq_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs_multi(q, out, lse)
+    out, lse = _outputs(q, out, lse)
     sl = _dev(seq_lens, "seq_lens", torch.int32)
     if block_table is None:
-        _, g, t_cap, _ = k_cache.shape
-        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, t_cap, num_splits, 0),
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, cap, num_splits, 0),
                              q, workspace)
         st = lib.kvc_decode_attention_multi(
             _dev(q, "q"), _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype), sl,
-            B, h, g, d, n, t_cap, float(scale), dt, num_splits,
+            B, h, g, d, n, cap, float(scale), dt, num_splits,
             ws.data_ptr() if ws is not None else None, wsb,
             _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_decode_attention_multi", st)
     else:
-        nb, g, bs, _ = k_cache.shape
-        mb = block_table.shape[1]
         ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, mb * bs, num_splits,
                                                             1), q, workspace)
         st = lib.kvc_decode_attention_multi_paged(
@@ -404,25 +454,25 @@ def append_decode_multi(q, k_new, v_new, k_cache, v_cache, seq_lens_before, bloc
     (out [B,h,n,d] float32, lse [B,h,n] float32)."""
     lib = load_library()
     dt = _dtype_code(q)
-    B, h, n, d = q.shape
+    B, h, n, d = _shape(q, (None, None, None, None), "q")
+    g, cap, bs, mb, nb = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    _new_tokens(k_new, v_new, B, g, n, d)
+    _shape(seq_lens_before, (B,), "seq_lens_before")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs_multi(q, out, lse)
+    out, lse = _outputs(q, out, lse)
     kn, vn = _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype)
     sl = _dev(seq_lens_before, "seq_lens_before", torch.int32)
     if block_table is None:
-        _, g, t_cap, _ = k_cache.shape
-        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, t_cap, num_splits, 0),
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, cap, num_splits, 0),
                              q, workspace)
         st = lib.kvc_append_decode_attention_multi(
             _dev(q, "q"), kn, vn, _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
-            sl, B, h, g, d, n, t_cap, float(scale), dt, num_splits,
+            sl, B, h, g, d, n, cap, float(scale), dt, num_splits,
             ws.data_ptr() if ws is not None else None, wsb,
             _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_append_decode_attention_multi", st)
     else:
-        nb, g, bs, _ = k_cache.shape
-        mb = block_table.shape[1]
         ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, mb * bs, num_splits,
                                                             1), q, workspace)
         st = lib.kvc_append_decode_attention_multi_paged(
@@ -453,37 +503,40 @@ def decode_window(q, k_cache, v_cache, seq_lens, window: int, ring: bool = False
     [B,h,n,d] float32, lse [B,h,n] float32)."""
     lib = load_library()
     dt = _dtype_code(q)
-    B, h, n, d = q.shape
+    B, h, n, d = _shape(q, (None, None, None, None), "q")
+    if ring and block_table is not None:
+        raise ValueError("a ring cache is contiguous")
+    g, cap, bs, mb, nb = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    _shape(seq_lens, (B,), "seq_lens")
+    fused = k_new is not None
+    if fused:
+        _new_tokens(k_new, v_new, B, g, n, d)
+    elif v_new is not None:
+        raise ValueError("v_new without k_new")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs_multi(q, out, lse)
+    out, lse = _outputs(q, out, lse)
     sl = _dev(seq_lens, "seq_lens", torch.int32)
-    fused = k_new is not None
     kn = _dev(k_new, "k_new", q.dtype) if fused else None
     vn = _dev(v_new, "v_new", q.dtype) if fused else None
     wsp = lambda nbytes: _workspace(nbytes, q, workspace)  # noqa: E731
     if block_table is None:
-        _, g, t_cap, _ = k_cache.shape
-        ws, wsb = wsp(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, _plan_len(t_cap, window, n),
+        ws, wsb = wsp(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt, _plan_len(cap, window, n),
                                                      num_splits, 0))
         wsptr = ws.data_ptr() if ws is not None else None
         kc, vc = _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype)
         if fused:
             st = lib.kvc_append_decode_attention_window(
-                _dev(q, "q"), kn, vn, kc, vc, sl, B, h, g, d, n, t_cap, window, int(ring),
+                _dev(q, "q"), kn, vn, kc, vc, sl, B, h, g, d, n, cap, window, int(ring),
                 float(scale), dt, num_splits, wsptr, wsb, _dev(out, "out", torch.float32),
                 _dev(lse, "lse", torch.float32), _stream(stream))
         else:
             st = lib.kvc_decode_attention_window(
-                _dev(q, "q"), kc, vc, sl, B, h, g, d, n, t_cap, window, int(ring), float(scale), dt,
+                _dev(q, "q"), kc, vc, sl, B, h, g, d, n, cap, window, int(ring), float(scale), dt,
                 num_splits, wsptr, wsb, _dev(out, "out", torch.float32),
                 _dev(lse, "lse", torch.float32), _stream(stream))
         _check("kvc_*decode_attention_window", st)
     else:
-        if ring:
-            raise ValueError("a ring cache is contiguous")
-        nb, g, bs, _ = k_cache.shape
-        mb = block_table.shape[1]
         ws, wsb = wsp(lib.kvc_decode_workspace_bytes(B, h * n, g, d, dt,
                                                      _plan_len(mb * bs, window, n), num_splits, 1))
         wsptr = ws.data_ptr() if ws is not None else None
@@ -508,8 +561,11 @@ def copy_blocks(k_pool, v_pool, pairs, stream=None):
     """Copy physical block src -> dst of both pools [NB,g,bs,d] for every row
     (src, dst) of the device int32 tensor ``pairs`` [n, 2] (copy-on-write)."""
     lib = load_library()
-    nb, g, bs, d = k_pool.shape
+    nb, g, bs, d = _shape(k_pool, (None, None, None, None), "k_pool")
+    _shape(v_pool, (nb, g, bs, d), "v_pool")
     n = pairs.shape[0] if pairs.numel() else 0
+    if n:
+        _shape(pairs, (n, 2), "pairs")
     _check("kvc_copy_blocks", lib.kvc_copy_blocks(
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
         _dev(pairs, "pairs", torch.int32) if n else None, n, nb, g, bs, d,
@@ -521,8 +577,9 @@ def fork_block_tables(block_table, seq_lens, parent, stream=None):
     """Forked tables: row b is row parent[b] (and its length).  Returns
     (tables [B,max_blocks], seq_lens [B]) on the device."""
     lib = load_library()
-    B_src, mb = block_table.shape
-    B = parent.shape[0]
+    B_src, mb = _shape(block_table, (None, None), "block_table")
+    _shape(seq_lens, (B_src,), "seq_lens")
+    (B,) = _shape(parent, (None,), "parent")
     out_t = torch.empty((B, mb), dtype=torch.int32, device=block_table.device)
     out_l = torch.empty((B,), dtype=torch.int32, device=block_table.device)
     _check("kvc_fork_block_tables", lib.kvc_fork_block_tables(
@@ -537,8 +594,12 @@ def gather_cache(k_src, v_src, seq_lens, parent, k_dst, v_dst, stream=None):
     """Contiguous caches re-ranked by parent into k_dst, v_dst [B,g,t_cap,d]:
     positions below seq_lens[parent[b]] of sequence b come from parent[b]."""
     lib = load_library()
-    B_src, g, t_cap, d = k_src.shape
-    B = parent.shape[0]
+    B_src, g, t_cap, d = _shape(k_src, (None, None, None, None), "k_src")
+    _shape(v_src, (B_src, g, t_cap, d), "v_src")
+    _shape(seq_lens, (B_src,), "seq_lens")
+    (B,) = _shape(parent, (None,), "parent")
+    _shape(k_dst, (B, g, t_cap, d), "k_dst")
+    _shape(v_dst, (B, g, t_cap, d), "v_dst")
     _check("kvc_gather_cache", lib.kvc_gather_cache(
         _dev(k_src, "k_src"), _dev(v_src, "v_src", k_src.dtype),
         _dev(seq_lens, "seq_lens", torch.int32), B_src, _dev(parent, "parent", torch.int32), B,
@@ -553,12 +614,15 @@ def append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, seq_lens_before
     (contiguous [B,g,t_cap,d] or pools [NB,g,bs,d]) with per-KV-head float32
     scales k_scale, v_scale [g]."""
     lib = load_library()
-    B, g, d = k_new.shape
-    if block_table is None:
-        capacity, mb, bs, bt = k_cache.shape[2], 0, 0, None
-    else:
-        capacity, bs, mb = k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
-        bt = _dev(block_table, "block_table", torch.int32)
+    B, g, d = _shape(k_new, (None, None, None), "k_new")
+    _shape(v_new, (B, g, d), "v_new")
+    _shape(seq_lens_before, (B,), "seq_lens_before")
+    gc, capacity, bs, mb, _ = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    if gc != g:
+        raise ValueError(f"k_new has {g} KV heads, the cache {gc}")
+    _shape(k_scale, (g,), "k_scale")
+    _shape(v_scale, (g,), "v_scale")
+    bt = _dev(block_table, "block_table", torch.int32) if block_table is not None else None
     _check("kvc_append_fp8", lib.kvc_append_fp8(
         _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16),
         _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
@@ -578,34 +642,39 @@ def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table=None
     the call quantises and appends the new token and attends (one launch).
     Returns (out [B,h,d] float32, lse [B,h] float32)."""
     lib = load_library()
-    B, h, d = q.shape
+    B, h, d = _shape(q, (None, None, None), "q")
+    g, cap, bs, mb, nb = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    _shape(k_scale, (g,), "k_scale")
+    _shape(v_scale, (g,), "v_scale")
+    _shape(seq_lens, (B,), "seq_lens")
+    fused = k_new is not None
+    if fused:
+        _new_tokens(k_new, v_new, B, g, None, d)
+    elif v_new is not None:
+        raise ValueError("v_new without k_new")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
     qp = _dev(q, "q", torch.bfloat16)
     ks, vs = _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32)
     sl = _dev(seq_lens, "seq_lens", torch.int32)
-    fused = k_new is not None
     kn = _dev(k_new, "k_new", torch.bfloat16) if fused else None
     vn = _dev(v_new, "v_new", torch.bfloat16) if fused else None
     if block_table is None:
-        _, g, t_cap, _ = k_cache.shape
-        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, BF16, t_cap, num_splits, 0),
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, BF16, cap, num_splits, 0),
                              q, workspace)
         wsp = ws.data_ptr() if ws is not None else None
         kc, vc = _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8)
         if fused:
             st = lib.kvc_append_decode_attention_fp8(qp, kn, vn, kc, vc, ks, vs, sl, B, h, g, d,
-                                                     t_cap, float(scale), num_splits, wsp, wsb,
+                                                     cap, float(scale), num_splits, wsp, wsb,
                                                      _dev(out, "out"), _dev(lse, "lse"),
                                                      _stream(stream))
         else:
-            st = lib.kvc_decode_attention_fp8(qp, kc, vc, ks, vs, sl, B, h, g, d, t_cap,
+            st = lib.kvc_decode_attention_fp8(qp, kc, vc, ks, vs, sl, B, h, g, d, cap,
                                               float(scale), num_splits, wsp, wsb,
                                               _dev(out, "out"), _dev(lse, "lse"), _stream(stream))
     else:
-        nb, g, bs, _ = k_cache.shape
-        mb = block_table.shape[1]
         ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h, g, d, BF16, mb * bs, num_splits, 1),
                              q, workspace)
         wsp = ws.data_ptr() if ws is not None else None

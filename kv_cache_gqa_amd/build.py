@@ -37,8 +37,8 @@ COMPILE_FLAGS = [
 ]
 
 
-def _compile(src: str, extra: list[str], verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], verbose: bool, objdir: str = OBJDIR) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMPILE_FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,18 +48,23 @@ def _compile(src: str, extra: list[str], verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8,
+          out: str = LIB, objdir: str = OBJDIR, link_extra: list[str] | None = None) -> str:
+    """Compile every source and link ``out``.  ``extra`` goes to every
+    compile, ``link_extra`` to the link (a sanitizer build of the host code
+    passes its flags there; the default is the product library)."""
+    os.makedirs(objdir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(sources))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra or [], verbose), sources))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, extra or [], verbose, objdir), sources))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *(link_extra or []),
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

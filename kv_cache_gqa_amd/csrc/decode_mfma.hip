@@ -218,21 +218,27 @@ struct MfmaEngine {
 
         // A call that appends writes its new tokens (positions raw ..
         // raw+n-1, the last ones of the unit) into their cache slots here,
-        // once per unit, and attends to them as a last tile built from
+        // once per unit, and attends to them as last tiles built from
         // k_new / v_new (FP8: from their codes, n = 1).
         const int fresh_lo = max(s, raw);
-        const bool has_new = a.k_new != nullptr && fresh_lo < e;  // at most n <= 32 positions
+        const bool has_new = a.k_new != nullptr && fresh_lo < e;
         const int e_cache = has_new ? fresh_lo : e;
         if (has_new) {
             if (KV8) store_new_rows_fp8_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
             else store_new_rows_bf16_d128(a, b, j, raw, fresh_lo, e, tid, 64 * W);
         }
-        // The wavefront that takes the new tile.  With one new token (always
-        // so without GEN) it loads the token's K and V rows now, one bf16
-        // pair of each per lane, so that the last tile does not wait for
-        // them; the tile is then built from those pairs through LDS.
+        // The new positions [fresh_lo, e) form tiles of 32 (more than one
+        // when more than 32 new tokens reach this segment); new tile i goes
+        // to wavefront (first + i) % W, first being the wavefront next in
+        // turn after the cached tiles.  With one new token (always so
+        // without GEN) the single new tile's wavefront loads the token's K
+        // and V rows now, one bf16 pair of each per lane, so that the last
+        // tile does not wait for them; the tile is then built from those
+        // pairs through LDS.
         constexpr bool kNewPair = KV8 || !GEN;
-        const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
+        const int new_tiles = has_new ? (e - fresh_lo + kTileTokens - 1) / kTileTokens : 0;
+        const int new_i0 = (wave - ((fresh_lo - s) / kTileTokens) % W + W) % W;  // this wave's first
+        const bool new_wave = new_i0 < new_tiles;
         const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : Q;
@@ -505,12 +511,20 @@ struct MfmaEngine {
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
         }
         // The appended tokens (the last positions of the unit) are taken
-        // last, as one tile by the wavefront next in turn.
+        // last, tile i by wavefront (first + i) % W.
         if (new_wave) {
             w1 = e;
-            TileRegs<KV8> tr;
-            load_new_tile(fresh_lo, tr);
-            compute_tile(fresh_lo, tr, no_hook, no_hook);
+            if constexpr (kNewPair) {  // one new token: one tile
+                TileRegs<KV8> tr;
+                load_new_tile(fresh_lo, tr);
+                compute_tile(fresh_lo, tr, no_hook, no_hook);
+            } else {
+                for (int t = fresh_lo + kTileTokens * new_i0; t < e; t += kTileTokens * W) {
+                    TileRegs<KV8> tr;
+                    load_new_tile(t, tr);
+                    compute_tile(t, tr, no_hook, no_hook);
+                }
+            }
         }
 
         // lex holds this lane's positions only: sum the four row groups.

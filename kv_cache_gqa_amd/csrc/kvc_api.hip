@@ -219,6 +219,14 @@ static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, b
     return split;
 }
 
+// Alignment the kernels' vector accesses rely on: 16 bytes for tensors of
+// elements (q, caches and pools, k_new / v_new, out, the workspace), 4 bytes
+// for arrays of int32 or float32 values (seq_lens, block tables, lse,
+// scales, pairs, parents).  A null pointer counts as aligned (the null
+// checks are separate).
+static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
 static int ilog2_exact(int x) {
     int l = 0;
     while ((1 << l) < x) ++l;
@@ -234,6 +242,8 @@ static int check_common(const void* q, const void* k, const void* v, const int32
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     if (d > 256) return KVC_ERR_UNSUPPORTED;
     if (B > 0 && (!q || !k || !v || !seq_lens || !out || !lse)) return KVC_ERR_INVALID;
+    if (!al16(q) || !al16(k) || !al16(v) || !al16(out) || !al4(seq_lens) || !al4(lse))
+        return KVC_ERR_INVALID;
     if (B > 65535 || g > 65535) return KVC_ERR_UNSUPPORTED;
     return KVC_OK;
 }
@@ -280,6 +290,9 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
     Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0);
     const size_t need = required_workspace(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
+    if (!al16(workspace) || !al16(a.k_new) || !al16(a.v_new) || !al4(a.block_table) ||
+        !al4(a.k_scale) || !al4(a.v_scale))
+        return KVC_ERR_INVALID;
     if (a.B == 0) return KVC_OK;
     resolve_launch(a, sc, paged, max_len);
     const size_t rows = workspace_rows(a.B, a.h, a.g, sc);
@@ -383,6 +396,9 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
     if (B == 0) return KVC_OK;
     if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens_before) return KVC_ERR_INVALID;
     if (block_table != nullptr && (max_blocks <= 0 || block_size <= 0)) return KVC_ERR_INVALID;
+    if (!al16(k_new) || !al16(v_new) || !al16(k_cache) || !al16(v_cache) || !al4(block_table) ||
+        !al4(seq_lens_before))
+        return KVC_ERR_INVALID;
     const int eb = dtype == KVC_F32 ? 4 : 2;
     if (launch_append(k_new, v_new, k_cache, v_cache, block_table, max_blocks, block_size,
                       seq_lens_before, B, g, 1, d, capacity, 0, eb, stream) != hipSuccess)
@@ -611,6 +627,7 @@ int kvc_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pa
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     if (num_pairs == 0) return KVC_OK;
     if (!k_pool || !v_pool || !pairs) return KVC_ERR_INVALID;
+    if (!al16(k_pool) || !al16(v_pool) || !al4(pairs)) return KVC_ERR_INVALID;
     const long block_bytes = (long)g * block_size * d * (dtype == KVC_F32 ? 4 : 2);
     if (launch_copy_blocks(k_pool, v_pool, pairs, num_pairs, num_blocks, block_bytes, stream) !=
         hipSuccess)
@@ -626,6 +643,9 @@ int kvc_fork_block_tables(const int32_t* block_table, const int32_t* seq_lens, i
     if (!block_table || !seq_lens || !parent || !block_table_out || !seq_lens_out)
         return KVC_ERR_INVALID;
     if (block_table_out == block_table || seq_lens_out == seq_lens) return KVC_ERR_INVALID;
+    if (!al4(block_table) || !al4(seq_lens) || !al4(parent) || !al4(block_table_out) ||
+        !al4(seq_lens_out))
+        return KVC_ERR_INVALID;
     if (launch_fork_tables(block_table, seq_lens, B_src, max_blocks, parent, B, block_table_out,
                            seq_lens_out, stream) != hipSuccess)
         return KVC_ERR_HIP;
@@ -640,6 +660,9 @@ int kvc_gather_cache(const void* k_src, const void* v_src, const int32_t* seq_le
     if (B == 0) return KVC_OK;
     if (!k_src || !v_src || !seq_lens || !parent || !k_dst || !v_dst) return KVC_ERR_INVALID;
     if (k_dst == k_src || v_dst == v_src || k_dst == v_src || v_dst == k_src || k_dst == v_dst)
+        return KVC_ERR_INVALID;
+    if (!al16(k_src) || !al16(v_src) || !al16(k_dst) || !al16(v_dst) || !al4(seq_lens) ||
+        !al4(parent))
         return KVC_ERR_INVALID;
     if ((long)B * g > 0x7fffffffL || ceil_div(t_cap, 64) > 65535) return KVC_ERR_UNSUPPORTED;
     const long row_bytes = (long)d * (dtype == KVC_F32 ? 4 : 2);
@@ -658,6 +681,9 @@ int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_
     if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !seq_lens_before)
         return KVC_ERR_INVALID;
     if (block_table != nullptr && (max_blocks <= 0 || block_size <= 0)) return KVC_ERR_INVALID;
+    if (!al16(k_new) || !al16(v_new) || !al16(k_cache) || !al16(v_cache) || !al4(k_scale) ||
+        !al4(v_scale) || !al4(block_table) || !al4(seq_lens_before))
+        return KVC_ERR_INVALID;
     if (launch_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
                           max_blocks, block_size, seq_lens_before, B, g, 1, d, capacity, 0,
                           stream) != hipSuccess)

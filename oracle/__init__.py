@@ -49,10 +49,13 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvc_oracle.so")
+# KVC_ORACLE_LIB names another build of kvc_oracle.c (the sanitizer test
+# loads one built with AddressSanitizer and UndefinedBehaviorSanitizer).
+LIB_PATH = os.environ.get("KVC_ORACLE_LIB") or os.path.join(HERE, "libkvc_oracle.so")
 
 F32 = 0
 BF16 = 1
+F64 = 2  # values already in float64 (dequantised FP8 codes, widened queries)
 
 _lib = None
 
@@ -102,12 +105,16 @@ def _raw(x, dtype_code=None):
             return t.view(torch.int16).numpy().view(np.uint16), BF16
         if t.dtype == torch.float32:
             return t.numpy(), F32
+        if t.dtype == torch.float64:
+            return t.numpy(), F64
         if t.dtype == torch.int32:
             return t.numpy(), None
         raise TypeError(f"unsupported oracle input dtype {t.dtype}")
     a = np.ascontiguousarray(x)
     if a.dtype == np.float32:
         return a, F32
+    if a.dtype == np.float64:
+        return a, F64
     if a.dtype == np.uint16:  # raw bf16 bits
         return a, BF16
     if a.dtype == np.int32:
@@ -483,60 +490,33 @@ def append_fp8(k_new, v_new, k_codes, v_codes, k_scale, v_scale, seq_lens_before
     return kc, vc
 
 
+def dequantize_fp8(codes, scale, head_axis):
+    """float64 values of E4M3 codes with one float32 scale per KV head
+    (``scale`` [g], indexed along ``head_axis``): the code's value times its
+    head's scale.  Both factors are exact in float64 and so is their product
+    (at most 4 + 24 significant bits)."""
+    x = e4m3_values()[np.asarray(codes, dtype=np.uint8)]
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    shape = [1] * x.ndim
+    shape[head_axis] = -1
+    return x * sc.reshape(shape)
+
+
+def widen(x):
+    """float64 copy of bf16 / float32 values (exact)."""
+    a, code = _raw(x)
+    if code == BF16:
+        a = (a.astype(np.uint32) << 16).view(np.float32)
+    return np.asarray(a, dtype=np.float64)
+
+
 def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale, block_table=None,
                block_size=16, nthreads=0):
-    """Single-token attention over dequantised FP8 caches: K = code * k_scale[j],
-    V = code * v_scale[j].  The code values are exact in float32, so each KV
-    head j is attended with the plain definition over the code values with
-    score scale scale * k_scale[j] (the float32 scale times the float32 head
-    scale, exact in float64) and its output multiplied by v_scale[j]."""
-    vals = e4m3_values().astype(np.float32)
-    kf = vals[np.asarray(k_codes, dtype=np.uint8)]
-    vf = vals[np.asarray(v_codes, dtype=np.uint8)]
-    qa, _ = _raw(q)
-    B, h, d = qa.shape
-    g = kf.shape[1]
-    m = h // g
-    ks = np.asarray(k_scale, dtype=np.float32)
-    vs = np.asarray(v_scale, dtype=np.float32)
-    out = np.zeros((B, h, d), dtype=np.float64)
-    lse = np.zeros((B, h), dtype=np.float64)
-    s32 = float(np.float32(scale))
-    for j in range(g):
-        qj = np.ascontiguousarray(qa[:, j * m:(j + 1) * m])
-        kj = np.ascontiguousarray(kf[:, j:j + 1])
-        vj = np.ascontiguousarray(vf[:, j:j + 1])
-        o, l = _decode_exact_scale(qj, kj, vj, seq_lens, s32 * float(ks[j]), block_table,
-                                   block_size, nthreads)
-        out[:, j * m:(j + 1) * m] = o * float(vs[j])
-        lse[:, j * m:(j + 1) * m] = l
-    return out, lse
-
-
-def _decode_exact_scale(q, k, v, seq_lens, scale_f64, block_table, block_size, nthreads):
-    """``decode`` with the score scale used as the given float64 value."""
-    qa, qd = _raw(q)
-    ka, kd = _raw(k)
-    va, vd = _raw(v)
-    if qd != kd:  # bf16 queries over float32 code values: widen q exactly
-        qa = (qa.astype(np.uint32) << 16).view(np.float32) if qd == BF16 else qa
-        qd = F32
-    dt = _same_dtype(qd, kd, vd)
-    sl = _i32(seq_lens)
-    B, h, d = qa.shape
-    if block_table is None:
-        _, g, t_cap, _ = ka.shape
-        bt, max_blocks, bsz = None, 0, 0
-    else:
-        bt = _i32(block_table)
-        _, g, bsz, _ = ka.shape
-        assert bsz == block_size
-        max_blocks = bt.shape[1]
-        t_cap = 0
-    out = np.zeros((B, h, d), dtype=np.float64)
-    lse = np.zeros((B, h), dtype=np.float64)
-    _load().kvo_decode(_ptr(np.ascontiguousarray(qa)), _ptr(ka), _ptr(va), dt,
-                       _ptr(bt) if bt is not None else None, max_blocks, bsz,
-                       _ptr(sl), B, h, g, d, t_cap, float(scale_f64), _ptr(out), _ptr(lse),
-                       int(nthreads))
-    return out, lse
+    """Single-token attention over FP8 caches: dequantise, then the plain
+    definition.  K = code * k_scale[j] and V = code * v_scale[j] in float64
+    (``dequantize_fp8``), the bf16 queries widened to float64, and ``decode``
+    over those values with the same float32 score scale."""
+    k = dequantize_fp8(k_codes, k_scale, 1)
+    v = dequantize_fp8(v_codes, v_scale, 1)
+    return decode(widen(q), k, v, seq_lens, scale, block_table=block_table,
+                  block_size=block_size, nthreads=nthreads)

@@ -12,14 +12,16 @@ SRC = os.path.join(HERE, "kvc_oracle.c")
 LIB = os.path.join(HERE, "libkvc_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, extra: list | None = None) -> str:
+    """Compile kvc_oracle.c into ``out``; ``extra`` flags go to gcc (the
+    sanitizer test builds a copy with AddressSanitizer and UBSan)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", LIB + ".tmp", SRC, "-lm"]
+           *(extra or []), "-o", out + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -42,11 +42,15 @@
 
 #define KVO_F32 0
 #define KVO_BF16 1
+#define KVO_F64 2 /* values already widened (e.g. dequantised FP8 codes) */
 
 /* Exact widening of one stored element to double.  A bf16 value is the top
  * 16 bits of an IEEE-754 binary32, so shifting its bits up by 16 gives the
  * float with the same value. */
 static double load_elem(const void* base, size_t idx, int dtype) {
+    if (dtype == KVO_F64) {
+        return ((const double*)base)[idx];
+    }
     if (dtype == KVO_F32) {
         return (double)((const float*)base)[idx];
     }
@@ -56,7 +60,9 @@ static double load_elem(const void* base, size_t idx, int dtype) {
     return (double)f;
 }
 
-static size_t elem_bytes(int dtype) { return dtype == KVO_F32 ? 4u : 2u; }
+static size_t elem_bytes(int dtype) {
+    return dtype == KVO_F64 ? 8u : (dtype == KVO_F32 ? 4u : 2u);
+}
 
 /* Row index (in units of d elements) of the K/V vector of sequence b, KV head
  * j, logical position p.

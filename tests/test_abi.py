@@ -355,3 +355,48 @@ def test_public_calls_carry_the_device_guard():
         fn = getattr(kvc, name)
         assert hasattr(fn, "__wrapped__"), name
         assert name in kvc.__all__, name
+
+
+def test_misaligned_pointers_are_rejected_before_any_hip_call():
+    """Element tensors must be 16-byte aligned, int32/float32 arrays 4-byte
+    aligned; anything else is KVC_ERR_INVALID (the pointers are never
+    dereferenced: validation fails first)."""
+    lib = kvc.load_library()
+    off8 = ctypes.c_void_p(0x1008)   # 8-byte aligned, not 16
+    off2 = ctypes.c_void_p(0x1002)   # 2-byte aligned, not 4
+    for i in (0, 1, 2, 14):          # q, k_cache, v_cache, out
+        bad = [FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, 1, None, 0, FAKE, FAKE, None]
+        bad[i] = off8
+        assert lib.kvc_decode_attention(*bad) == INVALID, i
+    for i in (3, 15):                # seq_lens, lse
+        bad = [FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, 1, None, 0, FAKE, FAKE, None]
+        bad[i] = off2
+        assert lib.kvc_decode_attention(*bad) == INVALID, i
+    # the workspace of a split plan
+    need = lib.kvc_decode_workspace_bytes(2, 8, 2, 128, 1, 64, 2, 0)
+    args = [FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, 2, off8, need, FAKE, FAKE, None]
+    assert lib.kvc_decode_attention(*args) == INVALID
+    # k_new / v_new of the one-call step
+    fargs = [FAKE, off8, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, 1, None, 0, FAKE, FAKE,
+             None]
+    assert lib.kvc_append_decode_attention(*fargs) == INVALID
+    # the block table of a paged call
+    assert lib.kvc_decode_attention_paged(FAKE, FAKE, FAKE, off2, 8, 16, 10, FAKE, 2, 8, 2, 128,
+                                          0.1, 1, 1, None, 0, FAKE, FAKE, None) == INVALID
+    # FP8 scales
+    assert lib.kvc_decode_attention_fp8(FAKE, FAKE, FAKE, off2, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1,
+                                        1, None, 0, FAKE, FAKE, None) == INVALID
+    # append, block copies, forks, gathers
+    assert lib.kvc_append(FAKE, FAKE, off8, FAKE, None, 0, 0, FAKE, 2, 2, 128, 64, 1,
+                          None) == INVALID
+    assert lib.kvc_append(FAKE, FAKE, FAKE, FAKE, None, 0, 0, off2, 2, 2, 128, 64, 1,
+                          None) == INVALID
+    assert lib.kvc_append_fp8(off8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 2, 2, 128, 64,
+                              None) == INVALID
+    assert lib.kvc_copy_blocks(off8, FAKE, FAKE, 2, 8, 2, 16, 128, 1, None) == INVALID
+    assert lib.kvc_copy_blocks(FAKE, FAKE, off2, 2, 8, 2, 16, 128, 1, None) == INVALID
+    other = ctypes.c_void_p(0x2000)
+    assert lib.kvc_fork_block_tables(FAKE, FAKE, 2, 4, off2, 2, other, ctypes.c_void_p(0x3000),
+                                     None) == INVALID
+    assert lib.kvc_gather_cache(FAKE, FAKE, FAKE, 2, FAKE, 2, other, off8, 2, 64, 128, 1,
+                                None) == INVALID

@@ -29,6 +29,10 @@ CASES = [
     ("mfma_rows30", dict(h=6, g=1, d=128, dtype="bf16"), 5),
     ("mfma_slices_64", dict(h=16, g=2, d=128, dtype="bf16"), 8),
     ("mfma_slices_33", dict(h=11, g=1, d=128, dtype="bf16"), 3),
+    # one query head per KV head and more than 32 new tokens: the new
+    # positions span two or more 32-position tiles
+    ("mfma_mha_n33", dict(h=1, g=1, d=128, dtype="bf16"), 33),
+    ("mfma_mha_n64", dict(h=2, g=2, d=128, dtype="bf16"), 64),
     ("generic_f32_d16", dict(h=4, g=2, d=16, dtype="f32"), 3),
     ("generic_f32_rows40", dict(h=8, g=1, d=16, dtype="f32"), 5),
 ]

@@ -156,3 +156,33 @@ def test_launch_planning_from_many_threads():
         assert want[1] > 1 or B * g == 1, (c, want)
         got = {results[(t, r, k)] for t in range(8) for r in range(20)}
         assert got == {want}, (c, got, want)
+
+
+@pytest.mark.parametrize("handle", [False, True], ids=["stream_object", "raw_handle"])
+def test_explicit_side_stream_owns_its_allocations(handle):
+    """stream= names a side stream (a torch stream, or its raw HIP handle):
+    the outputs and the split plan's workspace are allocated for that
+    stream, so work the default stream queues meanwhile (allocations and
+    writes) cannot reuse their memory while the call still runs."""
+    print(f"case side_stream handle={handle}", file=sys.stderr, flush=True)
+    gen = torch.Generator().manual_seed(506)
+    L = torch.randint(1, 6000, (6,), generator=gen, dtype=torch.int32)
+    w = W.Workload("side", B=6, h=16, g=2, d=128, dtype="bf16", T=0, seed=507)
+    x = W.make_contiguous(w, lengths=L)
+    q, kc, vc, sl = dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"]), dev(L)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    results = []
+    for rep in range(3):
+        out, lse = kvc.decode(q, kc, vc, sl, num_splits=5,
+                              stream=s.cuda_stream if handle else s)
+        # the default stream allocates and fills memory while the side stream runs
+        junk = [torch.full((1 << 20,), float(rep + 1), device="cuda") for _ in range(8)]
+        del junk
+        s.synchronize()
+        results.append((out.clone(), lse.clone()))
+        assert out.device.index == torch.cuda.current_device()
+    ro, rl = oracle.decode(x["q"], x["k_cache"], x["v_cache"], L, x["scale"])
+    for out, lse in results:
+        check_parity(out, lse, ro, rl, attended_vmax_contig(x["v_cache"], L), "side stream")
+        assert torch.equal(out, results[0][0]) and torch.equal(lse, results[0][1])

@@ -26,6 +26,9 @@ SHAPES = [
     ("mfma_rows32", dict(h=16, g=2, d=128, dtype="bf16"), 4),
     ("mfma_slices_64", dict(h=16, g=2, d=128, dtype="bf16"), 8),
     ("generic_f32_d16", dict(h=4, g=2, d=16, dtype="f32"), 2),
+    # more than 32 new tokens per KV head: the new positions span two tiles
+    ("mfma_mha_n33", dict(h=2, g=2, d=128, dtype="bf16"), 33),
+    ("mfma_mha_n64", dict(h=1, g=1, d=128, dtype="bf16"), 64),
 ]
 BEFORE = [0, 1, 5, 31, 32, 33, 100, 1000, 4095, 5000]
 

@@ -241,10 +241,25 @@ def _quantize_by_multiply(x, scale, head_axis):
     return oracle.e4m3_encode((xf * sc.reshape(shape)).astype(np.float32))
 
 
+def _dequantize_dividing(codes, scale, head_axis):
+    x = oracle.e4m3_values()[np.asarray(codes, dtype=np.uint8)]
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    shape = [1] * x.ndim
+    shape[head_axis] = -1
+    return x / sc.reshape(shape)
+
+
+def _dequantize_first_head_scale(codes, scale, head_axis):
+    x = oracle.e4m3_values()[np.asarray(codes, dtype=np.uint8)]
+    return x * float(np.asarray(scale, dtype=np.float32)[0])
+
+
 FP8_MUTATIONS = {
     "ties_to_odd": ("e4m3_encode", _encode_ties_odd),
     "no_saturation": ("e4m3_encode", _encode_no_saturation),
     "scale_multiplies": ("quantize_fp8", _quantize_by_multiply),
+    "dequantise_divides": ("dequantize_fp8", _dequantize_dividing),
+    "dequantise_one_scale": ("dequantize_fp8", _dequantize_first_head_scale),
 }
 
 
