@@ -81,20 +81,7 @@ struct Lds {
 // in the whole-unit kernel and make the 4-wavefront stream kernels spill.
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// Transposing 8-byte LDS read (gfx950 ds_read_b64_tr_b16).
-__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
-    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)((__attribute__((address_space(3))) unsigned char*)p));
-    return __builtin_bit_cast(uint2, r);
-}
-
-__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
+__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) { return mfma_bf16(a, b, c); }
 
 // Registers of one wavefront's 32-position tile.  bf16: K rows as MFMA A
 // operands (chunk ks: dims 32*ks + 8*G .. +8) and V rows 4u + G, dims

@@ -246,6 +246,27 @@ __device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, in
     }
 }
 
+// Transposing 8-byte LDS read (gfx950 ds_read_b64_tr_b16): within each
+// 16-lane group, lanes 4r..4r+3 read 8 contiguous bytes each of one row r
+// (r = 0..3), and lane i receives element i of each of the four rows -- one
+// column of four rows, the MFMA operand layout of a transposed matrix.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)((__attribute__((address_space(3))) unsigned char*)p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+// D = A B + C on the matrix cores, 16x16 fp32 result from 16x32 bf16 A and
+// 32x16 bf16 B (v_mfma_f32_16x16x32_bf16).  Lane l holds row l % 16 of A and
+// column l % 16 of B, elements 8*(l/16) .. +8 of the 32-long k dimension;
+// it receives rows 4*(l/16) .. +4 of column l % 16 of D.
+__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // LDS writes of a wavefront visible to all its lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -213,11 +213,17 @@ def append(k_new, v_new, k_cache, v_cache, seq_lens_before, block_table=None, bl
     if block_table is None:
         t_cap = kc.shape[2]
         bt, max_blocks, bsz = None, 0, 0
+        if B and (sl.min() < 0 or sl.max() >= t_cap):
+            raise ValueError("append position outside the cache")
     else:
         bt = _i32(block_table)
         max_blocks = bt.shape[1]
         bsz = kc.shape[2]
         t_cap = 0
+        blk = sl // bsz
+        if B and (sl.min() < 0 or blk.max() >= max_blocks or
+                  any(not 0 <= bt[b, blk[b]] < kc.shape[0] for b in range(B))):
+            raise ValueError("append position outside the pool")
     _load().kvo_append(_ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), dt,
                        _ptr(bt) if bt is not None else None, max_blocks, bsz,
                        _ptr(sl), B, g, d, t_cap)

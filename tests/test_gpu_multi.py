@@ -68,7 +68,7 @@ def _inputs(name, s, n, seed, paged=False, block_size=16):
     q = W.randn((B, w.h, n, w.d), w.torch_dtype, gen)
     k_new = W.randn((B, w.g, n, w.d), w.torch_dtype, gen)
     v_new = W.randn((B, w.g, n, w.d), w.torch_dtype, gen)
-    x = W.make_contiguous(w, lengths=before, t_cap=T_CAP, fill=float("nan"))
+    x = W.make_contiguous(w, lengths=before, t_cap=max(T_CAP, max(BEFORE) + n), fill=float("nan"))
     if paged:
         table, nb = W.make_block_table(before + n, block_size, perm_seed=seed + 2, extra_blocks=3)
         kc = W.scatter_to_pool(x["k_cache"], before, table, nb, block_size, fill=float("nan"))
