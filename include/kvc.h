@@ -76,7 +76,9 @@ typedef enum kvc_status {
                                  num_splits < -1 */
     KVC_ERR_UNSUPPORTED = 2,  /* dtype or head_dim not built (head_dim must be 1..256) */
     KVC_ERR_WORKSPACE = 3,    /* workspace missing or smaller than kvc_decode_workspace_bytes */
-    KVC_ERR_HIP = 4           /* a HIP launch reported an error */
+    KVC_ERR_HIP = 4,          /* a HIP launch reported an error */
+    KVC_ERR_SCRATCH = 5       /* kvc_append_decode_attention_noalloc: the split needs more
+                                 than kvc_noalloc_scratch_bytes() of scratch */
 } kvc_status;
 
 /* KVC_FP8_E4M3 is for the planning queries only (kvc_decode_plan,
@@ -261,6 +263,33 @@ int kvc_append_decode_attention_paged(const void* q, const void* k_new, const vo
                                       float scale, int dtype, int num_splits, void* workspace,
                                       size_t workspace_bytes, float* out, float* lse,
                                       hipStream_t stream);
+
+/*
+ * kvc_append_decode_attention_noalloc -- for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): kvc_append_decode_attention with no
+ * workspace argument.  Same arguments otherwise, same kernels, same results.
+ *
+ * When the call's plan splits positions, the partial results go to a
+ * static device buffer of the library (kvc_noalloc_scratch_bytes() = 16 MiB,
+ * one per GPU, held from the first use of the library on that GPU until the
+ * process ends) instead of a workspace; nothing is allocated, and the
+ * buffer needs no clearing (every call writes the partials it reads).  A
+ * call whose plan needs more (kvc_decode_workspace_bytes(B, h, g, d, dtype,
+ * t_cap, num_splits, 0) > 16 MiB) returns KVC_ERR_SCRATCH before any HIP
+ * call; choose fewer splits, or call kvc_append_decode_attention with a
+ * workspace.  All calls on one GPU share the buffer: calls that may overlap
+ * in time on one GPU (different streams, or several host threads) race on
+ * it and must be serialised by the caller.  The first call on a device
+ * queries the buffer's device address (hipGetSymbolAddress) with that
+ * device current.
+ */
+int kvc_append_decode_attention_noalloc(const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache,
+                                        const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                        int t_cap, float scale, int dtype, int num_splits,
+                                        float* out, float* lse, hipStream_t stream);
+size_t kvc_noalloc_scratch_bytes(void);
 
 /*
  * Several new tokens per sequence at once: kvc_decode_attention_multi[_paged]

@@ -37,7 +37,8 @@ F32, BF16 = 0, 1
 SPLITS_STREAM = -1  # num_splits value that asks for the stream split
 _MODES = {0: "chunks", 1: "stream", 2: "auto_chunks"}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype or shape",
-           3: "workspace missing or too small", 4: "HIP launch error"}
+           3: "workspace missing or too small", 4: "HIP launch error",
+           5: "split needs more than the library's static scratch"}
 
 _lib = None
 
@@ -73,6 +74,11 @@ def load_library():
     lib.kvc_append_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip,
                                                 ip, vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention.restype = ip
+    lib.kvc_append_decode_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip,
+                                                        fp, ip, ip, vp, vp, vp]
+    lib.kvc_append_decode_attention_noalloc.restype = ip
+    lib.kvc_noalloc_scratch_bytes.argtypes = []
+    lib.kvc_noalloc_scratch_bytes.restype = sz
     lib.kvc_append_decode_attention_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, vp, ip,
                                                       ip, ip, ip, fp, ip, ip, vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention_paged.restype = ip

@@ -284,11 +284,50 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     }
 }
 
+// Scratch of kvc_append_decode_attention_noalloc: the split partials of one
+// call live in this file-scope device array instead of a caller's
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: its device address comes from hipGetSymbolAddress,
+// once per device (scratch_address), and only that address is used.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's `scratch` (nullptr if the query fails).
+// The first call on a device makes the query with that device current.
+static void* scratch_address() {
+    static void* addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_cache_lock);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+// Marker for run_decode: take the split partials from `scratch`.
+static char g_use_scratch;
+static void* const kUseScratch = &g_use_scratch;
+
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
     const bool paged = a.block_table != nullptr;
     Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0);
     const size_t need = required_workspace(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
+    if (workspace == kUseScratch) {
+        // every other argument has been validated by now
+        if (need > kScratchBytes) return KVC_ERR_SCRATCH;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0 && a.B > 0) {
+            workspace = scratch_address();
+            if (workspace == nullptr) return KVC_ERR_HIP;
+            workspace_bytes = kScratchBytes;
+        }
+    }
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVC_ERR_WORKSPACE;
     if (!al16(workspace) || !al16(a.k_new) || !al16(a.v_new) || !al4(a.block_table) ||
         !al4(a.k_scale) || !al4(a.v_scale))
@@ -334,6 +373,7 @@ const char* kvc_status_string(int status) {
         case KVC_ERR_UNSUPPORTED: return "unsupported dtype or shape";
         case KVC_ERR_WORKSPACE: return "workspace missing or too small";
         case KVC_ERR_HIP: return "HIP launch error";
+        case KVC_ERR_SCRATCH: return "the call needs more split scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
@@ -511,6 +551,19 @@ int kvc_append_decode_attention(const void* q, const void* k_new, const void* v_
                              seq_lens_before, B, h, g, d, 1, t_cap, 0, 0, scale, dtype, num_splits,
                              workspace, workspace_bytes, out, lse, stream);
 }
+
+int kvc_append_decode_attention_noalloc(const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache,
+                                        const int32_t* seq_lens_before, int B, int h, int g, int d,
+                                        int t_cap, float scale, int dtype, int num_splits,
+                                        float* out, float* lse, hipStream_t stream) {
+    if (B > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
+                             seq_lens_before, B, h, g, d, 1, t_cap, 0, 0, scale, dtype, num_splits,
+                             kUseScratch, 0, out, lse, stream);
+}
+
+size_t kvc_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int kvc_append_decode_attention_paged(const void* q, const void* k_new, const void* v_new,
                                       void* k_pool, void* v_pool, const int32_t* block_table,

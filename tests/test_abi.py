@@ -400,3 +400,27 @@ def test_misaligned_pointers_are_rejected_before_any_hip_call():
                                      None) == INVALID
     assert lib.kvc_gather_cache(FAKE, FAKE, FAKE, 2, FAKE, 2, other, off8, 2, 64, 128, 1,
                                 None) == INVALID
+
+
+def test_noalloc_validation_codes():
+    """kvc_append_decode_attention_noalloc validates like the workspace entry
+    point and rejects a split beyond its static scratch (KVC_ERR_SCRATCH)
+    before any HIP call."""
+    lib = kvc.load_library()
+    f = lib.kvc_append_decode_attention_noalloc
+    assert lib.kvc_noalloc_scratch_bytes() == 16 << 20
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0.1, 1, 1, FAKE, FAKE, None]
+    bad = list(args); bad[1] = None                  # k_new missing
+    assert f(*bad) == INVALID
+    bad = list(args); bad[8] = 3                     # h % g != 0
+    assert f(*bad) == INVALID
+    bad = list(args); bad[0] = ctypes.c_void_p(0x1008)  # misaligned q
+    assert f(*bad) == INVALID
+    ok = list(args); ok[6] = 0                       # nothing to do
+    assert f(*ok) == OK
+    # 8 x 32 query rows over 131088 positions in 200 chunks: more than 16 MiB
+    # of partials
+    assert lib.kvc_decode_workspace_bytes(8, 32, 1, 128, 1, 131088, 200, 0) > 16 << 20
+    big = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 1, 128, 131088, 0.1, 1, 200, FAKE, FAKE, None]
+    assert f(*big) == 5
+    assert lib.kvc_status_string(5).startswith(b"the call needs more split scratch")
