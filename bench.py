@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -157,7 +158,44 @@ def algorithmic_bytes(w, attended, nblocks=None, n=1, kv_bytes=None):
                 fused=decode + new_read + append_write, kv_read=kv_read)
 
 
-def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0, fp8=None):
+def attention_flops(w, before, n=1, window=0):
+    """Floating-point operations of the attention of one step, counted per
+    visible position of every query row (not the dense rectangle): 2*d for
+    the score q.k and 2*d for adding p*V, so 4*d per (row, position).  Token
+    t of a sequence with ``before`` cached positions sees before + t + 1
+    positions, at most ``window`` with a sliding window."""
+    total = 0
+    for b0 in before.tolist():
+        for t in range(n):
+            vis = b0 + t + 1
+            total += min(vis, window) if window > 0 else vis
+    return 4 * w.d * w.h * total
+
+
+def cpu_model_name() -> str:
+    """The host CPU's model name (/proc/cpuinfo, or lscpu when that is terse)."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                alt = line.split(":", 1)[1].strip()
+                if len(alt) > len(model):
+                    model = alt
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return model
+
+
+def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0, fp8=None, decode_bytes=None):
     """The oracle (plain C, fp64, OpenMP over (sequence, head) rows) timed on
     this host on the same inputs.  Runs whole batches until about budget_s
     seconds have passed (at least one), reports decode tokens/s.  fp8:
@@ -195,18 +233,14 @@ def cpu_baseline(w, x, paged: bool, budget_s: float = 12.0, fp8=None):
         oracle.decode(x["q"], x["k_cache"], x["v_cache"], x["seq_lens_after"], x["scale"],
                       nthreads=1)
     single = time.perf_counter() - t0
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": w.B / per_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"full batch of the workload (B={w.B}), decode only, {runs} run(s), "
-                      f"{per_step:.3f} s per run",
-            "single_thread_value": w.B / single, "host_cpu": model}
+    res = {"value": w.B / per_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"full batch of the workload (B={w.B}), decode only, {runs} run(s), "
+                     f"{per_step:.3f} s per run",
+           "single_thread_value": w.B / single, "host_cpu": cpu_model_name()}
+    if decode_bytes:  # the same algorithmic bytes as the GPU's decode call
+        res["effective_gbs"] = round(decode_bytes / per_step / 1e9, 3)
+        res["single_thread_effective_gbs"] = round(decode_bytes / single / 1e9, 3)
+    return res
 
 
 def bench_block_op(args, torch, kvc, W):
@@ -285,6 +319,10 @@ def main():
     ap.add_argument("--queries", type=int, default=1,
                     help="new tokens per sequence in one step (draft tokens checked at once, or a "
                          "prefill chunk after the cached prefix): kvc_append_decode_attention_multi")
+    ap.add_argument("--slice-baseline", action="store_true",
+                    help="with --queries n: also time the attention of the same rows in groups "
+                         "of at most 32 rows per KV head, one kvc_decode_attention_multi call "
+                         "each (every call reads the unit's K/V), beside the one-call step")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window W: each token sees the last W positions up to itself "
                          "(kvc_append_decode_attention_window)")
@@ -343,8 +381,15 @@ def main():
         k_src, v_src = x["k_pool"], x["v_pool"]
         nblocks = W.block_counts(x["seq_lens_after"], x["block_size"])
     else:
-        # a ring cache holds W + n - 1 positions plus spare slots, every slot written
-        x = W.make_contiguous(w, t_cap=args.window + args.queries + 14 if args.ring else None)
+        # a ring cache holds W + n - 1 positions plus spare slots, every slot
+        # written; a linear cache holds the n new tokens past the spare slots
+        if args.ring:
+            t_cap = args.window + args.queries + 14
+        elif args.queries > w.cap_pad and w.T is not None:
+            t_cap = w.T + args.queries + w.cap_pad
+        else:
+            t_cap = None
+        x = W.make_contiguous(w, t_cap=t_cap)
         k_src, v_src = x["k_cache"], x["v_cache"]
         nblocks = None
     fp8 = args.kv_fp8
@@ -374,9 +419,12 @@ def main():
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     nq = args.queries
     win, ring = args.window, args.ring
-    if nq < 1 or (nq > 1 and (args.separate or w.paged or (nq > w.cap_pad and not ring))):
-        print(f"--queries takes n >= 1; n > 1 only with the one-call step on a contiguous "
-              f"workload, n <= {w.cap_pad} (the spare capacity)", file=sys.stderr)
+    if nq < 1 or (nq > 1 and (args.separate or w.paged or w.T is None)):
+        print("--queries takes n >= 1; n > 1 only with the one-call step on a contiguous "
+              "workload", file=sys.stderr)
+        sys.exit(2)
+    if args.slice_baseline and (nq < 2 or args.window):
+        print("--slice-baseline needs --queries n > 1 and no window", file=sys.stderr)
         sys.exit(2)
     if win < 0 or (win > 0 and args.separate) or (ring and (win <= 0 or w.paged)):
         print("--window takes W >= 0 with the one-call step; --ring needs --window and a "
@@ -578,6 +626,55 @@ def main():
     torch.cuda.synchronize()
     dec_avg_ms = d_start.elapsed_time(d_end) / (reps * copies)
 
+    # The same attention as groups of at most 32 rows per KV head, one
+    # kvc_decode_attention_multi call each over the cache that already holds
+    # the n tokens: every call reads its units' K/V again.
+    slice_res = None
+    if args.slice_baseline:
+        per = max(1, 32 // w.m)  # tokens per call
+        groups = [(t0, min(nq, t0 + per)) for t0 in range(0, nq, per)]
+        qs = [q[:, :, t0:t1].contiguous() for t0, t1 in groups]
+        outs = [torch.empty((w.B, w.h, t1 - t0, w.d), dtype=torch.float32, device=dev)
+                for t0, t1 in groups]
+        lses = [torch.empty((w.B, w.h, t1 - t0), dtype=torch.float32, device=dev)
+                for t0, t1 in groups]
+        sls = [(sl_before + t1).to(torch.int32) for t0, t1 in groups]
+        ws_s = torch.empty(max(1, kvc.workspace_bytes(w.B, w.h * per, w.g, w.d, k0.shape[2], ns)),
+                           dtype=torch.uint8, device=dev)
+
+        def slices_call(i):
+            kc, vc = ks[i % copies], vs[i % copies]
+            for qq, oo, ll, sl in zip(qs, outs, lses, sls):
+                kvc.decode_multi(qq, kc, vc, sl, scale=x["scale"], num_splits=ns, workspace=ws_s,
+                                 out=oo, lse=ll)
+        for r in range(copies):
+            slices_call(r)
+        torch.cuda.synchronize()
+        sgraph = None
+        if graphs:
+            sgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(sgraph):
+                for r in range(copies):
+                    slices_call(r)
+            sgraph.replay()
+            torch.cuda.synchronize()
+        s_start = torch.cuda.Event(enable_timing=True)
+        s_end = torch.cuda.Event(enable_timing=True)
+        s_start.record()
+        for _ in range(reps):
+            if sgraph is not None:
+                sgraph.replay()
+            else:
+                for r in range(copies):
+                    slices_call(r)
+        s_end.record()
+        torch.cuda.synchronize()
+        slice_ms = s_start.elapsed_time(s_end) / (reps * copies)
+        slice_res = {"calls_per_step": len(groups), "tokens_per_call": per,
+                     "ms_per_step": round(slice_ms, 5),
+                     "note": "attention only (the cache already holds the tokens), "
+                             "kvc_decode_attention_multi per group of <= 32 rows per KV head"}
+
     hi = x["seq_lens_before"].to(torch.int64) + nq
     lo = torch.clamp(x["seq_lens_before"].to(torch.int64) + 1 - win, min=0) if windowed \
         else torch.zeros_like(hi)
@@ -588,13 +685,19 @@ def main():
     call_bytes = nbytes["decode"] if args.separate else nbytes["fused"]
     achieved_gbs = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.B * nq / (ms_per_step * 1e-3)
+    # Which roof bounds the call: its bytes at 8 TB/s or its flops at the
+    # bf16 matrix-core peak, whichever takes longer.
+    flops = attention_flops(w, x["seq_lens_before"], n=nq, window=win)
+    mfma_bound = w.dtype == "bf16" and not fp8 and \
+        flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > call_bytes / (HBM_PEAK_GBS * 1e9)
+    achieved_tflops = flops / (dec_avg_ms * 1e-3) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline and nq == 1 and not windowed:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, x, w.paged,
                            fp8=(k_src.numpy(), v_src.numpy(), k_sc.numpy(), v_sc.numpy())
-                           if fp8 else None)
+                           if fp8 else None, decode_bytes=nbytes["decode"])
 
     res = {
         "metric": "decode tokens/s (GQA KV-cache attention, one layer)",
@@ -638,7 +741,19 @@ def main():
                          "note": "each step timed alone (includes its launch)"},
         "hot_ms_per_step": round(hot_ms, 5),
         "timing": "eager" if args.eager else "HIP graphs of whole steps (one step per cache copy)",
-        "roofline": {
+        "roofline": ({
+            "bound": "mfma",
+            "kernel": "append+decode call: " + ("partials + log-sum-exp merge" if merged
+                                                else "one kernel, no merge"),
+            "achieved": round(achieved_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops,
+            "flops_counted": "4*d per visible position per query row",
+            "hbm_achieved_gbs": round(achieved_gbs, 1),
+            "algorithmic_bytes_per_launch": call_bytes,
+            "decode_call_ms_avg": round(dec_avg_ms, 5),
+            "traffic": traffic,
+        } if mfma_bound else {
             "bound": "hbm",
             "kernel": ("decode call" if args.separate else "append+decode call") + ": "
                       + ("partials + log-sum-exp merge" if merged else "one kernel, no merge"),
@@ -647,9 +762,13 @@ def main():
             "algorithmic_bytes_per_launch": call_bytes,
             "decode_call_ms_avg": round(dec_avg_ms, 5),
             "traffic": traffic,
-        },
+            "mfma_achieved_tflops": round(achieved_tflops, 2),
+        }),
         "cpu_baseline": cpu,
     }
+    if slice_res is not None:
+        slice_res["speedup_of_one_call"] = round(slice_res["ms_per_step"] / dec_avg_ms, 3)
+        res["slice_baseline"] = slice_res
     print(json.dumps(res), flush=True)
 
 

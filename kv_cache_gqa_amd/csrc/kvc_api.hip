@@ -32,15 +32,34 @@ Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
     return Plan{(int)chunk, (int)ceil_div(max_seq_len, chunk)};
 }
 
-KernelKind choose_kernel(int dtype, int d, int m) {
-    if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : kMfma;
+// bf16 (or FP8) caches with head_dim 128: up to 3 rows per KV head on the
+// vector ALUs, 4..32 on the matrix-core decode kernel, more on the
+// multi-row kernel (bf16; FP8 caches run such rows as 32-row slices of the
+// decode kernel).  Everything else takes the generic kernel.
+KernelKind choose_kernel(int dtype, int d, int m, bool kv8) {
+    if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : (m <= 32 || kv8 ? kMfma : kPrefill);
     return kGeneric;
 }
 
-// Work-groups per unit that split its query rows: the MFMA kernels hold at
-// most 32 rows, so more rows (several new tokens per sequence) take slices
-// of 32, each reading the unit's K/V.
+// Work-groups per unit that split its query rows on the decode kernel: it
+// holds at most 32 rows, so more rows (FP8 caches only) take slices of 32,
+// each reading the unit's K/V.
 static int row_slices(KernelKind kind, int m) { return (kind == kMfma && m > 32) ? (m + 31) / 32 : 1; }
+
+// Shape of the multi-row kernel for m rows per KV head: 16-row query tiles
+// per wavefront, wavefronts per work-group, work-groups per unit.  Up to 64
+// rows (HBM-bound: a few rows per K/V byte) 16 rows per wavefront and four
+// wavefronts; up to 128, 32 rows per wavefront; beyond (bound by the matrix
+// cores) 256 rows per work-group of eight wavefronts, so that each K/V tile
+// staged in LDS serves 256 rows.
+struct PrefillShape {
+    int nqt, waves, row_blocks;
+};
+static PrefillShape prefill_shape(int m) {
+    if (m <= 64) return {1, 4, 1};
+    if (m <= 128) return {2, 4, 1};
+    return {2, 8, (m + 255) / 256};
+}
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -80,14 +99,16 @@ static long chunks_for_slots(long slots, int B, int g, int max_seq_len) {
 }
 
 static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq_len,
-                              int num_splits, bool paged, bool windowed = false) {
+                              int num_splits, bool paged, bool windowed = false,
+                              bool kv8 = false) {
     Schedule sc;
-    sc.kind = choose_kernel(dtype, d, h / g);
+    sc.kind = choose_kernel(dtype, d, h / g, kv8);
     // Stream mode keeps global positions in 64-bit products p * total with
     // p <= 1024: it is used only while B * g * max_seq_len < 2^40.
     const bool small_enough = (long double)B * g * max_seq_len < (long double)(1LL << 40);
     const int slices = row_slices(sc.kind, h / g);
-    const bool can_stream = sc.kind != kGeneric && slices == 1 && B <= kStreamMaxB && small_enough;
+    const bool can_stream = (sc.kind == kValu || sc.kind == kMfma) && slices == 1 &&
+                            B <= kStreamMaxB && small_enough;
     // automatic: paged caches stream (lengths vary); with a sliding window the
     // ranges are at most W + n - 1 long and nearly equal, so they chunk
     sc.stream = can_stream &&
@@ -255,6 +276,32 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     a.num_wgs = 0;
     a.waves = sc.kind == kGeneric ? 1 : 4;
     a.slices = row_slices(sc.kind, a.m);
+    a.row_blocks = 1;
+    a.nqt = 0;
+    if (sc.kind == kPrefill) {
+        const PrefillShape ps = prefill_shape(a.m);
+        a.nqt = ps.nqt;
+        a.waves = ps.waves;
+        a.row_blocks = ps.row_blocks;
+        if (sc.auto_chunks) {
+            // chunks per unit that fill the device's slots once, counting
+            // the row blocks; when the row blocks alone fill them, one chunk
+            // per unit (the kernel walks a long chunk in table windows) and
+            // no merge
+            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged), ps.waves);
+            const long groups = (long)a.B * ps.row_blocks * a.g;
+            if (groups >= slots) {
+                sc.plan = Plan{(int)(ceil_div(max_len, kTileTokens) * kTileTokens), 1};
+            } else {
+                const long C = chunks_for_slots(slots, a.B * ps.row_blocks, a.g, max_len);
+                sc.plan = C == 1 ? Plan{(int)(ceil_div(max_len, kTileTokens) * kTileTokens), 1}
+                                 : plan_for_chunks(max_len, C);
+            }
+        }
+        a.chunk_len = sc.plan.chunk_len;
+        a.num_chunks = sc.plan.num_chunks;
+        return;
+    }
     if (sc.stream) {
         long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4, general_features(a), a.kv8 != 0), 4);
         // No more work-groups than 256-position pieces of the largest possible batch.
@@ -315,7 +362,10 @@ static void* const kUseScratch = &g_use_scratch;
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
     const bool paged = a.block_table != nullptr;
-    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0);
+    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0,
+                                a.kv8 != 0);
+    // (the workspace query knows no FP8 flag: it sizes for the bf16 kernels,
+    // which bounds the FP8 ones)
     const size_t need = required_workspace(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
     if (workspace == kUseScratch) {
         // every other argument has been validated by now
@@ -347,6 +397,7 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
     switch (sc.kind) {
         case kValu: err = launch_decode_valu_bf16_d128(a, stream); break;
         case kMfma: err = launch_decode_mfma_bf16_d128(a, stream); break;
+        case kPrefill: err = launch_prefill_mfma(a, stream); break;
         default: err = launch_decode_generic(a, dtype, stream); break;
     }
     if (err != hipSuccess) return KVC_ERR_HIP;
@@ -402,7 +453,7 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     if (d > 256) return KVC_ERR_UNSUPPORTED;
-    Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
+    Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8);
     DecodeArgs a{};
     a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.n = 1; a.cap_len = max_seq_len;
     a.kv8 = kv8 ? 1 : 0;
@@ -410,7 +461,7 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     if (waves) *waves = a.waves;
     // the generic kernel: one wavefront per query row; the others: per unit
     // and row slice
-    const int per_chunk = sc.kind == kGeneric ? h : g * a.slices;
+    const int per_chunk = sc.kind == kGeneric ? h : g * a.slices * a.row_blocks;
     if (num_wgs) *num_wgs = a.stream ? a.num_wgs : a.num_chunks * per_chunk * B;
     if (chunk_len) *chunk_len = a.stream ? 0 : a.chunk_len;
     if (num_chunks) *num_chunks = a.stream ? 0 : a.num_chunks;

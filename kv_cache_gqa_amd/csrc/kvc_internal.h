@@ -72,6 +72,10 @@ struct DecodeArgs {
     // are served by ceil(m / 32) work-groups of 32 rows each, blockIdx.y =
     // j * slices + slice.
     int slices;
+    // Multi-row kernel (more than 32 rows per KV head, bf16): work-groups
+    // per unit over its rows, and 16-row query tiles per wavefront.
+    int row_blocks;
+    int nqt;
     // Sliding window: 0 = none; W > 0: a token at position x sees positions
     // max(0, x + 1 - W) .. x.  ring (contiguous only): position p lives in
     // slot p mod t_cap (positions are not clamped to the capacity).
@@ -93,6 +97,7 @@ struct DecodeArgs {
 hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prefill_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
@@ -100,6 +105,9 @@ hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
 // when that combination is not built.  MFMA: waves in {4, 8}; VALU: 4.
 const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8);
 const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8);
+// Multi-row kernel for (16-row query tiles per wavefront, wavefronts per
+// work-group, layout); nullptr when not built.
+const void* prefill_kernel(int nqt, int waves, bool paged);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }
@@ -122,7 +130,7 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, vo
                          int ring, int elem_bytes, hipStream_t s);
 
 // Which decode kernel a configuration uses (exposed for tests and tools).
-enum KernelKind { kGeneric = 0, kValu = 1, kMfma = 2 };
-KernelKind choose_kernel(int dtype, int d, int m);
+enum KernelKind { kGeneric = 0, kValu = 1, kMfma = 2, kPrefill = 3 };
+KernelKind choose_kernel(int dtype, int d, int m, bool kv8 = false);
 
 }  // namespace kvc

@@ -243,9 +243,105 @@ hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Chunked plans with d = 128 (every bf16 / FP8 head-dim-128 kernel): rows
+// packed into work-groups.  A (row, chunk group) is 32 lanes of 4 dims; a
+// row has G chunk groups (1, 2, 4 or 8 by the chunk count, so that no lane
+// folds more than eight chunks for up to 64 chunks: one round trip to
+// memory), and a 64-lane work-group holds 2 / G rows (G <= 2) or one row of
+// 32*G lanes.  The G partial states of a row are combined through LDS.
+template <int G>
+__global__ void __launch_bounds__(G <= 2 ? 64 : 32 * G) merge128_kernel(DecodeArgs a) {
+    constexpr int kRowsPerWg = G == 1 ? 2 : 1;
+    __shared__ float sm_m[G];
+    __shared__ float sm_w[G];
+    __shared__ float4 sm_o[G][32];
+    const int slot = threadIdx.x >> 5, lane = threadIdx.x & 31;
+    const int grp = slot % G;
+    const long row = (long)blockIdx.x * kRowsPerWg + slot / G;
+    const long rows = (long)a.B * a.h;
+    const int C = a.num_chunks;
+    float M = kNegInf, W = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < rows) {
+        for (int c0 = grp; c0 < C; c0 += G * kMergeBatch) {
+            float lse[kMergeBatch];
+            float4 x[kMergeBatch];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const int c = c0 + k * G;
+                const bool ok = c < C;
+                const long rec = row * C + (ok ? c : 0);
+                lse[k] = ok ? a.part_lse[rec] : kNegInf;
+                x[k] = ok ? *reinterpret_cast<const float4*>(a.part_o + rec * 128 + 4 * lane)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            float bm = M;
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, lse[k]);
+            const float ref = (bm == kNegInf) ? 0.0f : bm;
+            const float f = fast_exp2(M - ref);  // 0 while nothing was added
+            W *= f;
+            o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const float w = fast_exp2(lse[k] - ref);  // 0 for absent and empty chunks
+                W += w;
+                if (w > 0.0f) {  // the O of an empty chunk is never written
+                    o.x += w * x[k].x; o.y += w * x[k].y; o.z += w * x[k].z; o.w += w * x[k].w;
+                }
+            }
+            M = bm;
+        }
+    }
+    if constexpr (G > 1) {
+        if (lane == 0) {
+            sm_m[grp] = M;
+            sm_w[grp] = W;
+        }
+        sm_o[grp][lane] = o;
+        __syncthreads();
+        if (grp != 0) return;
+        float Mx = kNegInf;
+#pragma unroll
+        for (int q = 0; q < G; ++q) Mx = fmaxf(Mx, sm_m[q]);
+        const float ref = (Mx == kNegInf) ? 0.0f : Mx;
+        W = 0.0f;
+        o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const float f = fast_exp2(sm_m[q] - ref);
+            const float4 y = sm_o[q][lane];
+            W += sm_w[q] * f;
+            o.x += f * y.x; o.y += f * y.y; o.z += f * y.z; o.w += f * y.w;
+        }
+        M = Mx;
+    }
+    if (row >= rows) return;
+    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    *reinterpret_cast<float4*>(a.out + row * 128 + 4 * lane) =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (lane == 0) a.lse[row] = W > 0.0f ? (M + fast_log2(W)) * kLn2 : kNegInf;
+}
+
+template <int G>
+static void launch_merge128(const DecodeArgs& a, long rows, hipStream_t s) {
+    constexpr int kRowsPerWg = G == 1 ? 2 : 1;
+    constexpr int kThreads = G <= 2 ? 64 : 32 * G;
+    merge128_kernel<G><<<dim3((unsigned)((rows + kRowsPerWg - 1) / kRowsPerWg)), dim3(kThreads), 0,
+                         s>>>(a);
+}
+
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
     const long rows = (long)a.B * a.h;
-    merge_kernel<<<dim3((unsigned)rows), dim3(256), 0, s>>>(a);
+    if (a.d == 128) {
+        const int C = a.num_chunks;
+        if (C <= kMergeBatch) launch_merge128<1>(a, rows, s);
+        else if (C <= 2 * kMergeBatch) launch_merge128<2>(a, rows, s);
+        else if (C <= 4 * kMergeBatch) launch_merge128<4>(a, rows, s);
+        else launch_merge128<8>(a, rows, s);
+    } else {
+        merge_kernel<<<dim3((unsigned)rows), dim3(256), 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

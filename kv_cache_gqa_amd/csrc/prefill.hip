@@ -1,0 +1,373 @@
+// prefill.hip -- bf16 caches, head_dim 128, more than 32 query rows per KV
+// head: several new tokens per sequence attending at once (the new tokens
+// of a prefill after a cached prefix, "大语言模型研究15——注意力机制优化之KV
+// 缓存" (limoncc.com) section 5.2; draft tokens checked in one pass, "KV
+// Cache 优化与注意力机制加速" (plumephp.com) section 5.3), or more than 32
+// query heads per KV head.
+//
+// Query rows of one unit (sequence b, KV head j) are r = 0 .. m-1, m = (h/g)
+// * n; row r is query head j*(h/g) + r / n, token r % n, and token t sees
+// the positions below raw + len_add - (n - 1 - t): the causal mask of the
+// whole sequence aligned to its bottom-right corner (the zwjcode.cn page,
+// section 13, warns that a non-square is_causal mask is aligned top-left),
+// cut to a sliding window when one is given.
+//
+// A work-group of W wavefronts serves 16*NQT*W consecutive rows of one unit
+// over one range of positions.  Each 32-position tile of K and V is read
+// from memory once per work-group into LDS (every thread moves 16-byte
+// pieces; the next tile's pieces are in registers while this tile is
+// computed; two LDS buffers, one barrier per tile) and every wavefront
+// reads it there for its own 16*NQT rows, so a unit's K/V is read once per
+// row block instead of once per 32 rows.  Work-groups of the row blocks of
+// one unit get ids eight apart: MI355X hands work-group ids to its eight
+// XCDs in turn, so they run on one XCD at about the same time and share the
+// K/V lines in its L2.
+//
+// Per wavefront and tile, on the matrix cores (v_mfma_f32_16x16x32_bf16,
+// fp32 accumulate), as in the single-token kernels:
+//   S^T[16 pos x 16 rows] = K[16 pos x 128] . Q^T[128 x 16 rows]: the A
+//     operand is read from LDS (lane l: 16 bytes of K row l % 16 at dims
+//     32*ks + 8*(l/16)), the B operand is the wavefront's queries in
+//     registers.
+//   O^T[16 dims x 16 rows] += V^T[16 dims x 32 pos] . P^T[32 pos x 16 rows]:
+//     the S^T result already sits in the B-operand layout (lane l holds
+//     positions 4*(l/16) + v of both 16-position halves), and the A operand
+//     comes from transposing LDS reads of the V tile.
+//   An all-ones A operand gives the column sums of the bf16-rounded P.
+// Online softmax per row in base 2 ("KV Cache 优化与注意力机制加速"
+// (plumephp.com) section 2.2) with the lazy rescale of the single-token
+// kernels: the running reference moves only when a tile maximum passes it by
+// more than 8; out = sum bf16(P) V / sum bf16(P); lse = m + log2 of the fp32
+// sum of P.  Wavefronts own disjoint rows and see the same positions, so
+// each writes its rows directly, no merge between wavefronts.
+//
+// A call that appends reads its new positions (raw .. raw+n-1) from k_new /
+// v_new, and the work-group of the first row block writes them into the
+// cache.
+
+#include "kvc_schedule.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRowB = 2 * kD;                      // bytes of one K or V row
+constexpr int kTileB = kTileTokens * kRowB;        // 8 KB of K (or V) per tile
+constexpr int kPieces = 2 * kTileTokens * 16;      // 16-byte pieces of a K + V tile
+constexpr float kLazyRescale = 8.0f;
+
+// LDS offset of 16-byte chunk c of K row r: chunks XOR-swizzled by r % 16,
+// so the 16 rows an A-operand read touches at one chunk sit in 16
+// different chunk slots (all 64 banks, no conflict).
+__device__ __forceinline__ int k_off(int r, int c) { return r * kRowB + ((c ^ (r & 15)) << 4); }
+// V rows: the swizzle of the transposing reads, rows R..R+3 (R = 4k) on
+// disjoint 32-byte slices, chunk pairs (2k, 2k+1) kept adjacent.
+__device__ __forceinline__ int v_off(int r, int c) { return r * kRowB + ((c ^ ((r & 3) << 1)) << 4); }
+
+template <int NQT, int W, bool PAGED>
+struct PrefillEngine {
+    static constexpr int kRowsPerWave = 16 * NQT;
+    static constexpr int kRowsPerGroup = kRowsPerWave * W;
+    static constexpr int kPer = kPieces / (64 * W);  // pieces per thread per tile
+    static_assert(kPer * 64 * W == kPieces, "pieces must divide evenly");
+
+    struct Shared {
+        uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
+        __attribute__((aligned(16))) unsigned char k[2][kTileB];
+        __attribute__((aligned(16))) unsigned char v[2][kTileB];
+    };
+
+    // Rows rb*kRowsPerGroup .. +kRowsPerGroup of unit (b, j) over positions
+    // [s, e); chunk c of the unit's plan.  Called by all 64*W threads.
+    __device__ static void run(const DecodeArgs& a, Shared& sh, int b, int j, int c, int rb, int s,
+                               int e) {
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int G = lane >> 4, col = lane & 15;
+        const int row0 = rb * kRowsPerGroup + wave * kRowsPerWave;  // this wavefront's first row
+        const int rows = min(a.m - row0, kRowsPerWave);             // may be <= 0
+        const int raw = a.seq_lens[b];
+        const long bj = (long)b * a.g + j;
+
+        // B operands of Q K^T: row 16*qt + col, dims 32*ks + 8*G .. +8.
+        const uint16_t* Q = (const uint16_t*)a.q;
+        uint4 qb[NQT][4];
+        int lim[NQT];  // positions below lim are visible to the lane's row
+        const unsigned wlen = a.window > 0 ? (unsigned)a.window : 0x80000000u;
+        int hi_w = 0, lo_w = 0x7fffffff;  // visible span of the wavefront's rows
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            const int qi = 16 * qt + col;
+            const bool ok = qi < rows;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qb[qt][ks] = ok ? ld16(Q + ((b * (long)a.h + (long)j * a.m + row0 + qi) * kD + 32 * ks + 8 * G))
+                                : make_uint4(0u, 0u, 0u, 0u);
+            lim[qt] = visible_len(a, raw, (row0 + qi) % a.n);
+            if (ok) {
+                hi_w = max(hi_w, lim[qt]);
+                lo_w = min(lo_w, window_lo(a, lim[qt]));
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            hi_w = max(hi_w, __shfl_xor(hi_w, off, 64));
+            lo_w = min(lo_w, __shfl_xor(lo_w, off, 64));
+        }
+
+        f32x4_t acc[NQT][8];
+        f32x4_t lacc[NQT];  // sums of bf16-rounded P (normalise out)
+        float lex[NQT];     // sums of fp32 P over this lane's positions (give lse)
+        float mrun[NQT];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            mrun[qt] = kNegInf;
+            lex[qt] = 0.0f;
+            lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        const float sl2 = a.scale_log2e;
+
+        // The appended tokens: positions raw .. come from k_new / v_new rows
+        // (b, j, p - raw); the first row block's work-group writes this
+        // range's new positions into the cache (the kernels never read the
+        // cache there, so nothing waits for the writes).
+        const bool appends = a.k_new != nullptr;
+        if (appends && rb == 0 && max(s, raw) < e)
+            store_new_rows_bf16_d128(a, b, j, raw, max(s, raw), e, tid, 64 * W);
+        const char* knew = appends ? (const char*)a.k_new + bj * a.n * kRowB - (long)raw * kRowB : nullptr;
+        const char* vnew = appends ? (const char*)a.v_new + bj * a.n * kRowB - (long)raw * kRowB : nullptr;
+
+        // Several work-groups (row blocks) read each K/V line: ordinary loads
+        // keep it in L2 for the others; a single reader streams.
+        const bool reread = a.row_blocks > 1;
+        int blk0 = 0, w1 = e;
+        // Address of the 16-byte piece `chunk` of K (or V) at position p.
+        const char* kbase = (const char*)a.k;
+        const char* vbase = (const char*)a.v;
+        auto src = [&](bool isv, int p, int chunk) -> const void* {
+            if (appends && p >= raw) return (isv ? vnew : knew) + (long)p * kRowB + 16 * chunk;
+            const char* base = isv ? vbase : kbase;
+            uint64_t row;
+            if (PAGED) row = sh.tbl[(p >> a.log2_bs) - blk0] + (uint32_t)(p & (a.block_size - 1));
+            else row = (uint64_t)(bj * a.t_cap + cache_slot(a, p));
+            return base + row * kRowB + 16 * chunk;
+        };
+        uint4 pre[kPer];
+        // Pieces of the tile at t0 into registers: the thread's pieces k <
+        // kPer/2 are of K, the others of V; piece k is row q / 16, chunk q %
+        // 16 with q = tid + (k % (kPer/2)) * 64*W; positions past the range
+        // repeat its last one (masked).
+        constexpr int kHalf = kPer / 2;
+        auto load_tile = [&](int t0) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int q = tid + (k % kHalf) * 64 * W;
+                const int p = min(t0 + (q >> 4), w1 - 1);
+                const void* ptr = src(k >= kHalf, p, q & 15);
+                pre[k] = reread ? ld16(ptr) : ld16_stream(ptr);
+            }
+        };
+        auto stage_tile = [&](int buf) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int q = tid + (k % kHalf) * 64 * W;
+                unsigned char* dst = k >= kHalf ? sh.v[buf] + v_off(q >> 4, q & 15)
+                                                : sh.k[buf] + k_off(q >> 4, q & 15);
+                *reinterpret_cast<uint4*>(dst) = pre[k];
+            }
+        };
+
+        auto compute_tile = [&](int t0, int buf) {
+            const unsigned char* kt = sh.k[buf];
+            const unsigned char* vt = sh.v[buf];
+            f32x4_t S[NQT][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) S[qt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const uint4 ka = *reinterpret_cast<const uint4*>(kt + k_off(16 * tt + col, 4 * ks + G));
+#pragma unroll
+                    for (int qt = 0; qt < NQT; ++qt) S[qt][tt] = mfma_bf16(ka, qb[qt][ks], S[qt][tt]);
+                }
+            }
+            uint4 pb[NQT];
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                float sv[8];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int p = t0 + 16 * tt + 4 * G + v;
+                        const bool vis = p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen;
+                        sv[4 * tt + v] = vis ? S[qt][tt][v] * sl2 : kNegInf;
+                    }
+                }
+                float mt = sv[0];
+#pragma unroll
+                for (int k = 1; k < 8; ++k) mt = fmaxf(mt, sv[k]);
+                mt = fmaxf(mt, shfl_xor_f(mt, 16));
+                mt = fmaxf(mt, shfl_xor_f(mt, 32));
+                if (__any(mt > mrun[qt] + kLazyRescale)) {  // uniform branch
+                    const float mnew = fmaxf(mrun[qt], mt);
+                    const float r = (mnew == kNegInf) ? 0.0f : mnew;
+                    const float alpha = fast_exp2(mrun[qt] - r);  // 0 while nothing was seen
+                    mrun[qt] = mnew;
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
+                    lacc[qt] *= alpha;
+                    lex[qt] *= alpha;
+                }
+                const float ref = (mrun[qt] == kNegInf) ? 0.0f : mrun[qt];
+                float pv[8];
+                float psum = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    pv[k] = fast_exp2(sv[k] - ref);
+                    psum += pv[k];
+                }
+                lex[qt] += psum;
+                pb[qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+            }
+            // PV: lane 16G + 4r + qd reads 8 bytes of V rows 4G + r and
+            // 16 + 4G + r at dims 16*nt + 4*qd; the transposing read hands
+            // lane 16G + i dim 16*nt + i of those rows.
+            const int tr_r = (lane >> 2) & 3, tr_q = lane & 3;
+            const int r0 = 4 * G + tr_r, r1 = 16 + 4 * G + tr_r;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const int ch = 2 * nt + (tr_q >> 1), sub = (tr_q & 1) * 8;
+                const uint2 lo = lds_read_tr16(vt + v_off(r0, ch) + sub);
+                const uint2 hi = lds_read_tr16(vt + v_off(r1, ch) + sub);
+                const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma_bf16(av, pb[qt], acc[qt][nt]);
+            }
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) lacc[qt] = mfma_bf16(ones, pb[qt], lacc[qt]);
+        };
+
+        // Windows of at most kMaxChunk positions, so that a window's slice
+        // of the block table fits in LDS; within a window, tiles of 32.
+        for (int w0 = s; w0 < e; w0 = w1) {
+            w1 = min(e, w0 + kMaxChunk);
+            if (PAGED) {
+                blk0 = w0 >> a.log2_bs;
+                const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
+                for (int t = tid; t < nblk; t += 64 * W) {
+                    int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
+                    ph = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                    sh.tbl[t] = ((uint32_t)ph * (uint32_t)a.g + (uint32_t)j) * (uint32_t)a.block_size;
+                }
+                __syncthreads();
+            }
+            int t0 = w0;
+            load_tile(t0);
+            stage_tile(0);
+            if (t0 + kTileTokens < w1) load_tile(t0 + kTileTokens);
+            __syncthreads();
+            int buf = 0;
+            for (; t0 < w1; t0 += kTileTokens) {
+                // a wavefront whose rows see none of the tile skips it
+                if (rows > 0 && t0 < hi_w && t0 + kTileTokens > lo_w) compute_tile(t0, buf);
+                if (t0 + kTileTokens < w1) stage_tile(buf ^ 1);
+                if (t0 + 2 * kTileTokens < w1) load_tile(t0 + 2 * kTileTokens);
+                __syncthreads();
+                buf ^= 1;
+            }
+        }
+
+        // lex holds this lane's positions only: sum the four row groups.
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            lex[qt] += shfl_xor_f(lex[qt], 16);
+            lex[qt] += shfl_xor_f(lex[qt], 32);
+        }
+        if (rows <= 0) return;
+        const SegDst dst = chunk_dst(a, b, j, c, row0);
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            const int qi = 16 * qt + col;
+            if (qi >= rows) continue;
+            const float lr = lacc[qt][0];
+            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                *reinterpret_cast<f32x4_t*>(dst.o + (long)qi * dst.o_stride + 16 * nt + 4 * G) = acc[qt][nt] * inv;
+            if (G == 0) {
+                const float l = lex[qt];
+                float v;
+                if (dst.final_) v = l > 0.0f ? (mrun[qt] + fast_log2(l)) * kLn2 : kNegInf;
+                else v = l > 0.0f ? mrun[qt] + fast_log2(l) : kNegInf;
+                dst.lse[(long)qi * dst.lse_stride] = v;
+            }
+        }
+    }
+};
+
+}  // namespace
+
+// Resident wavefronts per SIMD the register allocator is asked to allow:
+// four with 16 rows per wavefront, two with 32.
+template <int NQT>
+struct PrefillOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 4 : 2; };
+
+// Grid: one work-group per (chunk, KV head, sequence, row block), as a 1-D
+// grid.  Units u = (b*g + j)*C + c go in groups of eight (the last group may
+// be narrower); within a group of width w, row block r of unit k has id
+// r*w + k, so the row blocks of a unit get ids eight apart.
+template <int NQT, int W, bool PAGED>
+__global__ void __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu(PrefillOccupancy<NQT>::kWavesPerEu)))
+prefill_mfma(DecodeArgs a) {
+    using E = PrefillEngine<NQT, W, PAGED>;
+    __shared__ typename E::Shared sh;
+    const long id = blockIdx.x;
+    const long units = (long)a.num_chunks * a.g * a.B;
+    const int R = a.row_blocks;
+    const long grp = id / (8L * R), rem = id - grp * 8L * R;
+    const long width = min(8L, units - grp * 8);
+    const long u = grp * 8 + rem % width;
+    const int rb = (int)(rem / width);
+    const int c = (int)(u % a.num_chunks);
+    const int j = (int)((u / a.num_chunks) % a.g);
+    const int b = (int)(u / ((long)a.num_chunks * a.g));
+    const PosRange ur = unit_range(a, a.seq_lens[b]);
+    const int p0 = ur.lo + c * a.chunk_len;
+    const int p1 = min(p0 + a.chunk_len, ur.hi);
+    if (p0 >= ur.hi && a.num_chunks > 1) {  // past the end: records of weight 0 for the merge
+        const int row0 = rb * E::kRowsPerGroup;
+        mark_empty_rows(chunk_dst(a, b, j, c, row0), min(a.m - row0, E::kRowsPerGroup), threadIdx.x);
+        return;
+    }
+    E::run(a, sh, b, j, c, rb, p0, p1);
+}
+
+// Kernel for (rows per wavefront tile count NQT, wavefronts W, layout).
+const void* prefill_kernel(int nqt, int waves, bool paged) {
+    if (nqt == 1 && waves == 4)
+        return paged ? (const void*)prefill_mfma<1, 4, true> : (const void*)prefill_mfma<1, 4, false>;
+    if (nqt == 2 && waves == 4)
+        return paged ? (const void*)prefill_mfma<2, 4, true> : (const void*)prefill_mfma<2, 4, false>;
+    if (nqt == 2 && waves == 8)
+        return paged ? (const void*)prefill_mfma<2, 8, true> : (const void*)prefill_mfma<2, 8, false>;
+    return nullptr;
+}
+
+hipError_t launch_prefill_mfma(const DecodeArgs& a, hipStream_t s) {
+    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr);
+    if (fn == nullptr || a.row_blocks < 1 || a.stream) return hipErrorInvalidValue;
+    if ((long)a.row_blocks * 16 * a.nqt * a.waves < a.m) return hipErrorInvalidValue;
+    const long wgs = (long)a.num_chunks * a.g * a.B * a.row_blocks;
+    if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
+    void* args[] = {const_cast<DecodeArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * a.waves), args, 0, s);
+}
+
+}  // namespace kvc

@@ -65,7 +65,7 @@ def _draw(mode: str, seed: int) -> dict:
     m = int(r.choice([1, 2, 3, 4, 5, 8, 12, 16, 24, 32, 40]))
     n = 1
     if mode in ("multi", "window"):
-        n = int(r.choice([1, 2, 3, 5, 8]))
+        n = int(r.choice([1, 2, 3, 5, 8, 17, 40]))
     B = int(r.integers(1, 7))
     lengths = r.integers(0, 2600, size=B)
     lengths[r.random(B) < 0.15] = 0
