@@ -59,6 +59,24 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
     return __shfl_xor(x, mask, 64);
 }
 
+// Max (sum) of x over the four lanes l, l^16, l^32, l^48 of a wavefront,
+// every lane getting the result, with the gfx950 cross-row swaps instead of
+// LDS permutes.  v_permlane16_swap of x with itself gives rows (0, 0, 2, 2)
+// in its first result and (1, 1, 3, 3) in its second; v_permlane32_swap
+// gives the low half twice and the high half twice.
+__device__ __forceinline__ float max_rows4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 16-byte global load through the vector memory path.
 __device__ __forceinline__ uint4 ld16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);

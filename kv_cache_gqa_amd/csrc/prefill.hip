@@ -94,7 +94,9 @@ struct PrefillEngine {
         uint4 qb[NQT][4];
         int lim[NQT];  // positions below lim are visible to the lane's row
         const unsigned wlen = a.window > 0 ? (unsigned)a.window : 0x80000000u;
-        int hi_w = 0, lo_w = 0x7fffffff;  // visible span of the wavefront's rows
+        // The wavefront's rows see positions in [lo_w, hi_w) between them;
+        // every one of them sees [full_lo, full_hi), where no mask is needed.
+        int hi_w = 0, lo_w = 0x7fffffff, full_lo = 0, full_hi = 0x7fffffff;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
             const int qi = 16 * qt + col;
@@ -105,14 +107,19 @@ struct PrefillEngine {
                                 : make_uint4(0u, 0u, 0u, 0u);
             lim[qt] = visible_len(a, raw, (row0 + qi) % a.n);
             if (ok) {
+                const int wl = window_lo(a, lim[qt]);
                 hi_w = max(hi_w, lim[qt]);
-                lo_w = min(lo_w, window_lo(a, lim[qt]));
+                lo_w = min(lo_w, wl);
+                full_hi = min(full_hi, lim[qt]);
+                full_lo = max(full_lo, wl);
             }
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             hi_w = max(hi_w, __shfl_xor(hi_w, off, 64));
             lo_w = min(lo_w, __shfl_xor(lo_w, off, 64));
+            full_hi = min(full_hi, __shfl_xor(full_hi, off, 64));
+            full_lo = max(full_lo, __shfl_xor(full_lo, off, 64));
         }
 
         f32x4_t acc[NQT][8];
@@ -195,24 +202,32 @@ struct PrefillEngine {
                     for (int qt = 0; qt < NQT; ++qt) S[qt][tt] = mfma_bf16(ka, qb[qt][ks], S[qt][tt]);
                 }
             }
+            // Every row of the wavefront sees the whole tile: no mask.
+            const bool full = t0 >= full_lo && t0 + kTileTokens <= min(full_hi, w1);
             uint4 pb[NQT];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
                 float sv[8];
+                if (full) {
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int p = t0 + 16 * tt + 4 * G + v;
-                        const bool vis = p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen;
-                        sv[4 * tt + v] = vis ? S[qt][tt][v] * sl2 : kNegInf;
+                        for (int v = 0; v < 4; ++v) sv[4 * tt + v] = S[qt][tt][v] * sl2;
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int p = t0 + 16 * tt + 4 * G + v;
+                            const bool vis = p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen;
+                            sv[4 * tt + v] = vis ? S[qt][tt][v] * sl2 : kNegInf;
+                        }
                     }
                 }
                 float mt = sv[0];
 #pragma unroll
                 for (int k = 1; k < 8; ++k) mt = fmaxf(mt, sv[k]);
-                mt = fmaxf(mt, shfl_xor_f(mt, 16));
-                mt = fmaxf(mt, shfl_xor_f(mt, 32));
+                mt = max_rows4(mt);
                 if (__any(mt > mrun[qt] + kLazyRescale)) {  // uniform branch
                     const float mnew = fmaxf(mrun[qt], mt);
                     const float r = (mnew == kNegInf) ? 0.0f : mnew;
@@ -285,10 +300,7 @@ struct PrefillEngine {
 
         // lex holds this lane's positions only: sum the four row groups.
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            lex[qt] += shfl_xor_f(lex[qt], 16);
-            lex[qt] += shfl_xor_f(lex[qt], 32);
-        }
+        for (int qt = 0; qt < NQT; ++qt) lex[qt] = sum_rows4(lex[qt]);
         if (rows <= 0) return;
         const SegDst dst = chunk_dst(a, b, j, c, row0);
 #pragma unroll
@@ -314,9 +326,10 @@ struct PrefillEngine {
 }  // namespace
 
 // Resident wavefronts per SIMD the register allocator is asked to allow:
-// four with 16 rows per wavefront, two with 32.
-template <int NQT>
-struct PrefillOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 4 : 2; };
+// four with 16 rows per wavefront (three when paged: the table lookups need
+// the registers of a fourth), two with 32.
+template <int NQT, bool PAGED>
+struct PrefillOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? (PAGED ? 3 : 4) : 2; };
 
 // Grid: one work-group per (chunk, KV head, sequence, row block), as a 1-D
 // grid.  Units u = (b*g + j)*C + c go in groups of eight (the last group may
@@ -324,7 +337,7 @@ struct PrefillOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? 4 : 2; }
 // r*w + k, so the row blocks of a unit get ids eight apart.
 template <int NQT, int W, bool PAGED>
 __global__ void __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(PrefillOccupancy<NQT>::kWavesPerEu)))
+__attribute__((amdgpu_waves_per_eu(PrefillOccupancy<NQT, PAGED>::kWavesPerEu)))
 prefill_mfma(DecodeArgs a) {
     using E = PrefillEngine<NQT, W, PAGED>;
     __shared__ typename E::Shared sh;
