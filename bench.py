@@ -393,9 +393,8 @@ def main():
         k_src, v_src = x["k_cache"], x["v_cache"]
         nblocks = None
     fp8 = args.kv_fp8
-    if fp8 and (w.dtype != "bf16" or args.queries != 1 or args.window or args.ring):
-        print("--kv-fp8 takes a bf16 workload, one token per sequence and no window",
-              file=sys.stderr)
+    if fp8 and w.dtype != "bf16":
+        print("--kv-fp8 takes a bf16 workload", file=sys.stderr)
         sys.exit(2)
     if fp8:
         # per-KV-head scales amax / 448 over the cache; codes by torch's
@@ -497,7 +496,11 @@ def main():
 
     def fused_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        if fp8:
+        if fp8 and (nq > 1 or windowed):
+            kvc.decode_fp8_window(q, kc, vc, k_sc_d, v_sc_d, sl_before, window=win, ring=ring,
+                                  block_table=bt, scale=x["scale"], num_splits=ns, workspace=ws,
+                                  out=out, lse=lse, k_new=k_new, v_new=v_new)
+        elif fp8:
             kvc.decode_fp8(q, kc, vc, k_sc_d, v_sc_d, sl_before, block_table=bt, scale=x["scale"],
                            num_splits=ns, workspace=ws, out=out, lse=lse, k_new=k_new,
                            v_new=v_new)
@@ -728,7 +731,9 @@ def main():
             "parallelism": "single GPU",
         },
         "step": (("kvc_append_fp8 + decode call" if args.separate
-                  else "one kvc_append_decode_attention_fp8 call") if fp8
+                  else f"one kvc_append_decode_attention_fp8_{'window' if windowed else 'multi'} "
+                       f"call (W={win}, ring={ring}, {nq} tokens per sequence)"
+                  if (nq > 1 or windowed) else "one kvc_append_decode_attention_fp8 call") if fp8
                  else "kvc_append + decode call" if args.separate
                  else f"one kvc_append_decode_attention_window call (W={win}, ring={ring}, "
                       f"{nq} tokens per sequence)" if windowed

@@ -420,7 +420,8 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
  * Everything else (validation, splits, workspace from
  * kvc_decode_workspace_bytes with dtype KVC_BF16, positions, status codes)
  * is as in the bf16 single-token calls.  The fast kernels cover d = 128;
- * other head dims take the generic kernel.
+ * other head dims take the generic kernel.  More than 32 query rows per KV
+ * head run as 32-row slices of the matrix-core decode kernel.
  */
 int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
@@ -452,6 +453,81 @@ int kvc_append_decode_attention_fp8_paged(const void* q, const void* k_new, cons
                                           int d, float scale, int num_splits, void* workspace,
                                           size_t workspace_bytes, float* out, float* lse,
                                           hipStream_t stream);
+
+/*
+ * FP8 caches with several new tokens per sequence ([P1] 5.2, [P4] 5.3) and
+ * sliding windows ([P4] 5.2, [P3] 10), the FP8 forms of the _multi and
+ * _window calls: kvc_decode_attention_fp8_multi[_paged],
+ * kvc_append_decode_attention_fp8_multi[_paged] and the _fp8_window
+ * versions of both, which take a window W (0 = none, the same as _multi)
+ * and, contiguous only, ring.
+ *
+ *   Shapes, positions, the bottom-right causal alignment, windows, ring
+ *   slots, capacity clamping and workspaces as in the bf16 _multi / _window
+ *   calls (q [B, h, n, d] and out [B, h, n, d], lse [B, h, n]; the workspace
+ *   is kvc_decode_workspace_bytes(B, h * n, g, d, KVC_BF16, L, ...) with L as
+ *   for the bf16 window calls).  Caches and scales as in the FP8 single-
+ *   token calls: OCP E4M3 codes, k_scale / v_scale float32 [g], q, k_new,
+ *   v_new bf16 [B, g, n, d].
+ *   The appending calls write the n tokens' codes (each the code of the
+ *   float32 quotient x / scale, as kvc_append_fp8 encodes) and attend to
+ *   those codes' values, so they give what writing the codes and then the
+ *   non-appending call gives.
+ *   Attention is over the dequantised values code * scale.
+ */
+int kvc_decode_attention_fp8_multi(const void* q, const void* k_cache, const void* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                                   int t_cap, float scale, int num_splits, void* workspace,
+                                   size_t workspace_bytes, float* out, float* lse,
+                                   hipStream_t stream);
+int kvc_decode_attention_fp8_multi_paged(const void* q, const void* k_pool, const void* v_pool,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_table, int max_blocks,
+                                         int block_size, int num_blocks, const int32_t* seq_lens,
+                                         int B, int h, int g, int d, int n, float scale,
+                                         int num_splits, void* workspace, size_t workspace_bytes,
+                                         float* out, float* lse, hipStream_t stream);
+int kvc_append_decode_attention_fp8_multi(const void* q, const void* k_new, const void* v_new,
+                                          void* k_cache, void* v_cache, const float* k_scale,
+                                          const float* v_scale, const int32_t* seq_lens_before,
+                                          int B, int h, int g, int d, int n, int t_cap,
+                                          float scale, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* out, float* lse,
+                                          hipStream_t stream);
+int kvc_append_decode_attention_fp8_multi_paged(
+    const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const float* k_scale, const float* v_scale, const int32_t* block_table, int max_blocks,
+    int block_size, int num_blocks, const int32_t* seq_lens_before, int B, int h, int g, int d,
+    int n, float scale, int num_splits, void* workspace, size_t workspace_bytes, float* out,
+    float* lse, hipStream_t stream);
+int kvc_decode_attention_fp8_window(const void* q, const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                                    int t_cap, int window, int ring, float scale, int num_splits,
+                                    void* workspace, size_t workspace_bytes, float* out, float* lse,
+                                    hipStream_t stream);
+int kvc_decode_attention_fp8_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                          const float* k_scale, const float* v_scale,
+                                          const int32_t* block_table, int max_blocks,
+                                          int block_size, int num_blocks, const int32_t* seq_lens,
+                                          int B, int h, int g, int d, int n, int window,
+                                          float scale, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* out, float* lse,
+                                          hipStream_t stream);
+int kvc_append_decode_attention_fp8_window(const void* q, const void* k_new, const void* v_new,
+                                           void* k_cache, void* v_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* seq_lens_before,
+                                           int B, int h, int g, int d, int n, int t_cap,
+                                           int window, int ring, float scale, int num_splits,
+                                           void* workspace, size_t workspace_bytes, float* out,
+                                           float* lse, hipStream_t stream);
+int kvc_append_decode_attention_fp8_window_paged(
+    const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const float* k_scale, const float* v_scale, const int32_t* block_table, int max_blocks,
+    int block_size, int num_blocks, const int32_t* seq_lens_before, int B, int h, int g, int d,
+    int n, int window, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+    float* out, float* lse, hipStream_t stream);
 
 /*
  * Block operations for shared and re-ranked caches ([P4] 4.3: requests that

@@ -25,7 +25,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["append", "decode", "decode_paged", "append_decode", "decode_multi",
-           "append_decode_multi", "decode_window", "append_fp8", "decode_fp8", "copy_blocks",
+           "append_decode_multi", "decode_window", "append_fp8", "decode_fp8", "decode_fp8_window",
+           "append_decode_noalloc", "copy_blocks",
            "fork_block_tables", "gather_cache", "plan", "workspace_bytes", "launch_shape",
            "KvcError", "load_library", "LIB_PATH", "F32", "BF16", "FP8_E4M3", "SPLITS_STREAM"]
 
@@ -123,6 +124,34 @@ def load_library():
                                                           ip, vp, ip, ip, ip, ip, fp, ip, vp, sz,
                                                           vp, vp, vp]
     lib.kvc_append_decode_attention_fp8_paged.restype = ip
+    # FP8 multi-token / window calls
+    lib.kvc_decode_attention_fp8_multi.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip,
+                                                   fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_fp8_multi_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, vp, ip,
+                                                         ip, ip, ip, ip, fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_fp8_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, ip, ip,
+                                                          ip, ip, ip, fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_append_decode_attention_fp8_multi_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip,
+                                                                ip, ip, vp, ip, ip, ip, ip, ip, fp,
+                                                                ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_fp8_window.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, ip,
+                                                    ip, ip, fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_fp8_window_paged.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, vp,
+                                                          ip, ip, ip, ip, ip, ip, fp, ip, vp, sz,
+                                                          vp, vp, vp]
+    lib.kvc_append_decode_attention_fp8_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, ip,
+                                                           ip, ip, ip, ip, ip, ip, fp, ip, vp, sz,
+                                                           vp, vp, vp]
+    lib.kvc_append_decode_attention_fp8_window_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                                                 ip, ip, ip, vp, ip, ip, ip, ip,
+                                                                 ip, ip, fp, ip, vp, sz, vp, vp,
+                                                                 vp]
+    for name in ("kvc_decode_attention_fp8_multi", "kvc_decode_attention_fp8_multi_paged",
+                 "kvc_append_decode_attention_fp8_multi",
+                 "kvc_append_decode_attention_fp8_multi_paged", "kvc_decode_attention_fp8_window",
+                 "kvc_decode_attention_fp8_window_paged", "kvc_append_decode_attention_fp8_window",
+                 "kvc_append_decode_attention_fp8_window_paged"):
+        getattr(lib, name).restype = ip
     lib.kvc_copy_blocks.argtypes = [vp, vp, vp, ip, ip, ip, ip, ip, ip, vp]
     lib.kvc_copy_blocks.restype = ip
     lib.kvc_fork_block_tables.argtypes = [vp, vp, ip, ip, vp, ip, vp, vp, vp]
@@ -697,4 +726,118 @@ def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table=None
                                                     _dev(out, "out"), _dev(lse, "lse"),
                                                     _stream(stream))
     _check("kvc_*decode_attention_fp8", st)
+    return out, lse
+
+
+@_on_device
+def decode_fp8_window(q, k_cache, v_cache, k_scale, v_scale, seq_lens, window: int = 0,
+                      ring: bool = False, block_table=None, scale: Optional[float] = None,
+                      num_splits: int = 0, workspace: Optional[torch.Tensor] = None, out=None,
+                      lse=None, stream=None, k_new=None, v_new=None):
+    """Several query tokens per sequence (q bf16 [B,h,n,d]) over uint8 FP8
+    E4M3 caches with per-KV-head scales [g]; token t at position
+    seq_lens[b] - n + t (or seq_lens_before[b] + t with k_new) sees the
+    positions up to itself, the last ``window`` of them when window > 0
+    (window 0: the _multi calls).  With k_new, v_new (bf16 [B,g,n,d]) the
+    call quantises and appends the n tokens (seq_lens = lengths before the
+    step).  ring: contiguous ring cache of t_cap slots.  Returns (out
+    [B,h,n,d] float32, lse [B,h,n] float32)."""
+    lib = load_library()
+    B, h, n, d = _shape(q, (None, None, None, None), "q")
+    if ring and block_table is not None:
+        raise ValueError("a ring cache is contiguous")
+    if ring and window <= 0:
+        raise ValueError("a ring cache needs a window")
+    g, cap, bs, mb, nb = _cache_shapes(k_cache, v_cache, B, d, block_table)
+    _shape(k_scale, (g,), "k_scale")
+    _shape(v_scale, (g,), "v_scale")
+    _shape(seq_lens, (B,), "seq_lens")
+    fused = k_new is not None
+    if fused:
+        _new_tokens(k_new, v_new, B, g, n, d)
+    elif v_new is not None:
+        raise ValueError("v_new without k_new")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    qp = _dev(q, "q", torch.bfloat16)
+    ks, vs = _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32)
+    sl = _dev(seq_lens, "seq_lens", torch.int32)
+    kn = _dev(k_new, "k_new", torch.bfloat16) if fused else None
+    vn = _dev(v_new, "v_new", torch.bfloat16) if fused else None
+    o, l_ = _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32)
+    sc, st = float(scale), _stream(stream)
+    if block_table is None:
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, BF16,
+                                                            _plan_len(cap, window, n), num_splits,
+                                                            0), q, workspace)
+        wsp = ws.data_ptr() if ws is not None else None
+        kc, vc = _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8)
+        if fused and window > 0:
+            r = lib.kvc_append_decode_attention_fp8_window(qp, kn, vn, kc, vc, ks, vs, sl, B, h, g,
+                                                           d, n, cap, window, int(ring), sc,
+                                                           num_splits, wsp, wsb, o, l_, st)
+        elif fused:
+            r = lib.kvc_append_decode_attention_fp8_multi(qp, kn, vn, kc, vc, ks, vs, sl, B, h, g, d,
+                                                          n, cap, sc, num_splits, wsp, wsb, o, l_,
+                                                          st)
+        elif window > 0:
+            r = lib.kvc_decode_attention_fp8_window(qp, kc, vc, ks, vs, sl, B, h, g, d, n, cap,
+                                                    window, int(ring), sc, num_splits, wsp, wsb, o,
+                                                    l_, st)
+        else:
+            r = lib.kvc_decode_attention_fp8_multi(qp, kc, vc, ks, vs, sl, B, h, g, d, n, cap, sc,
+                                                   num_splits, wsp, wsb, o, l_, st)
+    else:
+        ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, BF16,
+                                                            _plan_len(mb * bs, window, n),
+                                                            num_splits, 1), q, workspace)
+        wsp = ws.data_ptr() if ws is not None else None
+        kp, vp = _dev(k_cache, "k_pool", torch.uint8), _dev(v_cache, "v_pool", torch.uint8)
+        bt = _dev(block_table, "block_table", torch.int32)
+        if fused and window > 0:
+            r = lib.kvc_append_decode_attention_fp8_window_paged(qp, kn, vn, kp, vp, ks, vs, bt, mb,
+                                                                 bs, nb, sl, B, h, g, d, n, window,
+                                                                 sc, num_splits, wsp, wsb, o, l_,
+                                                                 st)
+        elif fused:
+            r = lib.kvc_append_decode_attention_fp8_multi_paged(qp, kn, vn, kp, vp, ks, vs, bt, mb,
+                                                                bs, nb, sl, B, h, g, d, n, sc,
+                                                                num_splits, wsp, wsb, o, l_, st)
+        elif window > 0:
+            r = lib.kvc_decode_attention_fp8_window_paged(qp, kp, vp, ks, vs, bt, mb, bs, nb, sl, B,
+                                                          h, g, d, n, window, sc, num_splits, wsp,
+                                                          wsb, o, l_, st)
+        else:
+            r = lib.kvc_decode_attention_fp8_multi_paged(qp, kp, vp, ks, vs, bt, mb, bs, nb, sl, B,
+                                                         h, g, d, n, sc, num_splits, wsp, wsb, o,
+                                                         l_, st)
+    _check("kvc_*decode_attention_fp8_(multi|window)", r)
+    return out, lse
+
+
+@_on_device
+def append_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seq_lens_before,
+                          scale: Optional[float] = None, num_splits: int = 0, out=None, lse=None,
+                          stream=None):
+    """append_decode on a contiguous cache without a workspace: split
+    partials go to the library's static scratch
+    (kvc_append_decode_attention_noalloc; KvcError status 5 when the split
+    needs more than it holds)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, h, d = _shape(q, (None, None, None), "q")
+    g, cap, _, _, _ = _cache_shapes(k_cache, v_cache, B, d, None)
+    _new_tokens(k_new, v_new, B, g, None, d)
+    _shape(seq_lens_before, (B,), "seq_lens_before")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    st = lib.kvc_append_decode_attention_noalloc(
+        _dev(q, "q"), _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
+        _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        _dev(seq_lens_before, "seq_lens_before", torch.int32), B, h, g, d, cap, float(scale), dt,
+        num_splits, _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32),
+        _stream(stream))
+    _check("kvc_append_decode_attention_noalloc", st)
     return out, lse

@@ -222,10 +222,17 @@ struct MfmaEngine {
         // and V rows now, one bf16 pair of each per lane, so that the last
         // tile does not wait for them; the tile is then built from those
         // pairs through LDS.
-        constexpr bool kNewPair = KV8 || !GEN;
-        const int new_tiles = has_new ? (e - fresh_lo + kTileTokens - 1) / kTileTokens : 0;
-        const int new_i0 = (wave - ((fresh_lo - s) / kTileTokens) % W + W) % W;  // this wave's first
-        const bool new_wave = new_i0 < new_tiles;
+        constexpr bool kNewPair = !GEN;
+        const int new_first = ((fresh_lo - s) / kTileTokens) % W;
+        bool new_wave;
+        int new_i0 = 0;  // this wavefront's first new tile (several new tokens)
+        if constexpr (kNewPair) {
+            new_wave = has_new && wave == new_first;
+        } else {
+            const int new_tiles = has_new ? (e - fresh_lo + kTileTokens - 1) / kTileTokens : 0;
+            new_i0 = (wave - new_first + W) % W;
+            new_wave = new_i0 < new_tiles;
+        }
         const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : Q;
@@ -271,7 +278,7 @@ struct MfmaEngine {
         // one new token every position of the tile is that token: its rows
         // (FP8: their codes) go to this wavefront's V staging area first.
         auto load_new_tile = [&](int t0, TileRegs<KV8>& tr) {
-            if constexpr (KV8) {
+            if constexpr (KV8 && kNewPair) {
                 new_row_codes_fp8_d128(a, j, lane, new_pair, vst);
                 wave_lds_sync();
 #pragma unroll
@@ -292,6 +299,25 @@ struct MfmaEngine {
                         tr.k[tt][ks] = *reinterpret_cast<const uint4*>(vst + 64 * ks + 16 * G);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) tr.v[u] = *reinterpret_cast<const uint4*>(vst + 256 + 16 * col);
+            } else if constexpr (KV8) {
+                // several new tokens over an FP8 cache: their bf16 rows,
+                // quantised here to the codes the cache receives
+                const float ks_ = a.k_scale[j], vs_ = a.v_scale[j];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const uint2 lo = e4m3_encode8(ld16(KN + r * kD + 64 * hh + 16 * G), ks_);
+                        const uint2 hi = e4m3_encode8(ld16(KN + r * kD + 64 * hh + 16 * G + 8), ks_);
+                        tr.k[tt][hh] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
+                    tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * col), vs_);
+                }
             } else {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
@@ -636,10 +662,13 @@ decode_mfma_stream(DecodeArgs a) {
 
 template <int NQT, bool PG, int WV>
 static const void* mfma_pick(bool stream, bool gen, bool kv8) {
-    if (kv8)  // FP8 caches: single-token calls only
-        return gen ? nullptr
-                   : stream ? (const void*)decode_mfma_stream<NQT, PG, WV, false, true>
-                            : (const void*)decode_mfma_chunked<NQT, PG, WV, false, true>;
+    if (kv8) {
+        if (stream)
+            return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true, true>
+                       : (const void*)decode_mfma_stream<NQT, PG, WV, false, true>;
+        return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true, true>
+                   : (const void*)decode_mfma_chunked<NQT, PG, WV, false, true>;
+    }
     if (stream)
         return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true, false>
                    : (const void*)decode_mfma_stream<NQT, PG, WV, false, false>;
@@ -651,8 +680,7 @@ static const void* mfma_pick(bool stream, bool gen, bool kv8) {
 // general features, FP8 cache); nullptr when that combination is not built.
 // Every (m, layout, mode) has a 4-wavefront kernel; a contiguous cache also
 // has 8-wavefront chunked kernels, for whole-unit work-groups and for chunk
-// grids smaller than the device's slots.  FP8 caches have the kernels
-// without the general features.
+// grids smaller than the device's slots.
 const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
     const bool two = m > 16;
     if (waves == 4) {
@@ -661,11 +689,15 @@ const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, boo
     }
     if (waves == 8 && !paged && !stream) {
         if (two) {
-            if (kv8) return gen ? nullptr : (const void*)decode_mfma_chunked<2, false, 8, false, true>;
+            if (kv8)
+                return gen ? (const void*)decode_mfma_chunked<2, false, 8, true, true>
+                           : (const void*)decode_mfma_chunked<2, false, 8, false, true>;
             return gen ? (const void*)decode_mfma_chunked<2, false, 8, true, false>
                        : (const void*)decode_mfma_chunked<2, false, 8, false, false>;
         }
-        if (kv8) return gen ? nullptr : (const void*)decode_mfma_chunked<1, false, 8, false, true>;
+        if (kv8)
+            return gen ? (const void*)decode_mfma_chunked<1, false, 8, true, true>
+                       : (const void*)decode_mfma_chunked<1, false, 8, false, true>;
         return gen ? (const void*)decode_mfma_chunked<1, false, 8, true, false>
                    : (const void*)decode_mfma_chunked<1, false, 8, false, false>;
     }

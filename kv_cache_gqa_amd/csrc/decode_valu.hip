@@ -54,7 +54,7 @@ struct ValuEngine {
         float red_m[W][M];
         float red_l[W][M];
         float red_o[W][M][kD];
-        __attribute__((aligned(16))) unsigned char nrow[GEN && !KV8 ? 1 : W][512];  // one new token's rows
+        __attribute__((aligned(16))) unsigned char nrow[GEN ? 1 : W][512];  // one new token's rows
     };
 
     // The M query heads of KV head j of sequence b over positions [s, e)
@@ -123,7 +123,7 @@ struct ValuEngine {
         // so without GEN) it loads the token's K and V rows now, one bf16
         // pair of each per lane, so that the last tile does not wait for
         // them; the tile is then built from those pairs through LDS.
-        constexpr bool kNewPair = KV8 || !GEN;
+        constexpr bool kNewPair = !GEN;
         const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
         const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
         const long bj = (long)b * a.g + j;
@@ -149,7 +149,7 @@ struct ValuEngine {
         // one new token every position of the tile is that token: its rows
         // (FP8: their codes) go to this wavefront's LDS area first.
         auto load_new_tile = [&](int t0, ValuTile<KV8>& tr) {
-            if constexpr (KV8) {
+            if constexpr (KV8 && kNewPair) {
                 unsigned char* codes = sh.nrow[wave];
                 new_row_codes_fp8_d128(a, j, lane, new_pair, codes);
                 wave_lds_sync();
@@ -167,6 +167,16 @@ struct ValuEngine {
                 for (int u = 0; u < 8; ++u) {
                     tr.k[u] = *reinterpret_cast<const uint4*>(rows + 16 * ds);
                     tr.v[u] = *reinterpret_cast<const uint4*>(rows + 256 + 16 * ds);
+                }
+            } else if constexpr (KV8) {
+                // several new tokens over an FP8 cache: their bf16 rows,
+                // quantised here to the codes the cache receives
+                const float ks_ = a.k_scale[j], vs_ = a.v_scale[j];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
+                    tr.k[u] = e4m3_encode8(ld16(KN + r * kD + 8 * ds), ks_);
+                    tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * ds), vs_);
                 }
             } else {
 #pragma unroll
@@ -364,10 +374,13 @@ __global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
 
 template <int M, bool PG>
 static const void* valu_pick(bool stream, bool gen, bool kv8) {
-    if (kv8)  // FP8 caches: single-token calls only
-        return gen ? nullptr
-                   : stream ? (const void*)decode_valu_stream<M, PG, 4, false, true>
-                            : (const void*)decode_valu_chunked<M, PG, 4, false, true>;
+    if (kv8) {
+        if (stream)
+            return gen ? (const void*)decode_valu_stream<M, PG, 4, true, true>
+                       : (const void*)decode_valu_stream<M, PG, 4, false, true>;
+        return gen ? (const void*)decode_valu_chunked<M, PG, 4, true, true>
+                   : (const void*)decode_valu_chunked<M, PG, 4, false, true>;
+    }
     if (stream)
         return gen ? (const void*)decode_valu_stream<M, PG, 4, true, false>
                    : (const void*)decode_valu_stream<M, PG, 4, false, false>;

@@ -847,4 +847,108 @@ int kvc_append_decode_attention_fp8_paged(const void* q, const void* k_new, cons
                         k_scale, v_scale);
 }
 
+// FP8 caches with several new tokens per sequence and / or a sliding window
+// (window 0 = none; the _multi calls are the _window calls without one).
+int kvc_decode_attention_fp8_window(const void* q, const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                                    int t_cap, int window, int ring, float scale, int num_splits,
+                                    void* workspace, size_t workspace_bytes, float* out, float* lse,
+                                    hipStream_t stream) {
+    if (B > 0 && (!k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h, g, d, n, t_cap,
+                             window, ring, scale, KVC_BF16, num_splits, workspace, workspace_bytes,
+                             out, lse, stream, k_scale, v_scale);
+}
+
+int kvc_decode_attention_fp8_window_paged(const void* q, const void* k_pool, const void* v_pool,
+                                          const float* k_scale, const float* v_scale,
+                                          const int32_t* block_table, int max_blocks,
+                                          int block_size, int num_blocks, const int32_t* seq_lens,
+                                          int B, int h, int g, int d, int n, int window,
+                                          float scale, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* out, float* lse,
+                                          hipStream_t stream) {
+    if (B > 0 && (!k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_paged(q, nullptr, nullptr, k_pool, v_pool, block_table, max_blocks, block_size,
+                        num_blocks, seq_lens, B, h, g, d, n, window, scale, KVC_BF16, num_splits,
+                        workspace, workspace_bytes, out, lse, stream, k_scale, v_scale);
+}
+
+int kvc_append_decode_attention_fp8_window(const void* q, const void* k_new, const void* v_new,
+                                           void* k_cache, void* v_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* seq_lens_before,
+                                           int B, int h, int g, int d, int n, int t_cap,
+                                           int window, int ring, float scale, int num_splits,
+                                           void* workspace, size_t workspace_bytes, float* out,
+                                           float* lse, hipStream_t stream) {
+    if (B > 0 && (!k_new || !v_new || !k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_contiguous(q, B > 0 ? k_new : nullptr, v_new, k_cache, v_cache,
+                             seq_lens_before, B, h, g, d, n, t_cap, window, ring, scale, KVC_BF16,
+                             num_splits, workspace, workspace_bytes, out, lse, stream, k_scale,
+                             v_scale);
+}
+
+int kvc_append_decode_attention_fp8_window_paged(
+    const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const float* k_scale, const float* v_scale, const int32_t* block_table, int max_blocks,
+    int block_size, int num_blocks, const int32_t* seq_lens_before, int B, int h, int g, int d,
+    int n, int window, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+    float* out, float* lse, hipStream_t stream) {
+    if (B > 0 && (!k_new || !v_new || !k_scale || !v_scale)) return KVC_ERR_INVALID;
+    return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table,
+                        max_blocks, block_size, num_blocks, seq_lens_before, B, h, g, d, n, window,
+                        scale, KVC_BF16, num_splits, workspace, workspace_bytes, out, lse, stream,
+                        k_scale, v_scale);
+}
+
+int kvc_decode_attention_fp8_multi(const void* q, const void* k_cache, const void* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* seq_lens, int B, int h, int g, int d, int n,
+                                   int t_cap, float scale, int num_splits, void* workspace,
+                                   size_t workspace_bytes, float* out, float* lse,
+                                   hipStream_t stream) {
+    return kvc_decode_attention_fp8_window(q, k_cache, v_cache, k_scale, v_scale, seq_lens, B, h,
+                                           g, d, n, t_cap, 0, 0, scale, num_splits, workspace,
+                                           workspace_bytes, out, lse, stream);
+}
+
+int kvc_decode_attention_fp8_multi_paged(const void* q, const void* k_pool, const void* v_pool,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_table, int max_blocks,
+                                         int block_size, int num_blocks, const int32_t* seq_lens,
+                                         int B, int h, int g, int d, int n, float scale,
+                                         int num_splits, void* workspace, size_t workspace_bytes,
+                                         float* out, float* lse, hipStream_t stream) {
+    return kvc_decode_attention_fp8_window_paged(q, k_pool, v_pool, k_scale, v_scale, block_table,
+                                                 max_blocks, block_size, num_blocks, seq_lens, B,
+                                                 h, g, d, n, 0, scale, num_splits, workspace,
+                                                 workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_fp8_multi(const void* q, const void* k_new, const void* v_new,
+                                          void* k_cache, void* v_cache, const float* k_scale,
+                                          const float* v_scale, const int32_t* seq_lens_before,
+                                          int B, int h, int g, int d, int n, int t_cap,
+                                          float scale, int num_splits, void* workspace,
+                                          size_t workspace_bytes, float* out, float* lse,
+                                          hipStream_t stream) {
+    return kvc_append_decode_attention_fp8_window(q, k_new, v_new, k_cache, v_cache, k_scale,
+                                                  v_scale, seq_lens_before, B, h, g, d, n, t_cap,
+                                                  0, 0, scale, num_splits, workspace,
+                                                  workspace_bytes, out, lse, stream);
+}
+
+int kvc_append_decode_attention_fp8_multi_paged(
+    const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const float* k_scale, const float* v_scale, const int32_t* block_table, int max_blocks,
+    int block_size, int num_blocks, const int32_t* seq_lens_before, int B, int h, int g, int d,
+    int n, float scale, int num_splits, void* workspace, size_t workspace_bytes, float* out,
+    float* lse, hipStream_t stream) {
+    return kvc_append_decode_attention_fp8_window_paged(
+        q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks, block_size,
+        num_blocks, seq_lens_before, B, h, g, d, n, 0, scale, num_splits, workspace,
+        workspace_bytes, out, lse, stream);
+}
+
 }  // extern "C"

@@ -150,6 +150,19 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     return sign | code;
 }
 
+// Codes of eight bf16 values (w: element 2k in the low half of word k) as
+// eight bytes, each the code of the float32 quotient x / scale -- the same
+// quotient and encoder as the stored codes of an appended token.
+__device__ __forceinline__ uint2 e4m3_encode8(uint4 w, float scale) {
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+    uint32_t c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        c[k] = e4m3_encode(__uint_as_float(x[k] << 16) / scale) |
+               (e4m3_encode(__uint_as_float(x[k] & 0xFFFF0000u) / scale) << 8);
+    return make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+}
+
 // Merge two online-softmax states (m2, l, acc) in base 2.  -inf maxima
 // (no positions seen) are handled so that no (-inf) - (-inf) is formed.
 __device__ __forceinline__ void rescale_pair(float ma, float mb, float& fa, float& fb, float& mnew) {

@@ -470,11 +470,12 @@ def quantize_fp8(x, scale, head_axis):
 
 
 def append_fp8(k_new, v_new, k_codes, v_codes, k_scale, v_scale, seq_lens_before,
-               block_table=None):
+               block_table=None, ring=False):
     """Quantise n new tokens per sequence (k_new, v_new [B,g,n,d] bf16) and
     write their codes at positions seq_lens_before[b] + t of uint8 caches
-    (contiguous [B,g,t_cap,d] or pools [NB,g,bs,d] through block_table).
-    Returns new uint8 caches."""
+    (contiguous [B,g,t_cap,d] or pools [NB,g,bs,d] through block_table; a
+    ring cache keeps position p in slot p mod t_cap).  Returns new uint8
+    caches."""
     kq = quantize_fp8(k_new, k_scale, 1)
     vq = quantize_fp8(v_new, v_scale, 1)
     kc = np.array(k_codes, dtype=np.uint8, copy=True)
@@ -486,8 +487,11 @@ def append_fp8(k_new, v_new, k_codes, v_codes, k_scale, v_scale, seq_lens_before
         for t in range(n):
             p = int(before[b]) + t
             if bt is None:
-                kc[b, :, p] = kq[b, :, t]
-                vc[b, :, p] = vq[b, :, t]
+                slot = _ring_slot(p, kc.shape[2]) if ring else p
+                if not 0 <= slot < kc.shape[2]:
+                    raise ValueError("append position outside the cache")
+                kc[b, :, slot] = kq[b, :, t]
+                vc[b, :, slot] = vq[b, :, t]
             else:
                 bs = kc.shape[2]
                 blk = int(bt[b, p // bs])
@@ -526,3 +530,15 @@ def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale, block_tab
     v = dequantize_fp8(v_codes, v_scale, 1)
     return decode(widen(q), k, v, seq_lens, scale, block_table=block_table,
                   block_size=block_size, nthreads=nthreads)
+
+
+def decode_fp8_window(q, k_codes, v_codes, k_scale, v_scale, seq_lens_before, scale, window=0,
+                      ring=False, block_table=None, block_size=16, nthreads=0):
+    """Several query tokens per sequence (q [B,h,n,d] bf16) over FP8 caches
+    that already hold them, with an optional sliding window (0: none) and
+    ring cache: dequantise (``dequantize_fp8``), then ``decode_window`` over
+    the dequantised values.  Returns out [B,h,n,d], lse [B,h,n]."""
+    k = dequantize_fp8(k_codes, k_scale, 1)
+    v = dequantize_fp8(v_codes, v_scale, 1)
+    return decode_window(widen(q), k, v, seq_lens_before, scale, window, ring=ring,
+                         block_table=block_table, block_size=block_size, nthreads=nthreads)

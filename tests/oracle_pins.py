@@ -612,6 +612,64 @@ def pin_fp8_dequantised_attention():
     assert changed.sum() <= B * 1 and not changed[0, 7:].any()
 
 
+def pin_fp8_multi_and_window():
+    """Several tokens per sequence over FP8 caches (window 0), and with a
+    sliding window and a ring cache: every token's row equals torch SDPA in
+    float64 over torch's dequantisation of the positions it sees."""
+    gen = torch.Generator().manual_seed(44)
+    B, h, g, d, n = 3, 4, 2, 16, 5
+    before = [0, 6, 23]
+    t_cap = 32
+    ks = np.array([0.04, 0.3], np.float32)
+    vs = np.array([0.02, 0.6], np.float32)
+    q = torch.randn(B, h, n, d, generator=gen).to(torch.bfloat16)
+    kn = torch.randn(B, g, n, d, generator=gen).to(torch.bfloat16)
+    vn = torch.randn(B, g, n, d, generator=gen).to(torch.bfloat16)
+    kc0 = oracle.quantize_fp8(torch.randn(B, g, t_cap, d, generator=gen) * 2, ks, 1)
+    vc0 = oracle.quantize_fp8(torch.randn(B, g, t_cap, d, generator=gen) * 3, vs, 1)
+    kc, vc = oracle.append_fp8(kn, vn, kc0, vc0, ks, vs, before)
+    # the n new codes are those of the bf16 rows, and nothing else moved
+    for b in range(B):
+        for t in range(n):
+            assert np.array_equal(kc[b, :, before[b] + t], oracle.quantize_fp8(kn, ks, 1)[b, :, t])
+    kd = torch.from_numpy(kc).view(torch.float8_e4m3fn).to(torch.float64) * \
+        torch.from_numpy(ks).double().view(1, g, 1, 1)
+    vd = torch.from_numpy(vc).view(torch.float8_e4m3fn).to(torch.float64) * \
+        torch.from_numpy(vs).double().view(1, g, 1, 1)
+    sc = 0.3
+    qf = q.to(torch.float64)
+    for window in (0, 1, 4, 100):
+        o, l = oracle.decode_fp8_window(q, kc, vc, ks, vs, before, sc, window)
+        for b in range(B):
+            for t in range(n):
+                x = before[b] + t
+                lo = max(0, x + 1 - window) if window else 0
+                for i in range(h):
+                    j = i * g // h
+                    s_ = (kd[b, j, lo:x + 1] @ qf[b, i, t]) * float(np.float32(sc))
+                    w = torch.softmax(s_, 0)
+                    ro = w @ vd[b, j, lo:x + 1]
+                    assert torch.max(torch.abs(torch.from_numpy(o[b, i, t]) - ro)) < 1e-12
+                    assert abs(l[b, i, t] - float(torch.logsumexp(s_, 0))) < 1e-12
+    # a ring of 8 slots written step by step gives the linear cache's rows
+    window, ring_cap = 4, 8
+    kr = np.zeros((B, g, ring_cap, d), np.uint8)
+    vr = np.zeros((B, g, ring_cap, d), np.uint8)
+    lin_k = np.zeros((B, g, 64, d), np.uint8)
+    lin_v = np.zeros((B, g, 64, d), np.uint8)
+    lens = np.array([0, 2, 9], np.int32)
+    for step in range(6):
+        kn = torch.randn(B, g, 3, d, generator=gen).to(torch.bfloat16)
+        vn = torch.randn(B, g, 3, d, generator=gen).to(torch.bfloat16)
+        qs = torch.randn(B, h, 3, d, generator=gen).to(torch.bfloat16)
+        kr, vr = oracle.append_fp8(kn, vn, kr, vr, ks, vs, lens, ring=True)
+        lin_k, lin_v = oracle.append_fp8(kn, vn, lin_k, lin_v, ks, vs, lens)
+        o1, l1 = oracle.decode_fp8_window(qs, kr, vr, ks, vs, lens, sc, window, ring=True)
+        o2, l2 = oracle.decode_fp8_window(qs, lin_k, lin_v, ks, vs, lens, sc, window)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), step
+        lens = lens + 3
+
+
 ALL_PINS = [
     pin_d1_worked_example,
     pin_sdpa_crosscheck,
@@ -634,4 +692,5 @@ ALL_PINS = [
     pin_beam_gather,
     pin_fp8_format,
     pin_fp8_dequantised_attention,
+    pin_fp8_multi_and_window,
 ]

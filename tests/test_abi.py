@@ -351,7 +351,8 @@ def test_public_calls_carry_the_device_guard():
     first GPU tensor made current (and rejects tensors of another device)."""
     for name in ["append", "decode", "decode_paged", "append_decode", "decode_multi",
                  "append_decode_multi", "decode_window", "copy_blocks", "fork_block_tables",
-                 "gather_cache", "append_fp8", "decode_fp8"]:
+                 "gather_cache", "append_fp8", "decode_fp8", "decode_fp8_window",
+                 "append_decode_noalloc"]:
         fn = getattr(kvc, name)
         assert hasattr(fn, "__wrapped__"), name
         assert name in kvc.__all__, name
@@ -424,3 +425,37 @@ def test_noalloc_validation_codes():
     big = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 1, 128, 131088, 0.1, 1, 200, FAKE, FAKE, None]
     assert f(*big) == 5
     assert lib.kvc_status_string(5).startswith(b"the call needs more split scratch")
+
+
+def test_fp8_multi_window_validation_codes():
+    """The FP8 multi-token and window calls validate like the bf16 ones,
+    plus the scales, before any HIP call."""
+    lib = kvc.load_library()
+    f = lib.kvc_decode_attention_fp8_window
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 2, 64, 10, 1, 0.1, 1, None, 0, FAKE,
+            FAKE, None]
+    bad = list(args); bad[3] = None                  # k_scale missing
+    assert f(*bad) == INVALID
+    bad = list(args); bad[12] = 0                    # ring without a window
+    assert f(*bad) == INVALID
+    bad = list(args); bad[12] = 64                   # window + n - 1 > t_cap
+    assert f(*bad) == INVALID
+    bad = list(args); bad[10] = 0                    # n = 0
+    assert f(*bad) == INVALID
+    fm = lib.kvc_append_decode_attention_fp8_multi
+    margs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 4, 64, 0.1, 1, None, 0,
+             FAKE, FAKE, None]
+    for i in (1, 2, 5, 6):                           # k_new, v_new, k_scale, v_scale
+        bad = list(margs); bad[i] = None
+        assert fm(*bad) == INVALID
+    bad = list(margs); bad[15] = 2                   # split plan without a workspace
+    assert fm(*bad) == WORKSPACE
+    fp = lib.kvc_append_decode_attention_fp8_window_paged
+    pargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 2, 5,
+             0.1, 1, None, 0, FAKE, FAKE, None]
+    bad = list(pargs); bad[17] = -1                  # negative window
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[9] = 12                   # block size not a power of two
+    assert fp(*bad) == INVALID
+    bad = list(pargs); bad[6] = ctypes.c_void_p(0x1002)  # misaligned k_scale
+    assert fp(*bad) == INVALID

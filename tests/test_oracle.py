@@ -254,12 +254,29 @@ def _dequantize_first_head_scale(codes, scale, head_axis):
     return x * float(np.asarray(scale, dtype=np.float32)[0])
 
 
+def _fp8_window_one_short(q, kc, vc, ks, vs, before, scale, window=0, ring=False,
+                          block_table=None, block_size=16, nthreads=0):
+    return _ORIG_FP8_WINDOW(q, kc, vc, ks, vs, before, scale, max(window - 1, 0) if window else 0,
+                            ring=ring, block_table=block_table, block_size=block_size)
+
+
+def _append_fp8_ring_shifted(k_new, v_new, kc, vc, ks, vs, before, block_table=None, ring=False):
+    shift = 1 if ring else 0
+    return _ORIG_APPEND_FP8(k_new, v_new, kc, vc, ks, vs, np.asarray(before) + shift,
+                            block_table=block_table, ring=ring)
+
+
+_ORIG_FP8_WINDOW = oracle.decode_fp8_window
+_ORIG_APPEND_FP8 = oracle.append_fp8
+
 FP8_MUTATIONS = {
     "ties_to_odd": ("e4m3_encode", _encode_ties_odd),
     "no_saturation": ("e4m3_encode", _encode_no_saturation),
     "scale_multiplies": ("quantize_fp8", _quantize_by_multiply),
     "dequantise_divides": ("dequantize_fp8", _dequantize_dividing),
     "dequantise_one_scale": ("dequantize_fp8", _dequantize_first_head_scale),
+    "fp8_window_one_short": ("decode_fp8_window", _fp8_window_one_short),
+    "fp8_ring_slot_shifted": ("append_fp8", _append_fp8_ring_shifted),
 }
 
 
@@ -268,7 +285,7 @@ def test_planted_fp8_mistake_is_caught(name, monkeypatch):
     attr, fn = FP8_MUTATIONS[name]
     monkeypatch.setattr(oracle, attr, fn)
     failed = 0
-    for pin in (P.pin_fp8_format, P.pin_fp8_dequantised_attention):
+    for pin in (P.pin_fp8_format, P.pin_fp8_dequantised_attention, P.pin_fp8_multi_and_window):
         try:
             pin()
         except Exception:  # noqa: BLE001 - any failure counts
