@@ -133,13 +133,14 @@ def stored_traffic(workload: str):
     return int(kv["traffic_bytes_per_call"])
 
 
-def algorithmic_bytes(w, attended, nblocks=None, n=1, kv_bytes=None):
+def algorithmic_bytes(w, attended, nblocks=None, n=1, kv_bytes=None, block_scales=False):
     """Bytes one step must move: KV read (``attended`` positions per
     sequence: all of them, or those a sliding window keeps), q read, out and
     lse written (float32), the appended K/V written, and the block table read
     (paged).  n new tokens (queries) per sequence.  kv_bytes: bytes per
     cached element when the cache is stored narrower than the inputs (1 for
-    FP8 codes, whose per-KV-head scales are read too)."""
+    FP8 codes, whose per-KV-head scales are read too; with block_scales one
+    K and one V scale per block and KV head read instead)."""
     B, h, g, d, eb = w.B, w.h, w.g, w.d, w.elem_bytes
     cb = eb if kv_bytes is None else kv_bytes
     kv_read = 2 * int(attended.sum()) * g * d * cb
@@ -149,6 +150,8 @@ def algorithmic_bytes(w, attended, nblocks=None, n=1, kv_bytes=None):
     append_read = 2 * B * g * n * d * eb
     table = 0 if nblocks is None else int(nblocks.sum()) * 4
     scales = 0 if kv_bytes is None else 2 * g * 4
+    if block_scales and nblocks is not None:
+        scales = 2 * int(nblocks.sum()) * g * 4
     decode = kv_read + q_read + out_write + table + B * 4 + scales
     # One-call step: the new token's K/V are read once, from k_new / v_new
     # (counted in kv_read at the cache's width, so the difference to the
@@ -335,6 +338,9 @@ def main():
     ap.add_argument("--kv-fp8", action="store_true",
                     help="the cache holds FP8 E4M3 codes with per-KV-head scales "
                          "(kvc_append_decode_attention_fp8); one token per sequence, no window")
+    ap.add_argument("--fp8-block-scales", action="store_true",
+                    help="with --kv-fp8 on a paged workload: one scale per (physical block, KV "
+                         "head) instead of per KV head (kvc_decode_attention_fp8_paged_block_scaled)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -396,11 +402,21 @@ def main():
     if fp8 and w.dtype != "bf16":
         print("--kv-fp8 takes a bf16 workload", file=sys.stderr)
         sys.exit(2)
+    blk_sc = args.fp8_block_scales
+    if blk_sc and not (fp8 and w.paged and not args.separate):
+        print("--fp8-block-scales needs --kv-fp8, a paged workload and the one-call step",
+              file=sys.stderr)
+        sys.exit(2)
     if fp8:
-        # per-KV-head scales amax / 448 over the cache; codes by torch's
+        # per-KV-head scales amax / 448 over the cache (or per block and KV
+        # head with --fp8-block-scales); codes by torch's
         # float8_e4m3fn conversion (round to nearest even), from the same
         # seeded N(0, 1) cache as the bf16 run
         def quantise(t):
+            if blk_sc:  # per (block, KV head): amax over the block's rows
+                sc = (t.float().abs().amax(dim=(2, 3)) / 448.0).clamp(min=1e-12)
+                codes = (t.float() / sc.view(sc.shape[0], -1, 1, 1)).to(torch.float8_e4m3fn)
+                return codes.view(torch.uint8), sc
             amax = t.float().abs().amax(dim=(0, 2, 3))
             sc = (amax / 448.0).clamp(min=1e-12)
             codes = (t.float() / sc.view(1, -1, 1, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
@@ -496,7 +512,15 @@ def main():
 
     def fused_call(i):
         kc, vc = ks[i % copies], vs[i % copies]
-        if fp8 and (nq > 1 or windowed):
+        if blk_sc:
+            kvc.decode_fp8_block_scaled(q.view(w.B, w.h, nq, w.d), kc, vc, k_sc_d, v_sc_d,
+                                        sl_before, bt, window=win, scale=x["scale"],
+                                        num_splits=ns, workspace=ws,
+                                        out=out.view(w.B, w.h, nq, w.d),
+                                        lse=lse.view(w.B, w.h, nq),
+                                        k_new=k_new.view(w.B, w.g, nq, w.d),
+                                        v_new=v_new.view(w.B, w.g, nq, w.d))
+        elif fp8 and (nq > 1 or windowed):
             kvc.decode_fp8_window(q, kc, vc, k_sc_d, v_sc_d, sl_before, window=win, ring=ring,
                                   block_table=bt, scale=x["scale"], num_splits=ns, workspace=ws,
                                   out=out, lse=lse, k_new=k_new, v_new=v_new)
@@ -681,7 +705,8 @@ def main():
     hi = x["seq_lens_before"].to(torch.int64) + nq
     lo = torch.clamp(x["seq_lens_before"].to(torch.int64) + 1 - win, min=0) if windowed \
         else torch.zeros_like(hi)
-    nbytes = algorithmic_bytes(w, hi - lo, nblocks, n=nq, kv_bytes=1 if fp8 else None)
+    nbytes = algorithmic_bytes(w, hi - lo, nblocks, n=nq, kv_bytes=1 if fp8 else None,
+                               block_scales=blk_sc)
     # stored counter runs are of the default (one-call) step
     traffic = None if (args.separate or nq > 1 or windowed) else \
         stored_traffic(w.name + ("_kvfp8" if fp8 else ""))
@@ -696,7 +721,7 @@ def main():
     achieved_tflops = flops / (dec_avg_ms * 1e-3) / 1e12
 
     cpu = None
-    if not args.no_cpu_baseline and nq == 1 and not windowed:
+    if not args.no_cpu_baseline and nq == 1 and not windowed and not blk_sc:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, x, w.paged,
                            fp8=(k_src.numpy(), v_src.numpy(), k_sc.numpy(), v_sc.numpy())
@@ -713,7 +738,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8 e4m3 KV cache (per-KV-head scales), bf16 q, fp32 accumulate" if fp8
+        "dtype": ("fp8 e4m3 KV cache (per-block, per-KV-head scales), bf16 q, fp32 accumulate"
+                  if blk_sc else
+                  "fp8 e4m3 KV cache (per-KV-head scales), bf16 q, fp32 accumulate" if fp8
                   else "bf16 in, fp32 accumulate" if w.dtype == "bf16" else "f32"),
         "data": "synthetic, seeded N(0,1)",
         "config": {

@@ -530,6 +530,46 @@ int kvc_append_decode_attention_fp8_window_paged(
     float* out, float* lse, hipStream_t stream);
 
 /*
+ * FP8 paged pools with a scale per (physical block, KV head) ([P3] 14 and
+ * [P4] 2.5: low-bit K/V; a scale per page lets each block follow the range
+ * of the values it holds): k_scale, v_scale are device float32 [num_blocks,
+ * g]; the value of a stored code in block blk, KV head j is code *
+ * scale[blk, j].  Choosing a block's scale (calibration) is the caller's
+ * business; it must be set before tokens are written into the block.
+ *
+ * kvc_append_fp8_paged_block_scaled -- n new tokens per sequence (k_new,
+ *   v_new bf16 [B, g, n, d]): token t of sequence b is written at position
+ *   seq_lens_before[b] + t as the codes of x / scale[blk, j] of its target
+ *   block (nearest code, ties to even, saturating, as kvc_append_fp8).
+ *   Positions outside the table or whose entry is not a valid block are
+ *   skipped.
+ * kvc_decode_attention_fp8_paged_block_scaled -- attention over such a
+ *   pool for n query tokens per sequence (q bf16 [B, h, n, d], out
+ *   [B, h, n, d], lse [B, h, n]), with an optional sliding window (window 0 =
+ *   none), and with k_new, v_new (bf16 [B, g, n, d]) also the append (one
+ *   launch; seq_lens are then the lengths before the step, else the lengths
+ *   including the n tokens).  Both or neither of k_new, v_new.  Positions,
+ *   masks, splits and the workspace (kvc_decode_workspace_bytes(B, h * n, g,
+ *   d, KVC_BF16, L, num_splits, 1) with L = min(W + n - 1, max_blocks *
+ *   block_size) for W > 0, else max_blocks * block_size) as in the bf16
+ *   paged _multi / _window calls.  Attention is over the dequantised values:
+ *   each score uses the K scale of its position's block, and each V row is
+ *   weighted by its block's V scale; a new token whose table entry is not a
+ *   valid block is attended with the scales of the clamped entry.
+ */
+int kvc_append_fp8_paged_block_scaled(const void* k_new, const void* v_new, void* k_pool,
+                                      void* v_pool, const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, int max_blocks, int block_size,
+                                      int num_blocks, const int32_t* seq_lens_before, int B, int g,
+                                      int d, int n, hipStream_t stream);
+int kvc_decode_attention_fp8_paged_block_scaled(
+    const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const float* k_scale, const float* v_scale, const int32_t* block_table, int max_blocks,
+    int block_size, int num_blocks, const int32_t* seq_lens, int B, int h, int g, int d, int n,
+    int window, float scale, int num_splits, void* workspace, size_t workspace_bytes, float* out,
+    float* lse, hipStream_t stream);
+
+/*
  * Block operations for shared and re-ranked caches ([P4] 4.3: requests that
  * share a prompt fork its block table and point at the same physical
  * blocks; before one of them writes into a shared block, the block is copied

@@ -26,7 +26,8 @@ import torch
 
 __all__ = ["append", "decode", "decode_paged", "append_decode", "decode_multi",
            "append_decode_multi", "decode_window", "append_fp8", "decode_fp8", "decode_fp8_window",
-           "append_decode_noalloc", "copy_blocks",
+           "append_decode_noalloc", "append_fp8_block_scaled", "decode_fp8_block_scaled",
+           "copy_blocks",
            "fork_block_tables", "gather_cache", "plan", "workspace_bytes", "launch_shape",
            "KvcError", "load_library", "LIB_PATH", "F32", "BF16", "FP8_E4M3", "SPLITS_STREAM"]
 
@@ -152,6 +153,13 @@ def load_library():
                  "kvc_decode_attention_fp8_window_paged", "kvc_append_decode_attention_fp8_window",
                  "kvc_append_decode_attention_fp8_window_paged"):
         getattr(lib, name).restype = ip
+    lib.kvc_append_fp8_paged_block_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, ip, ip, ip, vp,
+                                                      ip, ip, ip, ip, vp]
+    lib.kvc_append_fp8_paged_block_scaled.restype = ip
+    lib.kvc_decode_attention_fp8_paged_block_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip,
+                                                                ip, ip, vp, ip, ip, ip, ip, ip, ip,
+                                                                fp, ip, vp, sz, vp, vp, vp]
+    lib.kvc_decode_attention_fp8_paged_block_scaled.restype = ip
     lib.kvc_copy_blocks.argtypes = [vp, vp, vp, ip, ip, ip, ip, ip, ip, vp]
     lib.kvc_copy_blocks.restype = ip
     lib.kvc_fork_block_tables.argtypes = [vp, vp, ip, ip, vp, ip, vp, vp, vp]
@@ -840,4 +848,68 @@ def append_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seq_lens_before,
         num_splits, _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32),
         _stream(stream))
     _check("kvc_append_decode_attention_noalloc", st)
+    return out, lse
+
+
+@_on_device
+def append_fp8_block_scaled(k_new, v_new, k_pool, v_pool, k_scale, v_scale, seq_lens_before,
+                            block_table, stream=None):
+    """Quantise n new tokens per sequence (bf16 [B,g,n,d]) into uint8 FP8
+    pools [NB,g,bs,d] whose scales are per (physical block, KV head):
+    k_scale, v_scale float32 [NB, g]."""
+    lib = load_library()
+    B, g, n, d = _shape(k_new, (None, None, None, None), "k_new")
+    _shape(v_new, (B, g, n, d), "v_new")
+    _shape(seq_lens_before, (B,), "seq_lens_before")
+    gp, _, bs, mb, nb = _cache_shapes(k_pool, v_pool, B, d, block_table)
+    if gp != g:
+        raise ValueError(f"k_new has {g} KV heads, the pool {gp}")
+    _shape(k_scale, (nb, g), "k_scale")
+    _shape(v_scale, (nb, g), "v_scale")
+    _check("kvc_append_fp8_paged_block_scaled", lib.kvc_append_fp8_paged_block_scaled(
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16),
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(block_table, "block_table", torch.int32), mb, bs, nb,
+        _dev(seq_lens_before, "seq_lens_before", torch.int32), B, g, d, n, _stream(stream)))
+
+
+@_on_device
+def decode_fp8_block_scaled(q, k_pool, v_pool, k_scale, v_scale, seq_lens, block_table,
+                            window: int = 0, scale: Optional[float] = None, num_splits: int = 0,
+                            workspace: Optional[torch.Tensor] = None, out=None, lse=None,
+                            stream=None, k_new=None, v_new=None):
+    """Attention for q (bf16 [B,h,n,d]) over uint8 FP8 pools [NB,g,bs,d]
+    with per-(block, KV head) scales [NB, g]; token t sees the positions up
+    to its own (the last ``window`` of them when window > 0).  With k_new,
+    v_new (bf16 [B,g,n,d]) the call also quantises and appends the tokens
+    (seq_lens = lengths before the step).  Returns (out [B,h,n,d] float32,
+    lse [B,h,n] float32)."""
+    lib = load_library()
+    B, h, n, d = _shape(q, (None, None, None, None), "q")
+    g, _, bs, mb, nb = _cache_shapes(k_pool, v_pool, B, d, block_table)
+    _shape(k_scale, (nb, g), "k_scale")
+    _shape(v_scale, (nb, g), "v_scale")
+    _shape(seq_lens, (B,), "seq_lens")
+    fused = k_new is not None
+    if fused:
+        _new_tokens(k_new, v_new, B, g, n, d)
+    elif v_new is not None:
+        raise ValueError("v_new without k_new")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    ws, wsb = _workspace(lib.kvc_decode_workspace_bytes(B, h * n, g, d, BF16,
+                                                        _plan_len(mb * bs, window, n), num_splits,
+                                                        1), q, workspace)
+    st = lib.kvc_decode_attention_fp8_paged_block_scaled(
+        _dev(q, "q", torch.bfloat16), _dev(k_new, "k_new", torch.bfloat16) if fused else None,
+        _dev(v_new, "v_new", torch.bfloat16) if fused else None,
+        _dev(k_pool, "k_pool", torch.uint8), _dev(v_pool, "v_pool", torch.uint8),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(block_table, "block_table", torch.int32), mb, bs, nb,
+        _dev(seq_lens, "seq_lens", torch.int32), B, h, g, d, n, window, float(scale), num_splits,
+        ws.data_ptr() if ws is not None else None, wsb, _dev(out, "out", torch.float32),
+        _dev(lse, "lse", torch.float32), _stream(stream))
+    _check("kvc_decode_attention_fp8_paged_block_scaled", st)
     return out, lse

@@ -87,7 +87,8 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, vo
 }
 
 // FP8 E4M3 cache: new token k of sequence b, KV head j, element e: the
-// bf16 value divided by the head's float32 scale, encoded (nearest code,
+// bf16 value divided by the float32 scale (the KV head's, or with
+// block_scales that of the (target block, KV head)), encoded (nearest code,
 // ties to even, saturating at 448), written at position seq_lens[b] + k.
 // One thread per (tensor, sequence, KV head, token, element).
 __global__ void __launch_bounds__(256) append_fp8_kernel(
@@ -95,7 +96,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int max_blocks,
     int block_size, const int32_t* __restrict__ seq_lens, int B, int g, int n, int d, int capacity,
-    int ring) {
+    int ring, int block_scales) {
     const long total = (long)B * g * n * d;
     long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const bool is_v = t >= total;
@@ -111,6 +112,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(
     if (pos_l < 0 || pos_l > 0x7fffffffL) return;
     const int pos = (int)pos_l;
     long row;
+    long sidx = j;  // the scale: per KV head, or per (block, KV head)
     if (block_table == nullptr) {
         if (ring) {
             row = bj * (long)capacity + pos % capacity;
@@ -124,9 +126,10 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(
         const int phys = block_table[(long)b * max_blocks + logical];
         if (phys < 0 || phys >= capacity) return;
         row = ((long)phys * g + j) * block_size + (pos % block_size);
+        if (block_scales) sidx = (long)phys * g + j;
     }
     const float x = __uint_as_float((uint32_t)(is_v ? v_new : k_new)[tok * d + e] << 16);
-    const float sc = is_v ? v_scale[j] : k_scale[j];
+    const float sc = is_v ? v_scale[sidx] : k_scale[sidx];
     (is_v ? v_cache : k_cache)[row * d + e] = (uint8_t)e4m3_encode(x / sc);
 }
 
@@ -134,12 +137,12 @@ hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache
                              const float* k_scale, const float* v_scale,
                              const int32_t* block_table, int max_blocks, int block_size,
                              const int32_t* seq_lens_before, int B, int g, int n, int d,
-                             int capacity, int ring, hipStream_t s) {
+                             int capacity, int ring, int block_scales, hipStream_t s) {
     const long total = 2L * B * g * n * d;
     append_fp8_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
         (const uint16_t*)k_new, (const uint16_t*)v_new, (uint8_t*)k_cache, (uint8_t*)v_cache,
         k_scale, v_scale, block_table, max_blocks, block_size, seq_lens_before, B, g, n, d,
-        capacity, ring);
+        capacity, ring, block_scales);
     return hipGetLastError();
 }
 

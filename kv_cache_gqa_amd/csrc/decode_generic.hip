@@ -72,8 +72,11 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     const TQ* q = (const TQ*)a.q;
     const T* K = (const T*)a.k;
     const T* V = (const T*)a.v;
-    const float k_sc = a.kv8 ? a.k_scale[j] : 1.0f;
-    const float v_sc = a.kv8 ? a.v_scale[j] : 1.0f;
+    // FP8 scales: per KV head (folded into q and the output), or per
+    // (block, KV head) (applied per position)
+    const bool bsc = a.kv8 && a.block_scales;
+    const float k_sc = a.kv8 && !bsc ? a.k_scale[j] : 1.0f;
+    const float v_sc = a.kv8 && !bsc ? a.v_scale[j] : 1.0f;
     // new tokens: element type of k_new / v_new, their rows, cache rows
     using TN = typename std::conditional<sizeof(T) == 1, TQ, T>::type;
     const bool appends = a.k_new != nullptr;
@@ -85,10 +88,15 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         const int s0 = max(c0, raw), s1 = min(c0 + a.chunk_len, ur.hi);
         for (int p = s0; p < s1; ++p) {
             long row;
+            float wk = k_sc, wv = v_sc;  // the scales the new codes are made with
             if (a.block_table != nullptr) {
                 const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
                 if (phys < 0 || phys >= a.num_blocks) continue;
                 row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+                if (bsc) {
+                    wk = a.k_scale[(long)phys * a.g + j];
+                    wv = a.v_scale[(long)phys * a.g + j];
+                }
             } else {
                 row = contig_base + cache_slot(a, p);
             }
@@ -97,8 +105,8 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
                 if constexpr (sizeof(T) == 1) {
                     const float x = load_f((const TN*)a.k_new, src);
                     const float y = load_f((const TN*)a.v_new, src);
-                    const_cast<T*>(K)[row * d + dim] = (T)e4m3_encode(x / k_sc);
-                    const_cast<T*>(V)[row * d + dim] = (T)e4m3_encode(y / v_sc);
+                    const_cast<T*>(K)[row * d + dim] = (T)e4m3_encode(x / wk);
+                    const_cast<T*>(V)[row * d + dim] = (T)e4m3_encode(y / wv);
                 } else {
                     const_cast<T*>(K)[row * d + dim] = ((const T*)a.k_new)[src];
                     const_cast<T*>(V)[row * d + dim] = ((const T*)a.v_new)[src];
@@ -128,19 +136,27 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     };
     for (int pb = p0; pb < p1; pb += kBatch) {
         float kx[kBatch][4], vx[kBatch][4];
+        float ksp[kBatch], vsp[kBatch];  // per-block scales of the batch's positions
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int p = min(pb + u, p1 - 1);  // past the end: repeat the last position (masked)
             const bool fresh = appends && p >= raw;  // uniform over the wavefront
             const long row = row_of(p, fresh);
+            ksp[u] = vsp[u] = 1.0f;
+            if (bsc) {
+                const long si = fp8_scale_index(a, b, j, p);
+                ksp[u] = a.k_scale[si];
+                vsp[u] = a.v_scale[si];
+            }
+            const float nk = bsc ? ksp[u] : k_sc, nv = bsc ? vsp[u] : v_sc;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int dim = lane + 64 * kk;
                 kx[u][kk] = vx[u][kk] = 0.0f;
                 if (dim < d) {
                     if (fresh) {
-                        kx[u][kk] = new_value<T>(load_f((const TN*)a.k_new, row * d + dim), k_sc);
-                        vx[u][kk] = new_value<T>(load_f((const TN*)a.v_new, row * d + dim), v_sc);
+                        kx[u][kk] = new_value<T>(load_f((const TN*)a.k_new, row * d + dim), nk);
+                        vx[u][kk] = new_value<T>(load_f((const TN*)a.v_new, row * d + dim), nv);
                     } else {
                         kx[u][kk] = load_f(K, row * d + dim);
                         vx[u][kk] = load_f(V, row * d + dim);
@@ -155,7 +171,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
             float part = 0.0f;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) part += qv[kk] * kx[u][kk];
-            sc[u] = pb + u < p1 ? wave_sum(part) : kNegInf;
+            sc[u] = pb + u < p1 ? wave_sum(part) * ksp[u] : kNegInf;
             bmax = fmaxf(bmax, sc[u]);
         }
         const float mnew = fmaxf(m, bmax);
@@ -167,8 +183,9 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         for (int u = 0; u < kBatch; ++u) {
             const float pw = fast_exp2(sc[u] - mnew);  // 0 for masked positions
             l += pw;
+            const float pwv = pw * vsp[u];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc[kk] += pw * vx[u][kk];
+            for (int kk = 0; kk < 4; ++kk) acc[kk] += pwv * vx[u][kk];
         }
         m = mnew;
     }

@@ -102,18 +102,26 @@ struct TileRegs<true> {
 // GEN: several query tokens per sequence, sliding windows or ring caches
 // (per-row visibility masks, ring-aware windows).  Without it a row sees
 // every position of its segment, which keeps the common path's registers.
-// KV8: the cache holds FP8 E4M3 codes with a float32 scale per KV head;
-// the codes are converted to bf16 exactly and the head's scales are folded
-// into the score scale (K) and the output (V).
-template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
+// KV8: 0 = bf16 cache; 1 = FP8 E4M3 codes with a float32 scale per KV
+// head: the codes are converted to bf16 exactly and the head's scales are
+// folded into the score scale (K) and the output (V); 2 = FP8 codes with a
+// scale per (physical block, KV head) of a paged pool: each lane's K scale
+// multiplies its scores and its V scale the weights P of its positions
+// before they are rounded for the PV product (the normalising sum stays
+// that of the unscaled P).
+template <int NQT, bool PAGED, int W, bool GEN, int KV8>
 struct MfmaEngine {
     using L = Lds<NQT, W>;
+    static constexpr bool kF8 = KV8 != 0;
+    static constexpr bool kBS = KV8 == 2;  // per-block scales
+    static_assert(!kBS || PAGED, "per-block scales need a paged pool");
     // One set of tile registers: with two query tiles (64 accumulator and 32
     // query registers per lane) it lets two wavefronts share a SIMD; in the
     // 4-wavefront FP8 kernels, three.
     static constexpr bool kSingleBuffer = NQT >= 2 || (KV8 && W == 4);
     struct Shared {
         uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
+        float bsc[kBS ? 2 * kMaxTableSlice : 1];   // per block: K scale, then (+kMaxTableSlice) V scale
         __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     };
 
@@ -147,11 +155,15 @@ struct MfmaEngine {
         f32x4_t acc[NQT][8];
         f32x4_t lacc[NQT];  // sum of bf16-rounded P (normalises out)
         float lex[NQT];     // sum of fp32 P over this lane's positions (gives lse)
+        // per-block scales: sum over this lane's positions of the weights the
+        // PV product applies, bf16(P * v_scale) / v_scale (normalises out)
+        float lw[kBS ? NQT : 1];
         float mrun[NQT];
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
             mrun[qt] = kNegInf;
             lex[qt] = 0.0f;
+            if constexpr (kBS) lw[qt] = 0.0f;
             lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -160,8 +172,8 @@ struct MfmaEngine {
 
         unsigned char* vst = sh.lds + wave * kVStageBytes;
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
-        const float k_sc = KV8 ? a.k_scale[j] : 1.0f;  // FP8 head scales
-        const float v_sc = KV8 ? a.v_scale[j] : 1.0f;
+        const float k_sc = KV8 == 1 ? a.k_scale[j] : 1.0f;  // FP8 head scales
+        const float v_sc = KV8 == 1 ? a.v_scale[j] : 1.0f;
         const float sl2 = a.scale_log2e * k_sc;
         int blk0 = 0;  // first block of the current window (paged)
         int w0 = s;  // start of the current window
@@ -234,6 +246,8 @@ struct MfmaEngine {
             new_wave = new_i0 < new_tiles;
         }
         const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
+        // scale index of the one new token (FP8 single-token calls)
+        const long new_sidx = kBS && kNewPair && has_new ? fp8_scale_index(a, b, j, raw) : (long)j;
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : Q;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Q;
@@ -247,7 +261,7 @@ struct MfmaEngine {
         const bool reread = NQT >= 2 && a.slices > 1;
         auto ld16_kv = [&](const void* p) { return reread ? ld16(p) : ld16_stream(p); };
         auto ld8_kv = [&](const void* p) { return reread ? ld8(p) : ld8_stream(p); };
-        auto load_k = [&](int t0, TileRegs<KV8>& tr) {
+        auto load_k = [&](int t0, TileRegs<kF8>& tr) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const uint32_t row = kv_row(min(t0 + 16 * tt + col, w1 - 1));
@@ -261,7 +275,7 @@ struct MfmaEngine {
             }
         };
         // V rows 4u + G, chunk col: four whole rows per instruction.
-        auto load_v = [&](int t0, TileRegs<KV8>& tr) {
+        auto load_v = [&](int t0, TileRegs<kF8>& tr) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint32_t row = kv_row(min(t0 + 4 * u + G, w1 - 1));
@@ -269,7 +283,7 @@ struct MfmaEngine {
                 else tr.v[u] = ld16_kv(row_ptr(vwin, vlane, row, 0));
             }
         };
-        auto load_tile = [&](int t0, TileRegs<KV8>& tr) {
+        auto load_tile = [&](int t0, TileRegs<kF8>& tr) {
             load_k(t0, tr);
             load_v(t0, tr);
         };
@@ -277,9 +291,9 @@ struct MfmaEngine {
         // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  With
         // one new token every position of the tile is that token: its rows
         // (FP8: their codes) go to this wavefront's V staging area first.
-        auto load_new_tile = [&](int t0, TileRegs<KV8>& tr) {
+        auto load_new_tile = [&](int t0, TileRegs<kF8>& tr) {
             if constexpr (KV8 && kNewPair) {
-                new_row_codes_fp8_d128(a, j, lane, new_pair, vst);
+                new_row_codes_fp8_d128(a, new_sidx, lane, new_pair, vst);
                 wave_lds_sync();
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
@@ -302,10 +316,10 @@ struct MfmaEngine {
             } else if constexpr (KV8) {
                 // several new tokens over an FP8 cache: their bf16 rows,
                 // quantised here to the codes the cache receives
-                const float ks_ = a.k_scale[j], vs_ = a.v_scale[j];
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
+                    const float ks_ = a.k_scale[kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : j];
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
                         const uint2 lo = e4m3_encode8(ld16(KN + r * kD + 64 * hh + 16 * G), ks_);
@@ -316,6 +330,7 @@ struct MfmaEngine {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
+                    const float vs_ = a.v_scale[kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : j];
                     tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * col), vs_);
                 }
             } else {
@@ -333,7 +348,7 @@ struct MfmaEngine {
             }
         };
         // MFMA A operand of K chunk ks of sub-tile tt.
-        auto k_operand = [&](const TileRegs<KV8>& tr, int tt, int ks) -> uint4 {
+        auto k_operand = [&](const TileRegs<kF8>& tr, int tt, int ks) -> uint4 {
             if constexpr (KV8) {
                 const uint4 c = tr.k[tt][ks >> 1];
                 return e4m3x8_to_bf16((ks & 1) ? make_uint2(c.z, c.w) : make_uint2(c.x, c.y));
@@ -341,7 +356,7 @@ struct MfmaEngine {
                 return tr.k[tt][ks];
             }
         };
-        auto v_row = [&](const TileRegs<KV8>& tr, int u) -> uint4 {
+        auto v_row = [&](const TileRegs<kF8>& tr, int u) -> uint4 {
             if constexpr (KV8) return e4m3x8_to_bf16(tr.v[u]);
             else return tr.v[u];
         };
@@ -349,7 +364,33 @@ struct MfmaEngine {
         // after_qk runs once the K registers are consumed, after_stage once
         // the V registers are (a single-buffered walk reloads them there).
         auto no_hook = [] {};
-        auto compute_tile = [&](int t0, const TileRegs<KV8>& tr, auto after_qk, auto after_stage) {
+        // fresh: a tile of appended tokens (their scales are looked up, not
+        // in the table slice)
+        auto compute_tile = [&](int t0, const TileRegs<kF8>& tr, auto after_qk, auto after_stage,
+                                bool fresh) {
+            // per-block scales of the lane's eight positions 16*tt + 4*G + v
+            // (a segment may start anywhere, so they may span two blocks)
+            float sk[8], vf[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                sk[k] = sl2;
+                vf[k] = 1.0f;
+            }
+            if constexpr (kBS) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int p = min(t0 + 16 * (k >> 2) + 4 * G + (k & 3), w1 - 1);
+                    if (fresh) {
+                        const long si = fp8_scale_index(a, b, j, p);
+                        sk[k] = sl2 * a.k_scale[si];
+                        vf[k] = a.v_scale[si];
+                    } else {
+                        const int bi = (p >> a.log2_bs) - blk0;
+                        sk[k] = sl2 * sh.bsc[bi];
+                        vf[k] = sh.bsc[kMaxTableSlice + bi];
+                    }
+                }
+            }
             f32x4_t S[NQT][2];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -369,8 +410,10 @@ struct MfmaEngine {
                 *reinterpret_cast<uint4*>(vst + r * kVRowBytes + ((col ^ vswz(r)) << 4)) = v_row(tr, u);
             }
             after_stage();
-            // Online softmax; P as the B operand of the PV product.
+            // Online softmax; P as the B operand of the PV product (with
+            // per-block scales pbv = P times the V scales; pb stays P).
             uint4 pb[NQT];
+            uint4 pbv[kBS ? NQT : 1];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
                 float sv[8];
@@ -379,7 +422,7 @@ struct MfmaEngine {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int p = t0 + 16 * tt + 4 * G + v;
-                        const float x = S[qt][tt][v] * sl2;
+                        const float x = S[qt][tt][v] * sk[4 * tt + v];
                         const bool vis = GEN ? (p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen) : p < w1;
                         sv[4 * tt + v] = vis ? x : kNegInf;
                     }
@@ -403,6 +446,7 @@ struct MfmaEngine {
                     for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
                     lacc[qt] *= alpha;
                     lex[qt] *= alpha;
+                    if constexpr (kBS) lw[qt] *= alpha;
                 }
                 const float ref = (mrun[qt] == kNegInf) ? 0.0f : mrun[qt];
                 float pv[8];
@@ -415,6 +459,16 @@ struct MfmaEngine {
                 lex[qt] += psum;
                 pb[qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+                if constexpr (kBS) {
+                    pbv[qt] = make_uint4(pack_bf16x2(pv[0] * vf[0], pv[1] * vf[1]),
+                                         pack_bf16x2(pv[2] * vf[2], pv[3] * vf[3]),
+                                         pack_bf16x2(pv[4] * vf[4], pv[5] * vf[5]),
+                                         pack_bf16x2(pv[6] * vf[6], pv[7] * vf[7]));
+                    const uint4 w = pbv[qt];
+                    lw[qt] += bf16_lo(w.x) / vf[0] + bf16_hi(w.x) / vf[1] + bf16_lo(w.y) / vf[2] +
+                              bf16_hi(w.y) / vf[3] + bf16_lo(w.z) / vf[4] + bf16_hi(w.z) / vf[5] +
+                              bf16_lo(w.w) / vf[6] + bf16_hi(w.w) / vf[7];
+                }
             }
 
             wave_lds_sync();
@@ -433,10 +487,14 @@ struct MfmaEngine {
                 const uint2 hi = lds_read_tr16(vst + r1 * kVRowBytes + ((ch ^ vswz(r1)) << 4) + sub);
                 const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-                for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma(av, pb[qt], acc[qt][nt]);
+                for (int qt = 0; qt < NQT; ++qt) {
+                    if constexpr (kBS) acc[qt][nt] = mfma(av, pbv[qt], acc[qt][nt]);
+                    else acc[qt][nt] = mfma(av, pb[qt], acc[qt][nt]);
+                }
             }
 #pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) lacc[qt] = mfma(ones, pb[qt], lacc[qt]);
+            for (int qt = 0; qt < NQT; ++qt)
+                if constexpr (!kBS) lacc[qt] = mfma(ones, pb[qt], lacc[qt]);  // (per-block: lw)
 
             wave_lds_sync();
         };
@@ -462,6 +520,10 @@ struct MfmaEngine {
                     int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
                     ph = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
                     sh.tbl[t] = ((uint32_t)ph * (uint32_t)a.g + (uint32_t)j) * (uint32_t)a.block_size;
+                    if constexpr (kBS) {
+                        sh.bsc[t] = a.k_scale[(long)ph * a.g + j];
+                        sh.bsc[kMaxTableSlice + t] = a.v_scale[(long)ph * a.g + j];
+                    }
                 }
                 __syncthreads();
             }
@@ -481,43 +543,44 @@ struct MfmaEngine {
                 // this tile's V is staged; the schedule barriers keep the
                 // compiler from hoisting the loads (which would need a
                 // second set of registers).
-                TileRegs<KV8> tr;
+                TileRegs<kF8> tr;
                 load_tile(t0, tr);
                 for (; t0 < w1; t0 += stride) {
                     const int tn = t0 + stride;
                     compute_tile(t0, tr,
                                  [&] { __builtin_amdgcn_sched_barrier(0); load_k(tn, tr); __builtin_amdgcn_sched_barrier(0); },
-                                 [&] { __builtin_amdgcn_sched_barrier(0); load_v(tn, tr); __builtin_amdgcn_sched_barrier(0); });
+                                 [&] { __builtin_amdgcn_sched_barrier(0); load_v(tn, tr); __builtin_amdgcn_sched_barrier(0); },
+                                 false);
                 }
             } else if constexpr (kPair) {
-                TileRegs<KV8> a0, a1, b0, b1;
+                TileRegs<kF8> a0, a1, b0, b1;
                 load_tile(t0, a0);
                 load_tile(t0 + kTileTokens, a1);
                 for (;;) {
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, b0);
                     load_tile(t0 + stride + kTileTokens, b1);
-                    compute_tile(t0, a0, no_hook, no_hook);
-                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, a1, no_hook, no_hook);
+                    compute_tile(t0, a0, no_hook, no_hook, false);
+                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, a1, no_hook, no_hook, false);
                     t0 += stride;
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, a0);
                     load_tile(t0 + stride + kTileTokens, a1);
-                    compute_tile(t0, b0, no_hook, no_hook);
-                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, b1, no_hook, no_hook);
+                    compute_tile(t0, b0, no_hook, no_hook, false);
+                    if (t0 + kTileTokens < w1) compute_tile(t0 + kTileTokens, b1, no_hook, no_hook, false);
                     t0 += stride;
                 }
             } else {
-                TileRegs<KV8> tA, tB;
+                TileRegs<kF8> tA, tB;
                 load_tile(t0, tA);
                 for (;;) {
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, tB);
-                    compute_tile(t0, tA, no_hook, no_hook);
+                    compute_tile(t0, tA, no_hook, no_hook, false);
                     t0 += stride;
                     if (t0 >= w1) break;
                     load_tile(t0 + stride, tA);
-                    compute_tile(t0, tB, no_hook, no_hook);
+                    compute_tile(t0, tB, no_hook, no_hook, false);
                     t0 += stride;
                 }
             }
@@ -528,14 +591,14 @@ struct MfmaEngine {
         if (new_wave) {
             w1 = e;
             if constexpr (kNewPair) {  // one new token: one tile
-                TileRegs<KV8> tr;
+                TileRegs<kF8> tr;
                 load_new_tile(fresh_lo, tr);
-                compute_tile(fresh_lo, tr, no_hook, no_hook);
+                compute_tile(fresh_lo, tr, no_hook, no_hook, true);
             } else {
                 for (int t = fresh_lo + kTileTokens * new_i0; t < e; t += kTileTokens * W) {
-                    TileRegs<KV8> tr;
+                    TileRegs<kF8> tr;
                     load_new_tile(t, tr);
-                    compute_tile(t, tr, no_hook, no_hook);
+                    compute_tile(t, tr, no_hook, no_hook, true);
                 }
             }
         }
@@ -545,6 +608,10 @@ struct MfmaEngine {
         for (int qt = 0; qt < NQT; ++qt) {
             lex[qt] += shfl_xor_f(lex[qt], 16);
             lex[qt] += shfl_xor_f(lex[qt], 32);
+            if constexpr (kBS) {
+                lw[qt] += shfl_xor_f(lw[qt], 16);
+                lw[qt] += shfl_xor_f(lw[qt], 32);
+            }
         }
 
         // ---- every wavefront stores its state; then all threads combine
@@ -561,7 +628,8 @@ struct MfmaEngine {
                     *reinterpret_cast<f32x4_t*>(slot + qi * kOStride + 16 * nt + 4 * G) = acc[qt][nt];
                 if (G == 0) {
                     slot[16 * NQT * kOStride + qi] = mrun[qt];
-                    slot[16 * NQT * kOStride + 16 * NQT + qi] = lacc[qt][0];
+                    if constexpr (kBS) slot[16 * NQT * kOStride + 16 * NQT + qi] = lw[qt];
+                    else slot[16 * NQT * kOStride + 16 * NQT + qi] = lacc[qt][0];
                     slot[16 * NQT * kOStride + 32 * NQT + qi] = lex[qt];
                 }
             }
@@ -603,12 +671,13 @@ struct MfmaEngine {
 // Resident wavefronts per SIMD the register allocator is asked to allow: two
 // (256 registers; it fits them without spills: the 16-query bf16 variant
 // with two sets of tile registers, the 32-query variant with one), three for
-// the single-buffered 4-wavefront FP8 variant (168 registers; measured about
-// 5 % faster on paged caches than two).
-template <int NQT, int W, bool KV8>
-struct MfmaOccupancy { static constexpr int kWavesPerEu = (KV8 && W == 4 && NQT == 1) ? 3 : 2; };
+// the single-buffered 4-wavefront FP8 variant with per-head scales (168
+// registers; measured about 5 % faster on paged caches than two; the
+// per-block-scale variants need the registers of two).
+template <int NQT, int W, int KV8>
+struct MfmaOccupancy { static constexpr int kWavesPerEu = (KV8 == 1 && W == 4 && NQT == 1) ? 3 : 2; };
 
-template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
+template <int NQT, bool PAGED, int W, bool GEN, int KV8>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, KV8>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
@@ -646,7 +715,7 @@ decode_mfma_chunked(DecodeArgs a) {
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c, row0), row0);
 }
 
-template <int NQT, bool PAGED, int W, bool GEN, bool KV8>
+template <int NQT, bool PAGED, int W, bool GEN, int KV8>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, KV8>::kWavesPerEu)))
 decode_mfma_stream(DecodeArgs a) {
@@ -660,46 +729,46 @@ decode_mfma_stream(DecodeArgs a) {
     });
 }
 
-template <int NQT, bool PG, int WV>
-static const void* mfma_pick(bool stream, bool gen, bool kv8) {
-    if (kv8) {
-        if (stream)
-            return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true, true>
-                       : (const void*)decode_mfma_stream<NQT, PG, WV, false, true>;
-        return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true, true>
-                   : (const void*)decode_mfma_chunked<NQT, PG, WV, false, true>;
-    }
+template <int NQT, bool PG, int WV, int KV>
+static const void* mfma_pick_kv(bool stream, bool gen) {
     if (stream)
-        return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true, false>
-                   : (const void*)decode_mfma_stream<NQT, PG, WV, false, false>;
-    return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true, false>
-               : (const void*)decode_mfma_chunked<NQT, PG, WV, false, false>;
+        return gen ? (const void*)decode_mfma_stream<NQT, PG, WV, true, KV>
+                   : (const void*)decode_mfma_stream<NQT, PG, WV, false, KV>;
+    return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true, KV>
+               : (const void*)decode_mfma_chunked<NQT, PG, WV, false, KV>;
+}
+
+// 8-wavefront kernels: chunked grids of contiguous caches only.
+template <int NQT, int WV, int KV>
+static const void* mfma_chunked_kv(bool gen) {
+    return gen ? (const void*)decode_mfma_chunked<NQT, false, WV, true, KV>
+               : (const void*)decode_mfma_chunked<NQT, false, WV, false, KV>;
+}
+
+template <int NQT, bool PG, int WV>
+static const void* mfma_pick(bool stream, bool gen, int kv8) {
+    if (kv8 == 2) {  // per-block scales: paged pools only
+        if constexpr (PG) return mfma_pick_kv<NQT, PG, WV, 2>(stream, gen);
+        else return nullptr;
+    }
+    return kv8 ? mfma_pick_kv<NQT, PG, WV, 1>(stream, gen) : mfma_pick_kv<NQT, PG, WV, 0>(stream, gen);
 }
 
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
-// general features, FP8 cache); nullptr when that combination is not built.
+// general features, cache kind: 0 bf16, 1 FP8 with per-head scales, 2 FP8
+// with per-block scales); nullptr when that combination is not built.
 // Every (m, layout, mode) has a 4-wavefront kernel; a contiguous cache also
 // has 8-wavefront chunked kernels, for whole-unit work-groups and for chunk
 // grids smaller than the device's slots.
-const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
+const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8) {
     const bool two = m > 16;
     if (waves == 4) {
         if (two) return paged ? mfma_pick<2, true, 4>(stream, gen, kv8) : mfma_pick<2, false, 4>(stream, gen, kv8);
         return paged ? mfma_pick<1, true, 4>(stream, gen, kv8) : mfma_pick<1, false, 4>(stream, gen, kv8);
     }
-    if (waves == 8 && !paged && !stream) {
-        if (two) {
-            if (kv8)
-                return gen ? (const void*)decode_mfma_chunked<2, false, 8, true, true>
-                           : (const void*)decode_mfma_chunked<2, false, 8, false, true>;
-            return gen ? (const void*)decode_mfma_chunked<2, false, 8, true, false>
-                       : (const void*)decode_mfma_chunked<2, false, 8, false, false>;
-        }
-        if (kv8)
-            return gen ? (const void*)decode_mfma_chunked<1, false, 8, true, true>
-                       : (const void*)decode_mfma_chunked<1, false, 8, false, true>;
-        return gen ? (const void*)decode_mfma_chunked<1, false, 8, true, false>
-                   : (const void*)decode_mfma_chunked<1, false, 8, false, false>;
+    if (waves == 8 && !paged && !stream && kv8 != 2) {
+        if (two) return kv8 ? mfma_chunked_kv<2, 8, 1>(gen) : mfma_chunked_kv<2, 8, 0>(gen);
+        return kv8 ? mfma_chunked_kv<1, 8, 1>(gen) : mfma_chunked_kv<1, 8, 0>(gen);
     }
     return nullptr;
 }
@@ -709,7 +778,7 @@ hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s) {
     if (a.slices < 1 || (a.m > 32 * a.slices) || (a.slices > 1 && (a.stream || a.m <= 32)))
         return hipErrorInvalidValue;
     const void* fn = mfma_kernel(min(a.m, 32), a.block_table != nullptr, a.stream != 0, a.waves,
-                                 general_features(a), a.kv8 != 0);
+                                 general_features(a), kv_mode(a));
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
                                : dim3((unsigned)a.num_chunks, (unsigned)(a.g * a.slices),

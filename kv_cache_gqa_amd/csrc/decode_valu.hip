@@ -45,12 +45,18 @@ struct ValuTile<true> {
     uint2 v[8];
 };
 
-// KV8: the cache holds FP8 E4M3 codes with a float32 scale per KV head,
-// folded into the score scale (K) and the output (V).
-template <int M, bool PAGED, int W, bool GEN, bool KV8>
+// KV8: 0 = bf16 cache; 1 = FP8 E4M3 codes with a float32 scale per KV
+// head, folded into the score scale (K) and the output (V); 2 = FP8 codes
+// with a scale per (physical block, KV head) of a paged pool, applied per
+// position to the score (K) and to the weight of its V row.
+template <int M, bool PAGED, int W, bool GEN, int KV8>
 struct ValuEngine {
+    static constexpr bool kF8 = KV8 != 0;
+    static constexpr bool kBS = KV8 == 2;  // per-block scales
+    static_assert(!kBS || PAGED, "per-block scales need a paged pool");
     struct Shared {
         int tbl[PAGED ? kMaxTableSlice : 1];
+        float bsc[kBS ? 2 * kMaxTableSlice : 1];  // per block: K scale, then V scale
         float red_m[W][M];
         float red_l[W][M];
         float red_o[W][M][kD];
@@ -85,8 +91,8 @@ struct ValuEngine {
         }
         const long bj_base = ((long)b * a.g + j) * a.t_cap;
         long cbase = bj_base;  // row of position 0 in the current window (ring: shifted)
-        const float k_sc = KV8 ? a.k_scale[j] : 1.0f;  // FP8 head scales
-        const float v_sc = KV8 ? a.v_scale[j] : 1.0f;
+        const float k_sc = KV8 == 1 ? a.k_scale[j] : 1.0f;  // FP8 head scales
+        const float v_sc = KV8 == 1 ? a.v_scale[j] : 1.0f;
         const float sl2 = a.scale_log2e * k_sc;
         const int* tbl = sh.tbl;
         int blk0 = 0;
@@ -126,12 +132,14 @@ struct ValuEngine {
         constexpr bool kNewPair = !GEN;
         const bool new_wave = has_new && wave == ((fresh_lo - s) / kTileTokens) % W;
         const uint2 new_pair = kNewPair && new_wave ? new_row_pair_d128(a, b, j, lane) : make_uint2(0u, 0u);
+        // scale index of the one new token (FP8 single-token calls)
+        const long new_sidx = kBS && kNewPair && has_new ? fp8_scale_index(a, b, j, raw) : (long)j;
         const long bj = (long)b * a.g + j;
         const uint16_t* KN = has_new ? (const uint16_t*)a.k_new + bj * a.n * kD : K;
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
 
         // Positions clamped to the window's last one (in bounds past the end).
-        auto load_tile = [&](int t0, ValuTile<KV8>& tr) {
+        auto load_tile = [&](int t0, ValuTile<kF8>& tr) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const long row = kv_row(min(t0 + 4 * u + tsub, w1 - 1));
@@ -148,10 +156,10 @@ struct ValuEngine {
         // of the unit's k_new / v_new rows; positions clamp to w1 - 1.  With
         // one new token every position of the tile is that token: its rows
         // (FP8: their codes) go to this wavefront's LDS area first.
-        auto load_new_tile = [&](int t0, ValuTile<KV8>& tr) {
+        auto load_new_tile = [&](int t0, ValuTile<kF8>& tr) {
             if constexpr (KV8 && kNewPair) {
                 unsigned char* codes = sh.nrow[wave];
-                new_row_codes_fp8_d128(a, j, lane, new_pair, codes);
+                new_row_codes_fp8_d128(a, new_sidx, lane, new_pair, codes);
                 wave_lds_sync();
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -171,12 +179,12 @@ struct ValuEngine {
             } else if constexpr (KV8) {
                 // several new tokens over an FP8 cache: their bf16 rows,
                 // quantised here to the codes the cache receives
-                const float ks_ = a.k_scale[j], vs_ = a.v_scale[j];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
-                    tr.k[u] = e4m3_encode8(ld16(KN + r * kD + 8 * ds), ks_);
-                    tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * ds), vs_);
+                    const long si = kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : (long)j;
+                    tr.k[u] = e4m3_encode8(ld16(KN + r * kD + 8 * ds), a.k_scale[si]);
+                    tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * ds), a.v_scale[si]);
                 }
             } else {
 #pragma unroll
@@ -191,7 +199,28 @@ struct ValuEngine {
             if constexpr (KV8) return e4m3x8_to_bf16(x);
             else return x;
         };
-        auto compute_tile = [&](int t0, const ValuTile<KV8>& tr) {
+        // fresh: a tile of appended tokens (their scales are looked up, not
+        // in the table slice)
+        auto compute_tile = [&](int t0, const ValuTile<kF8>& tr, bool fresh) {
+            // per-block scales of the lane's eight positions
+            float sk[8], vf[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                sk[u] = sl2;
+                vf[u] = 1.0f;
+                if constexpr (kBS) {
+                    const int p = min(t0 + 4 * u + tsub, w1 - 1);
+                    if (fresh) {
+                        const long si = fp8_scale_index(a, b, j, p);
+                        sk[u] = sl2 * a.k_scale[si];
+                        vf[u] = a.v_scale[si];
+                    } else {
+                        const int bi = (p >> a.log2_bs) - blk0;
+                        sk[u] = sl2 * sh.bsc[bi];
+                        vf[u] = sh.bsc[kMaxTableSlice + bi];
+                    }
+                }
+            }
             float sc[M][8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -203,7 +232,7 @@ struct ValuEngine {
                     dot = dot2_bf16(qp[r][1], kb.y, dot);
                     dot = dot2_bf16(qp[r][2], kb.z, dot);
                     dot = dot2_bf16(qp[r][3], kb.w, dot);
-                    dot = row16_sum(dot) * sl2;
+                    dot = row16_sum(dot) * sk[u];
                     const bool vis = GEN ? (p < w1 && (unsigned)(lim[r] - 1 - p) < wlen) : p < w1;
                     sc[r][u] = vis ? dot : kNegInf;
                 }
@@ -231,12 +260,13 @@ struct ValuEngine {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint4 vb = as_bf16(tr.v[u]);
-                const float vf[8] = {bf16_lo(vb.x), bf16_hi(vb.x), bf16_lo(vb.y), bf16_hi(vb.y),
-                                     bf16_lo(vb.z), bf16_hi(vb.z), bf16_lo(vb.w), bf16_hi(vb.w)};
+                const float vfl[8] = {bf16_lo(vb.x), bf16_hi(vb.x), bf16_lo(vb.y), bf16_hi(vb.y),
+                                      bf16_lo(vb.z), bf16_hi(vb.z), bf16_lo(vb.w), bf16_hi(vb.w)};
 #pragma unroll
                 for (int r = 0; r < M; ++r) {
+                    const float w = kBS ? pr[r][u] * vf[u] : pr[r][u];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) acc[r][k] += pr[r][u] * vf[k];
+                    for (int k = 0; k < 8; ++k) acc[r][k] += w * vfl[k];
                 }
             }
         };
@@ -254,23 +284,28 @@ struct ValuEngine {
                 blk0 = w0 >> a.log2_bs;
                 const int nblk = ((w1 - 1) >> a.log2_bs) - blk0 + 1;
                 for (int t = tid; t < nblk; t += 64 * W) {
-                    const int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
-                    sh.tbl[t] = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                    int ph = a.block_table[(long)b * a.max_blocks + blk0 + t];
+                    ph = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+                    sh.tbl[t] = ph;
+                    if constexpr (kBS) {
+                        sh.bsc[t] = a.k_scale[(long)ph * a.g + j];
+                        sh.bsc[kMaxTableSlice + t] = a.v_scale[(long)ph * a.g + j];
+                    }
                 }
                 __syncthreads();
             }
             const int stride = W * kTileTokens;
             int t0 = w0 + wave * kTileTokens;
-            ValuTile<KV8> tA, tB;
+            ValuTile<kF8> tA, tB;
             load_tile(t0, tA);
             for (;;) {
                 if (t0 >= w1) break;
                 load_tile(t0 + stride, tB);
-                compute_tile(t0, tA);
+                compute_tile(t0, tA, false);
                 t0 += stride;
                 if (t0 >= w1) break;
                 load_tile(t0 + stride, tA);
-                compute_tile(t0, tB);
+                compute_tile(t0, tB, false);
                 t0 += stride;
             }
             if (PAGED) __syncthreads();  // the next window rewrites the table slice
@@ -279,9 +314,9 @@ struct ValuEngine {
         // last, as one tile by the wavefront next in turn.
         if (new_wave) {
             w1 = e;
-            ValuTile<KV8> tr;
+            ValuTile<kF8> tr;
             load_new_tile(fresh_lo, tr);
-            compute_tile(fresh_lo, tr);
+            compute_tile(fresh_lo, tr, true);
         }
 
         // Merge the four rows of 16 lanes (positions interleaved by lane/16).
@@ -342,7 +377,7 @@ struct ValuEngine {
 
 }  // namespace
 
-template <int M, bool PAGED, int W, bool GEN, bool KV8>
+template <int M, bool PAGED, int W, bool GEN, int KV8>
 __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
     using E = ValuEngine<M, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
@@ -360,7 +395,7 @@ __global__ void __launch_bounds__(64 * W) decode_valu_chunked(DecodeArgs a) {
     E::segment(a, sh, b, j, p0, p1, chunk_dst(a, b, j, c));
 }
 
-template <int M, bool PAGED, int W, bool GEN, bool KV8>
+template <int M, bool PAGED, int W, bool GEN, int KV8>
 __global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
     using E = ValuEngine<M, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
@@ -372,20 +407,22 @@ __global__ void __launch_bounds__(64 * W) decode_valu_stream(DecodeArgs a) {
     });
 }
 
-template <int M, bool PG>
-static const void* valu_pick(bool stream, bool gen, bool kv8) {
-    if (kv8) {
-        if (stream)
-            return gen ? (const void*)decode_valu_stream<M, PG, 4, true, true>
-                       : (const void*)decode_valu_stream<M, PG, 4, false, true>;
-        return gen ? (const void*)decode_valu_chunked<M, PG, 4, true, true>
-                   : (const void*)decode_valu_chunked<M, PG, 4, false, true>;
-    }
+template <int M, bool PG, int KV>
+static const void* valu_pick_kv(bool stream, bool gen) {
     if (stream)
-        return gen ? (const void*)decode_valu_stream<M, PG, 4, true, false>
-                   : (const void*)decode_valu_stream<M, PG, 4, false, false>;
-    return gen ? (const void*)decode_valu_chunked<M, PG, 4, true, false>
-               : (const void*)decode_valu_chunked<M, PG, 4, false, false>;
+        return gen ? (const void*)decode_valu_stream<M, PG, 4, true, KV>
+                   : (const void*)decode_valu_stream<M, PG, 4, false, KV>;
+    return gen ? (const void*)decode_valu_chunked<M, PG, 4, true, KV>
+               : (const void*)decode_valu_chunked<M, PG, 4, false, KV>;
+}
+
+template <int M, bool PG>
+static const void* valu_pick(bool stream, bool gen, int kv8) {
+    if (kv8 == 2) {  // per-block scales: paged pools only
+        if constexpr (PG) return valu_pick_kv<M, PG, 2>(stream, gen);
+        else return nullptr;
+    }
+    return kv8 ? valu_pick_kv<M, PG, 1>(stream, gen) : valu_pick_kv<M, PG, 0>(stream, gen);
 }
 
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
@@ -394,7 +431,7 @@ static const void* valu_pick(bool stream, bool gen, bool kv8) {
 // measured slower than split chunks plus a merge for these kernels (8, 12
 // and 16 wavefronts, m = 1; 12 keeps the occupancy of three chunks but not
 // their balance).
-const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8) {
+const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8) {
     if (waves != 4) return nullptr;
     switch (m) {
         case 1: return paged ? valu_pick<1, true>(stream, gen, kv8) : valu_pick<1, false>(stream, gen, kv8);
@@ -406,7 +443,7 @@ const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, boo
 
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s) {
     const void* fn = valu_kernel(a.m, a.block_table != nullptr, a.stream != 0, a.waves,
-                                 general_features(a), a.kv8 != 0);
+                                 general_features(a), kv_mode(a));
     if (fn == nullptr) return hipErrorInvalidValue;
     const dim3 grid = a.stream ? dim3((unsigned)a.num_wgs)
                                : dim3((unsigned)a.num_chunks, (unsigned)a.g, (unsigned)a.B);

@@ -198,8 +198,9 @@ static long device_slots(const void* fn, int waves) {
     return (long)cus * per_cu;
 }
 
+// kv8: the cache kind (kv_mode): 0 bf16, 1 FP8 per-head scales, 2 per-block
 static const void* kernel_for(KernelKind kind, int m, bool paged, bool stream, int waves, bool gen,
-                              bool kv8) {
+                              int kv8) {
     return kind == kMfma ? mfma_kernel(m, paged, stream, waves, gen, kv8)
                          : valu_kernel(m, paged, stream, waves, gen, kv8);
 }
@@ -225,7 +226,7 @@ struct AutoShape {
 };
 
 static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, bool paged,
-                            bool gen, bool kv8) {
+                            bool gen, int kv8) {
     const long units = (long)B * g;
     const void* f4 = kernel_for(kind, m, paged, false, 4, gen, kv8);
     const long slots4 = device_slots(f4, 4);
@@ -234,7 +235,7 @@ static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, b
     const void* fn = kernel_for(kind, m, paged, false, wv, gen, kv8);
     const long slots = fn != nullptr ? device_slots(fn, wv) : 0;
     // resident tiles in flight: the 8-wavefront FP8 kernel loads two per step
-    const long inflight = slots * wv * (kind == kMfma && kv8 ? 2 : 1);
+    const long inflight = slots * wv * (kind == kMfma && kv8 != 0 ? 2 : 1);
     if (slots > 0 && units >= slots && inflight >= slots4 * 4 && fill(units, slots) * 8.0 >= 7.0)
         return AutoShape{wv, 1};
     return split;
@@ -303,14 +304,14 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
         return;
     }
     if (sc.stream) {
-        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4, general_features(a), a.kv8 != 0), 4);
+        long P = device_slots(kernel_for(sc.kind, a.m, paged, true, 4, general_features(a), kv_mode(a)), 4);
         // No more work-groups than 256-position pieces of the largest possible batch.
         const long pieces = ((long)a.B * a.g * max_len + 255) / 256;
         if (P > pieces) P = pieces;
         a.num_wgs = (int)(P < 1 ? 1 : P);
     } else if (sc.auto_chunks) {
         const AutoShape sh = auto_shape(sc.kind, a.m < 32 ? a.m : 32, a.B * a.slices, a.g, max_len,
-                                        paged, general_features(a), a.kv8 != 0);
+                                        paged, general_features(a), kv_mode(a));
         a.waves = sh.waves;
         // One chunk per unit may exceed kMaxChunk: the engines walk a chunk in
         // windows of at most kMaxChunk positions.
@@ -325,7 +326,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
         // wavefronts that way (with one tile, 4-wavefront work-groups keep
         // the tiling of the paged kernels).
         const void* f8 = kernel_for(sc.kind, a.m < 32 ? a.m : 32, paged, false, 8,
-                                    general_features(a), a.kv8 != 0);
+                                    general_features(a), kv_mode(a));
         const long wgs = (long)a.num_chunks * a.g * a.slices * a.B;
         if (f8 != nullptr && wgs <= device_slots(f8, 8)) a.waves = 8;
     }
@@ -543,7 +544,7 @@ static int decode_paged(const void* q, const void* k_new, const void* v_new, con
                         int g, int d, int n, int window, float scale, int dtype, int num_splits,
                         void* workspace, size_t workspace_bytes, float* out, float* lse,
                         hipStream_t stream, const float* k_scale = nullptr,
-                        const float* v_scale = nullptr) {
+                        const float* v_scale = nullptr, int block_scales = 0) {
     int st = check_common(q, k_pool, v_pool, seq_lens, B, h, g, d, scale, dtype, num_splits,
                           out, lse);
     if (st != KVC_OK) return st;
@@ -564,6 +565,7 @@ static int decode_paged(const void* q, const void* k_new, const void* v_new, con
     a.t_cap = 0; a.cap_len = (int)cap;
     a.window = window; a.ring = 0;
     a.kv8 = k_scale != nullptr ? 1 : 0; a.k_scale = k_scale; a.v_scale = v_scale;
+    a.block_scales = block_scales;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.out = out; a.lse = lse;
     a.len_add = k_new != nullptr ? n : 0;
@@ -789,7 +791,7 @@ int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_
         !al4(v_scale) || !al4(block_table) || !al4(seq_lens_before))
         return KVC_ERR_INVALID;
     if (launch_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
-                          max_blocks, block_size, seq_lens_before, B, g, 1, d, capacity, 0,
+                          max_blocks, block_size, seq_lens_before, B, g, 1, d, capacity, 0, 0,
                           stream) != hipSuccess)
         return KVC_ERR_HIP;
     return KVC_OK;
@@ -949,6 +951,43 @@ int kvc_append_decode_attention_fp8_multi_paged(
         q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks, block_size,
         num_blocks, seq_lens_before, B, h, g, d, n, 0, scale, num_splits, workspace,
         workspace_bytes, out, lse, stream);
+}
+
+// FP8 pools with a scale per (physical block, KV head).
+int kvc_append_fp8_paged_block_scaled(const void* k_new, const void* v_new, void* k_pool,
+                                      void* v_pool, const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, int max_blocks, int block_size,
+                                      int num_blocks, const int32_t* seq_lens_before, int B, int g,
+                                      int d, int n, hipStream_t stream) {
+    if (B < 0 || g <= 0 || d <= 0 || n <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
+        block_size <= 0)
+        return KVC_ERR_INVALID;
+    if (B == 0) return KVC_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_table ||
+        !seq_lens_before)
+        return KVC_ERR_INVALID;
+    if (!al16(k_new) || !al16(v_new) || !al16(k_pool) || !al16(v_pool) || !al4(k_scale) ||
+        !al4(v_scale) || !al4(block_table) || !al4(seq_lens_before))
+        return KVC_ERR_INVALID;
+    if (launch_append_fp8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks,
+                          block_size, seq_lens_before, B, g, n, d, num_blocks, 0, 1, stream) !=
+        hipSuccess)
+        return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
+int kvc_decode_attention_fp8_paged_block_scaled(
+    const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const float* k_scale, const float* v_scale, const int32_t* block_table, int max_blocks,
+    int block_size, int num_blocks, const int32_t* seq_lens, int B, int h, int g, int d, int n,
+    int window, float scale, int num_splits, void* workspace, size_t workspace_bytes, float* out,
+    float* lse, hipStream_t stream) {
+    if (B > 0 && (!k_scale || !v_scale)) return KVC_ERR_INVALID;
+    if ((k_new == nullptr) != (v_new == nullptr)) return KVC_ERR_INVALID;
+    return decode_paged(q, B > 0 ? k_new : nullptr, v_new, k_pool, v_pool, block_table, max_blocks,
+                        block_size, num_blocks, seq_lens, B, h, g, d, n, window, scale, KVC_BF16,
+                        num_splits, workspace, workspace_bytes, out, lse, stream, k_scale, v_scale,
+                        1);
 }
 
 }  // extern "C"

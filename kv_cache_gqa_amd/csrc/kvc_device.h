@@ -318,16 +318,18 @@ __device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int
         const bool is_v = (idx & 128) != 0;
         const int e = idx & 127;
         long row;
+        long sidx = j;
         if (a.block_table != nullptr) {
             const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
             if (phys < 0 || phys >= a.num_blocks) continue;
             row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+            if (a.block_scales) sidx = (long)phys * a.g + j;
         } else {
             row = unit * a.t_cap + cache_slot(a, p);
         }
         const uint16_t x = reinterpret_cast<const uint16_t*>(is_v ? a.v_new : a.k_new)
                                [(unit * a.n + (p - raw)) * 128 + e];
-        const float sc = is_v ? a.v_scale[j] : a.k_scale[j];
+        const float sc = is_v ? a.v_scale[sidx] : a.k_scale[sidx];
         unsigned char* dst = reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? a.v : a.k));
         dst[row * 128 + e] = (unsigned char)e4m3_encode(__uint_as_float((uint32_t)x << 16) / sc);
     }
@@ -341,16 +343,27 @@ __device__ __forceinline__ uint2 new_row_pair_d128(const DecodeArgs& a, int b, i
                       reinterpret_cast<const uint32_t*>(a.v_new)[row * 64 + lane]);
 }
 
+// Index of the FP8 scale of position p of unit (b, j): the KV head's, or
+// with per-block scales that of its (block, KV head), the block id clamped
+// into the pool as the kernels' reads clamp it.
+__device__ __forceinline__ long fp8_scale_index(const DecodeArgs& a, int b, int j, int p) {
+    if (!a.block_scales) return j;
+    int ph = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+    ph = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
+    return (long)ph * a.g + j;
+}
+
 // FP8 cache, d = 128, one new token per sequence: the codes of the new K
-// row (bytes 0..127 of `codes`) and V row (128..255) of KV head j, written
+// row (bytes 0..127 of `codes`) and V row (128..255) for the scales at
+// index sidx (fp8_scale_index of the new position), written
 // to the calling wavefront's LDS area `codes` by its 64 lanes from their
 // pairs (new_row_pair_d128), with the same quotient and encoder as
 // store_new_rows_fp8_d128, so they equal what that call stores.  The caller
 // syncs the wavefront (wave_lds_sync) before reading them.
-__device__ __forceinline__ void new_row_codes_fp8_d128(const DecodeArgs& a, int j, int lane, uint2 pair,
-                                                       unsigned char* codes) {
+__device__ __forceinline__ void new_row_codes_fp8_d128(const DecodeArgs& a, long sidx, int lane,
+                                                       uint2 pair, unsigned char* codes) {
     const uint32_t kx = pair.x, vx = pair.y;
-    const float ks = a.k_scale[j], vs = a.v_scale[j];
+    const float ks = a.k_scale[sidx], vs = a.v_scale[sidx];
     const uint32_t kc = e4m3_encode(__uint_as_float(kx << 16) / ks) |
                         (e4m3_encode(__uint_as_float(kx & 0xFFFF0000u) / ks) << 8);
     const uint32_t vc = e4m3_encode(__uint_as_float(vx << 16) / vs) |

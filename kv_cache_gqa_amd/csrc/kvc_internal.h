@@ -81,8 +81,11 @@ struct DecodeArgs {
     // slot p mod t_cap (positions are not clamped to the capacity).
     int window;
     int ring;
-    // FP8 E4M3 cache (q, k_new, v_new stay bf16): per-KV-head float32 scales.
+    // FP8 E4M3 cache (q, k_new, v_new stay bf16): float32 scales, one per
+    // KV head ([g]), or with block_scales (paged pools only) one per
+    // physical block and KV head ([num_blocks, g]).
     int kv8;
+    int block_scales;
     const float* k_scale;
     const float* v_scale;
     // Chunked mode (C > 1): partial O [B,h,C,d], partial base-2 lse [B,h,C].
@@ -103,14 +106,19 @@ hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
 // Kernel function for (m, layout, split mode, wavefronts per work-group,
 // general features, FP8 cache), for launches and occupancy queries; nullptr
 // when that combination is not built.  MFMA: waves in {4, 8}; VALU: 4.
-const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8);
-const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, bool kv8);
+// kv8: 0 = bf16 cache, 1 = FP8 with per-KV-head scales, 2 = FP8 with
+// per-block scales (paged only).
+const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8);
+const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8);
 // Multi-row kernel for (16-row query tiles per wavefront, wavefronts per
 // work-group, layout); nullptr when not built.
 const void* prefill_kernel(int nqt, int waves, bool paged);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }
+// Cache kind of a call for kernel selection: 0 bf16, 1 FP8 with per-KV-head
+// scales, 2 FP8 with per-block scales.
+inline int kv_mode(const DecodeArgs& a) { return a.kv8 ? (a.block_scales ? 2 : 1) : 0; }
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs,
                               int num_blocks, long block_bytes, hipStream_t s);
 hipError_t launch_fork_tables(const int32_t* tables, const int32_t* lens, int B_src, int max_blocks,
@@ -123,7 +131,7 @@ hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache
                              const float* k_scale, const float* v_scale,
                              const int32_t* block_table, int max_blocks, int block_size,
                              const int32_t* seq_lens_before, int B, int g, int n, int d,
-                             int capacity, int ring, hipStream_t s);
+                             int capacity, int ring, int block_scales, hipStream_t s);
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int32_t* block_table, int max_blocks, int block_size,
                          const int32_t* seq_lens_before, int B, int g, int n, int d, int capacity,

@@ -542,3 +542,58 @@ def decode_fp8_window(q, k_codes, v_codes, k_scale, v_scale, seq_lens_before, sc
     v = dequantize_fp8(v_codes, v_scale, 1)
     return decode_window(widen(q), k, v, seq_lens_before, scale, window, ring=ring,
                          block_table=block_table, block_size=block_size, nthreads=nthreads)
+
+
+def dequantize_fp8_blocks(codes, scale):
+    """float64 values of a paged pool of E4M3 codes [NB, g, bs, d] with one
+    float32 scale per (physical block, KV head), ``scale`` [NB, g]: code
+    value times its block's scale (exact in float64)."""
+    x = e4m3_values()[np.asarray(codes, dtype=np.uint8)]
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return x * sc[:, :, None, None]
+
+
+def append_fp8_block_scaled(k_new, v_new, k_codes, v_codes, k_scale, v_scale, seq_lens_before,
+                            block_table):
+    """Quantise n new tokens per sequence (k_new, v_new [B,g,n,d] bf16) into
+    paged pools [NB,g,bs,d] with per-(block, KV head) scales [NB, g]: token t
+    of sequence b goes to position seq_lens_before[b] + t as the code of the
+    float32 quotient x / scale[blk, j] of its target block.  Positions whose
+    table entry is not a block of the pool are skipped.  Returns new pools."""
+    kc = np.array(k_codes, dtype=np.uint8, copy=True)
+    vc = np.array(v_codes, dtype=np.uint8, copy=True)
+    ks = np.asarray(k_scale, dtype=np.float32)
+    vs = np.asarray(v_scale, dtype=np.float32)
+    before = _i32(seq_lens_before)
+    bt = _i32(block_table)
+    nb, g, bs, _ = kc.shape
+
+    def floats(x):
+        a, code = _raw(x)
+        return (a.astype(np.uint32) << 16).view(np.float32) if code == BF16 else a
+    kf, vf = floats(k_new), floats(v_new)
+    B, _, n, _ = kf.shape
+    for b in range(B):
+        for t in range(n):
+            p = int(before[b]) + t
+            if p // bs >= bt.shape[1]:
+                continue
+            blk = int(bt[b, p // bs])
+            if not 0 <= blk < nb:
+                continue
+            for j in range(g):
+                kc[blk, j, p % bs] = e4m3_encode((kf[b, j, t] / ks[blk, j]).astype(np.float32))
+                vc[blk, j, p % bs] = e4m3_encode((vf[b, j, t] / vs[blk, j]).astype(np.float32))
+    return kc, vc
+
+
+def decode_fp8_block_scaled(q, k_codes, v_codes, k_scale, v_scale, seq_lens_before, scale,
+                            block_table, block_size, window=0, nthreads=0):
+    """n query tokens per sequence (q [B,h,n,d] bf16) over paged FP8 pools
+    with per-(block, KV head) scales that already hold them: dequantise
+    (``dequantize_fp8_blocks``), then ``decode_window`` over the values.
+    Returns out [B,h,n,d], lse [B,h,n]."""
+    k = dequantize_fp8_blocks(k_codes, k_scale)
+    v = dequantize_fp8_blocks(v_codes, v_scale)
+    return decode_window(widen(q), k, v, seq_lens_before, scale, window, block_table=block_table,
+                         block_size=block_size, nthreads=nthreads)

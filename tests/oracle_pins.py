@@ -670,6 +670,61 @@ def pin_fp8_multi_and_window():
         lens = lens + 3
 
 
+def pin_fp8_block_scales():
+    """Paged FP8 pools with a scale per (block, KV head): the appended codes
+    are torch's float8_e4m3fn conversion of x / (its block's scale); with
+    every block of a head at the head's scale the result equals the
+    per-head reference exactly; with random block scales every row equals
+    torch SDPA in float64 over torch's per-block dequantisation."""
+    gen = torch.Generator().manual_seed(45)
+    B, h, g, d, bs, n = 3, 4, 2, 16, 4, 3
+    before = torch.tensor([0, 5, 10], dtype=torch.int32)
+    table, nb = W.make_block_table(before + n, bs, perm_seed=46, extra_blocks=1)
+    kc = oracle.quantize_fp8(torch.randn(nb, g, bs, d, generator=gen) * 2, np.ones(g, np.float32), 1)
+    vc = kc.copy()[::-1].copy()
+    kb = (torch.rand(nb, g, generator=gen) * 0.5 + 0.02).numpy().astype(np.float32)
+    vb = (torch.rand(nb, g, generator=gen) * 0.5 + 0.02).numpy().astype(np.float32)
+    kn = (torch.randn(B, g, n, d, generator=gen) * 0.3).to(torch.bfloat16)
+    vn = (torch.randn(B, g, n, d, generator=gen) * 0.3).to(torch.bfloat16)
+    k2, v2 = oracle.append_fp8_block_scaled(kn, vn, kc, vc, kb, vb, before, table)
+    for b in range(B):
+        for t in range(n):
+            p = int(before[b]) + t
+            blk = int(table[b, p // bs])
+            want = (kn[b, :, t].float() / torch.from_numpy(kb[blk]).view(g, 1)).to(
+                torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(k2[blk, :, p % bs], want)
+    q = torch.randn(B, h, n, d, generator=gen).to(torch.bfloat16)
+    sc = 0.35
+    # all blocks of head j at that head's scale: the per-head reference
+    hk = np.array([0.07, 0.4], np.float32)
+    hv = np.array([0.3, 0.05], np.float32)
+    o1, l1 = oracle.decode_fp8_block_scaled(q, k2, v2, np.tile(hk, (nb, 1)), np.tile(hv, (nb, 1)),
+                                            before, sc, table, bs)
+    o2, l2 = oracle.decode_fp8_window(q, k2, v2, hk, hv, before, sc, 0, block_table=table,
+                                      block_size=bs)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # random block scales against torch's per-block dequantisation
+    o, l = oracle.decode_fp8_block_scaled(q, k2, v2, kb, vb, before, sc, table, bs)
+    kd = torch.from_numpy(k2).view(torch.float8_e4m3fn).double() * \
+        torch.from_numpy(kb).double().view(nb, g, 1, 1)
+    vd = torch.from_numpy(v2).view(torch.float8_e4m3fn).double() * \
+        torch.from_numpy(vb).double().view(nb, g, 1, 1)
+    qf = q.double()
+    for b in range(B):
+        for t in range(n):
+            x = int(before[b]) + t
+            rows = [int(table[b, p // bs]) for p in range(x + 1)]
+            for i in range(h):
+                j = i * g // h
+                kk = torch.stack([kd[rows[p], j, p % bs] for p in range(x + 1)])
+                vv = torch.stack([vd[rows[p], j, p % bs] for p in range(x + 1)])
+                s_ = (kk @ qf[b, i, t]) * float(np.float32(sc))
+                ro = torch.softmax(s_, 0) @ vv
+                assert torch.max(torch.abs(torch.from_numpy(o[b, i, t]) - ro)) < 1e-12
+                assert abs(l[b, i, t] - float(torch.logsumexp(s_, 0))) < 1e-12
+
+
 ALL_PINS = [
     pin_d1_worked_example,
     pin_sdpa_crosscheck,
@@ -693,4 +748,5 @@ ALL_PINS = [
     pin_fp8_format,
     pin_fp8_dequantised_attention,
     pin_fp8_multi_and_window,
+    pin_fp8_block_scales,
 ]

@@ -352,7 +352,7 @@ def test_public_calls_carry_the_device_guard():
     for name in ["append", "decode", "decode_paged", "append_decode", "decode_multi",
                  "append_decode_multi", "decode_window", "copy_blocks", "fork_block_tables",
                  "gather_cache", "append_fp8", "decode_fp8", "decode_fp8_window",
-                 "append_decode_noalloc"]:
+                 "append_decode_noalloc", "append_fp8_block_scaled", "decode_fp8_block_scaled"]:
         fn = getattr(kvc, name)
         assert hasattr(fn, "__wrapped__"), name
         assert name in kvc.__all__, name
@@ -459,3 +459,31 @@ def test_fp8_multi_window_validation_codes():
     assert fp(*bad) == INVALID
     bad = list(pargs); bad[6] = ctypes.c_void_p(0x1002)  # misaligned k_scale
     assert fp(*bad) == INVALID
+
+
+def test_fp8_block_scaled_validation_codes():
+    lib = kvc.load_library()
+    ap = lib.kvc_append_fp8_paged_block_scaled
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 2, 128, 1, None]
+    for i in (0, 1, 4, 5, 6, 10):                    # null data, scales, table, lengths
+        bad = list(args); bad[i] = None
+        assert ap(*bad) == INVALID, i
+    bad = list(args); bad[14] = 0                    # n = 0
+    assert ap(*bad) == INVALID
+    bad = list(args); bad[9] = 0                     # empty pool
+    assert ap(*bad) == INVALID
+    ok = list(args); ok[11] = 0                      # B = 0: nothing to do
+    assert ap(*ok) == OK
+    dc = lib.kvc_decode_attention_fp8_paged_block_scaled
+    dargs = [FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 10, FAKE, 2, 8, 2, 128, 1, 0,
+             0.1, 1, None, 0, FAKE, FAKE, None]
+    bad = list(dargs); bad[5] = None                 # k_scale missing
+    assert dc(*bad) == INVALID
+    bad = list(dargs); bad[1] = FAKE                 # k_new without v_new
+    assert dc(*bad) == INVALID
+    bad = list(dargs); bad[9] = 12                   # block size not a power of two
+    assert dc(*bad) == INVALID
+    bad = list(dargs); bad[17] = -1                  # negative window
+    assert dc(*bad) == INVALID
+    bad = list(dargs); bad[19] = 2                   # a split plan needs a workspace
+    assert dc(*bad) == WORKSPACE

@@ -266,6 +266,19 @@ def _append_fp8_ring_shifted(k_new, v_new, kc, vc, ks, vs, before, block_table=N
                             block_table=block_table, ring=ring)
 
 
+def _dequantize_blocks_head_scale(codes, scale):
+    x = oracle.e4m3_values()[np.asarray(codes, dtype=np.uint8)]
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return x * sc[0][None, :, None, None]   # block 0's scales for every block
+
+
+def _dequantize_blocks_transposed(codes, scale):
+    x = oracle.e4m3_values()[np.asarray(codes, dtype=np.uint8)]
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    nb, g = sc.shape
+    return x * sc.T.reshape(-1)[: nb * g].reshape(nb, g)[:, :, None, None]
+
+
 _ORIG_FP8_WINDOW = oracle.decode_fp8_window
 _ORIG_APPEND_FP8 = oracle.append_fp8
 
@@ -277,6 +290,8 @@ FP8_MUTATIONS = {
     "dequantise_one_scale": ("dequantize_fp8", _dequantize_first_head_scale),
     "fp8_window_one_short": ("decode_fp8_window", _fp8_window_one_short),
     "fp8_ring_slot_shifted": ("append_fp8", _append_fp8_ring_shifted),
+    "block_scales_of_block_0": ("dequantize_fp8_blocks", _dequantize_blocks_head_scale),
+    "block_scales_transposed": ("dequantize_fp8_blocks", _dequantize_blocks_transposed),
 }
 
 
@@ -285,7 +300,8 @@ def test_planted_fp8_mistake_is_caught(name, monkeypatch):
     attr, fn = FP8_MUTATIONS[name]
     monkeypatch.setattr(oracle, attr, fn)
     failed = 0
-    for pin in (P.pin_fp8_format, P.pin_fp8_dequantised_attention, P.pin_fp8_multi_and_window):
+    for pin in (P.pin_fp8_format, P.pin_fp8_dequantised_attention, P.pin_fp8_multi_and_window,
+                P.pin_fp8_block_scales):
         try:
             pin()
         except Exception:  # noqa: BLE001 - any failure counts
