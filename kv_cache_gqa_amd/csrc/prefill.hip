@@ -69,13 +69,21 @@ template <int NQT, int W, bool PAGED>
 struct PrefillEngine {
     static constexpr int kRowsPerWave = 16 * NQT;
     static constexpr int kRowsPerGroup = kRowsPerWave * W;
-    static constexpr int kPer = kPieces / (64 * W);  // pieces per thread per tile
-    static_assert(kPer * 64 * W == kPieces, "pieces must divide evenly");
+#ifndef KVC_PREFILL_SUB
+#define KVC_PREFILL_SUB 2
+#endif
+    // Positions per step: kSub tiles of 32 (two with eight wavefronts, so a
+    // barrier covers 64 positions and each wavefront has two independent
+    // score products in flight).
+    static constexpr int kSub = W == 8 ? KVC_PREFILL_SUB : 1;
+    static constexpr int kSpan = kSub * kTileTokens;
+    static constexpr int kPer = kSub * kPieces / (64 * W);  // pieces per thread per step
+    static_assert(kPer * 64 * W == kSub * kPieces, "pieces must divide evenly");
 
     struct Shared {
         uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
-        __attribute__((aligned(16))) unsigned char k[2][kTileB];
-        __attribute__((aligned(16))) unsigned char v[2][kTileB];
+        __attribute__((aligned(16))) unsigned char k[2][kSub * kTileB];  // tile s at s * kTileB
+        __attribute__((aligned(16))) unsigned char v[2][kSub * kTileB];
     };
 
     // Rows rb*kRowsPerGroup .. +kRowsPerGroup of unit (b, j) over positions
@@ -181,52 +189,51 @@ struct PrefillEngine {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int q = tid + (k % kHalf) * 64 * W;
-                unsigned char* dst = k >= kHalf ? sh.v[buf] + v_off(q >> 4, q & 15)
-                                                : sh.k[buf] + k_off(q >> 4, q & 15);
+                const int r = q >> 4, sub = r >> 5;
+                unsigned char* dst = k >= kHalf ? sh.v[buf] + sub * kTileB + v_off(r & 31, q & 15)
+                                                : sh.k[buf] + sub * kTileB + k_off(r & 31, q & 15);
                 *reinterpret_cast<uint4*>(dst) = pre[k];
             }
         };
 
         auto compute_tile = [&](int t0, int buf) {
-            const unsigned char* kt = sh.k[buf];
-            const unsigned char* vt = sh.v[buf];
-            f32x4_t S[NQT][2];
+            f32x4_t S[kSub][NQT][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
+            for (int u = 0; u < kSub; ++u) {
+                const unsigned char* kt = sh.k[buf] + u * kTileB;
 #pragma unroll
-                for (int qt = 0; qt < NQT; ++qt) S[qt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const uint4 ka = *reinterpret_cast<const uint4*>(kt + k_off(16 * tt + col, 4 * ks + G));
+                    for (int qt = 0; qt < NQT; ++qt) S[u][qt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int qt = 0; qt < NQT; ++qt) S[qt][tt] = mfma_bf16(ka, qb[qt][ks], S[qt][tt]);
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const uint4 ka = *reinterpret_cast<const uint4*>(kt + k_off(16 * tt + col, 4 * ks + G));
+#pragma unroll
+                        for (int qt = 0; qt < NQT; ++qt) S[u][qt][tt] = mfma_bf16(ka, qb[qt][ks], S[u][qt][tt]);
+                    }
                 }
             }
-            // Every row of the wavefront sees the whole tile: no mask.
-            const bool full = t0 >= full_lo && t0 + kTileTokens <= min(full_hi, w1);
-            uint4 pb[NQT];
+            // Every row of the wavefront sees the whole step: no mask.
+            const bool full = t0 >= full_lo && t0 + kSpan <= min(full_hi, w1);
+            uint4 pb[kSub][NQT];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
-                float sv[8];
+                // sv[8u + 4tt + v]: position t0 + 32u + 16tt + 4G + v
+                float sv[8 * kSub];
                 if (full) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) sv[4 * tt + v] = S[qt][tt][v] * sl2;
+                    for (int k = 0; k < 8 * kSub; ++k) sv[k] = S[k >> 3][qt][(k >> 2) & 1][k & 3] * sl2;
                 } else {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int p = t0 + 16 * tt + 4 * G + v;
-                            const bool vis = p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen;
-                            sv[4 * tt + v] = vis ? S[qt][tt][v] * sl2 : kNegInf;
-                        }
+                    for (int k = 0; k < 8 * kSub; ++k) {
+                        const int p = t0 + 32 * (k >> 3) + 16 * ((k >> 2) & 1) + 4 * G + (k & 3);
+                        const bool vis = p < w1 && (unsigned)(lim[qt] - 1 - p) < wlen;
+                        sv[k] = vis ? S[k >> 3][qt][(k >> 2) & 1][k & 3] * sl2 : kNegInf;
                     }
                 }
                 float mt = sv[0];
 #pragma unroll
-                for (int k = 1; k < 8; ++k) mt = fmaxf(mt, sv[k]);
+                for (int k = 1; k < 8 * kSub; ++k) mt = fmaxf(mt, sv[k]);
                 mt = max_rows4(mt);
                 if (__any(mt > mrun[qt] + kLazyRescale)) {  // uniform branch
                     const float mnew = fmaxf(mrun[qt], mt);
@@ -239,16 +246,15 @@ struct PrefillEngine {
                     lex[qt] *= alpha;
                 }
                 const float ref = (mrun[qt] == kNegInf) ? 0.0f : mrun[qt];
-                float pv[8];
-                float psum = 0.0f;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    pv[k] = fast_exp2(sv[k] - ref);
-                    psum += pv[k];
+                for (int u = 0; u < kSub; ++u) {
+                    float pv[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) pv[k] = fast_exp2(sv[8 * u + k] - ref);
+                    lex[qt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                    pb[u][qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
                 }
-                lex[qt] += psum;
-                pb[qt] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
             }
             // PV: lane 16G + 4r + qd reads 8 bytes of V rows 4G + r and
             // 16 + 4G + r at dims 16*nt + 4*qd; the transposing read hands
@@ -256,16 +262,20 @@ struct PrefillEngine {
             const int tr_r = (lane >> 2) & 3, tr_q = lane & 3;
             const int r0 = 4 * G + tr_r, r1 = 16 + 4 * G + tr_r;
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const int ch = 2 * nt + (tr_q >> 1), sub = (tr_q & 1) * 8;
-                const uint2 lo = lds_read_tr16(vt + v_off(r0, ch) + sub);
-                const uint2 hi = lds_read_tr16(vt + v_off(r1, ch) + sub);
-                const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            for (int u = 0; u < kSub; ++u) {
+                const unsigned char* vt = sh.v[buf] + u * kTileB;
 #pragma unroll
-                for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma_bf16(av, pb[qt], acc[qt][nt]);
+                for (int nt = 0; nt < 8; ++nt) {
+                    const int ch = 2 * nt + (tr_q >> 1), sub = (tr_q & 1) * 8;
+                    const uint2 lo = lds_read_tr16(vt + v_off(r0, ch) + sub);
+                    const uint2 hi = lds_read_tr16(vt + v_off(r1, ch) + sub);
+                    const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+                    for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma_bf16(av, pb[u][qt], acc[qt][nt]);
+                }
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) lacc[qt] = mfma_bf16(ones, pb[u][qt], lacc[qt]);
             }
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) lacc[qt] = mfma_bf16(ones, pb[qt], lacc[qt]);
         };
 
         // Windows of at most kMaxChunk positions, so that a window's slice
@@ -285,14 +295,14 @@ struct PrefillEngine {
             int t0 = w0;
             load_tile(t0);
             stage_tile(0);
-            if (t0 + kTileTokens < w1) load_tile(t0 + kTileTokens);
+            if (t0 + kSpan < w1) load_tile(t0 + kSpan);
             __syncthreads();
             int buf = 0;
-            for (; t0 < w1; t0 += kTileTokens) {
-                // a wavefront whose rows see none of the tile skips it
-                if (rows > 0 && t0 < hi_w && t0 + kTileTokens > lo_w) compute_tile(t0, buf);
-                if (t0 + kTileTokens < w1) stage_tile(buf ^ 1);
-                if (t0 + 2 * kTileTokens < w1) load_tile(t0 + 2 * kTileTokens);
+            for (; t0 < w1; t0 += kSpan) {
+                // a wavefront whose rows see none of the step skips it
+                if (rows > 0 && t0 < hi_w && t0 + kSpan > lo_w) compute_tile(t0, buf);
+                if (t0 + kSpan < w1) stage_tile(buf ^ 1);
+                if (t0 + 2 * kSpan < w1) load_tile(t0 + 2 * kSpan);
                 __syncthreads();
                 buf ^= 1;
             }
