@@ -13,12 +13,12 @@
 // cut to a sliding window when one is given.
 //
 // A work-group of W wavefronts serves 16*NQT*W consecutive rows of one unit
-// over one range of positions.  Each 32-position tile of K and V is read
-// from memory once per work-group into LDS (every thread moves 16-byte
-// pieces; the next tile's pieces are in registers while this tile is
-// computed; two LDS buffers, one barrier per tile) and every wavefront
-// reads it there for its own 16*NQT rows, so a unit's K/V is read once per
-// row block instead of once per 32 rows.  Work-groups of the row blocks of
+// over one range of positions, 64 positions (two 32-position tiles) per
+// step.  A step's K and V are read from memory once per work-group into LDS
+// (every thread moves 16-byte pieces; the next step's pieces are in
+// registers while this step is computed; two LDS buffers, one barrier per
+// step) and every wavefront reads them there for its own 16*NQT rows, so a
+// unit's K/V is read once per row block instead of once per 32 rows.  Work-groups of the row blocks of
 // one unit get ids eight apart: MI355X hands work-group ids to its eight
 // XCDs in turn, so they run on one XCD at about the same time and share the
 // K/V lines in its L2.
@@ -36,7 +36,7 @@
 //   An all-ones A operand gives the column sums of the bf16-rounded P.
 // Online softmax per row in base 2 ("KV Cache 优化与注意力机制加速"
 // (plumephp.com) section 2.2) with the lazy rescale of the single-token
-// kernels: the running reference moves only when a tile maximum passes it by
+// kernels: the running reference moves only when a step maximum passes it by
 // more than 8; out = sum bf16(P) V / sum bf16(P); lse = m + log2 of the fp32
 // sum of P.  Wavefronts own disjoint rows and see the same positions, so
 // each writes its rows directly, no merge between wavefronts.
@@ -69,13 +69,10 @@ template <int NQT, int W, bool PAGED>
 struct PrefillEngine {
     static constexpr int kRowsPerWave = 16 * NQT;
     static constexpr int kRowsPerGroup = kRowsPerWave * W;
-#ifndef KVC_PREFILL_SUB
-#define KVC_PREFILL_SUB 2
-#endif
-    // Positions per step: kSub tiles of 32 (two with eight wavefronts, so a
-    // barrier covers 64 positions and each wavefront has two independent
-    // score products in flight).
-    static constexpr int kSub = W == 8 ? KVC_PREFILL_SUB : 1;
+    // Positions per step: kSub tiles of 32, so that a barrier covers 64
+    // positions and each wavefront has two independent score products in
+    // flight (measured: 0.29 -> 0.33 of the matrix-core peak at 1024 rows).
+    static constexpr int kSub = 2;
     static constexpr int kSpan = kSub * kTileTokens;
     static constexpr int kPer = kSub * kPieces / (64 * W);  // pieces per thread per step
     static_assert(kPer * 64 * W == kSub * kPieces, "pieces must divide evenly");
@@ -171,7 +168,7 @@ struct PrefillEngine {
             return base + row * kRowB + 16 * chunk;
         };
         uint4 pre[kPer];
-        // Pieces of the tile at t0 into registers: the thread's pieces k <
+        // Pieces of the step at t0 into registers: the thread's pieces k <
         // kPer/2 are of K, the others of V; piece k is row q / 16, chunk q %
         // 16 with q = tid + (k % (kPer/2)) * 64*W; positions past the range
         // repeat its last one (masked).
@@ -336,10 +333,9 @@ struct PrefillEngine {
 }  // namespace
 
 // Resident wavefronts per SIMD the register allocator is asked to allow:
-// four with 16 rows per wavefront (three when paged: the table lookups need
-// the registers of a fourth), two with 32.
+// two (a 64-position step holds up to 256 registers per lane).
 template <int NQT, bool PAGED>
-struct PrefillOccupancy { static constexpr int kWavesPerEu = NQT == 1 ? (PAGED ? 3 : 4) : 2; };
+struct PrefillOccupancy { static constexpr int kWavesPerEu = 2; };
 
 // Grid: one work-group per (chunk, KV head, sequence, row block), as a 1-D
 // grid.  Units u = (b*g + j)*C + c go in groups of eight (the last group may
