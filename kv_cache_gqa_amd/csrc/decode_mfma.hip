@@ -121,7 +121,7 @@ struct MfmaEngine {
     static constexpr bool kSingleBuffer = NQT >= 2 || (KV8 && W == 4);
     struct Shared {
         uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
-        float bsc[kBS ? 2 * kMaxTableSlice : 1];   // per block: K scale, then (+kMaxTableSlice) V scale
+        float4 bsc[kBS ? kMaxTableSlice : 1];      // per block: scale*log2e*K scale, V scale, 1 / V scale
         __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     };
 
@@ -370,11 +370,12 @@ struct MfmaEngine {
                                 bool fresh) {
             // per-block scales of the lane's eight positions 16*tt + 4*G + v
             // (a segment may start anywhere, so they may span two blocks)
-            float sk[8], vf[8];
+            float sk[8], vf[8], rvf[8];  // rvf: 1 / vf (hardware reciprocal, shared by the query tiles)
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 sk[k] = sl2;
                 vf[k] = 1.0f;
+                rvf[k] = 1.0f;
             }
             if constexpr (kBS) {
 #pragma unroll
@@ -384,10 +385,12 @@ struct MfmaEngine {
                         const long si = fp8_scale_index(a, b, j, p);
                         sk[k] = sl2 * a.k_scale[si];
                         vf[k] = a.v_scale[si];
+                        rvf[k] = __builtin_amdgcn_rcpf(vf[k]);
                     } else {
-                        const int bi = (p >> a.log2_bs) - blk0;
-                        sk[k] = sl2 * sh.bsc[bi];
-                        vf[k] = sh.bsc[kMaxTableSlice + bi];
+                        const float4 e = sh.bsc[(p >> a.log2_bs) - blk0];
+                        sk[k] = e.x;
+                        vf[k] = e.y;
+                        rvf[k] = e.z;
                     }
                 }
             }
@@ -465,9 +468,9 @@ struct MfmaEngine {
                                          pack_bf16x2(pv[4] * vf[4], pv[5] * vf[5]),
                                          pack_bf16x2(pv[6] * vf[6], pv[7] * vf[7]));
                     const uint4 w = pbv[qt];
-                    lw[qt] += bf16_lo(w.x) / vf[0] + bf16_hi(w.x) / vf[1] + bf16_lo(w.y) / vf[2] +
-                              bf16_hi(w.y) / vf[3] + bf16_lo(w.z) / vf[4] + bf16_hi(w.z) / vf[5] +
-                              bf16_lo(w.w) / vf[6] + bf16_hi(w.w) / vf[7];
+                    lw[qt] += bf16_lo(w.x) * rvf[0] + bf16_hi(w.x) * rvf[1] + bf16_lo(w.y) * rvf[2] +
+                              bf16_hi(w.y) * rvf[3] + bf16_lo(w.z) * rvf[4] + bf16_hi(w.z) * rvf[5] +
+                              bf16_lo(w.w) * rvf[6] + bf16_hi(w.w) * rvf[7];
                 }
             }
 
@@ -521,8 +524,9 @@ struct MfmaEngine {
                     ph = ph < 0 ? 0 : (ph >= a.num_blocks ? a.num_blocks - 1 : ph);
                     sh.tbl[t] = ((uint32_t)ph * (uint32_t)a.g + (uint32_t)j) * (uint32_t)a.block_size;
                     if constexpr (kBS) {
-                        sh.bsc[t] = a.k_scale[(long)ph * a.g + j];
-                        sh.bsc[kMaxTableSlice + t] = a.v_scale[(long)ph * a.g + j];
+                        const float vs_ = a.v_scale[(long)ph * a.g + j];
+                        sh.bsc[t] = make_float4(a.scale_log2e * a.k_scale[(long)ph * a.g + j], vs_,
+                                                __builtin_amdgcn_rcpf(vs_), 0.0f);
                     }
                 }
                 __syncthreads();
