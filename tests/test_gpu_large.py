@@ -3,7 +3,8 @@ of more than 4 GB each, so that the rows of the later sequences (and of the
 high physical blocks) sit beyond 32-bit byte offsets.  The caches are filled
 on the GPU from a seeded generator; sampled sequences are copied back and
 checked against the oracle (the paged ones after gathering their rows
-through the block table with torch indexing)."""
+through the block table with torch indexing).  The decode kernels and the
+multi-row kernel (many new tokens per sequence) are both covered."""
 from __future__ import annotations
 
 import sys
@@ -133,4 +134,64 @@ def test_paged_fp8_pools_past_4gb(h):
         vmax = float((vals[vr.long()] * vs.double().view(1, -1, 1, 1)).abs().max())
         check_parity(out[b:b + 1], lse[b:b + 1], ro, rl, vmax, f"large paged fp8 b={b}")
     del kp, vp, pools
+    torch.cuda.empty_cache()
+
+
+def test_multi_rows_contiguous_past_4gb():
+    """The multi-row kernel (80 new tokens x 2 query heads per KV head = 160
+    rows: 256-row work-groups of eight wavefronts) over a contiguous cache of
+    5.2 GB per K and V, the sampled last sequence starting past 4 GB."""
+    _log("case large multi-row contiguous")
+    B, h, g, d, n, t_cap = 64, 16, 8, 128, 80, 40000
+    assert (B - 1) * g * t_cap * d * 2 > 4 * GiB
+    gen = torch.Generator().manual_seed(1530)
+    lengths = torch.randint(n, t_cap + 1, (B,), generator=gen, dtype=torch.int32)
+    lengths[-1] = t_cap
+    k = _randn_gpu((B, g, t_cap, d), 1531)
+    v = _randn_gpu((B, g, t_cap, d), 1532)
+    q = W.randn((B, h, n, d), torch.bfloat16, gen)
+    scale = d ** -0.5
+    out, lse = kvc.decode_multi(dev(q), k, v, dev(lengths), scale=scale)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu(), lse.cpu()
+    for b in [0, B - 1]:
+        Lb = int(lengths[b])
+        ks = k[b:b + 1, :, :Lb].cpu()
+        vs = v[b:b + 1, :, :Lb].cpu()
+        ro, rl = oracle.decode_multi(q[b:b + 1], ks, vs, lengths[b:b + 1] - n, scale)
+        check_parity(out_h[b:b + 1], lse_h[b:b + 1], ro, rl, _vmax(vs), f"large multi-row b={b}")
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_multi_rows_paged_past_4gb():
+    """The multi-row kernel over paged pools of 4.6 GB, the sampled sequences
+    holding blocks past 4 GB; the reference gathers their rows through the
+    table."""
+    _log("case large multi-row paged")
+    B, h, g, d, n, bs = 32, 16, 8, 128, 80, 16
+    gen = torch.Generator().manual_seed(1540)
+    lengths = torch.randint(n, 8193, (B,), generator=gen, dtype=torch.int32)
+    lengths[-1] = 8192
+    used = int(((lengths.to(torch.int64) + bs - 1) // bs).sum())
+    nb = 140000
+    table, _ = W.make_block_table(lengths, bs, perm_seed=1541, extra_blocks=nb - used)
+    assert int(table.max()) * g * bs * d * 2 > 4 * GiB
+    kp = _randn_gpu((nb, g, bs, d), 1542)
+    vp = _randn_gpu((nb, g, bs, d), 1543)
+    q = W.randn((B, h, n, d), torch.bfloat16, gen)
+    scale = d ** -0.5
+    bt = dev(table)
+    out, lse = kvc.decode_multi(dev(q), kp, vp, dev(lengths), block_table=bt, scale=scale)
+    torch.cuda.synchronize()
+    out_h, lse_h = out.cpu(), lse.cpu()
+    for b in [int(torch.argmax(table.max(dim=1).values)), B - 1]:
+        Lb = int(lengths[b])
+        pos = torch.arange(Lb, device="cuda")
+        blk = bt[b, pos // bs].long()
+        kr = kp[blk, :, pos % bs].permute(1, 0, 2).unsqueeze(0).contiguous().cpu()
+        vr = vp[blk, :, pos % bs].permute(1, 0, 2).unsqueeze(0).contiguous().cpu()
+        ro, rl = oracle.decode_multi(q[b:b + 1], kr, vr, lengths[b:b + 1] - n, scale)
+        check_parity(out_h[b:b + 1], lse_h[b:b + 1], ro, rl, _vmax(vr), f"large multi-row paged b={b}")
+    del kp, vp
     torch.cuda.empty_cache()
