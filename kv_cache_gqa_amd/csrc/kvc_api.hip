@@ -35,9 +35,12 @@ Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
 // bf16 (or FP8) caches with head_dim 128: up to 3 rows per KV head on the
 // vector ALUs, 4..32 on the matrix-core decode kernel, more on the
 // multi-row kernel (bf16; FP8 caches run such rows as 32-row slices of the
-// decode kernel).  Everything else takes the generic kernel.
+// decode kernel).  bf16 caches with head_dim 64 or 256: every row count on
+// the multi-row kernel (one K/V read per KV head).  Everything else (fp32,
+// other head dims, FP8 with d != 128) takes the generic kernel.
 KernelKind choose_kernel(int dtype, int d, int m, bool kv8) {
     if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : (m <= 32 || kv8 ? kMfma : kPrefill);
+    if (dtype == KVC_BF16 && !kv8 && (d == 64 || d == 256)) return kPrefill;
     return kGeneric;
 }
 
@@ -51,12 +54,15 @@ static int row_slices(KernelKind kind, int m) { return (kind == kMfma && m > 32)
 // rows (HBM-bound: a few rows per K/V byte) 16 rows per wavefront and four
 // wavefronts; up to 128, 32 rows per wavefront; beyond (bound by the matrix
 // cores) 256 rows per work-group of eight wavefronts, so that each K/V tile
-// staged in LDS serves 256 rows.
+// staged in LDS serves 256 rows.  Head dimension 256 keeps 16 rows per
+// wavefront (its accumulators take 64 registers per query tile): 128 rows
+// per eight-wavefront work-group beyond 64.
 struct PrefillShape {
     int nqt, waves, row_blocks;
 };
-static PrefillShape prefill_shape(int m) {
+static PrefillShape prefill_shape(int m, int d) {
     if (m <= 64) return {1, 4, 1};
+    if (d == 256) return {1, 8, (m + 127) / 128};
     if (m <= 128) return {2, 4, 1};
     return {2, 8, (m + 255) / 256};
 }
@@ -280,7 +286,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
     a.row_blocks = 1;
     a.nqt = 0;
     if (sc.kind == kPrefill) {
-        const PrefillShape ps = prefill_shape(a.m);
+        const PrefillShape ps = prefill_shape(a.m, a.d);
         a.nqt = ps.nqt;
         a.waves = ps.waves;
         a.row_blocks = ps.row_blocks;
@@ -289,7 +295,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
             // the row blocks; when the row blocks alone fill them, one chunk
             // per unit (the kernel walks a long chunk in table windows) and
             // no merge
-            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged), ps.waves);
+            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged, a.d), ps.waves);
             const long groups = (long)a.B * ps.row_blocks * a.g;
             if (groups >= slots) {
                 sc.plan = Plan{(int)(ceil_div(max_len, kTileTokens) * kTileTokens), 1};

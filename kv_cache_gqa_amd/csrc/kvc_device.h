@@ -248,18 +248,20 @@ __device__ __forceinline__ int cache_slot(const DecodeArgs& a, int p) {
     return a.ring ? p % a.t_cap : p;
 }
 
-// bf16, d = 128: write the appended tokens at positions [lo, hi) of unit
+// bf16, d = D: write the appended tokens at positions [lo, hi) of unit
 // (b, j) into their cache slots.  Position p holds new token p - raw of
 // k_new / v_new [B, g, n, d].  Each of the `nthreads` threads moves 16-byte
-// pieces (32 per position: 16 of K, 16 of V).  Paged: a position whose
+// pieces (D/4 per position: D/8 of K, D/8 of V).  Paged: a position whose
 // block-table entry is not a valid block is skipped, as the append entry
 // point skips it.
-__device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, int b, int j, int raw,
-                                                         int lo, int hi, int tid, int nthreads) {
+template <int D>
+__device__ __forceinline__ void store_new_rows_bf16(const DecodeArgs& a, int b, int j, int raw, int lo,
+                                                    int hi, int tid, int nthreads) {
+    constexpr int kC = D / 8;  // 16-byte chunks per row
     const long unit = (long)b * a.g + j;
-    for (int idx = tid; idx < (hi - lo) * 32; idx += nthreads) {
-        const int p = lo + (idx >> 5);
-        const int part = idx & 31;
+    for (int idx = tid; idx < (hi - lo) * 2 * kC; idx += nthreads) {
+        const int p = lo + idx / (2 * kC);
+        const int part = idx % (2 * kC);
         long row;
         if (a.block_table != nullptr) {
             const int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
@@ -268,13 +270,17 @@ __device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, in
         } else {
             row = unit * a.t_cap + cache_slot(a, p);
         }
-        const bool is_v = part >= 16;
-        const int c = part & 15;
+        const bool is_v = part >= kC;
+        const int c = part % kC;
         const uint4* src = reinterpret_cast<const uint4*>(is_v ? a.v_new : a.k_new) +
-                           (unit * a.n + (p - raw)) * 16 + c;
-        uint4* dst = reinterpret_cast<uint4*>(const_cast<void*>(is_v ? a.v : a.k)) + row * 16 + c;
+                           (unit * a.n + (p - raw)) * kC + c;
+        uint4* dst = reinterpret_cast<uint4*>(const_cast<void*>(is_v ? a.v : a.k)) + row * kC + c;
         *dst = *src;
     }
+}
+__device__ __forceinline__ void store_new_rows_bf16_d128(const DecodeArgs& a, int b, int j, int raw,
+                                                         int lo, int hi, int tid, int nthreads) {
+    store_new_rows_bf16<128>(a, b, j, raw, lo, hi, tid, nthreads);
 }
 
 // Transposing 8-byte LDS read (gfx950 ds_read_b64_tr_b16): within each

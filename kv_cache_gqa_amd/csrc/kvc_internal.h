@@ -112,7 +112,7 @@ const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, int
 const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8);
 // Multi-row kernel for (16-row query tiles per wavefront, wavefronts per
 // work-group, layout); nullptr when not built.
-const void* prefill_kernel(int nqt, int waves, bool paged);
+const void* prefill_kernel(int nqt, int waves, bool paged, int d);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }

@@ -51,28 +51,49 @@ namespace kvc {
 
 namespace {
 
-constexpr int kD = 128;
-constexpr int kRowB = 2 * kD;                      // bytes of one K or V row
-constexpr int kTileB = kTileTokens * kRowB;        // 8 KB of K (or V) per tile
-constexpr int kPieces = 2 * kTileTokens * 16;      // 16-byte pieces of a K + V tile
 constexpr float kLazyRescale = 8.0f;
 
-// LDS offset of 16-byte chunk c of K row r: chunks XOR-swizzled by r % 16,
-// so the 16 rows an A-operand read touches at one chunk sit in 16
-// different chunk slots (all 64 banks, no conflict).
-__device__ __forceinline__ int k_off(int r, int c) { return r * kRowB + ((c ^ (r & 15)) << 4); }
-// V rows: the swizzle of the transposing reads, rows R..R+3 (R = 4k) on
-// disjoint 32-byte slices, chunk pairs (2k, 2k+1) kept adjacent.
-__device__ __forceinline__ int v_off(int r, int c) { return r * kRowB + ((c ^ ((r & 3) << 1)) << 4); }
+// Sizes for head dimension D (64, 128 or 256; bf16 rows of 2*D bytes in
+// 16-byte chunks).
+template <int D>
+struct PfDims {
+    static constexpr int kRowB = 2 * D;                       // bytes of one K or V row
+    static constexpr int kChunks = D / 8;                     // 16-byte chunks per row
+    static constexpr int kTileB = kTileTokens * kRowB;        // one 32-position tile of K (or V)
+    static constexpr int kPieces = 2 * kTileTokens * kChunks; // 16-byte pieces of a K + V tile
+    static constexpr int kKs = D / 32;                        // 32-dim steps of Q K^T
+    static constexpr int kNt = D / 16;                        // 16-dim tiles of O
 
-template <int NQT, int W, bool PAGED>
+    // LDS offset of 16-byte chunk c of K row r.  An A-operand read touches
+    // rows 0..15 at one chunk: with rows of 256 or 512 bytes the chunks are
+    // XOR-swizzled by r % 16 (16 different slots of a 256-byte bank row);
+    // with 128-byte rows two rows share a bank row, so the slot follows
+    // (r / 2) % 8 and the row's half does the rest.  No conflict either way.
+    __device__ static int k_off(int r, int c) {
+        const int swz = D == 64 ? (r >> 1) & 7 : r & 15;
+        return r * kRowB + ((c ^ swz) << 4);
+    }
+    // V rows: the swizzle of the transposing reads, rows R..R+3 (R = 4k) on
+    // disjoint 32-byte slices of the 256-byte bank row, chunk pairs (2k,
+    // 2k+1) kept adjacent.
+    __device__ static int v_off(int r, int c) { return r * kRowB + ((c ^ ((r & 3) << 1)) << 4); }
+};
+
+template <int NQT, int W, bool PAGED, int D>
 struct PrefillEngine {
+    using Dm = PfDims<D>;
+    static constexpr int kRowB = Dm::kRowB;
+    static constexpr int kTileB = Dm::kTileB;
+    static constexpr int kPieces = Dm::kPieces;
+    static constexpr int kChunks = Dm::kChunks;
     static constexpr int kRowsPerWave = 16 * NQT;
     static constexpr int kRowsPerGroup = kRowsPerWave * W;
     // Positions per step: kSub tiles of 32, so that a barrier covers 64
     // positions and each wavefront has two independent score products in
-    // flight (measured: 0.29 -> 0.33 of the matrix-core peak at 1024 rows).
-    static constexpr int kSub = 2;
+    // flight (measured: 0.29 -> 0.33 of the matrix-core peak at 1024 rows,
+    // D = 128).  With D = 256 one tile: two would need 128 KB of LDS per
+    // work-group.
+    static constexpr int kSub = D == 256 ? 1 : 2;
     static constexpr int kSpan = kSub * kTileTokens;
     static constexpr int kPer = kSub * kPieces / (64 * W);  // pieces per thread per step
     static_assert(kPer * 64 * W == kSub * kPieces, "pieces must divide evenly");
@@ -96,7 +117,7 @@ struct PrefillEngine {
 
         // B operands of Q K^T: row 16*qt + col, dims 32*ks + 8*G .. +8.
         const uint16_t* Q = (const uint16_t*)a.q;
-        uint4 qb[NQT][4];
+        uint4 qb[NQT][Dm::kKs];
         int lim[NQT];  // positions below lim are visible to the lane's row
         const unsigned wlen = a.window > 0 ? (unsigned)a.window : 0x80000000u;
         // The wavefront's rows see positions in [lo_w, hi_w) between them;
@@ -107,8 +128,8 @@ struct PrefillEngine {
             const int qi = 16 * qt + col;
             const bool ok = qi < rows;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qb[qt][ks] = ok ? ld16(Q + ((b * (long)a.h + (long)j * a.m + row0 + qi) * kD + 32 * ks + 8 * G))
+            for (int ks = 0; ks < Dm::kKs; ++ks)
+                qb[qt][ks] = ok ? ld16(Q + ((b * (long)a.h + (long)j * a.m + row0 + qi) * D + 32 * ks + 8 * G))
                                 : make_uint4(0u, 0u, 0u, 0u);
             lim[qt] = visible_len(a, raw, (row0 + qi) % a.n);
             if (ok) {
@@ -127,7 +148,7 @@ struct PrefillEngine {
             full_lo = max(full_lo, __shfl_xor(full_lo, off, 64));
         }
 
-        f32x4_t acc[NQT][8];
+        f32x4_t acc[NQT][Dm::kNt];
         f32x4_t lacc[NQT];  // sums of bf16-rounded P (normalise out)
         float lex[NQT];     // sums of fp32 P over this lane's positions (give lse)
         float mrun[NQT];
@@ -137,7 +158,7 @@ struct PrefillEngine {
             lex[qt] = 0.0f;
             lacc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < Dm::kNt; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
         const float sl2 = a.scale_log2e;
@@ -148,7 +169,7 @@ struct PrefillEngine {
         // cache there, so nothing waits for the writes).
         const bool appends = a.k_new != nullptr;
         if (appends && rb == 0 && max(s, raw) < e)
-            store_new_rows_bf16_d128(a, b, j, raw, max(s, raw), e, tid, 64 * W);
+            store_new_rows_bf16<D>(a, b, j, raw, max(s, raw), e, tid, 64 * W);
         const char* knew = appends ? (const char*)a.k_new + bj * a.n * kRowB - (long)raw * kRowB : nullptr;
         const char* vnew = appends ? (const char*)a.v_new + bj * a.n * kRowB - (long)raw * kRowB : nullptr;
 
@@ -169,16 +190,16 @@ struct PrefillEngine {
         };
         uint4 pre[kPer];
         // Pieces of the step at t0 into registers: the thread's pieces k <
-        // kPer/2 are of K, the others of V; piece k is row q / 16, chunk q %
-        // 16 with q = tid + (k % (kPer/2)) * 64*W; positions past the range
-        // repeat its last one (masked).
+        // kPer/2 are of K, the others of V; piece k is row q / kChunks, chunk
+        // q % kChunks with q = tid + (k % (kPer/2)) * 64*W; positions past
+        // the range repeat its last one (masked).
         constexpr int kHalf = kPer / 2;
         auto load_tile = [&](int t0) {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int q = tid + (k % kHalf) * 64 * W;
-                const int p = min(t0 + (q >> 4), w1 - 1);
-                const void* ptr = src(k >= kHalf, p, q & 15);
+                const int p = min(t0 + q / kChunks, w1 - 1);
+                const void* ptr = src(k >= kHalf, p, q % kChunks);
                 pre[k] = reread ? ld16(ptr) : ld16_stream(ptr);
             }
         };
@@ -186,9 +207,9 @@ struct PrefillEngine {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int q = tid + (k % kHalf) * 64 * W;
-                const int r = q >> 4, sub = r >> 5;
-                unsigned char* dst = k >= kHalf ? sh.v[buf] + sub * kTileB + v_off(r & 31, q & 15)
-                                                : sh.k[buf] + sub * kTileB + k_off(r & 31, q & 15);
+                const int r = q / kChunks, sub = r >> 5;
+                unsigned char* dst = k >= kHalf ? sh.v[buf] + sub * kTileB + Dm::v_off(r & 31, q % kChunks)
+                                                : sh.k[buf] + sub * kTileB + Dm::k_off(r & 31, q % kChunks);
                 *reinterpret_cast<uint4*>(dst) = pre[k];
             }
         };
@@ -203,8 +224,8 @@ struct PrefillEngine {
 #pragma unroll
                     for (int qt = 0; qt < NQT; ++qt) S[u][qt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const uint4 ka = *reinterpret_cast<const uint4*>(kt + k_off(16 * tt + col, 4 * ks + G));
+                    for (int ks = 0; ks < Dm::kKs; ++ks) {
+                        const uint4 ka = *reinterpret_cast<const uint4*>(kt + Dm::k_off(16 * tt + col, 4 * ks + G));
 #pragma unroll
                         for (int qt = 0; qt < NQT; ++qt) S[u][qt][tt] = mfma_bf16(ka, qb[qt][ks], S[u][qt][tt]);
                     }
@@ -238,7 +259,7 @@ struct PrefillEngine {
                     const float alpha = fast_exp2(mrun[qt] - r);  // 0 while nothing was seen
                     mrun[qt] = mnew;
 #pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) acc[qt][nt] *= alpha;
+                    for (int nt = 0; nt < Dm::kNt; ++nt) acc[qt][nt] *= alpha;
                     lacc[qt] *= alpha;
                     lex[qt] *= alpha;
                 }
@@ -262,10 +283,10 @@ struct PrefillEngine {
             for (int u = 0; u < kSub; ++u) {
                 const unsigned char* vt = sh.v[buf] + u * kTileB;
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) {
+                for (int nt = 0; nt < Dm::kNt; ++nt) {
                     const int ch = 2 * nt + (tr_q >> 1), sub = (tr_q & 1) * 8;
-                    const uint2 lo = lds_read_tr16(vt + v_off(r0, ch) + sub);
-                    const uint2 hi = lds_read_tr16(vt + v_off(r1, ch) + sub);
+                    const uint2 lo = lds_read_tr16(vt + Dm::v_off(r0, ch) + sub);
+                    const uint2 hi = lds_read_tr16(vt + Dm::v_off(r1, ch) + sub);
                     const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
                     for (int qt = 0; qt < NQT; ++qt) acc[qt][nt] = mfma_bf16(av, pb[u][qt], acc[qt][nt]);
@@ -317,7 +338,7 @@ struct PrefillEngine {
             const float lr = lacc[qt][0];
             const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
+            for (int nt = 0; nt < Dm::kNt; ++nt)
                 *reinterpret_cast<f32x4_t*>(dst.o + (long)qi * dst.o_stride + 16 * nt + 4 * G) = acc[qt][nt] * inv;
             if (G == 0) {
                 const float l = lex[qt];
@@ -334,18 +355,16 @@ struct PrefillEngine {
 
 // Resident wavefronts per SIMD the register allocator is asked to allow:
 // two (a 64-position step holds up to 256 registers per lane).
-template <int NQT, bool PAGED>
-struct PrefillOccupancy { static constexpr int kWavesPerEu = 2; };
+constexpr int kPrefillWavesPerEu = 2;
 
 // Grid: one work-group per (chunk, KV head, sequence, row block), as a 1-D
 // grid.  Units u = (b*g + j)*C + c go in groups of eight (the last group may
 // be narrower); within a group of width w, row block r of unit k has id
 // r*w + k, so the row blocks of a unit get ids eight apart.
-template <int NQT, int W, bool PAGED>
-__global__ void __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(PrefillOccupancy<NQT, PAGED>::kWavesPerEu)))
+template <int NQT, int W, bool PAGED, int D>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerEu)))
 prefill_mfma(DecodeArgs a) {
-    using E = PrefillEngine<NQT, W, PAGED>;
+    using E = PrefillEngine<NQT, W, PAGED, D>;
     __shared__ typename E::Shared sh;
     const long id = blockIdx.x;
     const long units = (long)a.num_chunks * a.g * a.B;
@@ -368,19 +387,33 @@ prefill_mfma(DecodeArgs a) {
     E::run(a, sh, b, j, c, rb, p0, p1);
 }
 
-// Kernel for (rows per wavefront tile count NQT, wavefronts W, layout).
-const void* prefill_kernel(int nqt, int waves, bool paged) {
+template <int D>
+static const void* prefill_kernel_d(int nqt, int waves, bool paged) {
     if (nqt == 1 && waves == 4)
-        return paged ? (const void*)prefill_mfma<1, 4, true> : (const void*)prefill_mfma<1, 4, false>;
-    if (nqt == 2 && waves == 4)
-        return paged ? (const void*)prefill_mfma<2, 4, true> : (const void*)prefill_mfma<2, 4, false>;
-    if (nqt == 2 && waves == 8)
-        return paged ? (const void*)prefill_mfma<2, 8, true> : (const void*)prefill_mfma<2, 8, false>;
+        return paged ? (const void*)prefill_mfma<1, 4, true, D> : (const void*)prefill_mfma<1, 4, false, D>;
+    if constexpr (D == 256) {  // 16 rows per wavefront only (64 accumulator registers per query tile)
+        if (nqt == 1 && waves == 8)
+            return paged ? (const void*)prefill_mfma<1, 8, true, D> : (const void*)prefill_mfma<1, 8, false, D>;
+    } else {
+        if (nqt == 2 && waves == 4)
+            return paged ? (const void*)prefill_mfma<2, 4, true, D> : (const void*)prefill_mfma<2, 4, false, D>;
+        if (nqt == 2 && waves == 8)
+            return paged ? (const void*)prefill_mfma<2, 8, true, D> : (const void*)prefill_mfma<2, 8, false, D>;
+    }
+    return nullptr;
+}
+
+// Kernel for (rows per wavefront tile count NQT, wavefronts W, layout, head
+// dimension d).
+const void* prefill_kernel(int nqt, int waves, bool paged, int d) {
+    if (d == 64) return prefill_kernel_d<64>(nqt, waves, paged);
+    if (d == 128) return prefill_kernel_d<128>(nqt, waves, paged);
+    if (d == 256) return prefill_kernel_d<256>(nqt, waves, paged);
     return nullptr;
 }
 
 hipError_t launch_prefill_mfma(const DecodeArgs& a, hipStream_t s) {
-    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr);
+    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr, a.d);
     if (fn == nullptr || a.row_blocks < 1 || a.stream) return hipErrorInvalidValue;
     if ((long)a.row_blocks * 16 * a.nqt * a.waves < a.m) return hipErrorInvalidValue;
     const long wgs = (long)a.num_chunks * a.g * a.B * a.row_blocks;

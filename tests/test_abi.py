@@ -59,11 +59,15 @@ def test_plan_modes():
         assert kvc.plan(B, h, g, 128, T, 0) == ("auto_chunks", 0, 0)
         assert kvc.plan(B, h, g, 128, T, 0, paged=True) == ("stream", 0, 0)
         assert kvc.plan(B, h, g, 128, T, kvc.SPLITS_STREAM) == ("stream", 0, 0)
-    # the generic kernel (fp32, other head dims) always chunks
+    # the generic kernel (fp32; bf16 head dims other than 64, 128, 256) always chunks
     assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
-    assert kvc.plan(2, 8, 2, 64, 4096, 0, paged=True)[0] == "chunks"
+    assert kvc.plan(2, 8, 2, 96, 4096, 0, paged=True)[0] == "chunks"
     assert kvc.plan(2, 8, 2, 128, 4096, kvc.SPLITS_STREAM, dtype=torch.float32)[0] == "chunks"
-    # more than 32 query rows per KV head: MFMA row slices, never stream mode
+    # bf16 head dims 64 and 256: the multi-row kernel, chunks fixed at launch
+    for d in (64, 256):
+        assert kvc.plan(2, 8, 2, d, 4096, 0, paged=True)[0] == "auto_chunks"
+        assert kvc.plan(2, 8, 8, d, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"
+    # more than 32 query rows per KV head: the multi-row kernel, never stream mode
     assert kvc.plan(2, 64, 1, 128, 4096, 0, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"
     # stream mode needs B <= 1024
