@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import hashlib
 import json
 import os
@@ -312,6 +313,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_70b_bf16")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="override the workload's head dimension (bf16 caches: 64, 128 and 256 run "
+                         "on the matrix-core kernels, other values on the generic kernel)")
     ap.add_argument("--num-splits", type=int, default=None,
                     help="override the workload's split count (0 = library's choice)")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies to rotate (0 = auto)")
@@ -378,6 +382,10 @@ def main():
         bench_block_op(args, torch, kvc, W)
         return
     w = W.WORKLOADS[args.workload]
+    if args.head_dim is not None and args.head_dim != w.d:
+        # the same shapes, seeds and lengths with another head dimension;
+        # the workload name says so (and no stored counter figure matches)
+        w = dataclasses.replace(w, d=args.head_dim, name=f"{w.name}_d{args.head_dim}")
     ns = w.num_splits if args.num_splits is None else args.num_splits
     dev = torch.device("cuda:0")
 
