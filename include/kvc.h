@@ -317,9 +317,10 @@ size_t kvc_noalloc_scratch_bytes(void);
  * kvc_decode_plan and kvc_decode_launch_shape likewise take h * n as h.
  * Kernels by rows per KV head, r = (h / g) * n, for bf16 with d = 128: r <= 3
  * the VALU kernel; 4 <= r <= 32 the matrix-core decode kernel; r > 32 the
- * same kernel in ceil(r / 32) row slices of 32, each reading the unit's K/V
- * (any n: the appended tokens' positions are taken 32 at a time).  fp32 or
- * other head dims take the generic kernel for any r.
+ * multi-row matrix-core kernel, which stages each K/V tile in LDS once for
+ * up to 256 rows (ceil(r / 256) work-groups per unit, 128 at d = 256).  bf16
+ * with d = 64 or 256: the multi-row kernel for any r.  fp32 or other head
+ * dims take the generic kernel for any r.
  */
 int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* seq_lens, int B, int h, int g, int d, int n,
