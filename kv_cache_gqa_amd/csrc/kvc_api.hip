@@ -142,16 +142,22 @@ static size_t workspace_for(int B, int h, int g, int d, const Schedule& sc) {
     return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
 }
 
-// Workspace a call needs: for automatic splits of a paged cache, enough for
-// both schedules it may take (stream, or chunks under a sliding window), so
-// that one size query serves windowed and plain calls.
+// Workspace a call needs, the largest over the schedules one size query
+// stands for: for automatic splits of a paged cache, both schedules it may
+// take (stream, or chunks under a sliding window), so that one query serves
+// windowed and plain calls; and bf16 and FP8 caches alike (FP8 calls take q
+// in bf16 and size with KVC_BF16 or KVC_FP8_E4M3), whose kernels may differ
+// (bf16 head dims 64 and 256 run the multi-row kernel, FP8 ones the generic
+// kernel, whose plans take more chunks).
 static size_t required_workspace(int B, int h, int g, int d, int dtype, int max_len,
                                  int num_splits, bool paged) {
-    size_t need = workspace_for(B, h, g, d, make_schedule(B, h, g, d, dtype, max_len, num_splits, paged));
-    if (paged && num_splits == 0) {
-        const size_t w = workspace_for(B, h, g, d,
-                                       make_schedule(B, h, g, d, dtype, max_len, num_splits, paged, true));
-        if (w > need) need = w;
+    size_t need = 0;
+    for (int f8 = 0; f8 < (dtype == KVC_BF16 ? 2 : 1); ++f8) {
+        for (int win = 0; win < (paged && num_splits == 0 ? 2 : 1); ++win) {
+            const size_t w = workspace_for(
+                B, h, g, d, make_schedule(B, h, g, d, dtype, max_len, num_splits, paged, win != 0, f8 != 0));
+            if (w > need) need = w;
+        }
     }
     return need;
 }
@@ -391,6 +397,9 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
         return KVC_ERR_INVALID;
     if (a.B == 0) return KVC_OK;
     resolve_launch(a, sc, paged, max_len);
+    // the launch's own partials must fit what was checked above
+    if (workspace_for(a.B, a.h, a.g, a.d, sc) > (workspace != nullptr ? workspace_bytes : 0))
+        return KVC_ERR_WORKSPACE;
     const size_t rows = workspace_rows(a.B, a.h, a.g, sc);
     if (rows > 0) {
         char* w = static_cast<char*>(workspace);
@@ -441,9 +450,10 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
     if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
         max_seq_len < 0)
         return KVC_ERR_INVALID;
-    if (dtype == KVC_FP8_E4M3) dtype = KVC_BF16;  // the same plans
+    const bool kv8 = dtype == KVC_FP8_E4M3;  // bf16 q over an FP8 cache
+    if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
-    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0);
+    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8);
     if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : (sc.auto_chunks ? KVC_SPLIT_AUTO_CHUNKS : KVC_SPLIT_CHUNKS);
     const bool fixed = !sc.stream && !sc.auto_chunks;
     if (chunk_len) *chunk_len = fixed ? sc.plan.chunk_len : 0;
