@@ -32,15 +32,17 @@ Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
     return Plan{(int)chunk, (int)ceil_div(max_seq_len, chunk)};
 }
 
-// bf16 (or FP8) caches with head_dim 128: up to 3 rows per KV head on the
-// vector ALUs, 4..32 on the matrix-core decode kernel, more on the
-// multi-row kernel (bf16; FP8 caches run such rows as 32-row slices of the
-// decode kernel).  bf16 caches with head_dim 64 or 256: every row count on
-// the multi-row kernel (one K/V read per KV head).  Everything else (fp32,
-// other head dims, FP8 with d != 128) takes the generic kernel.
-KernelKind choose_kernel(int dtype, int d, int m, bool kv8) {
-    if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : (m <= 32 || kv8 ? kMfma : kPrefill);
-    if (dtype == KVC_BF16 && !kv8 && (d == 64 || d == 256)) return kPrefill;
+// kv8: the cache kind (kv_mode): 0 bf16, 1 FP8 with a scale per KV head,
+// 2 FP8 with a scale per (block, KV head).  bf16 or FP8 caches with head_dim
+// 128: up to 3 rows per KV head on the vector ALUs, 4..32 on the matrix-core
+// decode kernel, more on the multi-row kernel (per-block FP8 scales: as
+// 32-row slices of the decode kernel).  bf16 caches and FP8 caches with
+// per-head scales with head_dim 64 or 256: every row count on the multi-row
+// kernel (one K/V read per KV head).  Everything else (fp32, other head
+// dims, per-block FP8 scales with d != 128) takes the generic kernel.
+KernelKind choose_kernel(int dtype, int d, int m, int kv8) {
+    if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : (m <= 32 || kv8 == 2 ? kMfma : kPrefill);
+    if (dtype == KVC_BF16 && kv8 != 2 && (d == 64 || d == 256)) return kPrefill;
     return kGeneric;
 }
 
@@ -105,8 +107,7 @@ static long chunks_for_slots(long slots, int B, int g, int max_seq_len) {
 }
 
 static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq_len,
-                              int num_splits, bool paged, bool windowed = false,
-                              bool kv8 = false) {
+                              int num_splits, bool paged, bool windowed = false, int kv8 = 0) {
     Schedule sc;
     sc.kind = choose_kernel(dtype, d, h / g, kv8);
     // Stream mode keeps global positions in 64-bit products p * total with
@@ -152,10 +153,10 @@ static size_t workspace_for(int B, int h, int g, int d, const Schedule& sc) {
 static size_t required_workspace(int B, int h, int g, int d, int dtype, int max_len,
                                  int num_splits, bool paged) {
     size_t need = 0;
-    for (int f8 = 0; f8 < (dtype == KVC_BF16 ? 2 : 1); ++f8) {
+    for (int f8 = 0; f8 < (dtype == KVC_BF16 ? 3 : 1); ++f8) {
         for (int win = 0; win < (paged && num_splits == 0 ? 2 : 1); ++win) {
             const size_t w = workspace_for(
-                B, h, g, d, make_schedule(B, h, g, d, dtype, max_len, num_splits, paged, win != 0, f8 != 0));
+                B, h, g, d, make_schedule(B, h, g, d, dtype, max_len, num_splits, paged, win != 0, f8));
             if (w > need) need = w;
         }
     }
@@ -301,7 +302,7 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
             // the row blocks; when the row blocks alone fill them, one chunk
             // per unit (the kernel walks a long chunk in table windows) and
             // no merge
-            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged, a.d), ps.waves);
+            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged, a.d, kv_mode(a)), ps.waves);
             const long groups = (long)a.B * ps.row_blocks * a.g;
             if (groups >= slots) {
                 sc.plan = Plan{(int)(ceil_div(max_len, kTileTokens) * kTileTokens), 1};
@@ -376,7 +377,7 @@ static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, voi
                       size_t workspace_bytes, hipStream_t stream) {
     const bool paged = a.block_table != nullptr;
     Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0,
-                                a.kv8 != 0);
+                                kv_mode(a));
     // (the workspace query knows no FP8 flag: it sizes for the bf16 kernels,
     // which bounds the FP8 ones)
     const size_t need = required_workspace(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged);
@@ -453,7 +454,7 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
     const bool kv8 = dtype == KVC_FP8_E4M3;  // bf16 q over an FP8 cache
     if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
-    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8);
+    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8 ? 1 : 0);
     if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : (sc.auto_chunks ? KVC_SPLIT_AUTO_CHUNKS : KVC_SPLIT_CHUNKS);
     const bool fixed = !sc.stream && !sc.auto_chunks;
     if (chunk_len) *chunk_len = fixed ? sc.plan.chunk_len : 0;
@@ -470,7 +471,7 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     if (d > 256) return KVC_ERR_UNSUPPORTED;
-    Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8);
+    Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8 ? 1 : 0);
     DecodeArgs a{};
     a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.n = 1; a.cap_len = max_seq_len;
     a.kv8 = kv8 ? 1 : 0;

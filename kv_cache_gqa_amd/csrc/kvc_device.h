@@ -311,18 +311,19 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// FP8 cache, d = 128: quantise the appended tokens at positions [lo, hi) of
+// FP8 cache, d = D: quantise the appended tokens at positions [lo, hi) of
 // unit (b, j) (bf16 rows of k_new / v_new, position p = row p - raw) and
 // write their codes into their cache slots.  One code per thread and step
-// (256 per position: 128 of K, then 128 of V).  Paged: positions whose
+// (2*D per position: D of K, then D of V).  Paged: positions whose
 // block-table entry is not a valid block are skipped.
-__device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int b, int j, int raw,
-                                                        int lo, int hi, int tid, int nthreads) {
+template <int D>
+__device__ __forceinline__ void store_new_rows_fp8(const DecodeArgs& a, int b, int j, int raw, int lo,
+                                                   int hi, int tid, int nthreads) {
     const long unit = (long)b * a.g + j;
-    for (int idx = tid; idx < (hi - lo) * 256; idx += nthreads) {
-        const int p = lo + (idx >> 8);
-        const bool is_v = (idx & 128) != 0;
-        const int e = idx & 127;
+    for (int idx = tid; idx < (hi - lo) * 2 * D; idx += nthreads) {
+        const int p = lo + idx / (2 * D);
+        const bool is_v = (idx % (2 * D)) >= D;
+        const int e = idx % D;
         long row;
         long sidx = j;
         if (a.block_table != nullptr) {
@@ -334,11 +335,15 @@ __device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int
             row = unit * a.t_cap + cache_slot(a, p);
         }
         const uint16_t x = reinterpret_cast<const uint16_t*>(is_v ? a.v_new : a.k_new)
-                               [(unit * a.n + (p - raw)) * 128 + e];
+                               [(unit * a.n + (p - raw)) * D + e];
         const float sc = is_v ? a.v_scale[sidx] : a.k_scale[sidx];
         unsigned char* dst = reinterpret_cast<unsigned char*>(const_cast<void*>(is_v ? a.v : a.k));
-        dst[row * 128 + e] = (unsigned char)e4m3_encode(__uint_as_float((uint32_t)x << 16) / sc);
+        dst[row * D + e] = (unsigned char)e4m3_encode(__uint_as_float((uint32_t)x << 16) / sc);
     }
+}
+__device__ __forceinline__ void store_new_rows_fp8_d128(const DecodeArgs& a, int b, int j, int raw,
+                                                        int lo, int hi, int tid, int nthreads) {
+    store_new_rows_fp8<128>(a, b, j, raw, lo, hi, tid, nthreads);
 }
 
 // d = 128: the bf16 pairs at dims 2*lane, 2*lane + 1 of unit (b, j)'s

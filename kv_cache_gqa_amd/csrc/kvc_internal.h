@@ -112,7 +112,7 @@ const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, int
 const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8);
 // Multi-row kernel for (16-row query tiles per wavefront, wavefronts per
 // work-group, layout); nullptr when not built.
-const void* prefill_kernel(int nqt, int waves, bool paged, int d);
+const void* prefill_kernel(int nqt, int waves, bool paged, int d, int kv8);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }
@@ -139,6 +139,6 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, vo
 
 // Which decode kernel a configuration uses (exposed for tests and tools).
 enum KernelKind { kGeneric = 0, kValu = 1, kMfma = 2, kPrefill = 3 };
-KernelKind choose_kernel(int dtype, int d, int m, bool kv8 = false);
+KernelKind choose_kernel(int dtype, int d, int m, int kv8 = 0);
 
 }  // namespace kvc

@@ -79,10 +79,18 @@ struct PfDims {
     __device__ static int v_off(int r, int c) { return r * kRowB + ((c ^ ((r & 3) << 1)) << 4); }
 };
 
-template <int NQT, int W, bool PAGED, int D>
+// KV8: 0 = bf16 cache; 1 = FP8 E4M3 codes with a float32 scale per KV head.
+// The codes are widened to bf16 when a tile is staged in LDS (exact: every
+// E4M3 value is a bf16 value), so the tiles and products are those of bf16;
+// the K scale is folded into the score scale and the V scale into the
+// output.  New tokens (bf16 in k_new / v_new) are staged as the values of
+// their codes, the same quotient and encoder the stored codes get.
+template <int NQT, int W, bool PAGED, int D, int KV8>
 struct PrefillEngine {
     using Dm = PfDims<D>;
-    static constexpr int kRowB = Dm::kRowB;
+    static constexpr int kRowB = Dm::kRowB;                // bytes of one staged (bf16) row
+    static constexpr int kCacheRowB = KV8 ? D : 2 * D;     // bytes of one cached row
+    static constexpr int kPieceB = KV8 ? 8 : 16;           // cached bytes of one 8-element piece
     static constexpr int kTileB = Dm::kTileB;
     static constexpr int kPieces = Dm::kPieces;
     static constexpr int kChunks = Dm::kChunks;
@@ -161,15 +169,18 @@ struct PrefillEngine {
             for (int nt = 0; nt < Dm::kNt; ++nt) acc[qt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-        const float sl2 = a.scale_log2e;
+        const float k_sc = KV8 ? a.k_scale[j] : 1.0f, v_sc = KV8 ? a.v_scale[j] : 1.0f;
+        const float sl2 = a.scale_log2e * k_sc;
 
         // The appended tokens: positions raw .. come from k_new / v_new rows
         // (b, j, p - raw); the first row block's work-group writes this
         // range's new positions into the cache (the kernels never read the
         // cache there, so nothing waits for the writes).
         const bool appends = a.k_new != nullptr;
-        if (appends && rb == 0 && max(s, raw) < e)
-            store_new_rows_bf16<D>(a, b, j, raw, max(s, raw), e, tid, 64 * W);
+        if (appends && rb == 0 && max(s, raw) < e) {
+            if constexpr (KV8) store_new_rows_fp8<D>(a, b, j, raw, max(s, raw), e, tid, 64 * W);
+            else store_new_rows_bf16<D>(a, b, j, raw, max(s, raw), e, tid, 64 * W);
+        }
         const char* knew = appends ? (const char*)a.k_new + bj * a.n * kRowB - (long)raw * kRowB : nullptr;
         const char* vnew = appends ? (const char*)a.v_new + bj * a.n * kRowB - (long)raw * kRowB : nullptr;
 
@@ -180,27 +191,48 @@ struct PrefillEngine {
         // Address of the 16-byte piece `chunk` of K (or V) at position p.
         const char* kbase = (const char*)a.k;
         const char* vbase = (const char*)a.v;
-        auto src = [&](bool isv, int p, int chunk) -> const void* {
-            if (appends && p >= raw) return (isv ? vnew : knew) + (long)p * kRowB + 16 * chunk;
+        // Address of 8-element piece `chunk` of K (or V) at position p: in
+        // k_new / v_new (bf16) for appended positions, else in the cache.
+        auto fresh_src = [&](bool isv, int p, int chunk) -> const char* {
+            return (isv ? vnew : knew) + (long)p * kRowB + 16 * chunk;
+        };
+        auto cache_src = [&](bool isv, int p, int chunk) -> const char* {
             const char* base = isv ? vbase : kbase;
             uint64_t row;
             if (PAGED) row = sh.tbl[(p >> a.log2_bs) - blk0] + (uint32_t)(p & (a.block_size - 1));
             else row = (uint64_t)(bj * a.t_cap + cache_slot(a, p));
-            return base + row * kRowB + 16 * chunk;
+            return base + row * kCacheRowB + kPieceB * chunk;
         };
-        uint4 pre[kPer];
+        auto src = [&](bool isv, int p, int chunk) -> const void* {
+            return appends && p >= raw ? fresh_src(isv, p, chunk) : cache_src(isv, p, chunk);
+        };
+        // staged pieces in registers: bf16 values, or (FP8) their codes
+        std::conditional_t<KV8 != 0, uint2, uint4> pre[kPer];
         // Pieces of the step at t0 into registers: the thread's pieces k <
         // kPer/2 are of K, the others of V; piece k is row q / kChunks, chunk
         // q % kChunks with q = tid + (k % (kPer/2)) * 64*W; positions past
         // the range repeat its last one (masked).
         constexpr int kHalf = kPer / 2;
+        // FP8: a piece is 8 codes; an appended position's 8 bf16 values are
+        // quantised as they arrive (the quotient and encoder of the stored
+        // codes), which waits for those loads: one step per unit has them.
         auto load_tile = [&](int t0) {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int q = tid + (k % kHalf) * 64 * W;
                 const int p = min(t0 + q / kChunks, w1 - 1);
-                const void* ptr = src(k >= kHalf, p, q % kChunks);
-                pre[k] = reread ? ld16(ptr) : ld16_stream(ptr);
+                if constexpr (KV8) {
+                    if (appends && p >= raw) {
+                        pre[k] = e4m3_encode8(ld16(fresh_src(k >= kHalf, p, q % kChunks)),
+                                              k >= kHalf ? v_sc : k_sc);
+                    } else {
+                        const void* ptr = cache_src(k >= kHalf, p, q % kChunks);
+                        pre[k] = reread ? ld8(ptr) : ld8_stream(ptr);
+                    }
+                } else {
+                    const void* ptr = src(k >= kHalf, p, q % kChunks);
+                    pre[k] = reread ? ld16(ptr) : ld16_stream(ptr);
+                }
             }
         };
         auto stage_tile = [&](int buf) {
@@ -210,7 +242,8 @@ struct PrefillEngine {
                 const int r = q / kChunks, sub = r >> 5;
                 unsigned char* dst = k >= kHalf ? sh.v[buf] + sub * kTileB + Dm::v_off(r & 31, q % kChunks)
                                                 : sh.k[buf] + sub * kTileB + Dm::k_off(r & 31, q % kChunks);
-                *reinterpret_cast<uint4*>(dst) = pre[k];
+                if constexpr (KV8) *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16(pre[k]);
+                else *reinterpret_cast<uint4*>(dst) = pre[k];
             }
         };
 
@@ -336,7 +369,7 @@ struct PrefillEngine {
             const int qi = 16 * qt + col;
             if (qi >= rows) continue;
             const float lr = lacc[qt][0];
-            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+            const float inv = lr > 0.0f ? v_sc / lr : 0.0f;
 #pragma unroll
             for (int nt = 0; nt < Dm::kNt; ++nt)
                 *reinterpret_cast<f32x4_t*>(dst.o + (long)qi * dst.o_stride + 16 * nt + 4 * G) = acc[qt][nt] * inv;
@@ -361,10 +394,10 @@ constexpr int kPrefillWavesPerEu = 2;
 // grid.  Units u = (b*g + j)*C + c go in groups of eight (the last group may
 // be narrower); within a group of width w, row block r of unit k has id
 // r*w + k, so the row blocks of a unit get ids eight apart.
-template <int NQT, int W, bool PAGED, int D>
+template <int NQT, int W, bool PAGED, int D, int KV8>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerEu)))
 prefill_mfma(DecodeArgs a) {
-    using E = PrefillEngine<NQT, W, PAGED, D>;
+    using E = PrefillEngine<NQT, W, PAGED, D, KV8>;
     __shared__ typename E::Shared sh;
     const long id = blockIdx.x;
     const long units = (long)a.num_chunks * a.g * a.B;
@@ -387,33 +420,40 @@ prefill_mfma(DecodeArgs a) {
     E::run(a, sh, b, j, c, rb, p0, p1);
 }
 
-template <int D>
+template <int NQT, int W, int D, int KV8>
+static const void* prefill_pick(bool paged) {
+    return paged ? (const void*)prefill_mfma<NQT, W, true, D, KV8> : (const void*)prefill_mfma<NQT, W, false, D, KV8>;
+}
+
+template <int D, int KV8>
 static const void* prefill_kernel_d(int nqt, int waves, bool paged) {
-    if (nqt == 1 && waves == 4)
-        return paged ? (const void*)prefill_mfma<1, 4, true, D> : (const void*)prefill_mfma<1, 4, false, D>;
+    if (nqt == 1 && waves == 4) return prefill_pick<1, 4, D, KV8>(paged);
     if constexpr (D == 256) {  // 16 rows per wavefront only (64 accumulator registers per query tile)
-        if (nqt == 1 && waves == 8)
-            return paged ? (const void*)prefill_mfma<1, 8, true, D> : (const void*)prefill_mfma<1, 8, false, D>;
+        if (nqt == 1 && waves == 8) return prefill_pick<1, 8, D, KV8>(paged);
     } else {
-        if (nqt == 2 && waves == 4)
-            return paged ? (const void*)prefill_mfma<2, 4, true, D> : (const void*)prefill_mfma<2, 4, false, D>;
-        if (nqt == 2 && waves == 8)
-            return paged ? (const void*)prefill_mfma<2, 8, true, D> : (const void*)prefill_mfma<2, 8, false, D>;
+        if (nqt == 2 && waves == 4) return prefill_pick<2, 4, D, KV8>(paged);
+        if (nqt == 2 && waves == 8) return prefill_pick<2, 8, D, KV8>(paged);
     }
     return nullptr;
 }
 
 // Kernel for (rows per wavefront tile count NQT, wavefronts W, layout, head
-// dimension d).
-const void* prefill_kernel(int nqt, int waves, bool paged, int d) {
-    if (d == 64) return prefill_kernel_d<64>(nqt, waves, paged);
-    if (d == 128) return prefill_kernel_d<128>(nqt, waves, paged);
-    if (d == 256) return prefill_kernel_d<256>(nqt, waves, paged);
+// dimension d, cache kind: 0 bf16, 1 FP8 with per-KV-head scales).
+const void* prefill_kernel(int nqt, int waves, bool paged, int d, int kv8) {
+    if (kv8 == 0) {
+        if (d == 64) return prefill_kernel_d<64, 0>(nqt, waves, paged);
+        if (d == 128) return prefill_kernel_d<128, 0>(nqt, waves, paged);
+        if (d == 256) return prefill_kernel_d<256, 0>(nqt, waves, paged);
+    } else if (kv8 == 1) {
+        if (d == 64) return prefill_kernel_d<64, 1>(nqt, waves, paged);
+        if (d == 128) return prefill_kernel_d<128, 1>(nqt, waves, paged);
+        if (d == 256) return prefill_kernel_d<256, 1>(nqt, waves, paged);
+    }
     return nullptr;
 }
 
 hipError_t launch_prefill_mfma(const DecodeArgs& a, hipStream_t s) {
-    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr, a.d);
+    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr, a.d, kv_mode(a));
     if (fn == nullptr || a.row_blocks < 1 || a.stream) return hipErrorInvalidValue;
     if ((long)a.row_blocks * 16 * a.nqt * a.waves < a.m) return hipErrorInvalidValue;
     const long wgs = (long)a.num_chunks * a.g * a.B * a.row_blocks;

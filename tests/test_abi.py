@@ -338,21 +338,16 @@ def test_fp8_validation_codes():
 
 
 def test_fp8_planning_dtype_plans_like_bf16():
-    """KVC_FP8_E4M3 in the planning queries: at head dim 128 the plans of
-    bf16 (the same kernel families); at 64 the FP8 cache takes the generic
-    kernel (fixed chunks) where bf16 takes the multi-row one.  The workspace
-    query is the same for both dtypes (it sizes for either cache)."""
+    """KVC_FP8_E4M3 in the planning queries (FP8 caches with a scale per KV
+    head): the plans and workspaces of bf16, the same kernel families."""
     lib = kvc.load_library()
     for shape in [(32, 64, 8, 128, 4112, 0, 0), (64, 32, 8, 128, 8208, 0, 1), (4, 32, 1, 128, 131088, 64, 0),
-                  (3, 8, 2, 128, 5000, 3, 1), (2, 8, 2, 64, 100, -1, 0)]:
+                  (3, 8, 2, 128, 5000, 3, 1), (2, 8, 2, 64, 100, -1, 0), (8, 64, 8, 256, 4096, 0, 1)]:
         B, h, g, d, L, ns, paged = shape
-        if d == 128:
-            assert kvc.plan(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
-                kvc.plan(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
+        assert kvc.plan(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
+            kvc.plan(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
         assert kvc.workspace_bytes(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
             kvc.workspace_bytes(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
-    assert kvc.plan(2, 8, 2, 64, 100, -1, dtype="fp8")[0] == "chunks"
-    assert kvc.plan(2, 8, 2, 64, 100, -1, dtype=torch.bfloat16)[0] == "auto_chunks"
     assert lib.kvc_decode_plan(2, 8, 2, 128, 3, 64, 0, 0, None, None, None) == UNSUPPORTED
 
 
@@ -501,14 +496,16 @@ def test_fp8_block_scaled_validation_codes():
 
 def test_workspace_query_covers_fp8_plans():
     """One workspace query serves bf16 and FP8 caches (the FP8 calls size
-    with KVC_BF16 or KVC_FP8_E4M3).  With head dims 64 and 256 the two take
-    different kernels (multi-row for bf16, generic for FP8, whose plan has
-    more chunks): the query must cover the generic plan's partial rows."""
+    with KVC_BF16 or KVC_FP8_E4M3), per-block FP8 scales included.  At head
+    dims 64 and 256 those take the generic kernel while bf16 takes the
+    multi-row one, and the generic plan has more chunks: the query must cover
+    its partial rows (the generic plan is the one an fp32 query reports)."""
     for (B, h, g, d, T) in [(64, 32, 8, 64, 4096), (32, 64, 8, 256, 8192), (256, 8, 8, 64, 2048),
                             (6, 6, 2, 64, 4100)]:
         for paged in (False, True):
-            mode, _, chunks = kvc.plan(B, h, g, d, T, 0, dtype=kvc.FP8_E4M3, paged=paged)
+            mode, _, chunks = kvc.plan(B, h, g, d, T, 0, dtype=torch.float32, paged=paged)
             assert mode == "chunks", (B, h, g, d, mode)
+            assert kvc.plan(B, h, g, d, T, 0, dtype=torch.bfloat16, paged=paged)[0] == "auto_chunks"
             rows = B * h * chunks if chunks > 1 else 0
             need = rows * d * 4 + rows * 4
             for dt in (torch.bfloat16, kvc.FP8_E4M3):

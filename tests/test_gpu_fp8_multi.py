@@ -22,16 +22,26 @@ from gpu_util import check_parity, dev
 pytestmark = pytest.mark.gpu
 
 NAN_CODE = 0x7F
-# (id, h, g, n)
+# (id, h, g, n); head dim 128 unless the id says d64 / d256.  Rows per KV
+# head (h / g) * n: 1-3 the VALU kernel, 4-32 the matrix-core decode kernel,
+# more (and every row count at d = 64, 256) the multi-row kernel.
 SHAPES = [
     ("valu_rows2", 4, 4, 2),
     ("valu_rows3", 6, 2, 1),
     ("mfma_rows8", 8, 2, 2),
     ("mfma_rows32", 16, 2, 4),
-    ("mfma_slices40", 8, 1, 5),
-    ("mfma_mha_n33", 2, 2, 33),
-    ("generic_d64_rows6", 6, 2, 2),
+    ("multirow_rows40", 8, 1, 5),
+    ("multirow_mha_n33", 2, 2, 33),
+    ("multirow_rows96", 4, 2, 48),
+    ("multirow_rows320", 32, 2, 20),
+    ("multirow_d64_rows6", 6, 2, 2),
+    ("multirow_d256_rows4", 8, 2, 1),
+    ("multirow_d256_rows160", 16, 2, 20),
 ]
+
+
+def _head_dim(name):
+    return 64 if "d64" in name else (256 if "d256" in name else 128)
 BEFORE = [0, 1, 15, 33, 500, 4096]
 
 
@@ -90,7 +100,7 @@ def test_append_decode_fp8_multi_window(shape, layout, window, num_splits):
     name, h, g, n = shape
     if layout == "ring" and window == 0:
         pytest.skip("a ring cache needs a window")
-    d = 64 if name.startswith("generic") else 128
+    d = _head_dim(name)
     _log(f"case fp8_multi {name} n={n} {layout} W={window} splits={num_splits}")
     before, q, k_new, v_new, kc, vc, ks, vs, table, t_cap = _case(h, g, n, d, layout, window, 1400)
     ring, paged = layout == "ring", layout == "paged"
@@ -110,21 +120,22 @@ def test_append_decode_fp8_multi_window(shape, layout, window, num_splits):
     _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
 
 
-@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[3], SHAPES[4]],
-                         ids=[SHAPES[0][0], SHAPES[3][0], SHAPES[4][0]])
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[3], SHAPES[4], SHAPES[6], SHAPES[10]],
+                         ids=[SHAPES[0][0], SHAPES[3][0], SHAPES[4][0], SHAPES[6][0], SHAPES[10][0]])
 @pytest.mark.parametrize("layout", ["linear", "paged"])
 def test_decode_fp8_multi_over_filled_cache(shape, layout):
     """The tokens' codes are already in the cache; seq_lens counts them."""
     name, h, g, n = shape
+    d = _head_dim(name)
     _log(f"case fp8_multi_filled {name} {layout}")
-    before, q, k_new, v_new, kc, vc, ks, vs, table, t_cap = _case(h, g, n, 128, layout, 0, 1410)
+    before, q, k_new, v_new, kc, vc, ks, vs, table, t_cap = _case(h, g, n, d, layout, 0, 1410)
     ek, ev = oracle.append_fp8(k_new, v_new, kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(), before,
                                block_table=table)
     out, lse = kvc.decode_fp8_window(dev(q), dev(torch.from_numpy(ek)), dev(torch.from_numpy(ev)),
                                      dev(ks), dev(vs), dev(before + n),
                                      block_table=dev(table) if layout == "paged" else None,
                                      num_splits=2)
-    ro, rl = oracle.decode_fp8_window(q, ek, ev, ks.numpy(), vs.numpy(), before, 128 ** -0.5, 0,
+    ro, rl = oracle.decode_fp8_window(q, ek, ev, ks.numpy(), vs.numpy(), before, d ** -0.5, 0,
                                       block_table=table)
     check_parity(out, lse, ro, rl,
                  _vmax(torch.from_numpy(ev), vs, before, n, 0, layout, table, t_cap), name)
@@ -163,3 +174,42 @@ def test_fp8_multi_window_full_size_70b(n, window):
     vmax = _vmax(torch.from_numpy(ev), vs, before[seqs], n, window, "linear", None, ek.shape[2])
     e = check_parity(out[seqs], lse[seqs], ro, rl, vmax, f"70b fp8 n={n} W={window}")
     _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
+
+
+@pytest.mark.parametrize("n", [128])
+def test_fp8_many_tokens_full_size_70b(n):
+    """The 70B GQA cache as FP8 codes with 128 new tokens per sequence (1024
+    query rows per KV head: the multi-row kernel, codes widened to bf16 as
+    they are staged), in the launch the benchmark times: the new codes of
+    sampled sequences against the quantising append, and attention rows of
+    sampled tokens against the oracle, each computed alone."""
+    _log(f"case fp8_full_70b_many n={n}")
+    w = W.WORKLOADS["gqa_70b_bf16"]
+    x = W.make_contiguous(w, t_cap=w.T + n + w.cap_pad)
+    gen = torch.Generator().manual_seed(1430 + n)
+
+    def quantise(t):
+        sc = (t.float().abs().amax(dim=(0, 2, 3)) / 448.0).clamp(min=1e-12)
+        return (t.float() / sc.view(1, -1, 1, 1)).to(torch.float8_e4m3fn).view(torch.uint8), sc
+    kc, ks = quantise(x["k_cache"])
+    vc, vs = quantise(x["v_cache"])
+    q = W.randn((w.B, w.h, n, w.d), torch.bfloat16, gen)
+    k_new = W.randn((w.B, w.g, n, w.d), torch.bfloat16, gen)
+    v_new = W.randn((w.B, w.g, n, w.d), torch.bfloat16, gen)
+    before = x["seq_lens_before"]
+    kd, vd = dev(kc), dev(vc)
+    out, lse = kvc.decode_fp8_window(dev(q), kd, vd, dev(ks), dev(vs), dev(before),
+                                     k_new=dev(k_new), v_new=dev(v_new))
+    torch.cuda.synchronize()
+    seqs = [0, 31]
+    ek, ev = oracle.append_fp8(k_new[seqs], v_new[seqs], kc[seqs].numpy(), vc[seqs].numpy(),
+                               ks.numpy(), vs.numpy(), before[seqs])
+    assert np.array_equal(kd.cpu()[seqs].numpy(), ek) and np.array_equal(vd.cpu()[seqs].numpy(), ev)
+    out_h, lse_h = out.cpu()[seqs], lse.cpu()[seqs]
+    for t in [0, 1, 64, n - 1]:
+        vis = before[seqs] + t  # token t sees before + t + 1 positions: a single token after before + t
+        ro, rl = oracle.decode_fp8(q[seqs, :, t].contiguous(), ek, ev, ks.numpy(), vs.numpy(),
+                                   vis + 1, x["scale"])
+        vmax = _vmax(torch.from_numpy(ev), vs, vis, 1, 0, "linear", None, ek.shape[2])
+        e = check_parity(out_h[:, :, t], lse_h[:, :, t], ro, rl, vmax, f"70b fp8 n={n} t={t}")
+    _log(f"  last sampled token err/vmax {e[0]:.2e} lse {e[1]:.2e}")
