@@ -722,9 +722,10 @@ def main():
     achieved_gbs = call_bytes / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = w.B * nq / (ms_per_step * 1e-3)
     # Which roof bounds the call: its bytes at 8 TB/s or its flops at the
-    # bf16 matrix-core peak, whichever takes longer.
+    # bf16 matrix-core peak, whichever takes longer (FP8 caches too: their
+    # codes are widened to bf16 for the same matrix-core products).
     flops = attention_flops(w, x["seq_lens_before"], n=nq, window=win)
-    mfma_bound = w.dtype == "bf16" and not fp8 and \
+    mfma_bound = w.dtype == "bf16" and \
         flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > call_bytes / (HBM_PEAK_GBS * 1e9)
     achieved_tflops = flops / (dec_avg_ms * 1e-3) / 1e12
 

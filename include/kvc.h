@@ -420,9 +420,11 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
  *   but the token is still attended to.
  * Everything else (validation, splits, workspace from
  * kvc_decode_workspace_bytes with dtype KVC_BF16, positions, status codes)
- * is as in the bf16 single-token calls.  The fast kernels cover d = 128;
- * other head dims take the generic kernel.  More than 32 query rows per KV
- * head run as 32-row slices of the matrix-core decode kernel.
+ * is as in the bf16 single-token calls.  Kernels: at d = 128 as for bf16
+ * (up to 3 rows per KV head the VALU kernel, 4-32 the matrix-core decode
+ * kernel, more the multi-row kernel, which widens the codes to bf16 as it
+ * stages each tile in LDS); at d = 64 and 256 the multi-row kernel for any
+ * row count; other head dims the generic kernel.
  */
 int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
@@ -556,7 +558,10 @@ int kvc_append_decode_attention_fp8_window_paged(
  *   paged _multi / _window calls.  Attention is over the dequantised values:
  *   each score uses the K scale of its position's block, and each V row is
  *   weighted by its block's V scale; a new token whose table entry is not a
- *   valid block is attended with the scales of the clamped entry.
+ *   valid block is attended with the scales of the clamped entry.  Kernels:
+ *   at d = 128 up to 3 rows per KV head the VALU kernel, 4-32 the
+ *   matrix-core decode kernel, more as 32-row slices of it (each reading
+ *   the unit's K/V); other head dims the generic kernel.
  */
 int kvc_append_fp8_paged_block_scaled(const void* k_new, const void* v_new, void* k_pool,
                                       void* v_pool, const float* k_scale, const float* v_scale,
