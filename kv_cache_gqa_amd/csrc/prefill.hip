@@ -58,9 +58,7 @@ constexpr float kLazyRescale = 8.0f;
 template <int D>
 struct PfDims {
     static constexpr int kRowB = 2 * D;                       // bytes of one K or V row
-    static constexpr int kChunks = D / 8;                     // 16-byte chunks per row
     static constexpr int kTileB = kTileTokens * kRowB;        // one 32-position tile of K (or V)
-    static constexpr int kPieces = 2 * kTileTokens * kChunks; // 16-byte pieces of a K + V tile
     static constexpr int kKs = D / 32;                        // 32-dim steps of Q K^T
     static constexpr int kNt = D / 16;                        // 16-dim tiles of O
 
@@ -90,10 +88,7 @@ struct PrefillEngine {
     using Dm = PfDims<D>;
     static constexpr int kRowB = Dm::kRowB;                // bytes of one staged (bf16) row
     static constexpr int kCacheRowB = KV8 ? D : 2 * D;     // bytes of one cached row
-    static constexpr int kPieceB = KV8 ? 8 : 16;           // cached bytes of one 8-element piece
     static constexpr int kTileB = Dm::kTileB;
-    static constexpr int kPieces = Dm::kPieces;
-    static constexpr int kChunks = Dm::kChunks;
     static constexpr int kRowsPerWave = 16 * NQT;
     static constexpr int kRowsPerGroup = kRowsPerWave * W;
     // Positions per step: kSub tiles of 32, so that a barrier covers 64
@@ -103,8 +98,16 @@ struct PrefillEngine {
     // work-group.
     static constexpr int kSub = D == 256 ? 1 : 2;
     static constexpr int kSpan = kSub * kTileTokens;
-    static constexpr int kPer = kSub * kPieces / (64 * W);  // pieces per thread per step
-    static_assert(kPer * 64 * W == kSub * kPieces, "pieces must divide evenly");
+    // A piece is what one thread moves with one 16-byte load: 8 bf16
+    // elements, or 16 FP8 codes (two staged chunks) when the step has at
+    // least one K piece of that size per thread (else 8 codes, 8 bytes).
+    static constexpr bool kWide = KV8 && kSub * kTileTokens * (D / 16) >= 64 * W;
+    static constexpr int kPE = kWide ? 16 : 8;                // elements per piece
+    static constexpr int kPPR = D / kPE;                      // pieces per row
+    static constexpr int kPieceB = KV8 ? kPE : 16;            // cached bytes of one piece
+    static constexpr int kStepPieces = 2 * kSub * kTileTokens * kPPR;  // K and V pieces per step
+    static constexpr int kPer = kStepPieces / (64 * W);       // pieces per thread per step
+    static_assert(kPer >= 2 && kPer * 64 * W == kStepPieces, "pieces must divide evenly");
 
     struct Shared {
         uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
@@ -188,62 +191,79 @@ struct PrefillEngine {
         // keep it in L2 for the others; a single reader streams.
         const bool reread = a.row_blocks > 1;
         int blk0 = 0, w1 = e;
-        // Address of the 16-byte piece `chunk` of K (or V) at position p.
         const char* kbase = (const char*)a.k;
         const char* vbase = (const char*)a.v;
-        // Address of 8-element piece `chunk` of K (or V) at position p: in
-        // k_new / v_new (bf16) for appended positions, else in the cache.
-        auto fresh_src = [&](bool isv, int p, int chunk) -> const char* {
-            return (isv ? vnew : knew) + (long)p * kRowB + 16 * chunk;
+        // Address of piece pc of K (or V) at position p: in k_new / v_new
+        // (bf16) for appended positions, else in the cache.
+        auto fresh_src = [&](bool isv, int p, int pc) -> const char* {
+            return (isv ? vnew : knew) + (long)p * kRowB + 2 * kPE * pc;
         };
-        auto cache_src = [&](bool isv, int p, int chunk) -> const char* {
+        auto cache_src = [&](bool isv, int p, int pc) -> const char* {
             const char* base = isv ? vbase : kbase;
             uint64_t row;
             if (PAGED) row = sh.tbl[(p >> a.log2_bs) - blk0] + (uint32_t)(p & (a.block_size - 1));
             else row = (uint64_t)(bj * a.t_cap + cache_slot(a, p));
-            return base + row * kCacheRowB + kPieceB * chunk;
+            return base + row * kCacheRowB + kPieceB * pc;
         };
-        auto src = [&](bool isv, int p, int chunk) -> const void* {
-            return appends && p >= raw ? fresh_src(isv, p, chunk) : cache_src(isv, p, chunk);
+        auto src = [&](bool isv, int p, int pc) -> const void* {
+            return appends && p >= raw ? fresh_src(isv, p, pc) : cache_src(isv, p, pc);
         };
         // staged pieces in registers: bf16 values, or (FP8) their codes
-        std::conditional_t<KV8 != 0, uint2, uint4> pre[kPer];
+        std::conditional_t<KV8 != 0 && !kWide, uint2, uint4> pre[kPer];
         // Pieces of the step at t0 into registers: the thread's pieces k <
-        // kPer/2 are of K, the others of V; piece k is row q / kChunks, chunk
-        // q % kChunks with q = tid + (k % (kPer/2)) * 64*W; positions past
+        // kPer/2 are of K, the others of V; piece k is row q / kPPR, piece q %
+        // kPPR of the row with q = tid + (k % (kPer/2)) * 64*W; positions past
         // the range repeat its last one (masked).
         constexpr int kHalf = kPer / 2;
-        // FP8: a piece is 8 codes; an appended position's 8 bf16 values are
-        // quantised as they arrive (the quotient and encoder of the stored
-        // codes), which waits for those loads: one step per unit has them.
+        // FP8: an appended position's bf16 values are quantised as they
+        // arrive (the quotient and encoder of the stored codes), which waits
+        // for those loads: one step per unit has them.
         auto load_tile = [&](int t0) {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int q = tid + (k % kHalf) * 64 * W;
-                const int p = min(t0 + q / kChunks, w1 - 1);
+                const int p = min(t0 + q / kPPR, w1 - 1);
+                const bool isv = k >= kHalf;
                 if constexpr (KV8) {
+                    const float sc = isv ? v_sc : k_sc;
                     if (appends && p >= raw) {
-                        pre[k] = e4m3_encode8(ld16(fresh_src(k >= kHalf, p, q % kChunks)),
-                                              k >= kHalf ? v_sc : k_sc);
+                        const char* f = fresh_src(isv, p, q % kPPR);
+                        if constexpr (kWide) {
+                            const uint2 lo = e4m3_encode8(ld16(f), sc), hi = e4m3_encode8(ld16(f + 16), sc);
+                            pre[k] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                        } else {
+                            pre[k] = e4m3_encode8(ld16(f), sc);
+                        }
                     } else {
-                        const void* ptr = cache_src(k >= kHalf, p, q % kChunks);
-                        pre[k] = reread ? ld8(ptr) : ld8_stream(ptr);
+                        const void* ptr = cache_src(isv, p, q % kPPR);
+                        if constexpr (kWide) pre[k] = reread ? ld16(ptr) : ld16_stream(ptr);
+                        else pre[k] = reread ? ld8(ptr) : ld8_stream(ptr);
                     }
                 } else {
-                    const void* ptr = src(k >= kHalf, p, q % kChunks);
+                    const void* ptr = src(isv, p, q % kPPR);
                     pre[k] = reread ? ld16(ptr) : ld16_stream(ptr);
                 }
             }
+        };
+        // 16-byte staged chunk c of row r (within the step) of K or V, buffer buf
+        auto chunk_at = [&](bool isv, int buf, int r, int c) -> uint4* {
+            const int off = (r >> 5) * kTileB + (isv ? Dm::v_off(r & 31, c) : Dm::k_off(r & 31, c));
+            return reinterpret_cast<uint4*>((isv ? sh.v[buf] : sh.k[buf]) + off);
         };
         auto stage_tile = [&](int buf) {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int q = tid + (k % kHalf) * 64 * W;
-                const int r = q / kChunks, sub = r >> 5;
-                unsigned char* dst = k >= kHalf ? sh.v[buf] + sub * kTileB + Dm::v_off(r & 31, q % kChunks)
-                                                : sh.k[buf] + sub * kTileB + Dm::k_off(r & 31, q % kChunks);
-                if constexpr (KV8) *reinterpret_cast<uint4*>(dst) = e4m3x8_to_bf16(pre[k]);
-                else *reinterpret_cast<uint4*>(dst) = pre[k];
+                const int r = q / kPPR, pc = q % kPPR;
+                const bool isv = k >= kHalf;
+                if constexpr (KV8 && kWide) {
+                    *chunk_at(isv, buf, r, 2 * pc) = e4m3x8_to_bf16(make_uint2(pre[k].x, pre[k].y));
+                    *chunk_at(isv, buf, r, 2 * pc + 1) = e4m3x8_to_bf16(make_uint2(pre[k].z, pre[k].w));
+                } else if constexpr (KV8) {
+                    *chunk_at(isv, buf, r, pc) = e4m3x8_to_bf16(pre[k]);
+                } else {
+                    *chunk_at(isv, buf, r, pc) = pre[k];
+                }
             }
         };
 
