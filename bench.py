@@ -391,9 +391,10 @@ def main():
 
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     if w.paged:
-        x = W.make_paged(w)
+        # blocks for the n new tokens of a multi-token step
+        x = W.make_paged(w, new_tokens=max(args.queries, 1))
         k_src, v_src = x["k_pool"], x["v_pool"]
-        nblocks = W.block_counts(x["seq_lens_after"], x["block_size"])
+        nblocks = W.block_counts(x["seq_lens_before"] + max(args.queries, 1), x["block_size"])
     else:
         # a ring cache holds W + n - 1 positions plus spare slots, every slot
         # written; a linear cache holds the n new tokens past the spare slots
@@ -442,12 +443,12 @@ def main():
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     nq = args.queries
     win, ring = args.window, args.ring
-    if nq < 1 or (nq > 1 and (args.separate or w.paged or w.T is None)):
-        print("--queries takes n >= 1; n > 1 only with the one-call step on a contiguous "
-              "workload", file=sys.stderr)
+    if nq < 1 or (nq > 1 and (args.separate or (w.T is None and not w.paged))):
+        print("--queries takes n >= 1; n > 1 only with the one-call step", file=sys.stderr)
         sys.exit(2)
-    if args.slice_baseline and (nq < 2 or args.window):
-        print("--slice-baseline needs --queries n > 1 and no window", file=sys.stderr)
+    if args.slice_baseline and (nq < 2 or args.window or w.paged):
+        print("--slice-baseline needs --queries n > 1, no window and a contiguous workload",
+              file=sys.stderr)
         sys.exit(2)
     if win < 0 or (win > 0 and args.separate) or (ring and (win <= 0 or w.paged)):
         print("--window takes W >= 0 with the one-call step; --ring needs --window and a "

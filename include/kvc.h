@@ -137,16 +137,23 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
  *       4-wavefront work-groups take ceil(slots / units) chunks per unit,
  *       so that they fill the slots once.
  *     paged cache: stream mode (KVC_SPLIT_STREAM, below), which stays
- *       balanced whatever the mix of sequence lengths.
- *   KVC_SPLITS_STREAM (-1): stream mode for any layout.  A persistent grid of
- *     as many work-groups as the device keeps resident; all (sequence, KV
- *     head) ranges are laid end to end and every work-group takes an equal
- *     share of the positions.
+ *       balanced whatever the mix of sequence lengths, for the head_dim-128
+ *       decode kernels (up to 32 query rows per KV head) and for the
+ *       multi-row kernel with bf16 rows of 256 dims and at most 16 rows per
+ *       KV head; other multi-row shapes take chunks as on a contiguous cache
+ *       (the multi-row kernel's walk pays a prologue per segment, which
+ *       only wide rows repay).
+ *   KVC_SPLITS_STREAM (-1): stream mode.  A persistent grid of as many
+ *     work-groups as the device keeps resident; all (sequence, KV head)
+ *     ranges are laid end to end and every work-group takes an equal share
+ *     of the positions.  The head_dim-128 decode kernels take it on any
+ *     layout; the multi-row kernel on paged pools when the rows of a KV head
+ *     fit one 4-wavefront work-group (64 rows; 128 below head_dim 256).
  *   n > 0: chunks of chunk_len positions (a multiple of 32) so that about n
  *     chunks cover max_seq_len (KVC_SPLIT_CHUNKS); each (chunk, sequence, KV
  *     head) is one work-group.
- * Stream mode needs the bf16 head_dim-128 kernels, B <= 1024 and
- * B * g * max_seq_len < 2^40; otherwise the automatic choice is chunks.
+ * Stream mode also needs B <= 1024 and B * g * max_seq_len < 2^40;
+ * otherwise the automatic choice is chunks.
  * When results are split, partials go to the workspace and a second kernel
  * merges them.
  *

@@ -114,12 +114,21 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     // p <= 1024: it is used only while B * g * max_seq_len < 2^40.
     const bool small_enough = (long double)B * g * max_seq_len < (long double)(1LL << 40);
     const int slices = row_slices(sc.kind, h / g);
-    const bool can_stream = (sc.kind == kValu || sc.kind == kMfma) && slices == 1 &&
+    // the multi-row kernel streams over paged pools when a unit's rows fit
+    // one 4-wavefront work-group
+    const PrefillShape ps = prefill_shape(h / g, d);
+    const bool prefill_streams = sc.kind == kPrefill && paged && ps.row_blocks == 1 && ps.waves == 4;
+    const bool can_stream = (sc.kind == kValu || sc.kind == kMfma || prefill_streams) && slices == 1 &&
                             B <= kStreamMaxB && small_enough;
     // automatic: paged caches stream (lengths vary); with a sliding window the
-    // ranges are at most W + n - 1 long and nearly equal, so they chunk
-    sc.stream = can_stream &&
-                (num_splits == KVC_SPLITS_STREAM || (num_splits == 0 && paged && !windowed));
+    // ranges are at most W + n - 1 long and nearly equal, so they chunk.  The
+    // multi-row kernel's walk pays a prologue per segment (query tiles, table
+    // window, first step in flight): measured, it beats whole units over
+    // ragged lengths only with bf16 rows of 256 dims and at most 16 rows per
+    // KV head; elsewhere it streams only when asked to.
+    const bool auto_stream = sc.kind != kPrefill || (kv8 == 0 && d == 256 && h / g <= 16);
+    sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM ||
+                               (num_splits == 0 && paged && !windowed && auto_stream));
     sc.auto_chunks = !sc.stream && num_splits <= 0 && sc.kind != kGeneric;
     if (sc.auto_chunks) {
         // workspace bound: every slot of a 256-CU device, 4 work-groups each
@@ -297,12 +306,17 @@ static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len)
         a.nqt = ps.nqt;
         a.waves = ps.waves;
         a.row_blocks = ps.row_blocks;
-        if (sc.auto_chunks) {
+        if (sc.stream) {
+            long P = device_slots(prefill_kernel(ps.nqt, ps.waves, paged, true, a.d, kv_mode(a)), ps.waves);
+            const long pieces = ((long)a.B * a.g * max_len + 255) / 256;
+            if (P > pieces) P = pieces;
+            a.num_wgs = (int)(P < 1 ? 1 : P);
+        } else if (sc.auto_chunks) {
             // chunks per unit that fill the device's slots once, counting
             // the row blocks; when the row blocks alone fill them, one chunk
             // per unit (the kernel walks a long chunk in table windows) and
             // no merge
-            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged, a.d, kv_mode(a)), ps.waves);
+            const long slots = device_slots(prefill_kernel(ps.nqt, ps.waves, paged, false, a.d, kv_mode(a)), ps.waves);
             const long groups = (long)a.B * ps.row_blocks * a.g;
             if (groups >= slots) {
                 sc.plan = Plan{(int)(ceil_div(max_len, kTileTokens) * kTileTokens), 1};

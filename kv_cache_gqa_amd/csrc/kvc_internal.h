@@ -111,8 +111,9 @@ hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s);
 const void* mfma_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8);
 const void* valu_kernel(int m, bool paged, bool stream, int waves, bool gen, int kv8);
 // Multi-row kernel for (16-row query tiles per wavefront, wavefronts per
-// work-group, layout); nullptr when not built.
-const void* prefill_kernel(int nqt, int waves, bool paged, int d, int kv8);
+// work-group, layout, grid: chunks or the stream grid (paged pools with one
+// row block per unit), head dim, cache kind); nullptr when not built.
+const void* prefill_kernel(int nqt, int waves, bool paged, bool stream, int d, int kv8);
 // Whether a call needs the kernels' general features: several query tokens
 // per sequence, a sliding window or a ring cache.
 inline bool general_features(const DecodeArgs& a) { return a.n > 1 || a.window > 0 || a.ring != 0; }

@@ -116,9 +116,11 @@ struct PrefillEngine {
     };
 
     // Rows rb*kRowsPerGroup .. +kRowsPerGroup of unit (b, j) over positions
-    // [s, e); chunk c of the unit's plan.  Called by all 64*W threads.
-    __device__ static void run(const DecodeArgs& a, Shared& sh, int b, int j, int c, int rb, int s,
-                               int e) {
+    // [s, e); results go to `dst` (row 0 of the unit there: a chunk's
+    // records, a stream work-group's record slot, or the final rows).
+    // Called by all 64*W threads; may be called again for another segment.
+    __device__ static void run(const DecodeArgs& a, Shared& sh, int b, int j, int rb, int s, int e,
+                               const SegDst& unit_dst) {
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int G = lane >> 4, col = lane & 15;
         const int row0 = rb * kRowsPerGroup + wave * kRowsPerWave;  // this wavefront's first row
@@ -383,7 +385,9 @@ struct PrefillEngine {
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) lex[qt] = sum_rows4(lex[qt]);
         if (rows <= 0) return;
-        const SegDst dst = chunk_dst(a, b, j, c, row0);
+        SegDst dst = unit_dst;
+        dst.o += (long)row0 * dst.o_stride;
+        dst.lse += (long)row0 * dst.lse_stride;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
             const int qi = 16 * qt + col;
@@ -437,7 +441,24 @@ prefill_mfma(DecodeArgs a) {
         mark_empty_rows(chunk_dst(a, b, j, c, row0), min(a.m - row0, E::kRowsPerGroup), threadIdx.x);
         return;
     }
-    E::run(a, sh, b, j, c, rb, p0, p1);
+    E::run(a, sh, b, j, rb, p0, p1, chunk_dst(a, b, j, c));
+}
+
+// Paged pools whose unit's rows fit one work-group: the persistent,
+// position-balanced grid of kvc_schedule.h (ragged lengths), one segment
+// after another per work-group; partial segments go to the work-group's
+// record slots for the stream merge.
+template <int NQT, int W, int D, int KV8>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerEu)))
+prefill_stream(DecodeArgs a) {
+    using E = PrefillEngine<NQT, W, true, D, KV8>;
+    __shared__ typename E::Shared sh;
+    __shared__ long long cum[kStreamMaxB + 1];
+    stream_prefix(a, cum);
+    stream_walk(a, cum, [&](int b, int j, int s, int e, bool complete, int slot) {
+        const int lo = unit_range(a, a.seq_lens[b]).lo;  // walk offsets are relative to it
+        E::run(a, sh, b, j, 0, lo + s, lo + e, complete ? final_dst(a, b, j) : stream_dst(a, slot));
+    });
 }
 
 template <int NQT, int W, int D, int KV8>
@@ -446,7 +467,15 @@ static const void* prefill_pick(bool paged) {
 }
 
 template <int D, int KV8>
-static const void* prefill_kernel_d(int nqt, int waves, bool paged) {
+static const void* prefill_kernel_d(int nqt, int waves, bool paged, bool stream) {
+    if (stream) {  // paged pools, one row block per unit
+        if (!paged || waves != 4) return nullptr;
+        if (nqt == 1) return (const void*)prefill_stream<1, 4, D, KV8>;
+        if constexpr (D != 256) {
+            if (nqt == 2) return (const void*)prefill_stream<2, 4, D, KV8>;
+        }
+        return nullptr;
+    }
     if (nqt == 1 && waves == 4) return prefill_pick<1, 4, D, KV8>(paged);
     if constexpr (D == 256) {  // 16 rows per wavefront only (64 accumulator registers per query tile)
         if (nqt == 1 && waves == 8) return prefill_pick<1, 8, D, KV8>(paged);
@@ -457,26 +486,28 @@ static const void* prefill_kernel_d(int nqt, int waves, bool paged) {
     return nullptr;
 }
 
-// Kernel for (rows per wavefront tile count NQT, wavefronts W, layout, head
-// dimension d, cache kind: 0 bf16, 1 FP8 with per-KV-head scales).
-const void* prefill_kernel(int nqt, int waves, bool paged, int d, int kv8) {
+// Kernel for (rows per wavefront tile count NQT, wavefronts W, layout, grid
+// (chunks, or the stream grid of a paged pool), head dimension d, cache kind:
+// 0 bf16, 1 FP8 with per-KV-head scales); nullptr when not built.
+const void* prefill_kernel(int nqt, int waves, bool paged, bool stream, int d, int kv8) {
     if (kv8 == 0) {
-        if (d == 64) return prefill_kernel_d<64, 0>(nqt, waves, paged);
-        if (d == 128) return prefill_kernel_d<128, 0>(nqt, waves, paged);
-        if (d == 256) return prefill_kernel_d<256, 0>(nqt, waves, paged);
+        if (d == 64) return prefill_kernel_d<64, 0>(nqt, waves, paged, stream);
+        if (d == 128) return prefill_kernel_d<128, 0>(nqt, waves, paged, stream);
+        if (d == 256) return prefill_kernel_d<256, 0>(nqt, waves, paged, stream);
     } else if (kv8 == 1) {
-        if (d == 64) return prefill_kernel_d<64, 1>(nqt, waves, paged);
-        if (d == 128) return prefill_kernel_d<128, 1>(nqt, waves, paged);
-        if (d == 256) return prefill_kernel_d<256, 1>(nqt, waves, paged);
+        if (d == 64) return prefill_kernel_d<64, 1>(nqt, waves, paged, stream);
+        if (d == 128) return prefill_kernel_d<128, 1>(nqt, waves, paged, stream);
+        if (d == 256) return prefill_kernel_d<256, 1>(nqt, waves, paged, stream);
     }
     return nullptr;
 }
 
 hipError_t launch_prefill_mfma(const DecodeArgs& a, hipStream_t s) {
-    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr, a.d, kv_mode(a));
-    if (fn == nullptr || a.row_blocks < 1 || a.stream) return hipErrorInvalidValue;
+    const void* fn = prefill_kernel(a.nqt, a.waves, a.block_table != nullptr, a.stream != 0, a.d,
+                                    kv_mode(a));
+    if (fn == nullptr || a.row_blocks < 1 || (a.stream && a.row_blocks != 1)) return hipErrorInvalidValue;
     if ((long)a.row_blocks * 16 * a.nqt * a.waves < a.m) return hipErrorInvalidValue;
-    const long wgs = (long)a.num_chunks * a.g * a.B * a.row_blocks;
+    const long wgs = a.stream ? (long)a.num_wgs : (long)a.num_chunks * a.g * a.B * a.row_blocks;
     if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
     void* args[] = {const_cast<DecodeArgs*>(&a)};
     return hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * a.waves), args, 0, s);

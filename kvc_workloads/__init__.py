@@ -165,13 +165,14 @@ def scatter_to_pool(cache: torch.Tensor, lengths: torch.Tensor, block_table: tor
 
 
 def make_paged(w: Workload, seed: Optional[int] = None, lengths: Optional[torch.Tensor] = None,
-               fill: float = 0.0, max_blocks: Optional[int] = None) -> dict:
+               fill: float = 0.0, max_blocks: Optional[int] = None, new_tokens: int = 1) -> dict:
     """Host tensors for one decode step on a paged pool.
 
     Lengths before the step are ``lengths`` (or drawn from w.T_range with
-    w.seed); every sequence owns ceil((len + 1) / block_size) blocks so the
-    appended token has a slot.  Physical blocks are a random permutation
-    (seed w.seed + 1).  Pool slots at positions >= len hold ``fill``.
+    w.seed); every sequence owns ceil((len + new_tokens) / block_size) blocks
+    so that the appended tokens have slots (k_new / v_new below hold one).
+    Physical blocks are a random permutation (seed w.seed + 1).  Pool slots
+    at positions >= len hold ``fill``.
     Returns q, k_pool, v_pool [NB,g,bs,d], block_table [B,max_blocks],
     k_new, v_new, seq_lens_before, seq_lens_after, scale, num_blocks."""
     s = w.seed if seed is None else seed
@@ -179,7 +180,7 @@ def make_paged(w: Workload, seed: Optional[int] = None, lengths: Optional[torch.
     dt = w.torch_dtype
     bs = w.block_size
     lens = seq_lengths(w, s) if lengths is None else lengths.to(torch.int32)
-    table, nb = make_block_table(lens + 1, bs, perm_seed=s + 1, max_blocks=max_blocks)
+    table, nb = make_block_table(lens + new_tokens, bs, perm_seed=s + 1, max_blocks=max_blocks)
     q = randn((w.B, w.h, w.d), dt, gen)
     k_pool = randn((nb, w.g, bs, w.d), dt, gen)
     v_pool = randn((nb, w.g, bs, w.d), dt, gen)
@@ -188,7 +189,7 @@ def make_paged(w: Workload, seed: Optional[int] = None, lengths: Optional[torch.
     # Blank the unwritten tail slots of each sequence's last block(s).
     for b in range(w.B):
         L = int(lens[b].item())
-        nblk = int(((L + 1 + bs - 1) // bs))
+        nblk = int(((L + new_tokens + bs - 1) // bs))
         for lb in range(L // bs, nblk):
             phys = int(table[b, lb].item())
             first = max(L - lb * bs, 0)

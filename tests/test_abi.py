@@ -63,12 +63,27 @@ def test_plan_modes():
     assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
     assert kvc.plan(2, 8, 2, 96, 4096, 0, paged=True)[0] == "chunks"
     assert kvc.plan(2, 8, 2, 128, 4096, kvc.SPLITS_STREAM, dtype=torch.float32)[0] == "chunks"
-    # bf16 head dims 64 and 256: the multi-row kernel, chunks fixed at launch
+    # bf16 head dims 64 and 256: the multi-row kernel.  Paged pools stream
+    # automatically at d = 256 with at most 16 rows per KV head (FP8 not),
+    # and whenever asked while a unit's rows fit one 4-wavefront work-group
+    # (64 rows, or 128 below d = 256); contiguous caches take chunks fixed
+    # at launch.
+    assert kvc.plan(2, 8, 2, 256, 4096, 0, paged=True)[0] == "stream"
+    assert kvc.plan(2, 32, 2, 256, 4096, 0, paged=True)[0] == "stream"
+    assert kvc.plan(2, 8, 2, 256, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 34, 2, 256, 4096, 0, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 8, 2, 64, 4096, 0, paged=True)[0] == "auto_chunks"
     for d in (64, 256):
-        assert kvc.plan(2, 8, 2, d, 4096, 0, paged=True)[0] == "auto_chunks"
+        assert kvc.plan(2, 8, 2, d, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "stream"
+        assert kvc.plan(2, 8, 2, d, 4096, 0)[0] == "auto_chunks"
         assert kvc.plan(2, 8, 8, d, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"
-    # more than 32 query rows per KV head: the multi-row kernel, never stream mode
+    # more than 32 query rows per KV head at d = 128: the multi-row kernel,
+    # chunks unless a paged pool asks for the stream grid
     assert kvc.plan(2, 64, 1, 128, 4096, 0, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "stream"
+    assert kvc.plan(2, 128, 1, 128, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "stream"
+    assert kvc.plan(2, 256, 1, 128, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 128, 1, 256, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"
     # stream mode needs B <= 1024
     assert kvc.plan(2048, 8, 8, 128, 512, 0, paged=True)[0] == "auto_chunks"
@@ -339,15 +354,23 @@ def test_fp8_validation_codes():
 
 def test_fp8_planning_dtype_plans_like_bf16():
     """KVC_FP8_E4M3 in the planning queries (FP8 caches with a scale per KV
-    head): the plans and workspaces of bf16, the same kernel families."""
+    head): the workspaces of bf16, and its plans, the same kernel families,
+    except that a paged bf16 pool at d = 256 with at most 16 rows per KV head
+    streams the multi-row kernel automatically and an FP8 one does not (it
+    was not faster there)."""
     lib = kvc.load_library()
     for shape in [(32, 64, 8, 128, 4112, 0, 0), (64, 32, 8, 128, 8208, 0, 1), (4, 32, 1, 128, 131088, 64, 0),
-                  (3, 8, 2, 128, 5000, 3, 1), (2, 8, 2, 64, 100, -1, 0), (8, 64, 8, 256, 4096, 0, 1)]:
+                  (3, 8, 2, 128, 5000, 3, 1), (2, 8, 2, 64, 100, -1, 0), (8, 64, 8, 256, 4096, 0, 0),
+                  (8, 256, 8, 256, 4096, 0, 1), (8, 64, 8, 256, 4096, -1, 1)]:
         B, h, g, d, L, ns, paged = shape
         assert kvc.plan(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
             kvc.plan(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
         assert kvc.workspace_bytes(B, h, g, d, L, ns, dtype="fp8", paged=bool(paged)) == \
             kvc.workspace_bytes(B, h, g, d, L, ns, dtype=torch.bfloat16, paged=bool(paged))
+    assert kvc.plan(8, 64, 8, 256, 4096, 0, dtype=torch.bfloat16, paged=True)[0] == "stream"
+    assert kvc.plan(8, 64, 8, 256, 4096, 0, dtype="fp8", paged=True)[0] == "auto_chunks"
+    assert kvc.workspace_bytes(8, 64, 8, 256, 4096, 0, dtype="fp8", paged=True) == \
+        kvc.workspace_bytes(8, 64, 8, 256, 4096, 0, dtype=torch.bfloat16, paged=True)
     assert lib.kvc_decode_plan(2, 8, 2, 128, 3, 64, 0, 0, None, None, None) == UNSUPPORTED
 
 
@@ -505,7 +528,8 @@ def test_workspace_query_covers_fp8_plans():
         for paged in (False, True):
             mode, _, chunks = kvc.plan(B, h, g, d, T, 0, dtype=torch.float32, paged=paged)
             assert mode == "chunks", (B, h, g, d, mode)
-            assert kvc.plan(B, h, g, d, T, 0, dtype=torch.bfloat16, paged=paged)[0] == "auto_chunks"
+            assert kvc.plan(B, h, g, d, T, 0, dtype=torch.bfloat16, paged=paged)[0] == (
+                "stream" if paged and d == 256 and h // g <= 16 else "auto_chunks")
             rows = B * h * chunks if chunks > 1 else 0
             need = rows * d * 4 + rows * 4
             for dt in (torch.bfloat16, kvc.FP8_E4M3):

@@ -63,6 +63,41 @@ def test_algorithmic_bytes_paged_counts_the_table():
                                        paged_blocks=int(blocks.sum()))
 
 
+def test_paged_inputs_hold_every_new_token():
+    """A paged multi-token step (bench.py --queries n on a paged workload):
+    each sequence owns blocks for its n new tokens, the slots they land in
+    are blank, and the byte accounting counts their blocks and the n
+    tokens' reads and writes."""
+    w = W.Workload("p", B=5, h=8, g=2, d=16, dtype="bf16", T_range=(0, 70), paged=True, seed=7)
+    n = 21
+    one = W.make_paged(w)
+    x = W.make_paged(w, new_tokens=n, fill=float("nan"))
+    lens = x["seq_lens_before"]
+    assert torch.equal(lens, one["seq_lens_before"])
+    bs = x["block_size"]
+    table = x["block_table"]
+    owned = (table >= 0).sum(dim=1)
+    assert torch.equal(owned, W.block_counts(lens + n, bs))
+    assert x["num_blocks"] == int(W.block_counts(lens + n, bs).sum())
+    for b in range(w.B):
+        L = int(lens[b])
+        for p in range(L, L + n):
+            slot = x["k_pool"][int(table[b, p // bs]), :, p % bs]
+            assert torch.isnan(slot.float()).all(), (b, p)
+        if L > 0:
+            assert not torch.isnan(x["k_pool"][int(table[b, (L - 1) // bs]), :, (L - 1) % bs].float()).any()
+    blocks = W.block_counts(lens + n, bs)
+    after = (lens + n).to(torch.int64)
+    nb = bench.algorithmic_bytes(w, after, blocks, n=n)
+    eb = 2
+    expect = (2 * int(after.sum()) * w.g * w.d * eb          # K/V read (new rows from k_new)
+              + w.B * w.h * n * w.d * eb                      # queries
+              + w.B * w.h * n * (w.d * 4 + 4)                 # out and lse
+              + int(blocks.sum()) * 4 + w.B * 4               # block table, lengths
+              + 2 * w.B * w.g * n * w.d * eb)                 # the new rows written
+    assert nb["fused"] == expect
+
+
 def _write_counters(path, counter, rows):
     with open(path, "w", newline="") as fh:
         wr = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
