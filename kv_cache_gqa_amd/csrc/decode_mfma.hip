@@ -38,10 +38,10 @@
 // of each of the four rows -- one dim of four positions, the MFMA A layout.
 //
 // K and V are read with streaming (non-temporal) loads while the next
-// 32-position sub-tile is in flight: double-buffered registers for 16 bf16
-// query rows, one set reloaded in place for 32 rows and for the 4-wavefront
-// FP8 kernels (register budget and residency at MfmaEngine and
-// MfmaOccupancy below).  At the end of a segment the W wavefront states go to
+// 32-position sub-tile is in flight: double-buffered registers for 16 query
+// rows, one set reloaded in place for 32 rows and for the 4-wavefront FP8
+// kernels with per-head scales and no general features (register budget
+// and residency at MfmaEngine and MfmaOccupancy below).  At the end of a segment the W wavefront states go to
 // LDS and all threads combine them.
 //
 // Two entry points share the segment code: a chunked grid (chunk, KV head,
@@ -117,8 +117,13 @@ struct MfmaEngine {
     static_assert(!kBS || PAGED, "per-block scales need a paged pool");
     // One set of tile registers: with two query tiles (64 accumulator and 32
     // query registers per lane) it lets two wavefronts share a SIMD; in the
-    // 4-wavefront FP8 kernels, three.
-    static constexpr bool kSingleBuffer = NQT >= 2 || (KV8 && W == 4);
+    // 4-wavefront FP8 kernels with a scale per KV head and no general
+    // features, three (measured faster there: paged 0.617 vs 0.582 of
+    // 8 TB/s).  The per-block-scale and general-feature FP8 kernels keep two
+    // sets at two wavefronts per SIMD (block scales 0.521 vs 0.502, a
+    // 1024-position window over a paged pool 0.408 vs 0.321): with one set
+    // the compiler waits for every load in flight before each tile.
+    static constexpr bool kSingleBuffer = NQT >= 2 || (KV8 == 1 && W == 4 && !GEN);
     struct Shared {
         uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
         float4 bsc[kBS ? kMaxTableSlice : 1];      // per block: scale*log2e*K scale, V scale, 1 / V scale
@@ -257,8 +262,12 @@ struct MfmaEngine {
         // K/V read once are streamed (non-temporal loads); when the rows are
         // cut into slices that each read the unit's K/V, ordinary loads keep
         // the lines in the caches for the other slices (measured 20 % faster
-        // there, 10 % slower for single reads).
-        const bool reread = NQT >= 2 && a.slices > 1;
+        // there, 10 % slower for single reads).  Only FP8 pools with
+        // per-block scales take slices (other caches run more than 32 rows
+        // on the multi-row kernel), so the others keep one load form: a
+        // runtime choice puts every load in a branch, after which the
+        // compiler waits for all loads in flight before each tile.
+        const bool reread = NQT >= 2 && kBS && a.slices > 1;
         auto ld16_kv = [&](const void* p) { return reread ? ld16(p) : ld16_stream(p); };
         auto ld8_kv = [&](const void* p) { return reread ? ld8(p) : ld8_stream(p); };
         auto load_k = [&](int t0, TileRegs<kF8>& tr) {
@@ -314,24 +323,35 @@ struct MfmaEngine {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) tr.v[u] = *reinterpret_cast<const uint4*>(vst + 256 + 16 * col);
             } else if constexpr (KV8) {
-                // several new tokens over an FP8 cache: their bf16 rows,
-                // quantised here to the codes the cache receives
+                // several new tokens over an FP8 cache: the wavefront
+                // quantises the tile's new rows once (positions t0 ..
+                // min(t0 + 32, w1) - 1, rows p - raw of k_new / v_new; items
+                // of 8 values spread over its lanes) into its staging area,
+                // row i as 128 K codes then 128 V codes, with the quotient
+                // and encoder of the cache's append; the tile is then read
+                // from there, positions past the last clamped to it.
+                const int nrows = min(t0 + kTileTokens, w1) - t0;
+                for (int it = lane; it < nrows * 32; it += 64) {
+                    const int i = it >> 5, hv = (it >> 4) & 1, ch = it & 15;
+                    const long r = (long)(t0 - raw) + i;
+                    const long si = kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : (long)j;
+                    const float sc = hv ? a.v_scale[si] : a.k_scale[si];
+                    const uint16_t* row = (hv ? VN : KN) + r * kD + 8 * ch;
+                    *reinterpret_cast<uint2*>(vst + i * kVRowBytes + hv * kD + 8 * ch) =
+                        e4m3_encode8(ld16(row), sc);
+                }
+                wave_lds_sync();
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const long r = min(t0 + 16 * tt + col, w1 - 1) - raw;
-                    const float ks_ = a.k_scale[kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : j];
+                    const int i = min(t0 + 16 * tt + col, w1 - 1) - t0;
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const uint2 lo = e4m3_encode8(ld16(KN + r * kD + 64 * hh + 16 * G), ks_);
-                        const uint2 hi = e4m3_encode8(ld16(KN + r * kD + 64 * hh + 16 * G + 8), ks_);
-                        tr.k[tt][hh] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    }
+                    for (int hh = 0; hh < 2; ++hh)
+                        tr.k[tt][hh] = *reinterpret_cast<const uint4*>(vst + i * kVRowBytes + 64 * hh + 16 * G);
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const long r = min(t0 + 4 * u + G, w1 - 1) - raw;
-                    const float vs_ = a.v_scale[kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : j];
-                    tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * col), vs_);
+                    const int i = min(t0 + 4 * u + G, w1 - 1) - t0;
+                    tr.v[u] = *reinterpret_cast<const uint2*>(vst + i * kVRowBytes + kD + 8 * col);
                 }
             } else {
 #pragma unroll
@@ -673,17 +693,17 @@ struct MfmaEngine {
 }  // namespace
 
 // Resident wavefronts per SIMD the register allocator is asked to allow: two
-// (256 registers; it fits them without spills: the 16-query bf16 variant
-// with two sets of tile registers, the 32-query variant with one), three for
-// the single-buffered 4-wavefront FP8 variant with per-head scales (168
-// registers; measured about 5 % faster on paged caches than two; the
-// per-block-scale variants need the registers of two).
-template <int NQT, int W, int KV8>
-struct MfmaOccupancy { static constexpr int kWavesPerEu = (KV8 == 1 && W == 4 && NQT == 1) ? 3 : 2; };
+// (256 registers; it fits them without spills: the 16-query variants with
+// two sets of tile registers, the 32-query variant with one), three for the
+// single-buffered 4-wavefront FP8 variant with per-head scales and no
+// general features (168 registers; measured about 5 % faster on paged
+// caches than two).
+template <int NQT, int W, bool GEN, int KV8>
+struct MfmaOccupancy { static constexpr int kWavesPerEu = (KV8 == 1 && W == 4 && NQT == 1 && !GEN) ? 3 : 2; };
 
 template <int NQT, bool PAGED, int W, bool GEN, int KV8>
 __global__ void __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, KV8>::kWavesPerEu)))
+__attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, GEN, KV8>::kWavesPerEu)))
 decode_mfma_chunked(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
@@ -721,7 +741,7 @@ decode_mfma_chunked(DecodeArgs a) {
 
 template <int NQT, bool PAGED, int W, bool GEN, int KV8>
 __global__ void __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, KV8>::kWavesPerEu)))
+__attribute__((amdgpu_waves_per_eu(MfmaOccupancy<NQT, W, GEN, KV8>::kWavesPerEu)))
 decode_mfma_stream(DecodeArgs a) {
     using E = MfmaEngine<NQT, PAGED, W, GEN, KV8>;
     __shared__ typename E::Shared sh;
