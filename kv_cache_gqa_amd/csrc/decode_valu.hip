@@ -60,7 +60,9 @@ struct ValuEngine {
         float red_m[W][M];
         float red_l[W][M];
         float red_o[W][M][kD];
-        __attribute__((aligned(16))) unsigned char nrow[GEN ? 1 : W][512];  // one new token's rows
+        // one new token's rows; with general features over an FP8 cache, the
+        // codes of a tile of new tokens (32 rows of 128 K then 128 V codes)
+        __attribute__((aligned(16))) unsigned char nrow[GEN && !KV8 ? 1 : W][GEN && KV8 ? 32 * 256 : 512];
     };
 
     // The M query heads of KV head j of sequence b over positions [s, e)
@@ -177,14 +179,29 @@ struct ValuEngine {
                     tr.v[u] = *reinterpret_cast<const uint4*>(rows + 256 + 16 * ds);
                 }
             } else if constexpr (KV8) {
-                // several new tokens over an FP8 cache: their bf16 rows,
-                // quantised here to the codes the cache receives
+                // several new tokens over an FP8 cache: the wavefront
+                // quantises the tile's new rows once (positions t0 ..
+                // min(t0 + 32, w1) - 1, rows p - raw of k_new / v_new; items
+                // of 8 values spread over its lanes) into its LDS area, row
+                // i as 128 K codes then 128 V codes, with the quotient and
+                // encoder of the cache's append; the tile is then read from
+                // there, positions past the last clamped to it.
+                unsigned char* codes = sh.nrow[wave];
+                const int nrows = min(t0 + 32, w1) - t0;
+                for (int it = lane; it < nrows * 32; it += 64) {
+                    const int i = it >> 5, hv = (it >> 4) & 1, ch = it & 15;
+                    const long r = (long)(t0 - raw) + i;
+                    const long si = kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : (long)j;
+                    const float sc = hv ? a.v_scale[si] : a.k_scale[si];
+                    const uint16_t* row = (hv ? VN : KN) + r * kD + 8 * ch;
+                    *reinterpret_cast<uint2*>(codes + i * 256 + hv * kD + 8 * ch) = e4m3_encode8(ld16(row), sc);
+                }
+                wave_lds_sync();
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const long r = min(t0 + 4 * u + tsub, w1 - 1) - raw;
-                    const long si = kBS ? fp8_scale_index(a, b, j, (int)(raw + r)) : (long)j;
-                    tr.k[u] = e4m3_encode8(ld16(KN + r * kD + 8 * ds), a.k_scale[si]);
-                    tr.v[u] = e4m3_encode8(ld16(VN + r * kD + 8 * ds), a.v_scale[si]);
+                    const int i = min(t0 + 4 * u + tsub, w1 - 1) - t0;
+                    tr.k[u] = *reinterpret_cast<const uint2*>(codes + i * 256 + 8 * ds);
+                    tr.v[u] = *reinterpret_cast<const uint2*>(codes + i * 256 + kD + 8 * ds);
                 }
             } else {
 #pragma unroll
