@@ -141,17 +141,25 @@ struct ValuEngine {
         const uint16_t* VN = has_new ? (const uint16_t*)a.v_new + bj * a.n * kD : Vc;
 
         // Positions clamped to the window's last one (in bounds past the end).
+        // The tile's K rows are loaded before its V rows, kept in that order
+        // (FP8 caches, and bf16 without the general features, which measured
+        // faster that way; the bf16 general-feature kernels measured faster
+        // with the order left to the compiler): the scores consume K first,
+        // so a wait for K leaves the V loads in flight.
         auto load_tile = [&](int t0, ValuTile<kF8>& tr) {
+            long rows[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rows[u] = kv_row(min(t0 + 4 * u + tsub, w1 - 1));
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const long row = kv_row(min(t0 + 4 * u + tsub, w1 - 1));
-                if constexpr (KV8) {
-                    tr.k[u] = ld8_stream((const unsigned char*)a.k + row * kD + 8 * ds);
-                    tr.v[u] = ld8_stream((const unsigned char*)a.v + row * kD + 8 * ds);
-                } else {
-                    tr.k[u] = ld16_stream(K + row * kD + 8 * ds);
-                    tr.v[u] = ld16_stream(Vc + row * kD + 8 * ds);
-                }
+                if constexpr (KV8) tr.k[u] = ld8_stream((const unsigned char*)a.k + rows[u] * kD + 8 * ds);
+                else tr.k[u] = ld16_stream(K + rows[u] * kD + 8 * ds);
+            }
+            if constexpr (KV8 || !GEN) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if constexpr (KV8) tr.v[u] = ld8_stream((const unsigned char*)a.v + rows[u] * kD + 8 * ds);
+                else tr.v[u] = ld16_stream(Vc + rows[u] * kD + 8 * ds);
             }
         };
         // The appended tokens' tile at t0 (>= raw): position p is row p - raw
