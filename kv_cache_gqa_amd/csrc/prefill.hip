@@ -16,8 +16,8 @@
 // over one range of positions, 64 positions (two 32-position tiles) per
 // step.  A step's K and V are read from memory once per work-group into LDS
 // (every thread moves 16-byte pieces; the next step's pieces are in
-// registers while this step is computed; two LDS buffers, one barrier per
-// step) and every wavefront reads them there for its own 16*NQT rows, so a
+// registers while this step is computed, and with 256 rows per work-group
+// the step after it is loading too; two LDS buffers, one barrier per step) and every wavefront reads them there for its own 16*NQT rows, so a
 // unit's K/V is read once per row block instead of once per 32 rows.  Work-groups of the row blocks of
 // one unit get ids eight apart: MI355X hands work-group ids to its eight
 // XCDs in turn, so they run on one XCD at about the same time and share the
@@ -373,9 +373,23 @@ struct PrefillEngine {
             int buf = 0;
             for (; t0 < w1; t0 += kSpan) {
                 // a wavefront whose rows see none of the step skips it
-                if (rows > 0 && t0 < hi_w && t0 + kSpan > lo_w) compute_tile(t0, buf);
-                if (t0 + kSpan < w1) stage_tile(buf ^ 1);
-                if (t0 + 2 * kSpan < w1) load_tile(t0 + 2 * kSpan);
+                const bool busy = rows > 0 && t0 < hi_w && t0 + kSpan > lo_w;
+                // 8-wavefront work-groups (256 rows: the products bound the
+                // step) stage the next step into the other LDS buffer (last
+                // read before the previous barrier) and load the one after
+                // it before this step's products, so that those loads are
+                // in flight while it computes (the barrier waits for every
+                // load in flight); the 4-wavefront shapes, bound by memory,
+                // measured faster staging and loading after the products.
+                if constexpr (W == 8) {
+                    if (t0 + kSpan < w1) stage_tile(buf ^ 1);
+                    if (t0 + 2 * kSpan < w1) load_tile(t0 + 2 * kSpan);
+                    if (busy) compute_tile(t0, buf);
+                } else {
+                    if (busy) compute_tile(t0, buf);
+                    if (t0 + kSpan < w1) stage_tile(buf ^ 1);
+                    if (t0 + 2 * kSpan < w1) load_tile(t0 + 2 * kSpan);
+                }
                 __syncthreads();
                 buf ^= 1;
             }
