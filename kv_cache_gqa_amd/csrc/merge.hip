@@ -172,74 +172,91 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
 // partial record of it: record slot 1 of pa when pa's range starts before U
 // (u is then pa's last segment), slot 0 otherwise.  Work-groups with an empty
 // range are skipped.  Length-0 sequences get out = 0, lse = -inf here.
-__device__ __forceinline__ long long wave_sum_ll(long long x) {
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) x += __shfl_xor(x, mask, 64);
-    return x;
-}
+//
+// One work-group per unit: the prefix sums of the lengths and the unit's
+// span of work-groups are found once per unit (64-bit divisions: computed
+// per row they dominated the pass at many rows per unit), the records'
+// slots go to shared memory, and each thread folds one (row, 4 dims) item of
+// the unit's m rows over them, eight records per round trip.  The block has
+// as many threads as items (rounded up to wavefronts, at most 1024); more
+// items loop.  Head dimension a multiple of 4 (64, 128, 256 in stream plans).
+constexpr int kMergeStreamThreads = 1024;
 
-__global__ void __launch_bounds__(256) merge_stream_kernel(DecodeArgs a) {
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (long)a.B * a.h) return;
-    const int lane = threadIdx.x & 63;
-    const int d = a.d, m = a.m;
-    const int b = (int)(row / a.h);
-    const int i = (int)(row % a.h);
-    const int j = i / m, r = i % m;
-    const PosRange ur = unit_range(a, a.seq_lens[b]);
-    const long long L = ur.hi - ur.lo;
-    const bool pairs = (d % 2 == 0) && d <= 128;
-    if (L == 0) {
-        if (pairs) {
-            if (2 * lane < d) *reinterpret_cast<float2*>(a.out + row * d + 2 * lane) = make_float2(0.f, 0.f);
-        } else {
-            for (int dim = lane; dim < d; dim += 64) a.out[row * d + dim] = 0.0f;
+__global__ void __launch_bounds__(kMergeStreamThreads) merge_stream_kernel(DecodeArgs a) {
+    __shared__ long long cum[kStreamMaxB + 1];
+    __shared__ int slot_of[kMergeStreamThreads];  // per record of a batch: q * 2 + slot, or -1
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int b = blockIdx.x / a.g, j = blockIdx.x % a.g;
+    const int m = a.m, d = a.d, nq = d / 4;
+    const int items = m * nq;
+    const long row0 = (long)b * a.h + (long)j * m;
+    stream_prefix(a, cum);  // ends with a barrier
+    if (cum[b + 1] == cum[b]) {
+        for (int it = tid; it < items; it += nthr) {
+            const int r = it / nq, q4 = it - r * nq;
+            *reinterpret_cast<float4*>(a.out + (row0 + r) * d + 4 * q4) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (q4 == 0) a.lse[row0 + r] = kNegInf;
         }
-        if (lane == 0) a.lse[row] = kNegInf;
         return;
     }
-    long long before = 0, all = 0;
-    for (int bb = lane; bb < a.B; bb += 64) {
-        const PosRange rb = unit_range(a, a.seq_lens[bb]);
-        const long long Lb = rb.hi - rb.lo;
-        all += Lb;
-        if (bb < b) before += Lb;
-    }
-    before = wave_sum_ll(before);
-    all = wave_sum_ll(all);
-    const long long P = a.num_wgs;
-    const long long total = (long long)a.g * all;
-    const long long U = (long long)a.g * before + (long long)j * L;
-    const long long pa = stream_owner(U, total, P);
-    const long long pb = stream_owner(U + L - 1, total, P);
-    if (pa == pb) return;  // one work-group covered the whole unit
-    const bool pa_last = stream_start(pa, total, P) < U;
-    auto rec = [&](long long q) -> long long {
-        return (q * 2 + ((q == pa && pa_last) ? 1 : 0)) * m + r;
-    };
-    auto empty = [&](long long q) -> bool {
-        return stream_start(q, total, P) >= stream_start(q + 1, total, P);
-    };
-
-    MergeAcc acc;
-    for (long long q0 = pa; q0 <= pb; q0 += kMergeBatch) {
-        float lse[kMergeBatch], v[kMergeBatch][4];
+    const UnitSpan sp = unit_span(a, cum, b, j);
+    if (sp.pa == sp.pb) return;  // one work-group covered the whole unit
+    for (int it0 = 0; it0 < items; it0 += nthr) {
+        const int it = it0 + tid;
+        const bool act = it < items;
+        const int r = act ? it / nq : 0, q4 = act ? it - r * nq : 0;
+        float M = kNegInf, W = 0.0f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (long long q0 = sp.pa; q0 <= sp.pb; q0 += nthr) {
+            const int cnt = (int)min((long long)nthr, sp.pb - q0 + 1);
+            __syncthreads();  // the previous batch's slots are read
+            if (tid < cnt) {
+                const long long q = q0 + tid;
+                slot_of[tid] = sp.empty(q) ? -1 : (int)sp.record(q, 1, 0);
+            }
+            __syncthreads();
+            if (!act) continue;
+            for (int k0 = 0; k0 < cnt; k0 += kMergeBatch) {
+                float lse[kMergeBatch];
+                float4 x[kMergeBatch];
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-            const long long q = q0 + k;
-            const bool ok = q <= pb && !empty(q);
-            const long long rr = ok ? rec(q) : 0;
-            lse[k] = ok ? a.part_lse[rr] : kNegInf;
-            load_lane(a.part_o + rr * d, ok, lane, d, pairs, v[k]);
+                for (int k = 0; k < kMergeBatch; ++k) {
+                    const int sl = k0 + k < cnt ? slot_of[k0 + k] : -1;
+                    const long rec = (long)(sl < 0 ? 0 : sl) * m + r;
+                    lse[k] = sl >= 0 ? a.part_lse[rec] : kNegInf;
+                    x[k] = sl >= 0 ? *reinterpret_cast<const float4*>(a.part_o + rec * d + 4 * q4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                float bm = M;
+#pragma unroll
+                for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, lse[k]);
+                const float ref = (bm == kNegInf) ? 0.0f : bm;
+                const float f = fast_exp2(M - ref);  // 0 while nothing was added
+                W *= f;
+                o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+#pragma unroll
+                for (int k = 0; k < kMergeBatch; ++k) {
+                    const float w = fast_exp2(lse[k] - ref);  // 0 for absent records
+                    W += w;
+                    o.x += w * x[k].x; o.y += w * x[k].y; o.z += w * x[k].z; o.w += w * x[k].w;
+                }
+                M = bm;
+            }
         }
-        acc.add(lse, v);
+        if (!act) continue;
+        const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+        *reinterpret_cast<float4*>(a.out + (row0 + r) * d + 4 * q4) =
+            make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        if (q4 == 0) a.lse[row0 + r] = W > 0.0f ? (M + fast_log2(W)) * kLn2 : kNegInf;
     }
-    write_row(a, row, lane, pairs, acc);
 }
 
 hipError_t launch_merge_stream(const DecodeArgs& a, hipStream_t s) {
-    const long rows = (long)a.B * a.h;
-    merge_stream_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(a);
+    if (a.d % 4 != 0 || a.B > kStreamMaxB) return hipErrorInvalidValue;
+    const long items = (long)a.m * (a.d / 4);
+    const long rounded = (items + 63) / 64 * 64;
+    const int threads = (int)(rounded < kMergeStreamThreads ? rounded : kMergeStreamThreads);
+    merge_stream_kernel<<<dim3((unsigned)((long)a.B * a.g)), dim3(threads), 0, s>>>(a);
     return hipGetLastError();
 }
 
