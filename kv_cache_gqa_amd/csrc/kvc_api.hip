@@ -239,12 +239,28 @@ static double fill(long wgs, long slots) {
 // Automatic chunking of a contiguous cache.  Two shapes compete:
 //   whole units  one 8-wavefront work-group per (sequence, KV head), no
 //                partial results and no merge pass;
-//   chunks       4-wavefront work-groups, ceil(slots / units) chunks per
-//                unit, merged afterwards.
-// Whole units win when they keep at least as many tiles in flight per CU
+//   chunks       4-wavefront work-groups, several chunks per unit, merged
+//                afterwards.
+// The matrix-core kernels with one query tile and one token per sequence
+// (m <= 16): chunks of about kChunkTarget positions, at least one
+// work-group per CU, and two per unit when each gets at least
+// kMinSplitChunk positions; whole units on 8 wavefronts when they fill the
+// device's slots (>= 7/8 of slot-rounds busy) and either stay one chunk or
+// are bf16 with at least 512 positions per wavefront.  Measured over
+// batches of 4 to 64 sequences of 1024 to 8192 positions (64 or 32 query
+// heads, 8 KV heads): shorter chunks add partial results and merge work,
+// longer ones, or filling every slot once, leave CUs to a tail of long
+// work-groups (FP8 caches at 32 sequences of 4096 positions: 0.692 of
+// 8 TB/s with two chunks per unit against 0.678 for whole units on 8
+// wavefronts; bf16 at 8 sequences of 4096 positions: 0.602 with 4 chunks
+// against 0.550 with the 8 that fill the slots).  Other kernels: whole
+// units win when they keep at least as many tiles in flight per CU
 // (resident wavefronts, counted twice for the 8-wavefront FP8 kernel, which
-// loads two tiles per step) and the grid fills the slots nearly as well
-// (>= 7/8 of slot-rounds busy).
+// loads two tiles per step) and the grid fills the slots nearly as well;
+// chunks fill the slots once.
+constexpr long kChunkTarget = 2560;
+constexpr long kMinSplitChunk = 1024;
+
 struct AutoShape {
     int waves;
     long chunks;
@@ -253,6 +269,21 @@ struct AutoShape {
 static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, bool paged,
                             bool gen, int kv8) {
     const long units = (long)B * g;
+    if (kind == kMfma && m <= 16 && !gen) {
+        long C = ceil_div(max_len, kChunkTarget);
+        const long per_cu = ceil_div(device_cus(), units > 0 ? units : 1);
+        if (C < per_cu) C = per_cu;
+        if (C < 2 && max_len >= 2 * kMinSplitChunk) C = 2;
+        // within the workspace bound of automatic plans
+        const long bound = chunks_for_slots((long)kStreamMaxCUs * kStreamMaxWgPerCu, B, g, max_len);
+        if (C > bound) C = bound;
+        C = clamp_chunks(C, max_len);
+        const void* f8 = kernel_for(kind, m, paged, false, 8, gen, kv8);
+        const long slots8 = f8 != nullptr ? device_slots(f8, 8) : 0;
+        const bool wide = slots8 > 0 && units >= slots8 && fill(units, slots8) * 8.0 >= 7.0;
+        if (wide && (C == 1 || (kv8 == 0 && max_len >= 8 * 512))) return AutoShape{8, 1};
+        return AutoShape{4, C};
+    }
     const void* f4 = kernel_for(kind, m, paged, false, 4, gen, kv8);
     const long slots4 = device_slots(f4, 4);
     AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};

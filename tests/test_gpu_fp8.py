@@ -230,14 +230,15 @@ def test_fp8_full_size_paged():
 
 
 def test_fp8_launch_shape_70b():
-    """The 70B GQA shape with an FP8 cache runs one 8-wavefront work-group
-    per (sequence, KV head) on a 256-CU device (the FP8 8-wavefront kernel
-    keeps two tiles in flight per wavefront), with no merge pass."""
+    """The 70B GQA shape with an FP8 cache runs two chunks of about 2080
+    positions per (sequence, KV head) on 4-wavefront work-groups on a
+    256-CU device (measured faster than one 8-wavefront work-group per
+    unit), merged afterwards."""
     w = W.WORKLOADS["gqa_70b_bf16"]
     waves, wgs, cl, nc = kvc.launch_shape(w.B, w.h, w.g, w.d, w.T + 16, 0, dtype="fp8")
     _log(f"case fp8_launch_shape waves={waves} wgs={wgs} chunks={nc}")
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert (waves, wgs, nc) == (8, w.B * w.g, 1)
+        assert (waves, wgs, nc) == (4, 2 * w.B * w.g, 2)
 
 
 @pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[4], SHAPES[6]],
