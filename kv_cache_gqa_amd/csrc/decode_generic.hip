@@ -3,18 +3,24 @@
 // specialised bf16/d=128 kernels do not cover (the fp32 d=16 workload, the
 // d=1 worked example).
 //
-// One wavefront per (chunk, query head, sequence).  Lane k holds dims k,
-// k+64, k+128, k+192; positions go in batches of eight (one round trip to
-// memory per batch).  A call that appends reads its new tokens (positions
-// seq_lens[b] ..) from k_new / v_new (FP8: as their codes), and the first
-// query row of each KV head's group writes its chunk's new positions into
-// their cache slots.  For each batch the partial dot products are summed
-// across the wave, then the online-softmax update of "KV Cache 优化与注意力
-// 机制加速" (plumephp.com) section 2.2 is applied once for the batch:
-// m' = max(m, max_p s_p), l' = l exp(m - m') + sum_p exp(s_p - m'),
-// acc' = acc exp(m - m') + sum_p exp(s_p - m') V_p, all in base 2.  Query head i reads KV head
-// floor(i*g/h) ("大语言模型研究15——注意力机制优化之KV缓存" (limoncc.com),
-// section 三 3.3).
+// One work-group per (chunk, KV head j and a block of up to 16 of its m
+// query rows, sequence), one wavefront per query row: the wavefronts of a
+// work-group walk the same K/V positions together, so the rows of a KV
+// head's group share each line the first of them brings in, and K/V is read
+// from HBM once per KV head, not once per query head.  Query head i reads
+// KV head floor(i*g/h) ("大语言模型研究15——注意力机制优化之KV缓存"
+// (limoncc.com), section 三 3.3).
+//
+// Lane k holds dims k (head dims up to 64; positions in batches of sixteen)
+// or k, k+64, k+128, k+192 (batches of eight, four for FP8 codes): one
+// round trip to memory per batch.  For each batch the partial dot products
+// are summed across the wave, then the online-softmax update of "KV Cache
+// 优化与注意力机制加速" (plumephp.com) section 2.2 is applied once for the
+// batch: m' = max(m, max_p s_p), l' = l exp(m - m') + sum_p exp(s_p - m'),
+// acc' = acc exp(m - m') + sum_p exp(s_p - m') V_p, all in base 2.  A call
+// that appends reads its new tokens (positions seq_lens[b] ..) from k_new /
+// v_new (FP8: as their codes), and the first query row of each KV head's
+// group writes its chunk's new positions into their cache slots.
 #include "kvc_device.h"
 
 namespace kvc {
@@ -47,15 +53,25 @@ __device__ __forceinline__ float new_value(float x, float scale) {
     else return x;
 }
 
+// Query rows per work-group (one wavefront each).
+constexpr int kGenericRows = 16;
+
 // TQ: query element type; T: cache element type (uint8_t: FP8 E4M3 codes
 // with a float32 scale per KV head, folded into the query and the output;
-// k_new / v_new are then bf16, TQ).
-template <typename TQ, typename T>
-__global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
-    const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x;
+// k_new / v_new are then bf16, TQ).  NK: dims per lane (1: d <= 64; 4).
+// Work-group (c, y, b) with y = j * RB + rb (RB = ceil(m / R) row blocks,
+// R = min(m, kGenericRows) wavefronts): wavefront w takes query head
+// i = j*m + rb*R + w, if that is below (j+1)*m.
+template <typename TQ, typename T, int NK>
+__global__ void __launch_bounds__(64 * kGenericRows) decode_generic_kernel(DecodeArgs a) {
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int R = (int)(blockDim.x >> 6), RB = (a.m + R - 1) / R;
+    const int j = (int)blockIdx.y / RB, rb = (int)blockIdx.y - j * RB;
+    const int r = rb * R + (int)(threadIdx.x >> 6);
+    if (r >= a.m) return;  // the last row block of a group may be partial
+    const int i = j * a.m + r;  // query head: i * g / h = j
+    const int lane = threadIdx.x & 63;
     const int d = a.d;
-    const int j = (int)(((long)i * a.g) / a.h);
     const int raw = a.seq_lens[b];
     const PosRange ur = unit_range(a, raw);  // chunks cover [lo, hi)
     const int c0 = ur.lo + c * a.chunk_len;
@@ -114,9 +130,9 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
             }
         }
     }
-    float qv[4], acc[4];
+    float qv[NK], acc[NK];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
         const int dim = lane + 64 * kk;
         qv[kk] = dim < d ? load_f(q, ((long)b * a.h + i) * d + dim) * (a.scale_log2e * k_sc) : 0.0f;
         acc[kk] = 0.0f;
@@ -124,7 +140,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     float m = kNegInf, l = 0.0f;
     // Positions go in batches of kBatch: the K and V loads of a batch are
     // issued together, so a batch costs one memory round trip.
-    constexpr int kBatch = 8;
+    constexpr int kBatch = NK == 1 ? 16 : (sizeof(T) == 1 ? 4 : 8);  // FP8: room for the conversions
     auto row_of = [&](int p, bool fresh) -> long {
         if (fresh) return new_base + p;  // a row of k_new / v_new
         if (a.block_table != nullptr) {
@@ -135,7 +151,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         return contig_base + cache_slot(a, p);
     };
     for (int pb = p0; pb < p1; pb += kBatch) {
-        float kx[kBatch][4], vx[kBatch][4];
+        float kx[kBatch][NK], vx[kBatch][NK];
         float ksp[kBatch], vsp[kBatch];  // per-block scales of the batch's positions
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -150,7 +166,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
             }
             const float nk = bsc ? ksp[u] : k_sc, nv = bsc ? vsp[u] : v_sc;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < NK; ++kk) {
                 const int dim = lane + 64 * kk;
                 kx[u][kk] = vx[u][kk] = 0.0f;
                 if (dim < d) {
@@ -170,7 +186,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         for (int u = 0; u < kBatch; ++u) {
             float part = 0.0f;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) part += qv[kk] * kx[u][kk];
+            for (int kk = 0; kk < NK; ++kk) part += qv[kk] * kx[u][kk];
             sc[u] = pb + u < p1 ? wave_sum(part) * ksp[u] : kNegInf;
             bmax = fmaxf(bmax, sc[u]);
         }
@@ -178,14 +194,14 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         const float alpha = fast_exp2(m - mnew);  // m = -inf on the first batch -> 0
         l *= alpha;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc[kk] *= alpha;
+        for (int kk = 0; kk < NK; ++kk) acc[kk] *= alpha;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const float pw = fast_exp2(sc[u] - mnew);  // 0 for masked positions
             l += pw;
             const float pwv = pw * vsp[u];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc[kk] += pwv * vx[u][kk];
+            for (int kk = 0; kk < NK; ++kk) acc[kk] += pwv * vx[u][kk];
         }
         m = mnew;
     }
@@ -194,7 +210,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     if (single) {
         const float inv = l > 0.0f ? v_sc / l : 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < NK; ++kk) {
             const int dim = lane + 64 * kk;
             if (dim < d) a.out[row_out * d + dim] = acc[kk] * inv;
         }
@@ -203,7 +219,7 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
         const long prow = row_out * a.num_chunks + c;
         const float inv = l > 0.0f ? v_sc / l : 0.0f;  // l = 0: nothing visible in this chunk
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < NK; ++kk) {
             const int dim = lane + 64 * kk;
             if (dim < d) a.part_o[prow * d + dim] = acc[kk] * inv;
         }
@@ -211,15 +227,22 @@ __global__ void __launch_bounds__(64) decode_generic_kernel(DecodeArgs a) {
     }
 }
 
+int generic_rows_per_wg(int m) { return m < kGenericRows ? m : kGenericRows; }
+
+template <typename TQ, typename T>
+static void launch_generic(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.d <= 64) decode_generic_kernel<TQ, T, 1><<<grid, block, 0, s>>>(a);
+    else decode_generic_kernel<TQ, T, 4><<<grid, block, 0, s>>>(a);
+}
+
 hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s) {
-    dim3 grid((unsigned)a.num_chunks, (unsigned)a.h, (unsigned)a.B);
-    if (a.kv8) {
-        decode_generic_kernel<uint16_t, uint8_t><<<grid, dim3(64), 0, s>>>(a);
-    } else if (dtype == 0) {
-        decode_generic_kernel<float, float><<<grid, dim3(64), 0, s>>>(a);
-    } else {
-        decode_generic_kernel<uint16_t, uint16_t><<<grid, dim3(64), 0, s>>>(a);
-    }
+    const int R = generic_rows_per_wg(a.m), RB = (a.m + R - 1) / R;
+    if (a.waves != R || (long)a.g * RB > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.num_chunks, (unsigned)(a.g * RB), (unsigned)a.B);
+    const dim3 block((unsigned)(64 * R));
+    if (a.kv8) launch_generic<uint16_t, uint8_t>(a, grid, block, s);
+    else if (dtype == 0) launch_generic<float, float>(a, grid, block, s);
+    else launch_generic<uint16_t, uint16_t>(a, grid, block, s);
     return hipGetLastError();
 }
 

@@ -341,7 +341,7 @@ static int check_common(const void* q, const void* k, const void* v, const int32
 static void resolve_launch(DecodeArgs& a, Schedule& sc, bool paged, int max_len) {
     a.stream = sc.stream ? 1 : 0;
     a.num_wgs = 0;
-    a.waves = sc.kind == kGeneric ? 1 : 4;
+    a.waves = sc.kind == kGeneric ? generic_rows_per_wg(a.m) : 4;
     a.slices = row_slices(sc.kind, a.m);
     a.row_blocks = 1;
     a.nqt = 0;
@@ -535,9 +535,10 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     a.kv8 = kv8 ? 1 : 0;
     resolve_launch(a, sc, paged != 0, max_seq_len);
     if (waves) *waves = a.waves;
-    // the generic kernel: one wavefront per query row; the others: per unit
-    // and row slice
-    const int per_chunk = sc.kind == kGeneric ? h : g * a.slices * a.row_blocks;
+    // the generic kernel: per KV head and block of up to 16 query rows (one
+    // wavefront per row); the others: per unit and row slice
+    const int per_chunk = sc.kind == kGeneric ? g * ((a.m + a.waves - 1) / a.waves)
+                                              : g * a.slices * a.row_blocks;
     if (num_wgs) *num_wgs = a.stream ? a.num_wgs : a.num_chunks * per_chunk * B;
     if (chunk_len) *chunk_len = a.stream ? 0 : a.chunk_len;
     if (num_chunks) *num_chunks = a.stream ? 0 : a.num_chunks;

@@ -98,6 +98,8 @@ struct DecodeArgs {
 
 // Kernel families.  Each returns hipGetLastError() after its launch.
 hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s);
+// Query rows (one wavefront each) per work-group of the generic kernel.
+int generic_rows_per_wg(int m);
 hipError_t launch_decode_valu_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma_bf16_d128(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, hipStream_t s);

@@ -185,5 +185,6 @@ def test_head_dims_route_to_the_multi_row_kernel():
         for h, g, n in [(8, 8, 1), (32, 8, 1), (64, 8, 64)]:
             waves = kvc.launch_shape(B=4, h=h * n, g=g, d=d, max_seq_len=2048)[0]
             assert waves in (4, 8), (d, h, n, waves)
-    # fp32 stays on the generic kernel (one wavefront per query head)
-    assert kvc.launch_shape(B=4, h=8, g=2, d=64, max_seq_len=2048, dtype=torch.float32)[0] == 1
+    # fp32 stays on the generic kernel: one work-group per KV head with one
+    # wavefront per query row of its group (h / g = 4 here)
+    assert kvc.launch_shape(B=4, h=8, g=2, d=64, max_seq_len=2048, dtype=torch.float32)[0] == 4
