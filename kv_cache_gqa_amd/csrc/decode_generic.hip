@@ -38,6 +38,28 @@ __device__ __forceinline__ float load_f<uint8_t>(const uint8_t* p, long idx) {
     return e4m3_to_f32(p[idx]);  // FP8 E4M3 code
 }
 
+// Four consecutive elements (index idx .. idx+3, idx a multiple of 4) as
+// floats, in one vector load: 16 bytes of float32, 8 of bf16, 4 of codes.
+template <typename T>
+__device__ __forceinline__ void load4_f(const T* p, long idx, float (&x)[4]);
+template <>
+__device__ __forceinline__ void load4_f<float>(const float* p, long idx, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p + idx);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load4_f<uint16_t>(const uint16_t* p, long idx, float (&x)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p + idx);
+    x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ void load4_f<uint8_t>(const uint8_t* p, long idx, float (&x)[4]) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p + idx);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] = e4m3_to_f32((v >> (8 * t)) & 0xFFu);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
     x = row16_sum(x);
     x += shfl_xor_f(x, 16);
@@ -59,10 +81,14 @@ constexpr int kGenericRows = 16;
 // TQ: query element type; T: cache element type (uint8_t: FP8 E4M3 codes
 // with a float32 scale per KV head, folded into the query and the output;
 // k_new / v_new are then bf16, TQ).  NK: dims per lane (1: d <= 64; 4).
+// LP > 0 (head dims that are multiples of 4): LP lanes per position, four
+// dims each (one vector load per position and tensor), 64 / LP positions
+// side by side, each lane group with its own online-softmax state, merged
+// across the groups at the end; NK is then unused.
 // Work-group (c, y, b) with y = j * RB + rb (RB = ceil(m / R) row blocks,
 // R = min(m, kGenericRows) wavefronts): wavefront w takes query head
 // i = j*m + rb*R + w, if that is below (j+1)*m.
-template <typename TQ, typename T, int NK>
+template <typename TQ, typename T, int NK, int LP>
 __global__ void __launch_bounds__(64 * kGenericRows) decode_generic_kernel(DecodeArgs a) {
     const int c = blockIdx.x, b = blockIdx.z;
     const int R = (int)(blockDim.x >> 6), RB = (a.m + R - 1) / R;
@@ -129,6 +155,108 @@ __global__ void __launch_bounds__(64 * kGenericRows) decode_generic_kernel(Decod
                 }
             }
         }
+    }
+    if constexpr (LP > 0) {
+        // Lane group gs (of PP) takes positions pb + u*PP + gs of batch pb;
+        // lane sub of the group holds dims 4*sub .. 4*sub+3.
+        constexpr int PP = 64 / LP;
+        constexpr int kPasses = sizeof(T) == 1 ? 4 : 8;  // positions per group and batch
+        const int gs = lane / LP, dbase = 4 * (lane % LP);
+        const bool on = dbase < d;  // d is a multiple of 4
+        float qv[4], acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (on) load4_f(q, ((long)b * a.h + i) * d + dbase, qv);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qv[t] = on ? qv[t] * (a.scale_log2e * k_sc) : 0.0f;
+        float m = kNegInf, l = 0.0f;
+        for (int pb = p0; pb < p1; pb += PP * kPasses) {
+            float kx[kPasses][4], vx[kPasses][4], ksp[kPasses], vsp[kPasses];
+#pragma unroll
+            for (int u = 0; u < kPasses; ++u) {
+                const int p = min(pb + u * PP + gs, p1 - 1);  // past the end: the last position (masked)
+                const bool fresh = appends && p >= raw;
+                ksp[u] = vsp[u] = 1.0f;
+                if (bsc) {
+                    const long si = fp8_scale_index(a, b, j, p);
+                    ksp[u] = a.k_scale[si];
+                    vsp[u] = a.v_scale[si];
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) kx[u][t] = vx[u][t] = 0.0f;
+                if (on) {
+                    if (fresh) {
+                        const long src = (new_base + p) * d + dbase;
+                        load4_f((const TN*)a.k_new, src, kx[u]);
+                        load4_f((const TN*)a.v_new, src, vx[u]);
+                        const float nk = bsc ? ksp[u] : k_sc, nv = bsc ? vsp[u] : v_sc;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            kx[u][t] = new_value<T>(kx[u][t], nk);
+                            vx[u][t] = new_value<T>(vx[u][t], nv);
+                        }
+                    } else {
+                        long row;
+                        if (a.block_table != nullptr) {
+                            int phys = a.block_table[(long)b * a.max_blocks + (p >> a.log2_bs)];
+                            phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+                            row = ((long)phys * a.g + j) * a.block_size + (p & (a.block_size - 1));
+                        } else {
+                            row = contig_base + cache_slot(a, p);
+                        }
+                        load4_f(K, row * d + dbase, kx[u]);
+                        load4_f(V, row * d + dbase, vx[u]);
+                    }
+                }
+            }
+            float sc[kPasses];
+            float bmax = kNegInf;
+#pragma unroll
+            for (int u = 0; u < kPasses; ++u) {
+                float part = qv[0] * kx[u][0] + qv[1] * kx[u][1] + qv[2] * kx[u][2] + qv[3] * kx[u][3];
+#pragma unroll
+                for (int off = 1; off < LP; off <<= 1) part += shfl_xor_f(part, off);
+                sc[u] = pb + u * PP + gs < p1 ? part * ksp[u] : kNegInf;
+                bmax = fmaxf(bmax, sc[u]);
+            }
+            // a group may see no position of a batch (the last one)
+            const float mnew = fmaxf(m, bmax);
+            const float ref = mnew == kNegInf ? 0.0f : mnew;
+            const float alpha = fast_exp2(m - ref);  // 0 while nothing was seen
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kPasses; ++u) {
+                const float pw = fast_exp2(sc[u] - ref);  // 0 for masked positions
+                l += pw;
+                const float pwv = pw * vsp[u];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[t] += pwv * vx[u][t];
+            }
+            m = mnew;
+        }
+        // merge the PP groups' states (lanes with the same dims)
+#pragma unroll
+        for (int off = LP; off < 64; off <<= 1) {
+            const float mo = shfl_xor_f(m, off), lo = shfl_xor_f(l, off);
+            float fa, fb, mn;
+            rescale_pair(m, mo, fa, fb, mn);
+            l = l * fa + lo * fb;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = acc[t] * fa + shfl_xor_f(acc[t], off) * fb;
+            m = mn;
+        }
+        const long row_out = (long)b * a.h + i;
+        const float inv = l > 0.0f ? v_sc / l : 0.0f;  // l = 0: nothing visible
+        const float4 o4 = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        if (single) {
+            if (lane < LP && on) *reinterpret_cast<float4*>(a.out + row_out * d + dbase) = o4;
+            if (lane == 0) a.lse[row_out] = l > 0.0f ? (m + fast_log2(l)) * kLn2 : kNegInf;
+        } else {
+            const long prow = row_out * a.num_chunks + c;
+            if (lane < LP && on) *reinterpret_cast<float4*>(a.part_o + prow * d + dbase) = o4;
+            if (lane == 0) a.part_lse[prow] = l > 0.0f ? m + fast_log2(l) : kNegInf;
+        }
+        return;
     }
     float qv[NK], acc[NK];
 #pragma unroll
@@ -229,10 +357,23 @@ __global__ void __launch_bounds__(64 * kGenericRows) decode_generic_kernel(Decod
 
 int generic_rows_per_wg(int m) { return m < kGenericRows ? m : kGenericRows; }
 
+// Head dims that are multiples of 4 take four dims per lane and
+// LP = max(4, d/4 rounded up to a power of 2) lanes per position; others one
+// lane per dim (d <= 64) or four (d > 64).
 template <typename TQ, typename T>
 static void launch_generic(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-    if (a.d <= 64) decode_generic_kernel<TQ, T, 1><<<grid, block, 0, s>>>(a);
-    else decode_generic_kernel<TQ, T, 4><<<grid, block, 0, s>>>(a);
+    if (a.d % 4 == 0) {
+        const int q = a.d / 4;
+        if (q <= 4) decode_generic_kernel<TQ, T, 1, 4><<<grid, block, 0, s>>>(a);
+        else if (q <= 8) decode_generic_kernel<TQ, T, 1, 8><<<grid, block, 0, s>>>(a);
+        else if (q <= 16) decode_generic_kernel<TQ, T, 1, 16><<<grid, block, 0, s>>>(a);
+        else if (q <= 32) decode_generic_kernel<TQ, T, 1, 32><<<grid, block, 0, s>>>(a);
+        else decode_generic_kernel<TQ, T, 1, 64><<<grid, block, 0, s>>>(a);
+    } else if (a.d <= 64) {
+        decode_generic_kernel<TQ, T, 1, 0><<<grid, block, 0, s>>>(a);
+    } else {
+        decode_generic_kernel<TQ, T, 4, 0><<<grid, block, 0, s>>>(a);
+    }
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, int dtype, hipStream_t s) {

@@ -188,3 +188,68 @@ def test_head_dims_route_to_the_multi_row_kernel():
     # fp32 stays on the generic kernel: one work-group per KV head with one
     # wavefront per query row of its group (h / g = 4 here)
     assert kvc.launch_shape(B=4, h=8, g=2, d=64, max_seq_len=2048, dtype=torch.float32)[0] == 4
+
+
+# Head dims outside 64, 128 and 256, and fp32 caches, run on the generic
+# kernel: four dims per lane and 64 / LP positions per wavefront pass when d
+# is a multiple of 4 (d = 20: LP = 8 with three idle lanes per group; 96 and
+# 100: LP = 32; 200: LP = 64), one dim per lane otherwise (d = 6).
+GENERIC_DIMS = [6, 20, 96, 100, 200]
+
+
+def _host_bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.int32) if a.dtype == np.float32 else a
+
+
+def _device_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("d", GENERIC_DIMS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_append_decode_generic_head_dims(d, dtype, paged, num_splits):
+    """Two new tokens per sequence, three query heads per KV head, appended
+    in the same call over ragged lengths with NaN in every unwritten slot:
+    the cache bytes and every output row against the oracle."""
+    h, g, n, bs = 12, 4, 2, 16
+    _log(f"case generic_headdim d={d} {dtype} paged={paged} splits={num_splits}")
+    seed = 1700 + d
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    lens = torch.tensor(BEFORE, dtype=torch.int32)
+    B = len(BEFORE)
+    w = W.Workload("gen", B=B, h=h, g=g, d=d, dtype=dtype, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 1)
+    q = W.randn((B, h, n, d), tdt, gen)
+    k_new = W.randn((B, g, n, d), tdt, gen)
+    v_new = W.randn((B, g, n, d), tdt, gen)
+    x = W.make_contiguous(w, lengths=lens, t_cap=max(BEFORE) + n + 3, fill=float("nan"))
+    if paged:
+        table, nb = W.make_block_table(lens + n, bs, perm_seed=seed + 2, extra_blocks=2)
+        kc = W.scatter_to_pool(x["k_cache"], lens, table, nb, bs, fill=float("nan"))
+        vc = W.scatter_to_pool(x["v_cache"], lens, table, nb, bs, fill=float("nan"))
+    else:
+        table, kc, vc = None, x["k_cache"], x["v_cache"]
+    kd, vd = dev(kc), dev(vc)
+    out, lse = kvc.append_decode_multi(dev(q), dev(k_new), dev(v_new), kd, vd, dev(lens),
+                                       block_table=dev(table) if paged else None, scale=w.scale,
+                                       num_splits=num_splits)
+    torch.cuda.synchronize()
+    ek, ev = oracle.append_multi(k_new, v_new, kc, vc, lens, block_table=table)
+    assert np.array_equal(_device_bits(kd), _host_bits(ek)), "K cache"
+    assert np.array_equal(_device_bits(vd), _host_bits(ev)), "V cache"
+    if dtype == "bf16":
+        k_host, v_host = _to_torch(ek, kc), _to_torch(ev, vc)
+    else:
+        k_host, v_host = torch.from_numpy(ek.copy()), torch.from_numpy(ev.copy())
+    ro, rl = oracle.decode_multi(q, k_host, v_host, lens, w.scale, block_table=table,
+                                 block_size=bs)
+    after = lens + n
+    vmax = attended_vmax_paged(v_host, table, after, bs) if paged else \
+        attended_vmax_contig(v_host, after)
+    e = check_parity(out, lse, ro, rl, vmax, f"generic d={d} {dtype}")
+    _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
