@@ -53,28 +53,32 @@ namespace {
 
 constexpr float kLazyRescale = 8.0f;
 
-// Sizes for head dimension D (64, 128 or 256; bf16 rows of 2*D bytes in
-// 16-byte chunks).
+// Sizes for head dimension D (64, 96, 128 or 256; bf16 rows of 2*D bytes
+// in 16-byte chunks).  Staged rows of 96 dims take the 256-byte pitch of
+// 128-dim rows (chunks 12..15 of a row's slots unused), so that they keep
+// that layout's swizzles.
 template <int D>
 struct PfDims {
     static constexpr int kRowB = 2 * D;                       // bytes of one K or V row
-    static constexpr int kTileB = kTileTokens * kRowB;        // one 32-position tile of K (or V)
+    static constexpr int kPitch = D == 96 ? 256 : kRowB;      // bytes between staged rows in LDS
+    static constexpr int kTileB = kTileTokens * kPitch;       // one staged 32-position tile of K (or V)
     static constexpr int kKs = D / 32;                        // 32-dim steps of Q K^T
     static constexpr int kNt = D / 16;                        // 16-dim tiles of O
 
     // LDS offset of 16-byte chunk c of K row r.  An A-operand read touches
-    // rows 0..15 at one chunk: with rows of 256 or 512 bytes the chunks are
-    // XOR-swizzled by r % 16 (16 different slots of a 256-byte bank row);
-    // with 128-byte rows two rows share a bank row, so the slot follows
-    // (r / 2) % 8 and the row's half does the rest.  No conflict either way.
+    // rows 0..15 at one chunk: with a pitch of 256 or 512 bytes the chunks
+    // are XOR-swizzled by r % 16 (16 different slots of a 256-byte bank row;
+    // a 96-dim row's chunks 0..11 land in slots 0..15); with 128-byte rows
+    // two rows share a bank row, so the slot follows (r / 2) % 8 and the
+    // row's half does the rest.  No conflict either way.
     __device__ static int k_off(int r, int c) {
         const int swz = D == 64 ? (r >> 1) & 7 : r & 15;
-        return r * kRowB + ((c ^ swz) << 4);
+        return r * kPitch + ((c ^ swz) << 4);
     }
     // V rows: the swizzle of the transposing reads, rows R..R+3 (R = 4k) on
     // disjoint 32-byte slices of the 256-byte bank row, chunk pairs (2k,
     // 2k+1) kept adjacent.
-    __device__ static int v_off(int r, int c) { return r * kRowB + ((c ^ ((r & 3) << 1)) << 4); }
+    __device__ static int v_off(int r, int c) { return r * kPitch + ((c ^ ((r & 3) << 1)) << 4); }
 };
 
 // KV8: 0 = bf16 cache; 1 = FP8 E4M3 codes with a float32 scale per KV head.
@@ -108,6 +112,7 @@ struct PrefillEngine {
     static constexpr int kStepPieces = 2 * kSub * kTileTokens * kPPR;  // K and V pieces per step
     static constexpr int kPer = kStepPieces / (64 * W);       // pieces per thread per step
     static_assert(kPer >= 2 && kPer * 64 * W == kStepPieces, "pieces must divide evenly");
+    static_assert(kPer % 2 == 0, "a thread moves as many K pieces as V pieces");
 
     struct Shared {
         uint32_t tbl[PAGED ? kMaxTableSlice : 1];  // per block: row of its first position, head j
@@ -493,6 +498,8 @@ static const void* prefill_kernel_d(int nqt, int waves, bool paged, bool stream)
     if (nqt == 1 && waves == 4) return prefill_pick<1, 4, D, KV8>(paged);
     if constexpr (D == 256) {  // 16 rows per wavefront only (64 accumulator registers per query tile)
         if (nqt == 1 && waves == 8) return prefill_pick<1, 8, D, KV8>(paged);
+    } else if constexpr (D == 96) {  // four wavefronts only (eight would move 3 pieces per thread)
+        if (nqt == 2 && waves == 4) return prefill_pick<2, 4, D, KV8>(paged);
     } else {
         if (nqt == 2 && waves == 4) return prefill_pick<2, 4, D, KV8>(paged);
         if (nqt == 2 && waves == 8) return prefill_pick<2, 8, D, KV8>(paged);
@@ -506,6 +513,7 @@ static const void* prefill_kernel_d(int nqt, int waves, bool paged, bool stream)
 const void* prefill_kernel(int nqt, int waves, bool paged, bool stream, int d, int kv8) {
     if (kv8 == 0) {
         if (d == 64) return prefill_kernel_d<64, 0>(nqt, waves, paged, stream);
+        if (d == 96) return prefill_kernel_d<96, 0>(nqt, waves, paged, stream);
         if (d == 128) return prefill_kernel_d<128, 0>(nqt, waves, paged, stream);
         if (d == 256) return prefill_kernel_d<256, 0>(nqt, waves, paged, stream);
     } else if (kv8 == 1) {
