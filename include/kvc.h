@@ -430,8 +430,8 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
  * is as in the bf16 single-token calls.  Kernels: at d = 128 as for bf16
  * (up to 3 rows per KV head the VALU kernel, 4-32 the matrix-core decode
  * kernel, more the multi-row kernel, which widens the codes to bf16 as it
- * stages each tile in LDS); at d = 64 and 256 the multi-row kernel for any
- * row count; other head dims (d = 96 included) the generic kernel.
+ * stages each tile in LDS); at d = 64, 96 and 256 the multi-row kernel for
+ * any row count; other head dims the generic kernel.
  */
 int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,

@@ -37,14 +37,13 @@ Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
 // 128: up to 3 rows per KV head on the vector ALUs, 4..32 on the matrix-core
 // decode kernel, more on the multi-row kernel (per-block FP8 scales: as
 // 32-row slices of the decode kernel).  bf16 caches and FP8 caches with
-// per-head scales with head_dim 64 or 256, and bf16 caches with head_dim
-// 96: every row count on the multi-row kernel (one K/V read per KV head).
-// Everything else (fp32, other head dims, FP8 with d = 96, per-block FP8
-// scales with d != 128) takes the generic kernel.
+// per-head scales with head_dim 64, 96 or 256: every row count on the
+// multi-row kernel (one K/V read per KV head).  Everything else (fp32,
+// other head dims, per-block FP8 scales with d != 128) takes the generic
+// kernel.
 KernelKind choose_kernel(int dtype, int d, int m, int kv8) {
     if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : (m <= 32 || kv8 == 2 ? kMfma : kPrefill);
-    if (dtype == KVC_BF16 && kv8 != 2 && (d == 64 || d == 256)) return kPrefill;
-    if (dtype == KVC_BF16 && kv8 == 0 && d == 96) return kPrefill;
+    if (dtype == KVC_BF16 && kv8 != 2 && (d == 64 || d == 96 || d == 256)) return kPrefill;
     return kGeneric;
 }
 

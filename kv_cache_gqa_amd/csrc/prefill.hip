@@ -105,7 +105,8 @@ struct PrefillEngine {
     // A piece is what one thread moves with one 16-byte load: 8 bf16
     // elements, or 16 FP8 codes (two staged chunks) when the step has at
     // least one K piece of that size per thread (else 8 codes, 8 bytes).
-    static constexpr bool kWide = KV8 && kSub * kTileTokens * (D / 16) >= 64 * W;
+    // At D = 96 the wide pieces would leave three per thread, so 8 codes.
+    static constexpr bool kWide = KV8 && D != 96 && kSub * kTileTokens * (D / 16) >= 64 * W;
     static constexpr int kPE = kWide ? 16 : 8;                // elements per piece
     static constexpr int kPPR = D / kPE;                      // pieces per row
     static constexpr int kPieceB = KV8 ? kPE : 16;            // cached bytes of one piece
@@ -518,6 +519,7 @@ const void* prefill_kernel(int nqt, int waves, bool paged, bool stream, int d, i
         if (d == 256) return prefill_kernel_d<256, 0>(nqt, waves, paged, stream);
     } else if (kv8 == 1) {
         if (d == 64) return prefill_kernel_d<64, 1>(nqt, waves, paged, stream);
+        if (d == 96) return prefill_kernel_d<96, 1>(nqt, waves, paged, stream);
         if (d == 128) return prefill_kernel_d<128, 1>(nqt, waves, paged, stream);
         if (d == 256) return prefill_kernel_d<256, 1>(nqt, waves, paged, stream);
     }

@@ -59,11 +59,12 @@ def test_plan_modes():
         assert kvc.plan(B, h, g, 128, T, 0) == ("auto_chunks", 0, 0)
         assert kvc.plan(B, h, g, 128, T, 0, paged=True) == ("stream", 0, 0)
         assert kvc.plan(B, h, g, 128, T, kvc.SPLITS_STREAM) == ("stream", 0, 0)
-    # the generic kernel (fp32; bf16 head dims other than 64, 96, 128, 256;
-    # FP8 with d = 96) always chunks
+    # the generic kernel (fp32; bf16 or FP8 head dims other than 64, 96,
+    # 128, 256) always chunks
     assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
     assert kvc.plan(2, 8, 2, 80, 4096, 0, paged=True)[0] == "chunks"
-    assert kvc.plan(2, 8, 2, 96, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "chunks"
+    assert kvc.plan(2, 8, 2, 80, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "chunks"
+    assert kvc.plan(2, 8, 2, 96, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 8, 2, 128, 4096, kvc.SPLITS_STREAM, dtype=torch.float32)[0] == "chunks"
     # bf16 head dims 64, 96 and 256: the multi-row kernel.  Paged pools stream
     # automatically at d = 256 with at most 16 rows per KV head (FP8 not),

@@ -180,8 +180,7 @@ def test_window_head_dims(d, layout, window, n):
 def test_head_dims_route_to_the_multi_row_kernel():
     """bf16 caches with d = 64, 96 and 256 launch the multi-row kernel (a
     work-group of four or eight wavefronts), not the generic one (one
-    wavefront per query row of a KV head; four rows here); FP8 with d = 96
-    stays on the generic kernel."""
+    wavefront per query row of a KV head; four rows here, eight below)."""
     for d in (64, 96, 256):
         for h, g, n in [(8, 8, 1), (32, 8, 1), (64, 8, 64)]:
             waves = kvc.launch_shape(B=4, h=h * n, g=g, d=d, max_seq_len=2048)[0]
@@ -189,7 +188,7 @@ def test_head_dims_route_to_the_multi_row_kernel():
     # fp32 stays on the generic kernel: one work-group per KV head with one
     # wavefront per query row of its group (h / g = 4 here)
     assert kvc.launch_shape(B=4, h=8, g=2, d=64, max_seq_len=2048, dtype=torch.float32)[0] == 4
-    assert kvc.launch_shape(B=4, h=8, g=2, d=96, max_seq_len=2048, dtype="fp8")[0] == 4
+    assert kvc.launch_shape(B=4, h=16, g=2, d=80, max_seq_len=2048, dtype="fp8")[0] == 8
 
 
 # Head dims outside 64, 128 and 256, and fp32 caches, run on the generic
