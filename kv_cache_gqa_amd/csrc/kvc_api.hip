@@ -37,13 +37,13 @@ Plan make_plan(int B, int g, int max_seq_len, int num_splits) {
 // 128: up to 3 rows per KV head on the vector ALUs, 4..32 on the matrix-core
 // decode kernel, more on the multi-row kernel (per-block FP8 scales: as
 // 32-row slices of the decode kernel).  bf16 caches and FP8 caches with
-// per-head scales with head_dim 64, 96 or 256: every row count on the
+// per-head scales with head_dim 64, 80, 96 or 256: every row count on the
 // multi-row kernel (one K/V read per KV head).  Everything else (fp32,
 // other head dims, per-block FP8 scales with d != 128) takes the generic
 // kernel.
 KernelKind choose_kernel(int dtype, int d, int m, int kv8) {
     if (dtype == KVC_BF16 && d == 128) return m <= 3 ? kValu : (m <= 32 || kv8 == 2 ? kMfma : kPrefill);
-    if (dtype == KVC_BF16 && kv8 != 2 && (d == 64 || d == 96 || d == 256)) return kPrefill;
+    if (dtype == KVC_BF16 && kv8 != 2 && (d == 64 || d == 80 || d == 96 || d == 256)) return kPrefill;
     return kGeneric;
 }
 
@@ -59,16 +59,16 @@ static int row_slices(KernelKind kind, int m) { return (kind == kMfma && m > 32)
 // cores) 256 rows per work-group of eight wavefronts, so that each K/V tile
 // staged in LDS serves 256 rows.  Head dimension 256 keeps 16 rows per
 // wavefront (its accumulators take 64 registers per query tile): 128 rows
-// per eight-wavefront work-group beyond 64.  Head dimension 96 keeps four
-// wavefronts (eight would split a step's pieces unevenly): 128 rows per
-// work-group beyond 64.
+// per eight-wavefront work-group beyond 64.  Head dimensions 80 and 96 keep
+// four wavefronts (eight would split a step's pieces unevenly): 128 rows
+// per work-group beyond 64.
 struct PrefillShape {
     int nqt, waves, row_blocks;
 };
 static PrefillShape prefill_shape(int m, int d) {
     if (m <= 64) return {1, 4, 1};
     if (d == 256) return {1, 8, (m + 127) / 128};
-    if (d == 96) return {2, 4, (m + 127) / 128};  // four-wavefront work-groups only
+    if (d == 80 || d == 96) return {2, 4, (m + 127) / 128};  // four-wavefront work-groups only
     if (m <= 128) return {2, 4, 1};
     return {2, 8, (m + 255) / 256};
 }

@@ -53,16 +53,19 @@ namespace {
 
 constexpr float kLazyRescale = 8.0f;
 
-// Sizes for head dimension D (64, 96, 128 or 256; bf16 rows of 2*D bytes
-// in 16-byte chunks).  Staged rows of 96 dims take the 256-byte pitch of
-// 128-dim rows (chunks 12..15 of a row's slots unused), so that they keep
-// that layout's swizzles.
+// Sizes for head dimension D (64, 80, 96, 128 or 256; bf16 rows of 2*D
+// bytes in 16-byte chunks).  The products run over kDP dims, D rounded up to
+// a multiple of 32: at D = 80 dims 80..95 are zero in the staged K rows and
+// in the queries, so they add nothing to the scores.  Staged rows of 80 or
+// 96 dims take the 256-byte pitch of 128-dim rows (the other chunk slots of
+// a row unused), so that they keep that layout's swizzles.
 template <int D>
 struct PfDims {
+    static constexpr int kDP = (D + 31) / 32 * 32;            // dims of the score product
     static constexpr int kRowB = 2 * D;                       // bytes of one K or V row
-    static constexpr int kPitch = D == 96 ? 256 : kRowB;      // bytes between staged rows in LDS
+    static constexpr int kPitch = (D == 80 || D == 96) ? 256 : kRowB;  // bytes between staged rows in LDS
     static constexpr int kTileB = kTileTokens * kPitch;       // one staged 32-position tile of K (or V)
-    static constexpr int kKs = D / 32;                        // 32-dim steps of Q K^T
+    static constexpr int kKs = kDP / 32;                      // 32-dim steps of Q K^T
     static constexpr int kNt = D / 16;                        // 16-dim tiles of O
 
     // LDS offset of 16-byte chunk c of K row r.  An A-operand read touches
@@ -105,10 +108,13 @@ struct PrefillEngine {
     // A piece is what one thread moves with one 16-byte load: 8 bf16
     // elements, or 16 FP8 codes (two staged chunks) when the step has at
     // least one K piece of that size per thread (else 8 codes, 8 bytes).
-    // At D = 96 the wide pieces would leave three per thread, so 8 codes.
-    static constexpr bool kWide = KV8 && D != 96 && kSub * kTileTokens * (D / 16) >= 64 * W;
+    // At D = 80 and 96 the wide pieces would leave an odd count per thread,
+    // so 8 codes.  A staged row has kPPR pieces, the first kReal of them
+    // from the row's D dims, the others (D = 80) zero.
+    static constexpr bool kWide = KV8 && D != 80 && D != 96 && kSub * kTileTokens * (D / 16) >= 64 * W;
     static constexpr int kPE = kWide ? 16 : 8;                // elements per piece
-    static constexpr int kPPR = D / kPE;                      // pieces per row
+    static constexpr int kPPR = Dm::kDP / kPE;                // pieces per staged row
+    static constexpr int kReal = D / kPE;                     // pieces per row that hold its dims
     static constexpr int kPieceB = KV8 ? kPE : 16;            // cached bytes of one piece
     static constexpr int kStepPieces = 2 * kSub * kTileTokens * kPPR;  // K and V pieces per step
     static constexpr int kPer = kStepPieces / (64 * W);       // pieces per thread per step
@@ -148,8 +154,9 @@ struct PrefillEngine {
             const bool ok = qi < rows;
 #pragma unroll
             for (int ks = 0; ks < Dm::kKs; ++ks)
-                qb[qt][ks] = ok ? ld16(Q + ((b * (long)a.h + (long)j * a.m + row0 + qi) * D + 32 * ks + 8 * G))
-                                : make_uint4(0u, 0u, 0u, 0u);
+                qb[qt][ks] = ok && 32 * ks + 8 * G < D
+                                 ? ld16(Q + ((b * (long)a.h + (long)j * a.m + row0 + qi) * D + 32 * ks + 8 * G))
+                                 : make_uint4(0u, 0u, 0u, 0u);
             lim[qt] = visible_len(a, raw, (row0 + qi) % a.n);
             if (ok) {
                 const int wl = window_lo(a, lim[qt]);
@@ -232,6 +239,13 @@ struct PrefillEngine {
                 const int q = tid + (k % kHalf) * 64 * W;
                 const int p = min(t0 + q / kPPR, w1 - 1);
                 const bool isv = k >= kHalf;
+                if constexpr (kReal < kPPR) {
+                    if (q % kPPR >= kReal) {  // padding dims: zero
+                        if constexpr (KV8 && !kWide) pre[k] = make_uint2(0u, 0u);
+                        else pre[k] = make_uint4(0u, 0u, 0u, 0u);
+                        continue;
+                    }
+                }
                 if constexpr (KV8) {
                     const float sc = isv ? v_sc : k_sc;
                     if (appends && p >= raw) {
@@ -499,7 +513,7 @@ static const void* prefill_kernel_d(int nqt, int waves, bool paged, bool stream)
     if (nqt == 1 && waves == 4) return prefill_pick<1, 4, D, KV8>(paged);
     if constexpr (D == 256) {  // 16 rows per wavefront only (64 accumulator registers per query tile)
         if (nqt == 1 && waves == 8) return prefill_pick<1, 8, D, KV8>(paged);
-    } else if constexpr (D == 96) {  // four wavefronts only (eight would move 3 pieces per thread)
+    } else if constexpr (D == 80 || D == 96) {  // four wavefronts only (eight would move 3 pieces per thread)
         if (nqt == 2 && waves == 4) return prefill_pick<2, 4, D, KV8>(paged);
     } else {
         if (nqt == 2 && waves == 4) return prefill_pick<2, 4, D, KV8>(paged);
@@ -514,11 +528,13 @@ static const void* prefill_kernel_d(int nqt, int waves, bool paged, bool stream)
 const void* prefill_kernel(int nqt, int waves, bool paged, bool stream, int d, int kv8) {
     if (kv8 == 0) {
         if (d == 64) return prefill_kernel_d<64, 0>(nqt, waves, paged, stream);
+        if (d == 80) return prefill_kernel_d<80, 0>(nqt, waves, paged, stream);
         if (d == 96) return prefill_kernel_d<96, 0>(nqt, waves, paged, stream);
         if (d == 128) return prefill_kernel_d<128, 0>(nqt, waves, paged, stream);
         if (d == 256) return prefill_kernel_d<256, 0>(nqt, waves, paged, stream);
     } else if (kv8 == 1) {
         if (d == 64) return prefill_kernel_d<64, 1>(nqt, waves, paged, stream);
+        if (d == 80) return prefill_kernel_d<80, 1>(nqt, waves, paged, stream);
         if (d == 96) return prefill_kernel_d<96, 1>(nqt, waves, paged, stream);
         if (d == 128) return prefill_kernel_d<128, 1>(nqt, waves, paged, stream);
         if (d == 256) return prefill_kernel_d<256, 1>(nqt, waves, paged, stream);

@@ -59,14 +59,15 @@ def test_plan_modes():
         assert kvc.plan(B, h, g, 128, T, 0) == ("auto_chunks", 0, 0)
         assert kvc.plan(B, h, g, 128, T, 0, paged=True) == ("stream", 0, 0)
         assert kvc.plan(B, h, g, 128, T, kvc.SPLITS_STREAM) == ("stream", 0, 0)
-    # the generic kernel (fp32; bf16 or FP8 head dims other than 64, 96,
+    # the generic kernel (fp32; bf16 or FP8 head dims other than 64, 80, 96,
     # 128, 256) always chunks
     assert kvc.plan(1, 4, 2, 16, 48, 0, dtype=torch.float32)[0] == "chunks"
-    assert kvc.plan(2, 8, 2, 80, 4096, 0, paged=True)[0] == "chunks"
-    assert kvc.plan(2, 8, 2, 80, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "chunks"
-    assert kvc.plan(2, 8, 2, 96, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 8, 2, 112, 4096, 0, paged=True)[0] == "chunks"
+    assert kvc.plan(2, 8, 2, 112, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "chunks"
+    for d in (80, 96):
+        assert kvc.plan(2, 8, 2, d, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 8, 2, 128, 4096, kvc.SPLITS_STREAM, dtype=torch.float32)[0] == "chunks"
-    # bf16 head dims 64, 96 and 256: the multi-row kernel.  Paged pools stream
+    # bf16 head dims 64, 80, 96 and 256: the multi-row kernel.  Paged pools stream
     # automatically at d = 256 with at most 16 rows per KV head (FP8 not),
     # and whenever asked while a unit's rows fit one 4-wavefront work-group
     # (64 rows, or 128 below d = 256); contiguous caches take chunks fixed
@@ -76,8 +77,9 @@ def test_plan_modes():
     assert kvc.plan(2, 8, 2, 256, 4096, 0, dtype=kvc.FP8_E4M3, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 34, 2, 256, 4096, 0, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 8, 2, 64, 4096, 0, paged=True)[0] == "auto_chunks"
+    assert kvc.plan(2, 8, 2, 80, 4096, 0, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 8, 2, 96, 4096, 0, paged=True)[0] == "auto_chunks"
-    for d in (64, 96, 256):
+    for d in (64, 80, 96, 256):
         assert kvc.plan(2, 8, 2, d, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "stream"
         assert kvc.plan(2, 8, 2, d, 4096, 0)[0] == "auto_chunks"
         assert kvc.plan(2, 8, 8, d, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"

@@ -22,9 +22,10 @@ from gpu_util import check_parity, dev
 pytestmark = pytest.mark.gpu
 
 NAN_CODE = 0x7F
-# (id, h, g, n); head dim 128 unless the id says d64 / d96 / d256.  Rows
-# per KV head (h / g) * n: 1-3 the VALU kernel, 4-32 the matrix-core decode
-# kernel, more (and every row count at d = 64, 96, 256) the multi-row kernel.
+# (id, h, g, n); head dim 128 unless the id says d64 / d80 / d96 / d256.
+# Rows per KV head (h / g) * n: 1-3 the VALU kernel, 4-32 the matrix-core
+# decode kernel, more (and every row count at d = 64, 80, 96, 256) the
+# multi-row kernel.
 SHAPES = [
     ("valu_rows2", 4, 4, 2),
     ("valu_rows3", 6, 2, 1),
@@ -35,6 +36,8 @@ SHAPES = [
     ("multirow_rows96", 4, 2, 48),
     ("multirow_rows320", 32, 2, 20),
     ("multirow_d64_rows6", 6, 2, 2),
+    ("multirow_d80_rows6", 6, 2, 2),
+    ("multirow_d80_rows160", 16, 2, 20),
     ("multirow_d96_rows6", 6, 2, 2),
     ("multirow_d96_rows160", 16, 2, 20),
     ("multirow_d256_rows4", 8, 2, 1),
@@ -43,7 +46,10 @@ SHAPES = [
 
 
 def _head_dim(name):
-    return 64 if "d64" in name else (96 if "d96" in name else (256 if "d256" in name else 128))
+    for d in (64, 80, 96, 256):
+        if f"d{d}_" in name:
+            return d
+    return 128
 BEFORE = [0, 1, 15, 33, 500, 4096]
 
 

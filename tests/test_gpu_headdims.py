@@ -1,5 +1,5 @@
-"""GPU parity of bf16 caches with head dimension 64, 96 and 256, which run on
-the multi-row matrix-core kernel for every row count (one K/V read per KV head;
+"""GPU parity of bf16 caches with head dimension 64, 80, 96 and 256, which run
+on the multi-row matrix-core kernel for every row count (one K/V read per KV head;
 rows = query heads per KV head x new tokens):
 
 * one query row (MHA) up to 320 rows per KV head (the four work-group
@@ -68,7 +68,7 @@ def _case(h, g, n, d, paged, seed, before=BEFORE, bs=16):
     return w, lens, q, k_new, v_new, kc, vc, table
 
 
-@pytest.mark.parametrize("d", [64, 96, 256])
+@pytest.mark.parametrize("d", [64, 80, 96, 256])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("num_splits", [0, 3])
@@ -94,7 +94,7 @@ def test_append_decode_head_dims(d, shape, paged, num_splits):
     _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
 
 
-@pytest.mark.parametrize("d", [64, 96, 256])
+@pytest.mark.parametrize("d", [64, 80, 96, 256])
 @pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[4]], ids=[SHAPES[1][0], SHAPES[4][0]])
 def test_decode_head_dims_over_filled_cache(d, shape):
     """The new tokens already in the cache; seq_lens counts them.  One token:
@@ -118,7 +118,7 @@ def test_decode_head_dims_over_filled_cache(d, shape):
     check_parity(out, lse, ro, rl, attended_vmax_contig(v_host, before + n), f"d={d} {name}")
 
 
-@pytest.mark.parametrize("d", [64, 96, 256])
+@pytest.mark.parametrize("d", [64, 80, 96, 256])
 @pytest.mark.parametrize("layout", ["linear", "ring", "paged"])
 @pytest.mark.parametrize("window,n", [(1, 1), (40, 4), (300, 33)])
 def test_window_head_dims(d, layout, window, n):
@@ -178,24 +178,26 @@ def test_window_head_dims(d, layout, window, n):
 
 
 def test_head_dims_route_to_the_multi_row_kernel():
-    """bf16 caches with d = 64, 96 and 256 launch the multi-row kernel (a
+    """bf16 caches with d = 64, 80, 96 and 256 launch the multi-row kernel (a
     work-group of four or eight wavefronts), not the generic one (one
     wavefront per query row of a KV head; four rows here, eight below)."""
-    for d in (64, 96, 256):
+    for d in (64, 80, 96, 256):
         for h, g, n in [(8, 8, 1), (32, 8, 1), (64, 8, 64)]:
             waves = kvc.launch_shape(B=4, h=h * n, g=g, d=d, max_seq_len=2048)[0]
             assert waves in (4, 8), (d, h, n, waves)
     # fp32 stays on the generic kernel: one work-group per KV head with one
     # wavefront per query row of its group (h / g = 4 here)
     assert kvc.launch_shape(B=4, h=8, g=2, d=64, max_seq_len=2048, dtype=torch.float32)[0] == 4
-    assert kvc.launch_shape(B=4, h=16, g=2, d=80, max_seq_len=2048, dtype="fp8")[0] == 8
+    assert kvc.launch_shape(B=4, h=16, g=2, d=112, max_seq_len=2048, dtype="fp8")[0] == 8
 
 
-# Head dims outside 64, 128 and 256, and fp32 caches, run on the generic
-# kernel: four dims per lane and 64 / LP positions per wavefront pass when d
-# is a multiple of 4 (d = 20: LP = 8 with three idle lanes per group; 96 and
-# 100: LP = 32; 200: LP = 64), one dim per lane otherwise (d = 6).
-GENERIC_DIMS = [6, 20, 96, 100, 200]
+# Head dims outside 64, 80, 96, 128 and 256, and fp32 caches, run on the
+# generic kernel: four dims per lane and 64 / LP positions per wavefront pass
+# when d is a multiple of 4 (d = 20: LP = 8 with three idle lanes per group;
+# 100 and 112: LP = 32; 200: LP = 64), one dim per lane otherwise (d = 6).
+# bf16 caches with d = 96 take the multi-row kernel here, fp32 ones the
+# generic kernel.
+GENERIC_DIMS = [6, 20, 96, 100, 112, 200]
 
 
 def _host_bits(a: np.ndarray) -> np.ndarray:
