@@ -314,7 +314,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_70b_bf16")
     ap.add_argument("--head-dim", type=int, default=None,
-                    help="override the workload's head dimension (bf16 caches: 64, 96, 128 and 256 run "
+                    help="override the workload's head dimension (bf16 caches: 64, 80, 96, 128 and 256 run "
                          "on the matrix-core kernels, other values on the generic kernel)")
     ap.add_argument("--num-splits", type=int, default=None,
                     help="override the workload's split count (0 = library's choice)")

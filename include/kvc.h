@@ -325,9 +325,9 @@ size_t kvc_noalloc_scratch_bytes(void);
  * Kernels by rows per KV head, r = (h / g) * n, for bf16 with d = 128: r <= 3
  * the VALU kernel; 4 <= r <= 32 the matrix-core decode kernel; r > 32 the
  * multi-row matrix-core kernel, which stages each K/V tile in LDS once for
- * up to 256 rows (ceil(r / 256) work-groups per unit, 128 at d = 96 and
- * 256).  bf16 with d = 64, 96 or 256: the multi-row kernel for any r.  fp32
- * or other head dims take the generic kernel for any r.
+ * up to 256 rows (ceil(r / 256) work-groups per unit, 128 at d = 80, 96 and
+ * 256).  bf16 with d = 64, 80, 96 or 256: the multi-row kernel for any r.
+ * fp32 or other head dims take the generic kernel for any r.
  */
 int kvc_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* seq_lens, int B, int h, int g, int d, int n,
@@ -430,8 +430,8 @@ int kvc_append_decode_attention_window_paged(const void* q, const void* k_new, c
  * is as in the bf16 single-token calls.  Kernels: at d = 128 as for bf16
  * (up to 3 rows per KV head the VALU kernel, 4-32 the matrix-core decode
  * kernel, more the multi-row kernel, which widens the codes to bf16 as it
- * stages each tile in LDS); at d = 64, 96 and 256 the multi-row kernel for
- * any row count; other head dims the generic kernel.
+ * stages each tile in LDS); at d = 64, 80, 96 and 256 the multi-row kernel
+ * for any row count; other head dims the generic kernel.
  */
 int kvc_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                    const float* k_scale, const float* v_scale, const int32_t* block_table,
