@@ -138,11 +138,12 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
  *       so that they fill the slots once.
  *     paged cache: stream mode (KVC_SPLIT_STREAM, below), which stays
  *       balanced whatever the mix of sequence lengths, for the head_dim-128
- *       decode kernels (up to 32 query rows per KV head) and for the
- *       multi-row kernel with bf16 rows of 256 dims and at most 16 rows per
- *       KV head; other multi-row shapes take chunks as on a contiguous cache
- *       (the multi-row kernel's walk pays a prologue per segment, which
- *       only wide rows repay).
+ *       decode kernels (up to 32 query rows per KV head; FP8 caches up to
+ *       16) and for the multi-row kernel with bf16 rows of 256 dims and at
+ *       most 16 rows per KV head; other shapes take chunks as on a
+ *       contiguous cache (the multi-row kernel's walk pays a prologue per
+ *       segment, which only wide rows repay; the FP8 decode kernel with two
+ *       query tiles measured faster chunked).
  *   KVC_SPLITS_STREAM (-1): stream mode.  A persistent grid of as many
  *     work-groups as the device keeps resident; all (sequence, KV head)
  *     ranges are laid end to end and every work-group takes an equal share

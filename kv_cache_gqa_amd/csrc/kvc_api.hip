@@ -129,8 +129,15 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     // multi-row kernel's walk pays a prologue per segment (query tiles, table
     // window, first step in flight): measured, it beats whole units over
     // ragged lengths only with bf16 rows of 256 dims and at most 16 rows per
-    // KV head; elsewhere it streams only when asked to.
-    const bool auto_stream = sc.kind != kPrefill || (kv8 == 0 && d == 256 && h / g <= 16);
+    // KV head; elsewhere it streams only when asked to.  FP8 caches with two
+    // query tiles (17-32 rows per KV head) on the decode kernel also chunk:
+    // over the 64-sequence paged pool with 8 tokens per sequence, 3 chunks
+    // per unit took 164 us (per-head scales) and 189 us (per-block scales)
+    // against 241 us and 388 us streamed; with per-block scales the stream
+    // kernel's registers leave one wavefront per SIMD.
+    const bool fp8_two_tiles = kv8 != 0 && sc.kind == kMfma && h / g > 16;
+    const bool auto_stream = (sc.kind != kPrefill && !fp8_two_tiles) ||
+                             (sc.kind == kPrefill && kv8 == 0 && d == 256 && h / g <= 16);
     sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM ||
                                (num_splits == 0 && paged && !windowed && auto_stream));
     sc.auto_chunks = !sc.stream && num_splits <= 0 && sc.kind != kGeneric;

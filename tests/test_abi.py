@@ -91,6 +91,13 @@ def test_plan_modes():
     assert kvc.plan(2, 256, 1, 128, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 128, 1, 256, 4096, kvc.SPLITS_STREAM, paged=True)[0] == "auto_chunks"
     assert kvc.plan(2, 64, 1, 128, 4096, kvc.SPLITS_STREAM)[0] == "auto_chunks"
+    # FP8 caches with 17-32 rows per KV head on the decode kernel (two query
+    # tiles) chunk on paged pools; up to 16 rows and bf16 stream
+    for kv in (kvc.FP8_E4M3, torch.bfloat16):
+        want = "auto_chunks" if kv == kvc.FP8_E4M3 else "stream"
+        assert kvc.plan(64, 32, 1, 128, 8208, 0, dtype=kv, paged=True)[0] == want
+        assert kvc.plan(64, 24, 1, 128, 8208, 0, dtype=kv, paged=True)[0] == want
+        assert kvc.plan(64, 16, 1, 128, 8208, 0, dtype=kv, paged=True)[0] == "stream"
     # stream mode needs B <= 1024
     assert kvc.plan(2048, 8, 8, 128, 512, 0, paged=True)[0] == "auto_chunks"
     # chunks: a multiple of 32, covering max_seq_len, at most 4096
