@@ -148,8 +148,10 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
  *     work-groups as the device keeps resident; all (sequence, KV head)
  *     ranges are laid end to end and every work-group takes an equal share
  *     of the positions.  The head_dim-128 decode kernels take it on any
- *     layout; the multi-row kernel on paged pools when the rows of a KV head
- *     fit one 4-wavefront work-group (64 rows; 128 below head_dim 256).
+ *     layout (FP8 pools with per-block scales up to 16 query rows per KV
+ *     head; with more they take chunks); the multi-row kernel on paged
+ *     pools when the rows of a KV head fit one 4-wavefront work-group (64
+ *     rows; 128 below head_dim 256).
  *   n > 0: chunks of chunk_len positions (a multiple of 32) so that about n
  *     chunks cover max_seq_len (KVC_SPLIT_CHUNKS); each (chunk, sequence, KV
  *     head) is one work-group.

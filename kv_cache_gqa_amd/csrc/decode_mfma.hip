@@ -780,9 +780,16 @@ static const void* mfma_chunked_kv(bool gen) {
 
 template <int NQT, bool PG, int WV>
 static const void* mfma_pick(bool stream, bool gen, int kv8) {
-    if (kv8 == 2) {  // per-block scales: paged pools only
-        if constexpr (PG) return mfma_pick_kv<NQT, PG, WV, 2>(stream, gen);
-        else return nullptr;
+    if (kv8 == 2) {  // per-block scales: paged pools only; chunks only with two query tiles
+        if constexpr (PG && NQT == 2) {
+            if (stream) return nullptr;
+            return gen ? (const void*)decode_mfma_chunked<NQT, PG, WV, true, 2>
+                       : (const void*)decode_mfma_chunked<NQT, PG, WV, false, 2>;
+        } else if constexpr (PG) {
+            return mfma_pick_kv<NQT, PG, WV, 2>(stream, gen);
+        } else {
+            return nullptr;
+        }
     }
     return kv8 ? mfma_pick_kv<NQT, PG, WV, 1>(stream, gen) : mfma_pick_kv<NQT, PG, WV, 0>(stream, gen);
 }

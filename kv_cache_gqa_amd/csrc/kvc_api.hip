@@ -122,8 +122,12 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     // one 4-wavefront work-group
     const PrefillShape ps = prefill_shape(h / g, d);
     const bool prefill_streams = sc.kind == kPrefill && paged && ps.row_blocks == 1 && ps.waves == 4;
+    // FP8 caches with per-block scales and two query tiles have no stream
+    // kernel: its registers (tile scales on top of two query tiles) left one
+    // wavefront per SIMD, half the grid the occupancy query sized it for.
+    const bool fp8_two_tiles = kv8 != 0 && sc.kind == kMfma && h / g > 16;
     const bool can_stream = (sc.kind == kValu || sc.kind == kMfma || prefill_streams) && slices == 1 &&
-                            B <= kStreamMaxB && small_enough;
+                            B <= kStreamMaxB && small_enough && !(fp8_two_tiles && kv8 == 2);
     // automatic: paged caches stream (lengths vary); with a sliding window the
     // ranges are at most W + n - 1 long and nearly equal, so they chunk.  The
     // multi-row kernel's walk pays a prologue per segment (query tiles, table
@@ -133,9 +137,8 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     // query tiles (17-32 rows per KV head) on the decode kernel also chunk:
     // over the 64-sequence paged pool with 8 tokens per sequence, 3 chunks
     // per unit took 164 us (per-head scales) and 189 us (per-block scales)
-    // against 241 us and 388 us streamed; with per-block scales the stream
-    // kernel's registers leave one wavefront per SIMD.
-    const bool fp8_two_tiles = kv8 != 0 && sc.kind == kMfma && h / g > 16;
+    // against 241 us and 388 us streamed (the per-block-scale stream kernel
+    // has since been dropped, above).
     const bool auto_stream = (sc.kind != kPrefill && !fp8_two_tiles) ||
                              (sc.kind == kPrefill && kv8 == 0 && d == 256 && h / g <= 16);
     sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM ||

@@ -75,9 +75,11 @@ def _vmax(vc, vs, table, before, n, window, bs):
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
 @pytest.mark.parametrize("window", [0, 37])
-@pytest.mark.parametrize("num_splits", [0, 3])
+@pytest.mark.parametrize("num_splits", [0, 3, kvc.SPLITS_STREAM])
 @pytest.mark.parametrize("bs", [8, 16])
 def test_append_decode_block_scaled(shape, window, num_splits, bs):
+    """Every kernel family; the stream grid where asked for (up to 16 rows
+    per KV head: with two query tiles a request for it takes chunks)."""
     name, h, g, n, d = shape
     _log(f"case fp8_blocks {name} n={n} W={window} splits={num_splits} bs={bs}")
     before, q, k_new, v_new, kc, vc, ks, vs, table = _case(h, g, n, d, 1500, bs)
