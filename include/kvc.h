@@ -487,6 +487,9 @@ int kvc_append_decode_attention_fp8_paged(const void* q, const void* k_new, cons
  *   those codes' values, so they give what writing the codes and then the
  *   non-appending call gives.
  *   Attention is over the dequantised values code * scale.
+ *   Splits: with n > 1 an automatic split (num_splits = 0) of a paged pool
+ *   takes chunks, not the stream grid (measured faster there); the plan
+ *   queries, which take h * n and no n, describe the single-token call.
  */
 int kvc_decode_attention_fp8_multi(const void* q, const void* k_cache, const void* v_cache,
                                    const float* k_scale, const float* v_scale,

@@ -5,6 +5,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kvc_internal.h"
@@ -89,6 +90,13 @@ struct Schedule {
     Plan plan;
 };
 
+// Largest automatic chunk over a paged pool (whose lengths are ragged) when
+// it takes chunks: measured over the 64-sequence pool of 128-8192 positions
+// with FP8 codes and 2 or 4 new tokens per sequence, 3 chunks of 2 688
+// positions took 124 and 137 us per call against 146 and 151 us for 2 of
+// 4 032 (per-block scales, 8 tokens: 189 against 206 us).
+constexpr long kPagedChunk = 2816;
+
 static long clamp_chunks(long C, int max_seq_len) {
     const long lo = ceil_div(max_seq_len, kMaxChunk);
     const long hi = ceil_div(max_seq_len, kTileTokens);
@@ -110,8 +118,12 @@ static long chunks_for_slots(long slots, int B, int g, int max_seq_len) {
     return clamp_chunks(ceil_div(slots, units > 0 ? units : 1), max_seq_len);
 }
 
+// prefer_chunks: the call's position ranges suit chunks better than the
+// stream grid even on a paged pool (sliding windows: ranges of at most
+// W + n - 1 positions, nearly equal; FP8 caches with several new tokens per
+// sequence: measured faster chunked).
 static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq_len,
-                              int num_splits, bool paged, bool windowed = false, int kv8 = 0) {
+                              int num_splits, bool paged, bool prefer_chunks = false, int kv8 = 0) {
     Schedule sc;
     sc.kind = choose_kernel(dtype, d, h / g, kv8);
     // Stream mode keeps global positions in 64-bit products p * total with
@@ -128,8 +140,7 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     const bool fp8_two_tiles = kv8 != 0 && sc.kind == kMfma && h / g > 16;
     const bool can_stream = (sc.kind == kValu || sc.kind == kMfma || prefill_streams) && slices == 1 &&
                             B <= kStreamMaxB && small_enough && !(fp8_two_tiles && kv8 == 2);
-    // automatic: paged caches stream (lengths vary); with a sliding window the
-    // ranges are at most W + n - 1 long and nearly equal, so they chunk.  The
+    // automatic: paged caches stream (lengths vary) unless prefer_chunks.  The
     // multi-row kernel's walk pays a prologue per segment (query tiles, table
     // window, first step in flight): measured, it beats whole units over
     // ragged lengths only with bf16 rows of 256 dims and at most 16 rows per
@@ -142,7 +153,7 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
     const bool auto_stream = (sc.kind != kPrefill && !fp8_two_tiles) ||
                              (sc.kind == kPrefill && kv8 == 0 && d == 256 && h / g <= 16);
     sc.stream = can_stream && (num_splits == KVC_SPLITS_STREAM ||
-                               (num_splits == 0 && paged && !windowed && auto_stream));
+                               (num_splits == 0 && paged && !prefer_chunks && auto_stream));
     sc.auto_chunks = !sc.stream && num_splits <= 0 && sc.kind != kGeneric;
     if (sc.auto_chunks) {
         // workspace bound: every slot of a 256-CU device, 4 work-groups
@@ -150,6 +161,7 @@ static Schedule make_schedule(int B, int h, int g, int d, int dtype, int max_seq
         // two rounds); plan_for_chunks grows with the count asked for
         long bound = chunks_for_slots((long)kStreamMaxCUs * kStreamMaxWgPerCu, B * slices, g, max_seq_len);
         if (sc.kind == kValu) bound = clamp_chunks(2 * bound, max_seq_len);
+        if (paged) bound = clamp_chunks(std::max(bound, ceil_div(max_seq_len, kPagedChunk)), max_seq_len);
         sc.plan = plan_for_chunks(max_seq_len, bound);
     } else {
         sc.plan = make_plan(B, g, max_seq_len, num_splits > 0 ? num_splits : 0);
@@ -171,8 +183,8 @@ static size_t workspace_for(int B, int h, int g, int d, const Schedule& sc) {
 
 // Workspace a call needs, the largest over the schedules one size query
 // stands for: for automatic splits of a paged cache, both schedules it may
-// take (stream, or chunks under a sliding window), so that one query serves
-// windowed and plain calls; and bf16 and FP8 caches alike (FP8 calls take q
+// take (stream, or chunks when the call prefers them), so that one query
+// serves every call; and bf16 and FP8 caches alike (FP8 calls take q
 // in bf16 and size with KVC_BF16 or KVC_FP8_E4M3), whose kernels may differ
 // (bf16 head dims 64 and 256 run the multi-row kernel, FP8 ones the generic
 // kernel, whose plans take more chunks).
@@ -301,6 +313,10 @@ static AutoShape auto_shape(KernelKind kind, int m, int B, int g, int max_len, b
     const void* f4 = kernel_for(kind, m, paged, false, 4, gen, kv8);
     const long slots4 = device_slots(f4, 4);
     AutoShape split{4, chunks_for_slots(slots4 > 0 ? slots4 : 1, B, g, max_len)};
+    // A paged pool's lengths are ragged: chunks of at most kPagedChunk
+    // positions, so that the long sequences' work spreads over more
+    // work-groups.
+    if (paged) split.chunks = clamp_chunks(std::max(split.chunks, ceil_div(max_len, kPagedChunk)), max_len);
     // bf16 VALU work-groups that fill the slots in one round with 2-8
     // chunks per unit: twice the chunks, two rounds.  The first work-group
     // dispatched to a CU runs ahead of the others there; with a second
@@ -448,7 +464,13 @@ static void* const kUseScratch = &g_use_scratch;
 static int run_decode(DecodeArgs& a, int dtype, int max_len, int num_splits, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
     const bool paged = a.block_table != nullptr;
-    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, a.window > 0,
+    // Over a paged FP8 pool, several new tokens per sequence (the kernels'
+    // general features) ran faster chunked than on the stream grid: 8 rows
+    // per KV head (2 tokens) 130 vs 142 us, 16 rows 135 vs 167 us per call
+    // at 3 chunks over the 64-sequence pool; bf16 pools stream (212 vs 218,
+    // 221 vs 227 us).
+    const bool prefer_chunks = a.window > 0 || (kv_mode(a) != 0 && a.n > 1);
+    Schedule sc = make_schedule(a.B, a.h, a.g, a.d, dtype, max_len, num_splits, paged, prefer_chunks,
                                 kv_mode(a));
     // (the workspace query knows no FP8 flag: it sizes for the bf16 kernels,
     // which bounds the FP8 ones)
