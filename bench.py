@@ -59,7 +59,10 @@ def traffic_file(workload: str) -> str:
 
 
 def _is_decode_call_kernel(name: str) -> bool:
-    return name.startswith("void kvc::decode_") or name.startswith("kvc::merge")
+    """The kernels of one decode call: the decode kernel (or the multi-row
+    kernel) and its merge (a plain or a template kernel name)."""
+    return name.startswith(("void kvc::decode_", "void kvc::prefill_", "kvc::merge",
+                            "void kvc::merge"))
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, calib_mib: int, commands):
@@ -86,7 +89,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, calib_mib: int,
             if _is_decode_call_kernel(n):
                 e = per.setdefault(n, {"fetch": [], "write": []})
                 e[key].append(v)
-    decode_names = [n for n in per if n.startswith("void kvc::decode_")]
+    decode_names = [n for n in per if n.startswith(("void kvc::decode_", "void kvc::prefill_"))]
     if len(decode_names) != 1:
         raise SystemExit(f"expected one decode kernel, found {decode_names}")
     calls = len(per[decode_names[0]]["fetch"])

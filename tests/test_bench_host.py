@@ -133,3 +133,30 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     open(bench.traffic_file("unit_test"), "w").write(
         text.replace(kv["source_sha256"], "0" * 64))
     assert bench.stored_traffic("unit_test") is None
+
+
+def test_traffic_summary_counts_the_merge_kernels(tmp_path, monkeypatch):
+    """A split call's traffic is its decode kernel plus its merge, whether the
+    merge is a plain kernel (kvc::merge_stream_kernel) or a template one
+    (void kvc::merge128_kernel<G>); other kernels are left out."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    mib = 64
+    calib_kib = mib * 1024
+    decode = "void kvc::decode_valu_chunked<1, false, 4, false, 0>(kvc::DecodeArgs)"
+    merge_t = "void kvc::merge128_kernel<8>(kvc::DecodeArgs)"
+    merge_p = "kvc::merge_stream_kernel(kvc::DecodeArgs)"
+    other = "void at::native::vectorized_elementwise_kernel<4>(int)"
+    _write_counters(tmp_path / "f.csv", "FETCH_SIZE",
+                    [(1, "__amd_rocclr_copyBuffer", calib_kib / 2), (2, decode, 1000.0),
+                     (3, merge_t, 20.0), (4, merge_p, 6.0), (5, other, 500.0)])
+    _write_counters(tmp_path / "w.csv", "WRITE_SIZE",
+                    [(1, "__amd_rocclr_copyBuffer", calib_kib), (2, decode, 10.0),
+                     (3, merge_t, 2.0), (4, merge_p, 1.0), (5, other, 500.0)])
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "unit_merge", mib, ["cmd"])
+    kv = {}
+    for line in open(bench.traffic_file("unit_merge")):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    assert int(kv["fetch_bytes_per_call"]) == round((1000.0 + 20.0 + 6.0) * 1024 * 2)
+    assert int(kv["write_bytes_per_call"]) == round((10.0 + 2.0 + 1.0) * 1024)
