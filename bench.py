@@ -584,29 +584,26 @@ def main():
             with torch.cuda.graph(gr):
                 step(r)
             graphs.append(gr)
-        # one graph holding a step on every cache copy, back to back, as a
-        # model's decode graph holds one attention step per layer
+        # one graph holding all K steps back to back, step i on cache copy
+        # i mod copies, as a model's decode graph holds one attention step
+        # per layer: the timed region is one launch, so host launch latency
+        # does not sit between steps even when a step takes a few µs
         cycle = torch.cuda.CUDAGraph()
         with torch.cuda.graph(cycle):
-            for r in range(copies):
-                step(r)
+            for i in range(args.steps):
+                step(i)
         for r in range(copies):
             graphs[r].replay()
         cycle.replay()
         torch.cuda.synchronize()
 
-    # Timed region: exactly K steps between two synchronisations (whole
-    # cycles of `copies` steps, then single steps for the remainder).
+    # Timed region: exactly K steps between two synchronisations.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     if graphs:
-        full, rest = divmod(args.steps, copies)
-        for _ in range(full):
-            cycle.replay()
-        for r in range(rest):
-            graphs[r].replay()
+        cycle.replay()
     else:
         for i in range(args.steps):
             step(i)
@@ -785,7 +782,7 @@ def main():
                          "p90": round(pct(0.9), 5), "samples": len(each),
                          "note": "each step timed alone (includes its launch)"},
         "hot_ms_per_step": round(hot_ms, 5),
-        "timing": "eager" if args.eager else "HIP graphs of whole steps (one step per cache copy)",
+        "timing": "eager" if args.eager else "one HIP graph of the K whole steps (step i on cache copy i mod copies)",
         "roofline": ({
             "bound": "mfma",
             "kernel": "append+decode call: " + ("partials + log-sum-exp merge" if merged
