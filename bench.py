@@ -25,6 +25,7 @@ import csv
 import dataclasses
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -350,6 +351,10 @@ def main():
                          "head) instead of per KV head (kvc_decode_attention_fp8_paged_block_scaled)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying HIP graphs")
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="steps per HIP graph in the timed region (0 = automatic: whole cycles "
+                         "of the cache copies, enough of them that one replay keeps the GPU busy "
+                         "for about 200 us, so that host replays do not pace small steps)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before warm-up, copy this many MiB device-to-device once (a plain copy "
                          "of known size for scaling hardware byte counters)")
@@ -584,17 +589,38 @@ def main():
             with torch.cuda.graph(gr):
                 step(r)
             graphs.append(gr)
-        # one graph holding all K steps back to back, step i on cache copy
-        # i mod copies, as a model's decode graph holds one attention step
-        # per layer: the timed region is one launch, so host launch latency
-        # does not sit between steps even when a step takes a few µs
-        cycle = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(cycle):
-            for i in range(args.steps):
-                step(i)
         for r in range(copies):
             graphs[r].replay()
+        torch.cuda.synchronize()
+        # Graphs of G steps back to back, step i on cache copy i mod copies,
+        # as a model's decode graph holds one attention step per layer: G is
+        # a whole number of cycles over the copies, enough that one replay
+        # keeps the GPU busy for about 200 us (a step of a few µs would
+        # otherwise wait for the host's next replay), and at most K.
+        gsteps = args.graph_steps
+        if gsteps <= 0:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(copies):
+                graphs[r].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            cycle_us = max(e0.elapsed_time(e1) * 1e3, 1e-3)
+            gsteps = copies * max(1, math.ceil(200.0 / cycle_us))
+        gsteps = max(1, min(gsteps, args.steps))
+        full_graphs, rest_steps = divmod(args.steps, gsteps)
+
+        def capture(n):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(n):
+                    step(i)
+            return gr
+        cycle = capture(gsteps)
+        rest = capture(rest_steps) if rest_steps else None
         cycle.replay()
+        if rest is not None:
+            rest.replay()
         torch.cuda.synchronize()
 
     # Timed region: exactly K steps between two synchronisations.
@@ -603,7 +629,10 @@ def main():
     torch.cuda.synchronize()
     t_start.record()
     if graphs:
-        cycle.replay()
+        for _ in range(full_graphs):
+            cycle.replay()
+        if rest is not None:
+            rest.replay()
     else:
         for i in range(args.steps):
             step(i)
@@ -782,7 +811,7 @@ def main():
                          "p90": round(pct(0.9), 5), "samples": len(each),
                          "note": "each step timed alone (includes its launch)"},
         "hot_ms_per_step": round(hot_ms, 5),
-        "timing": "eager" if args.eager else "one HIP graph of the K whole steps (step i on cache copy i mod copies)",
+        "timing": "eager" if args.eager else f"HIP graphs of {gsteps} whole steps (step i on cache copy i mod copies)",
         "roofline": ({
             "bound": "mfma",
             "kernel": "append+decode call: " + ("partials + log-sum-exp merge" if merged
