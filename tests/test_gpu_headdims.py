@@ -256,3 +256,23 @@ def test_append_decode_generic_head_dims(d, dtype, paged, num_splits):
         attended_vmax_contig(v_host, after)
     e = check_parity(out, lse, ro, rl, vmax, f"generic d={d} {dtype}")
     _log(f"  err/vmax {e[0]:.2e} lse {e[1]:.2e}")
+
+
+def test_paged_multi_row_plans_take_short_chunks():
+    """Over a paged bf16 pool (ragged lengths) the multi-row kernel's row
+    groups that fill the device take chunks of at most 2816 positions
+    instead of whole units; FP8 pools and contiguous caches keep whole
+    units there.  (Launch shapes depend on the device's resident slots:
+    these hold on a 256-CU MI355X, where the 128-row work-group keeps two
+    per CU.)"""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"slot counts assume 256 compute units (this device has {cus})")
+    L = 8208  # a 513-entry table of 16-position blocks
+    for d, h in ((96, 32), (128, 32 * 32)):
+        waves, wgs, cl, nc = kvc.launch_shape(64, h, 8, d, L, 0, paged=True)
+        assert (nc, cl) == (3, 2752), (d, h, waves, wgs, cl, nc)
+        waves, wgs, cl, nc = kvc.launch_shape(64, h, 8, d, L, 0, paged=False)
+        assert nc == 1, (d, h, nc)
+    waves, wgs, cl, nc = kvc.launch_shape(64, 32 * 32, 8, 128, L, 0, dtype="fp8", paged=True)
+    assert nc == 1, nc
