@@ -482,20 +482,25 @@ def main():
     else:
         out = torch.empty((w.B, w.h, w.d), dtype=torch.float32, device=dev)
         lse = torch.empty((w.B, w.h), dtype=torch.float32, device=dev)
-    hq = w.h * nq  # query rows per sequence (the planning calls take h * n)
+    hq = w.h * nq  # query rows per sequence (the workspace query takes h * n)
     if w.paged:
-        max_len = bt.shape[1] * x["block_size"]
+        capacity = bt.shape[1] * x["block_size"]
     else:
-        max_len = k0.shape[2]
+        capacity = k0.shape[2]
+    max_len = capacity
     if windowed:  # plans and workspaces cover the positions a window reads
         max_len = min(win + nq - 1, max_len)
     ws_bytes = kvc.workspace_bytes(w.B, hq, w.g, w.d, max_len, ns, dtype=w.torch_dtype,
                                    paged=w.paged)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    split_mode, chunk_len, num_chunks = kvc.plan(w.B, hq, w.g, w.d, max_len, ns,
-                                                 dtype=w.torch_dtype, paged=w.paged)
-    waves, n_wgs, launch_chunk, launch_chunks = kvc.launch_shape(
-        w.B, hq, w.g, w.d, max_len, ns, dtype="fp8" if fp8 else w.torch_dtype, paged=w.paged)
+    # the plan and launch of this call (n tokens, window): the _multi queries
+    plan_dtype = "fp8" if fp8 else w.torch_dtype
+    split_mode, chunk_len, num_chunks = kvc.plan_multi(w.B, w.h, w.g, w.d, nq, capacity, window=win,
+                                                       num_splits=ns, dtype=plan_dtype,
+                                                       paged=w.paged)
+    waves, n_wgs, launch_chunk, launch_chunks = kvc.launch_shape_multi(
+        w.B, w.h, w.g, w.d, nq, capacity, window=win, num_splits=ns, dtype=plan_dtype,
+        paged=w.paged)
     merged = split_mode == "stream" or launch_chunks > 1
 
     if args.calibration_copy_mib > 0:

@@ -188,6 +188,25 @@ size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max
 int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_len,
                             int num_splits, int paged, int* waves, int* num_wgs,
                             int* chunk_len, int* num_chunks);
+/*
+ * The same two queries for the calls with n query tokens per sequence and a
+ * sliding window W (0 = none): the _multi, _window and FP8 _fp8_multi /
+ * _fp8_window calls, whose plans can differ from the single-token call's
+ * (their kernels' registers, and an automatic split of a paged FP8 pool with
+ * n > 1 takes chunks).  h is query heads (not h * n); capacity is t_cap
+ * (contiguous; ring caches too) or max_blocks * block_size (paged); the
+ * plan covers min(capacity, W + n - 1) positions with a window, as the
+ * calls do.  dtype KVC_FP8_E4M3 stands for FP8 caches with a scale per KV
+ * head.  n = 1 and W = 0 give kvc_decode_plan / kvc_decode_launch_shape
+ * with max_seq_len = capacity.  Returns KVC_OK, KVC_ERR_INVALID (n <= 0,
+ * W < 0, a negative capacity, or as the single-token queries) or
+ * KVC_ERR_UNSUPPORTED (h * n > 65535, or as the single-token queries).
+ */
+int kvc_decode_plan_multi(int B, int h, int g, int d, int n, int window, int dtype, int capacity,
+                          int num_splits, int paged, int* mode, int* chunk_len, int* num_chunks);
+int kvc_decode_launch_shape_multi(int B, int h, int g, int d, int n, int window, int dtype,
+                                  int capacity, int num_splits, int paged, int* waves,
+                                  int* num_wgs, int* chunk_len, int* num_chunks);
 
 /*
  * kvc_decode_attention -- decode attention over a contiguous cache.
@@ -324,7 +343,9 @@ size_t kvc_noalloc_scratch_bytes(void);
  *   Token t sees min(P_b + t + 1, capacity) positions (0 if negative).
  * Everything else is as for the single-token calls, which are the case
  * n = 1.  The workspace is kvc_decode_workspace_bytes(B, h * n, g, d, ...);
- * kvc_decode_plan and kvc_decode_launch_shape likewise take h * n as h.
+ * kvc_decode_plan_multi and kvc_decode_launch_shape_multi give these calls'
+ * plans (kvc_decode_plan and kvc_decode_launch_shape, taking h * n as h,
+ * describe a single-token call with as many rows).
  * Kernels by rows per KV head, r = (h / g) * n, for bf16 with d = 128: r <= 3
  * the VALU kernel; 4 <= r <= 32 the matrix-core decode kernel; r > 32 the
  * multi-row matrix-core kernel, which stages each K/V tile in LDS once for
@@ -488,8 +509,8 @@ int kvc_append_decode_attention_fp8_paged(const void* q, const void* k_new, cons
  *   non-appending call gives.
  *   Attention is over the dequantised values code * scale.
  *   Splits: with n > 1 an automatic split (num_splits = 0) of a paged pool
- *   takes chunks, not the stream grid (measured faster there); the plan
- *   queries, which take h * n and no n, describe the single-token call.
+ *   takes chunks, not the stream grid (measured faster there), as
+ *   kvc_decode_plan_multi reports.
  */
 int kvc_decode_attention_fp8_multi(const void* q, const void* k_cache, const void* v_cache,
                                    const float* k_scale, const float* v_scale,

@@ -29,6 +29,7 @@ __all__ = ["append", "decode", "decode_paged", "append_decode", "decode_multi",
            "append_decode_noalloc", "append_fp8_block_scaled", "decode_fp8_block_scaled",
            "copy_blocks",
            "fork_block_tables", "gather_cache", "plan", "workspace_bytes", "launch_shape",
+           "plan_multi", "launch_shape_multi",
            "KvcError", "load_library", "LIB_PATH", "F32", "BF16", "FP8_E4M3", "SPLITS_STREAM"]
 
 # KVC_LIB names another build of the library (the sanitizer test loads one
@@ -73,6 +74,10 @@ def load_library():
     lib.kvc_decode_workspace_bytes.restype = sz
     lib.kvc_decode_launch_shape.argtypes = [ip] * 8 + [ctypes.POINTER(ip)] * 4
     lib.kvc_decode_launch_shape.restype = ip
+    lib.kvc_decode_plan_multi.argtypes = [ip] * 10 + [ctypes.POINTER(ip)] * 3
+    lib.kvc_decode_plan_multi.restype = ip
+    lib.kvc_decode_launch_shape_multi.argtypes = [ip] * 10 + [ctypes.POINTER(ip)] * 4
+    lib.kvc_decode_launch_shape_multi.restype = ip
     lib.kvc_append_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ip, fp, ip,
                                                 ip, vp, sz, vp, vp, vp]
     lib.kvc_append_decode_attention.restype = ip
@@ -282,6 +287,34 @@ def launch_shape(B: int, h: int, g: int, d: int, max_seq_len: int, num_splits: i
     _check("kvc_decode_launch_shape",
            lib.kvc_decode_launch_shape(B, h, g, d, _code(dtype), max_seq_len, num_splits, int(paged),
                                        *(ctypes.byref(x) for x in out)))
+    return tuple(x.value for x in out)
+
+
+def plan_multi(B: int, h: int, g: int, d: int, n: int, capacity: int, window: int = 0,
+               num_splits: int = 0, dtype=torch.bfloat16, paged: bool = False) -> Tuple[str, int, int]:
+    """plan() of a call with n query tokens per sequence and a sliding window
+    (0 = none): h is query heads, capacity t_cap or max_blocks * block_size."""
+    lib = load_library()
+    mode, cl, nc = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check("kvc_decode_plan_multi",
+           lib.kvc_decode_plan_multi(B, h, g, d, n, window, _code(dtype), capacity, num_splits,
+                                     int(paged), ctypes.byref(mode), ctypes.byref(cl),
+                                     ctypes.byref(nc)))
+    return _MODES[mode.value], cl.value, nc.value
+
+
+def launch_shape_multi(B: int, h: int, g: int, d: int, n: int, capacity: int, window: int = 0,
+                       num_splits: int = 0, dtype=torch.bfloat16,
+                       paged: bool = False) -> Tuple[int, int, int, int]:
+    """launch_shape() of a call with n query tokens per sequence and a sliding
+    window (0 = none): h is query heads, capacity t_cap or max_blocks *
+    block_size."""
+    lib = load_library()
+    out = [ctypes.c_int(0) for _ in range(4)]
+    _check("kvc_decode_launch_shape_multi",
+           lib.kvc_decode_launch_shape_multi(B, h, g, d, n, window, _code(dtype), capacity,
+                                             num_splits, int(paged),
+                                             *(ctypes.byref(x) for x in out)))
     return tuple(x.value for x in out)
 
 

@@ -549,15 +549,33 @@ const char* kvc_status_string(int status) {
     }
 }
 
-int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
-                    int paged, int* mode, int* chunk_len, int* num_chunks) {
+// Longest position range a unit can read: the capacity, or with a sliding
+// window the window plus the other new tokens.  Chunk plans and workspaces
+// are sized for it.
+static int plan_len(int capacity, int window, int n) {
+    if (window <= 0) return capacity;
+    const long w = (long)window + n - 1;
+    return w < capacity ? (int)w : capacity;
+}
+
+// The schedule a call with n query tokens per sequence and window W makes
+// (n = 1, W = 0: the single-token call): h counts query rows (h * n).
+static Schedule query_schedule(int B, int h, int g, int d, int dtype, int max_len, int num_splits,
+                               bool paged, int n, int window, bool kv8) {
+    const bool prefer_chunks = window > 0 || (kv8 && n > 1);
+    return make_schedule(B, h, g, d, dtype, max_len, num_splits, paged, prefer_chunks, kv8 ? 1 : 0);
+}
+
+static int plan_query(int B, int h, int g, int d, int n, int window, int dtype, int max_seq_len,
+                      int num_splits, int paged, int* mode, int* chunk_len, int* num_chunks) {
     if (B < 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
-        max_seq_len < 0)
+        max_seq_len < 0 || n <= 0 || window < 0)
         return KVC_ERR_INVALID;
     const bool kv8 = dtype == KVC_FP8_E4M3;  // bf16 q over an FP8 cache
     if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
-    const Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8 ? 1 : 0);
+    const Schedule sc = query_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, n,
+                                       window, kv8);
     if (mode) *mode = sc.stream ? KVC_SPLIT_STREAM : (sc.auto_chunks ? KVC_SPLIT_AUTO_CHUNKS : KVC_SPLIT_CHUNKS);
     const bool fixed = !sc.stream && !sc.auto_chunks;
     if (chunk_len) *chunk_len = fixed ? sc.plan.chunk_len : 0;
@@ -565,18 +583,35 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
     return KVC_OK;
 }
 
-int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
-                            int paged, int* waves, int* num_wgs, int* chunk_len, int* num_chunks) {
+int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
+                    int paged, int* mode, int* chunk_len, int* num_chunks) {
+    return plan_query(B, h, g, d, 1, 0, dtype, max_seq_len, num_splits, paged, mode, chunk_len,
+                      num_chunks);
+}
+
+int kvc_decode_plan_multi(int B, int h, int g, int d, int n, int window, int dtype, int capacity,
+                          int num_splits, int paged, int* mode, int* chunk_len, int* num_chunks) {
+    if (n <= 0 || h <= 0 || window < 0 || capacity < 0) return KVC_ERR_INVALID;
+    if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
+    return plan_query(B, h * n, g, d, n, window, dtype, plan_len(capacity, window, n), num_splits,
+                      paged, mode, chunk_len, num_chunks);
+}
+
+static int launch_shape_query(int B, int h, int g, int d, int n, int window, int dtype,
+                              int max_seq_len, int num_splits, int paged, int* waves, int* num_wgs,
+                              int* chunk_len, int* num_chunks) {
     if (B <= 0 || h <= 0 || g <= 0 || d <= 0 || h % g != 0 || num_splits < KVC_SPLITS_STREAM ||
-        max_seq_len <= 0)
+        max_seq_len <= 0 || n <= 0 || window < 0)
         return KVC_ERR_INVALID;
     const bool kv8 = dtype == KVC_FP8_E4M3;
     if (kv8) dtype = KVC_BF16;
     if (dtype != KVC_F32 && dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
     if (d > 256) return KVC_ERR_UNSUPPORTED;
-    Schedule sc = make_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, false, kv8 ? 1 : 0);
+    Schedule sc = query_schedule(B, h, g, d, dtype, max_seq_len, num_splits, paged != 0, n, window,
+                                 kv8);
     DecodeArgs a{};
-    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.n = 1; a.cap_len = max_seq_len;
+    a.B = B; a.h = h; a.g = g; a.d = d; a.m = h / g; a.n = n; a.window = window;
+    a.cap_len = max_seq_len;
     a.kv8 = kv8 ? 1 : 0;
     resolve_launch(a, sc, paged != 0, max_seq_len);
     if (waves) *waves = a.waves;
@@ -588,6 +623,21 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
     if (chunk_len) *chunk_len = a.stream ? 0 : a.chunk_len;
     if (num_chunks) *num_chunks = a.stream ? 0 : a.num_chunks;
     return KVC_OK;
+}
+
+int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_len, int num_splits,
+                            int paged, int* waves, int* num_wgs, int* chunk_len, int* num_chunks) {
+    return launch_shape_query(B, h, g, d, 1, 0, dtype, max_seq_len, num_splits, paged, waves,
+                              num_wgs, chunk_len, num_chunks);
+}
+
+int kvc_decode_launch_shape_multi(int B, int h, int g, int d, int n, int window, int dtype,
+                                  int capacity, int num_splits, int paged, int* waves,
+                                  int* num_wgs, int* chunk_len, int* num_chunks) {
+    if (n <= 0 || h <= 0 || window < 0 || capacity <= 0) return KVC_ERR_INVALID;
+    if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
+    return launch_shape_query(B, h * n, g, d, n, window, dtype, plan_len(capacity, window, n),
+                              num_splits, paged, waves, num_wgs, chunk_len, num_chunks);
 }
 
 size_t kvc_decode_workspace_bytes(int B, int h, int g, int d, int dtype, int max_seq_len,
@@ -617,15 +667,6 @@ int kvc_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
                       seq_lens_before, B, g, 1, d, capacity, 0, eb, stream) != hipSuccess)
         return KVC_ERR_HIP;
     return KVC_OK;
-}
-
-// Longest position range a unit can read: the capacity, or with a sliding
-// window the window plus the other new tokens.  Chunk plans and workspaces
-// are sized for it.
-static int plan_len(int capacity, int window, int n) {
-    if (window <= 0) return capacity;
-    const long w = (long)window + n - 1;
-    return w < capacity ? (int)w : capacity;
 }
 
 // Shared body of the contiguous entry points.  n queries per sequence

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     for n in ("kvc_append", "kvc_decode_attention", "kvc_decode_attention_paged",
               "kvc_append_decode_attention", "kvc_append_decode_attention_paged",
               "kvc_decode_workspace_bytes", "kvc_decode_plan", "kvc_decode_launch_shape",
+              "kvc_decode_plan_multi", "kvc_decode_launch_shape_multi",
               "kvc_status_string", "kvc_version"):
         assert n in names
 
@@ -98,6 +99,28 @@ def test_plan_modes():
         assert kvc.plan(64, 32, 1, 128, 8208, 0, dtype=kv, paged=True)[0] == want
         assert kvc.plan(64, 24, 1, 128, 8208, 0, dtype=kv, paged=True)[0] == want
         assert kvc.plan(64, 16, 1, 128, 8208, 0, dtype=kv, paged=True)[0] == "stream"
+    # the queries of calls with several tokens or a window (h query heads,
+    # capacity): FP8 paged pools with n > 1 take chunks, bf16 ones stream;
+    # windows chunk; n = 1 and no window match the single-token query
+    fp8 = kvc.FP8_E4M3
+    assert kvc.plan_multi(64, 32, 8, 128, 2, 8208, dtype=fp8, paged=True)[0] == "auto_chunks"
+    assert kvc.plan_multi(64, 32, 8, 128, 2, 8208, paged=True)[0] == "stream"
+    assert kvc.plan_multi(64, 32, 8, 128, 1, 8208, dtype=fp8, paged=True)[0] == "stream"
+    assert kvc.plan_multi(64, 32, 8, 128, 2, 8208, window=1024, paged=True)[0] == "auto_chunks"
+    for (B, h, g, d, L, ns, dt, pg) in [(32, 64, 8, 128, 4112, 0, torch.bfloat16, False),
+                                         (64, 32, 8, 128, 8208, 0, fp8, True),
+                                         (8, 8, 2, 96, 1000, 3, torch.float32, False)]:
+        assert kvc.plan_multi(B, h, g, d, 1, L, num_splits=ns, dtype=dt, paged=pg) == \
+            kvc.plan(B, h, g, d, L, ns, dtype=dt, paged=pg)
+    # rows h * n; a window caps the planned length at W + n - 1
+    assert kvc.plan_multi(2, 8, 2, 128, 4, 4096, num_splits=2) == kvc.plan(2, 32, 2, 128, 4096, 2)
+    assert kvc.plan_multi(2, 8, 2, 128, 4, 4096, window=100, num_splits=2) == \
+        kvc.plan(2, 32, 2, 128, 103, 2)
+    lib = kvc.load_library()
+    assert lib.kvc_decode_plan_multi(2, 8, 2, 128, 0, 0, 1, 64, 0, 0, None, None, None) == INVALID
+    assert lib.kvc_decode_plan_multi(2, 8, 2, 128, 1, -1, 1, 64, 0, 0, None, None, None) == INVALID
+    assert lib.kvc_decode_plan_multi(2, 4096, 2, 128, 32, 0, 1, 64, 0, 0, None, None, None) == \
+        UNSUPPORTED
     # stream mode needs B <= 1024
     assert kvc.plan(2048, 8, 8, 128, 512, 0, paged=True)[0] == "auto_chunks"
     # chunks: a multiple of 32, covering max_seq_len, at most 4096

@@ -276,3 +276,8 @@ def test_paged_multi_row_plans_take_short_chunks():
         assert nc == 1, (d, h, nc)
     waves, wgs, cl, nc = kvc.launch_shape(64, 32 * 32, 8, 128, L, 0, dtype="fp8", paged=True)
     assert nc == 1, nc
+    # the FP8 decode kernel with two new tokens per sequence over the same
+    # pool: chunks (not the stream grid), 3 of 2752 positions; the bf16 one
+    # streams (chunk fields 0)
+    assert kvc.launch_shape_multi(64, 32, 8, 128, 2, L, dtype="fp8", paged=True)[2:] == (2752, 3)
+    assert kvc.launch_shape_multi(64, 32, 8, 128, 2, L, paged=True)[2:] == (0, 0)
