@@ -56,11 +56,18 @@ def _vmax(v, table, lengths, bs) -> float:
     return attended_vmax_paged(v, table, lengths, bs)
 
 
-def _draw(mode: str, seed: int) -> dict:
+DIMS = [16, 32, 64, 96, 128, 256]
+# the second sweep: head dims of every kernel family (80 and 96 on the
+# multi-row kernel with bf16, 112 and the fp32 ones on the generic kernel)
+DIMS_WIDE = [16, 32, 64, 80, 96, 112, 128, 256]
+CASES_PER_MODE_WIDE = 20
+
+
+def _draw(mode: str, seed: int, dims=DIMS) -> dict:
     r = np.random.default_rng(seed)
     fp8 = mode == "fp8"
     dtype = "bf16" if fp8 or r.random() < 0.75 else "f32"
-    d = 128 if (dtype == "bf16" and r.random() < 0.7) else int(r.choice([16, 32, 64, 96, 128, 256]))
+    d = 128 if (dtype == "bf16" and r.random() < 0.7) else int(r.choice(dims))
     g = int(r.choice([1, 2, 4, 8]))
     m = int(r.choice([1, 2, 3, 4, 5, 8, 12, 16, 24, 32, 40]))
     n = 1
@@ -83,12 +90,14 @@ def _cases():
     for mi, mode in enumerate(MODES):
         for k in range(CASES_PER_MODE):
             out.append((mode, 9000 + 100 * mi + k))
+        for k in range(CASES_PER_MODE_WIDE):  # seeds 19000.. draw from DIMS_WIDE
+            out.append((mode, 19000 + 100 * mi + k))
     return out
 
 
 @pytest.mark.parametrize("mode,seed", _cases(), ids=[f"{m}-{s}" for m, s in _cases()])
 def test_random_case(mode, seed):
-    c = _draw(mode, seed)
+    c = _draw(mode, seed, DIMS_WIDE if seed >= 19000 else DIMS)
     _log(f"case random {mode} seed={seed} {dict((k, v) for k, v in c.items() if k != 'lengths')} "
          f"lengths={c['lengths'].tolist()}")
     B, h, g, d, n, bs = c["B"], c["h"], c["g"], c["d"], c["n"], c["bs"]
