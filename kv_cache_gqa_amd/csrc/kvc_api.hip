@@ -591,7 +591,9 @@ int kvc_decode_plan(int B, int h, int g, int d, int dtype, int max_seq_len, int 
 
 int kvc_decode_plan_multi(int B, int h, int g, int d, int n, int window, int dtype, int capacity,
                           int num_splits, int paged, int* mode, int* chunk_len, int* num_chunks) {
-    if (n <= 0 || h <= 0 || window < 0 || capacity < 0) return KVC_ERR_INVALID;
+    // h counts query heads: the head map needs h % g == 0 before the rows multiply by n
+    if (n <= 0 || h <= 0 || g <= 0 || h % g != 0 || window < 0 || capacity < 0)
+        return KVC_ERR_INVALID;
     if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
     return plan_query(B, h * n, g, d, n, window, dtype, plan_len(capacity, window, n), num_splits,
                       paged, mode, chunk_len, num_chunks);
@@ -634,7 +636,8 @@ int kvc_decode_launch_shape(int B, int h, int g, int d, int dtype, int max_seq_l
 int kvc_decode_launch_shape_multi(int B, int h, int g, int d, int n, int window, int dtype,
                                   int capacity, int num_splits, int paged, int* waves,
                                   int* num_wgs, int* chunk_len, int* num_chunks) {
-    if (n <= 0 || h <= 0 || window < 0 || capacity <= 0) return KVC_ERR_INVALID;
+    if (n <= 0 || h <= 0 || g <= 0 || h % g != 0 || window < 0 || capacity <= 0)
+        return KVC_ERR_INVALID;
     if ((long)h * n > 65535) return KVC_ERR_UNSUPPORTED;
     return launch_shape_query(B, h * n, g, d, n, window, dtype, plan_len(capacity, window, n),
                               num_splits, paged, waves, num_wgs, chunk_len, num_chunks);

@@ -121,6 +121,15 @@ def test_plan_modes():
     assert lib.kvc_decode_plan_multi(2, 8, 2, 128, 1, -1, 1, 64, 0, 0, None, None, None) == INVALID
     assert lib.kvc_decode_plan_multi(2, 4096, 2, 128, 32, 0, 1, 64, 0, 0, None, None, None) == \
         UNSUPPORTED
+    # the head map is checked on the query heads, not on the h * n rows: 3 heads over 2 KV heads
+    # is invalid however many tokens make the row count even
+    for n in (1, 2, 4):
+        assert lib.kvc_decode_plan_multi(2, 3, 2, 128, n, 0, 1, 64, 0, 0, None, None, None) == INVALID
+        assert lib.kvc_decode_launch_shape_multi(2, 3, 2, 128, n, 0, 1, 64, 0, 0,
+                                                 None, None, None, None) == INVALID
+    assert lib.kvc_decode_plan_multi(2, 8, 0, 128, 2, 0, 1, 64, 0, 0, None, None, None) == INVALID
+    assert lib.kvc_decode_launch_shape_multi(2, 8, 0, 128, 2, 0, 1, 64, 0, 0,
+                                             None, None, None, None) == INVALID
     # stream mode needs B <= 1024
     assert kvc.plan(2048, 8, 8, 128, 512, 0, paged=True)[0] == "auto_chunks"
     # chunks: a multiple of 32, covering max_seq_len, at most 4096
